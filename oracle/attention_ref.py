@@ -1,0 +1,244 @@
+"""CPU fp64 oracle for exact attention and its split-KV / paged-KV decode form.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path imports this module; it
+is called by the tests, by the smoke check and by the bench's CPU baseline leg.
+
+The tiled method reaches, up to rounding order, the plain result of standard
+attention, so the oracle is that plain definition written out: materialise the
+score matrix S for one (batch, head), apply the score transforms and the mask,
+take a row-wise softmax, multiply by V ("FlashAttention及变种改进", section 二.1,
+the bottleneck of standard self-attention). Rows are
+independent, so the oracle may compute any subset of query rows and may chunk
+rows to bound host memory; no other blocking, fusion or reordering is done.
+
+Variant definitions (the flash-attn v2.0-v2.7 update article, its v2.1 to v2.6
+entries):
+
+* causal mask aligned to the bottom-right corner of the score matrix: with
+  off = Nk - Nq, query row i may see key j iff j <= i + off (v2.1 entry; the
+  one-token decode query sees every cached key).
+* sliding window (v2.3 entry): keys j in [i + off - window_left,
+  i + off + window_right], inclusive; -1 means unbounded on that side.
+* ALiBi (v2.4 entry): a linear position penalty, score -= slope_h * |i + off - j|.
+* softcap (v2.6 entry): tanh cap on the scaled score,
+  s <- softcap * tanh(s / softcap), applied before the bias and the mask.
+* split-KV (v2.2 entry): keys are cut along the sequence into contiguous chunks,
+  each chunk yields a normalised partial output and its log-sum-exp, and a
+  separate reduce step merges the chunks.
+* paged KV cache (v2.5 entry): logical key t of sequence b lives in physical page
+  block_table[b, t // page_size], row t % page_size.
+
+Conventions the pages leave open (each is stated with its reason where it is
+used): LSE is the natural log of the row's sum of exp over allowed keys; a row
+with no allowed key has O = 0 and LSE = -inf; split chunk length is
+ceil(Nk / S) rounded up to a whole number of pages.
+
+All arithmetic is float64 on the exact input values.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = float("-inf")
+_CHUNK_BYTES = 256 << 20
+
+
+# --------------------------------------------------------------------------
+# Mask geometry (flash-attn update article, v2.1 and v2.3 entries)
+# --------------------------------------------------------------------------
+def allowed_mask(nq: int, nk: int, rows: np.ndarray, causal: bool,
+                 window_left: int, window_right: int,
+                 key_lo: int = 0, key_hi: int | None = None) -> np.ndarray:
+    """Boolean [len(rows), nk]: may query row i attend to key j.
+
+    The diagonal is anchored at the bottom-right corner: i' = i + (nk - nq).
+    Causal keeps j <= i'. A window keeps i' - window_left <= j <= i' + window_right
+    (each side unbounded when negative). key_lo/key_hi further restrict the keys
+    to one split chunk [key_lo, key_hi).
+    """
+    off = nk - nq
+    ip = (np.asarray(rows, dtype=np.int64) + off)[:, None]
+    j = np.arange(nk, dtype=np.int64)[None, :]
+    ok = np.ones((ip.shape[0], nk), dtype=bool)
+    if causal:
+        ok &= j <= ip
+    if window_left >= 0:
+        ok &= j >= ip - window_left
+    if window_right >= 0:
+        ok &= j <= ip + window_right
+    if key_lo > 0:
+        ok &= j >= key_lo
+    if key_hi is not None:
+        ok &= j < key_hi
+    return ok
+
+
+# --------------------------------------------------------------------------
+# Scores for one (batch, head)
+# --------------------------------------------------------------------------
+def scores_ref(q_bh: np.ndarray, k_bh: np.ndarray, rows: np.ndarray, nq: int,
+               scale: float, causal: bool = False, window_left: int = -1,
+               window_right: int = -1, slope: float | None = None,
+               softcap: float = 0.0, key_lo: int = 0,
+               key_hi: int | None = None) -> np.ndarray:
+    """S[r, j] for the selected query rows: scaled, capped, biased, masked (-inf).
+
+    q_bh: [len(rows), d] (the selected rows), k_bh: [nk, d].
+    """
+    nk = k_bh.shape[0]
+    s = (q_bh @ k_bh.T) * scale                       # standard attention: Q K^T, scaled
+    if softcap > 0.0:                                 # v2.6: tanh cap on the scaled score
+        s = softcap * np.tanh(s / softcap)
+    if slope is not None:                             # v2.4: linear distance penalty
+        off = nk - nq
+        ip = (np.asarray(rows, dtype=np.int64) + off)[:, None]
+        j = np.arange(nk, dtype=np.int64)[None, :]
+        s = s - slope * np.abs(ip - j).astype(np.float64)
+    ok = allowed_mask(nq, nk, rows, causal, window_left, window_right, key_lo, key_hi)
+    return np.where(ok, s, NEG_INF)
+
+
+def softmax_rows(s: np.ndarray):
+    """Row softmax of a masked score block. Returns (P, row max m, row sum l).
+
+    A row whose every entry is -inf gets P = 0, m = -inf, l = 0.
+    """
+    m = s.max(axis=1)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    p = np.exp(s - m_safe[:, None])                   # exp(-inf) = 0 for masked keys
+    l = p.sum(axis=1)
+    p = np.where(l[:, None] > 0, p / np.where(l > 0, l, 1.0)[:, None], 0.0)
+    return p, m, l
+
+
+def attend_rows(s: np.ndarray, v_bh: np.ndarray):
+    """O = softmax(S) V and LSE = m + ln l for one block of rows."""
+    p, m, l = softmax_rows(s)
+    o = p @ v_bh
+    lse = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), NEG_INF)
+    return o, lse
+
+
+def _row_chunks(rows: np.ndarray, nk: int):
+    step = max(1, _CHUNK_BYTES // (8 * max(1, nk) * 3))
+    for c0 in range(0, len(rows), step):
+        yield rows[c0:c0 + step]
+
+
+def attention_bh(q_all, k_bh, v_bh, rows, nq, scale, causal=False, window_left=-1,
+                 window_right=-1, slope=None, softcap=0.0, key_lo=0, key_hi=None):
+    """O [len(rows), d] and LSE [len(rows)] for one (batch, head).
+
+    q_all: [nq, d] (every query row of the head); only `rows` are computed.
+    k_bh, v_bh: [nk, d]. key_lo/key_hi restrict the keys to one split chunk.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    o = np.zeros((len(rows), v_bh.shape[1]), dtype=np.float64)
+    lse = np.full(len(rows), NEG_INF, dtype=np.float64)
+    pos = 0
+    for rc in _row_chunks(rows, k_bh.shape[0]):
+        s = scores_ref(q_all[rc], k_bh, rc, nq, scale, causal, window_left,
+                       window_right, slope, softcap, key_lo, key_hi)
+        oc, lc = attend_rows(s, v_bh)
+        o[pos:pos + len(rc)] = oc
+        lse[pos:pos + len(rc)] = lc
+        pos += len(rc)
+    return o, lse
+
+
+def attention_ref(q, k, v, scale, causal=False, window_left=-1, window_right=-1,
+                  alibi_slopes=None, softcap=0.0, rows=None, bh=None):
+    """Exact attention forward over contiguous tensors.
+
+    q [B, Nq, H, d], k and v [B, Nk, H, d] (any float dtype; computed in fp64).
+    rows: optional subset of query rows; bh: optional list of (b, h) pairs.
+    Returns O [B, len(rows), H, d] and LSE [B, H, len(rows)]; entries of pairs
+    outside bh are NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, nq, H, _ = q.shape
+    rows = np.arange(nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if bh is None else bh
+    o = np.full((B, len(rows), H, v.shape[3]), np.nan)
+    lse = np.full((B, H, len(rows)), np.nan)
+    for b, h in pairs:
+        slope = None if alibi_slopes is None else float(alibi_slopes[h])
+        ob, lb = attention_bh(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], rows, nq,
+                              scale, causal, window_left, window_right, slope, softcap)
+        o[b, :, h, :] = ob
+        lse[b, h, :] = lb
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# Paged KV cache (flash-attn update article, v2.5 entry)
+# --------------------------------------------------------------------------
+def paged_gather_ref(cache: np.ndarray, block_table: np.ndarray, b: int, nk: int) -> np.ndarray:
+    """Logical keys [nk, H, d] of sequence b from a pool [num_pages, page_size, H, d].
+
+    Key t sits in physical page block_table[b, t // page_size], row t % page_size.
+    """
+    ps = cache.shape[1]
+    t = np.arange(nk)
+    return cache[np.asarray(block_table)[b, t // ps], t % ps]
+
+
+# --------------------------------------------------------------------------
+# Split-KV and its reduce step (flash-attn update article, v2.2 entry)
+# --------------------------------------------------------------------------
+def split_bounds(nk: int, num_splits: int, page_size: int = 1):
+    """Contiguous key chunks [lo, hi) for each split.
+
+    The chunk length is ceil(nk / num_splits) rounded up to a whole number of
+    pages, so a chunk never cuts a page; trailing chunks may be empty.
+    """
+    c = -(-nk // num_splits)
+    c = -(-c // page_size) * page_size
+    return [(min(nk, s * c), min(nk, (s + 1) * c)) for s in range(num_splits)]
+
+
+def splitkv_ref(q, k, v, num_splits, page_size, scale, causal=False, window_left=-1,
+                window_right=-1, alibi_slopes=None, softcap=0.0, bh=None):
+    """Per-split normalised outputs and log-sum-exps over contiguous logical K/V.
+
+    Returns o_part [S, B, H, Nq, d] and lse_part [S, B, H, Nq]; an empty chunk
+    (or a row with no allowed key inside it) has o = 0 and lse = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, nq, H, d = q.shape
+    nk = k.shape[1]
+    pairs = [(b, h) for b in range(B) for h in range(H)] if bh is None else bh
+    o_part = np.full((num_splits, B, H, nq, v.shape[3]), np.nan)
+    lse_part = np.full((num_splits, B, H, nq), np.nan)
+    rows = np.arange(nq)
+    for s, (lo, hi) in enumerate(split_bounds(nk, num_splits, page_size)):
+        for b, h in pairs:
+            slope = None if alibi_slopes is None else float(alibi_slopes[h])
+            ob, lb = attention_bh(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], rows, nq,
+                                  scale, causal, window_left, window_right, slope,
+                                  softcap, key_lo=lo, key_hi=hi)
+            o_part[s, b, h] = ob
+            lse_part[s, b, h] = lb
+    return o_part, lse_part
+
+
+def combine_ref(o_part: np.ndarray, lse_part: np.ndarray):
+    """Merge split partials: L = ln sum_s exp(lse_s), O = sum_s exp(lse_s - L) o_s.
+
+    o_part [S, ..., d], lse_part [S, ...]. Where every split is empty: O = 0, L = -inf.
+    """
+    o_part = np.asarray(o_part, dtype=np.float64)
+    lse_part = np.asarray(lse_part, dtype=np.float64)
+    m = lse_part.max(axis=0)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(lse_part - m_safe[None])               # exp(-inf) = 0 for empty splits
+    tot = w.sum(axis=0)
+    L = np.where(tot > 0, m_safe + np.log(np.where(tot > 0, tot, 1.0)), NEG_INF)
+    o = np.where((tot > 0)[..., None],
+                 (w[..., None] * o_part).sum(axis=0) / np.where(tot > 0, tot, 1.0)[..., None],
+                 0.0)
+    return o, L

@@ -1,0 +1,398 @@
+"""Pins for the CPU fp64 oracle: checks against facts that do not come from the oracle.
+
+Each test names what it pins. Together they are chosen so that a plausible slip
+in the oracle (a dropped transform, a wrong sign, a shifted diagonal, a
+transposed operand, a wrong log base, a wrong split rule) fails at least one.
+All CPU, float64.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_examples.json")
+
+MASKS = [  # (causal, window_left, window_right)
+    (False, -1, -1), (True, -1, -1), (False, 3, -1), (False, -1, 2), (False, 2, 5),
+    (True, 4, -1), (True, 0, -1), (False, 0, 0), (True, 1, 0),
+]
+
+
+def rnd(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def interval(i, nq, nk, causal, wl, wr):
+    """Closed-form allowed key interval [lo, hi] of row i (bottom-right anchored)."""
+    ip = i + nk - nq
+    lo, hi = 0, nk - 1
+    if causal:
+        hi = min(hi, ip)
+    if wl >= 0:
+        lo = max(lo, ip - wl)
+    if wr >= 0:
+        hi = min(hi, ip + wr)
+    return lo, hi
+
+
+# T1 -----------------------------------------------------------------------
+@pytest.mark.parametrize("causal,wl,wr", MASKS)
+def test_t1_softmax_rows_sum_to_one(causal, wl, wr):
+    nq, nk, d = 7, 11, 5
+    q, k = rnd(1, nq, d), rnd(2, nk, d)
+    rows = np.arange(nq)
+    s = O.scores_ref(q, k, rows, nq, 0.3, causal, wl, wr, slope=0.25, softcap=2.0)
+    p, m, l = O.softmax_rows(s)
+    ok = O.allowed_mask(nq, nk, rows, causal, wl, wr)
+    assert np.all(p >= 0)
+    assert np.all(p[~ok] == 0)
+    nonempty = ok.any(axis=1)
+    np.testing.assert_allclose(p[nonempty].sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(p[~nonempty] == 0)
+
+
+# T2 / T4 ------------------------------------------------------------------
+@pytest.mark.parametrize("causal,wl,wr", MASKS)
+@pytest.mark.parametrize("nq,nk", [(5, 5), (3, 9), (9, 4), (1, 6), (6, 1)])
+def test_t2_zero_query_gives_log_count_and_mean(causal, wl, wr, nq, nk):
+    """Q = 0: every allowed score is 0, so LSE_i = ln(n_i) and O_i = mean of allowed V."""
+    d = 4
+    q = np.zeros((1, nq, 1, d))
+    k = rnd(3, 1, nk, 1, d)
+    v = rnd(4, 1, nk, 1, d)
+    o, lse = O.attention_ref(q, k, v, 0.7, causal, wl, wr)
+    for i in range(nq):
+        lo, hi = interval(i, nq, nk, causal, wl, wr)
+        n = max(0, hi - lo + 1)
+        if n == 0:
+            assert lse[0, 0, i] == -math.inf
+            assert np.all(o[0, i, 0] == 0.0)
+        else:
+            assert abs(lse[0, 0, i] - math.log(n)) <= 1e-12
+            np.testing.assert_allclose(o[0, i, 0], v[0, lo:hi + 1, 0].mean(axis=0), atol=1e-12)
+
+
+def test_t4_bottom_right_counts():
+    """Causal counts: Nq=Nk -> i+1; Nq<Nk -> i+off+1; Nq>Nk -> first Nq-Nk rows empty."""
+    d = 3
+    for nq, nk in [(6, 6), (3, 8), (8, 3)]:
+        q = np.zeros((1, nq, 1, d))
+        k, v = rnd(5, 1, nk, 1, d), rnd(6, 1, nk, 1, d)
+        _, lse = O.attention_ref(q, k, v, 1.0, causal=True)
+        off = nk - nq
+        for i in range(nq):
+            n = i + off + 1
+            if n <= 0:
+                assert lse[0, 0, i] == -math.inf
+            else:
+                assert abs(lse[0, 0, i] - math.log(min(n, nk))) < 1e-12
+
+
+# T3 -----------------------------------------------------------------------
+def test_t3_decode_query_sees_all_keys_golden():
+    g = json.load(open(GOLDEN))["decode_query_sees_all_keys"]
+    d = 8
+    for n_cached in g["cached_tokens_N"]:
+        nk = n_cached + 1
+        q, k, v = rnd(7, 2, 1, 3, d), rnd(8, 2, nk, 3, d), rnd(9, 2, nk, 3, d)
+        oc, lc = O.attention_ref(q, k, v, 0.35, causal=True)
+        on, ln_ = O.attention_ref(q, k, v, 0.35, causal=False)
+        assert np.array_equal(oc, on) and np.array_equal(lc, ln_)
+        ok = O.allowed_mask(1, nk, np.arange(1), True, -1, -1)
+        assert ok.sum() == nk
+
+
+# T5 -----------------------------------------------------------------------
+@pytest.mark.parametrize("nq,nk", [(5, 5), (4, 9)])
+def test_t5_zero_window_selects_diagonal(nq, nk):
+    d = 6
+    q, k, v = rnd(10, 1, nq, 1, d), rnd(11, 1, nk, 1, d), rnd(12, 1, nk, 1, d)
+    o, lse = O.attention_ref(q, k, v, 0.4, False, 0, 0)
+    off = nk - nq
+    for i in range(nq):
+        assert np.array_equal(o[0, i, 0], v[0, i + off, 0])
+        s_diag = 0.4 * float(np.dot(q[0, i, 0], k[0, i + off, 0]))
+        assert abs(lse[0, 0, i] - s_diag) < 1e-12
+
+
+def test_t5_wide_window_equals_causal():
+    d, nq, nk = 5, 6, 10
+    q, k, v = rnd(13, 1, nq, 2, d), rnd(14, 1, nk, 2, d), rnd(15, 1, nk, 2, d)
+    a = O.attention_ref(q, k, v, 0.5, True, nk, 0)
+    b = O.attention_ref(q, k, v, 0.5, True, -1, -1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# T6 -----------------------------------------------------------------------
+@pytest.mark.parametrize("softcap", [0.0, 0.5])
+def test_t6_alibi_zero_query_geometric_closed_form(softcap):
+    """Q = 0 and causal: the weights are r^k with r = e^-slope over distances k = 0..n-1.
+
+    With softcap on, Q = 0 still gives capped score 0, so the closed form must hold
+    unchanged: this fails if the cap were applied after the bias.
+    """
+    nq, nk, d = 4, 9, 3
+    slopes = np.array([0.5, 0.125])
+    q = np.zeros((1, nq, 2, d))
+    k, v = rnd(16, 1, nk, 2, d), rnd(17, 1, nk, 2, d)
+    o, lse = O.attention_ref(q, k, v, 1.0, True, alibi_slopes=slopes, softcap=softcap)
+    off = nk - nq
+    for h in range(2):
+        r = math.exp(-slopes[h])
+        for i in range(nq):
+            n = i + off + 1
+            assert abs(lse[0, h, i] - math.log((1 - r ** n) / (1 - r))) < 1e-12
+            w = np.array([r ** kk for kk in range(n)])
+            want = sum(w[kk] * v[0, i + off - kk, h] for kk in range(n)) / w.sum()
+            np.testing.assert_allclose(o[0, i, h], want, atol=1e-12)
+
+
+def test_t6_alibi_symmetric_when_not_causal():
+    nq = nk = 5
+    q = np.zeros((1, nq, 1, 2))
+    k, v = rnd(18, 1, nk, 1, 2), rnd(19, 1, nk, 1, 2)
+    slope = 0.3
+    _, lse = O.attention_ref(q, k, v, 1.0, False, alibi_slopes=[slope])
+    for i in range(nq):
+        want = math.log(sum(math.exp(-slope * abs(i - j)) for j in range(nk)))
+        assert abs(lse[0, 0, i] - want) < 1e-12
+
+
+# T7 -----------------------------------------------------------------------
+def test_t7_zero_slopes_equal_no_alibi():
+    q, k, v = rnd(20, 2, 5, 3, 4), rnd(21, 2, 7, 3, 4), rnd(22, 2, 7, 3, 4)
+    a = O.attention_ref(q, k, v, 0.5, True, alibi_slopes=np.zeros(3))
+    b = O.attention_ref(q, k, v, 0.5, True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# T8 -----------------------------------------------------------------------
+def test_t8_softcap_bounds_limit_and_value():
+    nq, nk, d = 6, 8, 4
+    q, k = rnd(23, nq, d) * 1.5, rnd(24, nk, d) * 1.5
+    rows = np.arange(nq)
+    cap = 3.0
+    s = O.scores_ref(q, k, rows, nq, 1.0, softcap=cap)
+    assert np.all(np.abs(s) < cap)
+    raw = O.scores_ref(q, k, rows, nq, 1.0)
+    # order preserved, odd symmetry
+    assert np.all(np.argsort(s, axis=1) == np.argsort(raw, axis=1))
+    s_neg = O.scores_ref(-q, k, rows, nq, 1.0, softcap=cap)
+    np.testing.assert_allclose(s_neg, -s, atol=1e-15)
+    # huge cap -> no cap
+    s_big = O.scores_ref(q, k, rows, nq, 1.0, softcap=1e12)
+    np.testing.assert_allclose(s_big, raw, rtol=0, atol=1e-12)
+    # a scaled score equal to the cap maps to cap * tanh(1); tanh(1) = 0.76159415595576488812 (tables)
+    one = O.scores_ref(np.array([[2.0]]), np.array([[3.0]]), np.arange(1), 1, 0.5, softcap=3.0)
+    assert abs(one[0, 0] - 3.0 * 0.76159415595576488812) < 1e-14
+    # small-score regime matches the series s - s^3 / (3 cap^2) to O(s^5)
+    tiny = O.scores_ref(np.array([[1e-3]]), np.array([[1.0]]), np.arange(1), 1, 1.0, softcap=2.0)
+    assert abs(tiny[0, 0] - (1e-3 - 1e-9 / 12.0)) < 1e-16
+
+
+def test_t8_softcap_scale_applied_before_cap():
+    """Scaling is inside the cap: cap(scale*qk) differs from scale*cap(qk)."""
+    q, k = np.array([[4.0]]), np.array([[1.0]])
+    s = O.scores_ref(q, k, np.arange(1), 1, 0.25, softcap=1.0)
+    assert abs(s[0, 0] - 0.76159415595576488812) < 1e-14
+
+
+# T9 -----------------------------------------------------------------------
+def online_softmax_tiled(q, k, v, rows, nq, scale, causal, wl, wr, slope, cap, bm, bn):
+    """Independent tiled streaming softmax (running max / running sum), fp64."""
+    nk, d = k.shape[0], v.shape[1]
+    off = nk - nq
+    o_all = np.zeros((len(rows), d))
+    lse_all = np.zeros(len(rows))
+    for r0 in range(0, len(rows), bm):
+        rr = rows[r0:r0 + bm]
+        m = np.full(len(rr), -np.inf)
+        l = np.zeros(len(rr))
+        acc = np.zeros((len(rr), d))
+        for j0 in range(0, nk, bn):
+            jj = np.arange(j0, min(nk, j0 + bn))
+            s = scale * (q[rr] @ k[jj].T)
+            if cap > 0:
+                s = cap * np.tanh(s / cap)
+            for a, i in enumerate(rr):
+                for b, j in enumerate(jj):
+                    ip = i + off
+                    if slope is not None:
+                        s[a, b] -= slope * abs(ip - j)
+                    bad = (causal and j > ip) or (wl >= 0 and j < ip - wl) or (wr >= 0 and j > ip + wr)
+                    if bad:
+                        s[a, b] = -np.inf
+            m_new = np.maximum(m, s.max(axis=1))
+            base = np.where(np.isfinite(m_new), m_new, 0.0)
+            alpha = np.where(np.isfinite(m), np.exp(m - base), 0.0)
+            p = np.exp(s - base[:, None])
+            l = alpha * l + p.sum(axis=1)
+            acc = alpha[:, None] * acc + p @ v[jj]
+            m = m_new
+        for a in range(len(rr)):
+            if l[a] > 0:
+                o_all[r0 + a] = acc[a] / l[a]
+                lse_all[r0 + a] = m[a] + math.log(l[a])
+            else:
+                lse_all[r0 + a] = -np.inf
+    return o_all, lse_all
+
+
+@pytest.mark.parametrize("nq,nk", [(1, 1), (3, 2), (2, 9), (9, 9), (5, 17), (17, 5), (33, 33)])
+def test_t9_tiled_online_softmax_equals_materialised(nq, nk):
+    d = 4
+    q, k, v = rnd(25, nq, d), rnd(26, nk, d), rnd(27, nk, d)
+    rows = np.arange(nq)
+    for (causal, wl, wr), slope, cap in itertools.product(MASKS, [None, 0.3], [0.0, 1.5]):
+        want_o, want_l = O.attention_bh(q, k, v, rows, nq, 0.6, causal, wl, wr, slope, cap)
+        for bm, bn in [(2, 3), (4, 5)]:
+            got_o, got_l = online_softmax_tiled(q, k, v, rows, nq, 0.6, causal, wl, wr, slope, cap, bm, bn)
+            np.testing.assert_allclose(got_o, want_o, atol=1e-12)
+            fin = np.isfinite(want_l)
+            assert np.array_equal(fin, np.isfinite(got_l))
+            np.testing.assert_allclose(got_l[fin], want_l[fin], atol=1e-12)
+
+
+# T10 ----------------------------------------------------------------------
+@pytest.mark.parametrize("num_splits,page", [(1, 1), (2, 1), (3, 2), (4, 4), (7, 1), (16, 2)])
+@pytest.mark.parametrize("causal,wl,wr", [(False, -1, -1), (True, -1, -1), (True, 3, 0)])
+def test_t10_combine_of_splits_equals_unsplit(num_splits, page, causal, wl, wr):
+    B, nq, nk, H, d = 2, 3, 13, 2, 5
+    q, k, v = rnd(28, B, nq, H, d), rnd(29, B, nk, H, d), rnd(30, B, nk, H, d)
+    slopes = np.array([0.2, 0.05])
+    op, lp = O.splitkv_ref(q, k, v, num_splits, page, 0.45, causal, wl, wr, slopes, 4.0)
+    oc, lc = O.combine_ref(op, lp)
+    ou, lu = O.attention_ref(q, k, v, 0.45, causal, wl, wr, slopes, 4.0)
+    np.testing.assert_allclose(oc, np.transpose(ou, (0, 2, 1, 3)), atol=1e-12)
+    np.testing.assert_allclose(lc, lu, atol=1e-12)
+
+
+def test_t10_combine_with_empty_splits_and_all_empty():
+    o = np.array([[1.0, 2.0], [3.0, 4.0], [9.0, 9.0]])
+    lse = np.array([math.log(1.0), math.log(3.0), -math.inf])
+    oc, lc = O.combine_ref(o[:, None, :], lse[:, None])
+    np.testing.assert_allclose(oc[0], [0.25 * 1 + 0.75 * 3, 0.25 * 2 + 0.75 * 4], atol=1e-15)
+    assert abs(lc[0] - math.log(4.0)) < 1e-15
+    oe, le = O.combine_ref(np.ones((3, 1, 2)), np.full((3, 1), -math.inf))
+    assert np.all(oe == 0) and le[0] == -math.inf
+
+
+def test_split_bounds_golden_and_rules():
+    g = json.load(open(GOLDEN))["split_two_blocks_of_1000"]
+    assert O.split_bounds(g["seqlen_k"], g["num_splits"], 1) == [tuple(b) for b in g["bounds"]]
+    # chunks cover [0, nk) contiguously, never cut a page, trailing ones may be empty
+    for nk, s, ps in [(32768, 16, 256), (1000, 3, 64), (5, 8, 1), (300, 4, 256)]:
+        b = O.split_bounds(nk, s, ps)
+        assert b[0][0] == 0 and b[-1][1] == nk
+        for (lo, hi), (lo2, _) in zip(b, b[1:]):
+            assert hi == lo2 and lo <= hi
+        for lo, _ in b:
+            assert lo % ps == 0 or lo == nk
+    assert O.split_bounds(32768, 16, 256) == [(2048 * s, 2048 * (s + 1)) for s in range(16)]
+
+
+# T11 ----------------------------------------------------------------------
+@pytest.mark.parametrize("causal,wl,wr", [m for m in MASKS if m != (True, 0, -1)])
+@pytest.mark.parametrize("use_alibi", [False, True])
+def test_t11_matches_torch_sdpa_fp64(causal, wl, wr, use_alibi):
+    """torch's CPU scaled_dot_product_attention with an explicit float mask (fp64)."""
+    B, nq, nk, H, d = 2, 6, 9, 3, 8
+    q, k, v = rnd(31, B, nq, H, d), rnd(32, B, nk, H, d), rnd(33, B, nk, H, d)
+    slopes = np.array([0.5, 0.25, 0.125]) if use_alibi else None
+    scale = 0.3
+    off = nk - nq
+    bias = np.zeros((H, nq, nk))
+    for h in range(H):
+        for i in range(nq):
+            for j in range(nk):
+                ip = i + off
+                if (causal and j > ip) or (wl >= 0 and j < ip - wl) or (wr >= 0 and j > ip + wr):
+                    bias[h, i, j] = -np.inf
+                elif use_alibi:
+                    bias[h, i, j] = -slopes[h] * abs(ip - j)
+    nonempty = np.isfinite(bias).any(axis=2)  # [H, nq]
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=torch.from_numpy(bias)[None], scale=scale).permute(0, 2, 1, 3).numpy()
+    got, _ = O.attention_ref(q, k, v, scale, causal, wl, wr, slopes)
+    for h in range(H):
+        for i in range(nq):
+            if nonempty[h, i]:
+                np.testing.assert_allclose(got[:, i, h], want[:, i, h], atol=1e-12)
+
+
+# T12 ----------------------------------------------------------------------
+def test_t12_paged_gather_matches_loop_and_identity():
+    ps, H, d, B, nk = 4, 2, 3, 2, 10
+    npages = 8
+    pool = rnd(34, npages, ps, H, d)
+    bt = np.array([[5, 1, 7], [0, 6, 2]], dtype=np.int32)
+    for b in range(B):
+        g = O.paged_gather_ref(pool, bt, b, nk)
+        loop = np.stack([pool[bt[b][t // ps], t % ps] for t in range(nk)])
+        assert np.array_equal(g, loop)
+    contig = rnd(35, B, 12, H, d)
+    pool_id = contig.reshape(B * 3, ps, H, d)
+    bt_id = np.arange(B * 3, dtype=np.int32).reshape(B, 3)
+    for b in range(B):
+        assert np.array_equal(O.paged_gather_ref(pool_id, bt_id, b, 12), contig[b])
+
+
+def test_t12_workload_scatter_roundtrip():
+    """The workload's page placement and the oracle's gather are inverses."""
+    w = W.Workload(0, "t", B=2, H=3, Nq=1, Nk=37, d=4, dtype="bf16", paged=True,
+                   page_size=8, pool_factor=1.5, seed=9)
+    q, kc, vc, bt = W.gen_paged(w)
+    for b in range(w.B):
+        g = O.paged_gather_ref(kc, bt, b, w.Nk)
+        for h in range(w.H):
+            assert np.array_equal(g[:, h, :], W.gen_slice(w.seed, W.TENSOR_K, b, h, w.Nk, w.d, 1.0, "bf16"))
+
+
+# T13 ----------------------------------------------------------------------
+def test_t13_key_permutation_invariance():
+    q, k, v = rnd(36, 1, 4, 2, 5), rnd(37, 1, 11, 2, 5), rnd(38, 1, 11, 2, 5)
+    perm = np.random.default_rng(39).permutation(11)
+    a = O.attention_ref(q, k, v, 0.5, softcap=2.0)
+    b = O.attention_ref(q, k[:, perm], v[:, perm], 0.5, softcap=2.0)
+    np.testing.assert_allclose(a[0], b[0], atol=1e-12)
+    np.testing.assert_allclose(a[1], b[1], atol=1e-12)
+
+
+# T14 ----------------------------------------------------------------------
+def test_t14_single_key():
+    q, k, v = rnd(40, 1, 3, 1, 4), rnd(41, 1, 1, 1, 4), rnd(42, 1, 1, 1, 4)
+    o, lse = O.attention_ref(q, k, v, 0.9)
+    for i in range(3):
+        assert np.array_equal(o[0, i, 0], v[0, 0, 0])
+        assert abs(lse[0, 0, i] - 0.9 * float(q[0, i, 0] @ k[0, 0, 0])) < 1e-12
+
+
+# T15 ----------------------------------------------------------------------
+def test_t15_generator_reproducible_and_bf16_rounding():
+    a = W.gen_slice(3, 1, 0, 2, 16, 8, 1.0, "bf16")
+    b = W.gen_slice(3, 1, 0, 2, 16, 8, 1.0, "bf16")
+    c = W.gen_slice(3, 1, 0, 3, 16, 8, 1.0, "bf16")
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+    # rounding matches torch's float32 -> bfloat16 conversion (nearest, ties to even)
+    x = np.random.default_rng(0).standard_normal(4096).astype(np.float32) * 7
+    x[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0]  # exact ties
+    tb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(W.f32_to_bf16_bits(x), tb)
+    assert np.array_equal(W.bf16_bits_to_f32(tb), torch.from_numpy(tb.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+def test_golden_scores_at_4096_tokens():
+    g = json.load(open(GOLDEN))["scores_at_4096_tokens"]
+    n = g["seqlen"]
+    s = O.scores_ref(np.ones((n, 1)), np.ones((n, 1)), np.arange(n), n, 1.0)
+    assert s.size == n * n and s.size > g["more_than"]
