@@ -1,0 +1,203 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic input:
+  1. fa_fwd on the GPT-style causal prefill (B=4, H=16, Nq=Nk=2048, d=128, bf16),
+  2. fa_fwd_splitkv + fa_splitkv_combine on the paged decode
+     (B=8, H=32, Nq=1, Nk=32768, d=128, bf16, 256-token pages, 16 splits).
+`value` is the prefill's algorithmic TFLOP/s (4*B*H*d*allowed pairs over the
+prefill launch time); the decode's algorithmic GB/s is reported beside it.
+Inputs are resident in device memory before the timed region starts.
+
+Prints ONE JSON line on stdout. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def allowed_pairs(nq, nk, causal, wl, wr):
+    """Number of (query, key) pairs the mask keeps, summed over rows."""
+    off = nk - nq
+    i = np.arange(nq, dtype=np.int64) + off
+    lo = np.zeros(nq, dtype=np.int64)
+    hi = np.full(nq, nk - 1, dtype=np.int64)
+    if causal:
+        hi = np.minimum(hi, i)
+    if wl >= 0:
+        lo = np.maximum(lo, i - wl)
+    if wr >= 0:
+        hi = np.minimum(hi, i + wr)
+    return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the kernels run on one device's share of the work).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_tiled_attention_05_amd as fa
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fa.load_library()
+
+    def up(x, dtype):
+        x = np.ascontiguousarray(x)
+        if dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    # ---- prefill inputs
+    wp = W.WORKLOADS[2]
+    log(f"generating {wp.name}")
+    q, k, v = W.gen_qkv(wp)
+    pq, pk, pv = up(q, wp.dtype), up(k, wp.dtype), up(v, wp.dtype)
+    del q, k, v
+    po = torch.empty((wp.B, wp.Nq, wp.H, wp.d), dtype=torch.float32, device=dev)
+    plse = torch.empty((wp.B, wp.H, wp.Nq), dtype=torch.float32, device=dev)
+    pairs = allowed_pairs(wp.Nq, wp.Nk, True, -1, -1)
+    prefill_flops = 4.0 * wp.B * wp.H * wp.d * pairs
+
+    # ---- decode inputs
+    wd = W.WORKLOADS[4]
+    log(f"generating {wd.name}")
+    dq_np, kc, vc, bt = W.gen_paged(wd)
+    dq, dk, dv = up(dq_np, wd.dtype), up(kc, wd.dtype), up(vc, wd.dtype)
+    del kc, vc
+    dbt = torch.from_numpy(bt).to(dev)
+    S = wd.num_splits
+    o_part = torch.empty((S, wd.B, wd.H, wd.Nq, wd.d), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((S, wd.B, wd.H, wd.Nq), dtype=torch.float32, device=dev)
+    do = torch.empty((wd.B, wd.Nq, wd.H, wd.d), dtype=torch.float32, device=dev)
+    dlse = torch.empty((wd.B, wd.H, wd.Nq), dtype=torch.float32, device=dev)
+    kv_bytes = 2 * wd.B * wd.H * wd.Nk * wd.d * 2
+    part_bytes = S * wd.B * wd.H * wd.Nq * (wd.d + 1) * 4
+    split_bytes = kv_bytes + dq.numel() * 2 + bt.size * 4 + part_bytes
+    combine_bytes = part_bytes + do.numel() * 4 + dlse.numel() * 4
+    decode_bytes = split_bytes + combine_bytes
+
+    stream = torch.cuda.current_stream()
+
+    def check(st, where):
+        if st != 0:
+            raise fa.FaError(st, where)
+
+    def prefill():
+        check(fa.fa_fwd(pq, pk, pv, po, plse, wp.B, wp.H, wp.Nq, wp.Nk, wp.d, wp.scale,
+                        True, -1, -1, None, 0.0, stream), "fa_fwd")
+
+    def split_pass():
+        check(fa.fa_fwd_splitkv(dq, dk, dv, dbt, dbt.shape[1], wd.page_size, o_part, lse_part, S,
+                                wd.B, wd.H, wd.Nq, wd.Nk, wd.d, wd.scale, True, -1, -1, None,
+                                0.0, stream), "fa_fwd_splitkv")
+
+    def combine_pass():
+        check(fa.fa_splitkv_combine(o_part, lse_part, S, wd.B, wd.H, wd.Nq, wd.d, do, dlse,
+                                    stream), "fa_splitkv_combine")
+
+    log("warmup")
+    for _ in range(args.warmup):
+        prefill()
+        split_pass()
+        combine_pass()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        e = ev[s]
+        e[0].record(stream)
+        prefill()
+        e[1].record(stream)
+        split_pass()
+        e[2].record(stream)
+        combine_pass()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_prefill = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    t_split = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    t_comb = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+
+    pre_tflops = prefill_flops / t_prefill.mean() / 1e12
+    dec_time = (t_split + t_comb).mean()
+    dec_gbs = decode_bytes / dec_time / 1e9
+    split_gbs = split_bytes / t_split.mean() / 1e9
+    assert torch.isfinite(po).all() and torch.isfinite(do).all()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        from threadpoolctl import threadpool_info
+        log("cpu baseline: oracle on the full causal-prefill batch")
+        q, k, v = W.gen_qkv(wp)
+        qf, kf, vf = (W.to_float(x, wp.dtype) for x in (q, k, v))
+        t = time.perf_counter()
+        O.attention_ref(qf, kf, vf, wp.scale, True)
+        dt = time.perf_counter() - t
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        cpu = {"value": round(prefill_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"whole causal-prefill batch B4 H16 N2048 d128 (fp64 numpy, {dt:.1f} s, "
+                         f"host cpus {os.cpu_count()})"}
+
+    line = {
+        "metric": "attn fwd TFLOP/s (% bf16 MFMA peak); decode split-KV GB/s (% HBM peak)",
+        "value": round(pre_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 inputs, seeded block-table permutation)",
+        "config": {"workload": "gpt_causal_prefill B4 H16 Nq=Nk=2048 d128 bf16 causal "
+                               "+ paged_splitkv_decode B8 H32 Nq1 Nk32768 d128 page256 S16",
+                   "prefill_gflop": round(prefill_flops / 1e9, 4),
+                   "decode_gbytes": round(decode_bytes / 1e9, 5)},
+        "prefill": {"ms": round(t_prefill.mean() * 1e3, 5), "ms_min": round(t_prefill.min() * 1e3, 5),
+                    "tflops": round(pre_tflops, 3), "pct_peak": round(100 * pre_tflops / PEAK_BF16_TFLOPS, 2)},
+        "decode": {"ms": round(dec_time * 1e3, 5), "split_ms": round(t_split.mean() * 1e3, 5),
+                   "combine_ms": round(t_comb.mean() * 1e3, 5), "gbs": round(dec_gbs, 2),
+                   "pct_peak": round(100 * dec_gbs / PEAK_HBM_GBS, 2),
+                   "roofline": {"bound": "hbm", "achieved": round(split_gbs, 2), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
+                                "traffic": None}},
+        "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

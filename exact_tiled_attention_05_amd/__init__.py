@@ -1,0 +1,212 @@
+"""Python binding of libfa, the gfx950 exact tiled attention library.
+
+The functions named like the C ABI (``fa_fwd``, ``fa_fwd_splitkv``,
+``fa_splitkv_combine``, ``fa_status_string``, ``fa_split_chunk_len``) only
+marshal arguments: torch tensors become device pointers, the current torch
+stream becomes the HIP stream, and every step of the computation runs in the
+library's kernels. ``attention``, ``attention_paged_splitkv``, ``combine`` and
+``decode_paged`` add output allocation (torch.empty) on top of them.
+
+The library must be built (``python -m exact_tiled_attention_05_amd.build``);
+importing works without it, but every call raises if libfa.so is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "FA_FP32", "FA_BF16", "FaError", "library_path", "load_library",
+    "fa_fwd", "fa_fwd_splitkv", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len",
+    "attention", "attention_paged_splitkv", "combine", "decode_paged",
+]
+
+FA_FP32, FA_BF16 = 0, 1
+FA_OK = 0
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+_lib = None
+
+EXPORTED = ("fa_fwd", "fa_fwd_splitkv", "fa_splitkv_combine", "fa_status_string",
+            "fa_split_chunk_len")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {fa_status_string(status)}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libfa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m exact_tiled_attention_05_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.argtypes = [vp, vp, vp, i, vp, i, vp, i, i, i, i, i, f, i, i, i, vp, f, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, i, vp, i, i, vp, vp, i, i, i, i, i, i, f, i, i, i,
+                                   vp, f, vp]
+    lib.fa_fwd_splitkv.restype = i
+    lib.fa_splitkv_combine.argtypes = [vp, vp, i, i, i, i, i, vp, i, vp, vp]
+    lib.fa_splitkv_combine.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_split_chunk_len.argtypes = [i, i, i]
+    lib.fa_split_chunk_len.restype = i
+    _lib = lib
+    return lib
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != FA_OK:
+        raise FaError(status, where)
+
+
+# --------------------------------------------------------------------------
+# C ABI, same names
+# --------------------------------------------------------------------------
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_split_chunk_len(seqlen_k: int, num_splits: int, page_size: int) -> int:
+    return load_library().fa_split_chunk_len(int(seqlen_k), int(num_splits), int(page_size))
+
+
+def fa_fwd(q, k, v, o, lse, batch, heads, seqlen_q, seqlen_k, head_dim, softmax_scale,
+           causal=False, window_left=-1, window_right=-1, alibi_slopes=None, softcap=0.0,
+           stream=None) -> int:
+    """Call fa_fwd on caller-allocated tensors; returns the status code."""
+    return load_library().fa_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(o), _dtype_code(o), _ptr(lse),
+        int(batch), int(heads), int(seqlen_q), int(seqlen_k), int(head_dim),
+        float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
+        _ptr(alibi_slopes), float(softcap), _stream(stream))
+
+
+def fa_fwd_splitkv(q, k_cache, v_cache, block_table, max_pages_per_seq, page_size, o_part,
+                   lse_part, num_splits, batch, heads, seqlen_q, seqlen_k, head_dim,
+                   softmax_scale, causal=False, window_left=-1, window_right=-1,
+                   alibi_slopes=None, softcap=0.0, stream=None) -> int:
+    """Call fa_fwd_splitkv on caller-allocated tensors; returns the status code."""
+    return load_library().fa_fwd_splitkv(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q), _ptr(block_table),
+        int(max_pages_per_seq), int(page_size), _ptr(o_part), _ptr(lse_part), int(num_splits),
+        int(batch), int(heads), int(seqlen_q), int(seqlen_k), int(head_dim),
+        float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
+        _ptr(alibi_slopes), float(softcap), _stream(stream))
+
+
+def fa_splitkv_combine(o_part, lse_part, num_splits, batch, heads, seqlen_q, head_dim, o, lse,
+                       stream=None) -> int:
+    """Call fa_splitkv_combine on caller-allocated tensors; returns the status code."""
+    return load_library().fa_splitkv_combine(
+        _ptr(o_part), _ptr(lse_part), int(num_splits), int(batch), int(heads), int(seqlen_q),
+        int(head_dim), _ptr(o), _dtype_code(o), _ptr(lse), _stream(stream))
+
+
+# --------------------------------------------------------------------------
+# Allocating conveniences
+# --------------------------------------------------------------------------
+def _same_dtype(*ts):
+    d = ts[0].dtype
+    for t in ts[1:]:
+        if t.dtype != d:
+            raise TypeError("q, k and v must share one dtype")
+
+
+def attention(q, k, v, softmax_scale=None, causal=False, window_left=-1, window_right=-1,
+              alibi_slopes=None, softcap=0.0, out_dtype=torch.float32, stream=None):
+    """O [B, Nq, H, d] (out_dtype) and LSE [B, H, Nq] fp32 for q [B,Nq,H,d], k/v [B,Nk,H,d]."""
+    _same_dtype(q, k, v)
+    B, nq, H, d = q.shape
+    nk = k.shape[1]
+    if tuple(k.shape) != (B, nk, H, d) or tuple(v.shape) != (B, nk, H, d):
+        raise ValueError("k and v must be [B, Nk, H, d] matching q")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, nq, H, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, H, nq), dtype=torch.float32, device=q.device)
+    _check(fa_fwd(q, k, v, o, lse, B, H, nq, nk, d, softmax_scale, causal, window_left,
+                  window_right, alibi_slopes, softcap, stream), "fa_fwd")
+    return o, lse
+
+
+def attention_paged_splitkv(q, k_cache, v_cache, block_table, seqlen_k, num_splits,
+                            softmax_scale=None, causal=False, window_left=-1, window_right=-1,
+                            alibi_slopes=None, softcap=0.0, stream=None):
+    """Split partials o_part [S,B,H,Nq,d] and lse_part [S,B,H,Nq] over a paged cache."""
+    _same_dtype(q, k_cache, v_cache)
+    B, nq, H, d = q.shape
+    _, page_size, Hc, dc = k_cache.shape
+    if (Hc, dc) != (H, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache must be [num_pages, page_size, H, d] matching q")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages_per_seq]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    o_part = torch.empty((num_splits, B, H, nq, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((num_splits, B, H, nq), dtype=torch.float32, device=q.device)
+    _check(fa_fwd_splitkv(q, k_cache, v_cache, block_table, block_table.shape[1], page_size,
+                          o_part, lse_part, num_splits, B, H, nq, seqlen_k, d, softmax_scale,
+                          causal, window_left, window_right, alibi_slopes, softcap, stream),
+           "fa_fwd_splitkv")
+    return o_part, lse_part
+
+
+def combine(o_part, lse_part, out_dtype=torch.float32, stream=None):
+    """Merge split partials into O [B, Nq, H, d] and LSE [B, H, Nq]."""
+    S, B, H, nq, d = o_part.shape
+    o = torch.empty((B, nq, H, d), dtype=out_dtype, device=o_part.device)
+    lse = torch.empty((B, H, nq), dtype=torch.float32, device=o_part.device)
+    _check(fa_splitkv_combine(o_part, lse_part, S, B, H, nq, d, o, lse, stream),
+           "fa_splitkv_combine")
+    return o, lse
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seqlen_k, num_splits, out_dtype=torch.float32,
+                 **kw):
+    """Split-KV pass followed by the combine kernel, both on the current stream."""
+    o_part, lse_part = attention_paged_splitkv(q, k_cache, v_cache, block_table, seqlen_k,
+                                               num_splits, **kw)
+    return combine(o_part, lse_part, out_dtype=out_dtype, stream=kw.get("stream"))

@@ -1,0 +1,202 @@
+// C ABI of libfa: argument validation (host only, before any HIP call) and
+// dispatch to the gfx950 kernel instantiations. See include/fa.h for the
+// contract of each entry point.
+#include "fa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_params.h"
+
+namespace {
+
+constexpr int kMaxSeq = 1 << 28;
+constexpr int64_t kMaxGroups = (int64_t(1) << 31) - 1;
+
+using Launcher = int (*)(const fa::FwdParams&, void*);
+
+template <bool PAGED>
+Launcher pick(int in_dtype, int head_dim, bool softcap, bool alibi) {
+#define FA_PICK(FN, D)                                                         \
+  if (softcap && alibi) return &fa::FN<D, true, true, PAGED>;                  \
+  if (softcap) return &fa::FN<D, true, false, PAGED>;                          \
+  if (alibi) return &fa::FN<D, false, true, PAGED>;                            \
+  return &fa::FN<D, false, false, PAGED>;
+  if (in_dtype == FA_BF16) {
+    if (head_dim == 64) { FA_PICK(launch_fwd_bf16, 64) }
+    FA_PICK(launch_fwd_bf16, 128)
+  }
+  if (head_dim == 64) { FA_PICK(launch_fwd_f32, 64) }
+  FA_PICK(launch_fwd_f32, 128)
+#undef FA_PICK
+}
+
+int check_sizes(int batch, int heads, int seqlen_q, int seqlen_k) {
+  if (batch <= 0 || heads <= 0 || seqlen_q <= 0 || seqlen_k <= 0) return FA_ERR_SHAPE;
+  if (seqlen_q > kMaxSeq || seqlen_k > kMaxSeq || heads > (1 << 16) || batch > (1 << 24))
+    return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_kind(int in_dtype, int head_dim) {
+  if (in_dtype != FA_FP32 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int check_mask_and_values(int causal, int window_left, int window_right, float scale,
+                          float softcap) {
+  if (window_left < -1 || window_right < -1) return FA_ERR_MASK;
+  if (causal && window_right > 0) return FA_ERR_MASK;
+  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_VALUE;
+  if (!(softcap >= 0.0f) || !isfinite(softcap)) return FA_ERR_VALUE;
+  return FA_OK;
+}
+
+// Fill the fields common to both forward entry points. A window wider than
+// both sequences is no constraint, so it is folded to -1 (keeps index
+// arithmetic inside 32 bits); causal is the right window 0.
+void fill_common(fa::FwdParams& p, int batch, int heads, int seqlen_q, int seqlen_k,
+                 float scale, int causal, int window_left, int window_right,
+                 const float* alibi_slopes, float softcap, int tile_rows) {
+  p.B = batch;
+  p.H = heads;
+  p.Nq = seqlen_q;
+  p.Nk = seqlen_k;
+  const int span = seqlen_q + seqlen_k;
+  p.window_left = window_left > span ? -1 : window_left;
+  int wr = window_right > span ? -1 : window_right;
+  if (causal) wr = 0;
+  p.window_right = wr;
+  p.alibi = alibi_slopes;
+  const float log2e = 1.4426950408889634f;
+  p.scale_log2 = scale * log2e;
+  p.softcap_log2 = softcap * log2e;
+  p.scale_over_cap2 = softcap > 0.0f ? 2.0f * scale / softcap * log2e : 0.0f;
+  p.num_q_tiles = (seqlen_q + tile_rows - 1) / tile_rows;
+}
+
+int64_t split_len(int seqlen_k, int num_splits, int page_size) {
+  int64_t c = (seqlen_k + (int64_t)num_splits - 1) / num_splits;
+  return (c + page_size - 1) / page_size * page_size;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE:
+      return "bad sizes: every size must be >= 1, seqlens <= 2^28, heads <= 2^16, "
+             "batch <= 2^24, the launch below 2^31 workgroups, and "
+             "max_pages_per_seq * page_size >= seqlen_k";
+    case FA_ERR_UNSUPPORTED: return "unsupported dtype or head_dim (head_dim 64 or 128; FP32 or BF16)";
+    case FA_ERR_MASK: return "bad mask: windows must be >= -1 and causal needs window_right <= 0";
+    case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case FA_ERR_VALUE: return "bad value: softmax_scale must be finite and > 0, softcap finite and >= 0";
+    default: return "unknown status";
+  }
+}
+
+int fa_split_chunk_len(int seqlen_k, int num_splits, int page_size) {
+  if (seqlen_k <= 0 || num_splits <= 0 || page_size <= 0) return -1;
+  const int64_t c = split_len(seqlen_k, num_splits, page_size);
+  return c > kMaxSeq ? -1 : (int)c;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, int in_dtype, void* o, int o_dtype,
+           float* lse, int batch, int heads, int seqlen_q, int seqlen_k, int head_dim,
+           float softmax_scale, int causal, int window_left, int window_right,
+           const float* alibi_slopes, float softcap, void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
+  if (st) return st;
+  if ((st = check_kind(in_dtype, head_dim))) return st;
+  if (o_dtype != FA_FP32 && o_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
+    return st;
+
+  fa::FwdParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.o_bf16 = o_dtype == FA_BF16;
+  p.num_splits = 1;
+  const int tile = in_dtype == FA_BF16 ? fa::BF16_BM : fa::F32_BM;
+  fill_common(p, batch, heads, seqlen_q, seqlen_k, softmax_scale, causal, window_left,
+              window_right, alibi_slopes, softcap, tile);
+  p.split_len = seqlen_k;
+  if ((int64_t)p.num_q_tiles * heads * batch > kMaxGroups) return FA_ERR_SHAPE;
+
+  Launcher fn = pick<false>(in_dtype, head_dim, softcap > 0.0f, alibi_slopes != nullptr);
+  return fn(p, stream) ? FA_ERR_HIP : FA_OK;
+}
+
+int fa_fwd_splitkv(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
+                   const int* block_table, int max_pages_per_seq, int page_size,
+                   float* o_part, float* lse_part, int num_splits, int batch, int heads,
+                   int seqlen_q, int seqlen_k, int head_dim, float softmax_scale, int causal,
+                   int window_left, int window_right, const float* alibi_slopes, float softcap,
+                   void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !o_part || !lse_part) return FA_ERR_NULL;
+  int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
+  if (st) return st;
+  if (num_splits <= 0 || num_splits > (1 << 16) || max_pages_per_seq <= 0 || page_size <= 0)
+    return FA_ERR_SHAPE;
+  if ((int64_t)max_pages_per_seq * page_size < seqlen_k) return FA_ERR_SHAPE;
+  if ((st = check_kind(in_dtype, head_dim))) return st;
+  if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
+    return st;
+
+  fa::FwdParams p = {};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.block_table = block_table;
+  p.max_pages = max_pages_per_seq;
+  p.page_size = page_size;
+  p.num_splits = num_splits;
+  const int tile = in_dtype == FA_BF16 ? fa::BF16_BM : fa::F32_BM;
+  fill_common(p, batch, heads, seqlen_q, seqlen_k, softmax_scale, causal, window_left,
+              window_right, alibi_slopes, softcap, tile);
+  const int64_t c = split_len(seqlen_k, num_splits, page_size);
+  if (c > kMaxSeq) return FA_ERR_SHAPE;
+  p.split_len = (int)c;
+  if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
+
+  Launcher fn = pick<true>(in_dtype, head_dim, softcap > 0.0f, alibi_slopes != nullptr);
+  return fn(p, stream) ? FA_ERR_HIP : FA_OK;
+}
+
+int fa_splitkv_combine(const float* o_part, const float* lse_part, int num_splits, int batch,
+                       int heads, int seqlen_q, int head_dim, void* o, int o_dtype, float* lse,
+                       void* stream) {
+  if (!o_part || !lse_part || !o) return FA_ERR_NULL;
+  if (num_splits <= 0 || num_splits > (1 << 16)) return FA_ERR_SHAPE;
+  int st = check_sizes(batch, heads, seqlen_q, 1);
+  if (st) return st;
+  if (head_dim != 64 && head_dim != 128) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != FA_FP32 && o_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (((int64_t)batch * heads * seqlen_q + 3) / 4 > kMaxGroups) return FA_ERR_SHAPE;
+  fa::CombineParams p = {};
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.o = o;
+  p.lse = lse;
+  p.S = num_splits;
+  p.B = batch;
+  p.H = heads;
+  p.Nq = seqlen_q;
+  p.o_bf16 = o_dtype == FA_BF16;
+  const int rc = head_dim == 64 ? fa::launch_combine<64>(p, stream) : fa::launch_combine<128>(p, stream);
+  return rc ? FA_ERR_HIP : FA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,242 @@
+// Device helpers shared by the gfx950 attention kernels.
+//
+// Register layout used throughout: the score tile is computed transposed,
+// S^T = K Q^T, with the 32x32 MFMA output layout of CDNA: lane l owns output
+// column l % 32 (one query row) and, in its 16 accumulator slots v = 0..15,
+// the rows (keys) 8*(v/4) + 4*(l/32) + (v%4). A query row therefore lives in
+// two lanes (l and l ^ 32), so every softmax reduction is in-lane except one
+// exchange between the two wave halves.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_params.h"
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte chunks addressed by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.
+__device__ __forceinline__ s16x4_t ds_read_tr16(const uint16_t* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(lds_ptr));
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// Lazy running maximum: the exponent base is only moved when a tile's maximum
+// exceeds it by more than this many powers of two, so most tiles skip
+// rescaling the output accumulator. Used where P stays fp32. Where P is rounded
+// to bf16 the base must be the exact running maximum (threshold 0): then the
+// largest probability of a row is exactly 1 and rounds without error, which
+// keeps the bf16 rounding error of O well inside its bound.
+constexpr float kLazyRescaleThreshold = 8.0f;
+
+// Key offset (within a 32-key block) held in accumulator slot v of a lane in half h2.
+__device__ __forceinline__ constexpr int acc_key(int v, int h2) {
+  return 8 * (v >> 2) + 4 * h2 + (v & 3);
+}
+
+// Value of x in lane l ^ 32 (the other half of the wavefront).
+__device__ __forceinline__ float other_half(float x) {
+  return __shfl_xor(x, 32);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Keys that rows [r0, r1) may see, as the union [lo, hi) and the
+// intersection [flo, fhi) over the rows (bottom-right aligned: i' = i + off).
+struct KeyBounds {
+  int lo, hi, flo, fhi;
+};
+
+__device__ __forceinline__ KeyBounds key_bounds(int r0, int r1, int off, int slo, int shi,
+                                                int wl, int wr) {
+  KeyBounds kb;
+  kb.lo = slo;
+  kb.hi = shi;
+  kb.flo = slo;
+  kb.fhi = shi;
+  if (wl >= 0) {
+    kb.lo = max(kb.lo, r0 + off - wl);
+    kb.flo = max(kb.flo, r1 - 1 + off - wl);
+  }
+  if (wr >= 0) {
+    kb.hi = min(kb.hi, r1 - 1 + off + wr + 1);
+    kb.fhi = min(kb.fhi, r0 + off + wr + 1);
+  }
+  return kb;
+}
+
+// Score transform for one tile held as NB 32-key blocks of accumulators:
+// scale (log2 units), optional tanh cap, optional ALiBi distance penalty,
+// optional mask to [row_lo, row_hi). Results are log2-domain scores.
+template <int NB, bool SOFTCAP, bool ALIBI>
+__device__ __forceinline__ void transform_scores(float (&t)[NB][16], const FwdParams& p,
+                                                 float slope_log2, float rel_pos,
+                                                 bool need_mask, int key0, int row_lo,
+                                                 int row_hi, int h2) {
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float x = t[j][v];
+      if constexpr (SOFTCAP) {
+        // tanh(y) = 1 - 2 / (exp(2y) + 1), evaluated with exp2 and a reciprocal.
+        const float e = fast_exp2(x * p.scale_over_cap2);
+        x = p.softcap_log2 - 2.0f * p.softcap_log2 * __builtin_amdgcn_rcpf(e + 1.0f);
+      } else {
+        x *= p.scale_log2;
+      }
+      if constexpr (ALIBI) {
+        // rel_pos = (i + off) - (key0 + 4*h2): distance to key = rel_pos - offset.
+        const float dist = rel_pos - (float)(32 * j + 8 * (v >> 2) + (v & 3));
+        x -= slope_log2 * __builtin_fabsf(dist);
+      }
+      t[j][v] = x;
+    }
+  }
+  if (need_mask) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = key0 + 32 * j + acc_key(v, h2);
+        if (key < row_lo || key >= row_hi) t[j][v] = kNegInf;
+      }
+    }
+  }
+}
+
+// Online softmax step for this lane's row: updates the running max (lazily),
+// returns the factor the output accumulator must be multiplied by, and the
+// exponent base to subtract from this tile's scores.
+template <int NB>
+__device__ __forceinline__ float online_max(const float (&t)[NB][16], float& m_run, float& l_run,
+                                            bool& any_rescale, float& base, float threshold) {
+  float mt = kNegInf;
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mt = fmaxf(mt, t[j][v]);
+  mt = fmaxf(mt, other_half(mt));
+  const float m_new = fmaxf(m_run, mt);
+  const bool need = m_new > m_run + threshold;
+  float alpha = 1.0f;
+  if (need) {
+    alpha = fast_exp2(m_run - m_new);  // 0 when m_run is still -inf
+    m_run = m_new;
+  }
+  l_run *= alpha;
+  any_rescale = __any(need);
+  base = (m_run == kNegInf) ? 0.0f : m_run;
+  return alpha;
+}
+
+// Row-sum of 8 bf16 values (the rounded probabilities fed to the PV product).
+__device__ __forceinline__ float sum_bf16x8(bf16x8_t v, float acc) {
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bf16x2_t pr = {v[2 * e], v[2 * e + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ int64_t q_offset(const FwdParams& p, int b, int row, int h, int D) {
+  return (((int64_t)b * p.Nq + row) * p.H + h) * D;
+}
+
+template <bool PAGED>
+__device__ __forceinline__ int64_t kv_offset(const FwdParams& p, int b, int key, int h, int D) {
+  if constexpr (PAGED) {
+    const int page = p.block_table[(int64_t)b * p.max_pages + key / p.page_size];
+    const int slot = key % p.page_size;
+    return (((int64_t)page * p.page_size + slot) * p.H + h) * D;
+  } else {
+    return (((int64_t)b * p.Nk + key) * p.H + h) * D;
+  }
+}
+
+// Split range [slo, shi) of split s (whole sequence when not split).
+__device__ __forceinline__ void split_range(const FwdParams& p, int s, int& slo, int& shi) {
+  const int64_t lo = (int64_t)s * p.split_len;
+  slo = (int)min<int64_t>(p.Nk, lo);
+  shi = (int)min<int64_t>(p.Nk, lo + p.split_len);
+}
+
+// Store one lane's 4 consecutive output values of a row (normalised).
+__device__ __forceinline__ void store_out4(const FwdParams& p, int64_t off, float a, float b,
+                                           float c, float d) {
+  if (p.o_bf16) {
+    f32x4_t x = {a, b, c, d};
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    bf16x4_t y = __builtin_convertvector(x, bf16x4_t);
+    *(bf16x4_t*)((__bf16*)p.o + off) = y;
+  } else {
+    f32x4_t x = {a, b, c, d};
+    *(f32x4_t*)((float*)p.o + off) = x;
+  }
+}
+
+// Output of a workgroup whose rows see no key at all: O = 0, LSE = -inf.
+template <bool PAGED>
+__device__ void write_empty_rows(const FwdParams& p, int b, int h, int s, int q0, int q1, int D,
+                                 int tid, int nthreads) {
+  const int n = (q1 - q0) * D;
+  for (int idx = tid; idx < n; idx += nthreads) {
+    const int row = q0 + idx / D, d = idx % D;
+    if constexpr (PAGED) {
+      p.o_part[((((int64_t)s * p.B + b) * p.H + h) * p.Nq + row) * D + d] = 0.0f;
+    } else {
+      const int64_t o = q_offset(p, b, row, h, D) + d;
+      if (p.o_bf16)
+        ((__bf16*)p.o)[o] = (__bf16)0.0f;
+      else
+        ((float*)p.o)[o] = 0.0f;
+    }
+  }
+  for (int row = q0 + tid; row < q1; row += nthreads) {
+    if constexpr (PAGED) {
+      p.lse_part[(((int64_t)s * p.B + b) * p.H + h) * p.Nq + row] = kNegInf;
+    } else if (p.lse) {
+      p.lse[((int64_t)b * p.H + h) * p.Nq + row] = kNegInf;
+    }
+  }
+}
+
+// Decode the flat workgroup id: head fastest, then batch, then split, then the
+// query tile, heaviest (last) tile first.
+struct WorkItem {
+  int h, b, s, qt;
+};
+template <bool PAGED>
+__device__ __forceinline__ WorkItem decode_work(const FwdParams& p) {
+  WorkItem w;
+  int L = blockIdx.x;
+  w.h = L % p.H;
+  L /= p.H;
+  w.b = L % p.B;
+  L /= p.B;
+  w.s = 0;
+  if constexpr (PAGED) {
+    w.s = L % p.num_splits;
+    L /= p.num_splits;
+  }
+  w.qt = p.num_q_tiles - 1 - L;
+  return w;
+}
+
+}  // namespace fa

@@ -1,0 +1,51 @@
+// Parameters shared by the host dispatcher and the gfx950 kernels.
+#pragma once
+#include <stdint.h>
+
+namespace fa {
+
+// One forward launch: contiguous (fa_fwd) or paged + split (fa_fwd_splitkv).
+struct FwdParams {
+  const void* q;
+  const void* k;            // contiguous [B, Nk, H, D] or page pool [P, ps, H, D]
+  const void* v;
+  void* o;                  // [B, Nq, H, D] (o_bf16 selects bf16 vs fp32)
+  float* lse;               // [B, H, Nq] or nullptr
+  float* o_part;            // [S, B, H, Nq, D] (split launches)
+  float* lse_part;          // [S, B, H, Nq]
+  const int* block_table;   // [B, max_pages] (paged launches)
+  const float* alibi;       // [H] slopes, already multiplied by log2(e); nullptr = off
+  int B, H, Nq, Nk;
+  int max_pages, page_size;
+  int num_splits, split_len;
+  int num_q_tiles;
+  int window_left;          // -1 = unbounded
+  int window_right;         // -1 = unbounded; causal arrives here as 0
+  int o_bf16;
+  float scale_log2;         // softmax_scale * log2(e)
+  float softcap_log2;       // softcap * log2(e) (softcap launches)
+  float scale_over_cap2;    // 2 * softmax_scale / softcap * log2(e)  (tanh via exp2)
+};
+
+struct CombineParams {
+  const float* o_part;
+  const float* lse_part;
+  void* o;
+  float* lse;
+  int S, B, H, Nq;
+  int o_bf16;
+};
+
+// Launchers (defined in the .hip files). Return hipError_t as int.
+template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
+int launch_fwd_bf16(const FwdParams& p, void* stream);
+template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
+int launch_fwd_f32(const FwdParams& p, void* stream);
+template <int D>
+int launch_combine(const CombineParams& p, void* stream);
+
+// Tile geometry the host needs for grid sizing.
+constexpr int BF16_BM = 128;
+constexpr int F32_BM = 32;
+
+}  // namespace fa

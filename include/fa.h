@@ -1,0 +1,141 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) exact tiled attention library (libfa.so).
+ *
+ * What the library computes
+ * -------------------------
+ * Exact attention forward, O = softmax(S) V with S = scale * Q K^T plus the
+ * optional score transforms below, evaluated tile by tile so the Nq x Nk score
+ * matrix never reaches device memory: tiles of Q, K and V are staged on chip,
+ * a running row maximum and running row sum (online softmax) renormalise the
+ * partial output after each key tile, and the per-row log-sum-exp is emitted
+ * ("IO感知技术革命: FlashAttention如何重塑大模型训练的经济学", the sections on
+ * block-wise tiling and on the online softmax; "FlashAttention及变种改进",
+ * section 二.1 for the standard attention it reproduces).
+ *
+ * Score transforms and masks, applied in this order (the flash-attn v2.0-v2.7
+ * update article, v2.1 to v2.6 entries):
+ *   1. s = scale * q.k
+ *   2. softcap > 0:        s = softcap * tanh(s / softcap)                 (v2.6)
+ *   3. alibi_slopes != 0:  s = s - slope[h] * |i + (Nk - Nq) - j|          (v2.4)
+ *   4. mask (bottom-right aligned, off = Nk - Nq; v2.1 and v2.3):
+ *        causal:            keep j <= i + off
+ *        window_left  >= 0: keep j >= i + off - window_left
+ *        window_right >= 0: keep j <= i + off + window_right
+ *      (-1 leaves that side unbounded; causal acts as window_right = 0.)
+ * LSE[i] = ln(sum over kept keys of exp(s_ij)). A row with no kept key gets
+ * O = 0 and LSE = -inf.
+ *
+ * Memory layout (all row-major, contiguous, head_dim innermost):
+ *   q                [batch, seqlen_q, heads, head_dim]      in_dtype
+ *   k, v             [batch, seqlen_k, heads, head_dim]      in_dtype (fa_fwd)
+ *   k_cache, v_cache [num_pages, page_size, heads, head_dim] in_dtype (fa_fwd_splitkv)
+ *   block_table      [batch, max_pages_per_seq] int32; entry p of sequence b is the
+ *                    physical page holding logical keys [p*page_size, (p+1)*page_size)
+ *   o                [batch, seqlen_q, heads, head_dim]      o_dtype (FA_FP32 or FA_BF16)
+ *   lse              [batch, heads, seqlen_q] float32, natural log; may be NULL
+ *   o_part           [num_splits, batch, heads, seqlen_q, head_dim] float32
+ *   lse_part         [num_splits, batch, heads, seqlen_q] float32
+ *   alibi_slopes     [heads] float32, or NULL for no bias
+ *
+ * Ownership and execution: every pointer is a device pointer owned by the
+ * caller. The library allocates no device memory and keeps no mutable global
+ * state; calls are enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ * the null stream) and return without synchronising, so results are ready
+ * once the stream has reached the call. Calls on different streams may run
+ * concurrently as long as they do not write the same buffers.
+ *
+ * Errors: all arguments are validated on the host before any HIP call; on a
+ * validation error nothing is launched and nothing is written. FA_ERR_HIP
+ * means a launch was rejected by the runtime (hipGetLastError after launch).
+ * Block-table contents are not checked: ids outside [0, num_pages) are
+ * undefined behaviour (the table is maintained by the caller).
+ *
+ * Supported: in_dtype FA_BF16 or FA_FP32 (bf16 runs on bf16 MFMA with fp32
+ * accumulation, fp32 on fp32 MFMA); head_dim 64 or 128; any positive sizes
+ * with batch*heads*seqlen and every tensor's element count below 2^31 per
+ * dimension product as stated in fa_status_string(FA_ERR_SHAPE).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_dtype { FA_FP32 = 0, FA_BF16 = 1 };
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,       /* a size <= 0, too large, or inconsistent */
+  FA_ERR_UNSUPPORTED = 3, /* head_dim or dtype not instantiated */
+  FA_ERR_MASK = 4,        /* window < -1, or causal with window_right > 0 */
+  FA_ERR_HIP = 5,         /* the HIP runtime rejected a launch */
+  FA_ERR_VALUE = 6        /* softmax_scale not finite and > 0, softcap < 0 or not finite */
+};
+
+/*
+ * fa_fwd - exact attention forward over contiguous K/V.
+ *
+ * Follows the tiled IO-aware forward of the pages (see the header comment):
+ * one workgroup per (query tile, head, batch) streams the key tiles its rows
+ * can see, skipping tiles that the causal/window mask removes entirely (the
+ * v2.3 entry: only the in-window part is computed).
+ *
+ * Writes o (all batch*seqlen_q*heads rows) and, if lse != NULL, lse.
+ * Returns FA_OK or an fa_status error code.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, int in_dtype,
+           void* o, int o_dtype, float* lse,
+           int batch, int heads, int seqlen_q, int seqlen_k, int head_dim,
+           float softmax_scale, int causal, int window_left, int window_right,
+           const float* alibi_slopes, float softcap, void* stream);
+
+/*
+ * fa_fwd_splitkv - split-KV forward over a paged KV cache (the update article's
+ * v2.2 entry for the split along the key sequence, v2.5 for the paged cache
+ * addressed through block_table).
+ *
+ * The logical keys [0, seqlen_k) of each sequence are cut into num_splits
+ * contiguous chunks of C keys, C = ceil(seqlen_k / num_splits) rounded up to a
+ * multiple of page_size (so a chunk never cuts a page); trailing chunks may be
+ * empty. For every split s the call writes the attention of the queries over
+ * the keys of chunk s alone, with every mask and bias evaluated at the keys'
+ * absolute positions: o_part[s] is that chunk's normalised output and
+ * lse_part[s] its log-sum-exp (-inf, with o_part = 0, when no key of the chunk
+ * is kept). fa_splitkv_combine merges the splits into the full result.
+ *
+ * Requires max_pages_per_seq * page_size >= seqlen_k. Only the first
+ * ceil(seqlen_k / page_size) entries of each block_table row are read.
+ */
+int fa_fwd_splitkv(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
+                   const int* block_table, int max_pages_per_seq, int page_size,
+                   float* o_part, float* lse_part, int num_splits,
+                   int batch, int heads, int seqlen_q, int seqlen_k, int head_dim,
+                   float softmax_scale, int causal, int window_left, int window_right,
+                   const float* alibi_slopes, float softcap, void* stream);
+
+/*
+ * fa_splitkv_combine - the separate reduce step that merges split partials
+ * (the update article's v2.2 entry): for every (b, h, i),
+ *   L = ln(sum_s exp(lse_part[s])),  O = sum_s exp(lse_part[s] - L) * o_part[s].
+ * Rows where every split is empty get O = 0 and L = -inf.
+ *
+ * Writes o [batch, seqlen_q, heads, head_dim] in o_dtype and, if lse != NULL,
+ * lse [batch, heads, seqlen_q].
+ */
+int fa_splitkv_combine(const float* o_part, const float* lse_part, int num_splits,
+                       int batch, int heads, int seqlen_q, int head_dim,
+                       void* o, int o_dtype, float* lse, void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* Split chunk length C used by fa_fwd_splitkv for these sizes, or -1 on bad sizes. */
+int fa_split_chunk_len(int seqlen_k, int num_splits, int page_size);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

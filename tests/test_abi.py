@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, imports no device allocator, and rejects bad arguments with
+the documented status codes before making any HIP call.
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_tiled_attention_05_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.library_path()),
+                                reason="libfa.so not built (run __graft_entry__.build())")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+OK, NULL, SHAPE, UNSUP, MASK, HIP, VALUE = range(7)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_fwd_splitkv", "fa_splitkv_combine", "fa_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load_library()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in declared_functions():
+        assert n in exported, n
+
+
+def test_library_never_allocates_device_memory():
+    out = subprocess.run(["nm", "-D", "--undefined-only", fa.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    bad = [s for s in out.split() if re.match(r"hip(Ext)?Malloc|hipFree|hipMemAlloc|hipHostMalloc", s)]
+    assert bad == []
+
+
+def test_status_strings():
+    for s in range(7):
+        assert fa.fa_status_string(s)
+    assert fa.fa_status_string(99) == "unknown status"
+
+
+def test_split_chunk_len():
+    assert fa.fa_split_chunk_len(32768, 16, 256) == 2048
+    assert fa.fa_split_chunk_len(2000, 2, 1) == 1000
+    assert fa.fa_split_chunk_len(100, 3, 16) == 48
+    assert fa.fa_split_chunk_len(5, 8, 1) == 1
+    assert fa.fa_split_chunk_len(0, 1, 1) == -1
+
+
+def fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, in_dtype=1, o=FAKE, o_dtype=0, lse=None, batch=1, heads=1,
+             seqlen_q=4, seqlen_k=4, head_dim=64, scale=0.125, causal=0, wl=-1, wr=-1,
+             alibi=None, softcap=0.0, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_fwd(a["q"], a["k"], a["v"], a["in_dtype"], a["o"], a["o_dtype"],
+                                    a["lse"], a["batch"], a["heads"], a["seqlen_q"], a["seqlen_k"],
+                                    a["head_dim"], a["scale"], a["causal"], a["wl"], a["wr"],
+                                    a["alibi"], a["softcap"], a["stream"])
+
+
+def split(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, in_dtype=1, bt=FAKE, maxp=4, ps=16, op=FAKE, lp=FAKE, S=2,
+             batch=1, heads=1, seqlen_q=1, seqlen_k=64, head_dim=128, scale=0.1, causal=1,
+             wl=-1, wr=-1, alibi=None, softcap=0.0, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_fwd_splitkv(
+        a["q"], a["k"], a["v"], a["in_dtype"], a["bt"], a["maxp"], a["ps"], a["op"], a["lp"],
+        a["S"], a["batch"], a["heads"], a["seqlen_q"], a["seqlen_k"], a["head_dim"], a["scale"],
+        a["causal"], a["wl"], a["wr"], a["alibi"], a["softcap"], a["stream"])
+
+
+def comb(**kw):
+    a = dict(op=FAKE, lp=FAKE, S=2, batch=1, heads=1, seqlen_q=1, head_dim=128, o=FAKE,
+             o_dtype=0, lse=None, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_splitkv_combine(a["op"], a["lp"], a["S"], a["batch"], a["heads"],
+                                                a["seqlen_q"], a["head_dim"], a["o"],
+                                                a["o_dtype"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL),
+    (dict(batch=0), SHAPE), (dict(heads=-1), SHAPE), (dict(seqlen_q=0), SHAPE),
+    (dict(seqlen_k=0), SHAPE), (dict(seqlen_k=(1 << 28) + 1), SHAPE),
+    (dict(head_dim=96), UNSUP), (dict(head_dim=256), UNSUP), (dict(in_dtype=2), UNSUP),
+    (dict(o_dtype=5), UNSUP),
+    (dict(wl=-2), MASK), (dict(wr=-3), MASK), (dict(causal=1, wr=1), MASK),
+    (dict(scale=0.0), VALUE), (dict(scale=-1.0), VALUE), (dict(scale=math.inf), VALUE),
+    (dict(scale=math.nan), VALUE), (dict(softcap=-1.0), VALUE), (dict(softcap=math.nan), VALUE),
+])
+def test_fa_fwd_rejects(kw, code):
+    assert fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=None), NULL), (dict(op=None), NULL), (dict(lp=None), NULL), (dict(q=None), NULL),
+    (dict(S=0), SHAPE), (dict(ps=0), SHAPE), (dict(maxp=0), SHAPE),
+    (dict(maxp=3, ps=16, seqlen_k=64), SHAPE),
+    (dict(head_dim=32), UNSUP), (dict(in_dtype=7), UNSUP),
+    (dict(causal=1, wr=2), MASK), (dict(wl=-5), MASK), (dict(softcap=-0.5), VALUE),
+])
+def test_fa_fwd_splitkv_rejects(kw, code):
+    assert split(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(op=None), NULL), (dict(lp=None), NULL), (dict(o=None), NULL),
+    (dict(S=0), SHAPE), (dict(batch=0), SHAPE), (dict(seqlen_q=-1), SHAPE),
+    (dict(head_dim=80), UNSUP), (dict(o_dtype=3), UNSUP),
+])
+def test_fa_splitkv_combine_rejects(kw, code):
+    assert comb(**kw) == code
