@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_combine.hip"]
+HIP_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode_bf16.hip", "fa_combine.hip"]
 CPP_SOURCES = ["fa_api.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}"]
@@ -43,16 +43,17 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra_flags=None, out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every source and link `out` (default: the in-tree libfa.so)."""
+    os.makedirs(build_dir, exist_ok=True)
     hipcc = _hipcc()
     extra = list(extra_flags or [])
     jobs = []
     for s in HIP_SOURCES:
-        obj = os.path.join(BUILD, s + ".o")
+        obj = os.path.join(build_dir, s + ".o")
         jobs.append([hipcc, *COMMON, *HIP_FLAGS, *extra, "-c", os.path.join(CSRC, s), "-o", obj])
     for s in CPP_SOURCES:
-        obj = os.path.join(BUILD, s + ".o")
+        obj = os.path.join(build_dir, s + ".o")
         jobs.append([hipcc, *COMMON, *extra, "-c", os.path.join(CSRC, s), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
         outs = list(ex.map(_run, jobs))
@@ -61,10 +62,10 @@ def build(verbose: bool = False, extra_flags=None) -> str:
             if o.strip():
                 print(o)
     objs = [j[-1] for j in jobs]
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -31,6 +31,19 @@ Launcher pick(int in_dtype, int head_dim, bool softcap, bool alibi) {
 #undef FA_PICK
 }
 
+// One query row per (batch, head): the split pass streams the cache with the
+// dedicated decode kernel.
+Launcher pick_decode(int head_dim, bool softcap, bool alibi) {
+#define FA_PICK_DEC(D)                                                          \
+  if (softcap && alibi) return &fa::launch_decode_bf16<D, true, true>;          \
+  if (softcap) return &fa::launch_decode_bf16<D, true, false>;                  \
+  if (alibi) return &fa::launch_decode_bf16<D, false, true>;                    \
+  return &fa::launch_decode_bf16<D, false, false>;
+  if (head_dim == 64) { FA_PICK_DEC(64) }
+  FA_PICK_DEC(128)
+#undef FA_PICK_DEC
+}
+
 int check_sizes(int batch, int heads, int seqlen_q, int seqlen_k) {
   if (batch <= 0 || heads <= 0 || seqlen_q <= 0 || seqlen_k <= 0) return FA_ERR_SHAPE;
   if (seqlen_q > kMaxSeq || seqlen_k > kMaxSeq || heads > (1 << 16) || batch > (1 << 24))
@@ -91,8 +104,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE:
       return "bad sizes: every size must be >= 1, seqlens <= 2^28, heads <= 2^16, "
-             "batch <= 2^24, the launch below 2^31 workgroups, and "
-             "max_pages_per_seq * page_size >= seqlen_k";
+             "batch <= 2^24, the launch below 2^31 workgroups, "
+             "max_pages_per_seq * page_size >= seqlen_k, and page_size * heads * head_dim < 2^31";
     case FA_ERR_UNSUPPORTED: return "unsupported dtype or head_dim (head_dim 64 or 128; FP32 or BF16)";
     case FA_ERR_MASK: return "bad mask: windows must be >= -1 and causal needs window_right <= 0";
     case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
@@ -149,6 +162,7 @@ int fa_fwd_splitkv(const void* q, const void* k_cache, const void* v_cache, int 
   if (num_splits <= 0 || num_splits > (1 << 16) || max_pages_per_seq <= 0 || page_size <= 0)
     return FA_ERR_SHAPE;
   if ((int64_t)max_pages_per_seq * page_size < seqlen_k) return FA_ERR_SHAPE;
+  if ((int64_t)page_size * heads * head_dim >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
   if ((st = check_kind(in_dtype, head_dim))) return st;
   if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
     return st;
@@ -162,7 +176,13 @@ int fa_fwd_splitkv(const void* q, const void* k_cache, const void* v_cache, int 
   p.block_table = block_table;
   p.max_pages = max_pages_per_seq;
   p.page_size = page_size;
+  p.page_shift = -1;
+  if ((page_size & (page_size - 1)) == 0)
+    for (int sh = 0; sh < 31; ++sh)
+      if ((1 << sh) == page_size) p.page_shift = sh;
   p.num_splits = num_splits;
+  p.row_stride = heads * head_dim;
+  p.page_stride = (int64_t)page_size * heads * head_dim;
   const int tile = in_dtype == FA_BF16 ? fa::BF16_BM : fa::F32_BM;
   fill_common(p, batch, heads, seqlen_q, seqlen_k, softmax_scale, causal, window_left,
               window_right, alibi_slopes, softcap, tile);
@@ -171,7 +191,9 @@ int fa_fwd_splitkv(const void* q, const void* k_cache, const void* v_cache, int 
   p.split_len = (int)c;
   if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
 
-  Launcher fn = pick<true>(in_dtype, head_dim, softcap > 0.0f, alibi_slopes != nullptr);
+  Launcher fn = (in_dtype == FA_BF16 && seqlen_q == 1)
+                    ? pick_decode(head_dim, softcap > 0.0f, alibi_slopes != nullptr)
+                    : pick<true>(in_dtype, head_dim, softcap > 0.0f, alibi_slopes != nullptr);
   return fn(p, stream) ? FA_ERR_HIP : FA_OK;
 }
 

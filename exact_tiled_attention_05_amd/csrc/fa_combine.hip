@@ -16,6 +16,17 @@ namespace {
 
 constexpr int kRowsPerGroup = 4;
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * kRowsPerGroup) void combine_kernel(CombineParams p) {
   constexpr int PER_LANE = D / 64;
@@ -31,20 +42,23 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void combine_kernel(CombinePara
   const int64_t split_stride = (int64_t)p.B * p.H * p.Nq;
   const int64_t r0 = ((int64_t)b * p.H + h) * p.Nq + i;  // row index inside one split
 
+  // Split log-sum-exps (log2 units) loaded by the lanes in parallel.
   float m = kNegInf;
-  for (int s = 0; s < p.S; ++s) m = fmaxf(m, p.lse_part[s * split_stride + r0] * kLog2e);
-
+  for (int s = lane; s < p.S; s += 64) m = fmaxf(m, p.lse_part[s * split_stride + r0] * kLog2e);
+  m = wave_max(m);
+  float tot = 0.0f;
   float acc[PER_LANE];
 #pragma unroll
   for (int e = 0; e < PER_LANE; ++e) acc[e] = 0.0f;
-  float tot = 0.0f;
   if (m != kNegInf) {
+    for (int s = lane; s < p.S; s += 64) tot += fast_exp2(p.lse_part[s * split_stride + r0] * kLog2e - m);
+    tot = wave_sum(tot);
+    const float* op = p.o_part + r0 * D + lane;
+#pragma unroll 8
     for (int s = 0; s < p.S; ++s) {
       const float wgt = fast_exp2(p.lse_part[s * split_stride + r0] * kLog2e - m);
-      tot += wgt;
-      const float* op = p.o_part + (s * split_stride + r0) * D;
 #pragma unroll
-      for (int e = 0; e < PER_LANE; ++e) acc[e] += wgt * op[lane + 64 * e];
+      for (int e = 0; e < PER_LANE; ++e) acc[e] += wgt * op[s * split_stride * D + 64 * e];
     }
   }
   const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;

@@ -1,0 +1,234 @@
+// Split-KV pass for one query row per (batch, head): the decode step, run as
+// an HBM stream over the paged KV cache (flash-attn v2.0-v2.7 update article:
+// v2.2 entry for cutting the cache along the sequence across workgroups, v2.5
+// for pages addressed through block_table; the inference article's point that
+// decode time goes to loading the cache when the query is one token).
+//
+// One workgroup of 4 wavefronts per (split, head, batch), head fastest. 16 lanes
+// (8 for head_dim 64) share one key row: each lane owns a 16-byte chunk of the
+// row, so a wavefront-wide load reads 4 (8) whole 256-byte (128-byte) rows. A
+// lane keeps 8 K and 8 V loads in flight per batch. Scores are reduced across
+// the row's lanes with DPP, and each lane runs an fp32 online softmax over its
+// group's keys for its 8 output columns. Groups, then wavefronts, are merged
+// by log-sum-exp at the end.
+#include <hip/hip_runtime.h>
+
+#include "fa_device.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+#ifndef FA_DECODE_LOADS
+#define FA_DECODE_LOADS 8
+#endif
+constexpr int kU = FA_DECODE_LOADS;  // loads in flight per lane, per tensor
+// Block-table entries staged in LDS per workgroup (the pages its key range
+// touches); longer ranges read the table from global memory instead.
+constexpr int kTablePages = 1024;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                0xf, 0xf, false));
+}
+
+// Sum over each group of CH consecutive lanes (CH = 8 or 16); every lane of the
+// group receives the sum.
+template <int CH>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm(1,0,3,2): swap neighbours
+  x += dpp<0x4E>(x);   // quad_perm(2,3,0,1): swap pairs
+  x += dpp<0x141>(x);  // row_half_mirror: lane i <-> 7 - i within 8
+  if constexpr (CH == 16) x += dpp<0x140>(x);  // row_mirror: lane i <-> 15 - i within 16
+  return x;
+}
+
+__device__ __forceinline__ float lo_bf16(unsigned w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float hi_bf16(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+template <int D, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
+  constexpr int CH = D / 8;       // lanes per key row
+  constexpr int KPI = 64 / CH;    // keys per wavefront-wide load
+  constexpr int KPB = KPI * kU;   // keys per wavefront batch
+  __shared__ float s_m[kWaves], s_l[kWaves];
+  __shared__ float s_o[kWaves][D];
+  __shared__ int s_bt[kTablePages];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int c = lane % CH, g = lane / CH;
+  const WorkItem wi = decode_work<true>(p);
+  const int b = wi.b, h = wi.h, s = wi.s;
+
+  int slo, shi;
+  split_range(p, s, slo, shi);
+  const int ip = p.Nk - 1;  // the single query row, aligned to the last key
+  int lo = slo, hi = shi;
+  if (p.window_left >= 0) lo = max(lo, ip - p.window_left);
+  if (p.window_right >= 0) hi = min(hi, ip + p.window_right + 1);
+  if (hi <= lo) {
+    write_empty_rows<true>(p, b, h, s, 0, 1, D, tid, kThreads);
+    return;
+  }
+
+  // Pages [p0, p0 + np) hold this workgroup's keys; stage their ids in LDS.
+  const int p0 = p.page_shift >= 0 ? lo >> p.page_shift : lo / p.page_size;
+  const int p1 = p.page_shift >= 0 ? (hi - 1) >> p.page_shift : (hi - 1) / p.page_size;
+  const int np = p1 - p0 + 1;
+  const bool table_in_lds = np <= kTablePages;
+  const int* bt_row = p.block_table + (int64_t)b * p.max_pages;
+  if (table_in_lds)
+    for (int i = tid; i < np; i += kThreads) s_bt[i] = bt_row[p0 + i];
+  __syncthreads();
+
+  const u32x4_t qv = *(const u32x4_t*)((const uint16_t*)p.q + q_offset(p, b, 0, h, D) + 8 * c);
+  bf16x2_t qp[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const unsigned wq = qv[e];
+    qp[e] = as_bf16x2(wq);
+  }
+  float slope_log2 = 0.0f;
+  if constexpr (ALIBI) slope_log2 = p.alibi[h] * kLog2e;
+
+  float m = kNegInf, l = 0.0f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+
+  const uint16_t* kbase = (const uint16_t*)p.k + 8 * c;
+  const uint16_t* vbase = (const uint16_t*)p.v + 8 * c;
+  for (int base = lo + w * KPB; base < hi; base += kWaves * KPB) {
+    // Row offsets first, then every load back to back (no branches between
+    // them). A key past the end re-reads key `lo`, whose page is real, and its
+    // score is masked below, so its finite V row gets weight 0.
+    int64_t off[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int t = min(base + g + KPI * u, hi - 1);
+      const int tt = base + g + KPI * u < hi ? t : lo;
+      int idx, slot;
+      if (p.page_shift >= 0) {
+        idx = tt >> p.page_shift;
+        slot = tt & (p.page_size - 1);
+      } else {
+        idx = tt / p.page_size;
+        slot = tt - idx * p.page_size;
+      }
+      const int page = table_in_lds ? s_bt[idx - p0] : bt_row[idx];
+      off[u] = (int64_t)page * p.page_stride + slot * p.row_stride + h * D;
+    }
+    u32x4_t kx[kU], vx[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      kx[u] = *(const u32x4_t*)(kbase + off[u]);
+      vx[u] = *(const u32x4_t*)(vbase + off[u]);
+    }
+    float sc[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned wk = kx[u][e];
+        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wk), qp[e], a, false);
+      }
+      a = group_sum<CH>(a);
+      if constexpr (SOFTCAP) {
+        const float ex = fast_exp2(a * p.scale_over_cap2);
+        a = p.softcap_log2 - 2.0f * p.softcap_log2 * __builtin_amdgcn_rcpf(ex + 1.0f);
+      } else {
+        a *= p.scale_log2;
+      }
+      const int t = base + g + KPI * u;
+      if constexpr (ALIBI) a -= slope_log2 * (float)(ip - t);
+      sc[u] = t < hi ? a : kNegInf;
+    }
+    float mb = sc[0];
+#pragma unroll
+    for (int u = 1; u < kU; ++u) mb = fmaxf(mb, sc[u]);
+    const float m_new = fmaxf(m, mb);
+    if (m_new > m + kLazyRescaleThreshold) {
+      const float alpha = fast_exp2(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] *= alpha;
+      m = m_new;
+    }
+    const float bse = m == kNegInf ? 0.0f : m;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float pu = fast_exp2(sc[u] - bse);
+      l += pu;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] += pu * lo_bf16(vx[u][e]);
+        o[2 * e + 1] += pu * hi_bf16(vx[u][e]);
+      }
+    }
+  }
+
+  // Merge the KPI lane groups of this wavefront (same columns, different keys).
+#pragma unroll
+  for (int msk = CH; msk < 64; msk <<= 1) {
+    const float m2 = __shfl_xor(m, msk);
+    const float l2 = __shfl_xor(l, msk);
+    const float mn = fmaxf(m, m2);
+    const float a1 = m == kNegInf ? 0.0f : fast_exp2(m - mn);
+    const float a2 = m2 == kNegInf ? 0.0f : fast_exp2(m2 - mn);
+    l = l * a1 + l2 * a2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = o[e] * a1 + __shfl_xor(o[e], msk) * a2;
+    m = mn;
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_o[w][8 * c + e] = o[e];
+    if (c == 0) {
+      s_m[w] = m;
+      s_l[w] = l;
+    }
+  }
+  __syncthreads();
+  if (tid < D) {
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) M = fmaxf(M, s_m[i]);
+    float L = 0.0f, acc = 0.0f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) {
+        const float a = s_m[i] == kNegInf ? 0.0f : fast_exp2(s_m[i] - M);
+        L += a * s_l[i];
+        acc += a * s_o[i][tid];
+      }
+    }
+    const int64_t ro = (((int64_t)s * p.B + b) * p.H + h) * p.Nq;
+    p.o_part[ro * D + tid] = L > 0.0f ? acc / L : 0.0f;
+    if (tid == 0) p.lse_part[ro] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
+  }
+}
+
+}  // namespace
+
+template <int D, bool SOFTCAP, bool ALIBI>
+int launch_decode_bf16(const FwdParams& p, void* stream) {
+  const int64_t groups = (int64_t)p.H * p.B * p.num_splits;
+  hipLaunchKernelGGL((decode_bf16_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)groups),
+                     dim3(kThreads), 0, (hipStream_t)stream, p);
+  return (int)hipGetLastError();
+}
+
+#define FA_INST(D, SC, AL) template int launch_decode_bf16<D, SC, AL>(const FwdParams&, void*);
+FA_INST(64, false, false)
+FA_INST(64, false, true)
+FA_INST(64, true, false)
+FA_INST(64, true, true)
+FA_INST(128, false, false)
+FA_INST(128, false, true)
+FA_INST(128, true, false)
+FA_INST(128, true, true)
+
+}  // namespace fa

@@ -24,6 +24,11 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
+// Reinterpret one 32-bit word as two bf16. Takes the word by value: applying
+// __builtin_bit_cast directly to a vector subscript (v[e]) inside an unrolled
+// loop was seen to read element 0 for every e with this toolchain.
+__device__ __forceinline__ bf16x2_t as_bf16x2(unsigned w) { return __builtin_bit_cast(bf16x2_t, w); }
+
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 // i % 4 of the 8-byte chunks addressed by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.
 __device__ __forceinline__ s16x4_t ds_read_tr16(const uint16_t* lds_ptr) {
@@ -162,8 +167,15 @@ __device__ __forceinline__ int64_t q_offset(const FwdParams& p, int b, int row, 
 template <bool PAGED>
 __device__ __forceinline__ int64_t kv_offset(const FwdParams& p, int b, int key, int h, int D) {
   if constexpr (PAGED) {
-    const int page = p.block_table[(int64_t)b * p.max_pages + key / p.page_size];
-    const int slot = key % p.page_size;
+    int idx, slot;
+    if (p.page_shift >= 0) {
+      idx = key >> p.page_shift;
+      slot = key & (p.page_size - 1);
+    } else {
+      idx = key / p.page_size;
+      slot = key - idx * p.page_size;
+    }
+    const int page = p.block_table[(int64_t)b * p.max_pages + idx];
     return (((int64_t)page * p.page_size + slot) * p.H + h) * D;
   } else {
     return (((int64_t)b * p.Nk + key) * p.H + h) * D;

@@ -26,8 +26,14 @@ constexpr int kBM = BF16_BM;   // query rows per workgroup
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 256;  // 4 wavefronts
 
+// Wavefronts per SIMD the register budget is sized for: 2 lets one wavefront's
+// softmax overlap another's MFMA work and keeps accumulators out of AGPRs.
+#ifndef FA_PREFILL_WAVES
+#define FA_PREFILL_WAVES 2
+#endif
+
 template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FA_PREFILL_WAVES, FA_PREFILL_WAVES))) void fwd_bf16_kernel(FwdParams p) {
   constexpr int KS = D / 16;             // MFMA k-steps of Q K^T
   constexpr int NDB = D / 32;            // 32-row blocks of O^T
   // LDS row strides (bf16) picked for conflict-free operand reads: K rows are

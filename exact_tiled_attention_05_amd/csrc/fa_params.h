@@ -14,9 +14,12 @@ struct FwdParams {
   float* o_part;            // [S, B, H, Nq, D] (split launches)
   float* lse_part;          // [S, B, H, Nq]
   const int* block_table;   // [B, max_pages] (paged launches)
-  const float* alibi;       // [H] slopes, already multiplied by log2(e); nullptr = off
+  const float* alibi;       // [H] ALiBi slopes (natural-log units); nullptr = off
   int B, H, Nq, Nk;
   int max_pages, page_size;
+  int page_shift;           // log2(page_size) when it is a power of two, else -1
+  int row_stride;           // H * D: elements between consecutive keys of one page
+  int64_t page_stride;      // page_size * H * D: elements per page
   int num_splits, split_len;
   int num_q_tiles;
   int window_left;          // -1 = unbounded
@@ -41,6 +44,8 @@ template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
 int launch_fwd_bf16(const FwdParams& p, void* stream);
 template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
 int launch_fwd_f32(const FwdParams& p, void* stream);
+template <int D, bool SOFTCAP, bool ALIBI>
+int launch_decode_bf16(const FwdParams& p, void* stream);
 template <int D>
 int launch_combine(const CombineParams& p, void* stream);
 
