@@ -53,9 +53,18 @@ __device__ __forceinline__ constexpr int acc_key(int v, int h2) {
   return 8 * (v >> 2) + 4 * h2 + (v & 3);
 }
 
-// Value of x in lane l ^ 32 (the other half of the wavefront).
-__device__ __forceinline__ float other_half(float x) {
-  return __shfl_xor(x, 32);
+// Reductions over the lane pair (l, l ^ 32) that holds one query row, on the
+// VALU lane-swap (v_permlane32_swap) rather than the LDS crossbar: with both
+// operands = x it returns {x[l & 31], x[(l & 31) + 32]} in every lane.
+__device__ __forceinline__ float half_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -84,68 +93,85 @@ __device__ __forceinline__ KeyBounds key_bounds(int r0, int r1, int off, int slo
   return kb;
 }
 
+// Score units. Without a softcap or ALiBi the kernels keep the raw dot product
+// q.k and fold softmax_scale * log2(e) into the exponent (one FMA per score);
+// with either transform the transform itself yields log2-domain scores and the
+// exponent factor is 1. Probabilities are exp2(c * (t - m)).
+template <bool SOFTCAP, bool ALIBI>
+__device__ __forceinline__ float exponent_scale(const FwdParams& p) {
+  return (SOFTCAP || ALIBI) ? 1.0f : p.scale_log2;
+}
+
 // Score transform for one tile held as NB 32-key blocks of accumulators:
-// scale (log2 units), optional tanh cap, optional ALiBi distance penalty,
-// optional mask to [row_lo, row_hi). Results are log2-domain scores.
+// optional tanh cap (on the scaled score), optional ALiBi distance penalty,
+// optional mask to [row_lo, row_hi).
 template <int NB, bool SOFTCAP, bool ALIBI>
 __device__ __forceinline__ void transform_scores(float (&t)[NB][16], const FwdParams& p,
                                                  float slope_log2, float rel_pos,
                                                  bool need_mask, int key0, int row_lo,
                                                  int row_hi, int h2) {
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float x = t[j][v];
-      if constexpr (SOFTCAP) {
-        // tanh(y) = 1 - 2 / (exp(2y) + 1), evaluated with exp2 and a reciprocal.
-        const float e = fast_exp2(x * p.scale_over_cap2);
-        x = p.softcap_log2 - 2.0f * p.softcap_log2 * __builtin_amdgcn_rcpf(e + 1.0f);
-      } else {
-        x *= p.scale_log2;
-      }
-      if constexpr (ALIBI) {
-        // rel_pos = (i + off) - (key0 + 4*h2): distance to key = rel_pos - offset.
-        const float dist = rel_pos - (float)(32 * j + 8 * (v >> 2) + (v & 3));
-        x -= slope_log2 * __builtin_fabsf(dist);
-      }
-      t[j][v] = x;
-    }
-  }
-  if (need_mask) {
+  if constexpr (SOFTCAP || ALIBI) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int key = key0 + 32 * j + acc_key(v, h2);
-        if (key < row_lo || key >= row_hi) t[j][v] = kNegInf;
+        float x = t[j][v];
+        if constexpr (SOFTCAP) {
+          // tanh(y) = 1 - 2 / (exp(2y) + 1), evaluated with exp2 and a reciprocal.
+          const float e = fast_exp2(x * p.scale_over_cap2);
+          x = p.softcap_log2 - 2.0f * p.softcap_log2 * __builtin_amdgcn_rcpf(e + 1.0f);
+        } else {
+          x *= p.scale_log2;
+        }
+        if constexpr (ALIBI) {
+          // rel_pos = (i + off) - (key0 + 4*h2): distance to the key = rel_pos - offset.
+          const float dist = rel_pos - (float)(32 * j + 8 * (v >> 2) + (v & 3));
+          x -= slope_log2 * __builtin_fabsf(dist);
+        }
+        t[j][v] = x;
+      }
+    }
+  }
+  if (need_mask) {
+    // key = key0 + 4*h2 + kk with kk a compile-time offset per slot: compare kk
+    // against this lane's bounds shifted by key0 + 4*h2.
+    const int lo_rel = row_lo - key0 - 4 * h2;
+    const int hi_rel = row_hi - key0 - 4 * h2;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kk = 32 * j + 8 * (v >> 2) + (v & 3);
+        if (kk < lo_rel || kk >= hi_rel) t[j][v] = kNegInf;
       }
     }
   }
 }
 
-// Online softmax step for this lane's row: updates the running max (lazily),
-// returns the factor the output accumulator must be multiplied by, and the
-// exponent base to subtract from this tile's scores.
+// Online softmax step for this lane's row. m_run is the running max in score
+// units; it moves when the tile max exceeds it by more than `threshold`
+// (score units). Returns the factor for the output accumulator and sets
+// `mc` = c * m_run (0 while the row has seen no key) for the exponent FMA.
 template <int NB>
-__device__ __forceinline__ float online_max(const float (&t)[NB][16], float& m_run, float& l_run,
-                                            bool& any_rescale, float& base, float threshold) {
+__device__ __forceinline__ float online_max(const float (&t)[NB][16], float c, float& m_run,
+                                            float& l_run, bool& any_rescale, float& mc,
+                                            float threshold) {
   float mt = kNegInf;
 #pragma unroll
   for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int v = 0; v < 16; ++v) mt = fmaxf(mt, t[j][v]);
-  mt = fmaxf(mt, other_half(mt));
+  mt = half_max(mt);
   const float m_new = fmaxf(m_run, mt);
   const bool need = m_new > m_run + threshold;
   float alpha = 1.0f;
   if (need) {
-    alpha = fast_exp2(m_run - m_new);  // 0 when m_run is still -inf
+    alpha = fast_exp2((m_run - m_new) * c);  // 0 when m_run is still -inf
     m_run = m_new;
   }
   l_run *= alpha;
   any_rescale = __any(need);
-  base = (m_run == kNegInf) ? 0.0f : m_run;
+  mc = (m_run == kNegInf) ? 0.0f : m_run * c;
   return alpha;
 }
 

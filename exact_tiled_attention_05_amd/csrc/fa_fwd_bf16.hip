@@ -7,14 +7,19 @@
 //   score transform, mask, online softmax in VGPRs (row = lane pair l, l^32)
 //   O^T += V^T P^T  on v_mfma_f32_32x32x16_bf16 (V read transposed from LDS
 //                   with ds_read_b64_tr_b16, P from VGPRs)
-// K and V tiles are double-buffered in LDS in their natural [key][d] layout:
-// the next tile's global loads are issued before the current tile's math, and
-// stored after it.
+// K and V tiles travel HBM -> LDS with global_load_lds_dwordx4 (no staging
+// registers) into two buffers each, in their natural [key][d] layout with the
+// 16-byte chunks of each row XOR-swizzled so that both the K operand reads and
+// the transposed V reads are free of bank conflicts; the copies of tile t+1
+// are in flight while tile t is computed. Tiles inside every row's key range
+// take a path with no per-element mask.
 // (Tiled IO-aware forward with online softmax: "IO感知技术革命: FlashAttention如何
 // 重塑大模型训练的经济学", sections on block tiling, online softmax and overlap of
 // copies with compute; mask and score variants: flash-attn v2.0-v2.7 update
 // article, v2.1-v2.6 entries; split + paged form: its v2.2 and v2.5 entries.)
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "fa_device.h"
 
@@ -26,27 +31,71 @@ constexpr int kBM = BF16_BM;   // query rows per workgroup
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 256;  // 4 wavefronts
 
-// Wavefronts per SIMD the register budget is sized for: 2 lets one wavefront's
-// softmax overlap another's MFMA work and keeps accumulators out of AGPRs.
-#ifndef FA_PREFILL_WAVES
-#define FA_PREFILL_WAVES 2
+// Wavefronts per SIMD the register budget is sized for, per head_dim.
+#ifndef FA_WAVES_D128
+#define FA_WAVES_D128 2
+#endif
+#ifndef FA_WAVES_D64
+#define FA_WAVES_D64 3
+#endif
+template <int D>
+struct Tuning {
+  static constexpr int kWaves = D == 128 ? FA_WAVES_D128 : FA_WAVES_D64;
+};
+
+// MFMA issue runs at raised wave priority so the matrix pipe is refilled
+// promptly while the other wavefront on the SIMD works through its softmax.
+#ifndef FA_NO_SETPRIO
+#define FA_SETPRIO(x) __builtin_amdgcn_s_setprio(x)
+#else
+#define FA_SETPRIO(x)
 #endif
 
-template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FA_PREFILL_WAVES, FA_PREFILL_WAVES))) void fwd_bf16_kernel(FwdParams p) {
-  constexpr int KS = D / 16;             // MFMA k-steps of Q K^T
-  constexpr int NDB = D / 32;            // 32-row blocks of O^T
-  // LDS row strides (bf16) picked for conflict-free operand reads: K rows are
-  // read 16 bytes per lane (32 lanes = 32 rows), V with transposed 8-byte reads
-  // (16 lanes = 4 rows x 32 bytes, two 16-lane groups 16 d apart).
-  constexpr int KSTR = D + 8;
-  constexpr int VSTR = D + 32;
-  constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
-  constexpr int KPT = kBN * CPR / kThreads;  // K/V rows each thread moves per tile (4 or 2)
-  static_assert(KPT == 4 || KPT == 2, "tile split");
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBN * VSTR];
+// Chunk swizzle of an LDS tile row: logical 16-byte chunk c of row r lives at
+// physical chunk c ^ swz(r). For head_dim 128 (16 chunks per 256-byte row) the
+// 16 rows read together by a K operand load get 16 distinct chunks, and the 4
+// consecutive rows of a transposed V read (two 16-lane groups, 16 columns
+// apart) land on 16 distinct chunks; head_dim 64 (8 chunks per 128-byte row,
+// two rows per bank sweep) gets the same property from row bits 1..3.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Element offset of (row, logical 16-byte chunk) inside an LDS tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return row * D + 8 * (chunk ^ swz<D>(row));
+}
+
+__device__ __forceinline__ void wait_vmem() {
+  // vmcnt(0), leaving the LDS/export counters unconstrained.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Tuning<D>::kWaves, Tuning<D>::kWaves)))
+void fwd_bf16_kernel(FwdParams p) {
+  constexpr int KS = D / 16;                 // MFMA k-steps of Q K^T
+  constexpr int NDB = D / 32;                // 32-row blocks of O^T
+  constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+  constexpr int ROWS_PER_LOAD = 64 / CPR;    // rows one wavefront-wide LDS copy fills
+  constexpr int LOADS = kBN / ROWS_PER_LOAD / 4;  // copies per wavefront per tensor per tile
+  constexpr int TILE = kBN * D;              // elements per tile
+
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[TILE];
+#ifdef FA_DIAG_LDS_PAD
+  __shared__ uint16_t diag_pad[48 * 1024];  // occupancy experiment: one workgroup per CU
+  if (p.B < 0) diag_pad[threadIdx.x] = 0;
+#endif
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
@@ -76,6 +125,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FA_PRE
 
   float slope_log2 = 0.0f;
   if constexpr (ALIBI) slope_log2 = p.alibi[h] * kLog2e;
+  const float c = exponent_scale<SOFTCAP, ALIBI>(p);
 
   // Q fragment: row `row`, columns 16*ks + 8*h2 .. +7 (the B operand of S^T = K Q^T).
   bf16x8_t qf[KS];
@@ -89,128 +139,153 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FA_PRE
     }
   }
 
-  // Tile movement: thread handles chunk `lc` of rows lg*KPT .. lg*KPT+KPT-1.
-  const int lc = tid % CPR, lg = tid / CPR;
-  u32x4_t kr[KPT], vr[KPT];
-  auto load_tile = [&](int j0) {
+  const int j_first = (wg.lo / kBN) * kBN;
+  const int ntiles = (wg.hi - j_first + kBN - 1) / kBN;
+
+  // ---- HBM -> LDS copies of one tile of K and V. Copy i of this wavefront
+  // fills tile rows [ROWS_PER_LOAD * (LOADS*w + i), +ROWS_PER_LOAD); lane L
+  // writes physical chunk L % CPR of its row, i.e. logical chunk
+  // (L % CPR) ^ swz(row). K and V share the layout, hence one offset per copy.
+  // Keys past the end re-read the last key (finite data; masked later).
+  const uint16_t* kg = (const uint16_t*)p.k;
+  const uint16_t* vg = (const uint16_t*)p.v;
+  auto copy_tiles = [&](uint16_t* kdst, uint16_t* vdst, int j0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int key = j0 + lg * KPT + i;
-      if (key < p.Nk) {
-        const int64_t o = kv_offset<PAGED>(p, b, key, h, D) + 8 * lc;
-        kr[i] = *(const u32x4_t*)((const uint16_t*)p.k + o);
-        vr[i] = *(const u32x4_t*)((const uint16_t*)p.v + o);
-      } else {
-        kr[i] = u32x4_t{0, 0, 0, 0};
-        vr[i] = u32x4_t{0, 0, 0, 0};
-      }
+    for (int i = 0; i < LOADS; ++i) {
+      const int ld = LOADS * w + i;
+      const int trow = ROWS_PER_LOAD * ld + lane / CPR;
+      const int chunk = (lane % CPR) ^ swz<D>(trow);
+      const int key = min(j0 + trow, p.Nk - 1);
+      const int64_t o = kv_offset<PAGED>(p, b, key, h, D) + 8 * chunk;
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(kg + o), (lds_ptr_t)(kdst + 512 * ld), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(vg + o), (lds_ptr_t)(vdst + 512 * ld), 16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
+
+  // ---- S^T = K Q^T for one 64-key tile (two 32-key blocks).
+  auto qk = [&](const uint16_t* kt, f32x16_t (&sacc)[2]) __attribute__((always_inline)) {
+    FA_SETPRIO(1);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      *(u32x4_t*)&sK[buf][(lg * KPT + i) * KSTR + 8 * lc] = kr[i];
-      *(u32x4_t*)&sV[buf][(lg * KPT + i) * VSTR + 8 * lc] = vr[i];
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, *(const u32x4_t*)(kt + tile_off<D>(32 * j + r, 2 * ks + h2)));
+        sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? f32x16_t{} : sacc[j],
+                                                          0, 0, 0);
+      }
     }
+    FA_SETPRIO(0);
   };
 
   f32x16_t oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16_t{};
-  // m_run: running max (log2 units). l_run: row sum of the bf16-rounded P that
+  // m_run: running max (score units). l_run: row sum of the bf16-rounded P that
   // feeds the PV product (normalises O). l_exact: row sum of the unrounded P
   // (gives the log-sum-exp).
   float m_run = kNegInf, l_run = 0.0f, l_exact = 0.0f;
 
-  const int j_first = (wg.lo / kBN) * kBN;
-  const int ntiles = (wg.hi - j_first + kBN - 1) / kBN;
+  const int gl = lane & 15, sub = (lane >> 4) & 1;
 
-  load_tile(j_first);
-  store_tile(0);
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int j0 = j_first + it * kBN;
-    const int buf = it & 1;
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(j0 + kBN);
-
-    if (wave_live && j0 < wk.hi && j0 + kBN > wk.lo) {
-      // ---- S^T = K Q^T for 64 keys (two 32-key blocks)
-      f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
-      const uint16_t* kb = &sK[buf][r * KSTR + 8 * h2];
+  // ---- softmax of tile j0 (scores in sacc) and O^T += V^T P^T.
+  // MASKED: the tile crosses some row's key range boundary, so scores are
+  // masked element by element; full tiles skip that code entirely.
+  auto softmax_pv = [&](auto masked, const f32x16_t (&sacc)[2], const uint16_t* vt, int j0)
+                        __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    float t[2][16];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kb + 32 * j * KSTR + 16 * ks));
-          sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[j], 0, 0, 0);
-        }
-      }
-      float t[2][16];
+      for (int v = 0; v < 16; ++v) t[j][v] = sacc[j][v];
+    const float rel = (float)(row + off) - (float)(j0 + 4 * h2);
+    transform_scores<2, SOFTCAP, ALIBI>(t, p, slope_log2, rel, MASKED, j0, rk.lo, rk.hi, h2);
+    bool any_rescale;
+    float mc;
+    const float alpha = online_max<2>(t, c, m_run, l_run, any_rescale, mc, 0.0f);
+    l_exact *= alpha;
+    if (any_rescale) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) t[j][v] = sacc[j][v];
-
-      const bool full = j0 >= wk.flo && j0 + kBN <= wk.fhi;
-      const float rel = (float)(row + off) - (float)(j0 + 4 * h2);
-      transform_scores<2, SOFTCAP, ALIBI>(t, p, slope_log2, rel, !full, j0, rk.lo, rk.hi, h2);
-
-      bool any_rescale;
-      float base;
-      const float alpha = online_max<2>(t, m_run, l_run, any_rescale, base, 0.0f);
-      l_exact *= alpha;
-      if (any_rescale) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      }
-
-      // ---- P (bf16, rounded to nearest even) and its row sum
-      bf16x8_t pf[4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        f32x8_t x;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          x[e] = fast_exp2(t[tt >> 1][(tt & 1) * 8 + e] - base);
-          l_exact += x[e];
-        }
-        pf[tt] = __builtin_convertvector(x, bf16x8_t);
-        l_run = sum_bf16x8(pf[tt], l_run);
-      }
-
-      // ---- O^T += V^T P^T: k-step tt covers keys 16*tt .. 16*tt+15. The A operand
-      // (lane: d-row m = lane % 32, keys 16tt + 4*h2 + {0..3, 8..11}) comes from two
-      // transposed reads: in each 16-lane group, lanes 4k..4k+3 address the four
-      // 4-column chunks of key k, and lane i receives column i of those 4 keys.
-      const int gl = lane & 15, sub = (lane >> 4) & 1;
-      const uint16_t* vb = &sV[buf][(4 * h2 + (gl >> 2)) * VSTR + 16 * sub + 4 * (gl & 3)];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const uint16_t* vp = vb + 16 * tt * VSTR + 32 * db;
-          const s16x4_t lo = ds_read_tr16(vp);
-          const s16x4_t hi = ds_read_tr16(vp + 8 * VSTR);
-          const s16x8_t x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x), pf[tt],
-                                                             oacc[db], 0, 0, 0);
-        }
-      }
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
 
-    if (has_next) store_tile(buf ^ 1);
+    // P (bf16, rounded to nearest even) and its row sums.
+    bf16x8_t pf[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f32x8_t x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = fast_exp2(__builtin_fmaf(t[tt >> 1][(tt & 1) * 8 + e], c, -mc));
+        l_exact += x[e];
+      }
+      pf[tt] = __builtin_convertvector(x, bf16x8_t);
+      l_run = sum_bf16x8(pf[tt], l_run);
+    }
+
+    // k-step tt covers keys 16*tt .. 16*tt+15. The A operand (lane: d-row
+    // m = lane % 32, keys 16tt + 4*h2 + {0..3, 8..11}) comes from two transposed
+    // reads: in each 16-lane group, lanes 4k..4k+3 address the four 4-column
+    // pieces of key k, and lane i receives column i of those 4 keys.
+    FA_SETPRIO(1);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int vrow = 16 * tt + 4 * h2 + (gl >> 2);
+        const int col = 32 * db + 16 * sub + 4 * (gl & 3);
+        const s16x4_t lo = ds_read_tr16(vt + tile_off<D>(vrow, col >> 3) + (col & 7));
+        const s16x4_t hi = ds_read_tr16(vt + tile_off<D>(vrow + 8, col >> 3) + (col & 7));
+        const s16x8_t x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x), pf[tt],
+                                                           oacc[db], 0, 0, 0);
+      }
+    }
+    FA_SETPRIO(0);
+  };
+
+  auto live = [&](int j0) __attribute__((always_inline)) { return wave_live && j0 < wk.hi && j0 + kBN > wk.lo; };
+
+  // ---- prologue: K(0), V(0) resident.
+  copy_tiles(sK0, sV0, j_first);
+  wait_vmem();
+  __syncthreads();
+
+  // ---- step t: copy K(t+1), V(t+1) into buffers (t+1)&1 (free since the
+  // barrier that ended step t-1), then S(t), softmax(t), PV(t) from buffers t&1.
+  f32x16_t sacc[2];
+  auto step = [&](auto par, int it) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(par)::value;
+    const uint16_t* k_cur = ODD ? sK1 : sK0;
+    const uint16_t* v_cur = ODD ? sV1 : sV0;
+    uint16_t* k_nxt = ODD ? sK0 : sK1;
+    uint16_t* v_nxt = ODD ? sV0 : sV1;
+    const int j0 = j_first + it * kBN;
+    if (it + 1 < ntiles) copy_tiles(k_nxt, v_nxt, j0 + kBN);
+    if (live(j0)) {
+      qk(k_cur, sacc);
+      if (j0 >= wk.flo && j0 + kBN <= wk.fhi)
+        softmax_pv(std::false_type{}, sacc, v_cur, j0);
+      else
+        softmax_pv(std::true_type{}, sacc, v_cur, j0);
+    }
+    wait_vmem();
     __syncthreads();
+  };
+
+  for (int it = 0; it < ntiles; it += 2) {
+    step(std::false_type{}, it);
+    if (it + 1 < ntiles) step(std::true_type{}, it + 1);
   }
 
-  // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2
+  // ---- epilogue: O = O / l, LSE = (c m + log2 l) ln 2
   if (!wave_live) return;
-  const float l_tot = l_run + other_half(l_run);
-  const float l_ex = l_exact + other_half(l_exact);
+  const float l_tot = half_sum(l_run);
+  const float l_ex = half_sum(l_exact);
   if (row >= p.Nq) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse = l_ex > 0.0f ? (m_run + __log2f(l_ex)) * kLn2 : kNegInf;
+  const float lse = l_ex > 0.0f ? (m_run * c + __log2f(l_ex)) * kLn2 : kNegInf;
   if constexpr (PAGED) {
     const int64_t ro = (((int64_t)s * p.B + b) * p.H + h) * p.Nq + row;
     float* op = p.o_part + ro * D;

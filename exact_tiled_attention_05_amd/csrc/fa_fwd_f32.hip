@@ -45,6 +45,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
 
   float slope_log2 = 0.0f;
   if constexpr (ALIBI) slope_log2 = p.alibi[h] * kLog2e;
+  const float c = exponent_scale<SOFTCAP, ALIBI>(p);
 
   float qf[D / 2];
   {
@@ -92,8 +93,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
     transform_scores<1, SOFTCAP, ALIBI>(t, p, slope_log2, rel, !full, j0, rk.lo, rk.hi, h2);
 
     bool any_rescale;
-    float base;
-    const float alpha = online_max<1>(t, m_run, l_run, any_rescale, base, kLazyRescaleThreshold);
+    float mc;
+    const float alpha =
+        online_max<1>(t, c, m_run, l_run, any_rescale, mc, kLazyRescaleThreshold / c);
     if (any_rescale) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
     float pr[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      pr[v] = fast_exp2(t[0][v] - base);
+      pr[v] = fast_exp2(__builtin_fmaf(t[0][v], c, -mc));
       l_run += pr[v];
     }
     // k-step v pairs this lane's slot v (key acc_key(v, h2)) with V row of that key.
@@ -114,10 +116,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
     }
   }
 
-  const float l_tot = l_run + other_half(l_run);
+  const float l_tot = half_sum(l_run);
   if (row >= p.Nq) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+  const float lse = l_tot > 0.0f ? (m_run * c + __log2f(l_tot)) * kLn2 : kNegInf;
   if constexpr (PAGED) {
     const int64_t ro = (((int64_t)s * p.B + b) * p.H + h) * p.Nq + row;
     float* op = p.o_part + ro * D;
