@@ -23,6 +23,37 @@ import numpy as np
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "exact_tiled_attention_05_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# Source files each measured kernel is built from (a change voids its counters).
+KERNEL_SOURCES = {
+    "prefill": ["fa_fwd_bf16.hip", "fa_device.h", "fa_params.h"],
+    "decode_split": ["fa_decode_bf16.hip", "fa_device.h", "fa_params.h"],
+}
+
+
+def source_hash(kind):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind):
+    """HBM bytes per launch from the committed rocprofv3 counters, or None when the
+    kernel's sources changed since they were taken (or none were taken)."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)[kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha256") != source_hash(kind):
+        return None
+    return int(round((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024))
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -49,7 +80,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--print-source-hashes", action="store_true")
     args = ap.parse_args()
+    if args.print_source_hashes:
+        print(json.dumps({k: source_hash(k) for k in KERNEL_SOURCES}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the kernels run on one device's share of the work).", file=sys.stderr)
@@ -62,6 +99,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        x = torch.ones(1 << 28, device=dev)  # 1 GiB of fp32
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print("copied 3 x 1 GiB", flush=True)
+        return
     fa.load_library()
 
     def up(x, dtype):
@@ -80,6 +125,7 @@ def main():
     plse = torch.empty((wp.B, wp.H, wp.Nq), dtype=torch.float32, device=dev)
     pairs = allowed_pairs(wp.Nq, wp.Nk, True, -1, -1)
     prefill_flops = 4.0 * wp.B * wp.H * wp.d * pairs
+    prefill_bytes = 3 * pq.numel() * 2 + po.numel() * 4 + plse.numel() * 4
 
     # ---- decode inputs
     wd = W.WORKLOADS[4]
@@ -190,10 +236,12 @@ def main():
                    "pct_peak": round(100 * dec_gbs / PEAK_HBM_GBS, 2),
                    "roofline": {"bound": "hbm", "achieved": round(split_gbs, 2), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
-                                "traffic": None}},
+                                "traffic": measured_traffic("decode_split"),
+                                "algorithmic_bytes": int(split_bytes)}},
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic("prefill"),
+                     "algorithmic_bytes": int(prefill_bytes), "kernel": "fwd_bf16_kernel<128>"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
