@@ -169,7 +169,12 @@ def test_bf16_output_is_rounded_fp32_output():
     o32, l32 = run_fwd(q, k, v, "bf16", 0.09, True, -1, -1, None, 0.0)
     o16, l16 = run_fwd(q, k, v, "bf16", 0.09, True, -1, -1, None, 0.0, out_dtype=torch.bfloat16)
     want = torch.from_numpy(o32).to(torch.bfloat16).float().numpy()
-    assert np.array_equal(o16, want) and np.array_equal(l16, l32)
+    bad = np.argwhere(o16 != want)
+    assert len(bad) == 0, (f"{len(bad)} of {o16.size} bf16 outputs differ from the rounded fp32 "
+                           f"output; first {bad[:4].tolist()}: {o16[tuple(bad[0])]} vs "
+                           f"{want[tuple(bad[0])]} (fp32 {o32[tuple(bad[0])]!r})")
+    badl = np.argwhere(l16 != l32)
+    assert len(badl) == 0, f"{len(badl)} LSE values differ; first {badl[:4].tolist()}"
 
 
 def test_determinism_bitwise():
@@ -240,3 +245,4 @@ def test_combine_matches_oracle_on_random_partials():
     torch.cuda.synchronize()
     ro, rl = O.combine_ref(op, lp)        # [B, H, nq, d]
     check(o.cpu().numpy().transpose(0, 2, 1, 3), lse.cpu().numpy(), ro, rl, "fp32", "combine")
+
