@@ -156,11 +156,13 @@ template <int NB>
 __device__ __forceinline__ float online_max(const float (&t)[NB][16], float c, float& m_run,
                                             float& l_run, bool& any_rescale, float& mc,
                                             float threshold) {
-  float mt = kNegInf;
+  // Four independent partial maxima keep the dependent chain short.
+  float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
   for (int j = 0; j < NB; ++j)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mt = fmaxf(mt, t[j][v]);
+    for (int v = 0; v < 16; ++v) m4[v & 3] = fmaxf(m4[v & 3], t[j][v]);
+  float mt = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
   mt = half_max(mt);
   const float m_new = fmaxf(m_run, mt);
   const bool need = m_new > m_run + threshold;

@@ -7,12 +7,16 @@
 //   score transform, mask, online softmax in VGPRs (row = lane pair l, l^32)
 //   O^T += V^T P^T  on v_mfma_f32_32x32x16_bf16 (V read transposed from LDS
 //                   with ds_read_b64_tr_b16, P from VGPRs)
-// K and V tiles travel HBM -> LDS with global_load_lds_dwordx4 (no staging
-// registers) into two buffers each, in their natural [key][d] layout with the
-// 16-byte chunks of each row XOR-swizzled so that both the K operand reads and
-// the transposed V reads are free of bank conflicts; the copies of tile t+1
-// are in flight while tile t is computed. Tiles inside every row's key range
-// take a path with no per-element mask.
+// K and V tiles travel HBM -> LDS with loads that write LDS directly (no
+// staging registers) into two buffers each, in their natural [key][d] layout
+// with the 16-byte chunks of each row XOR-swizzled so that both the K operand
+// reads and the transposed V reads are free of bank conflicts; the copies of
+// tile t+1 are in flight while tile t is computed. Contiguous K/V use buffer
+// loads whose descriptor moves by whole tiles (scalar arithmetic only) and
+// whose range check turns keys past the end into zero rows; paged K/V gather
+// rows through the block table with global loads. Inside a tile the LDS reads
+// run several MFMAs ahead of their use (pinned with scheduling groups). Tiles
+// inside every row's key range take a path with no per-element mask.
 // (Tiled IO-aware forward with online softmax: "IO感知技术革命: FlashAttention如何
 // 重塑大模型训练的经济学", sections on block tiling, online softmax and overlap of
 // copies with compute; mask and score variants: flash-attn v2.0-v2.7 update
@@ -43,16 +47,30 @@ struct Tuning {
   static constexpr int kWaves = D == 128 ? FA_WAVES_D128 : FA_WAVES_D64;
 };
 
-// MFMA issue runs at raised wave priority so the matrix pipe is refilled
-// promptly while the other wavefront on the SIMD works through its softmax.
-#ifndef FA_NO_SETPRIO
-#define FA_SETPRIO(x) __builtin_amdgcn_s_setprio(x)
-#else
-#define FA_SETPRIO(x)
-#endif
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// LDS reads issued ahead of the MFMA that consumes them: K fragments in the
+// score product, transposed V reads (in MFMAs) in the PV product.
+constexpr int kQkReadAhead = 6;
+constexpr int kPvReadAhead = 4;
+
+// Word 3 of a raw (unswizzled, stride 0) buffer descriptor on gfx9 parts:
+// 32-bit data format, range-checked against num_records.
+constexpr int kBufferFlags = 0x00020000;
+
+// (The buffer builtins sit in plain device functions: called from a lambda in
+// the kernel they stop the host pass from emitting the kernel's launch stub.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int num_records) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, num_records, kBufferFlags);
+}
+
+// 16 bytes per lane from `rsrc` at byte offset `voffset` into LDS at
+// lds_base + 16 * lane; lanes past num_records write zeros.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds_base,
+                                                  unsigned voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)lds_base, 16, voffset, 0, 0, 0);
+}
 
 // Chunk swizzle of an LDS tile row: logical 16-byte chunk c of row r lives at
 // physical chunk c ^ swz(r). For head_dim 128 (16 chunks per 256-byte row) the
@@ -92,10 +110,6 @@ void fwd_bf16_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sK1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sV0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sV1[TILE];
-#ifdef FA_DIAG_LDS_PAD
-  __shared__ uint16_t diag_pad[48 * 1024];  // occupancy experiment: one workgroup per CU
-  if (p.B < 0) diag_pad[threadIdx.x] = 0;
-#endif
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
@@ -146,25 +160,56 @@ void fwd_bf16_kernel(FwdParams p) {
   // fills tile rows [ROWS_PER_LOAD * (LOADS*w + i), +ROWS_PER_LOAD); lane L
   // writes physical chunk L % CPR of its row, i.e. logical chunk
   // (L % CPR) ^ swz(row). K and V share the layout, hence one offset per copy.
-  // Keys past the end re-read the last key (finite data; masked later).
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  // Contiguous K/V: per-(batch, head) buffer descriptors rebased on the tile's
+  // first key and bounded by the end of the last key, so rows past the end
+  // arrive as zeros; the per-lane byte offsets are fixed.
+  const int64_t row_bytes = 2 * (int64_t)p.H * D;
+  const int64_t bh_bytes = 2 * (((int64_t)b * p.Nk * p.H + h) * D);
+  const int64_t end_bytes = (int64_t)(p.Nk - 1) * row_bytes + 2 * D;
+  const char* kbh = (const char*)p.k + bh_bytes;
+  const char* vbh = (const char*)p.v + bh_bytes;
+  unsigned lane_bytes[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int trow = ROWS_PER_LOAD * (LOADS * wu + i) + lane / CPR;
+    const int chunk = (lane % CPR) ^ swz<D>(trow);
+    lane_bytes[i] = (unsigned)(trow * row_bytes + 16 * chunk);
+  }
+  // Paged K/V: rows past the end re-read the last key (finite data; masked later).
   const uint16_t* kg = (const uint16_t*)p.k;
   const uint16_t* vg = (const uint16_t*)p.v;
   auto copy_tiles = [&](uint16_t* kdst, uint16_t* vdst, int j0) __attribute__((always_inline)) {
+    if constexpr (!PAGED) {
+      const int64_t tb = (int64_t)j0 * row_bytes;
+      const int64_t left = end_bytes - tb;
+      const int n = left <= 0 ? 0 : (left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbh + tb, n);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbh + tb, n);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int ld = LOADS * w + i;
-      const int trow = ROWS_PER_LOAD * ld + lane / CPR;
-      const int chunk = (lane % CPR) ^ swz<D>(trow);
-      const int key = min(j0 + trow, p.Nk - 1);
-      const int64_t o = kv_offset<PAGED>(p, b, key, h, D) + 8 * chunk;
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(kg + o), (lds_ptr_t)(kdst + 512 * ld), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(vg + o), (lds_ptr_t)(vdst + 512 * ld), 16, 0, 0);
+      for (int i = 0; i < LOADS; ++i) {
+        const int ld = LOADS * wu + i;
+        buffer_load_lds16(rk, kdst + 512 * ld, lane_bytes[i]);
+        buffer_load_lds16(rv, vdst + 512 * ld, lane_bytes[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int ld = LOADS * wu + i;
+        const int trow = ROWS_PER_LOAD * ld + lane / CPR;
+        const int chunk = (lane % CPR) ^ swz<D>(trow);
+        const int key = min(j0 + trow, p.Nk - 1);
+        const int64_t o = kv_offset<PAGED>(p, b, key, h, D) + 8 * chunk;
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(kg + o), (lds_ptr_t)(kdst + 512 * ld), 16, 0,
+                                         0);
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(vg + o), (lds_ptr_t)(vdst + 512 * ld), 16, 0,
+                                         0);
+      }
     }
   };
 
   // ---- S^T = K Q^T for one 64-key tile (two 32-key blocks).
   auto qk = [&](const uint16_t* kt, f32x16_t (&sacc)[2]) __attribute__((always_inline)) {
-    FA_SETPRIO(1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -175,7 +220,15 @@ void fwd_bf16_kernel(FwdParams p) {
                                                           0, 0, 0);
       }
     }
-    FA_SETPRIO(0);
+    // Schedule: kQkReadAhead K reads, then alternate one MFMA and one read.
+    static_assert(kQkReadAhead <= 2 * KS, "read-ahead");
+    __builtin_amdgcn_sched_group_barrier(0x100, kQkReadAhead, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < 2 * KS - kQkReadAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kQkReadAhead, 0);
   };
 
   f32x16_t oacc[NDB];
@@ -210,25 +263,28 @@ void fwd_bf16_kernel(FwdParams p) {
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
 
-    // P (bf16, rounded to nearest even) and its row sums.
+    // P (bf16, rounded to nearest even) and its row sums, each summed in
+    // independent partials (short dependency chains).
     bf16x8_t pf[4];
+    float le[4] = {0.0f, 0.0f, 0.0f, 0.0f}, lr[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       f32x8_t x;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         x[e] = fast_exp2(__builtin_fmaf(t[tt >> 1][(tt & 1) * 8 + e], c, -mc));
-        l_exact += x[e];
+        le[e & 3] += x[e];
       }
       pf[tt] = __builtin_convertvector(x, bf16x8_t);
-      l_run = sum_bf16x8(pf[tt], l_run);
+      lr[tt & 1] = sum_bf16x8(pf[tt], lr[tt & 1]);
     }
+    l_exact += (le[0] + le[1]) + (le[2] + le[3]);
+    l_run += lr[0] + lr[1];
 
     // k-step tt covers keys 16*tt .. 16*tt+15. The A operand (lane: d-row
     // m = lane % 32, keys 16tt + 4*h2 + {0..3, 8..11}) comes from two transposed
     // reads: in each 16-lane group, lanes 4k..4k+3 address the four 4-column
     // pieces of key k, and lane i receives column i of those 4 keys.
-    FA_SETPRIO(1);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
@@ -242,7 +298,16 @@ void fwd_bf16_kernel(FwdParams p) {
                                                            oacc[db], 0, 0, 0);
       }
     }
-    FA_SETPRIO(0);
+    // Schedule: the reads of kPvReadAhead MFMAs first, then one MFMA and the
+    // two reads of a later one, alternately.
+    static_assert(kPvReadAhead <= 4 * NDB, "read-ahead");
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvReadAhead, 1);  // DS reads
+#pragma unroll
+    for (int i = 0; i < 4 * NDB - kPvReadAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kPvReadAhead, 1);
   };
 
   auto live = [&](int j0) __attribute__((always_inline)) { return wave_live && j0 < wk.hi && j0 + kBN > wk.lo; };
