@@ -8,15 +8,18 @@
 //   O^T += V^T P^T  on v_mfma_f32_32x32x16_bf16 (V read transposed from LDS
 //                   with ds_read_b64_tr_b16, P from VGPRs)
 // K and V tiles travel HBM -> LDS with loads that write LDS directly (no
-// staging registers) into two buffers each, in their natural [key][d] layout
-// with the 16-byte chunks of each row XOR-swizzled so that both the K operand
-// reads and the transposed V reads are free of bank conflicts; the copies of
-// tile t+1 are in flight while tile t is computed. Contiguous K/V use buffer
+// staging registers), in their natural [key][d] layout with the 16-byte chunks
+// of each row XOR-swizzled so that both the K operand reads and the
+// transposed V reads are free of bank conflicts. Contiguous K/V use buffer
 // loads whose descriptor moves by whole tiles (scalar arithmetic only) and
-// whose range check turns keys past the end into zero rows; paged K/V gather
-// rows through the block table with global loads. Inside a tile the LDS reads
-// run several MFMAs ahead of their use (pinned with scheduling groups). Tiles
-// inside every row's key range take a path with no per-element mask.
+// whose range check turns keys past the end into zero rows; K sits in a
+// three-stage ring and V in two buffers, so step t copies V(t+1) as it starts
+// and K(t+2) after its score MFMAs (spreading the copies of a step over time)
+// and ends with K(t+2) still in flight. Paged K/V gather rows through the
+// block table with global loads into two buffers each. Inside a tile the LDS
+// reads run several MFMAs ahead of their use (pinned with scheduling groups).
+// Tiles inside every row's key range take a path with no per-element mask.
+// A workgroup uses 80 KiB of LDS at head_dim 128, so two fit on a CU.
 // (Tiled IO-aware forward with online softmax: "IO感知技术革命: FlashAttention如何
 // 重塑大模型训练的经济学", sections on block tiling, online softmax and overlap of
 // copies with compute; mask and score variants: flash-attn v2.0-v2.7 update
@@ -35,25 +38,17 @@ constexpr int kBM = BF16_BM;   // query rows per workgroup
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 256;  // 4 wavefronts
 
-// Wavefronts per SIMD the register budget is sized for, per head_dim.
-#ifndef FA_WAVES_D128
-#define FA_WAVES_D128 2
-#endif
-#ifndef FA_WAVES_D64
-#define FA_WAVES_D64 3
-#endif
-template <int D>
+// Wavefronts per SIMD the register budget is sized for: two at head_dim 128
+// (and for the tanh cap at 64, whose transform needs the extra registers),
+// three otherwise.
+template <int D, bool SOFTCAP>
 struct Tuning {
-  static constexpr int kWaves = D == 128 ? FA_WAVES_D128 : FA_WAVES_D64;
+  static constexpr int kWaves = (D == 128 || SOFTCAP) ? 2 : 3;
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 
-// LDS reads issued ahead of the MFMA that consumes them: K fragments in the
-// score product, transposed V reads (in MFMAs) in the PV product.
-constexpr int kQkReadAhead = 6;
-constexpr int kPvReadAhead = 4;
 
 // Word 3 of a raw (unswizzled, stride 0) buffer descriptor on gfx9 parts:
 // 32-bit data format, range-checked against num_records.
@@ -90,6 +85,16 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
   return row * D + 8 * (chunk ^ swz<D>(row));
 }
 
+// Wait until at most N vector-memory operations of this wavefront are in
+// flight, then meet the other wavefronts. Copies complete in issue order, so N
+// = the copies issued last stay in flight. (A plain __syncthreads() would wait
+// for all of them.) The memory clobber keeps LDS accesses on their side.
+template <int N>
+__device__ __forceinline__ void wait_vmem_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ void wait_vmem() {
   // vmcnt(0), leaving the LDS/export counters unconstrained.
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -97,7 +102,7 @@ __device__ __forceinline__ void wait_vmem() {
 
 template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(Tuning<D>::kWaves, Tuning<D>::kWaves)))
+__attribute__((amdgpu_waves_per_eu(Tuning<D, SOFTCAP>::kWaves, Tuning<D, SOFTCAP>::kWaves)))
 void fwd_bf16_kernel(FwdParams p) {
   constexpr int KS = D / 16;                 // MFMA k-steps of Q K^T
   constexpr int NDB = D / 32;                // 32-row blocks of O^T
@@ -105,11 +110,17 @@ void fwd_bf16_kernel(FwdParams p) {
   constexpr int ROWS_PER_LOAD = 64 / CPR;    // rows one wavefront-wide LDS copy fills
   constexpr int LOADS = kBN / ROWS_PER_LOAD / 4;  // copies per wavefront per tensor per tile
   constexpr int TILE = kBN * D;              // elements per tile
+  // LDS reads issued ahead of the MFMA that consumes them: K fragments in the
+  // score product, transposed V reads (in MFMAs) in the PV product. The score
+  // transforms need registers, so their PV product reads less far ahead.
+  constexpr int kQkReadAhead = 8 < 2 * KS ? 8 : 2 * KS;
+  constexpr int kPvReadAhead = (SOFTCAP || ALIBI) ? 4 : 6;
 
   __shared__ __attribute__((aligned(1024))) uint16_t sK0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sK1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sV0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sV1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK2[TILE];  // third K stage (contiguous K/V)
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
@@ -179,19 +190,18 @@ void fwd_bf16_kernel(FwdParams p) {
   // Paged K/V: rows past the end re-read the last key (finite data; masked later).
   const uint16_t* kg = (const uint16_t*)p.k;
   const uint16_t* vg = (const uint16_t*)p.v;
+  auto copy_one = [&](const char* bh, uint16_t* dst, int j0) __attribute__((always_inline)) {
+    const int64_t tb = (int64_t)j0 * row_bytes;
+    const int64_t left = end_bytes - tb;
+    const int n = left <= 0 ? 0 : (left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(bh + tb, n);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) buffer_load_lds16(rs, dst + 512 * (LOADS * wu + i), lane_bytes[i]);
+  };
   auto copy_tiles = [&](uint16_t* kdst, uint16_t* vdst, int j0) __attribute__((always_inline)) {
     if constexpr (!PAGED) {
-      const int64_t tb = (int64_t)j0 * row_bytes;
-      const int64_t left = end_bytes - tb;
-      const int n = left <= 0 ? 0 : (left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbh + tb, n);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbh + tb, n);
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int ld = LOADS * wu + i;
-        buffer_load_lds16(rk, kdst + 512 * ld, lane_bytes[i]);
-        buffer_load_lds16(rv, vdst + 512 * ld, lane_bytes[i]);
-      }
+      copy_one(kbh, kdst, j0);
+      copy_one(vbh, vdst, j0);
     } else {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
@@ -312,36 +322,81 @@ void fwd_bf16_kernel(FwdParams p) {
 
   auto live = [&](int j0) __attribute__((always_inline)) { return wave_live && j0 < wk.hi && j0 + kBN > wk.lo; };
 
-  // ---- prologue: K(0), V(0) resident.
-  copy_tiles(sK0, sV0, j_first);
-  wait_vmem();
-  __syncthreads();
-
-  // ---- step t: copy K(t+1), V(t+1) into buffers (t+1)&1 (free since the
-  // barrier that ended step t-1), then S(t), softmax(t), PV(t) from buffers t&1.
-  f32x16_t sacc[2];
-  auto step = [&](auto par, int it) __attribute__((always_inline)) {
-    constexpr bool ODD = decltype(par)::value;
-    const uint16_t* k_cur = ODD ? sK1 : sK0;
-    const uint16_t* v_cur = ODD ? sV1 : sV0;
-    uint16_t* k_nxt = ODD ? sK0 : sK1;
-    uint16_t* v_nxt = ODD ? sV0 : sV1;
-    const int j0 = j_first + it * kBN;
-    if (it + 1 < ntiles) copy_tiles(k_nxt, v_nxt, j0 + kBN);
-    if (live(j0)) {
-      qk(k_cur, sacc);
-      if (j0 >= wk.flo && j0 + kBN <= wk.fhi)
-        softmax_pv(std::false_type{}, sacc, v_cur, j0);
-      else
-        softmax_pv(std::true_type{}, sacc, v_cur, j0);
+  if constexpr (!PAGED) {
+    // ---- contiguous K/V: K(t) in stage t % 3, V(t) in buffer t & 1. Step t
+    // copies V(t+1) over V(t-1) and K(t+2) over K(t-1) (both last read in step
+    // t-1, ended by a barrier), computes tile t, then waits for all but the
+    // K(t+2) copies. Copies past the key range read nothing and write zeros.
+    constexpr int kKC = LOADS;  // vector-memory ops of one K tile copy
+    copy_one(kbh, sK0, j_first);
+    copy_one(vbh, sV0, j_first);
+    copy_one(kbh, sK1, j_first + kBN);
+    wait_vmem_barrier<kKC>();
+    f32x16_t sacc[2];
+    auto step3 = [&](auto kst, auto vpar, int it) __attribute__((always_inline)) {
+      constexpr int KSt = decltype(kst)::value;
+      constexpr bool VODD = decltype(vpar)::value;
+      const uint16_t* k_cur = KSt == 0 ? sK0 : KSt == 1 ? sK1 : sK2;
+      uint16_t* k_nn = KSt == 0 ? sK2 : KSt == 1 ? sK0 : sK1;
+      const uint16_t* v_cur = VODD ? sV1 : sV0;
+      uint16_t* v_nxt = VODD ? sV0 : sV1;
+      const int j0 = j_first + it * kBN;
+      copy_one(vbh, v_nxt, j0 + kBN);
+      const bool lv = live(j0);
+      if (lv) qk(k_cur, sacc);
+      copy_one(kbh, k_nn, j0 + 2 * kBN);
+      if (lv) {
+        if (j0 >= wk.flo && j0 + kBN <= wk.fhi)
+          softmax_pv(std::false_type{}, sacc, v_cur, j0);
+        else
+          softmax_pv(std::true_type{}, sacc, v_cur, j0);
+      }
+      wait_vmem_barrier<kKC>();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    for (int it = 0; it < ntiles; it += 6) {
+      step3(I0{}, std::false_type{}, it);
+      if (it + 1 < ntiles) step3(I1{}, std::true_type{}, it + 1);
+      if (it + 2 < ntiles) step3(I2{}, std::false_type{}, it + 2);
+      if (it + 3 < ntiles) step3(I0{}, std::true_type{}, it + 3);
+      if (it + 4 < ntiles) step3(I1{}, std::false_type{}, it + 4);
+      if (it + 5 < ntiles) step3(I2{}, std::true_type{}, it + 5);
     }
+    wait_vmem_barrier<0>();  // no copy may still be writing LDS at exit
+  } else {
+    // ---- paged K/V: two buffers each; step t copies tile t+1 and waits for it.
+    copy_tiles(sK0, sV0, j_first);
     wait_vmem();
     __syncthreads();
-  };
 
-  for (int it = 0; it < ntiles; it += 2) {
-    step(std::false_type{}, it);
-    if (it + 1 < ntiles) step(std::true_type{}, it + 1);
+    // Step t: copy K(t+1), V(t+1) into buffers (t+1)&1 (free since the
+    // barrier that ended step t-1), then S(t), softmax(t), PV(t) from buffers t&1.
+    f32x16_t sacc[2];
+    auto step = [&](auto par, int it) __attribute__((always_inline)) {
+      constexpr bool ODD = decltype(par)::value;
+      const uint16_t* k_cur = ODD ? sK1 : sK0;
+      const uint16_t* v_cur = ODD ? sV1 : sV0;
+      uint16_t* k_nxt = ODD ? sK0 : sK1;
+      uint16_t* v_nxt = ODD ? sV0 : sV1;
+      const int j0 = j_first + it * kBN;
+      if (it + 1 < ntiles) copy_tiles(k_nxt, v_nxt, j0 + kBN);
+      if (live(j0)) {
+        qk(k_cur, sacc);
+        if (j0 >= wk.flo && j0 + kBN <= wk.fhi)
+          softmax_pv(std::false_type{}, sacc, v_cur, j0);
+        else
+          softmax_pv(std::true_type{}, sacc, v_cur, j0);
+      }
+      wait_vmem();
+      __syncthreads();
+    };
+
+    for (int it = 0; it < ntiles; it += 2) {
+      step(std::false_type{}, it);
+      if (it + 1 < ntiles) step(std::true_type{}, it + 1);
+    }
   }
 
   // ---- epilogue: O = O / l, LSE = (c m + log2 l) ln 2
