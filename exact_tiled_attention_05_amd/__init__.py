@@ -20,8 +20,9 @@ import torch
 
 __all__ = [
     "FA_FP32", "FA_BF16", "FaError", "library_path", "load_library",
-    "fa_fwd", "fa_fwd_splitkv", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len",
-    "attention", "attention_paged_splitkv", "combine", "decode_paged",
+    "fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_splitkv_combine", "fa_status_string",
+    "fa_split_chunk_len", "attention", "attention_split", "attention_split_partials",
+    "attention_paged_splitkv", "combine", "decode_paged",
 ]
 
 FA_FP32, FA_BF16 = 0, 1
@@ -29,8 +30,8 @@ FA_OK = 0
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 _lib = None
 
-EXPORTED = ("fa_fwd", "fa_fwd_splitkv", "fa_splitkv_combine", "fa_status_string",
-            "fa_split_chunk_len")
+EXPORTED = ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_splitkv_combine",
+            "fa_status_string", "fa_split_chunk_len")
 
 
 class FaError(RuntimeError):
@@ -58,6 +59,8 @@ def load_library():
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, i, vp, i, i, vp, vp, i, i, i, i, i, i, f, i, i, i,
                                    vp, f, vp]
     lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_split.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, f, vp]
+    lib.fa_fwd_split.restype = i
     lib.fa_splitkv_combine.argtypes = [vp, vp, i, i, i, i, i, vp, i, vp, vp]
     lib.fa_splitkv_combine.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -137,6 +140,17 @@ def fa_fwd_splitkv(q, k_cache, v_cache, block_table, max_pages_per_seq, page_siz
         _ptr(alibi_slopes), float(softcap), _stream(stream))
 
 
+def fa_fwd_split(q, k, v, o_part, lse_part, num_splits, batch, heads, seqlen_q, seqlen_k,
+                 head_dim, softmax_scale, causal=False, window_left=-1, window_right=-1,
+                 alibi_slopes=None, softcap=0.0, stream=None) -> int:
+    """Call fa_fwd_split on caller-allocated tensors; returns the status code."""
+    return load_library().fa_fwd_split(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(o_part), _ptr(lse_part),
+        int(num_splits), int(batch), int(heads), int(seqlen_q), int(seqlen_k), int(head_dim),
+        float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
+        _ptr(alibi_slopes), float(softcap), _stream(stream))
+
+
 def fa_splitkv_combine(o_part, lse_part, num_splits, batch, heads, seqlen_q, head_dim, o, lse,
                        stream=None) -> int:
     """Call fa_splitkv_combine on caller-allocated tensors; returns the status code."""
@@ -192,6 +206,31 @@ def attention_paged_splitkv(q, k_cache, v_cache, block_table, seqlen_k, num_spli
                           causal, window_left, window_right, alibi_slopes, softcap, stream),
            "fa_fwd_splitkv")
     return o_part, lse_part
+
+
+def attention_split_partials(q, k, v, num_splits, softmax_scale=None, causal=False,
+                             window_left=-1, window_right=-1, alibi_slopes=None, softcap=0.0,
+                             stream=None):
+    """Split partials o_part [S,B,H,Nq,d] and lse_part [S,B,H,Nq] over contiguous K/V."""
+    _same_dtype(q, k, v)
+    B, nq, H, d = q.shape
+    nk = k.shape[1]
+    if tuple(k.shape) != (B, nk, H, d) or tuple(v.shape) != (B, nk, H, d):
+        raise ValueError("k and v must be [B, Nk, H, d] matching q")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    o_part = torch.empty((num_splits, B, H, nq, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((num_splits, B, H, nq), dtype=torch.float32, device=q.device)
+    _check(fa_fwd_split(q, k, v, o_part, lse_part, num_splits, B, H, nq, nk, d, softmax_scale,
+                        causal, window_left, window_right, alibi_slopes, softcap, stream),
+           "fa_fwd_split")
+    return o_part, lse_part
+
+
+def attention_split(q, k, v, num_splits, out_dtype=torch.float32, stream=None, **kw):
+    """fa_fwd_split followed by the combine kernel: the same result as attention()."""
+    o_part, lse_part = attention_split_partials(q, k, v, num_splits, stream=stream, **kw)
+    return combine(o_part, lse_part, out_dtype=out_dtype, stream=stream)
 
 
 def combine(o_part, lse_part, out_dtype=torch.float32, stream=None):

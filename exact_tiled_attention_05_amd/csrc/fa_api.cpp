@@ -15,19 +15,27 @@ constexpr int64_t kMaxGroups = (int64_t(1) << 31) - 1;
 
 using Launcher = int (*)(const fa::FwdParams&, void*);
 
+template <int MODE>
+Launcher pick_bf16(int head_dim, bool softcap, bool alibi) {
+#define FA_PICK(D)                                                      \
+  if (softcap && alibi) return &fa::launch_fwd_bf16<D, true, true, MODE>; \
+  if (softcap) return &fa::launch_fwd_bf16<D, true, false, MODE>;        \
+  if (alibi) return &fa::launch_fwd_bf16<D, false, true, MODE>;          \
+  return &fa::launch_fwd_bf16<D, false, false, MODE>;
+  if (head_dim == 64) { FA_PICK(64) }
+  FA_PICK(128)
+#undef FA_PICK
+}
+
 template <bool PAGED>
-Launcher pick(int in_dtype, int head_dim, bool softcap, bool alibi) {
-#define FA_PICK(FN, D)                                                         \
-  if (softcap && alibi) return &fa::FN<D, true, true, PAGED>;                  \
-  if (softcap) return &fa::FN<D, true, false, PAGED>;                          \
-  if (alibi) return &fa::FN<D, false, true, PAGED>;                            \
-  return &fa::FN<D, false, false, PAGED>;
-  if (in_dtype == FA_BF16) {
-    if (head_dim == 64) { FA_PICK(launch_fwd_bf16, 64) }
-    FA_PICK(launch_fwd_bf16, 128)
-  }
-  if (head_dim == 64) { FA_PICK(launch_fwd_f32, 64) }
-  FA_PICK(launch_fwd_f32, 128)
+Launcher pick_f32(int head_dim, bool softcap, bool alibi) {
+#define FA_PICK(D)                                                       \
+  if (softcap && alibi) return &fa::launch_fwd_f32<D, true, true, PAGED>;  \
+  if (softcap) return &fa::launch_fwd_f32<D, true, false, PAGED>;         \
+  if (alibi) return &fa::launch_fwd_f32<D, false, true, PAGED>;           \
+  return &fa::launch_fwd_f32<D, false, false, PAGED>;
+  if (head_dim == 64) { FA_PICK(64) }
+  FA_PICK(128)
 #undef FA_PICK
 }
 
@@ -146,7 +154,40 @@ int fa_fwd(const void* q, const void* k, const void* v, int in_dtype, void* o, i
   p.split_len = seqlen_k;
   if ((int64_t)p.num_q_tiles * heads * batch > kMaxGroups) return FA_ERR_SHAPE;
 
-  Launcher fn = pick<false>(in_dtype, head_dim, softcap > 0.0f, alibi_slopes != nullptr);
+  const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
+  Launcher fn = in_dtype == FA_BF16 ? pick_bf16<fa::FWD_CONTIG>(head_dim, sc, al)
+                                    : pick_f32<false>(head_dim, sc, al);
+  return fn(p, stream) ? FA_ERR_HIP : FA_OK;
+}
+
+int fa_fwd_split(const void* q, const void* k, const void* v, int in_dtype, float* o_part,
+                 float* lse_part, int num_splits, int batch, int heads, int seqlen_q,
+                 int seqlen_k, int head_dim, float softmax_scale, int causal, int window_left,
+                 int window_right, const float* alibi_slopes, float softcap, void* stream) {
+  if (!q || !k || !v || !o_part || !lse_part) return FA_ERR_NULL;
+  int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
+  if (st) return st;
+  if (num_splits <= 0 || num_splits > (1 << 16)) return FA_ERR_SHAPE;
+  if ((st = check_kind(in_dtype, head_dim))) return st;
+  if (in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
+    return st;
+
+  fa::FwdParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.num_splits = num_splits;
+  fill_common(p, batch, heads, seqlen_q, seqlen_k, softmax_scale, causal, window_left,
+              window_right, alibi_slopes, softcap, fa::BF16_BM);
+  const int64_t c = split_len(seqlen_k, num_splits, fa::SPLIT_ALIGN);
+  if (c > kMaxSeq) return FA_ERR_SHAPE;
+  p.split_len = (int)c;
+  if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
+
+  Launcher fn = pick_bf16<fa::FWD_CONTIG_SPLIT>(head_dim, softcap > 0.0f, alibi_slopes != nullptr);
   return fn(p, stream) ? FA_ERR_HIP : FA_OK;
 }
 
@@ -191,9 +232,10 @@ int fa_fwd_splitkv(const void* q, const void* k_cache, const void* v_cache, int 
   p.split_len = (int)c;
   if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
 
-  Launcher fn = (in_dtype == FA_BF16 && seqlen_q == 1)
-                    ? pick_decode(head_dim, softcap > 0.0f, alibi_slopes != nullptr)
-                    : pick<true>(in_dtype, head_dim, softcap > 0.0f, alibi_slopes != nullptr);
+  const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
+  Launcher fn = in_dtype != FA_BF16 ? pick_f32<true>(head_dim, sc, al)
+                : seqlen_q == 1     ? pick_decode(head_dim, sc, al)
+                                    : pick_bf16<fa::FWD_PAGED_SPLIT>(head_dim, sc, al);
   return fn(p, stream) ? FA_ERR_HIP : FA_OK;
 }
 

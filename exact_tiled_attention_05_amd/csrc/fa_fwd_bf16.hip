@@ -1,7 +1,7 @@
 // bf16 tiled attention forward for gfx950 (MI355X).
 //
 // One workgroup of 4 wavefronts owns a 128-row query tile of one (batch, head)
-// [and one key split when PAGED]. Each wavefront keeps its 32 query rows in
+// [and one key split in the split modes]. Each wavefront keeps its 32 query rows in
 // registers and walks the key range its rows can see in 64-key tiles:
 //   S^T = K Q^T     on v_mfma_f32_32x32x16_bf16 (K from LDS, Q from VGPRs)
 //   score transform, mask, online softmax in VGPRs (row = lane pair l, l^32)
@@ -100,10 +100,15 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
+// MODE: FWD_CONTIG (contiguous K/V -> O, LSE), FWD_CONTIG_SPLIT (contiguous K/V,
+// one key split per workgroup -> normalised partials) or FWD_PAGED_SPLIT (paged
+// K/V through the block table -> partials).
+template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Tuning<D, SOFTCAP>::kWaves, Tuning<D, SOFTCAP>::kWaves)))
 void fwd_bf16_kernel(FwdParams p) {
+  constexpr bool PAGED = MODE == FWD_PAGED_SPLIT;  // K/V rows gathered through the block table
+  constexpr bool SPLIT = MODE != FWD_CONTIG;       // one key split per workgroup, partial outputs
   constexpr int KS = D / 16;                 // MFMA k-steps of Q K^T
   constexpr int NDB = D / 32;                // 32-row blocks of O^T
   constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
@@ -124,18 +129,18 @@ void fwd_bf16_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
-  const WorkItem wi = decode_work<PAGED>(p);
+  const WorkItem wi = decode_work<SPLIT>(p);
   const int b = wi.b, h = wi.h, s = wi.s;
 
   const int off = p.Nk - p.Nq;
   int slo = 0, shi = p.Nk;
-  if constexpr (PAGED) split_range(p, s, slo, shi);
+  if constexpr (SPLIT) split_range(p, s, slo, shi);
 
   const int q0 = wi.qt * kBM;
   const int q1 = min(p.Nq, q0 + kBM);
   const KeyBounds wg = key_bounds(q0, q1, off, slo, shi, p.window_left, p.window_right);
   if (wg.hi <= wg.lo) {
-    write_empty_rows<PAGED>(p, b, h, s, q0, q1, D, tid, kThreads);
+    write_empty_rows<SPLIT>(p, b, h, s, q0, q1, D, tid, kThreads);
     return;
   }
 
@@ -406,7 +411,7 @@ void fwd_bf16_kernel(FwdParams p) {
   if (row >= p.Nq) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse = l_ex > 0.0f ? (m_run * c + __log2f(l_ex)) * kLn2 : kNegInf;
-  if constexpr (PAGED) {
+  if constexpr (SPLIT) {
     const int64_t ro = (((int64_t)s * p.B + b) * p.H + h) * p.Nq + row;
     float* op = p.o_part + ro * D;
 #pragma unroll
@@ -432,20 +437,23 @@ void fwd_bf16_kernel(FwdParams p) {
 
 }  // namespace
 
-template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
+template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 int launch_fwd_bf16(const FwdParams& p, void* stream) {
-  const int64_t groups = (int64_t)p.num_q_tiles * p.H * p.B * (PAGED ? p.num_splits : 1);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, SOFTCAP, ALIBI, PAGED>), dim3((unsigned)groups),
+  const int64_t groups =
+      (int64_t)p.num_q_tiles * p.H * p.B * (MODE != FWD_CONTIG ? p.num_splits : 1);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, SOFTCAP, ALIBI, MODE>), dim3((unsigned)groups),
                      dim3(kThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 
-#define FA_INST(D, SC, AL, PG) template int launch_fwd_bf16<D, SC, AL, PG>(const FwdParams&, void*);
-#define FA_INST_D(D)                                                                        \
-  FA_INST(D, false, false, false) FA_INST(D, false, true, false) FA_INST(D, true, false, false) \
-  FA_INST(D, true, true, false) FA_INST(D, false, false, true) FA_INST(D, false, true, true)     \
-  FA_INST(D, true, false, true) FA_INST(D, true, true, true)
+#define FA_INST(D, SC, AL, M) template int launch_fwd_bf16<D, SC, AL, M>(const FwdParams&, void*);
+#define FA_INST_M(D, M) \
+  FA_INST(D, false, false, M) FA_INST(D, false, true, M) FA_INST(D, true, false, M) FA_INST(D, true, true, M)
+#define FA_INST_D(D) FA_INST_M(D, FWD_CONTIG) FA_INST_M(D, FWD_CONTIG_SPLIT) FA_INST_M(D, FWD_PAGED_SPLIT)
 FA_INST_D(64)
 FA_INST_D(128)
+#undef FA_INST_D
+#undef FA_INST_M
+#undef FA_INST
 
 }  // namespace fa

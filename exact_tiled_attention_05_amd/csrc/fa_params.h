@@ -39,8 +39,15 @@ struct CombineParams {
   int o_bf16;
 };
 
+// Modes of the bf16 tiled forward.
+enum FwdMode {
+  FWD_CONTIG = 0,        // contiguous K/V, whole key range -> O, LSE
+  FWD_CONTIG_SPLIT = 1,  // contiguous K/V, one key split per workgroup -> o_part, lse_part
+  FWD_PAGED_SPLIT = 2,   // paged K/V through the block table, per split -> o_part, lse_part
+};
+
 // Launchers (defined in the .hip files). Return hipError_t as int.
-template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
+template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 int launch_fwd_bf16(const FwdParams& p, void* stream);
 template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
 int launch_fwd_f32(const FwdParams& p, void* stream);
@@ -51,6 +58,8 @@ int launch_combine(const CombineParams& p, void* stream);
 
 // Tile geometry the host needs for grid sizing.
 constexpr int BF16_BM = 128;
+// fa_fwd_split chunks are multiples of the key tile width.
+constexpr int SPLIT_ALIGN = 64;
 constexpr int F32_BM = 32;
 
 }  // namespace fa

@@ -116,6 +116,27 @@ int fa_fwd_splitkv(const void* q, const void* k_cache, const void* v_cache, int 
                    const float* alibi_slopes, float softcap, void* stream);
 
 /*
+ * fa_fwd_split - split-KV forward over contiguous K/V (the update article's
+ * v2.2 entry: splitting the key sequence when the query tiles alone leave the
+ * GPU idle, as with a short query set over a long key range).
+ *
+ * Same inputs as fa_fwd; bf16 only (FA_ERR_UNSUPPORTED for fp32). The keys
+ * [0, seqlen_k) are cut into num_splits chunks of C keys, C =
+ * ceil(seqlen_k / num_splits) rounded up to a multiple of 64 (the key tile;
+ * fa_split_chunk_len(seqlen_k, num_splits, 64) returns it); trailing chunks may
+ * be empty. Writes, per split s, o_part[s] [batch, heads, seqlen_q, head_dim]
+ * (normalised) and lse_part[s] [batch, heads, seqlen_q] exactly as
+ * fa_fwd_splitkv does; fa_splitkv_combine merges them. The caller owns the
+ * partial buffers (num_splits * batch * heads * seqlen_q * (head_dim + 1)
+ * floats); the library allocates nothing.
+ */
+int fa_fwd_split(const void* q, const void* k, const void* v, int in_dtype,
+                 float* o_part, float* lse_part, int num_splits,
+                 int batch, int heads, int seqlen_q, int seqlen_k, int head_dim,
+                 float softmax_scale, int causal, int window_left, int window_right,
+                 const float* alibi_slopes, float softcap, void* stream);
+
+/*
  * fa_splitkv_combine - the separate reduce step that merges split partials
  * (the update article's v2.2 entry): for every (b, h, i),
  *   L = ln(sum_s exp(lse_part[s])),  O = sum_s exp(lse_part[s] - L) * o_part[s].
@@ -131,7 +152,8 @@ int fa_splitkv_combine(const float* o_part, const float* lse_part, int num_split
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(int status);
 
-/* Split chunk length C used by fa_fwd_splitkv for these sizes, or -1 on bad sizes. */
+/* Split chunk length C used by fa_fwd_splitkv (page_size = the cache's page size)
+ * or fa_fwd_split (page_size = 64) for these sizes, or -1 on bad sizes. */
 int fa_split_chunk_len(int seqlen_k, int num_splits, int page_size);
 
 #ifdef __cplusplus

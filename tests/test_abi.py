@@ -27,9 +27,9 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
 
 
-def test_header_declares_the_three_calls():
+def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_splitkv", "fa_splitkv_combine", "fa_status_string"):
+    for n in ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_splitkv_combine", "fa_status_string"):
         assert n in names
 
 
@@ -87,6 +87,17 @@ def split(**kw):
         a["causal"], a["wl"], a["wr"], a["alibi"], a["softcap"], a["stream"])
 
 
+def fsplit(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, in_dtype=1, op=FAKE, lp=FAKE, S=4, batch=1, heads=1,
+             seqlen_q=8, seqlen_k=256, head_dim=128, scale=0.1, causal=1, wl=-1, wr=-1,
+             alibi=None, softcap=0.0, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_fwd_split(
+        a["q"], a["k"], a["v"], a["in_dtype"], a["op"], a["lp"], a["S"], a["batch"], a["heads"],
+        a["seqlen_q"], a["seqlen_k"], a["head_dim"], a["scale"], a["causal"], a["wl"], a["wr"],
+        a["alibi"], a["softcap"], a["stream"])
+
+
 def comb(**kw):
     a = dict(op=FAKE, lp=FAKE, S=2, batch=1, heads=1, seqlen_q=1, head_dim=128, o=FAKE,
              o_dtype=0, lse=None, stream=None)
@@ -119,6 +130,26 @@ def test_fa_fwd_rejects(kw, code):
 ])
 def test_fa_fwd_splitkv_rejects(kw, code):
     assert split(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(op=None), NULL),
+    (dict(lp=None), NULL), (dict(S=0), SHAPE), (dict(S=(1 << 16) + 1), SHAPE),
+    (dict(batch=0), SHAPE), (dict(seqlen_k=0), SHAPE),
+    (dict(in_dtype=0), UNSUP), (dict(in_dtype=3), UNSUP), (dict(head_dim=96), UNSUP),
+    (dict(causal=1, wr=1), MASK), (dict(wl=-2), MASK), (dict(scale=0.0), VALUE),
+    (dict(softcap=math.inf), VALUE),
+])
+def test_fa_fwd_split_rejects(kw, code):
+    assert fsplit(**kw) == code
+
+
+def test_split_chunk_len_for_contiguous_splits():
+    # fa_fwd_split cuts the keys in chunks that are whole 64-key tiles.
+    assert fa.fa_split_chunk_len(4096, 4, 64) == 1024
+    assert fa.fa_split_chunk_len(4096, 3, 64) == 1408
+    assert fa.fa_split_chunk_len(100, 8, 64) == 64
+    assert fa.fa_split_chunk_len(2000, 7, 64) == 320
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -234,6 +234,58 @@ def test_splitkv_paged_small(case):
     check(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, dtype, "combined")
 
 
+# --------------------------------------------------------------------------
+# Split-KV over contiguous K/V (fa_fwd_split): chunks of whole 64-key tiles
+# --------------------------------------------------------------------------
+CONTIG_SPLIT_CASES = [
+    # (d, B, H, nq, nk, num_splits, causal, wl, wr, alibi, cap)
+    (128, 2, 3, 70, 1000, 4, True, -1, -1, False, 0.0),
+    (64, 1, 4, 200, 333, 3, False, -1, -1, True, 10.0),
+    (128, 1, 2, 130, 130, 8, True, 40, 0, False, 0.0),
+    (64, 2, 2, 300, 90, 2, True, -1, -1, False, 0.0),     # Nq > Nk: leading rows see no key
+    (128, 1, 3, 1, 2000, 7, True, -1, -1, True, 30.0),
+    (128, 2, 2, 64, 64, 16, False, -1, -1, False, 0.0),   # more splits than key tiles
+]
+
+
+@pytest.mark.parametrize("case", CONTIG_SPLIT_CASES)
+def test_split_contiguous_small(case):
+    d, B, H, nq, nk, S, causal, wl, wr, alibi, cap = case
+    say(f"contig split {case}")
+    q, k, v = qkv_case(4000 + CONTIG_SPLIT_CASES.index(case), B, nq, nk, H, d, "bf16",
+                       2.0 if cap else 1.0)
+    slopes = W.alibi_slopes(H) if alibi else None
+    ts = None if slopes is None else torch.from_numpy(np.asarray(slopes, np.float32)).cuda()
+    scale = 1.0 / np.sqrt(d)
+    o_part, lse_part = fa.attention_split_partials(to_dev(q, "bf16"), to_dev(k, "bf16"),
+                                                   to_dev(v, "bf16"), S, scale, causal, wl, wr,
+                                                   ts, cap)
+    o, lse = fa.combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    qf, kf, vf = (W.to_float(x, "bf16") for x in (q, k, v))
+    assert fa.fa_split_chunk_len(nk, S, 64) == -(-(-(-nk // S)) // 64) * 64
+    rop, rlp = O.splitkv_ref(qf, kf, vf, S, 64, scale, causal, wl, wr, slopes, cap)
+    check(o_part.cpu().numpy(), lse_part.cpu().numpy(), rop, rlp, "bf16", "partials")
+    ro, rl = O.attention_ref(qf, kf, vf, scale, causal, wl, wr, slopes, cap)
+    check(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", "combined")
+
+
+def test_cfg5_split_full():
+    """ALiBi + softcap, Nq=512 over Nk=4096: 64 query tiles leave most CUs idle, so the
+    key range is split 8 ways and merged by the combine kernel."""
+    w = W.WORKLOADS[5]
+    say(f"cfg5 split {w}")
+    q, k, v = W.gen_qkv(w)
+    slopes = w.slopes()
+    ts = torch.from_numpy(np.asarray(slopes, np.float32)).cuda()
+    o, lse = fa.attention_split(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), 8,
+                                softmax_scale=w.scale, causal=True, alibi_slopes=ts,
+                                softcap=w.softcap)
+    torch.cuda.synchronize()
+    ro, rl = oracle_fwd(q, k, v, w.dtype, w.scale, True, -1, -1, slopes, w.softcap)
+    print(check(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", "cfg5 split"))
+
+
 def test_combine_matches_oracle_on_random_partials():
     rng = np.random.default_rng(5)
     S, B, H, nq, d = 6, 2, 3, 5, 128
