@@ -3,9 +3,12 @@
 One step = one pass of the whole path over one batch of seeded synthetic input:
   1. fa_fwd on the GPT-style causal prefill (B=4, H=16, Nq=Nk=2048, d=128, bf16),
   2. fa_fwd_splitkv + fa_splitkv_combine on the paged decode
-     (B=8, H=32, Nq=1, Nk=32768, d=128, bf16, 256-token pages, 16 splits).
+     (B=8, H=32, Nq=1, Nk=32768, d=128, bf16, 256-token pages, 16 splits),
+  3. fa_fwd_split (8 key splits) + fa_splitkv_combine on the short query set
+     with ALiBi and a tanh cap (B=2, H=8, Nq=512, Nk=4096, d=128, bf16).
 `value` is the prefill's algorithmic TFLOP/s (4*B*H*d*allowed pairs over the
-prefill launch time); the decode's algorithmic GB/s is reported beside it.
+prefill launch time); the decode's algorithmic GB/s and the split forward's
+TFLOP/s are reported beside it.
 Inputs are resident in device memory before the timed region starts.
 
 Prints ONE JSON line on stdout. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -145,6 +148,20 @@ def main():
     combine_bytes = part_bytes + do.numel() * 4 + dlse.numel() * 4
     decode_bytes = split_bytes + combine_bytes
 
+    # ---- short query set with ALiBi + softcap, split 8 ways over the keys
+    ws = W.WORKLOADS[5]
+    log(f"generating {ws.name}")
+    sq_np, sk_np, sv_np = W.gen_qkv(ws)
+    sq, sk, sv = up(sq_np, ws.dtype), up(sk_np, ws.dtype), up(sv_np, ws.dtype)
+    del sq_np, sk_np, sv_np
+    s_slopes = torch.from_numpy(np.asarray(ws.slopes(), np.float32)).to(dev)
+    SS = 8
+    s_opart = torch.empty((SS, ws.B, ws.H, ws.Nq, ws.d), dtype=torch.float32, device=dev)
+    s_lpart = torch.empty((SS, ws.B, ws.H, ws.Nq), dtype=torch.float32, device=dev)
+    s_o = torch.empty((ws.B, ws.Nq, ws.H, ws.d), dtype=torch.float32, device=dev)
+    s_lse = torch.empty((ws.B, ws.H, ws.Nq), dtype=torch.float32, device=dev)
+    split_flops = 4.0 * ws.B * ws.H * ws.d * allowed_pairs(ws.Nq, ws.Nk, True, -1, -1)
+
     stream = torch.cuda.current_stream()
 
     def check(st, where):
@@ -164,15 +181,23 @@ def main():
         check(fa.fa_splitkv_combine(o_part, lse_part, S, wd.B, wd.H, wd.Nq, wd.d, do, dlse,
                                     stream), "fa_splitkv_combine")
 
+    def short_split():
+        check(fa.fa_fwd_split(sq, sk, sv, s_opart, s_lpart, SS, ws.B, ws.H, ws.Nq, ws.Nk, ws.d,
+                              ws.scale, True, -1, -1, s_slopes, ws.softcap, stream),
+              "fa_fwd_split")
+        check(fa.fa_splitkv_combine(s_opart, s_lpart, SS, ws.B, ws.H, ws.Nq, ws.d, s_o, s_lse,
+                                    stream), "fa_splitkv_combine")
+
     log("warmup")
     for _ in range(args.warmup):
         prefill()
         split_pass()
         combine_pass()
+        short_split()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
@@ -184,17 +209,21 @@ def main():
         e[2].record(stream)
         combine_pass()
         e[3].record(stream)
+        short_split()
+        e[4].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     t_prefill = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
     t_split = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
     t_comb = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+    t_short = np.array([e[3].elapsed_time(e[4]) for e in ev]) * 1e-3
 
     pre_tflops = prefill_flops / t_prefill.mean() / 1e12
     dec_time = (t_split + t_comb).mean()
     dec_gbs = decode_bytes / dec_time / 1e9
     split_gbs = split_bytes / t_split.mean() / 1e9
-    assert torch.isfinite(po).all() and torch.isfinite(do).all()
+    short_tflops = split_flops / t_short.mean() / 1e12
+    assert torch.isfinite(po).all() and torch.isfinite(do).all() and torch.isfinite(s_o).all()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -226,7 +255,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 inputs, seeded block-table permutation)",
         "config": {"workload": "gpt_causal_prefill B4 H16 Nq=Nk=2048 d128 bf16 causal "
-                               "+ paged_splitkv_decode B8 H32 Nq1 Nk32768 d128 page256 S16",
+                               "+ paged_splitkv_decode B8 H32 Nq1 Nk32768 d128 page256 S16 "
+                               "+ alibi_softcap_nq_ne_nk B2 H8 Nq512 Nk4096 d128 split8",
                    "prefill_gflop": round(prefill_flops / 1e9, 4),
                    "decode_gbytes": round(decode_bytes / 1e9, 5)},
         "prefill": {"ms": round(t_prefill.mean() * 1e3, 5), "ms_min": round(t_prefill.min() * 1e3, 5),
@@ -238,6 +268,11 @@ def main():
                                 "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
                                 "traffic": measured_traffic("decode_split"),
                                 "algorithmic_bytes": int(split_bytes)}},
+        "short_query_split": {"ms": round(t_short.mean() * 1e3, 5),
+                              "ms_min": round(t_short.min() * 1e3, 5),
+                              "tflops": round(short_tflops, 3),
+                              "pct_peak": round(100 * short_tflops / PEAK_BF16_TFLOPS, 2),
+                              "num_splits": SS, "gflop": round(split_flops / 1e9, 4)},
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("prefill"),
