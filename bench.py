@@ -276,7 +276,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("prefill"),
-                     "algorithmic_bytes": int(prefill_bytes), "kernel": "fwd_bf16_kernel<128>"},
+                     "algorithmic_bytes": int(prefill_bytes), "kernel": "fwd_bf16_kernel<128, false, false, FWD_CONTIG>"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
