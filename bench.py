@@ -58,8 +58,45 @@ def measured_traffic(kind):
     return int(round((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024))
 
 
+def device_info(torch, dev):
+    """CU count and maximum shader clock of the GPU agent as rocminfo reports them, and the
+    dense bf16 MFMA rate they imply (4096 flop per clock per CU). `peak` in the roofline
+    objects stays MI355X's published figure."""
+    import subprocess
+    prop = torch.cuda.get_device_properties(dev)
+    out = {"name": prop.gcnArchName, "cus": int(prop.multi_processor_count), "max_sclk_mhz": None}
+    try:
+        text = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+        for agent in text.split("Agent ")[1:]:
+            if "gfx" not in agent or "Compute Unit" not in agent:
+                continue
+            for line in agent.splitlines():
+                if "Max Clock Freq. (MHz)" in line:
+                    out["max_sclk_mhz"] = int(line.split(":")[1].split()[0])
+                elif line.strip().startswith("Compute Unit:"):
+                    out["cus"] = int(line.split(":")[1].split()[0])
+            break
+    except (OSError, subprocess.SubprocessError, ValueError, IndexError):
+        pass
+    if out["max_sclk_mhz"]:
+        out["bf16_peak_at_max_sclk_tflops"] = round(
+            out["cus"] * out["max_sclk_mhz"] * 1e6 * 4096 / 1e12, 1)
+    return out
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown cpu"
 
 
 def allowed_pairs(nq, nk, causal, wl, wr):
@@ -228,18 +265,21 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle as O
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         log("cpu baseline: oracle on the full causal-prefill batch")
         q, k, v = W.gen_qkv(wp)
         qf, kf, vf = (W.to_float(x, wp.dtype) for x in (q, k, v))
-        t = time.perf_counter()
-        O.attention_ref(qf, kf, vf, wp.scale, True)
-        dt = time.perf_counter() - t
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        usable = len(os.sched_getaffinity(0))
+        with threadpool_limits(limits=usable):
+            t = time.perf_counter()
+            O.attention_ref(qf, kf, vf, wp.scale, True)
+            dt = time.perf_counter() - t
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         cpu = {"value": round(prefill_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"whole causal-prefill batch B4 H16 N2048 d128 (fp64 numpy, {dt:.1f} s, "
-                         f"host cpus {os.cpu_count()})"}
+               "sample": f"whole causal-prefill batch B4 H16 N2048 d128 (fp64 numpy, {dt:.1f} s; "
+                         f"BLAS threads {threads}, usable cpus {usable}, os.cpu_count "
+                         f"{os.cpu_count()}, {cpu_model()})"}
 
     line = {
         "metric": "attn fwd TFLOP/s (% bf16 MFMA peak); decode split-KV GB/s (% HBM peak)",
@@ -259,9 +299,14 @@ def main():
                                "+ alibi_softcap_nq_ne_nk B2 H8 Nq512 Nk4096 d128 split8",
                    "prefill_gflop": round(prefill_flops / 1e9, 4),
                    "decode_gbytes": round(decode_bytes / 1e9, 5)},
+        "device": device_info(torch, dev),
         "prefill": {"ms": round(t_prefill.mean() * 1e3, 5), "ms_min": round(t_prefill.min() * 1e3, 5),
+                    "ms_median": round(float(np.median(t_prefill)) * 1e3, 5),
                     "tflops": round(pre_tflops, 3), "pct_peak": round(100 * pre_tflops / PEAK_BF16_TFLOPS, 2)},
-        "decode": {"ms": round(dec_time * 1e3, 5), "split_ms": round(t_split.mean() * 1e3, 5),
+        "decode": {"ms": round(dec_time * 1e3, 5),
+                   "ms_median": round(float(np.median(t_split + t_comb)) * 1e3, 5),
+                   "ms_min": round(float((t_split + t_comb).min()) * 1e3, 5),
+                   "split_ms": round(t_split.mean() * 1e3, 5),
                    "combine_ms": round(t_comb.mean() * 1e3, 5), "gbs": round(dec_gbs, 2),
                    "pct_peak": round(100 * dec_gbs / PEAK_HBM_GBS, 2),
                    "roofline": {"bound": "hbm", "achieved": round(split_gbs, 2), "peak": PEAK_HBM_GBS,
@@ -270,6 +315,7 @@ def main():
                                 "algorithmic_bytes": int(split_bytes)}},
         "short_query_split": {"ms": round(t_short.mean() * 1e3, 5),
                               "ms_min": round(t_short.min() * 1e3, 5),
+                              "ms_median": round(float(np.median(t_short)) * 1e3, 5),
                               "tflops": round(short_tflops, 3),
                               "pct_peak": round(100 * short_tflops / PEAK_BF16_TFLOPS, 2),
                               "num_splits": SS, "gflop": round(split_flops / 1e9, 4)},
