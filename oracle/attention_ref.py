@@ -28,6 +28,17 @@ entries):
 * paged KV cache (v2.5 entry): logical key t of sequence b lives in physical page
   block_table[b, t // page_size], row t % page_size.
 
+Variable sequence lengths ("FlashAttention深度解析：从算法创新到产业变革的全面影响",
+the closing section on the roadmap, names them as a feature without defining
+them). Reading taken here: every sequence of a batch is its own attention
+problem over its own query rows and its own keys, with the v2.1 bottom-right
+rule applied to that sequence's lengths (off_b = nk_b - nq_b). Two forms:
+
+* a packed batch: sequence b owns query rows [cu_q[b], cu_q[b+1]) of a packed
+  q and key rows [cu_k[b], cu_k[b+1]) of packed k and v;
+* a paged cache with per-sequence key counts: sequence b uses only its first
+  seqlens_k[b] cached keys, and its split chunks are cut from that count.
+
 Conventions the pages leave open (each is stated with its reason where it is
 used): LSE is the natural log of the row's sum of exp over allowed keys; a row
 with no allowed key has O = 0 and LSE = -inf; split chunk length is
@@ -135,6 +146,8 @@ def attention_bh(q_all, k_bh, v_bh, rows, nq, scale, causal=False, window_left=-
     rows = np.asarray(rows, dtype=np.int64)
     o = np.zeros((len(rows), v_bh.shape[1]), dtype=np.float64)
     lse = np.full(len(rows), NEG_INF, dtype=np.float64)
+    if k_bh.shape[0] == 0:                            # no key at all: every row is empty
+        return o, lse
     pos = 0
     for rc in _row_chunks(rows, k_bh.shape[0]):
         s = scores_ref(q_all[rc], k_bh, rc, nq, scale, causal, window_left,
@@ -173,6 +186,43 @@ def attention_ref(q, k, v, scale, causal=False, window_left=-1, window_right=-1,
 
 
 # --------------------------------------------------------------------------
+# Packed variable-length batch (the deep-analysis page, roadmap section)
+# --------------------------------------------------------------------------
+def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
+                         window_left=-1, window_right=-1, alibi_slopes=None, softcap=0.0,
+                         seqs=None, heads=None):
+    """Exact attention of each sequence of a packed batch, on its own.
+
+    q [total_q, H, d], k and v [total_k, H, d]; sequence b owns query rows
+    [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows [cu_seqlens_k[b],
+    cu_seqlens_k[b+1]), and its mask and ALiBi distances are aligned to its own
+    bottom-right corner. seqs / heads: optional subsets to compute.
+    Returns O [total_q, H, d] and LSE [H, total_q]; entries not computed are NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64)
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    H = q.shape[1]
+    o = np.full((q.shape[0], H, v.shape[2]), np.nan)
+    lse = np.full((H, q.shape[0]), np.nan)
+    seqs = range(len(cq) - 1) if seqs is None else seqs
+    heads = range(H) if heads is None else heads
+    for b in seqs:
+        q0, q1, k0, k1 = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+        rows = np.arange(q1 - q0)
+        for h in heads:
+            slope = None if alibi_slopes is None else float(alibi_slopes[h])
+            ob, lb = attention_bh(q[q0:q1, h, :], k[k0:k1, h, :], v[k0:k1, h, :], rows,
+                                  q1 - q0, scale, causal, window_left, window_right, slope,
+                                  softcap)
+            o[q0:q1, h, :] = ob
+            lse[h, q0:q1] = lb
+    return o, lse
+
+
+# --------------------------------------------------------------------------
 # Paged KV cache (flash-attn update article, v2.5 entry)
 # --------------------------------------------------------------------------
 def paged_gather_ref(cache: np.ndarray, block_table: np.ndarray, b: int, nk: int) -> np.ndarray:
@@ -200,9 +250,12 @@ def split_bounds(nk: int, num_splits: int, page_size: int = 1):
 
 
 def splitkv_ref(q, k, v, num_splits, page_size, scale, causal=False, window_left=-1,
-                window_right=-1, alibi_slopes=None, softcap=0.0, bh=None):
+                window_right=-1, alibi_slopes=None, softcap=0.0, bh=None, seqlens_k=None):
     """Per-split normalised outputs and log-sum-exps over contiguous logical K/V.
 
+    seqlens_k: optional per-sequence key counts (each <= Nk); sequence b then
+    uses keys [0, seqlens_k[b]) only, aligned to its own bottom-right corner,
+    and its chunks are split_bounds(seqlens_k[b], ...).
     Returns o_part [S, B, H, Nq, d] and lse_part [S, B, H, Nq]; an empty chunk
     (or a row with no allowed key inside it) has o = 0 and lse = -inf.
     """
@@ -215,10 +268,13 @@ def splitkv_ref(q, k, v, num_splits, page_size, scale, causal=False, window_left
     o_part = np.full((num_splits, B, H, nq, v.shape[3]), np.nan)
     lse_part = np.full((num_splits, B, H, nq), np.nan)
     rows = np.arange(nq)
-    for s, (lo, hi) in enumerate(split_bounds(nk, num_splits, page_size)):
-        for b, h in pairs:
-            slope = None if alibi_slopes is None else float(alibi_slopes[h])
-            ob, lb = attention_bh(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], rows, nq,
+    for b, h in pairs:
+        nk_b = nk if seqlens_k is None else int(seqlens_k[b])
+        if not 0 <= nk_b <= nk:
+            raise ValueError("seqlens_k entries must lie in [0, Nk]")
+        slope = None if alibi_slopes is None else float(alibi_slopes[h])
+        for s, (lo, hi) in enumerate(split_bounds(nk_b, num_splits, page_size)):
+            ob, lb = attention_bh(q[b, :, h, :], k[b, :nk_b, h, :], v[b, :nk_b, h, :], rows, nq,
                                   scale, causal, window_left, window_right, slope,
                                   softcap, key_lo=lo, key_hi=hi)
             o_part[s, b, h] = ob

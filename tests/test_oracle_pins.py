@@ -396,3 +396,170 @@ def test_golden_scores_at_4096_tokens():
     n = g["seqlen"]
     s = O.scores_ref(np.ones((n, 1)), np.ones((n, 1)), np.arange(n), n, 1.0)
     assert s.size == n * n and s.size > g["more_than"]
+
+
+# T16-T20: variable sequence lengths ----------------------------------------
+# (Per-sequence lengths: every sequence is its own problem, aligned to its own
+# bottom-right corner.)
+VARLEN = [(3, 5), (0, 4), (4, 0), (5, 2), (1, 7), (6, 6), (2, 9)]
+
+
+def pack(lens, H, d, seed):
+    """Packed tensor [sum(lens), H, d] and its cumulative offsets."""
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return rnd(seed, int(cu[-1]), H, d), cu
+
+
+@pytest.mark.parametrize("causal,wl,wr", MASKS)
+def test_t16_varlen_zero_query_counts_per_sequence(causal, wl, wr):
+    """Q = 0: LSE of row i of sequence b is ln(n_i) with sequence b's own lengths,
+    and O is the mean of sequence b's own allowed V rows."""
+    H, d = 2, 3
+    lq = [a for a, _ in VARLEN]
+    lk = [b for _, b in VARLEN]
+    cq = np.concatenate([[0], np.cumsum(lq)])
+    k, ck = pack(lk, H, d, 40)
+    v, _ = pack(lk, H, d, 41)
+    q = np.zeros((int(cq[-1]), H, d))
+    o, lse = O.attention_varlen_ref(q, k, v, cq, ck, 0.9, causal, wl, wr)
+    for b, (nq, nk) in enumerate(VARLEN):
+        for h in range(H):
+            for i in range(nq):
+                lo, hi = interval(i, nq, nk, causal, wl, wr)
+                n = max(0, hi - lo + 1)
+                row = cq[b] + i
+                if n == 0:
+                    assert lse[h, row] == -math.inf and np.all(o[row, h] == 0.0)
+                else:
+                    assert abs(lse[h, row] - math.log(n)) <= 1e-12
+                    np.testing.assert_allclose(o[row, h], v[ck[b] + lo:ck[b] + hi + 1, h].mean(axis=0),
+                                               atol=1e-12)
+
+
+def test_t17_varlen_brute_force_loops():
+    """Pure-Python per-element loops over a tiny pack, with cap, ALiBi and a window."""
+    H, d, scale, cap = 2, 3, 0.8, 1.7
+    slopes = [0.3, 0.1]
+    lens = [(2, 3), (3, 1), (1, 4), (4, 4)]
+    q, cq = pack([a for a, _ in lens], H, d, 42)
+    k, ck = pack([b for _, b in lens], H, d, 43)
+    v, _ = pack([b for _, b in lens], H, d, 44)
+    for causal, wl, wr in [(True, -1, -1), (False, 1, 2), (True, 2, -1)]:
+        o, lse = O.attention_varlen_ref(q, k, v, cq, ck, scale, causal, wl, wr, slopes, cap)
+        for b, (nq, nk) in enumerate(lens):
+            for h in range(H):
+                for i in range(nq):
+                    ip = i + nk - nq
+                    sc = []
+                    for j in range(nk):
+                        if (causal and j > ip) or (wl >= 0 and j < ip - wl) or (wr >= 0 and j > ip + wr):
+                            continue
+                        dot = sum(q[cq[b] + i, h, e] * k[ck[b] + j, h, e] for e in range(d))
+                        x = cap * math.tanh(scale * dot / cap) - slopes[h] * abs(ip - j)
+                        sc.append((x, j))
+                    row = cq[b] + i
+                    if not sc:
+                        assert lse[h, row] == -math.inf
+                        continue
+                    den = sum(math.exp(x) for x, _ in sc)
+                    assert abs(lse[h, row] - math.log(den)) < 1e-12
+                    for e in range(d):
+                        want = sum(math.exp(x) * v[ck[b] + j, h, e] for x, j in sc) / den
+                        assert abs(o[row, h, e] - want) < 1e-12
+
+
+def test_t18_varlen_independence_and_pack_order():
+    """Changing one sequence's K/V changes only its rows; reversing the packing
+    order permutes the outputs and nothing else."""
+    H, d = 2, 4
+    lq = [a for a, _ in VARLEN]
+    lk = [b for _, b in VARLEN]
+    q, cq = pack(lq, H, d, 45)
+    k, ck = pack(lk, H, d, 46)
+    v, _ = pack(lk, H, d, 47)
+    o, lse = O.attention_varlen_ref(q, k, v, cq, ck, 0.5, True, 3, -1)
+    k2, v2 = k.copy(), v.copy()
+    b_hit = 4
+    k2[ck[b_hit]:ck[b_hit + 1]] += 1.0
+    v2[ck[b_hit]:ck[b_hit + 1]] *= -2.0
+    o2, lse2 = O.attention_varlen_ref(q, k2, v2, cq, ck, 0.5, True, 3, -1)
+    mine = np.zeros(q.shape[0], dtype=bool)
+    mine[cq[b_hit]:cq[b_hit + 1]] = True
+    assert np.array_equal(o2[~mine], o[~mine]) and np.array_equal(lse2[:, ~mine], lse[:, ~mine])
+    assert not np.allclose(o2[mine], o[mine])
+    # reversed order
+    order = list(reversed(range(len(VARLEN))))
+    qr = np.concatenate([q[cq[b]:cq[b + 1]] for b in order])
+    kr = np.concatenate([k[ck[b]:ck[b + 1]] for b in order])
+    vr = np.concatenate([v[ck[b]:ck[b + 1]] for b in order])
+    cqr = np.concatenate([[0], np.cumsum([lq[b] for b in order])])
+    ckr = np.concatenate([[0], np.cumsum([lk[b] for b in order])])
+    orr, lr = O.attention_varlen_ref(qr, kr, vr, cqr, ckr, 0.5, True, 3, -1)
+    for pos, b in enumerate(order):
+        assert np.array_equal(orr[cqr[pos]:cqr[pos + 1]], o[cq[b]:cq[b + 1]])
+        assert np.array_equal(lr[:, cqr[pos]:cqr[pos + 1]], lse[:, cq[b]:cq[b + 1]])
+
+
+def test_t18_varlen_equal_lengths_is_the_batched_problem():
+    B, nq, nk, H, d = 3, 4, 6, 2, 5
+    q, k, v = rnd(48, B, nq, H, d), rnd(49, B, nk, H, d), rnd(50, B, nk, H, d)
+    slopes = np.array([0.25, 0.5])
+    ob, lb = O.attention_ref(q, k, v, 0.4, True, 2, 0, slopes, 3.0)
+    cq, ck = np.arange(B + 1) * nq, np.arange(B + 1) * nk
+    ov, lv = O.attention_varlen_ref(q.reshape(B * nq, H, d), k.reshape(B * nk, H, d),
+                                    v.reshape(B * nk, H, d), cq, ck, 0.4, True, 2, 0, slopes, 3.0)
+    np.testing.assert_allclose(ov, ob.reshape(B * nq, H, d), atol=1e-14)
+    np.testing.assert_allclose(lv, np.transpose(lb, (1, 0, 2)).reshape(H, B * nq), atol=1e-14)
+
+
+@pytest.mark.parametrize("num_splits,page", [(1, 1), (3, 2), (4, 4), (16, 2)])
+@pytest.mark.parametrize("nq,causal,wl,wr", [(1, True, -1, -1), (3, True, -1, -1), (3, False, 2, 1),
+                                            (5, True, 4, 0)])
+def test_t19_seqlens_split_equals_truncated_cache(num_splits, page, nq, causal, wl, wr):
+    """Per-sequence key counts: combining the splits gives the attention over the
+    first seqlens[b] keys alone (later cache rows play no part)."""
+    B, nk, H, d = 4, 13, 2, 3
+    seqlens = [13, 0, 5, 8]
+    q, k, v = rnd(51, B, nq, H, d), rnd(52, B, nk, H, d), rnd(53, B, nk, H, d)
+    slopes = np.array([0.2, 0.07])
+    op, lp = O.splitkv_ref(q, k, v, num_splits, page, 0.6, causal, wl, wr, slopes, 2.5,
+                           seqlens_k=seqlens)
+    oc, lc = O.combine_ref(op, lp)
+    for b, n in enumerate(seqlens):
+        kb, vb = k[b:b + 1, :n].copy(), v[b:b + 1, :n].copy()
+        if n == 0:
+            assert np.all(lc[b] == -math.inf) and np.all(oc[b] == 0.0)
+            continue
+        ou, lu = O.attention_ref(q[b:b + 1], kb, vb, 0.6, causal, wl, wr, slopes, 2.5)
+        np.testing.assert_allclose(oc[b], np.transpose(ou[0], (1, 0, 2)), atol=1e-12)
+        np.testing.assert_allclose(lc[b], lu[0], atol=1e-12)
+    # Rows past seqlens[b] must not matter: poison them.
+    k2, v2 = k.copy(), v.copy()
+    for b, n in enumerate(seqlens):
+        k2[b, n:] = np.nan
+        v2[b, n:] = np.nan
+    op2, lp2 = O.splitkv_ref(q, k2, v2, num_splits, page, 0.6, causal, wl, wr, slopes, 2.5,
+                             seqlens_k=seqlens)
+    assert np.array_equal(op2, op) and np.array_equal(lp2, lp)
+
+
+def test_t20_seqlens_chunks_and_decode_counts():
+    """Q = 0 decode (Nq = 1, causal): split s of sequence b holds the keys of its
+    own chunk, C_b = ceil(n_b / S) rounded up to the page, so its LSE is
+    ln(#keys in that chunk); merged, LSE = ln(n_b)."""
+    B, nk, H, d, S, ps = 5, 40, 1, 2, 4, 4
+    seqlens = [40, 1, 0, 17, 33]
+    q = np.zeros((B, 1, H, d))
+    k, v = rnd(54, B, nk, H, d), rnd(55, B, nk, H, d)
+    op, lp = O.splitkv_ref(q, k, v, S, ps, 1.0, True, seqlens_k=seqlens)
+    want_chunks = {40: [12, 12, 12, 4], 1: [1, 0, 0, 0], 0: [0, 0, 0, 0], 17: [8, 8, 1, 0],
+                   33: [12, 12, 9, 0]}
+    for b, n in enumerate(seqlens):
+        for s, cnt in enumerate(want_chunks[n]):
+            if cnt == 0:
+                assert lp[s, b, 0, 0] == -math.inf and np.all(op[s, b, 0, 0] == 0.0)
+            else:
+                assert abs(lp[s, b, 0, 0] - math.log(cnt)) < 1e-12
+    _, lc = O.combine_ref(op, lp)
+    for b, n in enumerate(seqlens):
+        assert (lc[b, 0, 0] == -math.inf) if n == 0 else abs(lc[b, 0, 0] - math.log(n)) < 1e-12

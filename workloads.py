@@ -170,26 +170,60 @@ def gen_qkv(w: Workload):
     return q, k, v
 
 
-def gen_paged(w: Workload, poison_unused: bool = True):
+def gen_paged(w: Workload, poison_unused: bool = True, seqlens=None):
     """Q plus a paged K/V pool [pool_pages, page_size, H, d] and its block table.
 
-    Pages no sequence references are filled with bf16 NaN (or float32 NaN), so a
-    wrong gather shows up as NaN in the output.
+    Every sequence holds pages for w.Nk keys. With `seqlens`, sequence b stores
+    only its first seqlens[b] keys (the first seqlens[b] rows of the same
+    slices). With poison_unused, every pool row that holds no stored key (pages
+    no sequence references, and rows past a sequence's length) is bf16 NaN (or
+    float32 NaN), so a wrong gather or a read past a length shows up as NaN.
     """
     q = gen_tensor(w.seed, TENSOR_Q, w.B, w.Nq, w.H, w.d, w.amp, w.dtype)
     bt = gen_block_table(w.table_seed, w.B, w.pages_per_seq, w.pool_pages)
     st = np.uint16 if w.dtype == "bf16" else np.float32
     shape = (w.pool_pages, w.page_size, w.H, w.d)
-    kc = np.zeros(shape, dtype=st)
-    vc = np.zeros(shape, dtype=st)
-    if poison_unused:
-        used = np.zeros(w.pool_pages, dtype=bool)
-        used[bt.reshape(-1)] = True
-        nan = BF16_NAN_BITS if w.dtype == "bf16" else np.float32("nan")
-        kc[~used] = nan
-        vc[~used] = nan
+    nan = BF16_NAN_BITS if w.dtype == "bf16" else np.float32("nan")
+    kc = np.full(shape, nan if poison_unused else 0, dtype=st)
+    vc = np.full(shape, nan if poison_unused else 0, dtype=st)
     for b in range(w.B):
+        n = w.Nk if seqlens is None else int(seqlens[b])
         for h in range(w.H):
-            scatter_pages(kc, bt, b, h, gen_slice(w.seed, TENSOR_K, b, h, w.Nk, w.d, w.amp, w.dtype), w.page_size)
-            scatter_pages(vc, bt, b, h, gen_slice(w.seed, TENSOR_V, b, h, w.Nk, w.d, w.amp, w.dtype), w.page_size)
+            ks = gen_slice(w.seed, TENSOR_K, b, h, w.Nk, w.d, w.amp, w.dtype)[:n]
+            vs = gen_slice(w.seed, TENSOR_V, b, h, w.Nk, w.d, w.amp, w.dtype)[:n]
+            scatter_pages(kc, bt, b, h, ks, w.page_size)
+            scatter_pages(vc, bt, b, h, vs, w.page_size)
     return q, kc, vc, bt
+
+
+# --------------------------------------------------------------------------
+# Packed variable-length batches
+# --------------------------------------------------------------------------
+def cu_seqlens(lengths) -> np.ndarray:
+    """Cumulative offsets [0, l0, l0 + l1, ...] as int32."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def varlen_lengths(seed: int, batch: int, max_len: int, min_len: int = 1) -> np.ndarray:
+    """Seeded sequence lengths, uniform in [min_len, max_len]."""
+    rng = np.random.default_rng([int(seed), 7])
+    return rng.integers(min_len, max_len + 1, size=batch).astype(np.int64)
+
+
+def gen_varlen(seed: int, lens_q, lens_k, H: int, d: int, amp: float, dtype: str):
+    """Packed Q [sum(lens_q), H, d], K and V [sum(lens_k), H, d] plus cu_seqlens_q/k.
+
+    Sequence b's rows are the slices gen_slice(seed, tensor, b, h, len, d), so a
+    sequence of a pack equals batch entry b of a batched tensor of that length.
+    """
+    cq, ck = cu_seqlens(lens_q), cu_seqlens(lens_k)
+    st = np.uint16 if dtype == "bf16" else np.float32
+    q = np.empty((int(cq[-1]), H, d), dtype=st)
+    k = np.empty((int(ck[-1]), H, d), dtype=st)
+    v = np.empty((int(ck[-1]), H, d), dtype=st)
+    for b in range(len(lens_q)):
+        for h in range(H):
+            q[cq[b]:cq[b + 1], h] = gen_slice(seed, TENSOR_Q, b, h, int(lens_q[b]), d, amp, dtype)
+            k[ck[b]:ck[b + 1], h] = gen_slice(seed, TENSOR_K, b, h, int(lens_k[b]), d, amp, dtype)
+            v[ck[b]:ck[b + 1], h] = gen_slice(seed, TENSOR_V, b, h, int(lens_k[b]), d, amp, dtype)
+    return q, k, v, cq, ck
