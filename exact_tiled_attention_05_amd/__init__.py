@@ -1,11 +1,13 @@
 """Python binding of libfa, the gfx950 exact tiled attention library.
 
-The functions named like the C ABI (``fa_fwd``, ``fa_fwd_splitkv``,
+The functions named like the C ABI (``fa_fwd``, ``fa_fwd_split``,
+``fa_fwd_splitkv``, ``fa_fwd_splitkv_seqlens``, ``fa_fwd_varlen``,
 ``fa_splitkv_combine``, ``fa_status_string``, ``fa_split_chunk_len``) only
 marshal arguments: torch tensors become device pointers, the current torch
 stream becomes the HIP stream, and every step of the computation runs in the
-library's kernels. ``attention``, ``attention_paged_splitkv``, ``combine`` and
-``decode_paged`` add output allocation (torch.empty) on top of them.
+library's kernels. ``attention``, ``attention_varlen``, ``attention_split``,
+``attention_paged_splitkv``, ``combine`` and ``decode_paged`` add output
+allocation (torch.empty) on top of them.
 
 The library must be built (``python -m exact_tiled_attention_05_amd.build``);
 importing works without it, but every call raises if libfa.so is missing.
@@ -20,8 +22,9 @@ import torch
 
 __all__ = [
     "FA_FP32", "FA_BF16", "FaError", "library_path", "load_library",
-    "fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_splitkv_combine", "fa_status_string",
-    "fa_split_chunk_len", "attention", "attention_split", "attention_split_partials",
+    "fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens", "fa_fwd_varlen",
+    "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len", "attention",
+    "attention_varlen", "attention_split", "attention_split_partials",
     "attention_paged_splitkv", "combine", "decode_paged",
 ]
 
@@ -30,8 +33,8 @@ FA_OK = 0
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 _lib = None
 
-EXPORTED = ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_splitkv_combine",
-            "fa_status_string", "fa_split_chunk_len")
+EXPORTED = ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
+            "fa_fwd_varlen", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len")
 
 
 class FaError(RuntimeError):
@@ -61,6 +64,12 @@ def load_library():
     lib.fa_fwd_splitkv.restype = i
     lib.fa_fwd_split.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, f, vp]
     lib.fa_fwd_split.restype = i
+    lib.fa_fwd_splitkv_seqlens.argtypes = [vp, vp, vp, i, vp, i, i, vp, vp, vp, i, i, i, i, i, i,
+                                           f, i, i, i, vp, f, vp]
+    lib.fa_fwd_splitkv_seqlens.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, i, vp, i, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
+                                  i, vp, f, vp]
+    lib.fa_fwd_varlen.restype = i
     lib.fa_splitkv_combine.argtypes = [vp, vp, i, i, i, i, i, vp, i, vp, vp]
     lib.fa_splitkv_combine.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -140,6 +149,32 @@ def fa_fwd_splitkv(q, k_cache, v_cache, block_table, max_pages_per_seq, page_siz
         _ptr(alibi_slopes), float(softcap), _stream(stream))
 
 
+def fa_fwd_splitkv_seqlens(q, k_cache, v_cache, block_table, max_pages_per_seq, page_size,
+                           cache_seqlens, o_part, lse_part, num_splits, batch, heads, seqlen_q,
+                           max_seqlen_k, head_dim, softmax_scale, causal=False, window_left=-1,
+                           window_right=-1, alibi_slopes=None, softcap=0.0, stream=None) -> int:
+    """Call fa_fwd_splitkv_seqlens on caller-allocated tensors; returns the status code."""
+    return load_library().fa_fwd_splitkv_seqlens(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q), _ptr(block_table),
+        int(max_pages_per_seq), int(page_size), _ptr(cache_seqlens), _ptr(o_part), _ptr(lse_part),
+        int(num_splits), int(batch), int(heads), int(seqlen_q), int(max_seqlen_k), int(head_dim),
+        float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
+        _ptr(alibi_slopes), float(softcap), _stream(stream))
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, heads, total_q, total_k,
+                  max_seqlen_q, max_seqlen_k, head_dim, softmax_scale, causal=False,
+                  window_left=-1, window_right=-1, alibi_slopes=None, softcap=0.0,
+                  stream=None) -> int:
+    """Call fa_fwd_varlen on caller-allocated tensors; returns the status code."""
+    return load_library().fa_fwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(o), _dtype_code(o), _ptr(lse),
+        _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(batch), int(heads), int(total_q),
+        int(total_k), int(max_seqlen_q), int(max_seqlen_k), int(head_dim),
+        float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
+        _ptr(alibi_slopes), float(softcap), _stream(stream))
+
+
 def fa_fwd_split(q, k, v, o_part, lse_part, num_splits, batch, heads, seqlen_q, seqlen_k,
                  head_dim, softmax_scale, causal=False, window_left=-1, window_right=-1,
                  alibi_slopes=None, softcap=0.0, stream=None) -> int:
@@ -186,10 +221,43 @@ def attention(q, k, v, softmax_scale=None, causal=False, window_left=-1, window_
     return o, lse
 
 
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                     softmax_scale=None, causal=False, window_left=-1, window_right=-1,
+                     alibi_slopes=None, softcap=0.0, out_dtype=torch.float32, stream=None):
+    """O [total_q, H, d] (out_dtype) and LSE [H, total_q] fp32 for a packed batch.
+
+    q [total_q, H, d], k/v [total_k, H, d]; cu_seqlens_q/k are int32 [B + 1]
+    device offsets. max_seqlen_q/k are host ints bounding the lengths.
+    """
+    _same_dtype(q, k, v)
+    total_q, H, d = q.shape
+    total_k = k.shape[0]
+    if tuple(k.shape) != (total_k, H, d) or tuple(v.shape) != (total_k, H, d):
+        raise ValueError("k and v must be [total_k, H, d] matching q")
+    for cu in (cu_seqlens_q, cu_seqlens_k):
+        if cu.dtype != torch.int32 or cu.dim() != 1:
+            raise ValueError("cu_seqlens must be int32 [B + 1]")
+    if cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    B = cu_seqlens_q.shape[0] - 1
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    o = torch.empty((total_q, H, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    _check(fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k,
+                         max_seqlen_q, max_seqlen_k, d, softmax_scale, causal, window_left,
+                         window_right, alibi_slopes, softcap, stream), "fa_fwd_varlen")
+    return o, lse
+
+
 def attention_paged_splitkv(q, k_cache, v_cache, block_table, seqlen_k, num_splits,
                             softmax_scale=None, causal=False, window_left=-1, window_right=-1,
-                            alibi_slopes=None, softcap=0.0, stream=None):
-    """Split partials o_part [S,B,H,Nq,d] and lse_part [S,B,H,Nq] over a paged cache."""
+                            alibi_slopes=None, softcap=0.0, stream=None, cache_seqlens=None):
+    """Split partials o_part [S,B,H,Nq,d] and lse_part [S,B,H,Nq] over a paged cache.
+
+    With cache_seqlens (int32 [B] on the device), sequence b uses its first
+    cache_seqlens[b] keys and seqlen_k is the maximum length.
+    """
     _same_dtype(q, k_cache, v_cache)
     B, nq, H, d = q.shape
     _, page_size, Hc, dc = k_cache.shape
@@ -201,10 +269,19 @@ def attention_paged_splitkv(q, k_cache, v_cache, block_table, seqlen_k, num_spli
         softmax_scale = 1.0 / math.sqrt(d)
     o_part = torch.empty((num_splits, B, H, nq, d), dtype=torch.float32, device=q.device)
     lse_part = torch.empty((num_splits, B, H, nq), dtype=torch.float32, device=q.device)
-    _check(fa_fwd_splitkv(q, k_cache, v_cache, block_table, block_table.shape[1], page_size,
-                          o_part, lse_part, num_splits, B, H, nq, seqlen_k, d, softmax_scale,
-                          causal, window_left, window_right, alibi_slopes, softcap, stream),
-           "fa_fwd_splitkv")
+    if cache_seqlens is None:
+        _check(fa_fwd_splitkv(q, k_cache, v_cache, block_table, block_table.shape[1], page_size,
+                              o_part, lse_part, num_splits, B, H, nq, seqlen_k, d, softmax_scale,
+                              causal, window_left, window_right, alibi_slopes, softcap, stream),
+               "fa_fwd_splitkv")
+    else:
+        if cache_seqlens.dtype != torch.int32 or tuple(cache_seqlens.shape) != (B,):
+            raise ValueError("cache_seqlens must be int32 [B]")
+        _check(fa_fwd_splitkv_seqlens(q, k_cache, v_cache, block_table, block_table.shape[1],
+                                      page_size, cache_seqlens, o_part, lse_part, num_splits, B,
+                                      H, nq, seqlen_k, d, softmax_scale, causal, window_left,
+                                      window_right, alibi_slopes, softcap, stream),
+               "fa_fwd_splitkv_seqlens")
     return o_part, lse_part
 
 

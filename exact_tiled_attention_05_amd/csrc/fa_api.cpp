@@ -102,6 +102,55 @@ int64_t split_len(int seqlen_k, int num_splits, int page_size) {
   return (c + page_size - 1) / page_size * page_size;
 }
 
+// fa_fwd_splitkv and fa_fwd_splitkv_seqlens (seqlens_k = nullptr: every
+// sequence holds seqlen_k keys).
+int splitkv(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
+            const int* block_table, int max_pages_per_seq, int page_size, const int* seqlens_k,
+            float* o_part, float* lse_part, int num_splits, int batch, int heads, int seqlen_q,
+            int seqlen_k, int head_dim, float softmax_scale, int causal, int window_left,
+            int window_right, const float* alibi_slopes, float softcap, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !o_part || !lse_part) return FA_ERR_NULL;
+  int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
+  if (st) return st;
+  if (num_splits <= 0 || num_splits > (1 << 16) || max_pages_per_seq <= 0 || page_size <= 0)
+    return FA_ERR_SHAPE;
+  if ((int64_t)max_pages_per_seq * page_size < seqlen_k) return FA_ERR_SHAPE;
+  if ((int64_t)page_size * heads * head_dim >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  if ((st = check_kind(in_dtype, head_dim))) return st;
+  if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
+    return st;
+
+  fa::FwdParams p = {};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.block_table = block_table;
+  p.max_pages = max_pages_per_seq;
+  p.page_size = page_size;
+  p.page_shift = -1;
+  if ((page_size & (page_size - 1)) == 0)
+    for (int sh = 0; sh < 31; ++sh)
+      if ((1 << sh) == page_size) p.page_shift = sh;
+  p.num_splits = num_splits;
+  p.row_stride = heads * head_dim;
+  p.page_stride = (int64_t)page_size * heads * head_dim;
+  p.seqlens_k = seqlens_k;
+  const int tile = in_dtype == FA_BF16 ? fa::BF16_BM : fa::F32_BM;
+  fill_common(p, batch, heads, seqlen_q, seqlen_k, softmax_scale, causal, window_left,
+              window_right, alibi_slopes, softcap, tile);
+  if (split_len(seqlen_k, num_splits, page_size) > kMaxSeq) return FA_ERR_SHAPE;
+  p.split_align = page_size;
+  if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
+
+  const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
+  Launcher fn = in_dtype != FA_BF16 ? pick_f32<true>(head_dim, sc, al)
+                : seqlen_q == 1     ? pick_decode(head_dim, sc, al)
+                                    : pick_bf16<fa::FWD_PAGED_SPLIT>(head_dim, sc, al);
+  return fn(p, stream) ? FA_ERR_HIP : FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -151,7 +200,6 @@ int fa_fwd(const void* q, const void* k, const void* v, int in_dtype, void* o, i
   const int tile = in_dtype == FA_BF16 ? fa::BF16_BM : fa::F32_BM;
   fill_common(p, batch, heads, seqlen_q, seqlen_k, softmax_scale, causal, window_left,
               window_right, alibi_slopes, softcap, tile);
-  p.split_len = seqlen_k;
   if ((int64_t)p.num_q_tiles * heads * batch > kMaxGroups) return FA_ERR_SHAPE;
 
   const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
@@ -182,9 +230,8 @@ int fa_fwd_split(const void* q, const void* k, const void* v, int in_dtype, floa
   p.num_splits = num_splits;
   fill_common(p, batch, heads, seqlen_q, seqlen_k, softmax_scale, causal, window_left,
               window_right, alibi_slopes, softcap, fa::BF16_BM);
-  const int64_t c = split_len(seqlen_k, num_splits, fa::SPLIT_ALIGN);
-  if (c > kMaxSeq) return FA_ERR_SHAPE;
-  p.split_len = (int)c;
+  if (split_len(seqlen_k, num_splits, fa::SPLIT_ALIGN) > kMaxSeq) return FA_ERR_SHAPE;
+  p.split_align = fa::SPLIT_ALIGN;
   if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
 
   Launcher fn = pick_bf16<fa::FWD_CONTIG_SPLIT>(head_dim, softcap > 0.0f, alibi_slopes != nullptr);
@@ -197,45 +244,64 @@ int fa_fwd_splitkv(const void* q, const void* k_cache, const void* v_cache, int 
                    int seqlen_q, int seqlen_k, int head_dim, float softmax_scale, int causal,
                    int window_left, int window_right, const float* alibi_slopes, float softcap,
                    void* stream) {
-  if (!q || !k_cache || !v_cache || !block_table || !o_part || !lse_part) return FA_ERR_NULL;
-  int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
+  return splitkv(q, k_cache, v_cache, in_dtype, block_table, max_pages_per_seq, page_size,
+                 nullptr, o_part, lse_part, num_splits, batch, heads, seqlen_q, seqlen_k,
+                 head_dim, softmax_scale, causal, window_left, window_right, alibi_slopes,
+                 softcap, stream);
+}
+
+int fa_fwd_splitkv_seqlens(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
+                           const int* block_table, int max_pages_per_seq, int page_size,
+                           const int* cache_seqlens, float* o_part, float* lse_part,
+                           int num_splits, int batch, int heads, int seqlen_q, int max_seqlen_k,
+                           int head_dim, float softmax_scale, int causal, int window_left,
+                           int window_right, const float* alibi_slopes, float softcap,
+                           void* stream) {
+  if (!cache_seqlens) return FA_ERR_NULL;
+  return splitkv(q, k_cache, v_cache, in_dtype, block_table, max_pages_per_seq, page_size,
+                 cache_seqlens, o_part, lse_part, num_splits, batch, heads, seqlen_q,
+                 max_seqlen_k, head_dim, softmax_scale, causal, window_left, window_right,
+                 alibi_slopes, softcap, stream);
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, int in_dtype, void* o,
+                  int o_dtype, float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int batch, int heads, int total_q, int total_k, int max_seqlen_q,
+                  int max_seqlen_k, int head_dim, float softmax_scale, int causal,
+                  int window_left, int window_right, const float* alibi_slopes, float softcap,
+                  void* stream) {
+  if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+  if ((total_q > 0 && (!q || !o)) || (total_k > 0 && (!k || !v))) return FA_ERR_NULL;
+  if (batch <= 0 || batch > (1 << 24) || heads <= 0 || heads > (1 << 16)) return FA_ERR_SHAPE;
+  if (total_q < 0 || total_k < 0 || max_seqlen_q <= 0 || max_seqlen_k < 0) return FA_ERR_SHAPE;
+  if (max_seqlen_q > kMaxSeq || max_seqlen_k > kMaxSeq) return FA_ERR_SHAPE;
+  int st = check_kind(in_dtype, head_dim);
   if (st) return st;
-  if (num_splits <= 0 || num_splits > (1 << 16) || max_pages_per_seq <= 0 || page_size <= 0)
-    return FA_ERR_SHAPE;
-  if ((int64_t)max_pages_per_seq * page_size < seqlen_k) return FA_ERR_SHAPE;
-  if ((int64_t)page_size * heads * head_dim >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
-  if ((st = check_kind(in_dtype, head_dim))) return st;
+  if (o_dtype != FA_FP32 && o_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
     return st;
+  if (total_q == 0) return FA_OK;  // no query row: nothing to compute
 
   fa::FwdParams p = {};
   p.q = q;
-  p.k = k_cache;
-  p.v = v_cache;
-  p.o_part = o_part;
-  p.lse_part = lse_part;
-  p.block_table = block_table;
-  p.max_pages = max_pages_per_seq;
-  p.page_size = page_size;
-  p.page_shift = -1;
-  if ((page_size & (page_size - 1)) == 0)
-    for (int sh = 0; sh < 31; ++sh)
-      if ((1 << sh) == page_size) p.page_shift = sh;
-  p.num_splits = num_splits;
-  p.row_stride = heads * head_dim;
-  p.page_stride = (int64_t)page_size * heads * head_dim;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.o_bf16 = o_dtype == FA_BF16;
+  p.num_splits = 1;
+  p.cu_seqlens_q = cu_seqlens_q;
+  p.cu_seqlens_k = cu_seqlens_k;
+  p.total_q = total_q;
+  p.total_k = total_k;
   const int tile = in_dtype == FA_BF16 ? fa::BF16_BM : fa::F32_BM;
-  fill_common(p, batch, heads, seqlen_q, seqlen_k, softmax_scale, causal, window_left,
+  fill_common(p, batch, heads, max_seqlen_q, max_seqlen_k, softmax_scale, causal, window_left,
               window_right, alibi_slopes, softcap, tile);
-  const int64_t c = split_len(seqlen_k, num_splits, page_size);
-  if (c > kMaxSeq) return FA_ERR_SHAPE;
-  p.split_len = (int)c;
-  if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
+  if ((int64_t)p.num_q_tiles * heads * batch > kMaxGroups) return FA_ERR_SHAPE;
 
   const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
-  Launcher fn = in_dtype != FA_BF16 ? pick_f32<true>(head_dim, sc, al)
-                : seqlen_q == 1     ? pick_decode(head_dim, sc, al)
-                                    : pick_bf16<fa::FWD_PAGED_SPLIT>(head_dim, sc, al);
+  Launcher fn = in_dtype == FA_BF16 ? pick_bf16<fa::FWD_CONTIG>(head_dim, sc, al)
+                                    : pick_f32<false>(head_dim, sc, al);
   return fn(p, stream) ? FA_ERR_HIP : FA_OK;
 }
 

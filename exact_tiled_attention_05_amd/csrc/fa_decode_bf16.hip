@@ -62,15 +62,17 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
   const int c = lane % CH, g = lane / CH;
   const WorkItem wi = decode_work<true>(p);
   const int b = wi.b, h = wi.h, s = wi.s;
+  const SeqInfo si = seq_info(p, b, h);
+  const int nk = si.nk;
 
   int slo, shi;
-  split_range(p, s, slo, shi);
-  const int ip = p.Nk - 1;  // the single query row, aligned to the last key
+  split_range(p, nk, s, slo, shi);
+  const int ip = nk - 1;  // the single query row, aligned to the sequence's last key
   int lo = slo, hi = shi;
   if (p.window_left >= 0) lo = max(lo, ip - p.window_left);
   if (p.window_right >= 0) hi = min(hi, ip + p.window_right + 1);
   if (hi <= lo) {
-    write_empty_rows<true>(p, b, h, s, 0, 1, D, tid, kThreads);
+    write_empty_rows<true>(p, si, b, h, s, 0, 1, D, tid, kThreads);
     return;
   }
 
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
     for (int i = tid; i < np; i += kThreads) s_bt[i] = bt_row[p0 + i];
   __syncthreads();
 
-  const u32x4_t qv = *(const u32x4_t*)((const uint16_t*)p.q + q_offset(p, b, 0, h, D) + 8 * c);
+  const u32x4_t qv = *(const u32x4_t*)((const uint16_t*)p.q + q_offset(p, si, 0, h, D) + 8 * c);
   bf16x2_t qp[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {

@@ -188,12 +188,47 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8_t v, float acc) {
   return acc;
 }
 
-__device__ __forceinline__ int64_t q_offset(const FwdParams& p, int b, int row, int h, int D) {
-  return (((int64_t)b * p.Nq + row) * p.H + h) * D;
+// The sequence a workgroup works on: its lengths and where its rows sit.
+struct SeqInfo {
+  int nq, nk;       // query rows and keys of this sequence
+  int64_t q_row0;   // row (of H * D elements) of query 0 in q and o
+  int64_t k_row0;   // row of key 0 in contiguous or packed k and v
+  int64_t lse0;     // lse index of (this head, query 0); the sequence's rows follow
+};
+
+// Packed batches read their offsets from cu_seqlens_q/k, clamped into the
+// tensors and to the stated maxima, so that any contents keep every access in
+// bounds. A batched layout may carry per-sequence key counts (clamped to Nk).
+__device__ __forceinline__ SeqInfo seq_info(const FwdParams& p, int b, int h) {
+  SeqInfo si;
+  if (p.cu_seqlens_q) {
+    const int q0 = min(max(p.cu_seqlens_q[b], 0), p.total_q);
+    const int q1 = min(max(p.cu_seqlens_q[b + 1], q0), p.total_q);
+    const int k0 = min(max(p.cu_seqlens_k[b], 0), p.total_k);
+    const int k1 = min(max(p.cu_seqlens_k[b + 1], k0), p.total_k);
+    si.nq = min(q1 - q0, p.Nq);
+    si.nk = min(k1 - k0, p.Nk);
+    si.q_row0 = q0;
+    si.k_row0 = k0;
+    si.lse0 = (int64_t)h * p.total_q + q0;
+  } else {
+    si.nq = p.Nq;
+    si.nk = p.seqlens_k ? min(max(p.seqlens_k[b], 0), p.Nk) : p.Nk;
+    si.q_row0 = (int64_t)b * p.Nq;
+    si.k_row0 = (int64_t)b * p.Nk;
+    si.lse0 = ((int64_t)b * p.H + h) * p.Nq;
+  }
+  return si;
+}
+
+__device__ __forceinline__ int64_t q_offset(const FwdParams& p, const SeqInfo& si, int row, int h,
+                                            int D) {
+  return ((si.q_row0 + row) * p.H + h) * D;
 }
 
 template <bool PAGED>
-__device__ __forceinline__ int64_t kv_offset(const FwdParams& p, int b, int key, int h, int D) {
+__device__ __forceinline__ int64_t kv_offset(const FwdParams& p, int b, const SeqInfo& si, int key,
+                                             int h, int D) {
   if constexpr (PAGED) {
     int idx, slot;
     if (p.page_shift >= 0) {
@@ -206,15 +241,18 @@ __device__ __forceinline__ int64_t kv_offset(const FwdParams& p, int b, int key,
     const int page = p.block_table[(int64_t)b * p.max_pages + idx];
     return (((int64_t)page * p.page_size + slot) * p.H + h) * D;
   } else {
-    return (((int64_t)b * p.Nk + key) * p.H + h) * D;
+    return ((si.k_row0 + key) * p.H + h) * D;
   }
 }
 
-// Split range [slo, shi) of split s (whole sequence when not split).
-__device__ __forceinline__ void split_range(const FwdParams& p, int s, int& slo, int& shi) {
-  const int64_t lo = (int64_t)s * p.split_len;
-  slo = (int)min<int64_t>(p.Nk, lo);
-  shi = (int)min<int64_t>(p.Nk, lo + p.split_len);
+// Keys [slo, shi) of split s of a sequence with nk keys: chunks of
+// ceil(nk / num_splits) keys rounded up to a multiple of split_align.
+__device__ __forceinline__ void split_range(const FwdParams& p, int nk, int s, int& slo, int& shi) {
+  const int64_t a = p.split_align;
+  const int64_t c = ((nk + (int64_t)p.num_splits - 1) / p.num_splits + a - 1) / a * a;
+  const int64_t lo = (int64_t)s * c;
+  slo = (int)min<int64_t>(nk, lo);
+  shi = (int)min<int64_t>(nk, lo + c);
 }
 
 // Store one lane's 4 consecutive output values of a row (normalised).
@@ -233,15 +271,15 @@ __device__ __forceinline__ void store_out4(const FwdParams& p, int64_t off, floa
 
 // Output of a workgroup whose rows see no key at all: O = 0, LSE = -inf.
 template <bool PAGED>
-__device__ void write_empty_rows(const FwdParams& p, int b, int h, int s, int q0, int q1, int D,
-                                 int tid, int nthreads) {
+__device__ void write_empty_rows(const FwdParams& p, const SeqInfo& si, int b, int h, int s,
+                                 int q0, int q1, int D, int tid, int nthreads) {
   const int n = (q1 - q0) * D;
   for (int idx = tid; idx < n; idx += nthreads) {
     const int row = q0 + idx / D, d = idx % D;
     if constexpr (PAGED) {
       p.o_part[((((int64_t)s * p.B + b) * p.H + h) * p.Nq + row) * D + d] = 0.0f;
     } else {
-      const int64_t o = q_offset(p, b, row, h, D) + d;
+      const int64_t o = q_offset(p, si, row, h, D) + d;
       if (p.o_bf16)
         ((__bf16*)p.o)[o] = (__bf16)0.0f;
       else
@@ -252,15 +290,15 @@ __device__ void write_empty_rows(const FwdParams& p, int b, int h, int s, int q0
     if constexpr (PAGED) {
       p.lse_part[(((int64_t)s * p.B + b) * p.H + h) * p.Nq + row] = kNegInf;
     } else if (p.lse) {
-      p.lse[((int64_t)b * p.H + h) * p.Nq + row] = kNegInf;
+      p.lse[si.lse0 + row] = kNegInf;
     }
   }
 }
 
 // Decode the flat workgroup id: head fastest, then batch, then split, then the
-// query tile, heaviest (last) tile first.
+// query tile counted from the sequence's last (heaviest) tile.
 struct WorkItem {
-  int h, b, s, qt;
+  int h, b, s, rank;
 };
 template <bool PAGED>
 __device__ __forceinline__ WorkItem decode_work(const FwdParams& p) {
@@ -275,8 +313,14 @@ __device__ __forceinline__ WorkItem decode_work(const FwdParams& p) {
     w.s = L % p.num_splits;
     L /= p.num_splits;
   }
-  w.qt = p.num_q_tiles - 1 - L;
+  w.rank = L;
   return w;
+}
+
+// Query tile of a work item in a sequence of nq rows; negative when the
+// sequence has fewer tiles than the longest one.
+__device__ __forceinline__ int query_tile(const WorkItem& w, int nq, int tile_rows) {
+  return (nq + tile_rows - 1) / tile_rows - 1 - w.rank;
 }
 
 }  // namespace fa

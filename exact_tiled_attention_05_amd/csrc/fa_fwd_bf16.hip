@@ -131,23 +131,27 @@ void fwd_bf16_kernel(FwdParams p) {
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
   const WorkItem wi = decode_work<SPLIT>(p);
   const int b = wi.b, h = wi.h, s = wi.s;
+  const SeqInfo si = seq_info(p, b, h);
+  const int nq = si.nq, nk = si.nk;
+  const int qt = query_tile(wi, nq, kBM);
+  if (qt < 0) return;  // a packed sequence shorter than the longest
 
-  const int off = p.Nk - p.Nq;
-  int slo = 0, shi = p.Nk;
-  if constexpr (SPLIT) split_range(p, s, slo, shi);
+  const int off = nk - nq;
+  int slo = 0, shi = nk;
+  if constexpr (SPLIT) split_range(p, nk, s, slo, shi);
 
-  const int q0 = wi.qt * kBM;
-  const int q1 = min(p.Nq, q0 + kBM);
+  const int q0 = qt * kBM;
+  const int q1 = min(nq, q0 + kBM);
   const KeyBounds wg = key_bounds(q0, q1, off, slo, shi, p.window_left, p.window_right);
   if (wg.hi <= wg.lo) {
-    write_empty_rows<SPLIT>(p, b, h, s, q0, q1, D, tid, kThreads);
+    write_empty_rows<SPLIT>(p, si, b, h, s, q0, q1, D, tid, kThreads);
     return;
   }
 
   // This wavefront's rows and keys.
   const int wq0 = q0 + 32 * w;
-  const int wq1 = min(p.Nq, wq0 + 32);
-  const bool wave_live = wq0 < p.Nq;
+  const int wq1 = min(nq, wq0 + 32);
+  const bool wave_live = wq0 < nq;
   const KeyBounds wk = key_bounds(wq0, max(wq1, wq0 + 1), off, slo, shi, p.window_left,
                                   p.window_right);
   const int row = wq0 + r;
@@ -160,11 +164,11 @@ void fwd_bf16_kernel(FwdParams p) {
   // Q fragment: row `row`, columns 16*ks + 8*h2 .. +7 (the B operand of S^T = K Q^T).
   bf16x8_t qf[KS];
   {
-    const uint16_t* qp = (const uint16_t*)p.q + q_offset(p, b, min(row, p.Nq - 1), h, D) + 8 * h2;
+    const uint16_t* qp = (const uint16_t*)p.q + q_offset(p, si, min(row, nq - 1), h, D) + 8 * h2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4_t x = *(const u32x4_t*)(qp + 16 * ks);
-      if (row >= p.Nq) x = u32x4_t{0, 0, 0, 0};
+      if (row >= nq) x = u32x4_t{0, 0, 0, 0};
       qf[ks] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
@@ -181,8 +185,8 @@ void fwd_bf16_kernel(FwdParams p) {
   // first key and bounded by the end of the last key, so rows past the end
   // arrive as zeros; the per-lane byte offsets are fixed.
   const int64_t row_bytes = 2 * (int64_t)p.H * D;
-  const int64_t bh_bytes = 2 * (((int64_t)b * p.Nk * p.H + h) * D);
-  const int64_t end_bytes = (int64_t)(p.Nk - 1) * row_bytes + 2 * D;
+  const int64_t bh_bytes = 2 * ((si.k_row0 * p.H + h) * D);
+  const int64_t end_bytes = (int64_t)(nk - 1) * row_bytes + 2 * D;
   const char* kbh = (const char*)p.k + bh_bytes;
   const char* vbh = (const char*)p.v + bh_bytes;
   unsigned lane_bytes[LOADS];
@@ -213,8 +217,8 @@ void fwd_bf16_kernel(FwdParams p) {
         const int ld = LOADS * wu + i;
         const int trow = ROWS_PER_LOAD * ld + lane / CPR;
         const int chunk = (lane % CPR) ^ swz<D>(trow);
-        const int key = min(j0 + trow, p.Nk - 1);
-        const int64_t o = kv_offset<PAGED>(p, b, key, h, D) + 8 * chunk;
+        const int key = min(j0 + trow, nk - 1);
+        const int64_t o = kv_offset<PAGED>(p, b, si, key, h, D) + 8 * chunk;
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)(kg + o), (lds_ptr_t)(kdst + 512 * ld), 16, 0,
                                          0);
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)(vg + o), (lds_ptr_t)(vdst + 512 * ld), 16, 0,
@@ -408,7 +412,7 @@ void fwd_bf16_kernel(FwdParams p) {
   if (!wave_live) return;
   const float l_tot = half_sum(l_run);
   const float l_ex = half_sum(l_exact);
-  if (row >= p.Nq) return;
+  if (row >= nq) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse = l_ex > 0.0f ? (m_run * c + __log2f(l_ex)) * kLn2 : kNegInf;
   if constexpr (SPLIT) {
@@ -424,14 +428,14 @@ void fwd_bf16_kernel(FwdParams p) {
       }
     if (h2 == 0) p.lse_part[ro] = lse;
   } else {
-    const int64_t ob = q_offset(p, b, row, h, D);
+    const int64_t ob = q_offset(p, si, row, h, D);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         store_out4(p, ob + 32 * db + 8 * g + 4 * h2, oacc[db][4 * g] * inv,
                    oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-    if (h2 == 0 && p.lse) p.lse[((int64_t)b * p.H + h) * p.Nq + row] = lse;
+    if (h2 == 0 && p.lse) p.lse[si.lse0 + row] = lse;
   }
 }
 

@@ -28,16 +28,20 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
   const int lane = threadIdx.x, r = lane & 31, h2 = lane >> 5;
   const WorkItem wi = decode_work<PAGED>(p);
   const int b = wi.b, h = wi.h, s = wi.s;
+  const SeqInfo si = seq_info(p, b, h);
+  const int nq = si.nq, nk = si.nk;
+  const int qt = query_tile(wi, nq, F32_BM);
+  if (qt < 0) return;  // a packed sequence shorter than the longest
 
-  const int off = p.Nk - p.Nq;
-  int slo = 0, shi = p.Nk;
-  if constexpr (PAGED) split_range(p, s, slo, shi);
+  const int off = nk - nq;
+  int slo = 0, shi = nk;
+  if constexpr (PAGED) split_range(p, nk, s, slo, shi);
 
-  const int q0 = wi.qt * F32_BM;
-  const int q1 = min(p.Nq, q0 + F32_BM);
+  const int q0 = qt * F32_BM;
+  const int q1 = min(nq, q0 + F32_BM);
   const KeyBounds wk = key_bounds(q0, q1, off, slo, shi, p.window_left, p.window_right);
   if (wk.hi <= wk.lo) {
-    write_empty_rows<PAGED>(p, b, h, s, q0, q1, D, lane, kThreads);
+    write_empty_rows<PAGED>(p, si, b, h, s, q0, q1, D, lane, kThreads);
     return;
   }
   const int row = q0 + r;
@@ -49,9 +53,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
 
   float qf[D / 2];
   {
-    const float* qp = (const float*)p.q + q_offset(p, b, min(row, p.Nq - 1), h, D) + h2;
+    const float* qp = (const float*)p.q + q_offset(p, si, min(row, nq - 1), h, D) + h2;
 #pragma unroll
-    for (int ks = 0; ks < D / 2; ++ks) qf[ks] = row < p.Nq ? qp[2 * ks] : 0.0f;
+    for (int ks = 0; ks < D / 2; ++ks) qf[ks] = row < nq ? qp[2 * ks] : 0.0f;
   }
 
   f32x16_t oacc[NDB];
@@ -66,8 +70,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
       const int kk = idx / (D / 4), c = idx % (D / 4);
       const int key = j0 + kk;
       f32x4_t kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-      if (key < p.Nk) {
-        const int64_t o = kv_offset<PAGED>(p, b, key, h, D) + 4 * c;
+      if (key < nk) {
+        const int64_t o = kv_offset<PAGED>(p, b, si, key, h, D) + 4 * c;
         kx = *(const f32x4_t*)((const float*)p.k + o);
         vx = *(const f32x4_t*)((const float*)p.v + o);
       }
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
   }
 
   const float l_tot = half_sum(l_run);
-  if (row >= p.Nq) return;
+  if (row >= nq) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse = l_tot > 0.0f ? (m_run * c + __log2f(l_tot)) * kLn2 : kNegInf;
   if constexpr (PAGED) {
@@ -133,14 +137,14 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
       }
     if (h2 == 0) p.lse_part[ro] = lse;
   } else {
-    const int64_t ob = q_offset(p, b, row, h, D);
+    const int64_t ob = q_offset(p, si, row, h, D);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         store_out4(p, ob + 32 * db + 8 * g + 4 * h2, oacc[db][4 * g] * inv,
                    oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-    if (h2 == 0 && p.lse) p.lse[((int64_t)b * p.H + h) * p.Nq + row] = lse;
+    if (h2 == 0 && p.lse) p.lse[si.lse0 + row] = lse;
   }
 }
 

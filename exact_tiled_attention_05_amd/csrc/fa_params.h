@@ -4,24 +4,31 @@
 
 namespace fa {
 
-// One forward launch: contiguous (fa_fwd) or paged + split (fa_fwd_splitkv).
+// One forward launch: contiguous (fa_fwd, fa_fwd_split), packed variable-length
+// (fa_fwd_varlen) or paged + split (fa_fwd_splitkv, fa_fwd_splitkv_seqlens).
 struct FwdParams {
-  const void* q;
-  const void* k;            // contiguous [B, Nk, H, D] or page pool [P, ps, H, D]
+  const void* q;            // [B, Nq, H, D], or packed [total_q, H, D]
+  const void* k;            // contiguous [B, Nk, H, D], packed [total_k, H, D] or page pool [P, ps, H, D]
   const void* v;
-  void* o;                  // [B, Nq, H, D] (o_bf16 selects bf16 vs fp32)
-  float* lse;               // [B, H, Nq] or nullptr
+  void* o;                  // like q (o_bf16 selects bf16 vs fp32)
+  float* lse;               // [B, H, Nq], packed [H, total_q], or nullptr
   float* o_part;            // [S, B, H, Nq, D] (split launches)
   float* lse_part;          // [S, B, H, Nq]
   const int* block_table;   // [B, max_pages] (paged launches)
   const float* alibi;       // [H] ALiBi slopes (natural-log units); nullptr = off
-  int B, H, Nq, Nk;
+  const int* cu_seqlens_q;  // [B + 1] packed batch offsets, or nullptr (batched layout)
+  const int* cu_seqlens_k;  // [B + 1]
+  const int* seqlens_k;     // [B] per-sequence key counts of a batched layout, or nullptr
+  int B, H;
+  int Nq, Nk;               // query rows and keys per sequence (packed: the maxima)
+  int total_q, total_k;     // rows of the packed tensors
   int max_pages, page_size;
   int page_shift;           // log2(page_size) when it is a power of two, else -1
   int row_stride;           // H * D: elements between consecutive keys of one page
   int64_t page_stride;      // page_size * H * D: elements per page
-  int num_splits, split_len;
-  int num_q_tiles;
+  int num_splits;
+  int split_align;          // split chunks are whole multiples of this many keys
+  int num_q_tiles;          // query tiles of the longest sequence
   int window_left;          // -1 = unbounded
   int window_right;         // -1 = unbounded; causal arrives here as 0
   int o_bf16;

@@ -137,6 +137,64 @@ int fa_fwd_split(const void* q, const void* k, const void* v, int in_dtype,
                  const float* alibi_slopes, float softcap, void* stream);
 
 /*
+ * fa_fwd_splitkv_seqlens - fa_fwd_splitkv over a cache whose sequences hold
+ * different numbers of keys (variable sequence lengths, named as a feature in
+ * the closing section of "FlashAttention深度解析：从算法创新到产业变革的全面影响";
+ * the paged cache and its block_table are the update article's v2.5 entry).
+ *
+ * cache_seqlens: device int32 [batch]; sequence b holds keys [0, cache_seqlens[b])
+ * and is treated exactly as fa_fwd_splitkv treats a batch of one sequence with
+ * seqlen_k = cache_seqlens[b]: its causal/window/ALiBi geometry is aligned to
+ * its own last key (off = cache_seqlens[b] - seqlen_q), and its split chunks are
+ * C_b = ceil(cache_seqlens[b] / num_splits) rounded up to a multiple of
+ * page_size (a sequence with 0 keys gets o_part = 0 and lse_part = -inf in every
+ * split). Rows of the cache past a sequence's length are never read.
+ *
+ * max_seqlen_k bounds the lengths and sizes the table: max_pages_per_seq *
+ * page_size >= max_seqlen_k. The lengths live in device memory and are not
+ * checked on the host; each is clamped to [0, max_seqlen_k] on the device.
+ * Other arguments and layouts as fa_fwd_splitkv. NULL cache_seqlens is
+ * FA_ERR_NULL.
+ */
+int fa_fwd_splitkv_seqlens(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
+                           const int* block_table, int max_pages_per_seq, int page_size,
+                           const int* cache_seqlens, float* o_part, float* lse_part,
+                           int num_splits, int batch, int heads, int seqlen_q, int max_seqlen_k,
+                           int head_dim, float softmax_scale, int causal, int window_left,
+                           int window_right, const float* alibi_slopes, float softcap,
+                           void* stream);
+
+/*
+ * fa_fwd_varlen - exact attention forward over a packed batch of sequences of
+ * different lengths (variable sequence lengths: closing section of
+ * "FlashAttention深度解析：从算法创新到产业变革的全面影响"). Each sequence is its
+ * own attention problem, computed as fa_fwd computes one batch entry, with its
+ * mask and ALiBi distances aligned to its own bottom-right corner
+ * (off_b = nk_b - nq_b, the update article's v2.1 rule per sequence).
+ *
+ *   q, o           [total_q, heads, head_dim]   rows of sequence b: [cu_seqlens_q[b], cu_seqlens_q[b+1])
+ *   k, v           [total_k, heads, head_dim]   rows of sequence b: [cu_seqlens_k[b], cu_seqlens_k[b+1])
+ *   lse            [heads, total_q] float32, or NULL
+ *   cu_seqlens_q/k device int32 [batch + 1], non-decreasing, starting at 0
+ *
+ * max_seqlen_q (>= 1) and max_seqlen_k (>= 0) bound the sequence lengths and
+ * size the launch. The offsets live in device memory and are not checked on
+ * the host; on the device they are clamped into [0, total] and each length to
+ * its maximum, so every access stays inside the tensors, but rows of a
+ * sequence beyond max_seqlen_q, and rows that no sequence owns, are not
+ * written. A sequence with no key gets O = 0 and LSE = -inf. total_q = 0
+ * returns FA_OK with nothing launched; q/o (k/v) may be NULL when total_q
+ * (total_k) is 0. Dtypes, head_dim, masks and scores as fa_fwd.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, int in_dtype,
+                  void* o, int o_dtype, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int batch, int heads, int total_q, int total_k,
+                  int max_seqlen_q, int max_seqlen_k, int head_dim,
+                  float softmax_scale, int causal, int window_left, int window_right,
+                  const float* alibi_slopes, float softcap, void* stream);
+
+/*
  * fa_splitkv_combine - the separate reduce step that merges split partials
  * (the update article's v2.2 entry): for every (b, h, i),
  *   L = ln(sum_s exp(lse_part[s])),  O = sum_s exp(lse_part[s] - L) * o_part[s].

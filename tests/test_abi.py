@@ -29,8 +29,10 @@ def declared_functions():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_splitkv_combine", "fa_status_string"):
+    for n in ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
+              "fa_fwd_varlen", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len"):
         assert n in names
+    assert set(fa.EXPORTED) == set(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -159,3 +161,56 @@ def test_split_chunk_len_for_contiguous_splits():
 ])
 def test_fa_splitkv_combine_rejects(kw, code):
     assert comb(**kw) == code
+
+
+def split_seqlens(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, in_dtype=1, bt=FAKE, maxp=4, ps=16, sl=FAKE, op=FAKE, lp=FAKE,
+             S=2, batch=1, heads=1, seqlen_q=1, max_k=64, head_dim=128, scale=0.1, causal=1,
+             wl=-1, wr=-1, alibi=None, softcap=0.0, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_fwd_splitkv_seqlens(
+        a["q"], a["k"], a["v"], a["in_dtype"], a["bt"], a["maxp"], a["ps"], a["sl"], a["op"],
+        a["lp"], a["S"], a["batch"], a["heads"], a["seqlen_q"], a["max_k"], a["head_dim"],
+        a["scale"], a["causal"], a["wl"], a["wr"], a["alibi"], a["softcap"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sl=None), NULL), (dict(bt=None), NULL), (dict(op=None), NULL), (dict(k=None), NULL),
+    (dict(S=0), SHAPE), (dict(max_k=0), SHAPE), (dict(maxp=3, ps=16, max_k=64), SHAPE),
+    (dict(seqlen_q=0), SHAPE), (dict(head_dim=32), UNSUP), (dict(in_dtype=9), UNSUP),
+    (dict(causal=1, wr=3), MASK), (dict(scale=-2.0), VALUE),
+])
+def test_fa_fwd_splitkv_seqlens_rejects(kw, code):
+    assert split_seqlens(**kw) == code
+
+
+def varlen(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, in_dtype=1, o=FAKE, o_dtype=0, lse=None, cq=FAKE, ck=FAKE,
+             batch=2, heads=1, total_q=10, total_k=12, max_q=6, max_k=8, head_dim=64, scale=0.125,
+             causal=0, wl=-1, wr=-1, alibi=None, softcap=0.0, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_fwd_varlen(
+        a["q"], a["k"], a["v"], a["in_dtype"], a["o"], a["o_dtype"], a["lse"], a["cq"], a["ck"],
+        a["batch"], a["heads"], a["total_q"], a["total_k"], a["max_q"], a["max_k"],
+        a["head_dim"], a["scale"], a["causal"], a["wl"], a["wr"], a["alibi"], a["softcap"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cq=None), NULL), (dict(ck=None), NULL), (dict(q=None), NULL), (dict(o=None), NULL),
+    (dict(k=None), NULL), (dict(v=None), NULL),
+    (dict(batch=0), SHAPE), (dict(heads=0), SHAPE), (dict(total_q=-1), SHAPE),
+    (dict(total_k=-1), SHAPE), (dict(max_q=0), SHAPE), (dict(max_k=-1), SHAPE),
+    (dict(max_q=(1 << 28) + 1), SHAPE),
+    (dict(head_dim=96), UNSUP), (dict(in_dtype=4), UNSUP), (dict(o_dtype=2), UNSUP),
+    (dict(wl=-2), MASK), (dict(causal=1, wr=1), MASK), (dict(scale=math.nan), VALUE),
+])
+def test_fa_fwd_varlen_rejects(kw, code):
+    assert varlen(**kw) == code
+
+
+def test_fa_fwd_varlen_empty_pack_launches_nothing():
+    # No query row: the call returns before any HIP call (so it runs without a GPU),
+    # and tensors of zero rows may be NULL.
+    assert varlen(total_q=0, q=None, o=None) == OK
+    assert varlen(total_q=0, total_k=0, q=None, o=None, k=None, v=None, max_k=0) == OK

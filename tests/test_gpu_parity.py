@@ -298,3 +298,168 @@ def test_combine_matches_oracle_on_random_partials():
     ro, rl = O.combine_ref(op, lp)        # [B, H, nq, d]
     check(o.cpu().numpy().transpose(0, 2, 1, 3), lse.cpu().numpy(), ro, rl, "fp32", "combine")
 
+
+
+# --------------------------------------------------------------------------
+# Variable sequence lengths: packed batches (fa_fwd_varlen)
+# --------------------------------------------------------------------------
+VARLEN_CASES = [
+    # (dtype, d, H, [(nq, nk), ...], causal, wl, wr, alibi, cap)
+    ("bf16", 128, 2, [(1, 1), (17, 300), (128, 128), (129, 64), (300, 1000), (0, 5), (7, 0),
+                      (255, 257)], True, -1, -1, False, 0.0),
+    ("bf16", 64, 3, [(64, 64), (130, 500), (1, 700), (200, 3), (33, 33)], True, 60, 0, True, 0.0),
+    ("bf16", 128, 2, [(100, 100), (250, 140), (3, 400)], False, -1, -1, True, 20.0),
+    ("bf16", 64, 2, [(129, 129), (0, 0), (90, 2000)], False, 30, 30, False, 8.0),
+    ("fp32", 64, 2, [(1, 1), (33, 100), (70, 40), (0, 3), (5, 0)], True, -1, -1, False, 0.0),
+    ("fp32", 128, 2, [(40, 90), (64, 64)], True, 20, 0, True, 5.0),
+]
+
+
+def run_varlen(q, k, v, cq, ck, dtype, maxq, maxk, scale, causal, wl, wr, slopes, cap,
+               out_dtype=torch.float32):
+    ts = None if slopes is None else torch.from_numpy(np.asarray(slopes, np.float32)).cuda()
+    o, lse = fa.attention_varlen(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype),
+                                 torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda(), maxq,
+                                 maxk, scale, causal, wl, wr, ts, cap, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES)
+def test_varlen_packed_small(case):
+    dtype, d, H, lens, causal, wl, wr, alibi, cap = case
+    say(f"varlen {case}")
+    lq, lk = [a for a, _ in lens], [b for _, b in lens]
+    q, k, v, cq, ck = W.gen_varlen(5000 + VARLEN_CASES.index(case), lq, lk, H, d,
+                                   2.0 if cap else 1.0, dtype)
+    slopes = W.alibi_slopes(H) if alibi else None
+    scale = 1.0 / np.sqrt(d)
+    o, lse = run_varlen(q, k, v, cq, ck, dtype, max(lq), max(lk), scale, causal, wl, wr,
+                        slopes, cap)
+    ro, rl = O.attention_varlen_ref(W.to_float(q, dtype), W.to_float(k, dtype),
+                                    W.to_float(v, dtype), cq, ck, scale, causal, wl, wr, slopes,
+                                    cap)
+    check(o, lse, ro, rl, dtype, f"varlen {case}")
+
+
+def test_varlen_equal_lengths_bitwise_equals_batched():
+    """A pack of equal-length sequences is the batched problem: the same kernel
+    computes the same tiles, so O and LSE match fa_fwd bit for bit."""
+    B, nq, nk, H, d = 3, 200, 333, 4, 128
+    q, k, v = qkv_case(90, B, nq, nk, H, d, "bf16")
+    ob, lb = run_fwd(q, k, v, "bf16", 0.09, True, 100, 0, W.alibi_slopes(H), 0.0)
+    cq, ck = W.cu_seqlens([nq] * B), W.cu_seqlens([nk] * B)
+    ov, lv = run_varlen(q.reshape(B * nq, H, d), k.reshape(B * nk, H, d),
+                        v.reshape(B * nk, H, d), cq, ck, "bf16", nq, nk, 0.09, True, 100, 0,
+                        W.alibi_slopes(H), 0.0)
+    assert np.array_equal(ov, ob.reshape(B * nq, H, d))
+    assert np.array_equal(lv, lb.transpose(1, 0, 2).reshape(H, B * nq))
+
+
+def test_varlen_mixed_lengths_sampled_heads():
+    """Eight causal sequences of seeded lengths up to 2048 at the prefill head
+    shape (16 heads of 128): every row of two heads against the oracle."""
+    H, d = 16, 128
+    lens = W.varlen_lengths(91, 8, 2048)
+    say(f"varlen mixed lengths {lens.tolist()}")
+    q, k, v, cq, ck = W.gen_varlen(91, lens, lens, H, d, 1.0, "bf16")
+    o, lse = run_varlen(q, k, v, cq, ck, "bf16", int(lens.max()), int(lens.max()),
+                        1.0 / np.sqrt(d), True, -1, -1, None, 0.0)
+    heads = [0, 11]
+    ro, rl = O.attention_varlen_ref(W.to_float(q, "bf16"), W.to_float(k, "bf16"),
+                                    W.to_float(v, "bf16"), cq, ck, 1.0 / np.sqrt(d), True,
+                                    heads=heads)
+    check(o[:, heads], lse[heads], ro[:, heads], rl[heads], "bf16", "varlen mixed")
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+
+
+# --------------------------------------------------------------------------
+# Per-sequence cache lengths in the split pass (fa_fwd_splitkv_seqlens)
+# --------------------------------------------------------------------------
+SEQLENS_CASES = [
+    # (dtype, d, H, nq, max_k, page_size, num_splits, seqlens, causal, wl, wr, alibi, cap)
+    ("bf16", 128, 2, 1, 1000, 64, 4, [1000, 0, 1, 513, 64, 999], True, -1, -1, False, 0.0),
+    ("bf16", 64, 3, 1, 777, 16, 16, [777, 5, 300, 0], True, 100, 0, True, 0.0),
+    ("bf16", 128, 2, 1, 4096, 256, 16, [4096, 2047, 2048, 1, 3000], True, -1, -1, True, 30.0),
+    ("bf16", 128, 2, 5, 300, 7, 3, [300, 4, 0, 150], True, 50, 0, False, 10.0),
+    ("bf16", 64, 2, 130, 400, 64, 2, [400, 100, 129, 0], True, -1, -1, True, 0.0),
+    ("bf16", 128, 1, 40, 256, 256, 4, [256, 17, 39, 40, 41], False, -1, -1, False, 0.0),
+    ("fp32", 64, 2, 1, 500, 32, 5, [500, 0, 77], True, -1, -1, False, 0.0),
+    ("fp32", 128, 2, 20, 200, 16, 3, [200, 10, 25], True, -1, -1, True, 5.0),
+]
+
+
+@pytest.mark.parametrize("case", SEQLENS_CASES)
+def test_splitkv_seqlens_small(case):
+    dtype, d, H, nq, nk, ps, S, seqlens, causal, wl, wr, alibi, cap = case
+    say(f"split seqlens {case}")
+    B = len(seqlens)
+    w = W.Workload(0, "split_seqlens", B=B, H=H, Nq=nq, Nk=nk, d=d, dtype=dtype, causal=causal,
+                   paged=True, page_size=ps, pool_factor=1.3, num_splits=S,
+                   seed=6000 + SEQLENS_CASES.index(case))
+    q, kc, vc, bt = W.gen_paged(w, seqlens=seqlens)   # every row past a length is NaN
+    slopes = W.alibi_slopes(H) if alibi else None
+    ts = None if slopes is None else torch.from_numpy(slopes).cuda()
+    scale = 1.0 / np.sqrt(d)
+    tsl = torch.tensor(seqlens, dtype=torch.int32).cuda()
+    o_part, lse_part = fa.attention_paged_splitkv(
+        to_dev(q, dtype), to_dev(kc, dtype), to_dev(vc, dtype), torch.from_numpy(bt).cuda(), nk, S,
+        scale, causal, wl, wr, ts, cap, cache_seqlens=tsl)
+    o, lse = fa.combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    qf = W.to_float(q, dtype)
+    k = np.zeros((B, nk, H, d))
+    v = np.zeros((B, nk, H, d))
+    for b, n in enumerate(seqlens):
+        k[b, :n] = O.paged_gather_ref(W.to_float(kc, dtype), bt, b, n)
+        v[b, :n] = O.paged_gather_ref(W.to_float(vc, dtype), bt, b, n)
+    rop, rlp = O.splitkv_ref(qf, k, v, S, ps, scale, causal, wl, wr, slopes, cap,
+                             seqlens_k=seqlens)
+    check(o_part.cpu().numpy(), lse_part.cpu().numpy(), rop, rlp, dtype, "partials")
+    ro, rl = O.combine_ref(rop, rlp)
+    check(o.cpu().numpy().transpose(0, 2, 1, 3), lse.cpu().numpy(), ro, rl, dtype, "combined")
+
+
+def test_splitkv_seqlens_decode_full_size():
+    """The paged decode shape (8 x 32 heads, 32768-key capacity, 256-key pages,
+    16 splits) with per-sequence lengths from 0 to the capacity; every row past a
+    length is NaN. Sampled (b, h) pairs against the oracle."""
+    w = W.WORKLOADS[4]
+    seqlens = [32768, 1, 0, 20000, 256, 255, 31000, 12345]
+    say(f"cfg4 seqlens {seqlens}: generating inputs")
+    q, kc, vc, bt = W.gen_paged(w, seqlens=seqlens)
+    tq, tk, tv = to_dev(q, w.dtype), to_dev(kc, w.dtype), to_dev(vc, w.dtype)
+    del kc, vc
+    tbt = torch.from_numpy(bt).cuda()
+    tsl = torch.tensor(seqlens, dtype=torch.int32).cuda()
+    o, lse = fa.decode_paged(tq, tk, tv, tbt, w.Nk, w.num_splits, softmax_scale=w.scale,
+                             causal=True, cache_seqlens=tsl)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    assert not np.isnan(o).any()
+    qf = W.to_float(q, w.dtype)
+    for b, h in [(0, 3), (1, 0), (2, 31), (3, 17), (4, 5), (5, 30), (6, 9), (7, 22)]:
+        n = seqlens[b]
+        kb = W.to_float(W.gen_slice(w.seed, W.TENSOR_K, b, h, w.Nk, w.d, w.amp, w.dtype)[:n], w.dtype)
+        vb = W.to_float(W.gen_slice(w.seed, W.TENSOR_V, b, h, w.Nk, w.d, w.amp, w.dtype)[:n], w.dtype)
+        ro, rl = O.attention_bh(qf[b, :, h, :], kb, vb, np.arange(1), 1, w.scale, True)
+        check(o[b, :, h, :], lse[b, h, :], ro, rl, "bf16", f"cfg4 seqlens b{b} h{h}")
+
+
+@pytest.mark.parametrize("dtype,d,nq", [("bf16", 128, 1), ("bf16", 64, 1), ("bf16", 128, 6),
+                                        ("fp32", 64, 3)])
+def test_splitkv_seqlens_uniform_bitwise_equals_splitkv(dtype, d, nq):
+    """Lengths all equal to the capacity reproduce fa_fwd_splitkv bit for bit."""
+    w = W.Workload(0, "uniform", B=3, H=4, Nq=nq, Nk=3000, d=d, dtype=dtype, causal=True,
+                   paged=True, page_size=64, pool_factor=1.2, num_splits=5, seed=92)
+    say(f"seqlens uniform {dtype} d{d} nq{nq}")
+    q, kc, vc, bt = W.gen_paged(w)
+    tq, tk, tv = to_dev(q, dtype), to_dev(kc, dtype), to_dev(vc, dtype)
+    tbt = torch.from_numpy(bt).cuda()
+    full = torch.full((w.B,), w.Nk, dtype=torch.int32).cuda()
+    ts = torch.from_numpy(W.alibi_slopes(w.H)).cuda()
+    a = fa.attention_paged_splitkv(tq, tk, tv, tbt, w.Nk, w.num_splits, w.scale, True, 500, 0, ts,
+                                   cache_seqlens=full)
+    c = fa.attention_paged_splitkv(tq, tk, tv, tbt, w.Nk, w.num_splits, w.scale, True, 500, 0, ts)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
