@@ -8,7 +8,9 @@ One step = one pass of the whole path over one batch of seeded synthetic input:
      with ALiBi and a tanh cap (B=2, H=8, Nq=512, Nk=4096, d=128, bf16).
 `value` is the prefill's algorithmic TFLOP/s (4*B*H*d*allowed pairs over the
 prefill launch time); the decode's algorithmic GB/s and the split forward's
-TFLOP/s are reported beside it.
+TFLOP/s are reported beside it. After the timed steps, the variable-length
+entry points are timed on their own (a packed causal prefill of 8 sequences of
+seeded lengths, and the decode with seeded per-sequence cache lengths).
 Inputs are resident in device memory before the timed region starts.
 
 Prints ONE JSON line on stdout. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -255,6 +257,65 @@ def main():
     t_comb = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
     t_short = np.array([e[3].elapsed_time(e[4]) for e in ev]) * 1e-3
 
+    # ---- variable sequence lengths (side measurements, after the timed steps):
+    # a packed causal prefill of 8 sequences of seeded lengths in [1, 2048] at the
+    # prefill head shape, and the paged decode with seeded per-sequence cache
+    # lengths in [1, 32768] over the same pool.
+    vl = W.varlen_lengths(91, 8, 2048)
+    log(f"generating packed prefill, lengths {vl.tolist()}")
+    vq_np, vk_np, vv_np, vcq, vck = W.gen_varlen(91, vl, vl, wp.H, wp.d, 1.0, "bf16")
+    vq, vk, vv = up(vq_np, "bf16"), up(vk_np, "bf16"), up(vv_np, "bf16")
+    del vq_np, vk_np, vv_np
+    tcq, tck = torch.from_numpy(vcq).to(dev), torch.from_numpy(vck).to(dev)
+    tot = int(vl.sum())
+    vo = torch.empty((tot, wp.H, wp.d), dtype=torch.float32, device=dev)
+    vlse = torch.empty((wp.H, tot), dtype=torch.float32, device=dev)
+    var_flops = 4.0 * wp.H * wp.d * sum(allowed_pairs(int(n), int(n), True, -1, -1) for n in vl)
+    dl = np.random.default_rng([92, 7]).integers(1, wd.Nk + 1, size=wd.B)
+    tdl = torch.from_numpy(dl.astype(np.int32)).to(dev)
+    dl_bytes = (2 * wd.H * wd.d * 2 * int(dl.sum()) + dq.numel() * 2
+                + int(sum(-(-int(n) // wd.page_size) for n in dl)) * 4 + part_bytes + combine_bytes)
+
+    def varlen_prefill():
+        check(fa.fa_fwd_varlen(vq, vk, vv, vo, vlse, tcq, tck, len(vl), wp.H, tot, tot,
+                               int(vl.max()), int(vl.max()), wp.d, wp.scale, True, -1, -1, None,
+                               0.0, stream), "fa_fwd_varlen")
+
+    def seqlens_decode():
+        check(fa.fa_fwd_splitkv_seqlens(dq, dk, dv, dbt, dbt.shape[1], wd.page_size, tdl, o_part,
+                                        lse_part, S, wd.B, wd.H, wd.Nq, wd.Nk, wd.d, wd.scale,
+                                        True, -1, -1, None, 0.0, stream),
+              "fa_fwd_splitkv_seqlens")
+        combine_pass()
+
+    for _ in range(args.warmup):
+        varlen_prefill()
+        seqlens_decode()
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for s in range(K):
+        e = ev2[s]
+        e[0].record(stream)
+        varlen_prefill()
+        e[1].record(stream)
+        seqlens_decode()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    t_var = np.array([e[0].elapsed_time(e[1]) for e in ev2]) * 1e-3
+    t_sld = np.array([e[1].elapsed_time(e[2]) for e in ev2]) * 1e-3
+    assert torch.isfinite(vo).all() and torch.isfinite(do).all()
+    variable = {
+        "packed_prefill": {"lengths": vl.tolist(), "gflop": round(var_flops / 1e9, 4),
+                           "ms": round(t_var.mean() * 1e3, 5),
+                           "ms_median": round(float(np.median(t_var)) * 1e3, 5),
+                           "tflops": round(var_flops / t_var.mean() / 1e12, 3),
+                           "pct_peak": round(100 * var_flops / t_var.mean() / 1e12 / PEAK_BF16_TFLOPS, 2)},
+        "decode_cache_seqlens": {"lengths": dl.tolist(), "gbytes": round(dl_bytes / 1e9, 5),
+                                 "ms": round(t_sld.mean() * 1e3, 5),
+                                 "ms_median": round(float(np.median(t_sld)) * 1e3, 5),
+                                 "gbs": round(dl_bytes / t_sld.mean() / 1e9, 2),
+                                 "pct_peak": round(100 * dl_bytes / t_sld.mean() / 1e9 / PEAK_HBM_GBS, 2)},
+    }
+
     pre_tflops = prefill_flops / t_prefill.mean() / 1e12
     dec_time = (t_split + t_comb).mean()
     dec_gbs = decode_bytes / dec_time / 1e9
@@ -319,6 +380,7 @@ def main():
                               "tflops": round(short_tflops, 3),
                               "pct_peak": round(100 * short_tflops / PEAK_BF16_TFLOPS, 2),
                               "num_splits": SS, "gflop": round(split_flops / 1e9, 4)},
+        "variable_lengths": variable,
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("prefill"),
