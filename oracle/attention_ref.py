@@ -39,6 +39,11 @@ rule applied to that sequence's lengths (off_b = nk_b - nq_b). Two forms:
 * a paged cache with per-sequence key counts: sequence b uses only its first
   seqlens_k[b] cached keys, and its split chunks are cut from that count.
 
+Appending to the cache ("解密FlashAttention：如何让大语言模型推理速度翻倍", the
+sections on the key-value cache and on incremental processing of new tokens):
+each step writes its new keys behind a sequence's cached ones and attends over
+both, the new queries aligned with the new keys.
+
 Conventions the pages leave open (each is stated with its reason where it is
 used): LSE is the natural log of the row's sum of exp over allowed keys; a row
 with no allowed key has O = 0 and LSE = -inf; split chunk length is
@@ -235,6 +240,27 @@ def paged_gather_ref(cache: np.ndarray, block_table: np.ndarray, b: int, nk: int
     return cache[np.asarray(block_table)[b, t // ps], t % ps]
 
 
+def kvcache_append_ref(k_cache: np.ndarray, v_cache: np.ndarray, block_table: np.ndarray,
+                       seqlens, k_new: np.ndarray, v_new: np.ndarray):
+    """Copies of the page pools with the new keys of every sequence written in.
+
+    Row i of k_new[b] / v_new[b] ([B, n_new, H, d]) becomes logical key
+    seqlens[b] + i of sequence b, i.e. pool row
+    [block_table[b, t // page_size], t % page_size] with t = seqlens[b] + i
+    (the update article's v2.5 entry for the page addressing; the inference
+    article's incremental decoding for appending each step's keys to the cache).
+    """
+    kc, vc = k_cache.copy(), v_cache.copy()
+    ps = kc.shape[1]
+    bt = np.asarray(block_table)
+    for b in range(k_new.shape[0]):
+        for i in range(k_new.shape[1]):
+            t = int(seqlens[b]) + i
+            kc[bt[b, t // ps], t % ps] = k_new[b, i]
+            vc[bt[b, t // ps], t % ps] = v_new[b, i]
+    return kc, vc
+
+
 # --------------------------------------------------------------------------
 # Split-KV and its reduce step (flash-attn update article, v2.2 entry)
 # --------------------------------------------------------------------------
@@ -280,6 +306,31 @@ def splitkv_ref(q, k, v, num_splits, page_size, scale, causal=False, window_left
             o_part[s, b, h] = ob
             lse_part[s, b, h] = lb
     return o_part, lse_part
+
+
+def splitkv_append_ref(q, k, v, k_new, v_new, seqlens, num_splits, page_size, scale,
+                       causal=False, window_left=-1, window_right=-1, alibi_slopes=None,
+                       softcap=0.0, bh=None):
+    """Split pass after appending each sequence's new keys to its cache.
+
+    k, v [B, Nk, H, d]: logical cache contents (only keys [0, seqlens[b]) of
+    sequence b are used); k_new, v_new [B, Nq, H, d]: one new key per query
+    row. Sequence b attends over its seqlens[b] cached keys followed by its Nq
+    new ones, so its queries line up with the new keys (bottom-right rule).
+    """
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, nq = q.shape[0], q.shape[1]
+    n_new = [int(n) + nq for n in seqlens]
+    cap = max(n_new + [k.shape[1]])
+    k2 = np.zeros((B, cap) + k.shape[2:])
+    v2 = np.zeros((B, cap) + v.shape[2:])
+    for b, n in enumerate(seqlens):
+        n = int(n)
+        k2[b, :n], v2[b, :n] = k[b, :n], v[b, :n]
+        k2[b, n:n + nq], v2[b, n:n + nq] = k_new[b], v_new[b]
+    return splitkv_ref(q, k2, v2, num_splits, page_size, scale, causal, window_left,
+                       window_right, alibi_slopes, softcap, bh=bh, seqlens_k=n_new)
 
 
 def combine_ref(o_part: np.ndarray, lse_part: np.ndarray):

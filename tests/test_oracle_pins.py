@@ -563,3 +563,61 @@ def test_t20_seqlens_chunks_and_decode_counts():
     _, lc = O.combine_ref(op, lp)
     for b, n in enumerate(seqlens):
         assert (lc[b, 0, 0] == -math.inf) if n == 0 else abs(lc[b, 0, 0] - math.log(n)) < 1e-12
+
+
+# T21-T22: appending the new keys to a paged cache -----------------------------
+def test_t21_kvcache_append_positions_by_hand():
+    """Pages of 2 rows, sequence 0 mapped to pages [3, 0, 1] and holding 3 keys:
+    its new keys 3 and 4 land in page 0 row 1 and page 1 row 0; sequence 1
+    (pages [2, 4], 0 keys) gets new keys 0 and 1 in page 2 rows 0 and 1. No
+    other pool row changes."""
+    H, d = 1, 2
+    pool = rnd(60, 5, 2, H, d)
+    vpool = rnd(61, 5, 2, H, d)
+    bt = np.array([[3, 0, 1], [2, 4, 4]])
+    kn, vn = rnd(62, 2, 2, H, d), rnd(63, 2, 2, H, d)
+    kc, vc = O.kvcache_append_ref(pool, vpool, bt, [3, 0], kn, vn)
+    assert np.array_equal(kc[0, 1], kn[0, 0]) and np.array_equal(kc[1, 0], kn[0, 1])
+    assert np.array_equal(kc[2, 0], kn[1, 0]) and np.array_equal(kc[2, 1], kn[1, 1])
+    assert np.array_equal(vc[0, 1], vn[0, 0]) and np.array_equal(vc[2, 1], vn[1, 1])
+    changed = {(0, 1), (1, 0), (2, 0), (2, 1)}
+    for pg in range(5):
+        for row in range(2):
+            if (pg, row) not in changed:
+                assert np.array_equal(kc[pg, row], pool[pg, row])
+                assert np.array_equal(vc[pg, row], vpool[pg, row])
+
+
+@pytest.mark.parametrize("nq,causal,wl,wr", [(1, True, -1, -1), (3, True, -1, -1), (2, False, 4, 1),
+                                            (4, True, 2, 0)])
+def test_t22_append_then_attend_equals_attention_over_the_joined_keys(nq, causal, wl, wr):
+    B, nk, H, d, S, ps = 3, 12, 2, 3, 3, 2
+    seqlens = [5, 0, 8]
+    q = rnd(64, B, nq, H, d)
+    k, v = rnd(65, B, nk, H, d), rnd(66, B, nk, H, d)
+    kn, vn = rnd(67, B, nq, H, d), rnd(68, B, nq, H, d)
+    slopes = np.array([0.3, 0.1])
+    op, lp = O.splitkv_append_ref(q, k, v, kn, vn, seqlens, S, ps, 0.7, causal, wl, wr, slopes, 3.0)
+    oc, lc = O.combine_ref(op, lp)
+    for b, n in enumerate(seqlens):
+        kj = np.concatenate([k[b, :n], kn[b]])[None]
+        vj = np.concatenate([v[b, :n], vn[b]])[None]
+        ou, lu = O.attention_ref(q[b:b + 1], kj, vj, 0.7, causal, wl, wr, slopes, 3.0)
+        np.testing.assert_allclose(oc[b], np.transpose(ou[0], (1, 0, 2)), atol=1e-12)
+        np.testing.assert_allclose(lc[b], lu[0], atol=1e-12)
+
+
+def test_t22_decode_after_append_sees_every_key():
+    """One new token per sequence, Q = 0, causal: it sees its n_b cached keys and
+    itself, so LSE = ln(n_b + 1) and O is the mean of those n_b + 1 V rows."""
+    B, nk, H, d = 4, 9, 1, 2
+    seqlens = [0, 3, 8, 5]
+    q = np.zeros((B, 1, H, d))
+    k, v = rnd(69, B, nk, H, d), rnd(70, B, nk, H, d)
+    kn, vn = rnd(71, B, 1, H, d), rnd(72, B, 1, H, d)
+    op, lp = O.splitkv_append_ref(q, k, v, kn, vn, seqlens, 4, 1, 1.0, True)
+    oc, lc = O.combine_ref(op, lp)
+    for b, n in enumerate(seqlens):
+        assert abs(lc[b, 0, 0] - math.log(n + 1)) < 1e-12
+        want = np.concatenate([v[b, :n, 0], vn[b, :, 0]]).mean(axis=0)
+        np.testing.assert_allclose(oc[b, 0, 0], want, atol=1e-12)
