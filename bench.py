@@ -10,7 +10,8 @@ One step = one pass of the whole path over one batch of seeded synthetic input:
 prefill launch time); the decode's algorithmic GB/s and the split forward's
 TFLOP/s are reported beside it. After the timed steps, the variable-length
 entry points are timed on their own (a packed causal prefill of 8 sequences of
-seeded lengths, and the decode with seeded per-sequence cache lengths).
+seeded lengths, the decode with seeded per-sequence cache lengths, and the
+decode step that appends one key per sequence before attending).
 Inputs are resident in device memory before the timed region starts.
 
 Prints ONE JSON line on stdout. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -276,6 +277,19 @@ def main():
     dl_bytes = (2 * wd.H * wd.d * 2 * int(dl.sum()) + dq.numel() * 2
                 + int(sum(-(-int(n) // wd.page_size) for n in dl)) * 4 + part_bytes + combine_bytes)
 
+    # decode step with a fused append: every sequence holds 32767 cached keys and
+    # appends one, so it attends over the same 32768 keys as the decode above.
+    an = torch.full((wd.B,), wd.Nk - 1, dtype=torch.int32, device=dev)
+    akn = up(W.gen_tensor(94, W.TENSOR_K, wd.B, 1, wd.H, wd.d, 1.0, "bf16"), "bf16")
+    avn = up(W.gen_tensor(94, W.TENSOR_V, wd.B, 1, wd.H, wd.d, 1.0, "bf16"), "bf16")
+
+    def append_decode():
+        check(fa.fa_fwd_splitkv_append(dq, akn, avn, dk, dv, dbt, dbt.shape[1], wd.page_size, an,
+                                       o_part, lse_part, S, wd.B, wd.H, wd.Nq, wd.Nk, wd.d,
+                                       wd.scale, True, -1, -1, None, 0.0, stream),
+              "fa_fwd_splitkv_append")
+        combine_pass()
+
     def varlen_prefill():
         check(fa.fa_fwd_varlen(vq, vk, vv, vo, vlse, tcq, tck, len(vl), wp.H, tot, tot,
                                int(vl.max()), int(vl.max()), wp.d, wp.scale, True, -1, -1, None,
@@ -291,7 +305,8 @@ def main():
     for _ in range(args.warmup):
         varlen_prefill()
         seqlens_decode()
-    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        append_decode()
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     for s in range(K):
         e = ev2[s]
         e[0].record(stream)
@@ -299,9 +314,13 @@ def main():
         e[1].record(stream)
         seqlens_decode()
         e[2].record(stream)
+        append_decode()
+        e[3].record(stream)
     torch.cuda.synchronize()
     t_var = np.array([e[0].elapsed_time(e[1]) for e in ev2]) * 1e-3
     t_sld = np.array([e[1].elapsed_time(e[2]) for e in ev2]) * 1e-3
+    t_app = np.array([e[2].elapsed_time(e[3]) for e in ev2]) * 1e-3
+    app_bytes = decode_bytes + 2 * 2 * wd.B * wd.H * wd.d * 2  # plus the new rows read and written
     assert torch.isfinite(vo).all() and torch.isfinite(do).all()
     variable = {
         "packed_prefill": {"lengths": vl.tolist(), "gflop": round(var_flops / 1e9, 4),
@@ -314,6 +333,11 @@ def main():
                                  "ms_median": round(float(np.median(t_sld)) * 1e3, 5),
                                  "gbs": round(dl_bytes / t_sld.mean() / 1e9, 2),
                                  "pct_peak": round(100 * dl_bytes / t_sld.mean() / 1e9 / PEAK_HBM_GBS, 2)},
+        "decode_append": {"appended_per_sequence": 1, "keys_attended": wd.Nk,
+                          "gbytes": round(app_bytes / 1e9, 5), "ms": round(t_app.mean() * 1e3, 5),
+                          "ms_median": round(float(np.median(t_app)) * 1e3, 5),
+                          "gbs": round(app_bytes / t_app.mean() / 1e9, 2),
+                          "pct_peak": round(100 * app_bytes / t_app.mean() / 1e9 / PEAK_HBM_GBS, 2)},
     }
 
     pre_tflops = prefill_flops / t_prefill.mean() / 1e12

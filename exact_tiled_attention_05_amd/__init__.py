@@ -1,7 +1,7 @@
 """Python binding of libfa, the gfx950 exact tiled attention library.
 
 The functions named like the C ABI (``fa_fwd``, ``fa_fwd_split``,
-``fa_fwd_splitkv``, ``fa_fwd_splitkv_seqlens``, ``fa_fwd_varlen``,
+``fa_fwd_splitkv``, ``fa_fwd_splitkv_seqlens``, ``fa_fwd_splitkv_append``, ``fa_fwd_varlen``,
 ``fa_splitkv_combine``, ``fa_status_string``, ``fa_split_chunk_len``) only
 marshal arguments: torch tensors become device pointers, the current torch
 stream becomes the HIP stream, and every step of the computation runs in the
@@ -22,9 +22,9 @@ import torch
 
 __all__ = [
     "FA_FP32", "FA_BF16", "FaError", "library_path", "load_library",
-    "fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens", "fa_fwd_varlen",
-    "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len", "attention",
-    "attention_varlen", "attention_split", "attention_split_partials",
+    "fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
+    "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len", "attention",
+    "attention_varlen", "attention_split", "attention_split_partials", "attention_paged_append",
     "attention_paged_splitkv", "combine", "decode_paged",
 ]
 
@@ -34,7 +34,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 _lib = None
 
 EXPORTED = ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
-            "fa_fwd_varlen", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len")
+            "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len")
 
 
 class FaError(RuntimeError):
@@ -67,6 +67,9 @@ def load_library():
     lib.fa_fwd_splitkv_seqlens.argtypes = [vp, vp, vp, i, vp, i, i, vp, vp, vp, i, i, i, i, i, i,
                                            f, i, i, i, vp, f, vp]
     lib.fa_fwd_splitkv_seqlens.restype = i
+    lib.fa_fwd_splitkv_append.argtypes = [vp, vp, vp, vp, vp, i, vp, i, i, vp, vp, vp, i, i, i,
+                                          i, i, i, f, i, i, i, vp, f, vp]
+    lib.fa_fwd_splitkv_append.restype = i
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, i, vp, i, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
                                   i, vp, f, vp]
     lib.fa_fwd_varlen.restype = i
@@ -160,6 +163,21 @@ def fa_fwd_splitkv_seqlens(q, k_cache, v_cache, block_table, max_pages_per_seq, 
         int(num_splits), int(batch), int(heads), int(seqlen_q), int(max_seqlen_k), int(head_dim),
         float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
         _ptr(alibi_slopes), float(softcap), _stream(stream))
+
+
+def fa_fwd_splitkv_append(q, k_new, v_new, k_cache, v_cache, block_table, max_pages_per_seq,
+                          page_size, cache_seqlens, o_part, lse_part, num_splits, batch, heads,
+                          seqlen_q, max_seqlen_k, head_dim, softmax_scale, causal=False,
+                          window_left=-1, window_right=-1, alibi_slopes=None, softcap=0.0,
+                          stream=None) -> int:
+    """Call fa_fwd_splitkv_append on caller-allocated tensors; returns the status code."""
+    return load_library().fa_fwd_splitkv_append(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _dtype_code(q),
+        _ptr(block_table), int(max_pages_per_seq), int(page_size), _ptr(cache_seqlens),
+        _ptr(o_part), _ptr(lse_part), int(num_splits), int(batch), int(heads), int(seqlen_q),
+        int(max_seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)),
+        int(window_left), int(window_right), _ptr(alibi_slopes), float(softcap),
+        _stream(stream))
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, heads, total_q, total_k,
@@ -282,6 +300,36 @@ def attention_paged_splitkv(q, k_cache, v_cache, block_table, seqlen_k, num_spli
                                       H, nq, seqlen_k, d, softmax_scale, causal, window_left,
                                       window_right, alibi_slopes, softcap, stream),
                "fa_fwd_splitkv_seqlens")
+    return o_part, lse_part
+
+
+def attention_paged_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens,
+                           max_seqlen_k, num_splits, softmax_scale=None, causal=False,
+                           window_left=-1, window_right=-1, alibi_slopes=None, softcap=0.0,
+                           stream=None):
+    """Append k_new/v_new [B,Nq,H,d] to the paged cache behind cache_seqlens[b] keys and
+    return the split partials over the joined keys (o_part [S,B,H,Nq,d], lse_part
+    [S,B,H,Nq]). The caches are updated in place; cache_seqlens is not."""
+    _same_dtype(q, k_new, v_new, k_cache, v_cache)
+    B, nq, H, d = q.shape
+    _, page_size, Hc, dc = k_cache.shape
+    if (Hc, dc) != (H, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache must be [num_pages, page_size, H, d] matching q")
+    if tuple(k_new.shape) != (B, nq, H, d) or tuple(v_new.shape) != (B, nq, H, d):
+        raise ValueError("k_new and v_new must be [B, Nq, H, d] matching q")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages_per_seq]")
+    if cache_seqlens.dtype != torch.int32 or tuple(cache_seqlens.shape) != (B,):
+        raise ValueError("cache_seqlens must be int32 [B]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    o_part = torch.empty((num_splits, B, H, nq, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((num_splits, B, H, nq), dtype=torch.float32, device=q.device)
+    _check(fa_fwd_splitkv_append(q, k_new, v_new, k_cache, v_cache, block_table,
+                                 block_table.shape[1], page_size, cache_seqlens, o_part, lse_part,
+                                 num_splits, B, H, nq, max_seqlen_k, d, softmax_scale, causal,
+                                 window_left, window_right, alibi_slopes, softcap, stream),
+           "fa_fwd_splitkv_append")
     return o_part, lse_part
 
 

@@ -41,12 +41,13 @@ Launcher pick_f32(int head_dim, bool softcap, bool alibi) {
 
 // One query row per (batch, head): the split pass streams the cache with the
 // dedicated decode kernel.
+template <bool APPEND>
 Launcher pick_decode(int head_dim, bool softcap, bool alibi) {
 #define FA_PICK_DEC(D)                                                          \
-  if (softcap && alibi) return &fa::launch_decode_bf16<D, true, true>;          \
-  if (softcap) return &fa::launch_decode_bf16<D, true, false>;                  \
-  if (alibi) return &fa::launch_decode_bf16<D, false, true>;                    \
-  return &fa::launch_decode_bf16<D, false, false>;
+  if (softcap && alibi) return &fa::launch_decode_bf16<D, true, true, APPEND>;  \
+  if (softcap) return &fa::launch_decode_bf16<D, true, false, APPEND>;          \
+  if (alibi) return &fa::launch_decode_bf16<D, false, true, APPEND>;            \
+  return &fa::launch_decode_bf16<D, false, false, APPEND>;
   if (head_dim == 64) { FA_PICK_DEC(64) }
   FA_PICK_DEC(128)
 #undef FA_PICK_DEC
@@ -102,10 +103,12 @@ int64_t split_len(int seqlen_k, int num_splits, int page_size) {
   return (c + page_size - 1) / page_size * page_size;
 }
 
-// fa_fwd_splitkv and fa_fwd_splitkv_seqlens (seqlens_k = nullptr: every
-// sequence holds seqlen_k keys).
-int splitkv(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
-            const int* block_table, int max_pages_per_seq, int page_size, const int* seqlens_k,
+// fa_fwd_splitkv, fa_fwd_splitkv_seqlens and fa_fwd_splitkv_append
+// (seqlens_k = nullptr: every sequence holds seqlen_k keys; k_new = nullptr: no
+// append).
+int splitkv(const void* q, const void* k_cache, const void* v_cache, const void* k_new,
+            const void* v_new, int in_dtype, const int* block_table, int max_pages_per_seq,
+            int page_size, const int* seqlens_k,
             float* o_part, float* lse_part, int num_splits, int batch, int heads, int seqlen_q,
             int seqlen_k, int head_dim, float softmax_scale, int causal, int window_left,
             int window_right, const float* alibi_slopes, float softcap, void* stream) {
@@ -137,6 +140,8 @@ int splitkv(const void* q, const void* k_cache, const void* v_cache, int in_dtyp
   p.row_stride = heads * head_dim;
   p.page_stride = (int64_t)page_size * heads * head_dim;
   p.seqlens_k = seqlens_k;
+  p.k_new = k_new;
+  p.v_new = v_new;
   const int tile = in_dtype == FA_BF16 ? fa::BF16_BM : fa::F32_BM;
   fill_common(p, batch, heads, seqlen_q, seqlen_k, softmax_scale, causal, window_left,
               window_right, alibi_slopes, softcap, tile);
@@ -146,8 +151,9 @@ int splitkv(const void* q, const void* k_cache, const void* v_cache, int in_dtyp
 
   const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
   Launcher fn = in_dtype != FA_BF16 ? pick_f32<true>(head_dim, sc, al)
-                : seqlen_q == 1     ? pick_decode(head_dim, sc, al)
-                                    : pick_bf16<fa::FWD_PAGED_SPLIT>(head_dim, sc, al);
+                : seqlen_q != 1     ? pick_bf16<fa::FWD_PAGED_SPLIT>(head_dim, sc, al)
+                : k_new             ? pick_decode<true>(head_dim, sc, al)
+                                    : pick_decode<false>(head_dim, sc, al);
   return fn(p, stream) ? FA_ERR_HIP : FA_OK;
 }
 
@@ -244,9 +250,10 @@ int fa_fwd_splitkv(const void* q, const void* k_cache, const void* v_cache, int 
                    int seqlen_q, int seqlen_k, int head_dim, float softmax_scale, int causal,
                    int window_left, int window_right, const float* alibi_slopes, float softcap,
                    void* stream) {
-  return splitkv(q, k_cache, v_cache, in_dtype, block_table, max_pages_per_seq, page_size,
-                 nullptr, o_part, lse_part, num_splits, batch, heads, seqlen_q, seqlen_k,
-                 head_dim, softmax_scale, causal, window_left, window_right, alibi_slopes,
+  return splitkv(q, k_cache, v_cache, nullptr, nullptr, in_dtype, block_table,
+                 max_pages_per_seq, page_size, nullptr, o_part, lse_part, num_splits, batch,
+                 heads, seqlen_q, seqlen_k, head_dim, softmax_scale, causal, window_left,
+                 window_right, alibi_slopes,
                  softcap, stream);
 }
 
@@ -258,8 +265,23 @@ int fa_fwd_splitkv_seqlens(const void* q, const void* k_cache, const void* v_cac
                            int window_right, const float* alibi_slopes, float softcap,
                            void* stream) {
   if (!cache_seqlens) return FA_ERR_NULL;
-  return splitkv(q, k_cache, v_cache, in_dtype, block_table, max_pages_per_seq, page_size,
-                 cache_seqlens, o_part, lse_part, num_splits, batch, heads, seqlen_q,
+  return splitkv(q, k_cache, v_cache, nullptr, nullptr, in_dtype, block_table,
+                 max_pages_per_seq, page_size, cache_seqlens, o_part, lse_part, num_splits,
+                 batch, heads, seqlen_q, max_seqlen_k, head_dim, softmax_scale, causal,
+                 window_left, window_right, alibi_slopes, softcap, stream);
+}
+
+int fa_fwd_splitkv_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                          void* v_cache, int in_dtype, const int* block_table,
+                          int max_pages_per_seq, int page_size, const int* cache_seqlens,
+                          float* o_part, float* lse_part, int num_splits, int batch, int heads,
+                          int seqlen_q, int max_seqlen_k, int head_dim, float softmax_scale,
+                          int causal, int window_left, int window_right,
+                          const float* alibi_slopes, float softcap, void* stream) {
+  if (!cache_seqlens || !k_new || !v_new) return FA_ERR_NULL;
+  if (seqlen_q > 0 && max_seqlen_k < seqlen_q) return FA_ERR_SHAPE;
+  return splitkv(q, k_cache, v_cache, k_new, v_new, in_dtype, block_table, max_pages_per_seq,
+                 page_size, cache_seqlens, o_part, lse_part, num_splits, batch, heads, seqlen_q,
                  max_seqlen_k, head_dim, softmax_scale, causal, window_left, window_right,
                  alibi_slopes, softcap, stream);
 }

@@ -10,7 +10,10 @@
 // lane keeps 8 K and 8 V loads in flight per batch. Scores are reduced across
 // the row's lanes with DPP, and each lane runs an fp32 online softmax over its
 // group's keys for its 8 output columns. Groups, then wavefronts, are merged
-// by log-sum-exp at the end.
+// by log-sum-exp at the end. With an append, this step's new keys are read
+// from k_new / v_new and written into their pages by one workgroup per
+// (batch, head) (the inference article's key-value cache, which keeps each
+// processed key for later steps).
 #include <hip/hip_runtime.h>
 
 #include "fa_device.h"
@@ -49,7 +52,9 @@ __device__ __forceinline__ float group_sum(float x) {
 __device__ __forceinline__ float lo_bf16(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float hi_bf16(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-template <int D, bool SOFTCAP, bool ALIBI>
+// APPEND: keys [n_cached, nk) are this step's new keys, read from k_new / v_new;
+// the split-0 workgroup of each (b, h) also copies them into their cache pages.
+template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
   constexpr int CH = D / 8;       // lanes per key row
   constexpr int KPI = 64 / CH;    // keys per wavefront-wide load
@@ -64,6 +69,9 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
   const int b = wi.b, h = wi.h, s = wi.s;
   const SeqInfo si = seq_info(p, b, h);
   const int nk = si.nk;
+  if constexpr (APPEND) {
+    if (s == 0) append_rows<uint16_t>(p, si, b, h, D, tid, kThreads);
+  }
 
   int slo, shi;
   split_range(p, nk, s, slo, shi);
@@ -102,11 +110,14 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
 
   const uint16_t* kbase = (const uint16_t*)p.k + 8 * c;
   const uint16_t* vbase = (const uint16_t*)p.v + 8 * c;
+  const uint16_t* knew = (const uint16_t*)p.k_new + 8 * c;
+  const uint16_t* vnew = (const uint16_t*)p.v_new + 8 * c;
   for (int base = lo + w * KPB; base < hi; base += kWaves * KPB) {
     // Row offsets first, then every load back to back (no branches between
     // them). A key past the end re-reads key `lo`, whose page is real, and its
     // score is masked below, so its finite V row gets weight 0.
     int64_t off[kU];
+    bool fresh[kU];  // an appended key (APPEND only)
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int t = min(base + g + KPI * u, hi - 1);
@@ -121,12 +132,17 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
       }
       const int page = table_in_lds ? s_bt[idx - p0] : bt_row[idx];
       off[u] = (int64_t)page * p.page_stride + slot * p.row_stride + h * D;
+      fresh[u] = false;
+      if constexpr (APPEND) {
+        fresh[u] = tt >= si.n_cached;
+        if (fresh[u]) off[u] = new_key_offset(p, si, b, tt, h, D);
+      }
     }
     u32x4_t kx[kU], vx[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      kx[u] = *(const u32x4_t*)(kbase + off[u]);
-      vx[u] = *(const u32x4_t*)(vbase + off[u]);
+      kx[u] = *(const u32x4_t*)((fresh[u] ? knew : kbase) + off[u]);
+      vx[u] = *(const u32x4_t*)((fresh[u] ? vnew : vbase) + off[u]);
     }
     float sc[kU];
 #pragma unroll
@@ -215,15 +231,17 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
 
 }  // namespace
 
-template <int D, bool SOFTCAP, bool ALIBI>
+template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream) {
   const int64_t groups = (int64_t)p.H * p.B * p.num_splits;
-  hipLaunchKernelGGL((decode_bf16_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)groups),
+  hipLaunchKernelGGL((decode_bf16_kernel<D, SOFTCAP, ALIBI, APPEND>), dim3((unsigned)groups),
                      dim3(kThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 
-#define FA_INST(D, SC, AL) template int launch_decode_bf16<D, SC, AL>(const FwdParams&, void*);
+#define FA_INST(D, SC, AL) \
+  template int launch_decode_bf16<D, SC, AL, false>(const FwdParams&, void*); \
+  template int launch_decode_bf16<D, SC, AL, true>(const FwdParams&, void*);
 FA_INST(64, false, false)
 FA_INST(64, false, true)
 FA_INST(64, true, false)

@@ -191,6 +191,7 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8_t v, float acc) {
 // The sequence a workgroup works on: its lengths and where its rows sit.
 struct SeqInfo {
   int nq, nk;       // query rows and keys of this sequence
+  int n_cached;     // keys [0, n_cached) come from k/v, keys [n_cached, nk) from k_new/v_new
   int64_t q_row0;   // row (of H * D elements) of query 0 in q and o
   int64_t k_row0;   // row of key 0 in contiguous or packed k and v
   int64_t lse0;     // lse index of (this head, query 0); the sequence's rows follow
@@ -208,12 +209,22 @@ __device__ __forceinline__ SeqInfo seq_info(const FwdParams& p, int b, int h) {
     const int k1 = min(max(p.cu_seqlens_k[b + 1], k0), p.total_k);
     si.nq = min(q1 - q0, p.Nq);
     si.nk = min(k1 - k0, p.Nk);
+    si.n_cached = si.nk;
     si.q_row0 = q0;
     si.k_row0 = k0;
     si.lse0 = (int64_t)h * p.total_q + q0;
   } else {
     si.nq = p.Nq;
-    si.nk = p.seqlens_k ? min(max(p.seqlens_k[b], 0), p.Nk) : p.Nk;
+    int n = p.seqlens_k ? min(max(p.seqlens_k[b], 0), p.Nk) : p.Nk;
+    if (p.k_new) {
+      // Append: the Nq new keys follow the cached ones and must fit in Nk.
+      n = min(n, p.Nk - p.Nq);
+      si.n_cached = n;
+      n += p.Nq;
+    } else {
+      si.n_cached = n;
+    }
+    si.nk = n;
     si.q_row0 = (int64_t)b * p.Nq;
     si.k_row0 = (int64_t)b * p.Nk;
     si.lse0 = ((int64_t)b * p.H + h) * p.Nq;
@@ -226,23 +237,52 @@ __device__ __forceinline__ int64_t q_offset(const FwdParams& p, const SeqInfo& s
   return ((si.q_row0 + row) * p.H + h) * D;
 }
 
+// Physical element offset of logical key `key` of sequence b, head h, in a page pool.
+__device__ __forceinline__ int64_t page_offset(const FwdParams& p, int b, int key, int h, int D) {
+  int idx, slot;
+  if (p.page_shift >= 0) {
+    idx = key >> p.page_shift;
+    slot = key & (p.page_size - 1);
+  } else {
+    idx = key / p.page_size;
+    slot = key - idx * p.page_size;
+  }
+  const int page = p.block_table[(int64_t)b * p.max_pages + idx];
+  return (((int64_t)page * p.page_size + slot) * p.H + h) * D;
+}
+
 template <bool PAGED>
 __device__ __forceinline__ int64_t kv_offset(const FwdParams& p, int b, const SeqInfo& si, int key,
                                              int h, int D) {
   if constexpr (PAGED) {
-    int idx, slot;
-    if (p.page_shift >= 0) {
-      idx = key >> p.page_shift;
-      slot = key & (p.page_size - 1);
-    } else {
-      idx = key / p.page_size;
-      slot = key - idx * p.page_size;
-    }
-    const int page = p.block_table[(int64_t)b * p.max_pages + idx];
-    return (((int64_t)page * p.page_size + slot) * p.H + h) * D;
+    return page_offset(p, b, key, h, D);
   } else {
     return ((si.k_row0 + key) * p.H + h) * D;
   }
+}
+
+// Append: copy the Nq new key and value rows of (b, h) into their cache pages,
+// logical keys [n_cached, n_cached + Nq), in 16-byte pieces (T: element type).
+// Within the launch no workgroup reads those cache rows (new keys are read from
+// k_new / v_new), so exactly one workgroup per (b, h) may write them at any time.
+template <typename T>
+__device__ void append_rows(const FwdParams& p, const SeqInfo& si, int b, int h, int D, int tid,
+                            int nthreads) {
+  constexpr int EPC = 16 / sizeof(T);
+  const int cpr = D / EPC;
+  for (int idx = tid; idx < p.Nq * cpr; idx += nthreads) {
+    const int i = idx / cpr, c = idx - (idx / cpr) * cpr;
+    const int64_t dst = page_offset(p, b, si.n_cached + i, h, D) + c * EPC;
+    const int64_t src = (((int64_t)b * p.Nq + i) * p.H + h) * D + c * EPC;
+    *(u32x4_t*)((T*)const_cast<void*>(p.k) + dst) = *(const u32x4_t*)((const T*)p.k_new + src);
+    *(u32x4_t*)((T*)const_cast<void*>(p.v) + dst) = *(const u32x4_t*)((const T*)p.v_new + src);
+  }
+}
+
+// Element offset of appended key `key` (>= n_cached) of (b, h) in k_new / v_new.
+__device__ __forceinline__ int64_t new_key_offset(const FwdParams& p, const SeqInfo& si, int b,
+                                                  int key, int h, int D) {
+  return (((int64_t)b * p.Nq + (key - si.n_cached)) * p.H + h) * D;
 }
 
 // Keys [slo, shi) of split s of a sequence with nk keys: chunks of

@@ -133,6 +133,10 @@ void fwd_bf16_kernel(FwdParams p) {
   const int b = wi.b, h = wi.h, s = wi.s;
   const SeqInfo si = seq_info(p, b, h);
   const int nq = si.nq, nk = si.nk;
+  if constexpr (PAGED) {
+    // Append: one workgroup per (b, h) copies the new keys into their pages.
+    if (p.k_new && s == 0 && wi.rank == 0) append_rows<uint16_t>(p, si, b, h, D, tid, kThreads);
+  }
   const int qt = query_tile(wi, nq, kBM);
   if (qt < 0) return;  // a packed sequence shorter than the longest
 
@@ -196,9 +200,12 @@ void fwd_bf16_kernel(FwdParams p) {
     const int chunk = (lane % CPR) ^ swz<D>(trow);
     lane_bytes[i] = (unsigned)(trow * row_bytes + 16 * chunk);
   }
-  // Paged K/V: rows past the end re-read the last key (finite data; masked later).
+  // Paged K/V: rows past the end re-read the last key (finite data; masked later);
+  // appended keys come from k_new / v_new.
   const uint16_t* kg = (const uint16_t*)p.k;
   const uint16_t* vg = (const uint16_t*)p.v;
+  const uint16_t* kn = (const uint16_t*)p.k_new;
+  const uint16_t* vn = (const uint16_t*)p.v_new;
   auto copy_one = [&](const char* bh, uint16_t* dst, int j0) __attribute__((always_inline)) {
     const int64_t tb = (int64_t)j0 * row_bytes;
     const int64_t left = end_bytes - tb;
@@ -218,11 +225,13 @@ void fwd_bf16_kernel(FwdParams p) {
         const int trow = ROWS_PER_LOAD * ld + lane / CPR;
         const int chunk = (lane % CPR) ^ swz<D>(trow);
         const int key = min(j0 + trow, nk - 1);
-        const int64_t o = kv_offset<PAGED>(p, b, si, key, h, D) + 8 * chunk;
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(kg + o), (lds_ptr_t)(kdst + 512 * ld), 16, 0,
-                                         0);
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(vg + o), (lds_ptr_t)(vdst + 512 * ld), 16, 0,
-                                         0);
+        const bool fresh = key >= si.n_cached;
+        const int64_t o = (fresh ? new_key_offset(p, si, b, key, h, D)
+                                 : kv_offset<PAGED>(p, b, si, key, h, D)) + 8 * chunk;
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)((fresh ? kn : kg) + o),
+                                         (lds_ptr_t)(kdst + 512 * ld), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)((fresh ? vn : vg) + o),
+                                         (lds_ptr_t)(vdst + 512 * ld), 16, 0, 0);
       }
     }
   };

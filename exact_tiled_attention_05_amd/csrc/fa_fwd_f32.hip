@@ -30,6 +30,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
   const int b = wi.b, h = wi.h, s = wi.s;
   const SeqInfo si = seq_info(p, b, h);
   const int nq = si.nq, nk = si.nk;
+  if constexpr (PAGED) {
+    // Append: one workgroup per (b, h) copies the new keys into their pages.
+    if (p.k_new && s == 0 && wi.rank == 0) append_rows<float>(p, si, b, h, D, lane, kThreads);
+  }
   const int qt = query_tile(wi, nq, F32_BM);
   if (qt < 0) return;  // a packed sequence shorter than the longest
 
@@ -71,9 +75,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
       const int key = j0 + kk;
       f32x4_t kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
       if (key < nk) {
-        const int64_t o = kv_offset<PAGED>(p, b, si, key, h, D) + 4 * c;
-        kx = *(const f32x4_t*)((const float*)p.k + o);
-        vx = *(const f32x4_t*)((const float*)p.v + o);
+        // Appended keys (paged launches with k_new) come from k_new / v_new.
+        const bool fresh = PAGED && key >= si.n_cached;
+        const int64_t o = (fresh ? new_key_offset(p, si, b, key, h, D)
+                                 : kv_offset<PAGED>(p, b, si, key, h, D)) + 4 * c;
+        kx = *(const f32x4_t*)((const float*)(fresh ? p.k_new : p.k) + o);
+        vx = *(const f32x4_t*)((const float*)(fresh ? p.v_new : p.v) + o);
       }
       float* kd = &sK[kk * KSTR + 4 * c];
       kd[0] = kx[0];

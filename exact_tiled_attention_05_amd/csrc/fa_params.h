@@ -19,6 +19,8 @@ struct FwdParams {
   const int* cu_seqlens_q;  // [B + 1] packed batch offsets, or nullptr (batched layout)
   const int* cu_seqlens_k;  // [B + 1]
   const int* seqlens_k;     // [B] per-sequence key counts of a batched layout, or nullptr
+  const void* k_new;        // [B, Nq, H, D] keys appended to the paged cache before attending
+  const void* v_new;        //   (fa_fwd_splitkv_append), or nullptr
   int B, H;
   int Nq, Nk;               // query rows and keys per sequence (packed: the maxima)
   int total_q, total_k;     // rows of the packed tensors
@@ -58,7 +60,7 @@ template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 int launch_fwd_bf16(const FwdParams& p, void* stream);
 template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
 int launch_fwd_f32(const FwdParams& p, void* stream);
-template <int D, bool SOFTCAP, bool ALIBI>
+template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream);
 template <int D>
 int launch_combine(const CombineParams& p, void* stream);

@@ -165,6 +165,41 @@ int fa_fwd_splitkv_seqlens(const void* q, const void* k_cache, const void* v_cac
                            void* stream);
 
 /*
+ * fa_fwd_splitkv_append - append each sequence's new keys to its paged cache,
+ * then run the split pass over the cached keys followed by the new ones, in
+ * one launch. (The key-value cache of "解密FlashAttention：如何让大语言模型推理
+ * 速度翻倍": processed keys are kept and reused, and each step only adds its own
+ * new tokens; page addressing as the update article's v2.5 entry.)
+ *
+ *   k_new, v_new   [batch, seqlen_q, heads, head_dim] in_dtype: one new key and
+ *                  value per query row of this step
+ *   cache_seqlens  device int32 [batch]: keys already cached per sequence, n_b
+ *
+ * Row i of k_new[b] / v_new[b] is written into logical key n_b + i of sequence
+ * b (page block_table[b, t / page_size], row t % page_size). The partials are
+ * those of fa_fwd_splitkv_seqlens with lengths n_b + seqlen_q: the queries
+ * line up with the new keys (bottom-right rule), so under causal the last
+ * query sees every key. The new keys are read from k_new / v_new during the
+ * launch, never from the cache rows being written, so the call is
+ * well-defined in one launch; when it has completed the cache holds them.
+ * cache_seqlens is not updated (the caller owns it and adds seqlen_q).
+ *
+ * Requires max_seqlen_k >= seqlen_q and max_pages_per_seq * page_size >=
+ * max_seqlen_k; n_b is clamped on the device to [0, max_seqlen_k - seqlen_q],
+ * so every write stays inside the mapped pages. Two sequences whose tables
+ * share a page row written here race (the table is the caller's). Other
+ * arguments as fa_fwd_splitkv; NULL cache_seqlens, k_new or v_new is
+ * FA_ERR_NULL.
+ */
+int fa_fwd_splitkv_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                          void* v_cache, int in_dtype, const int* block_table,
+                          int max_pages_per_seq, int page_size, const int* cache_seqlens,
+                          float* o_part, float* lse_part, int num_splits, int batch, int heads,
+                          int seqlen_q, int max_seqlen_k, int head_dim, float softmax_scale,
+                          int causal, int window_left, int window_right,
+                          const float* alibi_slopes, float softcap, void* stream);
+
+/*
  * fa_fwd_varlen - exact attention forward over a packed batch of sequences of
  * different lengths (variable sequence lengths: closing section of
  * "FlashAttention深度解析：从算法创新到产业变革的全面影响"). Each sequence is its

@@ -214,3 +214,26 @@ def test_fa_fwd_varlen_empty_pack_launches_nothing():
     # and tensors of zero rows may be NULL.
     assert varlen(total_q=0, q=None, o=None) == OK
     assert varlen(total_q=0, total_k=0, q=None, o=None, k=None, v=None, max_k=0) == OK
+
+
+def split_append(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, k=FAKE, v=FAKE, in_dtype=1, bt=FAKE, maxp=4, ps=16, sl=FAKE,
+             op=FAKE, lp=FAKE, S=2, batch=1, heads=1, seqlen_q=1, max_k=64, head_dim=128,
+             scale=0.1, causal=1, wl=-1, wr=-1, alibi=None, softcap=0.0, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_fwd_splitkv_append(
+        a["q"], a["kn"], a["vn"], a["k"], a["v"], a["in_dtype"], a["bt"], a["maxp"], a["ps"],
+        a["sl"], a["op"], a["lp"], a["S"], a["batch"], a["heads"], a["seqlen_q"], a["max_k"],
+        a["head_dim"], a["scale"], a["causal"], a["wl"], a["wr"], a["alibi"], a["softcap"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), NULL), (dict(vn=None), NULL), (dict(sl=None), NULL), (dict(k=None), NULL),
+    (dict(bt=None), NULL), (dict(op=None), NULL),
+    (dict(seqlen_q=5, max_k=4), SHAPE), (dict(S=0), SHAPE), (dict(maxp=3, ps=16, max_k=64), SHAPE),
+    (dict(batch=0), SHAPE), (dict(head_dim=80), UNSUP), (dict(in_dtype=3), UNSUP),
+    (dict(wl=-4), MASK), (dict(softcap=-1.0), VALUE),
+])
+def test_fa_fwd_splitkv_append_rejects(kw, code):
+    assert split_append(**kw) == code

@@ -463,3 +463,100 @@ def test_splitkv_seqlens_uniform_bitwise_equals_splitkv(dtype, d, nq):
     c = fa.attention_paged_splitkv(tq, tk, tv, tbt, w.Nk, w.num_splits, w.scale, True, 500, 0, ts)
     torch.cuda.synchronize()
     assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+
+
+# --------------------------------------------------------------------------
+# Appending the new keys to the paged cache (fa_fwd_splitkv_append)
+# --------------------------------------------------------------------------
+APPEND_CASES = [
+    # (dtype, d, H, nq, max_k, page_size, num_splits, seqlens, causal, wl, wr, alibi, cap)
+    ("bf16", 128, 2, 1, 1000, 64, 4, [999, 0, 1, 511, 63, 700], True, -1, -1, False, 0.0),
+    ("bf16", 64, 3, 1, 777, 16, 16, [776, 5, 300, 0], True, 100, 0, True, 0.0),
+    ("bf16", 128, 2, 1, 4096, 256, 16, [4095, 2047, 255, 1], True, -1, -1, True, 30.0),
+    ("bf16", 128, 2, 5, 300, 7, 3, [295, 4, 0, 150], True, 50, 0, False, 10.0),
+    ("bf16", 64, 2, 130, 400, 64, 2, [270, 100, 0], True, -1, -1, True, 0.0),
+    ("fp32", 64, 2, 1, 500, 32, 5, [499, 0, 77], True, -1, -1, False, 0.0),
+    ("fp32", 128, 2, 20, 200, 16, 3, [180, 10, 0], True, -1, -1, True, 5.0),
+]
+
+
+def bits(x):
+    return x.view(np.uint16) if x.dtype == np.uint16 else x.view(np.uint32)
+
+
+def from_dev(t, dtype):
+    if dtype == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", APPEND_CASES)
+def test_splitkv_append_small(case):
+    dtype, d, H, nq, nk, ps, S, seqlens, causal, wl, wr, alibi, cap = case
+    say(f"append {case}")
+    B = len(seqlens)
+    seed = 7000 + APPEND_CASES.index(case)
+    w = W.Workload(0, "append", B=B, H=H, Nq=nq, Nk=nk, d=d, dtype=dtype, causal=causal,
+                   paged=True, page_size=ps, pool_factor=1.3, num_splits=S, seed=seed)
+    q, kc, vc, bt = W.gen_paged(w, seqlens=seqlens)    # rows past each length are NaN
+    kn = W.gen_tensor(seed + 500, W.TENSOR_K, B, nq, H, d, 1.0, dtype)
+    vn = W.gen_tensor(seed + 500, W.TENSOR_V, B, nq, H, d, 1.0, dtype)
+    slopes = W.alibi_slopes(H) if alibi else None
+    ts = None if slopes is None else torch.from_numpy(slopes).cuda()
+    scale = 1.0 / np.sqrt(d)
+    tkc, tvc = to_dev(kc, dtype), to_dev(vc, dtype)
+    o_part, lse_part = fa.attention_paged_append(
+        to_dev(q, dtype), to_dev(kn, dtype), to_dev(vn, dtype), tkc, tvc,
+        torch.from_numpy(bt).cuda(), torch.tensor(seqlens, dtype=torch.int32).cuda(), nk, S,
+        scale, causal, wl, wr, ts, cap)
+    o, lse = fa.combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    # The cache now holds the new keys, bit for bit, and nothing else changed.
+    want_k, want_v = O.kvcache_append_ref(kc, vc, bt, seqlens, kn, vn)
+    assert np.array_equal(bits(from_dev(tkc, dtype)), bits(want_k))
+    assert np.array_equal(bits(from_dev(tvc, dtype)), bits(want_v))
+    qf = W.to_float(q, dtype)
+    k = np.zeros((B, nk, H, d))
+    v = np.zeros((B, nk, H, d))
+    for b, n in enumerate(seqlens):
+        k[b, :n] = O.paged_gather_ref(W.to_float(kc, dtype), bt, b, n)
+        v[b, :n] = O.paged_gather_ref(W.to_float(vc, dtype), bt, b, n)
+    rop, rlp = O.splitkv_append_ref(qf, k, v, W.to_float(kn, dtype), W.to_float(vn, dtype),
+                                    seqlens, S, ps, scale, causal, wl, wr, slopes, cap)
+    check(o_part.cpu().numpy(), lse_part.cpu().numpy(), rop, rlp, dtype, "partials")
+    ro, rl = O.combine_ref(rop, rlp)
+    check(o.cpu().numpy().transpose(0, 2, 1, 3), lse.cpu().numpy(), ro, rl, dtype, "combined")
+
+
+def test_incremental_decode_three_steps():
+    """Three decode steps, each appending one token per sequence and attending
+    over everything cached so far, against the oracle on the growing cache."""
+    B, H, d, nk, ps, S = 3, 4, 128, 600, 32, 8
+    start = [0, 97, 590]
+    w = W.Workload(0, "incremental", B=B, H=H, Nq=1, Nk=nk, d=d, dtype="bf16", causal=True,
+                   paged=True, page_size=ps, pool_factor=1.25, num_splits=S, seed=93)
+    _, kc, vc, bt = W.gen_paged(w, seqlens=start)
+    tkc, tvc = to_dev(kc, "bf16"), to_dev(vc, "bf16")
+    tbt = torch.from_numpy(bt).cuda()
+    kf, vf = W.to_float(kc, "bf16"), W.to_float(vc, "bf16")
+    for step in range(3):
+        say(f"incremental decode step {step}")
+        lens = [n + step for n in start]
+        q = W.gen_tensor(940 + step, W.TENSOR_Q, B, 1, H, d, 1.0, "bf16")
+        kn = W.gen_tensor(940 + step, W.TENSOR_K, B, 1, H, d, 1.0, "bf16")
+        vn = W.gen_tensor(940 + step, W.TENSOR_V, B, 1, H, d, 1.0, "bf16")
+        o_part, lse_part = fa.attention_paged_append(
+            to_dev(q, "bf16"), to_dev(kn, "bf16"), to_dev(vn, "bf16"), tkc, tvc, tbt,
+            torch.tensor(lens, dtype=torch.int32).cuda(), nk, S, causal=True)
+        o, lse = fa.combine(o_part, lse_part)
+        torch.cuda.synchronize()
+        kf, vf = O.kvcache_append_ref(kf, vf, bt, lens, W.to_float(kn, "bf16"),
+                                      W.to_float(vn, "bf16"))
+        for b, n in enumerate(lens):
+            kb = O.paged_gather_ref(kf, bt, b, n + 1)
+            vb = O.paged_gather_ref(vf, bt, b, n + 1)
+            for h in range(H):
+                ro, rl = O.attention_bh(W.to_float(q, "bf16")[b, :, h], kb[:, h], vb[:, h],
+                                        np.arange(1), 1, 1.0 / np.sqrt(d), True)
+                check(o.cpu().numpy()[b, :, h], lse.cpu().numpy()[b, h], ro, rl, "bf16",
+                      f"step {step} b{b} h{h}")
