@@ -191,6 +191,72 @@ def attention_ref(q, k, v, scale, causal=False, window_left=-1, window_right=-1,
 
 
 # --------------------------------------------------------------------------
+# Backward pass (gradients of the forward above)
+# --------------------------------------------------------------------------
+def attention_bwd_bh(q_bh, k_bh, v_bh, do_bh, nq, scale, causal=False, window_left=-1,
+                     window_right=-1, slope=None, softcap=0.0):
+    """dQ, dK, dV [n, d] and D [nq] for one (batch, head), by the chain rule.
+
+    The forward is O = P V with P = softmax(S) over the allowed keys and
+    S = T(scale * Q K^T), T the tanh cap then the ALiBi shift (a constant).
+    With dO given: dV = P^T dO; dP = dO V^T; D_i = sum_j P_ij dP_ij (= dO_i . O_i);
+    dS = P * (dP - D); through the cap dZ = dS * (1 - tanh^2(z / softcap));
+    dQ = scale dZ K; dK = scale dZ^T Q. Rows with no allowed key have P = 0 and
+    contribute nothing. (The pages call the training pass the backward pass and
+    list a deterministic backward in the update article's v2.4 entry; the
+    arithmetic is the derivative of standard attention, [Variants] section 二.1.)
+    """
+    rows = np.arange(nq)
+    k_bh = np.asarray(k_bh, dtype=np.float64)
+    q_bh = np.asarray(q_bh, dtype=np.float64)
+    v_bh = np.asarray(v_bh, dtype=np.float64)
+    do_bh = np.asarray(do_bh, dtype=np.float64)
+    dq = np.zeros_like(q_bh)
+    dk = np.zeros_like(k_bh)
+    dv = np.zeros_like(v_bh)
+    D = np.zeros(nq)
+    if k_bh.shape[0] == 0 or nq == 0:
+        return dq, dk, dv, D
+    s = scores_ref(q_bh, k_bh, rows, nq, scale, causal, window_left, window_right, slope, softcap)
+    p, _, _ = softmax_rows(s)
+    dv = p.T @ do_bh
+    dp = do_bh @ v_bh.T
+    D = (p * dp).sum(axis=1)
+    ds = p * (dp - D[:, None])
+    if softcap > 0.0:
+        t = np.tanh((q_bh @ k_bh.T) * scale / softcap)
+        ds = ds * (1.0 - t * t)
+    dq = scale * (ds @ k_bh)
+    dk = scale * (ds.T @ q_bh)
+    return dq, dk, dv, D
+
+
+def attention_bwd_ref(q, k, v, do, scale, causal=False, window_left=-1, window_right=-1,
+                      alibi_slopes=None, softcap=0.0, bh=None):
+    """Gradients of attention_ref's O with respect to q, k, v, given dO.
+
+    q, do [B, Nq, H, d]; k, v [B, Nk, H, d]. Returns dq, dk, dv (shaped like
+    q, k, v) and D [B, H, Nq] = rowsum(dO * O); pairs outside bh are NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, nq, H, _ = q.shape
+    pairs = [(b, h) for b in range(B) for h in range(H)] if bh is None else bh
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    D = np.full((B, H, nq), np.nan)
+    for b, h in pairs:
+        slope = None if alibi_slopes is None else float(alibi_slopes[h])
+        g = attention_bwd_bh(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], nq, scale, causal,
+                             window_left, window_right, slope, softcap)
+        dq[b, :, h], dk[b, :, h], dv[b, :, h], D[b, h] = g
+    return dq, dk, dv, D
+
+
+# --------------------------------------------------------------------------
 # Packed variable-length batch (the deep-analysis page, roadmap section)
 # --------------------------------------------------------------------------
 def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,

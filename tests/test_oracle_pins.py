@@ -621,3 +621,89 @@ def test_t22_decode_after_append_sees_every_key():
         assert abs(lc[b, 0, 0] - math.log(n + 1)) < 1e-12
         want = np.concatenate([v[b, :n, 0], vn[b, :, 0]]).mean(axis=0)
         np.testing.assert_allclose(oc[b, 0, 0], want, atol=1e-12)
+
+
+# T23-T26: the backward pass ------------------------------------------------------
+BWD_VARIANTS = [  # (nq, nk, causal, wl, wr, slope, cap)
+    (3, 5, False, -1, -1, None, 0.0), (4, 4, True, -1, -1, None, 0.0),
+    (5, 3, True, -1, -1, 0.3, 0.0),          # Nq > Nk: the first rows see no key
+    (3, 6, True, 2, 0, None, 1.5), (4, 5, False, 1, 2, 0.2, 2.0), (2, 7, True, -1, -1, 0.5, 0.8),
+]
+
+
+def _loss(q, k, v, g, scale, causal, wl, wr, slope, cap):
+    o, _ = O.attention_bh(q, k, v, np.arange(q.shape[0]), q.shape[0], scale, causal, wl, wr,
+                          slope, cap)
+    return float((o * g).sum())
+
+
+@pytest.mark.parametrize("nq,nk,causal,wl,wr,slope,cap", BWD_VARIANTS)
+def test_t23_backward_matches_central_differences(nq, nk, causal, wl, wr, slope, cap):
+    """L = sum(O * G): every entry of dQ, dK, dV against (L(x + e) - L(x - e)) / 2e of
+    the forward oracle (float64, e = 1e-6)."""
+    d, scale, eps = 3, 0.7, 1e-6
+    q, k, v, g = rnd(80, nq, d), rnd(81, nk, d), rnd(82, nk, d), rnd(83, nq, d)
+    dq, dk, dv, _ = O.attention_bwd_bh(q, k, v, g, nq, scale, causal, wl, wr, slope, cap)
+    for x, grad in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            lp = _loss(q, k, v, g, scale, causal, wl, wr, slope, cap)
+            x[idx] = old - eps
+            lm = _loss(q, k, v, g, scale, causal, wl, wr, slope, cap)
+            x[idx] = old
+            assert abs((lp - lm) / (2 * eps) - grad[idx]) < 1e-7, (idx, grad[idx])
+
+
+@pytest.mark.parametrize("causal,wl,wr,use_alibi,cap", [
+    (False, -1, -1, False, 0.0), (True, -1, -1, True, 0.0), (True, 3, 0, False, 4.0),
+    (False, 2, 5, True, 2.5)])
+def test_t24_backward_matches_torch_autograd_fp64(causal, wl, wr, use_alibi, cap):
+    """torch's own autograd through its float64 softmax and matmuls (CPU)."""
+    B, nq, nk, H, d, scale = 2, 6, 9, 2, 4, 0.45
+    q, k, v, g = rnd(84, B, nq, H, d), rnd(85, B, nk, H, d), rnd(86, B, nk, H, d), rnd(87, B, nq, H, d)
+    slopes = np.array([0.25, 0.6]) if use_alibi else None
+    dq, dk, dv, _ = O.attention_bwd_ref(q, k, v, g, scale, causal, wl, wr, slopes, cap)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    s = torch.einsum("bihd,bjhd->bhij", tq, tk) * scale
+    if cap > 0:
+        s = cap * torch.tanh(s / cap)
+    i = torch.arange(nq)[:, None] + (nk - nq)
+    j = torch.arange(nk)[None, :]
+    if use_alibi:
+        s = s - torch.tensor(slopes)[None, :, None, None] * (i - j).abs()
+    ok = torch.ones(nq, nk, dtype=torch.bool)
+    if causal:
+        ok &= j <= i
+    if wl >= 0:
+        ok &= j >= i - wl
+    if wr >= 0:
+        ok &= j <= i + wr
+    s = s.masked_fill(~ok, float("-inf"))
+    o = torch.einsum("bhij,bjhd->bihd", torch.softmax(s, dim=-1), tv)
+    o.backward(torch.tensor(g))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,wl,wr,slope", [(False, -1, -1, None), (True, -1, -1, 0.4),
+                                                (True, 2, 0, None)])
+def test_t25_backward_shift_invariances(causal, wl, wr, slope):
+    """Adding one vector to every key moves each row's scores by a constant, which the
+    softmax ignores, so the dK rows sum to 0; adding one vector to every value moves
+    each non-empty row's output by it, so the dV rows sum to the dO of those rows."""
+    nq, nk, d = 6, 8, 3
+    q, k, v, g = rnd(88, nq, d), rnd(89, nk, d), rnd(90, nk, d), rnd(91, nq, d)
+    dq, dk, dv, _ = O.attention_bwd_bh(q, k, v, g, nq, 0.8, causal, wl, wr, slope, 0.0)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+    nonempty = O.allowed_mask(nq, nk, np.arange(nq), causal, wl, wr).any(axis=1)
+    np.testing.assert_allclose(dv.sum(axis=0), g[nonempty].sum(axis=0), atol=1e-12)
+
+
+def test_t26_backward_row_term_is_do_dot_o():
+    B, nq, nk, H, d = 2, 5, 7, 2, 4
+    q, k, v, g = rnd(92, B, nq, H, d), rnd(93, B, nk, H, d), rnd(94, B, nk, H, d), rnd(95, B, nq, H, d)
+    o, _ = O.attention_ref(q, k, v, 0.5, True, -1, -1, np.array([0.1, 0.2]), 3.0)
+    _, _, _, D = O.attention_bwd_ref(q, k, v, g, 0.5, True, -1, -1, np.array([0.1, 0.2]), 3.0)
+    np.testing.assert_allclose(D, np.einsum("bihd,bihd->bhi", g, o), atol=1e-12)
