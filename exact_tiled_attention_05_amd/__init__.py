@@ -2,12 +2,13 @@
 
 The functions named like the C ABI (``fa_fwd``, ``fa_fwd_split``,
 ``fa_fwd_splitkv``, ``fa_fwd_splitkv_seqlens``, ``fa_fwd_splitkv_append``, ``fa_fwd_varlen``,
-``fa_splitkv_combine``, ``fa_status_string``, ``fa_split_chunk_len``) only
+``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_splitkv_combine``, ``fa_status_string``,
+``fa_split_chunk_len``) only
 marshal arguments: torch tensors become device pointers, the current torch
 stream becomes the HIP stream, and every step of the computation runs in the
 library's kernels. ``attention``, ``attention_varlen``, ``attention_split``,
-``attention_paged_splitkv``, ``combine`` and ``decode_paged`` add output
-allocation (torch.empty) on top of them.
+``attention_paged_splitkv``, ``attention_paged_append``, ``attention_backward``,
+``combine`` and ``decode_paged`` add output allocation (torch.empty) on top of them.
 
 The library must be built (``python -m exact_tiled_attention_05_amd.build``);
 importing works without it, but every call raises if libfa.so is missing.
@@ -23,9 +24,11 @@ import torch
 __all__ = [
     "FA_FP32", "FA_BF16", "FaError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
-    "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len", "attention",
-    "attention_varlen", "attention_split", "attention_split_partials", "attention_paged_append",
-    "attention_paged_splitkv", "combine", "decode_paged",
+    "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_bytes",
+    "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len",
+    "attention", "attention_varlen", "attention_split", "attention_split_partials",
+    "attention_paged_splitkv", "attention_paged_append", "attention_backward", "combine",
+    "decode_paged",
 ]
 
 FA_FP32, FA_BF16 = 0, 1
@@ -34,7 +37,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 _lib = None
 
 EXPORTED = ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
-            "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len")
+            "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_bytes", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len")
 
 
 class FaError(RuntimeError):
@@ -70,6 +73,11 @@ def load_library():
     lib.fa_fwd_splitkv_append.argtypes = [vp, vp, vp, vp, vp, i, vp, i, i, vp, vp, vp, i, i, i,
                                           i, i, i, f, i, i, i, vp, f, vp]
     lib.fa_fwd_splitkv_append.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, i, vp, i, i, i, i, i, f, i,
+                           i, i, vp, f, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_longlong
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, i, vp, i, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
                                   i, vp, f, vp]
     lib.fa_fwd_varlen.restype = i
@@ -178,6 +186,21 @@ def fa_fwd_splitkv_append(q, k_new, v_new, k_cache, v_cache, block_table, max_pa
         int(max_seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)),
         int(window_left), int(window_right), _ptr(alibi_slopes), float(softcap),
         _stream(stream))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, batch, heads, seqlen_q, seqlen_k,
+           head_dim, softmax_scale, causal=False, window_left=-1, window_right=-1,
+           alibi_slopes=None, softcap=0.0, stream=None) -> int:
+    """Call fa_bwd on caller-allocated tensors; returns the status code."""
+    return load_library().fa_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _dtype_code(q), _dtype_code(o),
+        _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq), _ptr(workspace), int(batch), int(heads),
+        int(seqlen_q), int(seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)),
+        int(window_left), int(window_right), _ptr(alibi_slopes), float(softcap), _stream(stream))
+
+
+def fa_bwd_workspace_bytes(batch: int, heads: int, seqlen_q: int) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(int(batch), int(heads), int(seqlen_q)))
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, heads, total_q, total_k,
@@ -301,6 +324,31 @@ def attention_paged_splitkv(q, k_cache, v_cache, block_table, seqlen_k, num_spli
                                       window_right, alibi_slopes, softcap, stream),
                "fa_fwd_splitkv_seqlens")
     return o_part, lse_part
+
+
+def attention_backward(q, k, v, o, lse, dout, softmax_scale=None, causal=False, window_left=-1,
+                       window_right=-1, alibi_slopes=None, softcap=0.0,
+                       grad_dtype=torch.float32, stream=None):
+    """dq, dk, dv (grad_dtype) for q [B,Nq,H,d], k/v [B,Nk,H,d], the forward's o and lse,
+    and dout [B,Nq,H,d] (same dtype as q)."""
+    _same_dtype(q, k, v, dout)
+    B, nq, H, d = q.shape
+    nk = k.shape[1]
+    if tuple(k.shape) != (B, nk, H, d) or tuple(v.shape) != (B, nk, H, d):
+        raise ValueError("k and v must be [B, Nk, H, d] matching q")
+    if tuple(o.shape) != (B, nq, H, d) or tuple(dout.shape) != (B, nq, H, d):
+        raise ValueError("o and dout must be [B, Nq, H, d]")
+    if tuple(lse.shape) != (B, H, nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, Nq]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    dq = torch.empty((B, nq, H, d), dtype=grad_dtype, device=q.device)
+    dk = torch.empty((B, nk, H, d), dtype=grad_dtype, device=q.device)
+    dv = torch.empty((B, nk, H, d), dtype=grad_dtype, device=q.device)
+    ws = torch.empty((2 * B * H * nq,), dtype=torch.float32, device=q.device)
+    _check(fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, nq, nk, d, softmax_scale, causal,
+                  window_left, window_right, alibi_slopes, softcap, stream), "fa_bwd")
+    return dq, dk, dv
 
 
 def attention_paged_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens,

@@ -327,6 +327,79 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, int in_dtype, voi
   return fn(p, stream) ? FA_ERR_HIP : FA_OK;
 }
 
+long long fa_bwd_workspace_bytes(int batch, int heads, int seqlen_q) {
+  if (batch <= 0 || heads <= 0 || seqlen_q <= 0) return -1;
+  return 2LL * batch * heads * seqlen_q * (long long)sizeof(float);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, int in_dtype, int o_dtype, void* dq, void* dk, void* dv,
+           int grad_dtype, float* workspace, int batch, int heads, int seqlen_q, int seqlen_k,
+           int head_dim, float softmax_scale, int causal, int window_left, int window_right,
+           const float* alibi_slopes, float softcap, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+  int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
+  if (st) return st;
+  if ((st = check_kind(in_dtype, head_dim))) return st;
+  if (in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != FA_FP32 && o_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (grad_dtype != FA_FP32 && grad_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
+    return st;
+
+  // Reuse the forward's mask folding (a window wider than both sequences is no
+  // constraint; causal is the right window 0).
+  fa::FwdParams f = {};
+  fill_common(f, batch, heads, seqlen_q, seqlen_k, softmax_scale, causal, window_left,
+              window_right, alibi_slopes, softcap, fa::BWD_BM);
+  fa::BwdParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  const int64_t rows = (int64_t)batch * heads * seqlen_q;
+  p.dsum = workspace;
+  p.lse2 = workspace + rows;
+  p.alibi = alibi_slopes;
+  p.B = batch;
+  p.H = heads;
+  p.Nq = seqlen_q;
+  p.Nk = seqlen_k;
+  p.window_left = f.window_left;
+  p.window_right = f.window_right;
+  p.o_bf16 = o_dtype == FA_BF16;
+  p.g_bf16 = grad_dtype == FA_BF16;
+  p.num_q_tiles = (seqlen_q + fa::BWD_BM - 1) / fa::BWD_BM;
+  p.num_k_tiles = (seqlen_k + fa::BWD_BK - 1) / fa::BWD_BK;
+  p.scale = softmax_scale;
+  p.scale_log2 = f.scale_log2;
+  p.softcap_log2 = f.softcap_log2;
+  p.scale_over_cap2 = f.scale_over_cap2;
+  if ((int64_t)p.num_q_tiles * heads * batch > kMaxGroups ||
+      (int64_t)p.num_k_tiles * heads * batch > kMaxGroups || rows / 8 > kMaxGroups)
+    return FA_ERR_SHAPE;
+
+  const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
+  int rc;
+#define FA_BWD(D)                                                       \
+  if (sc && al) rc = fa::launch_bwd_bf16<D, true, true>(p, stream);     \
+  else if (sc) rc = fa::launch_bwd_bf16<D, true, false>(p, stream);     \
+  else if (al) rc = fa::launch_bwd_bf16<D, false, true>(p, stream);     \
+  else rc = fa::launch_bwd_bf16<D, false, false>(p, stream);
+  if (head_dim == 64) {
+    FA_BWD(64)
+  } else {
+    FA_BWD(128)
+  }
+#undef FA_BWD
+  return rc ? FA_ERR_HIP : FA_OK;
+}
+
 int fa_splitkv_combine(const float* o_part, const float* lse_part, int num_splits, int batch,
                        int heads, int seqlen_q, int head_dim, void* o, int o_dtype, float* lse,
                        void* stream) {

@@ -1,0 +1,612 @@
+// Backward pass of the bf16 tiled attention for gfx950 (MI355X).
+//
+// The probabilities are recomputed from the forward's per-row log-sum-exp
+// instead of being stored, so no Nq x Nk matrix reaches device memory in this
+// direction either ("IO感知技术革命: FlashAttention如何重塑大模型训练的经济学", the
+// sections on tiling and on O(N) memory; the backward is what its training
+// figures run on). Three launches, none with atomics: every gradient element
+// is produced by one workgroup in one fixed order, so the pass is
+// deterministic by construction (the update article lists a deterministic
+// backward under v2.4).
+//
+//   1. prep:  D_i = dO_i . O_i and the LSE in log2 units (+inf for a row with
+//             no key, so that its probabilities come out 0).
+//   2. dK/dV: one workgroup of 4 wavefronts per (128-key tile, head, batch).
+//             Each wavefront keeps 32 keys in its lanes: K as the B operand of
+//             S = Q K^T in registers, V in LDS for dP = dO V^T, and walks the
+//             32-row query blocks that see its keys:
+//               P = exp2(S' - LSE2), dS = P (dP - D), dZ = dS (1 - tanh^2) with a cap,
+//               dV^T += dO^T P and dK^T += Q^T dZ, the transposed dO and Q read
+//               from LDS with ds_read_b64_tr_b16 (P and dZ stay in registers).
+//   3. dQ:    one workgroup per (128-row query tile, head, batch), laid out as
+//             the forward (a query row per lane pair): S^T = K Q^T and
+//             dP^T = V dO^T with Q and dO in registers, dQ^T += K^T dZ^T with K
+//             read transposed from LDS.
+// All products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and
+// dZ are rounded to bf16 (nearest even) as MFMA operands. K/V (dQ) and Q/dO
+// (dK/dV) tiles travel HBM -> LDS with buffer loads that write LDS directly,
+// two stages deep, in the forward's swizzled layout.
+#include <hip/hip_runtime.h>
+
+#include "fa_device.h"
+#include "fa_lds.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 256;  // 4 wavefronts
+constexpr int kBQ = 32;        // query rows per dK/dV step
+constexpr int kBN = 64;        // keys per dQ step
+constexpr int kBK = BWD_BK;    // keys per dK/dV workgroup (32 per wavefront)
+constexpr int kBM = BWD_BM;    // query rows per dQ workgroup (32 per wavefront)
+constexpr float kInf = __builtin_inff();
+
+// Wavefronts per SIMD the dK/dV kernel is register-budgeted for: at head_dim
+// 128 its two 128 x 32 fp32 accumulators, the S and dP tiles and K need more
+// than the 256 registers of two wavefronts, so it runs one per SIMD.
+template <int D>
+struct DkdvWaves {
+  static constexpr int value = D == 128 ? 1 : 2;
+};
+
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// 1. D = rowsum(dO * O) and LSE2, LPR lanes per row (8 elements each).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = kThreads / LPR;
+  const int tid = threadIdx.x, c = tid % LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;  // (b * Nq + i) * H + h
+  const bool ok = row < (int64_t)p.B * p.Nq * p.H;
+  float acc = 0.0f;
+  if (ok) {
+    const int64_t e = row * D + 8 * c;
+    const u32x4_t g = *(const u32x4_t*)((const uint16_t*)p.dout + e);
+    float o[8];
+    if (p.o_bf16) {
+      const u32x4_t x = *(const u32x4_t*)((const uint16_t*)p.o + e);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        o[2 * k] = bf16_lo(x[k]);
+        o[2 * k + 1] = bf16_hi(x[k]);
+      }
+    } else {
+      const f32x4_t x0 = *(const f32x4_t*)((const float*)p.o + e);
+      const f32x4_t x1 = *(const f32x4_t*)((const float*)p.o + e + 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        o[k] = x0[k];
+        o[4 + k] = x1[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc += bf16_lo(g[k]) * o[2 * k] + bf16_hi(g[k]) * o[2 * k + 1];
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m);
+  if (ok && c == 0) {
+    const int h = (int)(row % p.H);
+    const int64_t bi = row / p.H;
+    const int i = (int)(bi % p.Nq);
+    const int b = (int)(bi / p.Nq);
+    const int64_t idx = ((int64_t)b * p.H + h) * p.Nq + i;
+    p.dsum[idx] = acc;
+    const float l = p.lse[idx];
+    p.lse2[idx] = l == kNegInf ? kInf : l * kLog2e;
+  }
+}
+
+// Score in log2 units for a raw product s = q.k: scaled, capped (th = the tanh
+// value, for the cap's derivative), ALiBi-shifted by dist = |i + off - j|.
+template <bool SOFTCAP, bool ALIBI>
+__device__ __forceinline__ float bwd_score(const BwdParams& p, float s, float slope_log2,
+                                           float dist, float& th) {
+  float x;
+  if constexpr (SOFTCAP) {
+    const float e = fast_exp2(s * p.scale_over_cap2);
+    th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+    x = p.softcap_log2 * th;
+  } else {
+    th = 0.0f;
+    x = s * p.scale_log2;
+  }
+  if constexpr (ALIBI) x -= slope_log2 * dist;
+  return x;
+}
+
+// Queries that may see key j: [lo, hi), bottom-right aligned (off = Nk - Nq).
+__device__ __forceinline__ void query_range(int j, int off, int nq, int wl, int wr, int& lo,
+                                            int& hi) {
+  lo = wr >= 0 ? max(0, j - off - wr) : 0;
+  hi = wl >= 0 ? min(nq, j - off + wl + 1) : nq;
+  hi = max(hi, lo);
+}
+
+// Store 4 consecutive gradient values (scaled) as fp32 or bf16.
+__device__ __forceinline__ void store_grad4(void* base, int bf16, int64_t off, float a, float b,
+                                            float c, float d) {
+  f32x4_t x = {a, b, c, d};
+  if (bf16) {
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    *(bf16x4_t*)((__bf16*)base + off) = __builtin_convertvector(x, bf16x4_t);
+  } else {
+    *(f32x4_t*)((float*)base + off) = x;
+  }
+}
+
+// Zero rows [r0, r1) of a [B, N, H, D] gradient for (b, h).
+__device__ void zero_rows(void* base, int bf16, int b, int h, int N, int H, int D, int r0, int r1,
+                          int tid) {
+  const int n = (r1 - r0) * D / 4;
+  for (int idx = tid; idx < n; idx += kThreads) {
+    const int row = r0 + idx / (D / 4), c = idx % (D / 4);
+    store_grad4(base, bf16, (((int64_t)b * N + row) * H + h) * D + 4 * c, 0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK and dV
+// ---------------------------------------------------------------------------
+template <int D, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(DkdvWaves<D>::value, DkdvWaves<D>::value)))
+void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int KS = D / 16;               // k-steps over head_dim
+  constexpr int NDB = D / 32;              // 32-row blocks of dK^T / dV^T
+  constexpr int CPR = D / 8;               // 16-byte chunks per row
+  constexpr int RPL = 64 / CPR;            // rows per wavefront-wide copy
+  constexpr int QLOADS = kBQ / RPL / 4;    // copies per wavefront per tensor per step
+  constexpr int VLOADS = kBK / RPL / 4;    // copies per wavefront for the V tile
+  static_assert(QLOADS >= 1 && VLOADS >= 1, "tile shape");
+  constexpr int QT = kBQ * D;
+  constexpr int kReadAhead = 4;            // transposed-read MFMAs in flight
+
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[kBK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ0[QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ1[QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sG0[QT];  // dO
+  __shared__ __attribute__((aligned(1024))) uint16_t sG1[QT];
+  __shared__ __attribute__((aligned(16))) float sL0[kBQ], sL1[kBQ], sD0[kBQ], sD1[kBQ];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
+  int L = blockIdx.x;
+  const int h = L % p.H;
+  L /= p.H;
+  const int b = L % p.B;
+  const int kt = L / p.B;  // ascending: under causal the first key tile is seen by the most rows
+  const int nq = p.Nq, nk = p.Nk, off = nk - nq;
+  const int wl = p.window_left, wr = p.window_right;
+  const int k0 = kt * kBK, k1 = min(nk, k0 + kBK);
+
+  // Query rows the workgroup's keys are seen by (union over its keys).
+  int ulo, uhi, tmp;
+  query_range(k0, off, nq, wl, wr, ulo, tmp);
+  query_range(k1 - 1, off, nq, wl, wr, tmp, uhi);
+  uhi = max(uhi, ulo);
+  if (uhi <= ulo) {
+    zero_rows(p.dk, p.g_bf16, b, h, nk, p.H, D, k0, k1, tid);
+    zero_rows(p.dv, p.g_bf16, b, h, nk, p.H, D, k0, k1, tid);
+    return;
+  }
+
+  // This wavefront's keys: the union [wlo, whi) and intersection [wflo, wfhi)
+  // of their query ranges; this lane's key and its own range [rlo, rhi).
+  const int kw0 = k0 + 32 * w, kw1 = min(k1, kw0 + 32);
+  const bool wave_live = kw0 < k1;
+  int wlo = 0, whi = 0, wflo = 0, wfhi = 0;
+  if (wave_live) {
+    query_range(kw0, off, nq, wl, wr, wlo, wfhi);
+    query_range(kw1 - 1, off, nq, wl, wr, wflo, whi);
+  }
+  const bool wave_full = kw1 - kw0 == 32;
+  const int key = kw0 + r;
+  int rlo = 0, rhi = 0;
+  if (key < k1) query_range(key, off, nq, wl, wr, rlo, rhi);
+
+  float slope_log2 = 0.0f;
+  if constexpr (ALIBI) slope_log2 = p.alibi[h] * kLog2e;
+
+  // K of this lane's key: columns 16ks + 8h2 .. +7 (B operand of S = Q K^T).
+  bf16x8_t kf[KS];
+  {
+    const uint16_t* kp =
+        (const uint16_t*)p.k + (((int64_t)b * nk + min(key, nk - 1)) * p.H + h) * D + 8 * h2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t x = *(const u32x4_t*)(kp + 16 * ks);
+      if (key >= k1) x = u32x4_t{0, 0, 0, 0};
+      kf[ks] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+
+  // HBM -> LDS copies. Copy i of wavefront w fills rows RPL*(n*w + i) + lane/CPR
+  // (n copies per wavefront), lane L the physical chunk L % CPR of its row.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int64_t row_bytes = 2 * (int64_t)p.H * D;
+  auto lane_off = [&](int ld) __attribute__((always_inline)) {
+    const int trow = RPL * ld + lane / CPR;
+    const int chunk = (lane % CPR) ^ swz<D>(trow);
+    return (unsigned)(trow * row_bytes + 16 * chunk);
+  };
+  {
+    // V tile of the workgroup's keys (rows past Nk arrive as zeros).
+    const char* vb = (const char*)p.v + 2 * ((((int64_t)b * nk + k0) * p.H + h) * D);
+    const int64_t left = (int64_t)(nk - 1 - k0) * row_bytes + 2 * D;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vb, left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i)
+      buffer_load_lds16(rs, sV + 512 * (VLOADS * wu + i), lane_off(VLOADS * wu + i));
+  }
+  const char* qbh = (const char*)p.q + 2 * (((int64_t)b * nq * p.H + h) * D);
+  const char* gbh = (const char*)p.dout + 2 * (((int64_t)b * nq * p.H + h) * D);
+  const int64_t qend = (int64_t)(nq - 1) * row_bytes + 2 * D;
+  const int64_t rowbase = ((int64_t)b * p.H + h) * nq;
+  auto copy_block = [&](uint16_t* dq_, uint16_t* dg_, int qb) __attribute__((always_inline)) {
+    const int64_t tb = (int64_t)qb * row_bytes;
+    const int64_t left = qend - tb;
+    const int n = left <= 0 ? 0 : (left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbh + tb, n);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gbh + tb, n);
+#pragma unroll
+    for (int i = 0; i < QLOADS; ++i) {
+      buffer_load_lds16(rq, dq_ + 512 * (QLOADS * wu + i), lane_off(QLOADS * wu + i));
+      buffer_load_lds16(rg, dg_ + 512 * (QLOADS * wu + i), lane_off(QLOADS * wu + i));
+    }
+  };
+  // LSE2 and D of a block (rows past Nq: LSE2 = +inf, D = 0), by the first wavefront.
+  auto load_rowterms = [&](int qb, float& lv, float& dv) __attribute__((always_inline)) {
+    const int i = qb + (lane & 31);
+    lv = kInf;
+    dv = 0.0f;
+    if (i < nq) {
+      if (lane < 32) lv = p.lse2[rowbase + i];
+      else dv = p.dsum[rowbase + i];
+    }
+  };
+  auto store_rowterms = [&](float* sl, float* sd, float lv, float dv) __attribute__((always_inline)) {
+    if (lane < 32) sl[lane] = lv;
+    else sd[lane - 32] = dv;
+  };
+
+  f32x16_t dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dkacc[db] = f32x16_t{};
+    dvacc[db] = f32x16_t{};
+  }
+  const int gl = lane & 15, sub = (lane >> 4) & 1;
+
+  auto compute = [&](const uint16_t* sq, const uint16_t* sg, const float* sl, const float* sd,
+                     int qb) __attribute__((always_inline)) {
+    // S = Q K^T and dP = dO V^T for 32 queries x this wavefront's 32 keys.
+    f32x16_t sacc = f32x16_t{}, pacc = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sq + tile_off<D>(r, 2 * ks + h2)));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sacc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sg + tile_off<D>(r, 2 * ks + h2)));
+      const bf16x8_t bv =
+          __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sV + tile_off<D>(32 * w + r, 2 * ks + h2)));
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, pacc, 0, 0, 0);
+    }
+    // Slot v holds query qb + 8*(v/4) + 4*h2 + v%4 of this lane's key.
+    const bool masked = !(wave_full && qb >= wflo && qb + kBQ <= wfhi);
+    const int lo_rel = rlo - qb - 4 * h2, hi_rel = rhi - qb - 4 * h2;
+    const float rel = (float)(key - off - qb - 4 * h2);
+    bf16x8_t pb[2], zb[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      f32x8_t pa, za;
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = 2 * tt + gg;
+        const f32x4_t l4 = *(const f32x4_t*)(sl + 8 * g + 4 * h2);
+        const f32x4_t d4 = *(const f32x4_t*)(sd + 8 * g + 4 * h2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * g + e, kk = 8 * g + e;
+          float th;
+          const float x = bwd_score<SOFTCAP, ALIBI>(p, sacc[v], slope_log2,
+                                                    __builtin_fabsf(rel - (float)kk), th);
+          float pr = fast_exp2(x - l4[e]);
+          if (masked && (kk < lo_rel || kk >= hi_rel)) pr = 0.0f;
+          float dz = pr * (pacc[v] - d4[e]);
+          if constexpr (SOFTCAP) dz *= 1.0f - th * th;
+          pa[4 * gg + e] = pr;
+          za[4 * gg + e] = dz;
+        }
+      }
+      pb[tt] = __builtin_convertvector(pa, bf16x8_t);
+      zb[tt] = __builtin_convertvector(za, bf16x8_t);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dZ: k-step tt covers the block's queries
+    // 16tt + 4h2 + {0..3, 8..11}, read transposed from the dO and Q tiles.
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int vrow = 16 * tt + 4 * h2 + (gl >> 2);
+        const int col = 32 * db + 16 * sub + 4 * (gl & 3);
+        const int o_lo = tile_off<D>(vrow, col >> 3) + (col & 7);
+        const int o_hi = tile_off<D>(vrow + 8, col >> 3) + (col & 7);
+        const s16x4_t g_lo = ds_read_tr16(sg + o_lo), g_hi = ds_read_tr16(sg + o_hi);
+        const s16x4_t q_lo = ds_read_tr16(sq + o_lo), q_hi = ds_read_tr16(sq + o_hi);
+        const s16x8_t ga = {g_lo[0], g_lo[1], g_lo[2], g_lo[3], g_hi[0], g_hi[1], g_hi[2], g_hi[3]};
+        const s16x8_t qa = {q_lo[0], q_lo[1], q_lo[2], q_lo[3], q_hi[0], q_hi[1], q_hi[2], q_hi[3]};
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ga), pb[tt],
+                                                            dvacc[db], 0, 0, 0);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qa), zb[tt],
+                                                            dkacc[db], 0, 0, 0);
+      }
+    }
+    // Schedule: the transposed reads of kReadAhead MFMAs first, then one MFMA
+    // and the two reads of a later one, alternately (bounds the live operands).
+    constexpr int kMf = 4 * NDB;  // MFMAs of the two products
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadAhead, 0);
+#pragma unroll
+    for (int i = 0; i < kMf - kReadAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 0);
+  };
+
+  const int qb_first = (ulo / kBQ) * kBQ;
+  const int nblocks = (uhi - qb_first + kBQ - 1) / kBQ;
+  float lv, dvv;
+  copy_block(sQ0, sG0, qb_first);
+  if (wu == 0) {
+    load_rowterms(qb_first, lv, dvv);
+    store_rowterms(sL0, sD0, lv, dvv);
+  }
+  wait_vmem_barrier<0>();
+  auto step = [&](auto par, int it) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(par)::value;
+    const int qb = qb_first + it * kBQ;
+    const bool more = it + 1 < nblocks;
+    if (more) {
+      copy_block(ODD ? sQ0 : sQ1, ODD ? sG0 : sG1, qb + kBQ);
+      if (wu == 0) load_rowterms(qb + kBQ, lv, dvv);
+    }
+    if (wave_live && qb < whi && qb + kBQ > wlo)
+      compute(ODD ? sQ1 : sQ0, ODD ? sG1 : sG0, ODD ? sL1 : sL0, ODD ? sD1 : sD0, qb);
+    if (more && wu == 0) store_rowterms(ODD ? sL0 : sL1, ODD ? sD0 : sD1, lv, dvv);
+    wait_vmem_barrier<0>();
+  };
+  for (int it = 0; it < nblocks; it += 2) {
+    step(std::false_type{}, it);
+    if (it + 1 < nblocks) step(std::true_type{}, it + 1);
+  }
+
+  // Epilogue: lane = key, slots = head_dim rows 32db + 8g + 4h2 + {0..3}.
+  if (key >= k1) return;
+  const int64_t base = (((int64_t)b * nk + key) * p.H + h) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t o = base + 32 * db + 8 * g + 4 * h2;
+      store_grad4(p.dk, p.g_bf16, o, dkacc[db][4 * g] * p.scale, dkacc[db][4 * g + 1] * p.scale,
+                  dkacc[db][4 * g + 2] * p.scale, dkacc[db][4 * g + 3] * p.scale);
+      store_grad4(p.dv, p.g_bf16, o, dvacc[db][4 * g], dvacc[db][4 * g + 1], dvacc[db][4 * g + 2],
+                  dvacc[db][4 * g + 3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ
+// ---------------------------------------------------------------------------
+template <int D, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdParams p) {
+  constexpr int KS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int RPL = 64 / CPR;
+  constexpr int LOADS = kBN / RPL / 4;
+  constexpr int TILE = kBN * D;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[TILE];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
+  int L = blockIdx.x;
+  const int h = L % p.H;
+  L /= p.H;
+  const int b = L % p.B;
+  const int qt = p.num_q_tiles - 1 - L / p.B;  // heaviest (last) tile first
+  const int nq = p.Nq, nk = p.Nk, off = nk - nq;
+  const int q0 = qt * kBM, q1 = min(nq, q0 + kBM);
+  const KeyBounds wg = key_bounds(q0, q1, off, 0, nk, p.window_left, p.window_right);
+  if (wg.hi <= wg.lo) {
+    zero_rows(p.dq, p.g_bf16, b, h, nq, p.H, D, q0, q1, tid);
+    return;
+  }
+  const int wq0 = q0 + 32 * w, wq1 = min(nq, wq0 + 32);
+  const bool wave_live = wq0 < nq;
+  const KeyBounds wk = key_bounds(wq0, max(wq1, wq0 + 1), off, 0, nk, p.window_left, p.window_right);
+  const int row = wq0 + r;
+  const KeyBounds rk = key_bounds(row, row + 1, off, 0, nk, p.window_left, p.window_right);
+
+  float slope_log2 = 0.0f;
+  if constexpr (ALIBI) slope_log2 = p.alibi[h] * kLog2e;
+
+  // Q and dO of this lane's row: columns 16ks + 8h2 .. +7 (B operands).
+  bf16x8_t qf[KS], gf[KS];
+  {
+    const int64_t ro = (((int64_t)b * nq + min(row, nq - 1)) * p.H + h) * D + 8 * h2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t x = *(const u32x4_t*)((const uint16_t*)p.q + ro + 16 * ks);
+      u32x4_t y = *(const u32x4_t*)((const uint16_t*)p.dout + ro + 16 * ks);
+      if (row >= nq) x = y = u32x4_t{0, 0, 0, 0};
+      qf[ks] = __builtin_bit_cast(bf16x8_t, x);
+      gf[ks] = __builtin_bit_cast(bf16x8_t, y);
+    }
+  }
+  const int64_t ri = ((int64_t)b * p.H + h) * nq + min(row, nq - 1);
+  const float lse2 = row < nq ? p.lse2[ri] : kInf;
+  const float drow = row < nq ? p.dsum[ri] : 0.0f;
+
+  // Contiguous K/V copies, as in the forward.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int64_t row_bytes = 2 * (int64_t)p.H * D;
+  const int64_t bh_bytes = 2 * (((int64_t)b * nk * p.H + h) * D);
+  const int64_t end_bytes = (int64_t)(nk - 1) * row_bytes + 2 * D;
+  const char* kbh = (const char*)p.k + bh_bytes;
+  const char* vbh = (const char*)p.v + bh_bytes;
+  unsigned lane_bytes[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int trow = RPL * (LOADS * wu + i) + lane / CPR;
+    const int chunk = (lane % CPR) ^ swz<D>(trow);
+    lane_bytes[i] = (unsigned)(trow * row_bytes + 16 * chunk);
+  }
+  auto copy_tiles = [&](uint16_t* kd, uint16_t* vd, int j0) __attribute__((always_inline)) {
+    const int64_t tb = (int64_t)j0 * row_bytes;
+    const int64_t left = end_bytes - tb;
+    const int n = left <= 0 ? 0 : (left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
+    const __amdgpu_buffer_rsrc_t rk_ = make_rsrc(kbh + tb, n);
+    const __amdgpu_buffer_rsrc_t rv_ = make_rsrc(vbh + tb, n);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      buffer_load_lds16(rk_, kd + 512 * (LOADS * wu + i), lane_bytes[i]);
+      buffer_load_lds16(rv_, vd + 512 * (LOADS * wu + i), lane_bytes[i]);
+    }
+  };
+
+  f32x16_t dqacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16_t{};
+  const int gl = lane & 15, sub = (lane >> 4) & 1;
+
+  auto compute = [&](const uint16_t* kt, const uint16_t* vt, int j0) __attribute__((always_inline)) {
+    // S^T = K Q^T and dP^T = V dO^T for 64 keys x this wavefront's 32 rows.
+    f32x16_t sacc[2], pacc[2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kt + tile_off<D>(32 * j + r, 2 * ks + h2)));
+        sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? f32x16_t{} : sacc[j], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(vt + tile_off<D>(32 * j + r, 2 * ks + h2)));
+        pacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gf[ks], ks == 0 ? f32x16_t{} : pacc[j], 0, 0, 0);
+      }
+    }
+    // Slot v of block j holds key j0 + 32j + 8*(v/4) + 4*h2 + v%4 of this lane's row.
+    const bool masked = !(j0 >= wk.flo && j0 + kBN <= wk.fhi);
+    const int lo_rel = rk.lo - j0 - 4 * h2, hi_rel = rk.hi - j0 - 4 * h2;
+    const float rel = (float)(row + off - j0 - 4 * h2);
+    float zv[2][16];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kk = 32 * j + 8 * (v >> 2) + (v & 3);
+        float th;
+        const float x = bwd_score<SOFTCAP, ALIBI>(p, sacc[j][v], slope_log2,
+                                                  __builtin_fabsf(rel - (float)kk), th);
+        float pr = fast_exp2(x - lse2);
+        if (masked && (kk < lo_rel || kk >= hi_rel)) pr = 0.0f;
+        float dz = pr * (pacc[j][v] - drow);
+        if constexpr (SOFTCAP) dz *= 1.0f - th * th;
+        zv[j][v] = dz;
+      }
+    // dQ^T += K^T dZ^T: k-step tt covers keys 16tt + 4h2 + {0..3, 8..11},
+    // K read transposed from LDS.
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f32x8_t z;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] = zv[tt >> 1][(tt & 1) * 8 + e];
+      const bf16x8_t zb = __builtin_convertvector(z, bf16x8_t);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int krow = 16 * tt + 4 * h2 + (gl >> 2);
+        const int col = 32 * db + 16 * sub + 4 * (gl & 3);
+        const s16x4_t lo = ds_read_tr16(kt + tile_off<D>(krow, col >> 3) + (col & 7));
+        const s16x4_t hi = ds_read_tr16(kt + tile_off<D>(krow + 8, col >> 3) + (col & 7));
+        const s16x8_t x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x), zb,
+                                                            dqacc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  const int j_first = (wg.lo / kBN) * kBN;
+  const int ntiles = (wg.hi - j_first + kBN - 1) / kBN;
+  copy_tiles(sK0, sV0, j_first);
+  wait_vmem_barrier<0>();
+  auto step = [&](auto par, int it) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(par)::value;
+    const int j0 = j_first + it * kBN;
+    if (it + 1 < ntiles) copy_tiles(ODD ? sK0 : sK1, ODD ? sV0 : sV1, j0 + kBN);
+    if (wave_live && j0 < wk.hi && j0 + kBN > wk.lo) compute(ODD ? sK1 : sK0, ODD ? sV1 : sV0, j0);
+    wait_vmem_barrier<0>();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(std::false_type{}, it);
+    if (it + 1 < ntiles) step(std::true_type{}, it + 1);
+  }
+
+  if (row >= nq) return;
+  const int64_t base = (((int64_t)b * nq + row) * p.H + h) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      store_grad4(p.dq, p.g_bf16, base + 32 * db + 8 * g + 4 * h2, dqacc[db][4 * g] * p.scale,
+                  dqacc[db][4 * g + 1] * p.scale, dqacc[db][4 * g + 2] * p.scale,
+                  dqacc[db][4 * g + 3] * p.scale);
+}
+
+}  // namespace
+
+template <int D, bool SOFTCAP, bool ALIBI>
+int launch_bwd_bf16(const BwdParams& p, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t rows = (int64_t)p.B * p.Nq * p.H;
+  constexpr int RPB = kThreads / (D / 8);
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads),
+                     0, s, p);
+  int rc = (int)hipGetLastError();
+  if (rc) return rc;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, SOFTCAP, ALIBI>),
+                     dim3((unsigned)((int64_t)p.num_k_tiles * p.H * p.B)), dim3(kThreads), 0, s, p);
+  rc = (int)hipGetLastError();
+  if (rc) return rc;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, SOFTCAP, ALIBI>),
+                     dim3((unsigned)((int64_t)p.num_q_tiles * p.H * p.B)), dim3(kThreads), 0, s, p);
+  return (int)hipGetLastError();
+}
+
+#define FA_INST(D, SC, AL) template int launch_bwd_bf16<D, SC, AL>(const BwdParams&, void*);
+FA_INST(64, false, false)
+FA_INST(64, false, true)
+FA_INST(64, true, false)
+FA_INST(64, true, true)
+FA_INST(128, false, false)
+FA_INST(128, false, true)
+FA_INST(128, true, false)
+FA_INST(128, true, true)
+#undef FA_INST
+
+}  // namespace fa

@@ -48,6 +48,30 @@ struct CombineParams {
   int o_bf16;
 };
 
+// One backward launch (fa_bwd): gradients of the contiguous forward.
+struct BwdParams {
+  const void* q;            // [B, Nq, H, D] bf16
+  const void* k;            // [B, Nk, H, D] bf16
+  const void* v;
+  const void* o;            // [B, Nq, H, D], fp32 or bf16 (o_bf16): the forward's output
+  const void* dout;         // [B, Nq, H, D] bf16
+  const float* lse;         // [B, H, Nq] the forward's log-sum-exp (natural log)
+  void* dq;                 // [B, Nq, H, D], fp32 or bf16 (g_bf16)
+  void* dk;                 // [B, Nk, H, D]
+  void* dv;
+  float* dsum;              // [B, H, Nq] workspace: D = rowsum(dO * O)
+  float* lse2;              // [B, H, Nq] workspace: LSE * log2(e), +inf for rows with no key
+  const float* alibi;       // [H] or nullptr
+  int B, H, Nq, Nk;
+  int window_left, window_right;
+  int o_bf16, g_bf16;
+  int num_q_tiles, num_k_tiles;
+  float scale;              // softmax_scale
+  float scale_log2;         // softmax_scale * log2(e)
+  float softcap_log2;       // softcap * log2(e)
+  float scale_over_cap2;    // 2 * softmax_scale / softcap * log2(e)
+};
+
 // Modes of the bf16 tiled forward.
 enum FwdMode {
   FWD_CONTIG = 0,        // contiguous K/V, whole key range -> O, LSE
@@ -64,11 +88,16 @@ template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream);
 template <int D>
 int launch_combine(const CombineParams& p, void* stream);
+template <int D, bool SOFTCAP, bool ALIBI>
+int launch_bwd_bf16(const BwdParams& p, void* stream);  // preprocess, dK/dV, dQ
 
 // Tile geometry the host needs for grid sizing.
 constexpr int BF16_BM = 128;
 // fa_fwd_split chunks are multiples of the key tile width.
 constexpr int SPLIT_ALIGN = 64;
 constexpr int F32_BM = 32;
+// Backward tiles: keys per dK/dV workgroup, query rows per dQ workgroup.
+constexpr int BWD_BK = 128;
+constexpr int BWD_BM = 128;
 
 }  // namespace fa

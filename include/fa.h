@@ -230,6 +230,41 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, int in_dtype,
                   const float* alibi_slopes, float softcap, void* stream);
 
 /*
+ * fa_bwd - backward pass of fa_fwd: dQ, dK, dV from dO, with the attention
+ * probabilities recomputed from the forward's LSE (no Nq x Nk matrix is
+ * stored; "IO感知技术革命: FlashAttention如何重塑大模型训练的经济学", tiling and
+ * O(N) memory, whose training figures rest on this pass). Every mask and
+ * score transform of fa_fwd is differentiated through: with S the scaled,
+ * capped, ALiBi-shifted and masked scores and P = exp(S - LSE),
+ *   dV = P^T dO,  dP = dO V^T,  D_i = rowsum(dO * O)_i,  dS = P * (dP - D),
+ *   dZ = dS * (1 - tanh^2(scale q.k / softcap)) with a cap (dZ = dS without),
+ *   dQ = scale dZ K,  dK = scale dZ^T Q.
+ * Deterministic: no atomics; each gradient element is written by one
+ * workgroup in a fixed order, so repeated calls give identical bits (the
+ * update article's v2.4 entry lists a deterministic backward).
+ *
+ *   q, dout        [batch, seqlen_q, heads, head_dim] in_dtype (FA_BF16 only)
+ *   k, v           [batch, seqlen_k, heads, head_dim] in_dtype
+ *   o              [batch, seqlen_q, heads, head_dim] o_dtype: fa_fwd's output
+ *   lse            [batch, heads, seqlen_q] float32: fa_fwd's log-sum-exp
+ *   dq / dk, dv    shaped as q / k, v, in grad_dtype (FA_FP32 or FA_BF16)
+ *   workspace      2 * batch * heads * seqlen_q floats (fa_bwd_workspace_bytes),
+ *                  device memory owned by the caller; overwritten
+ * P and dZ are rounded to bf16 as matrix-core operands (accumulation in
+ * fp32). Masks, scale, ALiBi and softcap must be those of the forward call.
+ * Three kernels run in order on `stream`. Errors as fa_fwd; fp32 inputs are
+ * FA_ERR_UNSUPPORTED.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, int in_dtype, int o_dtype, void* dq, void* dk, void* dv,
+           int grad_dtype, float* workspace, int batch, int heads, int seqlen_q, int seqlen_k,
+           int head_dim, float softmax_scale, int causal, int window_left, int window_right,
+           const float* alibi_slopes, float softcap, void* stream);
+
+/* Bytes of the workspace fa_bwd needs (-1 for a size <= 0). */
+long long fa_bwd_workspace_bytes(int batch, int heads, int seqlen_q);
+
+/*
  * fa_splitkv_combine - the separate reduce step that merges split partials
  * (the update article's v2.2 entry): for every (b, h, i),
  *   L = ln(sum_s exp(lse_part[s])),  O = sum_s exp(lse_part[s] - L) * o_part[s].

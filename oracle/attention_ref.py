@@ -194,7 +194,7 @@ def attention_ref(q, k, v, scale, causal=False, window_left=-1, window_right=-1,
 # Backward pass (gradients of the forward above)
 # --------------------------------------------------------------------------
 def attention_bwd_bh(q_bh, k_bh, v_bh, do_bh, nq, scale, causal=False, window_left=-1,
-                     window_right=-1, slope=None, softcap=0.0):
+                     window_right=-1, slope=None, softcap=0.0, with_bounds=False):
     """dQ, dK, dV [n, d] and D [nq] for one (batch, head), by the chain rule.
 
     The forward is O = P V with P = softmax(S) over the allowed keys and
@@ -205,6 +205,13 @@ def attention_bwd_bh(q_bh, k_bh, v_bh, do_bh, nq, scale, causal=False, window_le
     contribute nothing. (The pages call the training pass the backward pass and
     list a deterministic backward in the update article's v2.4 entry; the
     arithmetic is the derivative of standard attention, [Variants] section 二.1.)
+
+    with_bounds: also return a dict of magnitudes that bound how rounding moves
+    the gradients. "dq", "dk", "dv" = scale |dZ| |K|, scale |dZ|^T |Q|, P^T |dO|:
+    a relative change r of every entry of P and dZ moves dQ, dK, dV by at most r
+    times them. "dq_cancel", "dk_cancel" = the same products with |dZ| replaced
+    by P (|dP| + |D|): an absolute error e (|dP| + |D|) in dP - D (rounding of
+    the two sums before they cancel) moves dQ, dK by at most e times them.
     """
     rows = np.arange(nq)
     k_bh = np.asarray(k_bh, dtype=np.float64)
@@ -216,6 +223,10 @@ def attention_bwd_bh(q_bh, k_bh, v_bh, do_bh, nq, scale, causal=False, window_le
     dv = np.zeros_like(v_bh)
     D = np.zeros(nq)
     if k_bh.shape[0] == 0 or nq == 0:
+        if with_bounds:
+            return dq, dk, dv, D, {"dq": np.zeros_like(dq), "dk": np.zeros_like(dk),
+                                   "dv": np.zeros_like(dv), "dq_cancel": np.zeros_like(dq),
+                                   "dk_cancel": np.zeros_like(dk)}
         return dq, dk, dv, D
     s = scores_ref(q_bh, k_bh, rows, nq, scale, causal, window_left, window_right, slope, softcap)
     p, _, _ = softmax_rows(s)
@@ -228,15 +239,24 @@ def attention_bwd_bh(q_bh, k_bh, v_bh, do_bh, nq, scale, causal=False, window_le
         ds = ds * (1.0 - t * t)
     dq = scale * (ds @ k_bh)
     dk = scale * (ds.T @ q_bh)
+    if with_bounds:
+        a = np.abs(ds)
+        c = p * (np.abs(dp) + np.abs(D)[:, None])
+        ak, aq = np.abs(k_bh), np.abs(q_bh)
+        return dq, dk, dv, D, {"dq": scale * (a @ ak), "dk": scale * (a.T @ aq),
+                               "dv": p.T @ np.abs(do_bh), "dq_cancel": scale * (c @ ak),
+                               "dk_cancel": scale * (c.T @ aq)}
     return dq, dk, dv, D
 
 
 def attention_bwd_ref(q, k, v, do, scale, causal=False, window_left=-1, window_right=-1,
-                      alibi_slopes=None, softcap=0.0, bh=None):
+                      alibi_slopes=None, softcap=0.0, bh=None, with_bounds=False):
     """Gradients of attention_ref's O with respect to q, k, v, given dO.
 
     q, do [B, Nq, H, d]; k, v [B, Nk, H, d]. Returns dq, dk, dv (shaped like
     q, k, v) and D [B, H, Nq] = rowsum(dO * O); pairs outside bh are NaN.
+    with_bounds: also the bound magnitudes of attention_bwd_bh (a dict of arrays
+    shaped like the gradient each bounds).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -248,11 +268,18 @@ def attention_bwd_ref(q, k, v, do, scale, causal=False, window_left=-1, window_r
     dk = np.full(k.shape, np.nan)
     dv = np.full(v.shape, np.nan)
     D = np.full((B, H, nq), np.nan)
+    like = {"dq": q, "dk": k, "dv": v, "dq_cancel": q, "dk_cancel": k}
+    bounds = {n: np.full(x.shape, np.nan) for n, x in like.items()}
     for b, h in pairs:
         slope = None if alibi_slopes is None else float(alibi_slopes[h])
         g = attention_bwd_bh(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], nq, scale, causal,
-                             window_left, window_right, slope, softcap)
-        dq[b, :, h], dk[b, :, h], dv[b, :, h], D[b, h] = g
+                             window_left, window_right, slope, softcap, with_bounds)
+        dq[b, :, h], dk[b, :, h], dv[b, :, h], D[b, h] = g[:4]
+        if with_bounds:
+            for n in bounds:
+                bounds[n][b, :, h] = g[4][n]
+    if with_bounds:
+        return dq, dk, dv, D, bounds
     return dq, dk, dv, D
 
 

@@ -24,7 +24,8 @@ OK, NULL, SHAPE, UNSUP, MASK, HIP, VALUE = range(7)
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:\w+\s+)*\w+\s*\*?\s*(fa_\w+)\s*\(", text,
+                                 re.M)))
 
 
 def test_header_declares_the_calls():
@@ -237,3 +238,33 @@ def split_append(**kw):
 ])
 def test_fa_fwd_splitkv_append_rejects(kw, code):
     assert split_append(**kw) == code
+
+
+
+def bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, in_dtype=1, o_dtype=0, dq=FAKE,
+             dk=FAKE, dv=FAKE, g_dtype=0, ws=FAKE, batch=1, heads=2, seqlen_q=8, seqlen_k=8,
+             head_dim=128, scale=0.1, causal=1, wl=-1, wr=-1, alibi=None, softcap=0.0, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_bwd(
+        a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["in_dtype"], a["o_dtype"], a["dq"],
+        a["dk"], a["dv"], a["g_dtype"], a["ws"], a["batch"], a["heads"], a["seqlen_q"],
+        a["seqlen_k"], a["head_dim"], a["scale"], a["causal"], a["wl"], a["wr"], a["alibi"],
+        a["softcap"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(o=None), NULL), (dict(do=None), NULL), (dict(lse=None), NULL),
+    (dict(dq=None), NULL), (dict(dk=None), NULL), (dict(dv=None), NULL), (dict(ws=None), NULL),
+    (dict(batch=0), SHAPE), (dict(seqlen_q=0), SHAPE), (dict(seqlen_k=-1), SHAPE),
+    (dict(in_dtype=0), UNSUP), (dict(head_dim=96), UNSUP), (dict(o_dtype=4), UNSUP),
+    (dict(g_dtype=2), UNSUP), (dict(causal=1, wr=2), MASK), (dict(wl=-3), MASK),
+    (dict(scale=0.0), VALUE), (dict(softcap=math.inf), VALUE),
+])
+def test_fa_bwd_rejects(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(4, 16, 2048) == 2 * 4 * 16 * 2048 * 4
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1) == -1

@@ -560,3 +560,113 @@ def test_incremental_decode_three_steps():
                                         np.arange(1), 1, 1.0 / np.sqrt(d), True)
                 check(o.cpu().numpy()[b, :, h], lse.cpu().numpy()[b, h], ro, rl, "bf16",
                       f"step {step} b{b} h{h}")
+
+
+# --------------------------------------------------------------------------
+# Backward pass (fa_bwd)
+# --------------------------------------------------------------------------
+# The tolerance follows from the arithmetic: the kernels round P and dZ to bf16
+# (relative error at most 2^-9) as matrix-core operands and do everything else
+# in fp32. A relative change r of every P and dZ entry moves dV by at most
+# r P^T|dO|, dK by r scale |dZ|^T|Q| and dQ by r scale |dZ||K| (the oracle's
+# bound terms); the test allows twice that. dP and D are fp32 sums over head_dim
+# terms, so dP - D carries an error up to about d 2^-24 (|dP| + |D|) before it
+# cancels (to exactly 0 where a row sees a single key); the test allows 2^-16
+# (>= 2 d 2^-24 for d <= 128) times the oracle's cancellation magnitudes, plus
+# 2e-5 of the largest gradient for the remaining fp32 arithmetic. O and LSE
+# come from the oracle here, so the forward's own rounding stays out.
+U_BF16 = 2.0 ** -9
+E_CANCEL = 2.0 ** -16
+BWD_CASES = [
+    # (d, B, H, nq, nk, causal, wl, wr, alibi, cap)
+    (128, 1, 2, 128, 128, True, -1, -1, False, 0.0),
+    (128, 2, 2, 200, 333, True, -1, -1, False, 0.0),
+    (64, 1, 3, 300, 90, True, -1, -1, False, 0.0),       # Nq > Nk: rows with no key
+    (128, 1, 2, 257, 257, False, -1, -1, True, 0.0),
+    (64, 2, 2, 150, 400, True, 50, 0, False, 10.0),
+    (128, 1, 2, 100, 300, False, 40, 20, True, 20.0),
+    (64, 1, 2, 1, 129, True, -1, -1, True, 0.0),
+    (128, 1, 1, 129, 1, False, -1, -1, False, 0.0),
+    (128, 1, 2, 64, 1000, True, 100, 0, True, 30.0),
+]
+
+
+def check_grad(g, ref, bound, what, cancel=0.0):
+    g = np.asarray(g, dtype=np.float64)
+    assert not np.isnan(g).any(), f"{what}: NaN"
+    err = np.abs(g - ref)
+    tol = 2 * U_BF16 * bound + E_CANCEL * cancel + 2e-5 * max(float(np.abs(ref).max()), 1e-30)
+    bad = np.argwhere(err > tol)
+    assert len(bad) == 0, (f"{what}: {len(bad)} entries over the bound; first {bad[0].tolist()}: "
+                           f"{g[tuple(bad[0])]} vs {ref[tuple(bad[0])]} (tol {tol[tuple(bad[0])]:.3e})")
+    return float(err.max())
+
+
+def bwd_inputs(seed, B, nq, nk, H, d, amp):
+    q, k, v = qkv_case(seed, B, nq, nk, H, d, "bf16", amp)
+    do = W.gen_tensor(seed, 3, B, nq, H, d, 1.0, "bf16")
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("case", BWD_CASES)
+def test_bwd_small(case):
+    d, B, H, nq, nk, causal, wl, wr, alibi, cap = case
+    say(f"bwd {case}")
+    q, k, v, do = bwd_inputs(8000 + BWD_CASES.index(case), B, nq, nk, H, d, 2.0 if cap else 1.0)
+    qf, kf, vf, gf = (W.to_float(x, "bf16") for x in (q, k, v, do))
+    slopes = W.alibi_slopes(H) if alibi else None
+    ts = None if slopes is None else torch.from_numpy(slopes).cuda()
+    scale = 1.0 / np.sqrt(d)
+    o_ref, l_ref = O.attention_ref(qf, kf, vf, scale, causal, wl, wr, slopes, cap)
+    dq, dk, dv = fa.attention_backward(
+        to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+        torch.from_numpy(o_ref.astype(np.float32)).cuda(),
+        torch.from_numpy(l_ref.astype(np.float32)).cuda(), to_dev(do, "bf16"), scale, causal, wl,
+        wr, ts, cap)
+    torch.cuda.synchronize()
+    rq, rk, rv, _, bd = O.attention_bwd_ref(qf, kf, vf, gf, scale, causal, wl, wr, slopes, cap,
+                                             with_bounds=True)
+    print(check_grad(dq.cpu().numpy(), rq, bd["dq"], "dQ", bd["dq_cancel"]),
+          check_grad(dk.cpu().numpy(), rk, bd["dk"], "dK", bd["dk_cancel"]),
+          check_grad(dv.cpu().numpy(), rv, bd["dv"], "dV"))
+
+
+def test_bwd_deterministic_and_bf16_output():
+    """Two calls give identical bits; bf16 gradients are the fp32 ones rounded."""
+    B, nq, nk, H, d = 2, 300, 500, 4, 128
+    q, k, v, do = bwd_inputs(8100, B, nq, nk, H, d, 1.0)
+    tq, tk, tv, tg = (to_dev(x, "bf16") for x in (q, k, v, do))
+    ts = torch.from_numpy(W.alibi_slopes(H)).cuda()
+    o, lse = fa.attention(tq, tk, tv, 0.09, True, 200, 0, ts, 15.0)
+    a = fa.attention_backward(tq, tk, tv, o, lse, tg, 0.09, True, 200, 0, ts, 15.0)
+    b = fa.attention_backward(tq, tk, tv, o, lse, tg, 0.09, True, 200, 0, ts, 15.0)
+    c = fa.attention_backward(tq, tk, tv, o, lse, tg, 0.09, True, 200, 0, ts, 15.0,
+                              grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for x, y, z in zip(a, b, c):
+        assert torch.equal(x, y)
+        assert torch.equal(x.to(torch.bfloat16), z)
+
+
+def test_bwd_causal_prefill_full_size():
+    """The causal prefill shape (B4 H16 N2048 d128), end to end from the GPU
+    forward's O and LSE: sampled (b, h) pairs against the oracle. The forward's
+    own bf16 rounding enters D here, so the check is on the norm: every gradient
+    within 1e-2 of the oracle's in relative Frobenius norm, per (b, h)."""
+    w = W.WORKLOADS[2]
+    say(f"bwd full size {w}")
+    q, k, v = W.gen_qkv(w)
+    do = W.gen_tensor(w.seed, 3, w.B, w.Nq, w.H, w.d, 1.0, "bf16")
+    tq, tk, tv, tg = (to_dev(x, "bf16") for x in (q, k, v, do))
+    o, lse = fa.attention(tq, tk, tv, w.scale, True)
+    dq, dk, dv = fa.attention_backward(tq, tk, tv, o, lse, tg, w.scale, True)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+    assert not (np.isnan(dq).any() or np.isnan(dk).any() or np.isnan(dv).any())
+    for b, h in [(0, 0), (3, 15), (2, 7)]:
+        sl = lambda x: W.to_float(x[b, :, h], "bf16")  # noqa: E731
+        rq, rk, rv, _ = O.attention_bwd_bh(sl(q), sl(k), sl(v), sl(do), w.Nq, w.scale, True)
+        for got, ref, name in ((dq[b, :, h], rq, "dQ"), (dk[b, :, h], rk, "dK"), (dv[b, :, h], rv, "dV")):
+            rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+            say(f"  b{b} h{h} {name}: relative error {rel:.2e}")
+            assert rel <= 1e-2, (b, h, name, rel)
