@@ -11,7 +11,8 @@ prefill launch time); the decode's algorithmic GB/s and the split forward's
 TFLOP/s are reported beside it. After the timed steps, the variable-length
 entry points are timed on their own (a packed causal prefill of 8 sequences of
 seeded lengths, the decode with seeded per-sequence cache lengths, and the
-decode step that appends one key per sequence before attending).
+decode step that appends one key per sequence before attending), and the
+backward pass of the causal prefill.
 Inputs are resident in device memory before the timed region starts.
 
 Prints ONE JSON line on stdout. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -340,6 +341,40 @@ def main():
                           "pct_peak": round(100 * app_bytes / t_app.mean() / 1e9 / PEAK_HBM_GBS, 2)},
     }
 
+    # ---- backward of the causal prefill (side measurement): fa_bwd from the
+    # forward's O and LSE above; algorithmic work 10*d flop per visible pair
+    # and head (the five products dS = ..., dV, dP, dQ, dK of the recomputation
+    # scheme, 2.5x the forward's 4*d).
+    bg = up(W.gen_tensor(wp.seed, 3, wp.B, wp.Nq, wp.H, wp.d, 1.0, "bf16"), "bf16")
+    bdq = torch.empty((wp.B, wp.Nq, wp.H, wp.d), dtype=torch.float32, device=dev)
+    bdk = torch.empty((wp.B, wp.Nk, wp.H, wp.d), dtype=torch.float32, device=dev)
+    bdv = torch.empty_like(bdk)
+    bws = torch.empty((fa.fa_bwd_workspace_bytes(wp.B, wp.H, wp.Nq) // 4,), dtype=torch.float32,
+                      device=dev)
+    bwd_flops = 2.5 * prefill_flops
+
+    def backward():
+        check(fa.fa_bwd(pq, pk, pv, po, bg, plse, bdq, bdk, bdv, bws, wp.B, wp.H, wp.Nq, wp.Nk,
+                        wp.d, wp.scale, True, -1, -1, None, 0.0, stream), "fa_bwd")
+
+    prefill()
+    for _ in range(args.warmup):
+        backward()
+    ev3 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for a, e in ev3:
+        a.record(stream)
+        backward()
+        e.record(stream)
+    torch.cuda.synchronize()
+    t_bwd = np.array([a.elapsed_time(e) for a, e in ev3]) * 1e-3
+    assert torch.isfinite(bdq).all() and torch.isfinite(bdk).all() and torch.isfinite(bdv).all()
+    backward_line = {"workload": "gpt_causal_prefill backward (fa_bwd: prep, dK/dV, dQ)",
+                     "gflop": round(bwd_flops / 1e9, 4), "ms": round(t_bwd.mean() * 1e3, 5),
+                     "ms_median": round(float(np.median(t_bwd)) * 1e3, 5),
+                     "tflops": round(bwd_flops / t_bwd.mean() / 1e12, 3),
+                     "pct_peak": round(100 * bwd_flops / t_bwd.mean() / 1e12 / PEAK_BF16_TFLOPS, 2)}
+
     pre_tflops = prefill_flops / t_prefill.mean() / 1e12
     dec_time = (t_split + t_comb).mean()
     dec_gbs = decode_bytes / dec_time / 1e9
@@ -405,6 +440,7 @@ def main():
                               "pct_peak": round(100 * short_tflops / PEAK_BF16_TFLOPS, 2),
                               "num_splits": SS, "gflop": round(split_flops / 1e9, 4)},
         "variable_lengths": variable,
+        "backward": backward_line,
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("prefill"),

@@ -345,7 +345,8 @@ def attention_backward(q, k, v, o, lse, dout, softmax_scale=None, causal=False, 
     dq = torch.empty((B, nq, H, d), dtype=grad_dtype, device=q.device)
     dk = torch.empty((B, nk, H, d), dtype=grad_dtype, device=q.device)
     dv = torch.empty((B, nk, H, d), dtype=grad_dtype, device=q.device)
-    ws = torch.empty((2 * B * H * nq,), dtype=torch.float32, device=q.device)
+    ws = torch.empty((fa_bwd_workspace_bytes(B, H, nq) // 4,), dtype=torch.float32,
+                     device=q.device)
     _check(fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, nq, nk, d, softmax_scale, causal,
                   window_left, window_right, alibi_slopes, softcap, stream), "fa_bwd")
     return dq, dk, dv

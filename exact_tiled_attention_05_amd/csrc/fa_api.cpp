@@ -329,7 +329,8 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, int in_dtype, voi
 
 long long fa_bwd_workspace_bytes(int batch, int heads, int seqlen_q) {
   if (batch <= 0 || heads <= 0 || seqlen_q <= 0) return -1;
-  return 2LL * batch * heads * seqlen_q * (long long)sizeof(float);
+  const long long nblk = (seqlen_q + fa::BWD_RB - 1) / fa::BWD_RB;
+  return 2LL * fa::BWD_RB * nblk * batch * heads * (long long)sizeof(float);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -363,8 +364,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   p.dk = dk;
   p.dv = dv;
   const int64_t rows = (int64_t)batch * heads * seqlen_q;
-  p.dsum = workspace;
-  p.lse2 = workspace + rows;
+  p.rowterms = workspace;
+  p.nblk = (seqlen_q + fa::BWD_RB - 1) / fa::BWD_RB;
   p.alibi = alibi_slopes;
   p.B = batch;
   p.H = heads;

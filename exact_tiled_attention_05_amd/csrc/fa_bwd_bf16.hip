@@ -28,6 +28,8 @@
 // two stages deep, in the forward's swizzled layout.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_lds.h"
 
@@ -54,18 +56,26 @@ __device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O) and LSE2, LPR lanes per row (8 elements each).
+// 1. Row terms: per (b, h) and block of 32 query rows, LSE * log2(e) for the 32
+//    rows (+inf for a row with no key, so its probabilities come out 0, and for
+//    rows past Nq) and then D = rowsum(dO * O) (0 past Nq). LPR lanes per row,
+//    8 elements each; rows run fastest within a (b, h).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
   constexpr int LPR = D / 8;
   constexpr int RPB = kThreads / LPR;
   const int tid = threadIdx.x, c = tid % LPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;  // (b * Nq + i) * H + h
-  const bool ok = row < (int64_t)p.B * p.Nq * p.H;
+  const int nqp = p.nblk * BWD_RB;
+  const int64_t slot = (int64_t)blockIdx.x * RPB + tid / LPR;  // (b * H + h) * nqp + i
+  const bool ok = slot < (int64_t)p.B * p.H * nqp;
+  const int i = (int)(slot % nqp);
+  const int64_t bh = slot / nqp;
+  const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+  const bool live = ok && i < p.Nq;
   float acc = 0.0f;
-  if (ok) {
-    const int64_t e = row * D + 8 * c;
+  if (live) {
+    const int64_t e = (((int64_t)b * p.Nq + i) * p.H + h) * D + 8 * c;
     const u32x4_t g = *(const u32x4_t*)((const uint16_t*)p.dout + e);
     float o[8];
     if (p.o_bf16) {
@@ -90,14 +100,14 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
 #pragma unroll
   for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m);
   if (ok && c == 0) {
-    const int h = (int)(row % p.H);
-    const int64_t bi = row / p.H;
-    const int i = (int)(bi % p.Nq);
-    const int b = (int)(bi / p.Nq);
-    const int64_t idx = ((int64_t)b * p.H + h) * p.Nq + i;
-    p.dsum[idx] = acc;
-    const float l = p.lse[idx];
-    p.lse2[idx] = l == kNegInf ? kInf : l * kLog2e;
+    float l2 = kInf;
+    if (live) {
+      const float l = p.lse[((int64_t)b * p.H + h) * p.Nq + i];
+      l2 = l == kNegInf ? kInf : l * kLog2e;
+    }
+    float* rt = p.rowterms + (bh * p.nblk + i / BWD_RB) * (2 * BWD_RB) + i % BWD_RB;
+    rt[0] = l2;
+    rt[BWD_RB] = acc;
   }
 }
 
@@ -160,18 +170,30 @@ void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NDB = D / 32;              // 32-row blocks of dK^T / dV^T
   constexpr int CPR = D / 8;               // 16-byte chunks per row
   constexpr int RPL = 64 / CPR;            // rows per wavefront-wide copy
-  constexpr int QLOADS = kBQ / RPL / 4;    // copies per wavefront per tensor per step
+  constexpr int QLOADS = kBQ / RPL / 4;    // copies per wavefront per tensor per block
   constexpr int VLOADS = kBK / RPL / 4;    // copies per wavefront for the V tile
-  static_assert(QLOADS >= 1 && VLOADS >= 1, "tile shape");
+  static_assert(QLOADS >= 1 && VLOADS >= 1 && kBQ == BWD_RB, "tile shape");
   constexpr int QT = kBQ * D;
+  // Vector-memory operations per wavefront per block: Q, dO and the row terms.
+  constexpr int kCopies = 2 * QLOADS + 1;
+  constexpr int kSReadAhead = 2;           // k-steps of S / dP operands read ahead
   constexpr int kReadAhead = 4;            // transposed-read MFMAs in flight
 
+  // Q / dO / row-term blocks cycle through four stages: the copy of block t+3
+  // is issued while block t is computed, so three blocks of copies are in flight.
   __shared__ __attribute__((aligned(1024))) uint16_t sV[kBK * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sQ0[QT];
   __shared__ __attribute__((aligned(1024))) uint16_t sQ1[QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ2[QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ3[QT];
   __shared__ __attribute__((aligned(1024))) uint16_t sG0[QT];  // dO
   __shared__ __attribute__((aligned(1024))) uint16_t sG1[QT];
-  __shared__ __attribute__((aligned(16))) float sL0[kBQ], sL1[kBQ], sD0[kBQ], sD1[kBQ];
+  __shared__ __attribute__((aligned(1024))) uint16_t sG2[QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sG3[QT];
+  __shared__ __attribute__((aligned(256))) float sR0[2 * kBQ];  // LSE2 | D
+  __shared__ __attribute__((aligned(256))) float sR1[2 * kBQ];
+  __shared__ __attribute__((aligned(256))) float sR2[2 * kBQ];
+  __shared__ __attribute__((aligned(256))) float sR3[2 * kBQ];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
@@ -246,10 +268,16 @@ void bwd_dkdv_kernel(BwdParams p) {
   const char* qbh = (const char*)p.q + 2 * (((int64_t)b * nq * p.H + h) * D);
   const char* gbh = (const char*)p.dout + 2 * (((int64_t)b * nq * p.H + h) * D);
   const int64_t qend = (int64_t)(nq - 1) * row_bytes + 2 * D;
-  const int64_t rowbase = ((int64_t)b * p.H + h) * nq;
-  auto copy_block = [&](uint16_t* dq_, uint16_t* dg_, int qb) __attribute__((always_inline)) {
+  const float* rbh = p.rowterms + ((int64_t)b * p.H + h) * p.nblk * (2 * kBQ);
+  const int qb_first = (ulo / kBQ) * kBQ;
+  const int nblocks = (uhi - qb_first + kBQ - 1) / kBQ;
+  const int qb_end = qb_first + nblocks * kBQ;
+  // Block starting at row qb into one stage. Every wavefront issues the same
+  // number of operations for every block; blocks past the range read nothing
+  // and write zeros (range-checked descriptors), which keeps the wait counts fixed.
+  auto copy_block = [&](uint16_t* dq_, uint16_t* dg_, float* dr_, int qb) __attribute__((always_inline)) {
     const int64_t tb = (int64_t)qb * row_bytes;
-    const int64_t left = qend - tb;
+    const int64_t left = qb < qb_end ? qend - tb : 0;
     const int n = left <= 0 ? 0 : (left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbh + tb, n);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(gbh + tb, n);
@@ -258,20 +286,10 @@ void bwd_dkdv_kernel(BwdParams p) {
       buffer_load_lds16(rq, dq_ + 512 * (QLOADS * wu + i), lane_off(QLOADS * wu + i));
       buffer_load_lds16(rg, dg_ + 512 * (QLOADS * wu + i), lane_off(QLOADS * wu + i));
     }
-  };
-  // LSE2 and D of a block (rows past Nq: LSE2 = +inf, D = 0), by the first wavefront.
-  auto load_rowterms = [&](int qb, float& lv, float& dv) __attribute__((always_inline)) {
-    const int i = qb + (lane & 31);
-    lv = kInf;
-    dv = 0.0f;
-    if (i < nq) {
-      if (lane < 32) lv = p.lse2[rowbase + i];
-      else dv = p.dsum[rowbase + i];
-    }
-  };
-  auto store_rowterms = [&](float* sl, float* sd, float lv, float dv) __attribute__((always_inline)) {
-    if (lane < 32) sl[lane] = lv;
-    else sd[lane - 32] = dv;
+    // The block's 64 row terms, 4 bytes per lane (every wavefront writes the same values).
+    const __amdgpu_buffer_rsrc_t rr =
+        make_rsrc((const char*)(rbh + (int64_t)(qb / kBQ) * (2 * kBQ)), qb < qb_end ? 8 * kBQ : 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr_t)dr_, 4, 4 * lane, 0, 0, 0);
   };
 
   f32x16_t dkacc[NDB], dvacc[NDB];
@@ -282,24 +300,29 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
   const int gl = lane & 15, sub = (lane >> 4) & 1;
 
-  auto compute = [&](const uint16_t* sq, const uint16_t* sg, const float* sl, const float* sd,
+  auto compute = [&](auto masked_t, const uint16_t* sq, const uint16_t* sg, const float* sr,
                      int qb) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_t)::value;
     // S = Q K^T and dP = dO V^T for 32 queries x this wavefront's 32 keys.
     f32x16_t sacc = f32x16_t{}, pacc = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sq + tile_off<D>(r, 2 * ks + h2)));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sacc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sg + tile_off<D>(r, 2 * ks + h2)));
+      const bf16x8_t aq = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sq + tile_off<D>(r, 2 * ks + h2)));
+      const bf16x8_t ag = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sg + tile_off<D>(r, 2 * ks + h2)));
       const bf16x8_t bv =
           __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sV + tile_off<D>(32 * w + r, 2 * ks + h2)));
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, pacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, bv, pacc, 0, 0, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 3 * kSReadAhead, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < KS - kSReadAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kSReadAhead, 0);
+
     // Slot v holds query qb + 8*(v/4) + 4*h2 + v%4 of this lane's key.
-    const bool masked = !(wave_full && qb >= wflo && qb + kBQ <= wfhi);
     const int lo_rel = rlo - qb - 4 * h2, hi_rel = rhi - qb - 4 * h2;
     const float rel = (float)(key - off - qb - 4 * h2);
     bf16x8_t pb[2], zb[2];
@@ -309,8 +332,8 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
         const int g = 2 * tt + gg;
-        const f32x4_t l4 = *(const f32x4_t*)(sl + 8 * g + 4 * h2);
-        const f32x4_t d4 = *(const f32x4_t*)(sd + 8 * g + 4 * h2);
+        const f32x4_t l4 = *(const f32x4_t*)(sr + 8 * g + 4 * h2);
+        const f32x4_t d4 = *(const f32x4_t*)(sr + kBQ + 8 * g + 4 * h2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = 4 * g + e, kk = 8 * g + e;
@@ -318,9 +341,12 @@ void bwd_dkdv_kernel(BwdParams p) {
           const float x = bwd_score<SOFTCAP, ALIBI>(p, sacc[v], slope_log2,
                                                     __builtin_fabsf(rel - (float)kk), th);
           float pr = fast_exp2(x - l4[e]);
-          if (masked && (kk < lo_rel || kk >= hi_rel)) pr = 0.0f;
           float dz = pr * (pacc[v] - d4[e]);
           if constexpr (SOFTCAP) dz *= 1.0f - th * th;
+          if (MASKED && (kk < lo_rel || kk >= hi_rel)) {
+            pr = 0.0f;
+            dz = 0.0f;
+          }
           pa[4 * gg + e] = pr;
           za[4 * gg + e] = dz;
         }
@@ -351,41 +377,49 @@ void bwd_dkdv_kernel(BwdParams p) {
     // Schedule: the transposed reads of kReadAhead MFMAs first, then one MFMA
     // and the two reads of a later one, alternately (bounds the live operands).
     constexpr int kMf = 4 * NDB;  // MFMAs of the two products
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadAhead, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadAhead, 1);
 #pragma unroll
     for (int i = 0; i < kMf - kReadAhead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 1);
   };
 
-  const int qb_first = (ulo / kBQ) * kBQ;
-  const int nblocks = (uhi - qb_first + kBQ - 1) / kBQ;
-  float lv, dvv;
-  copy_block(sQ0, sG0, qb_first);
-  if (wu == 0) {
-    load_rowterms(qb_first, lv, dvv);
-    store_rowterms(sL0, sD0, lv, dvv);
-  }
-  wait_vmem_barrier<0>();
-  auto step = [&](auto par, int it) __attribute__((always_inline)) {
-    constexpr bool ODD = decltype(par)::value;
+  copy_block(sQ0, sG0, sR0, qb_first);
+  copy_block(sQ1, sG1, sR1, qb_first + kBQ);
+  copy_block(sQ2, sG2, sR2, qb_first + 2 * kBQ);
+  wait_vmem_barrier<2 * kCopies>();  // V and block 0 have landed
+  auto step = [&](auto st, int it) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value;
+    uint16_t* sq = S == 0 ? sQ0 : S == 1 ? sQ1 : S == 2 ? sQ2 : sQ3;
+    uint16_t* sg = S == 0 ? sG0 : S == 1 ? sG1 : S == 2 ? sG2 : sG3;
+    float* sr = S == 0 ? sR0 : S == 1 ? sR1 : S == 2 ? sR2 : sR3;
+    // Stage (S + 3) % 4 held block it - 1, finished before the last barrier.
+    uint16_t* nq_ = S == 0 ? sQ3 : S == 1 ? sQ0 : S == 2 ? sQ1 : sQ2;
+    uint16_t* ng_ = S == 0 ? sG3 : S == 1 ? sG0 : S == 2 ? sG1 : sG2;
+    float* nr_ = S == 0 ? sR3 : S == 1 ? sR0 : S == 2 ? sR1 : sR2;
     const int qb = qb_first + it * kBQ;
-    const bool more = it + 1 < nblocks;
-    if (more) {
-      copy_block(ODD ? sQ0 : sQ1, ODD ? sG0 : sG1, qb + kBQ);
-      if (wu == 0) load_rowterms(qb + kBQ, lv, dvv);
+    copy_block(nq_, ng_, nr_, qb + 3 * kBQ);
+    if (wave_live && qb < whi && qb + kBQ > wlo) {
+      if (wave_full && qb >= wflo && qb + kBQ <= wfhi)
+        compute(std::false_type{}, sq, sg, sr, qb);
+      else
+        compute(std::true_type{}, sq, sg, sr, qb);
     }
-    if (wave_live && qb < whi && qb + kBQ > wlo)
-      compute(ODD ? sQ1 : sQ0, ODD ? sG1 : sG0, ODD ? sL1 : sL0, ODD ? sD1 : sD0, qb);
-    if (more && wu == 0) store_rowterms(ODD ? sL0 : sL1, ODD ? sD0 : sD1, lv, dvv);
-    wait_vmem_barrier<0>();
+    wait_vmem_barrier<2 * kCopies>();  // block it + 1 has landed
   };
-  for (int it = 0; it < nblocks; it += 2) {
-    step(std::false_type{}, it);
-    if (it + 1 < nblocks) step(std::true_type{}, it + 1);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  for (int it = 0; it < nblocks; it += 4) {
+    step(I0{}, it);
+    if (it + 1 < nblocks) step(I1{}, it + 1);
+    if (it + 2 < nblocks) step(I2{}, it + 2);
+    if (it + 3 < nblocks) step(I3{}, it + 3);
   }
+  wait_vmem_barrier<0>();  // no copy may still be writing LDS at exit
 
   // Epilogue: lane = key, slots = head_dim rows 32db + 8g + 4h2 + {0..3}.
   if (key >= k1) return;
@@ -456,9 +490,11 @@ void bwd_dq_kernel(BwdParams p) {
       gf[ks] = __builtin_bit_cast(bf16x8_t, y);
     }
   }
-  const int64_t ri = ((int64_t)b * p.H + h) * nq + min(row, nq - 1);
-  const float lse2 = row < nq ? p.lse2[ri] : kInf;
-  const float drow = row < nq ? p.dsum[ri] : 0.0f;
+  const int rc = min(row, nq - 1);
+  const float* rt = p.rowterms + (((int64_t)b * p.H + h) * p.nblk + rc / BWD_RB) * (2 * BWD_RB) +
+                    rc % BWD_RB;
+  const float lse2 = row < nq ? rt[0] : kInf;
+  const float drow = row < nq ? rt[BWD_RB] : 0.0f;
 
   // Contiguous K/V copies, as in the forward.
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -583,7 +619,7 @@ void bwd_dq_kernel(BwdParams p) {
 template <int D, bool SOFTCAP, bool ALIBI>
 int launch_bwd_bf16(const BwdParams& p, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  const int64_t rows = (int64_t)p.B * p.Nq * p.H;
+  const int64_t rows = (int64_t)p.B * p.H * p.nblk * BWD_RB;
   constexpr int RPB = kThreads / (D / 8);
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads),
                      0, s, p);

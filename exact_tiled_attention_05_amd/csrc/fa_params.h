@@ -59,8 +59,10 @@ struct BwdParams {
   void* dq;                 // [B, Nq, H, D], fp32 or bf16 (g_bf16)
   void* dk;                 // [B, Nk, H, D]
   void* dv;
-  float* dsum;              // [B, H, Nq] workspace: D = rowsum(dO * O)
-  float* lse2;              // [B, H, Nq] workspace: LSE * log2(e), +inf for rows with no key
+  float* rowterms;          // workspace [B, H, nblk, 64]: per block of 32 query rows, LSE*log2(e)
+                            // (32, +inf for a row with no key or past Nq) then D = rowsum(dO*O)
+                            // (32, 0 past Nq)
+  int nblk;                 // ceil(Nq / 32)
   const float* alibi;       // [H] or nullptr
   int B, H, Nq, Nk;
   int window_left, window_right;
@@ -96,8 +98,10 @@ constexpr int BF16_BM = 128;
 // fa_fwd_split chunks are multiples of the key tile width.
 constexpr int SPLIT_ALIGN = 64;
 constexpr int F32_BM = 32;
-// Backward tiles: keys per dK/dV workgroup, query rows per dQ workgroup.
+// Backward tiles: keys per dK/dV workgroup, query rows per dQ workgroup, and
+// the query-row block of the row-term workspace.
 constexpr int BWD_BK = 128;
 constexpr int BWD_BM = 128;
+constexpr int BWD_RB = 32;
 
 }  // namespace fa

@@ -248,8 +248,9 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, int in_dtype,
  *   o              [batch, seqlen_q, heads, head_dim] o_dtype: fa_fwd's output
  *   lse            [batch, heads, seqlen_q] float32: fa_fwd's log-sum-exp
  *   dq / dk, dv    shaped as q / k, v, in grad_dtype (FA_FP32 or FA_BF16)
- *   workspace      2 * batch * heads * seqlen_q floats (fa_bwd_workspace_bytes),
- *                  device memory owned by the caller; overwritten
+ *   workspace      fa_bwd_workspace_bytes(batch, heads, seqlen_q) bytes of device
+ *                  memory owned by the caller (2 floats per query row, rows
+ *                  rounded up to a multiple of 32 per (batch, head)); overwritten
  * P and dZ are rounded to bf16 as matrix-core operands (accumulation in
  * fp32). Masks, scale, ALiBi and softcap must be those of the forward call.
  * Three kernels run in order on `stream`. Errors as fa_fwd; fp32 inputs are

@@ -267,4 +267,5 @@ def test_fa_bwd_rejects(kw, code):
 
 def test_bwd_workspace_bytes():
     assert fa.fa_bwd_workspace_bytes(4, 16, 2048) == 2 * 4 * 16 * 2048 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 2, 33) == 2 * 2 * 64 * 4  # rows padded to 32 per head
     assert fa.fa_bwd_workspace_bytes(0, 1, 1) == -1
