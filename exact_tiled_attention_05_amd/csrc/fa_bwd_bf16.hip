@@ -11,13 +11,14 @@
 //
 //   1. prep:  D_i = dO_i . O_i and the LSE in log2 units (+inf for a row with
 //             no key, so that its probabilities come out 0).
-//   2. dK/dV: one workgroup of 4 wavefronts per (128-key tile, head, batch).
-//             Each wavefront keeps 32 keys in its lanes: K as the B operand of
-//             S = Q K^T in registers, V in LDS for dP = dO V^T, and walks the
-//             32-row query blocks that see its keys:
+//   2. dK/dV: one workgroup per (128-key tile, head, batch), keys in lanes (32
+//             per wavefront): K as the B operand of S = Q K^T in registers, V in
+//             LDS for dP = dO V^T, walking the 32-row query blocks that see the keys:
 //               P = exp2(S' - LSE2), dS = P (dP - D), dZ = dS (1 - tanh^2) with a cap,
 //               dV^T += dO^T P and dK^T += Q^T dZ, the transposed dO and Q read
-//               from LDS with ds_read_b64_tr_b16 (P and dZ stay in registers).
+//               from LDS with ds_read_b64_tr_b16. At head_dim 128 two wavefronts
+//               share each 32-key group (one for S, P, dV; one for dP, dZ, dK),
+//               at head_dim 64 one wavefront does all of it.
 //   3. dQ:    one workgroup per (128-row query tile, head, batch), laid out as
 //             the forward (a query row per lane pair): S^T = K Q^T and
 //             dP^T = V dO^T with Q and dO in registers, dQ^T += K^T dZ^T with K
@@ -43,14 +44,6 @@ constexpr int kBN = 64;        // keys per dQ step
 constexpr int kBK = BWD_BK;    // keys per dK/dV workgroup (32 per wavefront)
 constexpr int kBM = BWD_BM;    // query rows per dQ workgroup (32 per wavefront)
 constexpr float kInf = __builtin_inff();
-
-// Wavefronts per SIMD the dK/dV kernel is register-budgeted for: at head_dim
-// 128 its two 128 x 32 fp32 accumulators, the S and dP tiles and K need more
-// than the 256 registers of two wavefronts, so it runs one per SIMD.
-template <int D>
-struct DkdvWaves {
-  static constexpr int value = D == 128 ? 1 : 2;
-};
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
@@ -149,23 +142,382 @@ __device__ __forceinline__ void store_grad4(void* base, int bf16, int64_t off, f
   }
 }
 
-// Zero rows [r0, r1) of a [B, N, H, D] gradient for (b, h).
+// Zero rows [r0, r1) of a [B, N, H, D] gradient for (b, h), NT threads.
+template <int NT>
 __device__ void zero_rows(void* base, int bf16, int b, int h, int N, int H, int D, int r0, int r1,
                           int tid) {
   const int n = (r1 - r0) * D / 4;
-  for (int idx = tid; idx < n; idx += kThreads) {
+  for (int idx = tid; idx < n; idx += NT) {
     const int row = r0 + idx / (D / 4), c = idx % (D / 4);
     store_grad4(base, bf16, (((int64_t)b * N + row) * H + h) * D + 4 * c, 0.f, 0.f, 0.f, 0.f);
   }
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK and dV
+// 2. dK and dV (head_dim 128)
+//
+// Eight wavefronts: four key groups of 32 keys (the workgroup's 128 keys) times
+// two roles, so that each SIMD runs one wavefront of each role side by side.
+// Role 0 (S, P, dV): S = Q K^T with K in registers, P = exp2(S' - LSE2) under
+// the mask, dV^T += dO^T P; it also publishes P' = P (1 - tanh^2 with a cap, 1
+// without) in fp32 through LDS. Role 1 (dP, dZ, dK): dP = dO V^T with V from
+// LDS, and one block behind, dZ = P' (dP - D) and dK^T += Q^T dZ. The 32-row
+// query blocks (Q, dO, row terms) cycle through four LDS stages with the copy
+// of block t+2 issued in step t, so block t-1 is still resident while role 1
+// finishes it.
+// ---------------------------------------------------------------------------
+constexpr int kDkdvThreads = 512;
+
+template <int D, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int KS = D / 16;               // k-steps over head_dim
+  constexpr int NDB = D / 32;              // 32-row blocks of dK^T / dV^T
+  constexpr int CPR = D / 8;               // 16-byte chunks per row
+  constexpr int RPL = 64 / CPR;            // rows per wavefront-wide copy
+  constexpr int QL = kBQ / RPL / 4;        // copies per wavefront of its role's tensor per block
+  constexpr int VL = kBK / RPL / 8;        // copies per wavefront for the V tile
+  static_assert(QL >= 1 && VL >= 1 && kBQ == BWD_RB, "tile shape");
+  constexpr int QT = kBQ * D;
+  constexpr int kCopies = QL + 1;          // vector-memory ops per wavefront per block
+  constexpr int kSReadAhead = 2;           // k-steps of operands read ahead
+  constexpr int kReadAhead = 4;            // transposed-read MFMAs in flight
+  constexpr int XG = 16 * 64;              // floats of P' per key group
+
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[kBK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ0[QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ1[QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ2[QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ3[QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sG0[QT];  // dO
+  __shared__ __attribute__((aligned(1024))) uint16_t sG1[QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sG2[QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sG3[QT];
+  __shared__ __attribute__((aligned(256))) float sR0[2 * kBQ];  // LSE2 | D
+  __shared__ __attribute__((aligned(256))) float sR1[2 * kBQ];
+  __shared__ __attribute__((aligned(256))) float sR2[2 * kBQ];
+  __shared__ __attribute__((aligned(256))) float sR3[2 * kBQ];
+  __shared__ __attribute__((aligned(1024))) float sX0[4 * XG];  // P' of even blocks
+  __shared__ __attribute__((aligned(1024))) float sX1[4 * XG];  // P' of odd blocks
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
+  const int grp = w & 3;
+  const int role = __builtin_amdgcn_readfirstlane(w >> 2);
+  int L = blockIdx.x;
+  const int h = L % p.H;
+  L /= p.H;
+  const int b = L % p.B;
+  const int kt = L / p.B;  // ascending: under causal the first key tile is seen by the most rows
+  const int nq = p.Nq, nk = p.Nk, off = nk - nq;
+  const int wl = p.window_left, wr = p.window_right;
+  const int k0 = kt * kBK, k1 = min(nk, k0 + kBK);
+
+  // Query rows the workgroup's keys are seen by (union over its keys).
+  int ulo, uhi, tmp;
+  query_range(k0, off, nq, wl, wr, ulo, tmp);
+  query_range(k1 - 1, off, nq, wl, wr, tmp, uhi);
+  uhi = max(uhi, ulo);
+  if (uhi <= ulo) {
+    zero_rows<kDkdvThreads>(p.dk, p.g_bf16, b, h, nk, p.H, D, k0, k1, tid);
+    zero_rows<kDkdvThreads>(p.dv, p.g_bf16, b, h, nk, p.H, D, k0, k1, tid);
+    return;
+  }
+
+  // This group's keys: the union [wlo, whi) and intersection [wflo, wfhi) of
+  // their query ranges; this lane's key and its own range [rlo, rhi).
+  const int kw0 = k0 + 32 * grp, kw1 = min(k1, kw0 + 32);
+  const bool group_live = kw0 < k1;
+  int wlo = 0, whi = 0, wflo = 0, wfhi = 0;
+  if (group_live) {
+    query_range(kw0, off, nq, wl, wr, wlo, wfhi);
+    query_range(kw1 - 1, off, nq, wl, wr, wflo, whi);
+  }
+  const bool group_full = kw1 - kw0 == 32;
+  const int key = kw0 + r;
+  int rlo = 0, rhi = 0;
+  if (key < k1) query_range(key, off, nq, wl, wr, rlo, rhi);
+  auto live = [&](int qb) __attribute__((always_inline)) {
+    return group_live && qb < whi && qb + kBQ > wlo;
+  };
+
+  // HBM -> LDS copies. Copy i of a wavefront with copy slot c fills rows
+  // RPL*(n*c + i) + lane/CPR (n copies per slot), lane L the physical chunk L % CPR.
+  const int64_t row_bytes = 2 * (int64_t)p.H * D;
+  auto lane_off = [&](int ld) __attribute__((always_inline)) {
+    const int trow = RPL * ld + lane / CPR;
+    const int chunk = (lane % CPR) ^ swz<D>(trow);
+    return (unsigned)(trow * row_bytes + 16 * chunk);
+  };
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  {
+    // V tile of the workgroup's keys (rows past Nk arrive as zeros), all eight wavefronts.
+    const char* vb = (const char*)p.v + 2 * ((((int64_t)b * nk + k0) * p.H + h) * D);
+    const int64_t left = (int64_t)(nk - 1 - k0) * row_bytes + 2 * D;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vb, left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
+#pragma unroll
+    for (int i = 0; i < VL; ++i) buffer_load_lds16(rs, sV + 512 * (VL * wu + i), lane_off(VL * wu + i));
+  }
+  // Role 0 copies Q, role 1 copies dO (4 wavefronts each); every wavefront
+  // copies the block's 64 row terms (identical values). Blocks past the range
+  // read nothing and write zeros, which keeps the wait counts fixed.
+  const int cs = __builtin_amdgcn_readfirstlane(grp);
+  const char* tbh = (const char*)(role == 0 ? p.q : p.dout) + 2 * (((int64_t)b * nq * p.H + h) * D);
+  const int64_t qend = (int64_t)(nq - 1) * row_bytes + 2 * D;
+  const float* rbh = p.rowterms + ((int64_t)b * p.H + h) * p.nblk * (2 * kBQ);
+  const int qb_first = (ulo / kBQ) * kBQ;
+  const int nblocks = (uhi - qb_first + kBQ - 1) / kBQ;
+  const int qb_end = qb_first + nblocks * kBQ;
+  auto copy_block = [&](uint16_t* dq_, uint16_t* dg_, float* dr_, int qb) __attribute__((always_inline)) {
+    const int64_t tb = (int64_t)qb * row_bytes;
+    const int64_t left = qb < qb_end ? qend - tb : 0;
+    const int n = left <= 0 ? 0 : (left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(tbh + tb, n);
+    uint16_t* dst = role == 0 ? dq_ : dg_;
+#pragma unroll
+    for (int i = 0; i < QL; ++i) buffer_load_lds16(rt, dst + 512 * (QL * cs + i), lane_off(QL * cs + i));
+    const __amdgpu_buffer_rsrc_t rr =
+        make_rsrc((const char*)(rbh + (int64_t)(qb / kBQ) * (2 * kBQ)), qb < qb_end ? 8 * kBQ : 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr_t)dr_, 4, 4 * lane, 0, 0, 0);
+  };
+
+  const int gl = lane & 15, sub = (lane >> 4) & 1;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  auto stq = [&](auto st) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value;
+    return S == 0 ? sQ0 : S == 1 ? sQ1 : S == 2 ? sQ2 : sQ3;
+  };
+  auto stg = [&](auto st) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value;
+    return S == 0 ? sG0 : S == 1 ? sG1 : S == 2 ? sG2 : sG3;
+  };
+  auto str = [&](auto st) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value;
+    return S == 0 ? sR0 : S == 1 ? sR1 : S == 2 ? sR2 : sR3;
+  };
+  // Issue the copies of block it + 2 into stage (S + 2) % 4 (held block it - 2).
+  auto prefetch = [&](auto st, int it) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value;
+    using N = std::integral_constant<int, (S + 2) % 4>;
+    copy_block(stq(N{}), stg(N{}), str(N{}), qb_first + (it + 2) * kBQ);
+  };
+  // Transposed head_dim x 16-row operand of k-step tt from a 32-row tile.
+  auto tr_operand = [&](const uint16_t* t, int tt, int db) __attribute__((always_inline)) {
+    const int vrow = 16 * tt + 4 * h2 + (gl >> 2);
+    const int col = 32 * db + 16 * sub + 4 * (gl & 3);
+    const s16x4_t lo = ds_read_tr16(t + tile_off<D>(vrow, col >> 3) + (col & 7));
+    const s16x4_t hi = ds_read_tr16(t + tile_off<D>(vrow + 8, col >> 3) + (col & 7));
+    const s16x8_t x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, x);
+  };
+
+  copy_block(sQ0, sG0, sR0, qb_first);
+  copy_block(sQ1, sG1, sR1, qb_first + kBQ);
+  wait_vmem_barrier<kCopies>();  // V and block 0 have landed
+
+  f32x16_t acc[NDB];  // dV^T (role 0) or dK^T (role 1)
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+
+  if (role == 0) {
+    // ---- role 0: S, P, dV
+    float slope_log2 = 0.0f;
+    if constexpr (ALIBI) slope_log2 = p.alibi[h] * kLog2e;
+    bf16x8_t kf[KS];
+    {
+      const uint16_t* kp =
+          (const uint16_t*)p.k + (((int64_t)b * nk + min(key, nk - 1)) * p.H + h) * D + 8 * h2;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t x = *(const u32x4_t*)(kp + 16 * ks);
+        if (key >= k1) x = u32x4_t{0, 0, 0, 0};
+        kf[ks] = __builtin_bit_cast(bf16x8_t, x);
+      }
+    }
+    auto compute = [&](auto masked_t, const uint16_t* sq, const uint16_t* sg, const float* sr,
+                       float* sx, int qb) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked_t)::value;
+      f32x16_t sacc = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t aq =
+            __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sq + tile_off<D>(r, 2 * ks + h2)));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], sacc, 0, 0, 0);
+      }
+      // Slot v holds query qb + 8*(v/4) + 4*h2 + v%4 of this lane's key.
+      const int lo_rel = rlo - qb - 4 * h2, hi_rel = rhi - qb - 4 * h2;
+      const float rel = (float)(key - off - qb - 4 * h2);
+      bf16x8_t pb[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x8_t pa;
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const int g = 2 * tt + gg;
+          const f32x4_t l4 = *(const f32x4_t*)(sr + 8 * g + 4 * h2);
+          f32x4_t px;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * g + e, kk = 8 * g + e;
+            float th;
+            const float x = bwd_score<SOFTCAP, ALIBI>(p, sacc[v], slope_log2,
+                                                      __builtin_fabsf(rel - (float)kk), th);
+            float pr = fast_exp2(x - l4[e]);
+            if (MASKED && (kk < lo_rel || kk >= hi_rel)) pr = 0.0f;
+            pa[4 * gg + e] = pr;
+            px[e] = SOFTCAP ? pr * (1.0f - th * th) : pr;
+          }
+          *(f32x4_t*)(sx + 4 * (g * 64 + lane)) = px;
+        }
+        pb[tt] = __builtin_convertvector(pa, bf16x8_t);
+      }
+      // dV^T += dO^T P: k-step tt covers the block's queries 16tt + 4h2 + {0..3, 8..11}.
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(sg, tt, db), pb[tt], acc[db], 0,
+                                                            0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadAhead, 1);
+#pragma unroll
+      for (int i = 0; i < 2 * NDB - kReadAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 1);
+    };
+    auto step = [&](auto st, int it) __attribute__((always_inline)) {
+      const int qb = qb_first + it * kBQ;
+      prefetch(st, it);
+      if (live(qb)) {
+        float* sx = (it & 1) ? sX1 : sX0;
+        sx += grp * XG;
+        if (group_full && qb >= wflo && qb + kBQ <= wfhi)
+          compute(std::false_type{}, stq(st), stg(st), str(st), sx, qb);
+        else
+          compute(std::true_type{}, stq(st), stg(st), str(st), sx, qb);
+      }
+      wait_vmem_barrier<kCopies>();  // block it + 1 has landed; P' of block it is visible
+    };
+    for (int it = 0; it < nblocks; it += 4) {
+      step(I0{}, it);
+      if (it + 1 < nblocks) step(I1{}, it + 1);
+      if (it + 2 < nblocks) step(I2{}, it + 2);
+      if (it + 3 < nblocks) step(I3{}, it + 3);
+    }
+  } else {
+    // ---- role 1: dP, then dZ and dK one block behind
+    f32x16_t pprev = f32x16_t{};
+    auto dp_block = [&](const uint16_t* sg) __attribute__((always_inline)) {
+      f32x16_t pacc = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t ag =
+            __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sg + tile_off<D>(r, 2 * ks + h2)));
+        const bf16x8_t bv =
+            __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sV + tile_off<D>(32 * grp + r, 2 * ks + h2)));
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, bv, pacc, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kSReadAhead, 2);
+#pragma unroll
+      for (int i = 0; i < KS - kSReadAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kSReadAhead, 2);
+      return pacc;
+    };
+    // dZ = P' (dP - D) of a finished block and dK^T += Q^T dZ.
+    auto dk_block = [&](const uint16_t* sq, const float* sr, const float* sx,
+                        const f32x16_t& pacc) __attribute__((always_inline)) {
+      bf16x8_t zb[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x8_t za;
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const int g = 2 * tt + gg;
+          const f32x4_t d4 = *(const f32x4_t*)(sr + kBQ + 8 * g + 4 * h2);
+          const f32x4_t px = *(const f32x4_t*)(sx + 4 * (g * 64 + lane));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) za[4 * gg + e] = px[e] * (pacc[4 * g + e] - d4[e]);
+        }
+        zb[tt] = __builtin_convertvector(za, bf16x8_t);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(sq, tt, db), zb[tt], acc[db], 0,
+                                                            0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadAhead, 3);
+#pragma unroll
+      for (int i = 0; i < 2 * NDB - kReadAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 3);
+    };
+    auto step = [&](auto st, int it) __attribute__((always_inline)) {
+      constexpr int S = decltype(st)::value;
+      using P1 = std::integral_constant<int, (S + 3) % 4>;  // stage of block it - 1
+      const int qb = qb_first + it * kBQ;
+      prefetch(st, it);
+      f32x16_t pcur = f32x16_t{};
+      if (live(qb)) pcur = dp_block(stg(st));
+      if (it > 0 && live(qb - kBQ)) {
+        const float* sx = ((it - 1) & 1) ? sX1 : sX0;
+        dk_block(stq(P1{}), str(P1{}), sx + grp * XG, pprev);
+      }
+      pprev = pcur;
+      wait_vmem_barrier<kCopies>();
+    };
+    for (int it = 0; it < nblocks; it += 4) {
+      step(I0{}, it);
+      if (it + 1 < nblocks) step(I1{}, it + 1);
+      if (it + 2 < nblocks) step(I2{}, it + 2);
+      if (it + 3 < nblocks) step(I3{}, it + 3);
+    }
+    // The last block: its stage, row terms and P' are still resident.
+    const int last = nblocks - 1;
+    if (live(qb_first + last * kBQ)) {
+      const int sl = last & 3;
+      const uint16_t* sq = sl == 0 ? sQ0 : sl == 1 ? sQ1 : sl == 2 ? sQ2 : sQ3;
+      const float* sr = sl == 0 ? sR0 : sl == 1 ? sR1 : sl == 2 ? sR2 : sR3;
+      const float* sx = (last & 1) ? sX1 : sX0;
+      dk_block(sq, sr, sx + grp * XG, pprev);
+    }
+  }
+  wait_vmem_barrier<0>();  // no copy may still be writing LDS at exit
+
+  // Epilogue: lane = key, slots = head_dim rows 32db + 8g + 4h2 + {0..3}.
+  if (key >= k1) return;
+  const int64_t base = (((int64_t)b * nk + key) * p.H + h) * D;
+  void* dst = role == 0 ? p.dv : p.dk;
+  const float sc = role == 0 ? 1.0f : p.scale;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      store_grad4(dst, p.g_bf16, base + 32 * db + 8 * g + 4 * h2, acc[db][4 * g] * sc,
+                  acc[db][4 * g + 1] * sc, acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc);
+}
+
+// ---------------------------------------------------------------------------
+// 2b. dK and dV with four wavefronts (head_dim 64)
+//
+// Each wavefront owns 32 keys and does both roles of the kernel above for them:
+// S, dP, dV and dK per 32-row block, with the Q / dO / row-term blocks in a
+// four-stage ring prefetched three blocks ahead. At head_dim 64 it needs no
+// P' exchange, so its 50 KiB of LDS let two workgroups share a CU, which the
+// split kernel's larger footprint does not.
 // ---------------------------------------------------------------------------
 template <int D, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(DkdvWaves<D>::value, DkdvWaves<D>::value)))
-void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_w4_kernel(BwdParams p) {
   constexpr int KS = D / 16;               // k-steps over head_dim
   constexpr int NDB = D / 32;              // 32-row blocks of dK^T / dV^T
   constexpr int CPR = D / 8;               // 16-byte chunks per row
@@ -212,8 +564,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   query_range(k1 - 1, off, nq, wl, wr, tmp, uhi);
   uhi = max(uhi, ulo);
   if (uhi <= ulo) {
-    zero_rows(p.dk, p.g_bf16, b, h, nk, p.H, D, k0, k1, tid);
-    zero_rows(p.dv, p.g_bf16, b, h, nk, p.H, D, k0, k1, tid);
+    zero_rows<kThreads>(p.dk, p.g_bf16, b, h, nk, p.H, D, k0, k1, tid);
+    zero_rows<kThreads>(p.dv, p.g_bf16, b, h, nk, p.H, D, k0, k1, tid);
     return;
   }
 
@@ -465,7 +817,7 @@ void bwd_dq_kernel(BwdParams p) {
   const int q0 = qt * kBM, q1 = min(nq, q0 + kBM);
   const KeyBounds wg = key_bounds(q0, q1, off, 0, nk, p.window_left, p.window_right);
   if (wg.hi <= wg.lo) {
-    zero_rows(p.dq, p.g_bf16, b, h, nq, p.H, D, q0, q1, tid);
+    zero_rows<kThreads>(p.dq, p.g_bf16, b, h, nq, p.H, D, q0, q1, tid);
     return;
   }
   const int wq0 = q0 + 32 * w, wq1 = min(nq, wq0 + 32);
@@ -625,8 +977,11 @@ int launch_bwd_bf16(const BwdParams& p, void* stream) {
                      0, s, p);
   int rc = (int)hipGetLastError();
   if (rc) return rc;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, SOFTCAP, ALIBI>),
-                     dim3((unsigned)((int64_t)p.num_k_tiles * p.H * p.B)), dim3(kThreads), 0, s, p);
+  const dim3 kgrid((unsigned)((int64_t)p.num_k_tiles * p.H * p.B));
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, SOFTCAP, ALIBI>), kgrid, dim3(kDkdvThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_w4_kernel<D, SOFTCAP, ALIBI>), kgrid, dim3(kThreads), 0, s, p);
   rc = (int)hipGetLastError();
   if (rc) return rc;
   hipLaunchKernelGGL((bwd_dq_kernel<D, SOFTCAP, ALIBI>),
