@@ -49,6 +49,14 @@ used): LSE is the natural log of the row's sum of exp over allowed keys; a row
 with no allowed key has O = 0 and LSE = -inf; split chunk length is
 ceil(Nk / S) rounded up to a whole number of pages.
 
+FP8 inputs ("IO感知技术革命: FlashAttention如何重塑大模型训练的经济学", the
+section on FlashAttention-3 and H100 FP8; the deep-analysis page's roadmap):
+the pages give no quantisation scheme. Reading taken here: Q, K, V arrive as
+E4M3 codes with one descale factor per tensor, and the method computes exact
+attention of the dequantised values, so the oracle is attention_ref on those
+values; prob_weighted_abs_ref gives the bound that rounding the probabilities
+to E4M3 inside the kernel may move O by.
+
 All arithmetic is float64 on the exact input values.
 """
 from __future__ import annotations
@@ -188,6 +196,34 @@ def attention_ref(q, k, v, scale, causal=False, window_left=-1, window_right=-1,
         o[b, :, h, :] = ob
         lse[b, h, :] = lb
     return o, lse
+
+
+def prob_weighted_abs_ref(q, k, v, scale, causal=False, window_left=-1, window_right=-1,
+                          alibi_slopes=None, softcap=0.0, bh=None):
+    """sum_j P_ij |v_j| per row and column, shaped like attention_ref's O.
+
+    A relative change of at most r in every probability (before the row is
+    normalised by the unchanged sum) moves O_i by at most r times this; it is
+    the bound used where probabilities are rounded to a short format.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, nq, H, _ = q.shape
+    pairs = [(b, h) for b in range(B) for h in range(H)] if bh is None else bh
+    out = np.full((B, nq, H, v.shape[3]), np.nan)
+    rows = np.arange(nq)
+    for b, h in pairs:
+        slope = None if alibi_slopes is None else float(alibi_slopes[h])
+        if k.shape[1] == 0:
+            out[b, :, h] = 0.0
+            continue
+        for rc in _row_chunks(rows, k.shape[1]):
+            s = scores_ref(q[b, rc, h], k[b, :, h], rc, nq, scale, causal, window_left,
+                           window_right, slope, softcap)
+            p, _, _ = softmax_rows(s)
+            out[b, rc, h] = p @ np.abs(v[b, :, h])
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -707,3 +707,40 @@ def test_t26_backward_row_term_is_do_dot_o():
     o, _ = O.attention_ref(q, k, v, 0.5, True, -1, -1, np.array([0.1, 0.2]), 3.0)
     _, _, _, D = O.attention_bwd_ref(q, k, v, g, 0.5, True, -1, -1, np.array([0.1, 0.2]), 3.0)
     np.testing.assert_allclose(D, np.einsum("bihd,bihd->bhi", g, o), atol=1e-12)
+
+
+# T27-T29: fp8 inputs ----------------------------------------------------------------
+def test_t27_e4m3_decode_closed_form_and_torch():
+    """E4M3 (1 sign, 4 exponent bits biased by 7, 3 mantissa bits, no infinities)."""
+    dec = W.e4m3_bits_to_f32(np.arange(256, dtype=np.uint8)).astype(np.float64)
+    assert dec[0x38] == 1.0 and dec[0x7E] == 448.0 and dec[0x01] == 2.0 ** -9
+    assert dec[0x08] == 2.0 ** -6 and dec[0x07] == 7 * 2.0 ** -9 and dec[0x40] == 2.0
+    assert dec[0x80] == 0.0 and math.copysign(1.0, dec[0x80]) == -1.0
+    assert np.isnan(dec[0x7F]) and np.isnan(dec[0xFF]) and np.isfinite(dec[:0x7F]).all()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    same = (dec == ref) | (np.isnan(dec) & np.isnan(ref))
+    assert same.all()
+
+
+def test_t28_e4m3_encode_is_round_to_nearest_even():
+    x = np.random.default_rng(73).standard_normal(20000) * 30.0
+    x = np.concatenate([x, [1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 448.0, -447.0, 0.0]])
+    got = W.f32_to_e4m3_bits(x)
+    want = torch.tensor(x, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+    assert W.f32_to_e4m3_bits(np.array([500.0, -1e6]))[0] == 0x7E          # saturates
+    assert W.f32_to_e4m3_bits(np.array([-1e6]))[0] == 0xFE
+
+
+def test_t29_probability_weighted_bound():
+    """P|V| equals O when V >= 0 and bounds |O| otherwise; it is 0 for rows with no key."""
+    B, nq, nk, H, d = 1, 5, 7, 2, 3
+    q, k, v = rnd(74, B, nq, H, d), rnd(75, B, nk, H, d), rnd(76, B, nk, H, d)
+    o, _ = O.attention_ref(q, k, np.abs(v), 0.6, True)
+    np.testing.assert_allclose(O.prob_weighted_abs_ref(q, k, v, 0.6, True), o, atol=1e-14)
+    o2, _ = O.attention_ref(q, k, v, 0.6, True, 2, 0, np.array([0.3, 0.1]), 2.0)
+    bnd = O.prob_weighted_abs_ref(q, k, v, 0.6, True, 2, 0, np.array([0.3, 0.1]), 2.0)
+    assert np.all(bnd >= np.abs(o2) - 1e-14)
+    q3, k3, v3 = rnd(77, 1, 6, 1, 2), rnd(78, 1, 2, 1, 2), rnd(79, 1, 2, 1, 2)
+    b3 = O.prob_weighted_abs_ref(q3, k3, v3, 1.0, True)                 # Nq > Nk: empty rows
+    assert np.all(b3[0, :4] == 0.0)

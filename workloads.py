@@ -43,10 +43,50 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def to_float(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Storage array (float32, or uint16 bf16 bits) -> float64 values, exactly."""
+    """Storage array (float32, uint16 bf16 bits or uint8 E4M3 codes) -> float64 values, exactly."""
     if dtype == "bf16":
         return bf16_bits_to_f32(x).astype(np.float64)
+    if dtype == "fp8":
+        return e4m3_bits_to_f32(x).astype(np.float64)
     return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# fp8 E4M3 bit helpers (storage format only; OCP "E4M3FN": 1 sign bit, 4
+# exponent bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN,
+# largest finite 448, smallest subnormal 2^-9)
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact values of E4M3 codes (uint8) as float32; NaN codes give NaN."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7))
+    mag = np.where((e == 15) & ((b & 7) == 7), np.nan, mag)
+    return (sign * mag).astype(np.float32)
+
+
+_E4M3_POS = None
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite float32 values to E4M3 (nearest, ties to the even code),
+    saturating at +-448; returns uint8 codes."""
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        _E4M3_POS = e4m3_bits_to_f32(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)  # 0 .. 448
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS, a, side="left").clip(0, len(_E4M3_POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(x < 0, code | 0x80, code).astype(np.uint8)
 
 
 # --------------------------------------------------------------------------
@@ -66,13 +106,15 @@ def gen_slice(seed: int, tensor_id: int, b: int, h: int, n: int, d: int,
         return f32_to_bf16_bits(x)
     if dtype == "fp32":
         return x
+    if dtype == "fp8":
+        return f32_to_e4m3_bits(x)
     raise ValueError(dtype)
 
 
 def gen_tensor(seed: int, tensor_id: int, B: int, N: int, H: int, d: int,
                amp: float, dtype: str) -> np.ndarray:
     """A [B, N, H, d] tensor assembled from its per-(b, h) slices."""
-    out = np.empty((B, N, H, d), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    out = np.empty((B, N, H, d), dtype={"bf16": np.uint16, "fp8": np.uint8}.get(dtype, np.float32))
     for b in range(B):
         for h in range(H):
             out[b, :, h, :] = gen_slice(seed, tensor_id, b, h, N, d, amp, dtype)
