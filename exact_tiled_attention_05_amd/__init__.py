@@ -2,11 +2,11 @@
 
 The functions named like the C ABI (``fa_fwd``, ``fa_fwd_split``,
 ``fa_fwd_splitkv``, ``fa_fwd_splitkv_seqlens``, ``fa_fwd_splitkv_append``, ``fa_fwd_varlen``,
-``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_splitkv_combine``, ``fa_status_string``,
+``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_splitkv_combine``, ``fa_status_string``,
 ``fa_split_chunk_len``) only
 marshal arguments: torch tensors become device pointers, the current torch
 stream becomes the HIP stream, and every step of the computation runs in the
-library's kernels. ``attention``, ``attention_varlen``, ``attention_split``,
+library's kernels. ``attention``, ``attention_fp8``, ``attention_varlen``, ``attention_split``,
 ``attention_paged_splitkv``, ``attention_paged_append``, ``attention_backward``,
 ``combine`` and ``decode_paged`` add output allocation (torch.empty) on top of them.
 
@@ -24,9 +24,9 @@ import torch
 __all__ = [
     "FA_FP32", "FA_BF16", "FaError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
-    "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_bytes",
+    "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes",
     "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len",
-    "attention", "attention_varlen", "attention_split", "attention_split_partials",
+    "attention", "attention_fp8", "attention_varlen", "attention_split", "attention_split_partials",
     "attention_paged_splitkv", "attention_paged_append", "attention_backward", "combine",
     "decode_paged",
 ]
@@ -37,7 +37,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 _lib = None
 
 EXPORTED = ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
-            "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_bytes", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len")
+            "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd",
+            "fa_bwd_workspace_bytes", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len")
 
 
 class FaError(RuntimeError):
@@ -73,6 +74,8 @@ def load_library():
     lib.fa_fwd_splitkv_append.argtypes = [vp, vp, vp, vp, vp, i, vp, i, i, vp, vp, vp, i, i, i,
                                           i, i, i, f, i, i, i, vp, f, vp]
     lib.fa_fwd_splitkv_append.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, i, vp, i, i, i, i, i, f, i, i, i, vp, f, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, i, vp, i, i, i, i, i, f, i,
                            i, i, vp, f, vp]
     lib.fa_bwd.restype = i
@@ -188,6 +191,23 @@ def fa_fwd_splitkv_append(q, k_new, v_new, k_cache, v_cache, block_table, max_pa
         _stream(stream))
 
 
+def _ptr_fp8(t):
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("fp8 inputs must be uint8 codes or torch.float8_e4m3fn")
+    return _ptr(t)
+
+
+def fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, batch, heads, seqlen_q,
+               seqlen_k, head_dim, softmax_scale, causal=False, window_left=-1, window_right=-1,
+               alibi_slopes=None, softcap=0.0, stream=None) -> int:
+    """Call fa_fwd_fp8 on caller-allocated tensors (q, k, v: E4M3 codes); returns the status."""
+    return load_library().fa_fwd_fp8(
+        _ptr_fp8(q), _ptr_fp8(k), _ptr_fp8(v), float(q_descale), float(k_descale),
+        float(v_descale), _ptr(o), _dtype_code(o), _ptr(lse), int(batch), int(heads),
+        int(seqlen_q), int(seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)),
+        int(window_left), int(window_right), _ptr(alibi_slopes), float(softcap), _stream(stream))
+
+
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, batch, heads, seqlen_q, seqlen_k,
            head_dim, softmax_scale, causal=False, window_left=-1, window_right=-1,
            alibi_slopes=None, softcap=0.0, stream=None) -> int:
@@ -259,6 +279,25 @@ def attention(q, k, v, softmax_scale=None, causal=False, window_left=-1, window_
     lse = torch.empty((B, H, nq), dtype=torch.float32, device=q.device)
     _check(fa_fwd(q, k, v, o, lse, B, H, nq, nk, d, softmax_scale, causal, window_left,
                   window_right, alibi_slopes, softcap, stream), "fa_fwd")
+    return o, lse
+
+
+def attention_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, softmax_scale=None,
+                  causal=False, window_left=-1, window_right=-1, alibi_slopes=None, softcap=0.0,
+                  out_dtype=torch.float32, stream=None):
+    """O [B, Nq, H, d] and LSE [B, H, Nq] for E4M3 q [B,Nq,H,d], k/v [B,Nk,H,d] (uint8 codes
+    or float8_e4m3fn) with per-tensor descale factors."""
+    B, nq, H, d = q.shape
+    nk = k.shape[1]
+    if tuple(k.shape) != (B, nk, H, d) or tuple(v.shape) != (B, nk, H, d):
+        raise ValueError("k and v must be [B, Nk, H, d] matching q")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, nq, H, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, H, nq), dtype=torch.float32, device=q.device)
+    _check(fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, B, H, nq, nk, d,
+                      softmax_scale, causal, window_left, window_right, alibi_slopes, softcap,
+                      stream), "fa_fwd_fp8")
     return o, lse
 
 

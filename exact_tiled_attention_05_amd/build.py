@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode_bf16.hip", "fa_combine.hip",
-               "fa_bwd_bf16.hip"]
+               "fa_bwd_bf16.hip", "fa_fwd_fp8.hip"]
 CPP_SOURCES = ["fa_api.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -327,6 +327,44 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, int in_dtype, voi
   return fn(p, stream) ? FA_ERR_HIP : FA_OK;
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, float k_descale,
+               float v_descale, void* o, int o_dtype, float* lse, int batch, int heads,
+               int seqlen_q, int seqlen_k, int head_dim, float softmax_scale, int causal,
+               int window_left, int window_right, const float* alibi_slopes, float softcap,
+               void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
+  if (st) return st;
+  if (head_dim != 128) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != FA_FP32 && o_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
+    return st;
+  for (float d : {q_descale, k_descale, v_descale})
+    if (!(d > 0.0f) || !isfinite(d)) return FA_ERR_VALUE;
+  const float qk = softmax_scale * q_descale * k_descale;
+  if (!(qk > 0.0f) || !isfinite(qk)) return FA_ERR_VALUE;
+
+  fa::FwdParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.o_bf16 = o_dtype == FA_BF16;
+  p.num_splits = 1;
+  p.v_descale = v_descale;
+  // The descales of Q and K scale every score, so they join softmax_scale.
+  fill_common(p, batch, heads, seqlen_q, seqlen_k, qk, causal, window_left, window_right,
+              alibi_slopes, softcap, fa::FP8_BM);
+  if ((int64_t)p.num_q_tiles * heads * batch > kMaxGroups) return FA_ERR_SHAPE;
+  const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
+  const int rc = sc && al ? fa::launch_fwd_fp8<true, true>(p, stream)
+                 : sc     ? fa::launch_fwd_fp8<true, false>(p, stream)
+                 : al     ? fa::launch_fwd_fp8<false, true>(p, stream)
+                          : fa::launch_fwd_fp8<false, false>(p, stream);
+  return rc ? FA_ERR_HIP : FA_OK;
+}
+
 long long fa_bwd_workspace_bytes(int batch, int heads, int seqlen_q) {
   if (batch <= 0 || heads <= 0 || seqlen_q <= 0) return -1;
   const long long nblk = (seqlen_q + fa::BWD_RB - 1) / fa::BWD_RB;

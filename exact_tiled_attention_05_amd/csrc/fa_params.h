@@ -37,6 +37,7 @@ struct FwdParams {
   float scale_log2;         // softmax_scale * log2(e)
   float softcap_log2;       // softcap * log2(e) (softcap launches)
   float scale_over_cap2;    // 2 * softmax_scale / softcap * log2(e)  (tanh via exp2)
+  float v_descale;          // fp8 launches: the value of V's code 1.0
 };
 
 struct CombineParams {
@@ -86,6 +87,8 @@ template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 int launch_fwd_bf16(const FwdParams& p, void* stream);
 template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
 int launch_fwd_f32(const FwdParams& p, void* stream);
+template <bool SOFTCAP, bool ALIBI>
+int launch_fwd_fp8(const FwdParams& p, void* stream);  // head_dim 128
 template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream);
 template <int D>
@@ -98,6 +101,7 @@ constexpr int BF16_BM = 128;
 // fa_fwd_split chunks are multiples of the key tile width.
 constexpr int SPLIT_ALIGN = 64;
 constexpr int F32_BM = 32;
+constexpr int FP8_BM = 128;
 // Backward tiles: keys per dK/dV workgroup, query rows per dQ workgroup, and
 // the query-row block of the row-term workspace.
 constexpr int BWD_BK = 128;

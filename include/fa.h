@@ -230,6 +230,31 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, int in_dtype,
                   const float* alibi_slopes, float softcap, void* stream);
 
 /*
+ * fa_fwd_fp8 - fa_fwd for FP8 inputs (FlashAttention-3's FP8 forward: the
+ * section on H100 and FP8 of "IO感知技术革命: FlashAttention如何重塑大模型训练的
+ * 经济学"; FP8 forward support on the roadmap of "FlashAttention深度解析：从算法
+ * 创新到产业变革的全面影响").
+ *
+ *   q, k, v   [batch, seqlen, heads, 128] E4M3 codes (OCP "E4M3FN": bias 7,
+ *             no infinities, largest 448), one byte per element
+ *   q_descale, k_descale, v_descale  per-tensor factors: element x stands for
+ *             descale * e4m3(x); finite and > 0 (FA_ERR_VALUE otherwise)
+ * Computes exactly what fa_fwd computes for the dequantised Q, K, V (same
+ * masks, ALiBi, softcap, LSE and empty-row rules; o and lse as in fa_fwd).
+ * Both products run on FP8 matrix instructions with fp32 accumulation. The
+ * probabilities are scaled so that a row's largest is 2^8 and rounded to E4M3
+ * (nearest even) for the output product, so O can differ from the exact
+ * result by up to 2^-4 * sum_j P_ij |v_j| (plus fp32 rounding); O and LSE are
+ * normalised by the unrounded row sum. head_dim 128 only (FA_ERR_UNSUPPORTED
+ * otherwise).
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, float k_descale,
+               float v_descale, void* o, int o_dtype, float* lse, int batch, int heads,
+               int seqlen_q, int seqlen_k, int head_dim, float softmax_scale, int causal,
+               int window_left, int window_right, const float* alibi_slopes, float softcap,
+               void* stream);
+
+/*
  * fa_bwd - backward pass of fa_fwd: dQ, dK, dV from dO, with the attention
  * probabilities recomputed from the forward's LSE (no Nq x Nk matrix is
  * stored; "IO感知技术革命: FlashAttention如何重塑大模型训练的经济学", tiling and

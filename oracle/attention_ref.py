@@ -199,12 +199,14 @@ def attention_ref(q, k, v, scale, causal=False, window_left=-1, window_right=-1,
 
 
 def prob_weighted_abs_ref(q, k, v, scale, causal=False, window_left=-1, window_right=-1,
-                          alibi_slopes=None, softcap=0.0, bh=None):
-    """sum_j P_ij |v_j| per row and column, shaped like attention_ref's O.
+                          alibi_slopes=None, softcap=0.0, bh=None, weight=None):
+    """sum_j w(P_ij) |v_j| per row and column, shaped like attention_ref's O
+    (w = identity unless `weight` is given, a function applied to P elementwise).
 
-    A relative change of at most r in every probability (before the row is
-    normalised by the unchanged sum) moves O_i by at most r times this; it is
-    the bound used where probabilities are rounded to a short format.
+    If every probability moves by at most w(P) (before the row is normalised by
+    the unchanged sum), O_i moves by at most this; it is the bound used where
+    probabilities are rounded to a short format (w(P) = r P for a relative
+    error r, or half the format's spacing at P).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -222,7 +224,8 @@ def prob_weighted_abs_ref(q, k, v, scale, causal=False, window_left=-1, window_r
             s = scores_ref(q[b, rc, h], k[b, :, h], rc, nq, scale, causal, window_left,
                            window_right, slope, softcap)
             p, _, _ = softmax_rows(s)
-            out[b, rc, h] = p @ np.abs(v[b, :, h])
+            wp = p if weight is None else np.where(p > 0, weight(p), 0.0)
+            out[b, rc, h] = wp @ np.abs(v[b, :, h])
     return out
 
 

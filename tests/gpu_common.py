@@ -53,3 +53,12 @@ def qkv_case(seed, B, nq, nk, H, d, dtype, amp=1.0):
     k = W.gen_tensor(seed, W.TENSOR_K, B, nk, H, d, amp, dtype)
     v = W.gen_tensor(seed, W.TENSOR_V, B, nk, H, d, amp, dtype)
     return q, k, v
+
+
+def e4m3_half_spacing(x):
+    """Half the gap between neighbouring E4M3 values around x >= 0 (the largest
+    error of rounding x to nearest): 2^(e - 4) for normal x in [2^e, 2^(e+1)),
+    2^-10 below 2^-6 (subnormals, spacing 2^-9)."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -6)))
+    return np.where(x < 2.0 ** -6, 2.0 ** -10, np.exp2(e - 4))

@@ -269,3 +269,25 @@ def test_bwd_workspace_bytes():
     assert fa.fa_bwd_workspace_bytes(4, 16, 2048) == 2 * 4 * 16 * 2048 * 4
     assert fa.fa_bwd_workspace_bytes(1, 2, 33) == 2 * 2 * 64 * 4  # rows padded to 32 per head
     assert fa.fa_bwd_workspace_bytes(0, 1, 1) == -1
+
+
+def fp8(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, qd=1.0, kd=1.0, vd=1.0, o=FAKE, o_dtype=0, lse=None, batch=1,
+             heads=1, seqlen_q=4, seqlen_k=4, head_dim=128, scale=0.125, causal=0, wl=-1, wr=-1,
+             alibi=None, softcap=0.0, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_fwd_fp8(
+        a["q"], a["k"], a["v"], a["qd"], a["kd"], a["vd"], a["o"], a["o_dtype"], a["lse"],
+        a["batch"], a["heads"], a["seqlen_q"], a["seqlen_k"], a["head_dim"], a["scale"],
+        a["causal"], a["wl"], a["wr"], a["alibi"], a["softcap"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL),
+    (dict(batch=0), SHAPE), (dict(seqlen_k=0), SHAPE), (dict(head_dim=64), UNSUP),
+    (dict(o_dtype=3), UNSUP), (dict(causal=1, wr=2), MASK), (dict(qd=0.0), VALUE),
+    (dict(kd=-1.0), VALUE), (dict(vd=math.inf), VALUE), (dict(qd=math.nan), VALUE),
+    (dict(qd=1e30, kd=1e30), VALUE), (dict(scale=0.0), VALUE),
+])
+def test_fa_fwd_fp8_rejects(kw, code):
+    assert fp8(**kw) == code

@@ -13,7 +13,7 @@ import torch
 import exact_tiled_attention_05_amd as fa
 import oracle as O
 import workloads as W
-from gpu_common import check, qkv_case, say, to_dev
+from gpu_common import TOL_LSE, check, qkv_case, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -670,3 +670,102 @@ def test_bwd_causal_prefill_full_size():
             rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
             say(f"  b{b} h{h} {name}: relative error {rel:.2e}")
             assert rel <= 1e-2, (b, h, name, rel)
+
+
+# --------------------------------------------------------------------------
+# FP8 forward (fa_fwd_fp8)
+# --------------------------------------------------------------------------
+# Tolerance from the arithmetic: the kernel rounds 2^8 P to E4M3 (nearest; the
+# error is at most half the format's spacing there) for the output product and
+# normalises by the unrounded row sum, so O_i moves by at most
+# sum_j halfspacing(2^8 P_ij) / 2^8 |v_j| (the oracle's weighted bound). The test
+# allows twice that (fp32 rounding of P can move a value across a tie), plus
+# 1e-5 of max|O| for the fp32 products; LSE (from the unrounded sum) within 1e-3.
+FP8_CASES = [
+    # (B, H, nq, nk, causal, wl, wr, alibi, cap, q_ds, k_ds, v_ds)
+    (1, 2, 128, 128, True, -1, -1, False, 0.0, 1.0, 1.0, 1.0),
+    (2, 2, 200, 333, True, -1, -1, False, 0.0, 0.5, 0.25, 2.0),
+    (1, 3, 300, 90, True, -1, -1, False, 0.0, 1.0, 1.0, 1.0),      # Nq > Nk: rows with no key
+    (1, 2, 257, 257, False, -1, -1, True, 0.0, 0.125, 1.0, 0.5),
+    (2, 2, 150, 400, True, 50, 0, False, 10.0, 1.0, 0.5, 1.0),
+    (1, 2, 100, 300, False, 40, 20, True, 20.0, 2.0, 0.5, 4.0),
+    (1, 4, 1, 1000, True, -1, -1, False, 0.0, 1.0, 1.0, 1.0),
+    (1, 1, 129, 1, False, -1, -1, False, 0.0, 1.0, 1.0, 1.0),
+]
+
+
+def fp8_case(seed, B, nq, nk, H):
+    d = 128
+    return (W.gen_tensor(seed, W.TENSOR_Q, B, nq, H, d, 1.0, "fp8"),
+            W.gen_tensor(seed, W.TENSOR_K, B, nk, H, d, 1.0, "fp8"),
+            W.gen_tensor(seed, W.TENSOR_V, B, nk, H, d, 1.0, "fp8"))
+
+
+def check_fp8(o, lse, q8, k8, v8, ds, scale, causal, wl, wr, slopes, cap, what, bh=None, rows=None):
+    from gpu_common import e4m3_half_spacing
+    qf = W.to_float(q8, "fp8") * ds[0]
+    kf = W.to_float(k8, "fp8") * ds[1]
+    vf = W.to_float(v8, "fp8") * ds[2]
+    ro, rl = O.attention_ref(qf, kf, vf, scale, causal, wl, wr, slopes, cap, bh=bh)
+    bound = O.prob_weighted_abs_ref(qf, kf, vf, scale, causal, wl, wr, slopes, cap, bh=bh,
+                                    weight=lambda pp: e4m3_half_spacing(256.0 * pp) / 256.0)
+    sel = [(b, h) for b in range(q8.shape[0]) for h in range(q8.shape[2])] if bh is None else bh
+    for b, h in sel:
+        og, rg, bd = o[b, :, h], ro[b, :, h], bound[b, :, h]
+        assert not np.isnan(og).any(), f"{what}: NaN"
+        empty = ~np.isfinite(rl[b, h])
+        assert np.array_equal(empty, ~np.isfinite(lse[b, h])), f"{what}: empty-row pattern"
+        err = np.abs(og - rg)
+        tol = 2.0 * bd + 1e-5 * max(float(np.abs(rg).max()), 1e-30)
+        bad = np.argwhere(err > tol)
+        assert len(bad) == 0, (f"{what} b{b} h{h}: {len(bad)} over the bound, first {bad[0].tolist()}"
+                               f" {og[tuple(bad[0])]} vs {rg[tuple(bad[0])]} tol {tol[tuple(bad[0])]:.3e}")
+        if (~empty).any():
+            assert np.abs(lse[b, h][~empty] - rl[b, h][~empty]).max() <= TOL_LSE, what
+    return float(np.abs(o - ro)[np.isfinite(ro)].max()) if bh is None else 0.0
+
+
+def to_dev_fp8(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+@pytest.mark.parametrize("case", FP8_CASES)
+def test_fp8_small(case):
+    B, H, nq, nk, causal, wl, wr, alibi, cap, qd, kd, vd = case
+    say(f"fp8 {case}")
+    q8, k8, v8 = fp8_case(9000 + FP8_CASES.index(case), B, nq, nk, H)
+    slopes = W.alibi_slopes(H) if alibi else None
+    ts = None if slopes is None else torch.from_numpy(slopes).cuda()
+    scale = 1.0 / np.sqrt(128)
+    o, lse = fa.attention_fp8(to_dev_fp8(q8), to_dev_fp8(k8), to_dev_fp8(v8), qd, kd, vd, scale,
+                              causal, wl, wr, ts, cap)
+    torch.cuda.synchronize()
+    print(check_fp8(o.cpu().numpy(), lse.cpu().numpy(), q8, k8, v8, (qd, kd, vd), scale, causal,
+                    wl, wr, slopes, cap, f"fp8 {case}"))
+
+
+def test_fp8_bf16_output_and_determinism():
+    q8, k8, v8 = fp8_case(9100, 2, 300, 500, 4)
+    tq, tk, tv = to_dev_fp8(q8), to_dev_fp8(k8), to_dev_fp8(v8)
+    a = fa.attention_fp8(tq, tk, tv, 0.5, 0.5, 1.0, 0.09, True)
+    b = fa.attention_fp8(tq, tk, tv, 0.5, 0.5, 1.0, 0.09, True)
+    c = fa.attention_fp8(tq, tk, tv, 0.5, 0.5, 1.0, 0.09, True, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(a[0].to(torch.bfloat16), c[0]) and torch.equal(a[1], c[1])
+
+
+def test_fp8_causal_prefill_sampled_heads():
+    """The causal prefill shape (B4 H16 N2048 d128) in FP8: three (b, h) pairs
+    against the oracle on the dequantised inputs."""
+    w = W.WORKLOADS[2]
+    say("fp8 causal prefill")
+    q8, k8, v8 = (W.gen_tensor(w.seed, t, w.B, w.Nq, w.H, w.d, 1.0, "fp8")
+                  for t in (W.TENSOR_Q, W.TENSOR_K, W.TENSOR_V))
+    o, lse = fa.attention_fp8(to_dev_fp8(q8), to_dev_fp8(k8), to_dev_fp8(v8), 1.0, 1.0, 1.0,
+                              w.scale, True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    assert not np.isnan(o).any()
+    check_fp8(o, lse, q8, k8, v8, (1.0, 1.0, 1.0), w.scale, True, -1, -1, None, 0.0,
+              "fp8 prefill", bh=[(0, 0), (3, 15), (2, 7)])

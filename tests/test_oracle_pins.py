@@ -744,3 +744,16 @@ def test_t29_probability_weighted_bound():
     q3, k3, v3 = rnd(77, 1, 6, 1, 2), rnd(78, 1, 2, 1, 2), rnd(79, 1, 2, 1, 2)
     b3 = O.prob_weighted_abs_ref(q3, k3, v3, 1.0, True)                 # Nq > Nk: empty rows
     assert np.all(b3[0, :4] == 0.0)
+
+
+def test_t29_e4m3_half_spacing_matches_the_code_table():
+    import gpu_common as G
+    vals = W.e4m3_bits_to_f32(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)   # 0 .. 448
+    for c in range(0x7E):
+        lo, hi = vals[c], vals[c + 1]
+        for x in (lo, 0.5 * (lo + hi), lo + 0.99 * (hi - lo)):
+            assert G.e4m3_half_spacing(x) == (hi - lo) / 2, (c, x)
+    # rounding to nearest never moves a value by more than it
+    x = np.random.default_rng(80).uniform(0, 256, 5000)
+    xr = W.e4m3_bits_to_f32(W.f32_to_e4m3_bits(x)).astype(np.float64)
+    assert np.all(np.abs(xr - x) <= G.e4m3_half_spacing(x) * (1 + 1e-12))
