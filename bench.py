@@ -11,8 +11,8 @@ prefill launch time); the decode's algorithmic GB/s and the split forward's
 TFLOP/s are reported beside it. After the timed steps, the variable-length
 entry points are timed on their own (a packed causal prefill of 8 sequences of
 seeded lengths, the decode with seeded per-sequence cache lengths, and the
-decode step that appends one key per sequence before attending), and the
-backward pass of the causal prefill.
+decode step that appends one key per sequence before attending), the
+backward pass of the causal prefill, and its forward in FP8.
 Inputs are resident in device memory before the timed region starts.
 
 Prints ONE JSON line on stdout. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -29,6 +29,7 @@ import numpy as np
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "exact_tiled_attention_05_amd", "csrc")
@@ -158,6 +159,9 @@ def main():
         if dtype == "bf16":
             return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(x).to(dev)
+
+    def up8(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # E4M3 codes as uint8
 
     # ---- prefill inputs
     wp = W.WORKLOADS[2]
@@ -375,6 +379,35 @@ def main():
                      "tflops": round(bwd_flops / t_bwd.mean() / 1e12, 3),
                      "pct_peak": round(100 * bwd_flops / t_bwd.mean() / 1e12 / PEAK_BF16_TFLOPS, 2)}
 
+    # ---- FP8 forward on the causal prefill shape (side measurement): E4M3 codes of
+    # the same seeded draws, unit descales; roofline against the FP8 MFMA peak.
+    f8 = [up8(W.gen_tensor(wp.seed, t, wp.B, wp.Nq, wp.H, wp.d, 1.0, "fp8"))
+          for t in (W.TENSOR_Q, W.TENSOR_K, W.TENSOR_V)]
+    fo = torch.empty_like(po)
+    flse = torch.empty_like(plse)
+
+    def fp8_prefill():
+        check(fa.fa_fwd_fp8(f8[0], f8[1], f8[2], 1.0, 1.0, 1.0, fo, flse, wp.B, wp.H, wp.Nq,
+                            wp.Nk, wp.d, wp.scale, True, -1, -1, None, 0.0, stream), "fa_fwd_fp8")
+
+    for _ in range(args.warmup):
+        fp8_prefill()
+    ev4 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for a, e in ev4:
+        a.record(stream)
+        fp8_prefill()
+        e.record(stream)
+    torch.cuda.synchronize()
+    t_f8 = np.array([a.elapsed_time(e) for a, e in ev4]) * 1e-3
+    assert torch.isfinite(fo).all()
+    f8_tflops = prefill_flops / t_f8.mean() / 1e12
+    fp8_line = {"workload": "gpt_causal_prefill in E4M3 (fa_fwd_fp8)",
+                "gflop": round(prefill_flops / 1e9, 4), "ms": round(t_f8.mean() * 1e3, 5),
+                "ms_median": round(float(np.median(t_f8)) * 1e3, 5), "tflops": round(f8_tflops, 3),
+                "roofline": {"bound": "mfma", "achieved": round(f8_tflops, 3), "peak": PEAK_FP8_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(f8_tflops / PEAK_FP8_TFLOPS, 4)}}
+
     pre_tflops = prefill_flops / t_prefill.mean() / 1e12
     dec_time = (t_split + t_comb).mean()
     dec_gbs = decode_bytes / dec_time / 1e9
@@ -441,6 +474,7 @@ def main():
                               "num_splits": SS, "gflop": round(split_flops / 1e9, 4)},
         "variable_lengths": variable,
         "backward": backward_line,
+        "fp8_prefill": fp8_line,
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("prefill"),
