@@ -36,7 +36,7 @@ CSRC = os.path.join(ROOT, "exact_tiled_attention_05_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Source files each measured kernel is built from (a change voids its counters).
 KERNEL_SOURCES = {
-    "prefill": ["fa_fwd_bf16.hip", "fa_device.h", "fa_params.h"],
+    "prefill": ["fa_fwd_bf16.hip", "fa_lds.h", "fa_device.h", "fa_params.h"],
     "decode_split": ["fa_decode_bf16.hip", "fa_device.h", "fa_params.h"],
 }
 
