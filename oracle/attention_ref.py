@@ -249,8 +249,10 @@ def attention_bwd_bh(q_bh, k_bh, v_bh, do_bh, nq, scale, causal=False, window_le
     the gradients. "dq", "dk", "dv" = scale |dZ| |K|, scale |dZ|^T |Q|, P^T |dO|:
     a relative change r of every entry of P and dZ moves dQ, dK, dV by at most r
     times them. "dq_cancel", "dk_cancel" = the same products with |dZ| replaced
-    by P (|dP| + |D|): an absolute error e (|dP| + |D|) in dP - D (rounding of
-    the two sums before they cancel) moves dQ, dK by at most e times them.
+    by P (|dO| |V|^T + |dO|.|O|): dP_ij = dO_i . v_j and D_i = dO_i . O_i are sums
+    over head_dim, and rounding such a sum errs by at most e times the sum of
+    the absolute values of its terms (e about d times the unit roundoff), so an
+    error of that size in dP - D moves dQ, dK by at most e times these.
     """
     rows = np.arange(nq)
     k_bh = np.asarray(k_bh, dtype=np.float64)
@@ -280,7 +282,8 @@ def attention_bwd_bh(q_bh, k_bh, v_bh, do_bh, nq, scale, causal=False, window_le
     dk = scale * (ds.T @ q_bh)
     if with_bounds:
         a = np.abs(ds)
-        c = p * (np.abs(dp) + np.abs(D)[:, None])
+        o_bh = p @ v_bh
+        c = p * (np.abs(do_bh) @ np.abs(v_bh).T + (np.abs(do_bh) * np.abs(o_bh)).sum(axis=1)[:, None])
         ak, aq = np.abs(k_bh), np.abs(q_bh)
         return dq, dk, dv, D, {"dq": scale * (a @ ak), "dk": scale * (a.T @ aq),
                                "dv": p.T @ np.abs(do_bh), "dq_cancel": scale * (c @ ak),

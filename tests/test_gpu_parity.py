@@ -570,11 +570,12 @@ def test_incremental_decode_three_steps():
 # in fp32. A relative change r of every P and dZ entry moves dV by at most
 # r P^T|dO|, dK by r scale |dZ|^T|Q| and dQ by r scale |dZ||K| (the oracle's
 # bound terms); the test allows twice that. dP and D are fp32 sums over head_dim
-# terms, so dP - D carries an error up to about d 2^-24 (|dP| + |D|) before it
-# cancels (to exactly 0 where a row sees a single key); the test allows 2^-16
-# (>= 2 d 2^-24 for d <= 128) times the oracle's cancellation magnitudes, plus
-# 2e-5 of the largest gradient for the remaining fp32 arithmetic. O and LSE
-# come from the oracle here, so the forward's own rounding stays out.
+# terms, so each carries an error up to about d 2^-24 times the sum of the
+# absolute values of its terms before dP - D cancels (to exactly 0 where a row
+# sees a single key); the test allows 2^-16 (>= 2 d 2^-24 for d <= 128) times
+# the oracle's cancellation magnitudes, plus 2e-5 of the largest gradient for
+# the remaining fp32 arithmetic. O and LSE come from the oracle here, so the
+# forward's own rounding stays out.
 U_BF16 = 2.0 ** -9
 E_CANCEL = 2.0 ** -16
 BWD_CASES = [
@@ -769,3 +770,60 @@ def test_fp8_causal_prefill_sampled_heads():
     assert not np.isnan(o).any()
     check_fp8(o, lse, q8, k8, v8, (1.0, 1.0, 1.0), w.scale, True, -1, -1, None, 0.0,
               "fp8 prefill", bh=[(0, 0), (3, 15), (2, 7)])
+
+
+# --------------------------------------------------------------------------
+# Brute-force sweeps of small and ragged shapes: backward and FP8
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("d", [128, 64])
+def test_bwd_sweep_small_shapes(d):
+    case = 0
+    for nq, nk in itertools.product(SIZES, SIZES):
+        for (causal, wl, wr) in mask_variants(nq, nk):
+            case += 1
+            if (nq + 2 * nk + case) % 3:
+                continue  # a deterministic third of the grid (every size and mask still occurs)
+            alibi = case % 3 == 1
+            cap = 7.5 if case % 4 == 2 else 0.0
+            what = f"bwd d{d} nq{nq} nk{nk} causal{causal} wl{wl} wr{wr} alibi{alibi} cap{cap}"
+            say(what)
+            q, k, v, do = bwd_inputs(20000 + case, 1, nq, nk, 2, d, 2.0 if cap else 1.0)
+            qf, kf, vf, gf = (W.to_float(x, "bf16") for x in (q, k, v, do))
+            slopes = W.alibi_slopes(2) if alibi else None
+            ts = None if slopes is None else torch.from_numpy(slopes).cuda()
+            scale = 1.0 / np.sqrt(d)
+            o_ref, l_ref = O.attention_ref(qf, kf, vf, scale, causal, wl, wr, slopes, cap)
+            dq, dk, dv = fa.attention_backward(
+                to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                torch.from_numpy(o_ref.astype(np.float32)).cuda(),
+                torch.from_numpy(l_ref.astype(np.float32)).cuda(), to_dev(do, "bf16"), scale,
+                causal, wl, wr, ts, cap)
+            torch.cuda.synchronize()
+            rq, rk, rv, _, bd = O.attention_bwd_ref(qf, kf, vf, gf, scale, causal, wl, wr, slopes,
+                                                    cap, with_bounds=True)
+            check_grad(dq.cpu().numpy(), rq, bd["dq"], what + " dQ", bd["dq_cancel"])
+            check_grad(dk.cpu().numpy(), rk, bd["dk"], what + " dK", bd["dk_cancel"])
+            check_grad(dv.cpu().numpy(), rv, bd["dv"], what + " dV")
+
+
+def test_fp8_sweep_small_shapes():
+    case = 0
+    for nq, nk in itertools.product(SIZES, SIZES):
+        for (causal, wl, wr) in mask_variants(nq, nk):
+            case += 1
+            if (2 * nq + nk + case) % 3:
+                continue
+            alibi = case % 3 == 1
+            cap = 7.5 if case % 4 == 2 else 0.0
+            ds = (0.5, 2.0, 0.25) if case % 5 == 0 else (1.0, 1.0, 1.0)
+            what = f"fp8 nq{nq} nk{nk} causal{causal} wl{wl} wr{wr} alibi{alibi} cap{cap} ds{ds}"
+            say(what)
+            q8, k8, v8 = fp8_case(30000 + case, 1 + case % 2, nq, nk, 2)
+            slopes = W.alibi_slopes(2) if alibi else None
+            ts = None if slopes is None else torch.from_numpy(slopes).cuda()
+            scale = 1.0 / np.sqrt(128)
+            o, lse = fa.attention_fp8(to_dev_fp8(q8), to_dev_fp8(k8), to_dev_fp8(v8), *ds, scale,
+                                      causal, wl, wr, ts, cap)
+            torch.cuda.synchronize()
+            check_fp8(o.cpu().numpy(), lse.cpu().numpy(), q8, k8, v8, ds, scale, causal, wl, wr,
+                      slopes, cap, what)
