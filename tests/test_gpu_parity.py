@@ -827,3 +827,68 @@ def test_fp8_sweep_small_shapes():
             torch.cuda.synchronize()
             check_fp8(o.cpu().numpy(), lse.cpu().numpy(), q8, k8, v8, ds, scale, causal, wl, wr,
                       slopes, cap, what)
+
+
+def test_varlen_random_packs():
+    """Seeded random packs (0-300 rows per sequence, empty sequences included)
+    across head sizes, dtypes and mask / score variants."""
+    rng = np.random.default_rng(95)
+    for case in range(24):
+        dtype, d = [("bf16", 128), ("bf16", 64), ("fp32", 64), ("fp32", 128)][case % 4]
+        B = int(rng.integers(1, 7))
+        lq = rng.integers(0, 301, B)
+        lk = rng.integers(0, 301, B)
+        if case % 3 == 0:
+            lq[rng.integers(0, B)] = 0
+        causal, wl, wr = [(True, -1, -1), (False, -1, -1), (True, 40, 0), (False, 17, 9)][(case // 4) % 4]
+        alibi, cap = case % 5 == 1, (6.0 if case % 7 == 3 else 0.0)
+        if lq.sum() == 0:
+            lq[0] = 5
+        what = f"varlen random {case}: {dtype} d{d} lq{lq.tolist()} lk{lk.tolist()} {causal} {wl} {wr} {alibi} {cap}"
+        say(what)
+        q, k, v, cq, ck = W.gen_varlen(9500 + case, lq, lk, 2, d, 2.0 if cap else 1.0, dtype)
+        slopes = W.alibi_slopes(2) if alibi else None
+        scale = 1.0 / np.sqrt(d)
+        o, lse = run_varlen(q, k, v, cq, ck, dtype, int(lq.max()), int(max(lk.max(), 0)), scale,
+                            causal, wl, wr, slopes, cap)
+        ro, rl = O.attention_varlen_ref(W.to_float(q, dtype), W.to_float(k, dtype),
+                                        W.to_float(v, dtype), cq, ck, scale, causal, wl, wr,
+                                        slopes, cap)
+        check(o, lse, ro, rl, dtype, what)
+
+
+def test_splitkv_seqlens_random():
+    """Seeded random per-sequence cache lengths, page sizes and split counts,
+    for the decode kernel (Nq = 1) and the multi-row paged kernel."""
+    rng = np.random.default_rng(96)
+    for case in range(16):
+        dtype, d = [("bf16", 128), ("bf16", 64), ("fp32", 64), ("bf16", 128)][case % 4]
+        nq = [1, 1, 3, 33][case % 4]
+        ps = int([16, 64, 7, 256][case % 4])
+        nk = int(rng.integers(100, 1500))
+        B = int(rng.integers(1, 6))
+        S = int(rng.integers(1, 12))
+        seqlens = rng.integers(0, nk + 1, B).tolist()
+        causal, wl = [(True, -1), (True, 200), (False, -1), (True, -1)][case % 4]
+        alibi, cap = case % 3 == 2, (12.0 if case % 5 == 4 else 0.0)
+        what = f"seqlens random {case}: {dtype} d{d} nq{nq} nk{nk} ps{ps} S{S} {seqlens} {causal} {wl}"
+        say(what)
+        w = W.Workload(0, "rand", B=B, H=2, Nq=nq, Nk=nk, d=d, dtype=dtype, causal=causal,
+                       paged=True, page_size=ps, pool_factor=1.25, num_splits=S, seed=9600 + case)
+        q, kc, vc, bt = W.gen_paged(w, seqlens=seqlens)
+        slopes = W.alibi_slopes(2) if alibi else None
+        ts = None if slopes is None else torch.from_numpy(slopes).cuda()
+        scale = 1.0 / np.sqrt(d)
+        o_part, lse_part = fa.attention_paged_splitkv(
+            to_dev(q, dtype), to_dev(kc, dtype), to_dev(vc, dtype), torch.from_numpy(bt).cuda(), nk,
+            S, scale, causal, wl, 0 if causal else -1, ts, cap,
+            cache_seqlens=torch.tensor(seqlens, dtype=torch.int32).cuda())
+        torch.cuda.synchronize()
+        k = np.zeros((B, nk, 2, d))
+        v = np.zeros((B, nk, 2, d))
+        for b, n in enumerate(seqlens):
+            k[b, :n] = O.paged_gather_ref(W.to_float(kc, dtype), bt, b, n)
+            v[b, :n] = O.paged_gather_ref(W.to_float(vc, dtype), bt, b, n)
+        rop, rlp = O.splitkv_ref(W.to_float(q, dtype), k, v, S, ps, scale, causal, wl,
+                                 0 if causal else -1, slopes, cap, seqlens_k=seqlens)
+        check(o_part.cpu().numpy(), lse_part.cpu().numpy(), rop, rlp, dtype, what)
