@@ -892,3 +892,67 @@ def test_splitkv_seqlens_random():
         rop, rlp = O.splitkv_ref(W.to_float(q, dtype), k, v, S, ps, scale, causal, wl,
                                  0 if causal else -1, slopes, cap, seqlens_k=seqlens)
         check(o_part.cpu().numpy(), lse_part.cpu().numpy(), rop, rlp, dtype, what)
+
+
+# --------------------------------------------------------------------------
+# Large shapes (index arithmetic far from the workloads' sizes)
+# --------------------------------------------------------------------------
+def test_many_heads_and_large_batch():
+    """4096 heads (2 MiB rows between keys of one head) and a batch of 2048;
+    sampled (b, h) pairs against the oracle."""
+    for B, H, nq, nk, d in [(1, 4096, 65, 130, 128), (2048, 2, 3, 70, 64)]:
+        say(f"large B/H: B{B} H{H} nq{nq} nk{nk} d{d}")
+        q, k, v = qkv_case(97, B, nq, nk, H, d, "bf16")
+        o, lse = run_fwd(q, k, v, "bf16", 0.1, True, -1, -1, None, 0.0)
+        pairs = [(0, 0), (B - 1, H - 1), (B // 2, H // 3), (B - 1, 0)]
+        ro, rl = oracle_fwd(q, k, v, "bf16", 0.1, True, -1, -1, None, 0.0, bh=pairs)
+        for b, h in pairs:
+            check(o[b, :, h], lse[b, h], ro[b, :, h], rl[b, h], "bf16", f"B{B} H{H} b{b} h{h}")
+
+
+def test_long_window_sequence():
+    """65536 keys with a 2048-key causal window (sampled rows across the range)."""
+    B, H, n, d = 1, 2, 65536, 64
+    say("long window sequence")
+    q, k, v = qkv_case(98, B, n, n, H, d, "bf16")
+    o, lse = run_fwd(q, k, v, "bf16", 0.125, True, 2048, 0, None, 0.0)
+    rows = np.array([0, 1, 2047, 2048, 2049, 32767, 32768, 65534, 65535, 40000, 12345])
+    ro, rl = oracle_fwd(q, k, v, "bf16", 0.125, True, 2048, 0, None, 0.0, rows=rows)
+    check(o[:, rows], lse[:, :, rows], ro, rl, "bf16", "long window")
+
+
+def test_decode_over_a_quarter_million_keys():
+    """One query row over 262144 cached keys in 256-key pages, 64 splits."""
+    w = W.Workload(0, "long_decode", B=1, H=2, Nq=1, Nk=262144, d=128, dtype="bf16", causal=True,
+                   paged=True, page_size=256, pool_factor=1.1, num_splits=64, seed=99)
+    say("decode over 262144 keys")
+    q, kc, vc, bt = W.gen_paged(w)
+    o, lse = fa.decode_paged(to_dev(q, "bf16"), to_dev(kc, "bf16"), to_dev(vc, "bf16"),
+                             torch.from_numpy(bt).cuda(), w.Nk, w.num_splits, softmax_scale=w.scale,
+                             causal=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    qf = W.to_float(q, "bf16")
+    for h in range(w.H):
+        kb = W.to_float(W.gen_slice(w.seed, W.TENSOR_K, 0, h, w.Nk, w.d, 1.0, "bf16"), "bf16")
+        vb = W.to_float(W.gen_slice(w.seed, W.TENSOR_V, 0, h, w.Nk, w.d, 1.0, "bf16"), "bf16")
+        ro, rl = O.attention_bh(qf[0, :, h], kb, vb, np.arange(1), 1, w.scale, True)
+        check(o[0, :, h], lse[0, h], ro, rl, "bf16", f"long decode h{h}")
+
+
+def test_bwd_many_heads():
+    """The backward with 1024 heads (its row-term workspace and tile decode at large H)."""
+    B, H, nq, nk, d = 1, 1024, 40, 150, 128
+    say("bwd many heads")
+    q, k, v, do = bwd_inputs(8200, B, nq, nk, H, d, 1.0)
+    tq, tk, tv, tg = (to_dev(x, "bf16") for x in (q, k, v, do))
+    o, lse = fa.attention(tq, tk, tv, 0.1, True)
+    dq, dk, dv = fa.attention_backward(tq, tk, tv, o, lse, tg, 0.1, True)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+    for h in (0, 511, 1023):
+        sl = lambda x: W.to_float(x[0, :, h], "bf16")  # noqa: E731
+        rq, rk, rv, _ = O.attention_bwd_bh(sl(q), sl(k), sl(v), sl(do), nq, 0.1, True)
+        for got, ref, name in ((dq[0, :, h], rq, "dQ"), (dk[0, :, h], rk, "dK"), (dv[0, :, h], rv, "dV")):
+            rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+            assert rel <= 1e-2, (h, name, rel)
