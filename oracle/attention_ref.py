@@ -362,6 +362,42 @@ def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=Fals
     return o, lse
 
 
+def attention_varlen_bwd_ref(q, k, v, do, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
+                             window_left=-1, window_right=-1, alibi_slopes=None, softcap=0.0,
+                             with_bounds=False):
+    """Gradients of attention_varlen_ref: each sequence's own backward (attention_bwd_bh).
+
+    q, do [total_q, H, d]; k, v [total_k, H, d]. Returns dq, dk, dv shaped like
+    q, k, v (rows no sequence owns are 0), plus, with with_bounds, the bound
+    magnitudes of attention_bwd_bh in a dict of arrays shaped the same way.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64)
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    H = q.shape[1]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    like = {"dq": q, "dk": k, "dv": v, "dq_cancel": q, "dk_cancel": k}
+    bounds = {n: np.zeros(x.shape) for n, x in like.items()}
+    for b in range(len(cq) - 1):
+        q0, q1, k0, k1 = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+        for h in range(H):
+            slope = None if alibi_slopes is None else float(alibi_slopes[h])
+            g = attention_bwd_bh(q[q0:q1, h], k[k0:k1, h], v[k0:k1, h], do[q0:q1, h], q1 - q0,
+                                 scale, causal, window_left, window_right, slope, softcap,
+                                 with_bounds)
+            dq[q0:q1, h], dk[k0:k1, h], dv[k0:k1, h] = g[0], g[1], g[2]
+            if with_bounds:
+                for n in bounds:
+                    rows = slice(q0, q1) if n.startswith("dq") else slice(k0, k1)
+                    bounds[n][rows, h] = g[4][n]
+    if with_bounds:
+        return dq, dk, dv, bounds
+    return dq, dk, dv
+
+
 # --------------------------------------------------------------------------
 # Paged KV cache (flash-attn update article, v2.5 entry)
 # --------------------------------------------------------------------------

@@ -757,3 +757,43 @@ def test_t29_e4m3_half_spacing_matches_the_code_table():
     x = np.random.default_rng(80).uniform(0, 256, 5000)
     xr = W.e4m3_bits_to_f32(W.f32_to_e4m3_bits(x)).astype(np.float64)
     assert np.all(np.abs(xr - x) <= G.e4m3_half_spacing(x) * (1 + 1e-12))
+
+
+def test_t30_varlen_backward_equals_batched_and_is_per_sequence():
+    """Equal lengths: the batched backward; mixed lengths: each sequence's gradients
+    depend on that sequence alone (checked against central differences of the
+    packed forward for one entry per tensor and sequence)."""
+    B, nq, nk, H, d = 2, 4, 6, 2, 3
+    q, k, v, g = rnd(100, B, nq, H, d), rnd(101, B, nk, H, d), rnd(102, B, nk, H, d), rnd(103, B, nq, H, d)
+    sl = np.array([0.2, 0.4])
+    bq, bk, bv, _ = O.attention_bwd_ref(q, k, v, g, 0.6, True, 3, 0, sl, 2.0)
+    cq, ck = np.arange(B + 1) * nq, np.arange(B + 1) * nk
+    vq, vk, vv = O.attention_varlen_bwd_ref(q.reshape(-1, H, d), k.reshape(-1, H, d),
+                                            v.reshape(-1, H, d), g.reshape(-1, H, d), cq, ck, 0.6,
+                                            True, 3, 0, sl, 2.0)
+    np.testing.assert_allclose(vq, bq.reshape(-1, H, d), atol=1e-14)
+    np.testing.assert_allclose(vk, bk.reshape(-1, H, d), atol=1e-14)
+    np.testing.assert_allclose(vv, bv.reshape(-1, H, d), atol=1e-14)
+    lens = [(3, 5), (0, 2), (4, 1), (2, 0)]
+    qp, cqp = pack([a for a, _ in lens], H, d, 104)
+    kp, ckp = pack([b for _, b in lens], H, d, 105)
+    vp_, _ = pack([b for _, b in lens], H, d, 106)
+    gp, _ = pack([a for a, _ in lens], H, d, 107)
+    dq, dk, dv = O.attention_varlen_bwd_ref(qp, kp, vp_, gp, cqp, ckp, 0.7, True)
+
+    def loss():
+        o, _ = O.attention_varlen_ref(qp, kp, vp_, cqp, ckp, 0.7, True)
+        return float(np.nansum(o * gp))
+    eps = 1e-6
+    for x, grad, cu in ((qp, dq, cqp), (kp, dk, ckp), (vp_, dv, ckp)):
+        for b in range(len(lens)):
+            if cu[b + 1] == cu[b]:
+                continue
+            idx = (int(cu[b]), 1, 2)
+            old = x[idx]
+            x[idx] = old + eps
+            lp = loss()
+            x[idx] = old - eps
+            lm = loss()
+            x[idx] = old
+            assert abs((lp - lm) / (2 * eps) - grad[idx]) < 1e-7
