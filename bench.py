@@ -373,6 +373,38 @@ def main():
     torch.cuda.synchronize()
     t_bwd = np.array([a.elapsed_time(e) for a, e in ev3]) * 1e-3
     assert torch.isfinite(bdq).all() and torch.isfinite(bdk).all() and torch.isfinite(bdv).all()
+    # the packed prefill's backward (fa_bwd_varlen) from its forward's O and LSE above
+    vg = up(W.gen_tensor(91, 3, 1, tot, wp.H, wp.d, 1.0, "bf16")[0], "bf16")
+    vdq = torch.empty((tot, wp.H, wp.d), dtype=torch.float32, device=dev)
+    vdk, vdv = torch.empty_like(vdq), torch.empty_like(vdq)
+    vws = torch.empty((fa.fa_bwd_workspace_bytes(len(vl), wp.H, int(vl.max())) // 4,),
+                      dtype=torch.float32, device=dev)
+
+    def varlen_backward():
+        check(fa.fa_bwd_varlen(vq, vk, vv, vo, vg, vlse, vdq, vdk, vdv, vws, tcq, tck, len(vl),
+                               wp.H, tot, tot, int(vl.max()), int(vl.max()), wp.d, wp.scale, True,
+                               -1, -1, None, 0.0, stream), "fa_bwd_varlen")
+
+    varlen_prefill()
+    for _ in range(args.warmup):
+        varlen_backward()
+    ev5 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for a, e in ev5:
+        a.record(stream)
+        varlen_backward()
+        e.record(stream)
+    torch.cuda.synchronize()
+    t_vbwd = np.array([a.elapsed_time(e) for a, e in ev5]) * 1e-3
+    assert torch.isfinite(vdq).all() and torch.isfinite(vdk).all() and torch.isfinite(vdv).all()
+    vbwd_flops = 2.5 * var_flops
+    variable["packed_backward"] = {
+        "lengths": vl.tolist(), "gflop": round(vbwd_flops / 1e9, 4),
+        "ms": round(t_vbwd.mean() * 1e3, 5), "ms_median": round(float(np.median(t_vbwd)) * 1e3, 5),
+        "tflops": round(vbwd_flops / t_vbwd.mean() / 1e12, 3),
+        "pct_peak": round(100 * vbwd_flops / t_vbwd.mean() / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    del vg, vdq, vdk, vdv, vws
+
     backward_line = {"workload": "gpt_causal_prefill backward (fa_bwd: prep, dK/dV, dQ)",
                      "gflop": round(bwd_flops / 1e9, 4), "ms": round(t_bwd.mean() * 1e3, 5),
                      "ms_median": round(float(np.median(t_bwd)) * 1e3, 5),

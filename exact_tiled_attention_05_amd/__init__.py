@@ -25,10 +25,10 @@ __all__ = [
     "FA_FP32", "FA_BF16", "FaError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
     "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes",
-    "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len",
+    "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len",
     "attention", "attention_fp8", "attention_varlen", "attention_split", "attention_split_partials",
-    "attention_paged_splitkv", "attention_paged_append", "attention_backward", "combine",
-    "decode_paged",
+    "attention_paged_splitkv", "attention_paged_append", "attention_backward",
+    "attention_varlen_backward", "combine", "decode_paged",
 ]
 
 FA_FP32, FA_BF16 = 0, 1
@@ -38,7 +38,7 @@ _lib = None
 
 EXPORTED = ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
             "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd",
-            "fa_bwd_workspace_bytes", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len")
+            "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len")
 
 
 class FaError(RuntimeError):
@@ -79,6 +79,9 @@ def load_library():
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, i, vp, i, i, i, i, i, f, i,
                            i, i, vp, f, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, i, vp, vp, vp, i, i,
+                                  i, i, i, i, i, f, i, i, i, vp, f, vp]
+    lib.fa_bwd_varlen.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_longlong
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, i, vp, i, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
@@ -221,6 +224,20 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, batch, heads, seqlen_q,
 
 def fa_bwd_workspace_bytes(batch: int, heads: int, seqlen_q: int) -> int:
     return int(load_library().fa_bwd_workspace_bytes(int(batch), int(heads), int(seqlen_q)))
+
+
+def fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens_q, cu_seqlens_k,
+                  batch, heads, total_q, total_k, max_seqlen_q, max_seqlen_k, head_dim,
+                  softmax_scale, causal=False, window_left=-1, window_right=-1,
+                  alibi_slopes=None, softcap=0.0, stream=None) -> int:
+    """Call fa_bwd_varlen on caller-allocated tensors; returns the status code."""
+    return load_library().fa_bwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _dtype_code(q), _dtype_code(o),
+        _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq), _ptr(workspace), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), int(batch), int(heads), int(total_q), int(total_k),
+        int(max_seqlen_q), int(max_seqlen_k), int(head_dim), float(softmax_scale),
+        int(bool(causal)), int(window_left), int(window_right), _ptr(alibi_slopes),
+        float(softcap), _stream(stream))
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, heads, total_q, total_k,
@@ -388,6 +405,41 @@ def attention_backward(q, k, v, o, lse, dout, softmax_scale=None, causal=False, 
                      device=q.device)
     _check(fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, nq, nk, d, softmax_scale, causal,
                   window_left, window_right, alibi_slopes, softcap, stream), "fa_bwd")
+    return dq, dk, dv
+
+
+def attention_varlen_backward(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                              max_seqlen_k, softmax_scale=None, causal=False, window_left=-1,
+                              window_right=-1, alibi_slopes=None, softcap=0.0,
+                              grad_dtype=torch.float32, stream=None):
+    """dq [total_q,H,d], dk, dv [total_k,H,d] (grad_dtype) for a packed batch, from
+    attention_varlen's o and lse [H, total_q] and dout [total_q,H,d] (same dtype as q)."""
+    _same_dtype(q, k, v, dout)
+    total_q, H, d = q.shape
+    total_k = k.shape[0]
+    if tuple(k.shape) != (total_k, H, d) or tuple(v.shape) != (total_k, H, d):
+        raise ValueError("k and v must be [total_k, H, d] matching q")
+    if tuple(o.shape) != (total_q, H, d) or tuple(dout.shape) != (total_q, H, d):
+        raise ValueError("o and dout must be [total_q, H, d]")
+    if tuple(lse.shape) != (H, total_q) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [H, total_q]")
+    for cu in (cu_seqlens_q, cu_seqlens_k):
+        if cu.dtype != torch.int32 or cu.dim() != 1:
+            raise ValueError("cu_seqlens must be int32 [B + 1]")
+    if cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    B = cu_seqlens_q.shape[0] - 1
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    dq = torch.empty((total_q, H, d), dtype=grad_dtype, device=q.device)
+    dk = torch.empty((total_k, H, d), dtype=grad_dtype, device=q.device)
+    dv = torch.empty((total_k, H, d), dtype=grad_dtype, device=q.device)
+    ws = torch.empty((fa_bwd_workspace_bytes(B, H, max_seqlen_q) // 4,), dtype=torch.float32,
+                     device=q.device)
+    _check(fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, ws, cu_seqlens_q, cu_seqlens_k, B, H,
+                         total_q, total_k, max_seqlen_q, max_seqlen_k, d, softmax_scale, causal,
+                         window_left, window_right, alibi_slopes, softcap, stream),
+           "fa_bwd_varlen")
     return dq, dk, dv
 
 

@@ -157,6 +157,80 @@ int splitkv(const void* q, const void* k_cache, const void* v_cache, const void*
   return fn(p, stream) ? FA_ERR_HIP : FA_OK;
 }
 
+// fa_bwd and fa_bwd_varlen (cu_seqlens_q = nullptr: the batched layout; seqlen_q,
+// seqlen_k are then the lengths, else the maxima). Sizes are checked by the callers.
+int bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+        const float* lse, int in_dtype, int o_dtype, void* dq, void* dk, void* dv, int grad_dtype,
+        float* workspace, const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int heads,
+        int total_q, int total_k, int seqlen_q, int seqlen_k, int head_dim, float softmax_scale,
+        int causal, int window_left, int window_right, const float* alibi_slopes, float softcap,
+        void* stream) {
+  int st = check_kind(in_dtype, head_dim);
+  if (st) return st;
+  if (in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != FA_FP32 && o_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (grad_dtype != FA_FP32 && grad_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
+    return st;
+  if (cu_seqlens_q && total_q == 0 && total_k == 0) return FA_OK;  // an empty pack
+
+  // Reuse the forward's mask folding (a window wider than both sequences is no
+  // constraint; causal is the right window 0).
+  fa::FwdParams f = {};
+  fill_common(f, batch, heads, seqlen_q, seqlen_k, softmax_scale, causal, window_left,
+              window_right, alibi_slopes, softcap, fa::BWD_BM);
+  fa::BwdParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.rowterms = workspace;
+  p.nblk = (seqlen_q + fa::BWD_RB - 1) / fa::BWD_RB;
+  p.alibi = alibi_slopes;
+  p.cu_seqlens_q = cu_seqlens_q;
+  p.cu_seqlens_k = cu_seqlens_k;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  p.B = batch;
+  p.H = heads;
+  p.Nq = seqlen_q;
+  p.Nk = seqlen_k;
+  p.window_left = f.window_left;
+  p.window_right = f.window_right;
+  p.o_bf16 = o_dtype == FA_BF16;
+  p.g_bf16 = grad_dtype == FA_BF16;
+  p.num_q_tiles = (seqlen_q + fa::BWD_BM - 1) / fa::BWD_BM;
+  p.num_k_tiles = (seqlen_k + fa::BWD_BK - 1) / fa::BWD_BK;
+  p.scale = softmax_scale;
+  p.scale_log2 = f.scale_log2;
+  p.softcap_log2 = f.softcap_log2;
+  p.scale_over_cap2 = f.scale_over_cap2;
+  if ((int64_t)p.num_q_tiles * heads * batch > kMaxGroups ||
+      (int64_t)p.num_k_tiles * heads * batch > kMaxGroups ||
+      (int64_t)p.nblk * fa::BWD_RB * heads * batch / 8 > kMaxGroups)
+    return FA_ERR_SHAPE;
+
+  const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
+  int rc;
+#define FA_BWD(D)                                                       \
+  if (sc && al) rc = fa::launch_bwd_bf16<D, true, true>(p, stream);     \
+  else if (sc) rc = fa::launch_bwd_bf16<D, true, false>(p, stream);     \
+  else if (al) rc = fa::launch_bwd_bf16<D, false, true>(p, stream);     \
+  else rc = fa::launch_bwd_bf16<D, false, false>(p, stream);
+  if (head_dim == 64) {
+    FA_BWD(64)
+  } else {
+    FA_BWD(128)
+  }
+#undef FA_BWD
+  return rc ? FA_ERR_HIP : FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -377,66 +451,30 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int head_dim, float softmax_scale, int causal, int window_left, int window_right,
            const float* alibi_slopes, float softcap, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
-  int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
+  const int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
   if (st) return st;
-  if ((st = check_kind(in_dtype, head_dim))) return st;
-  if (in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-  if (o_dtype != FA_FP32 && o_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-  if (grad_dtype != FA_FP32 && grad_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-  if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
-    return st;
+  return bwd(q, k, v, o, dout, lse, in_dtype, o_dtype, dq, dk, dv, grad_dtype, workspace, nullptr,
+             nullptr, batch, heads, 0, 0, seqlen_q, seqlen_k, head_dim, softmax_scale, causal,
+             window_left, window_right, alibi_slopes, softcap, stream);
+}
 
-  // Reuse the forward's mask folding (a window wider than both sequences is no
-  // constraint; causal is the right window 0).
-  fa::FwdParams f = {};
-  fill_common(f, batch, heads, seqlen_q, seqlen_k, softmax_scale, causal, window_left,
-              window_right, alibi_slopes, softcap, fa::BWD_BM);
-  fa::BwdParams p = {};
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = o;
-  p.dout = dout;
-  p.lse = lse;
-  p.dq = dq;
-  p.dk = dk;
-  p.dv = dv;
-  const int64_t rows = (int64_t)batch * heads * seqlen_q;
-  p.rowterms = workspace;
-  p.nblk = (seqlen_q + fa::BWD_RB - 1) / fa::BWD_RB;
-  p.alibi = alibi_slopes;
-  p.B = batch;
-  p.H = heads;
-  p.Nq = seqlen_q;
-  p.Nk = seqlen_k;
-  p.window_left = f.window_left;
-  p.window_right = f.window_right;
-  p.o_bf16 = o_dtype == FA_BF16;
-  p.g_bf16 = grad_dtype == FA_BF16;
-  p.num_q_tiles = (seqlen_q + fa::BWD_BM - 1) / fa::BWD_BM;
-  p.num_k_tiles = (seqlen_k + fa::BWD_BK - 1) / fa::BWD_BK;
-  p.scale = softmax_scale;
-  p.scale_log2 = f.scale_log2;
-  p.softcap_log2 = f.softcap_log2;
-  p.scale_over_cap2 = f.scale_over_cap2;
-  if ((int64_t)p.num_q_tiles * heads * batch > kMaxGroups ||
-      (int64_t)p.num_k_tiles * heads * batch > kMaxGroups || rows / 8 > kMaxGroups)
-    return FA_ERR_SHAPE;
-
-  const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
-  int rc;
-#define FA_BWD(D)                                                       \
-  if (sc && al) rc = fa::launch_bwd_bf16<D, true, true>(p, stream);     \
-  else if (sc) rc = fa::launch_bwd_bf16<D, true, false>(p, stream);     \
-  else if (al) rc = fa::launch_bwd_bf16<D, false, true>(p, stream);     \
-  else rc = fa::launch_bwd_bf16<D, false, false>(p, stream);
-  if (head_dim == 64) {
-    FA_BWD(64)
-  } else {
-    FA_BWD(128)
-  }
-#undef FA_BWD
-  return rc ? FA_ERR_HIP : FA_OK;
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, int in_dtype, int o_dtype, void* dq, void* dk, void* dv,
+                  int grad_dtype, float* workspace, const int* cu_seqlens_q,
+                  const int* cu_seqlens_k, int batch, int heads, int total_q, int total_k,
+                  int max_seqlen_q, int max_seqlen_k, int head_dim, float softmax_scale,
+                  int causal, int window_left, int window_right, const float* alibi_slopes,
+                  float softcap, void* stream) {
+  if (!cu_seqlens_q || !cu_seqlens_k || !workspace) return FA_ERR_NULL;
+  if (total_q > 0 && (!q || !o || !dout || !lse || !dq)) return FA_ERR_NULL;
+  if (total_k > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULL;
+  if (batch <= 0 || batch > (1 << 24) || heads <= 0 || heads > (1 << 16)) return FA_ERR_SHAPE;
+  if (total_q < 0 || total_k < 0 || max_seqlen_q <= 0 || max_seqlen_k < 0) return FA_ERR_SHAPE;
+  if (max_seqlen_q > kMaxSeq || max_seqlen_k > kMaxSeq) return FA_ERR_SHAPE;
+  return bwd(q, k, v, o, dout, lse, in_dtype, o_dtype, dq, dk, dv, grad_dtype, workspace,
+             cu_seqlens_q, cu_seqlens_k, batch, heads, total_q, total_k, max_seqlen_q,
+             max(max_seqlen_k, 1), head_dim, softmax_scale, causal, window_left, window_right,
+             alibi_slopes, softcap, stream);
 }
 
 int fa_splitkv_combine(const float* o_part, const float* lse_part, int num_splits, int batch,

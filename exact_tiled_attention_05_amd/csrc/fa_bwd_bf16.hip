@@ -45,6 +45,36 @@ constexpr int kBK = BWD_BK;    // keys per dK/dV workgroup (32 per wavefront)
 constexpr int kBM = BWD_BM;    // query rows per dQ workgroup (32 per wavefront)
 constexpr float kInf = __builtin_inff();
 
+// The sequence of (b, h): its lengths and where its rows sit. A packed batch
+// reads its offsets from cu_seqlens_q/k, clamped into the tensors and to the
+// maxima so that any contents keep every access in bounds.
+struct BwdSeq {
+  int nq, nk;
+  int64_t q_row0, k_row0;  // rows (of H * D elements) of query 0 and key 0
+  int64_t lse0;            // lse index of (h, query 0)
+};
+__device__ __forceinline__ BwdSeq bwd_seq(const BwdParams& p, int b, int h) {
+  BwdSeq s;
+  if (p.cu_seqlens_q) {
+    const int q0 = min(max(p.cu_seqlens_q[b], 0), p.total_q);
+    const int q1 = min(max(p.cu_seqlens_q[b + 1], q0), p.total_q);
+    const int k0 = min(max(p.cu_seqlens_k[b], 0), p.total_k);
+    const int k1 = min(max(p.cu_seqlens_k[b + 1], k0), p.total_k);
+    s.nq = min(q1 - q0, p.Nq);
+    s.nk = min(k1 - k0, p.Nk);
+    s.q_row0 = q0;
+    s.k_row0 = k0;
+    s.lse0 = (int64_t)h * p.total_q + q0;
+  } else {
+    s.nq = p.Nq;
+    s.nk = p.Nk;
+    s.q_row0 = (int64_t)b * p.Nq;
+    s.k_row0 = (int64_t)b * p.Nk;
+    s.lse0 = ((int64_t)b * p.H + h) * p.Nq;
+  }
+  return s;
+}
+
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
@@ -65,10 +95,11 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
   const int i = (int)(slot % nqp);
   const int64_t bh = slot / nqp;
   const int h = (int)(bh % p.H), b = (int)(bh / p.H);
-  const bool live = ok && i < p.Nq;
+  const BwdSeq sq = bwd_seq(p, ok ? b : 0, h);
+  const bool live = ok && i < sq.nq;
   float acc = 0.0f;
   if (live) {
-    const int64_t e = (((int64_t)b * p.Nq + i) * p.H + h) * D + 8 * c;
+    const int64_t e = ((sq.q_row0 + i) * p.H + h) * D + 8 * c;
     const u32x4_t g = *(const u32x4_t*)((const uint16_t*)p.dout + e);
     float o[8];
     if (p.o_bf16) {
@@ -95,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
   if (ok && c == 0) {
     float l2 = kInf;
     if (live) {
-      const float l = p.lse[((int64_t)b * p.H + h) * p.Nq + i];
+      const float l = p.lse[sq.lse0 + i];
       l2 = l == kNegInf ? kInf : l * kLog2e;
     }
     float* rt = p.rowterms + (bh * p.nblk + i / BWD_RB) * (2 * BWD_RB) + i % BWD_RB;
@@ -144,12 +175,12 @@ __device__ __forceinline__ void store_grad4(void* base, int bf16, int64_t off, f
 
 // Zero rows [r0, r1) of a [B, N, H, D] gradient for (b, h), NT threads.
 template <int NT>
-__device__ void zero_rows(void* base, int bf16, int b, int h, int N, int H, int D, int r0, int r1,
+__device__ void zero_rows(void* base, int bf16, int64_t row0, int h, int H, int D, int r0, int r1,
                           int tid) {
   const int n = (r1 - r0) * D / 4;
   for (int idx = tid; idx < n; idx += NT) {
     const int row = r0 + idx / (D / 4), c = idx % (D / 4);
-    store_grad4(base, bf16, (((int64_t)b * N + row) * H + h) * D + 4 * c, 0.f, 0.f, 0.f, 0.f);
+    store_grad4(base, bf16, ((row0 + row) * H + h) * D + 4 * c, 0.f, 0.f, 0.f, 0.f);
   }
 }
 
@@ -209,9 +240,11 @@ void bwd_dkdv_kernel(BwdParams p) {
   L /= p.H;
   const int b = L % p.B;
   const int kt = L / p.B;  // ascending: under causal the first key tile is seen by the most rows
-  const int nq = p.Nq, nk = p.Nk, off = nk - nq;
+  const BwdSeq sq = bwd_seq(p, b, h);
+  const int nq = sq.nq, nk = sq.nk, off = nk - nq;
   const int wl = p.window_left, wr = p.window_right;
   const int k0 = kt * kBK, k1 = min(nk, k0 + kBK);
+  if (k0 >= nk) return;  // a packed sequence shorter than the longest
 
   // Query rows the workgroup's keys are seen by (union over its keys).
   int ulo, uhi, tmp;
@@ -219,8 +252,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   query_range(k1 - 1, off, nq, wl, wr, tmp, uhi);
   uhi = max(uhi, ulo);
   if (uhi <= ulo) {
-    zero_rows<kDkdvThreads>(p.dk, p.g_bf16, b, h, nk, p.H, D, k0, k1, tid);
-    zero_rows<kDkdvThreads>(p.dv, p.g_bf16, b, h, nk, p.H, D, k0, k1, tid);
+    zero_rows<kDkdvThreads>(p.dk, p.g_bf16, sq.k_row0, h, p.H, D, k0, k1, tid);
+    zero_rows<kDkdvThreads>(p.dv, p.g_bf16, sq.k_row0, h, p.H, D, k0, k1, tid);
     return;
   }
 
@@ -252,7 +285,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int wu = __builtin_amdgcn_readfirstlane(w);
   {
     // V tile of the workgroup's keys (rows past Nk arrive as zeros), all eight wavefronts.
-    const char* vb = (const char*)p.v + 2 * ((((int64_t)b * nk + k0) * p.H + h) * D);
+    const char* vb = (const char*)p.v + 2 * (((sq.k_row0 + k0) * p.H + h) * D);
     const int64_t left = (int64_t)(nk - 1 - k0) * row_bytes + 2 * D;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(vb, left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
 #pragma unroll
@@ -262,7 +295,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   // copies the block's 64 row terms (identical values). Blocks past the range
   // read nothing and write zeros, which keeps the wait counts fixed.
   const int cs = __builtin_amdgcn_readfirstlane(grp);
-  const char* tbh = (const char*)(role == 0 ? p.q : p.dout) + 2 * (((int64_t)b * nq * p.H + h) * D);
+  const char* tbh = (const char*)(role == 0 ? p.q : p.dout) + 2 * ((sq.q_row0 * p.H + h) * D);
   const int64_t qend = (int64_t)(nq - 1) * row_bytes + 2 * D;
   const float* rbh = p.rowterms + ((int64_t)b * p.H + h) * p.nblk * (2 * kBQ);
   const int qb_first = (ulo / kBQ) * kBQ;
@@ -329,7 +362,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     bf16x8_t kf[KS];
     {
       const uint16_t* kp =
-          (const uint16_t*)p.k + (((int64_t)b * nk + min(key, nk - 1)) * p.H + h) * D + 8 * h2;
+          (const uint16_t*)p.k + ((sq.k_row0 + min(key, nk - 1)) * p.H + h) * D + 8 * h2;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4_t x = *(const u32x4_t*)(kp + 16 * ks);
@@ -495,7 +528,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   // Epilogue: lane = key, slots = head_dim rows 32db + 8g + 4h2 + {0..3}.
   if (key >= k1) return;
-  const int64_t base = (((int64_t)b * nk + key) * p.H + h) * D;
+  const int64_t base = ((sq.k_row0 + key) * p.H + h) * D;
   void* dst = role == 0 ? p.dv : p.dk;
   const float sc = role == 0 ? 1.0f : p.scale;
 #pragma unroll
@@ -554,9 +587,11 @@ void bwd_dkdv_w4_kernel(BwdParams p) {
   L /= p.H;
   const int b = L % p.B;
   const int kt = L / p.B;  // ascending: under causal the first key tile is seen by the most rows
-  const int nq = p.Nq, nk = p.Nk, off = nk - nq;
+  const BwdSeq sq = bwd_seq(p, b, h);
+  const int nq = sq.nq, nk = sq.nk, off = nk - nq;
   const int wl = p.window_left, wr = p.window_right;
   const int k0 = kt * kBK, k1 = min(nk, k0 + kBK);
+  if (k0 >= nk) return;  // a packed sequence shorter than the longest
 
   // Query rows the workgroup's keys are seen by (union over its keys).
   int ulo, uhi, tmp;
@@ -564,8 +599,8 @@ void bwd_dkdv_w4_kernel(BwdParams p) {
   query_range(k1 - 1, off, nq, wl, wr, tmp, uhi);
   uhi = max(uhi, ulo);
   if (uhi <= ulo) {
-    zero_rows<kThreads>(p.dk, p.g_bf16, b, h, nk, p.H, D, k0, k1, tid);
-    zero_rows<kThreads>(p.dv, p.g_bf16, b, h, nk, p.H, D, k0, k1, tid);
+    zero_rows<kThreads>(p.dk, p.g_bf16, sq.k_row0, h, p.H, D, k0, k1, tid);
+    zero_rows<kThreads>(p.dv, p.g_bf16, sq.k_row0, h, p.H, D, k0, k1, tid);
     return;
   }
 
@@ -590,7 +625,7 @@ void bwd_dkdv_w4_kernel(BwdParams p) {
   bf16x8_t kf[KS];
   {
     const uint16_t* kp =
-        (const uint16_t*)p.k + (((int64_t)b * nk + min(key, nk - 1)) * p.H + h) * D + 8 * h2;
+        (const uint16_t*)p.k + ((sq.k_row0 + min(key, nk - 1)) * p.H + h) * D + 8 * h2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4_t x = *(const u32x4_t*)(kp + 16 * ks);
@@ -610,15 +645,15 @@ void bwd_dkdv_w4_kernel(BwdParams p) {
   };
   {
     // V tile of the workgroup's keys (rows past Nk arrive as zeros).
-    const char* vb = (const char*)p.v + 2 * ((((int64_t)b * nk + k0) * p.H + h) * D);
+    const char* vb = (const char*)p.v + 2 * (((sq.k_row0 + k0) * p.H + h) * D);
     const int64_t left = (int64_t)(nk - 1 - k0) * row_bytes + 2 * D;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(vb, left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i)
       buffer_load_lds16(rs, sV + 512 * (VLOADS * wu + i), lane_off(VLOADS * wu + i));
   }
-  const char* qbh = (const char*)p.q + 2 * (((int64_t)b * nq * p.H + h) * D);
-  const char* gbh = (const char*)p.dout + 2 * (((int64_t)b * nq * p.H + h) * D);
+  const char* qbh = (const char*)p.q + 2 * ((sq.q_row0 * p.H + h) * D);
+  const char* gbh = (const char*)p.dout + 2 * ((sq.q_row0 * p.H + h) * D);
   const int64_t qend = (int64_t)(nq - 1) * row_bytes + 2 * D;
   const float* rbh = p.rowterms + ((int64_t)b * p.H + h) * p.nblk * (2 * kBQ);
   const int qb_first = (ulo / kBQ) * kBQ;
@@ -775,7 +810,7 @@ void bwd_dkdv_w4_kernel(BwdParams p) {
 
   // Epilogue: lane = key, slots = head_dim rows 32db + 8g + 4h2 + {0..3}.
   if (key >= k1) return;
-  const int64_t base = (((int64_t)b * nk + key) * p.H + h) * D;
+  const int64_t base = ((sq.k_row0 + key) * p.H + h) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -812,12 +847,14 @@ void bwd_dq_kernel(BwdParams p) {
   const int h = L % p.H;
   L /= p.H;
   const int b = L % p.B;
-  const int qt = p.num_q_tiles - 1 - L / p.B;  // heaviest (last) tile first
-  const int nq = p.Nq, nk = p.Nk, off = nk - nq;
+  const BwdSeq sq = bwd_seq(p, b, h);
+  const int nq = sq.nq, nk = sq.nk, off = nk - nq;
+  const int qt = (nq + kBM - 1) / kBM - 1 - L / p.B;  // heaviest (last) tile first
+  if (qt < 0) return;  // a packed sequence shorter than the longest
   const int q0 = qt * kBM, q1 = min(nq, q0 + kBM);
   const KeyBounds wg = key_bounds(q0, q1, off, 0, nk, p.window_left, p.window_right);
   if (wg.hi <= wg.lo) {
-    zero_rows<kThreads>(p.dq, p.g_bf16, b, h, nq, p.H, D, q0, q1, tid);
+    zero_rows<kThreads>(p.dq, p.g_bf16, sq.q_row0, h, p.H, D, q0, q1, tid);
     return;
   }
   const int wq0 = q0 + 32 * w, wq1 = min(nq, wq0 + 32);
@@ -832,7 +869,7 @@ void bwd_dq_kernel(BwdParams p) {
   // Q and dO of this lane's row: columns 16ks + 8h2 .. +7 (B operands).
   bf16x8_t qf[KS], gf[KS];
   {
-    const int64_t ro = (((int64_t)b * nq + min(row, nq - 1)) * p.H + h) * D + 8 * h2;
+    const int64_t ro = ((sq.q_row0 + min(row, nq - 1)) * p.H + h) * D + 8 * h2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4_t x = *(const u32x4_t*)((const uint16_t*)p.q + ro + 16 * ks);
@@ -851,7 +888,7 @@ void bwd_dq_kernel(BwdParams p) {
   // Contiguous K/V copies, as in the forward.
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int64_t row_bytes = 2 * (int64_t)p.H * D;
-  const int64_t bh_bytes = 2 * (((int64_t)b * nk * p.H + h) * D);
+  const int64_t bh_bytes = 2 * ((sq.k_row0 * p.H + h) * D);
   const int64_t end_bytes = (int64_t)(nk - 1) * row_bytes + 2 * D;
   const char* kbh = (const char*)p.k + bh_bytes;
   const char* vbh = (const char*)p.v + bh_bytes;
@@ -956,7 +993,7 @@ void bwd_dq_kernel(BwdParams p) {
   }
 
   if (row >= nq) return;
-  const int64_t base = (((int64_t)b * nq + row) * p.H + h) * D;
+  const int64_t base = ((sq.q_row0 + row) * p.H + h) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll

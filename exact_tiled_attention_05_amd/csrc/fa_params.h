@@ -49,14 +49,15 @@ struct CombineParams {
   int o_bf16;
 };
 
-// One backward launch (fa_bwd): gradients of the contiguous forward.
+// One backward launch (fa_bwd, fa_bwd_varlen): gradients of the forward over a
+// batched or a packed variable-length layout.
 struct BwdParams {
-  const void* q;            // [B, Nq, H, D] bf16
-  const void* k;            // [B, Nk, H, D] bf16
+  const void* q;            // [B, Nq, H, D] bf16, or packed [total_q, H, D]
+  const void* k;            // [B, Nk, H, D] bf16, or packed [total_k, H, D]
   const void* v;
-  const void* o;            // [B, Nq, H, D], fp32 or bf16 (o_bf16): the forward's output
-  const void* dout;         // [B, Nq, H, D] bf16
-  const float* lse;         // [B, H, Nq] the forward's log-sum-exp (natural log)
+  const void* o;            // like q, fp32 or bf16 (o_bf16): the forward's output
+  const void* dout;         // like q, bf16
+  const float* lse;         // [B, H, Nq] or packed [H, total_q]: the forward's log-sum-exp
   void* dq;                 // [B, Nq, H, D], fp32 or bf16 (g_bf16)
   void* dk;                 // [B, Nk, H, D]
   void* dv;
@@ -65,7 +66,10 @@ struct BwdParams {
                             // (32, 0 past Nq)
   int nblk;                 // ceil(Nq / 32)
   const float* alibi;       // [H] or nullptr
-  int B, H, Nq, Nk;
+  const int* cu_seqlens_q;  // [B + 1] packed batch offsets (fa_bwd_varlen), or nullptr
+  const int* cu_seqlens_k;  // [B + 1]
+  int B, H, Nq, Nk;         // packed: Nq, Nk are the maxima
+  int total_q, total_k;     // rows of the packed tensors
   int window_left, window_right;
   int o_bf16, g_bf16;
   int num_q_tiles, num_k_tiles;

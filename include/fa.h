@@ -291,6 +291,36 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 long long fa_bwd_workspace_bytes(int batch, int heads, int seqlen_q);
 
 /*
+ * fa_bwd_varlen - backward of fa_fwd_varlen: dQ, dK, dV of a packed batch of
+ * sequences of different lengths (variable sequence lengths: closing section
+ * of "FlashAttention深度解析：从算法创新到产业变革的全面影响"), each sequence
+ * differentiated on its own as fa_bwd differentiates one batch entry, with its
+ * mask and ALiBi distances aligned to its own bottom-right corner.
+ *
+ *   q, dout, o, dq [total_q, heads, head_dim]   rows of sequence b: [cu_seqlens_q[b], cu_seqlens_q[b+1])
+ *   k, v, dk, dv   [total_k, heads, head_dim]   rows of sequence b: [cu_seqlens_k[b], cu_seqlens_k[b+1])
+ *   lse            [heads, total_q] float32: fa_fwd_varlen's log-sum-exp
+ *   cu_seqlens_q/k device int32 [batch + 1], non-decreasing, starting at 0
+ *   workspace      fa_bwd_workspace_bytes(batch, heads, max_seqlen_q) bytes of
+ *                  caller-owned device memory; overwritten
+ *
+ * The offsets are clamped on the device as in fa_fwd_varlen, so every access
+ * stays inside the tensors; rows that no sequence owns, and rows of a
+ * sequence beyond max_seqlen_q (max_seqlen_k), are not written. A key seen by
+ * no query gets dK = dV = 0; a query with no key gets dQ = 0. With
+ * total_q = total_k = 0 nothing is launched; q, dout, o, lse, dq (k, v, dk,
+ * dv) may be NULL when total_q (total_k) is 0. Dtypes, rounding, determinism
+ * and errors as fa_bwd; sizes as fa_fwd_varlen.
+ */
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, int in_dtype, int o_dtype, void* dq, void* dk, void* dv,
+                  int grad_dtype, float* workspace, const int* cu_seqlens_q,
+                  const int* cu_seqlens_k, int batch, int heads, int total_q, int total_k,
+                  int max_seqlen_q, int max_seqlen_k, int head_dim, float softmax_scale,
+                  int causal, int window_left, int window_right, const float* alibi_slopes,
+                  float softcap, void* stream);
+
+/*
  * fa_splitkv_combine - the separate reduce step that merges split partials
  * (the update article's v2.2 entry): for every (b, h, i),
  *   L = ln(sum_s exp(lse_part[s])),  O = sum_s exp(lse_part[s] - L) * o_part[s].

@@ -271,6 +271,42 @@ def test_bwd_workspace_bytes():
     assert fa.fa_bwd_workspace_bytes(0, 1, 1) == -1
 
 
+def bwd_varlen(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, in_dtype=1, o_dtype=0, dq=FAKE,
+             dk=FAKE, dv=FAKE, g_dtype=0, ws=FAKE, cq=FAKE, ck=FAKE, batch=2, heads=2,
+             total_q=8, total_k=8, max_q=4, max_k=4, head_dim=128, scale=0.1, causal=1, wl=-1,
+             wr=-1, alibi=None, softcap=0.0, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_bwd_varlen(
+        a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["in_dtype"], a["o_dtype"], a["dq"],
+        a["dk"], a["dv"], a["g_dtype"], a["ws"], a["cq"], a["ck"], a["batch"], a["heads"],
+        a["total_q"], a["total_k"], a["max_q"], a["max_k"], a["head_dim"], a["scale"],
+        a["causal"], a["wl"], a["wr"], a["alibi"], a["softcap"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cq=None), NULL), (dict(ck=None), NULL), (dict(ws=None), NULL), (dict(q=None), NULL),
+    (dict(o=None), NULL), (dict(do=None), NULL), (dict(lse=None), NULL), (dict(dq=None), NULL),
+    (dict(k=None), NULL), (dict(v=None), NULL), (dict(dk=None), NULL), (dict(dv=None), NULL),
+    (dict(batch=0), SHAPE), (dict(heads=0), SHAPE), (dict(total_q=-1), SHAPE),
+    (dict(total_k=-1), SHAPE), (dict(max_q=0), SHAPE), (dict(max_k=-1), SHAPE),
+    (dict(max_q=(1 << 28) + 1), SHAPE),
+    (dict(in_dtype=0), UNSUP), (dict(head_dim=96), UNSUP), (dict(o_dtype=4), UNSUP),
+    (dict(g_dtype=2), UNSUP), (dict(causal=1, wr=2), MASK), (dict(wl=-3), MASK),
+    (dict(scale=0.0), VALUE), (dict(softcap=math.inf), VALUE),
+])
+def test_fa_bwd_varlen_rejects(kw, code):
+    assert bwd_varlen(**kw) == code
+
+
+def test_fa_bwd_varlen_empty_pack_launches_nothing():
+    # No row on either side: the call returns before any HIP call, and the
+    # tensors of zero rows may be NULL.
+    assert bwd_varlen(total_q=0, total_k=0, q=None, o=None, do=None, lse=None, dq=None, k=None,
+                      v=None, dk=None, dv=None) == OK
+    assert bwd_varlen(total_q=0, total_k=0, in_dtype=0) == UNSUP  # still validated
+
+
 def fp8(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, qd=1.0, kd=1.0, vd=1.0, o=FAKE, o_dtype=0, lse=None, batch=1,
              heads=1, seqlen_q=4, seqlen_k=4, head_dim=128, scale=0.125, causal=0, wl=-1, wr=-1,

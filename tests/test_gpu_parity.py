@@ -956,3 +956,153 @@ def test_bwd_many_heads():
         for got, ref, name in ((dq[0, :, h], rq, "dQ"), (dk[0, :, h], rk, "dK"), (dv[0, :, h], rv, "dV")):
             rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
             assert rel <= 1e-2, (h, name, rel)
+
+
+# --------------------------------------------------------------------------
+# Backward of packed batches (fa_bwd_varlen)
+# --------------------------------------------------------------------------
+VARLEN_BWD_CASES = [
+    # (d, H, [(nq, nk), ...], causal, wl, wr, alibi, cap)
+    (128, 2, [(1, 1), (17, 300), (128, 128), (129, 64), (300, 1000), (0, 5), (7, 0),
+              (255, 257)], True, -1, -1, False, 0.0),
+    (64, 3, [(64, 64), (130, 500), (1, 700), (200, 3), (33, 33), (0, 40)], True, 60, 0, True,
+     0.0),
+    (128, 2, [(100, 100), (250, 140), (3, 400), (0, 0)], False, -1, -1, True, 20.0),
+    (64, 2, [(129, 129), (40, 0), (90, 600)], False, 30, 30, False, 8.0),
+    (128, 1, [(300, 90), (1, 129), (129, 1)], True, -1, -1, False, 0.0),
+]
+
+
+def varlen_bwd_inputs(seed, lq, lk, H, d, amp):
+    q, k, v, cq, ck = W.gen_varlen(seed, lq, lk, H, d, amp, "bf16")
+    do = W.gen_tensor(seed, 3, 1, int(cq[-1]), H, d, 1.0, "bf16")[0]
+    return q, k, v, do, cq, ck
+
+
+def run_varlen_bwd(q, k, v, o, lse, do, cq, ck, maxq, maxk, scale, causal, wl, wr, slopes, cap,
+                   grad_dtype=torch.float32):
+    ts = None if slopes is None else torch.from_numpy(np.asarray(slopes, np.float32)).cuda()
+    g = fa.attention_varlen_backward(
+        to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+        torch.from_numpy(np.asarray(o, np.float32)).cuda(),
+        torch.from_numpy(np.asarray(lse, np.float32)).cuda(), to_dev(do, "bf16"),
+        torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda(), maxq, maxk, scale, causal, wl,
+        wr, ts, cap, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return [x.float().cpu().numpy() for x in g]
+
+
+def check_varlen_bwd(seed, lq, lk, H, d, causal, wl, wr, alibi, cap, what):
+    q, k, v, do, cq, ck = varlen_bwd_inputs(seed, lq, lk, H, d, 2.0 if cap else 1.0)
+    qf, kf, vf, gf = (W.to_float(x, "bf16") for x in (q, k, v, do))
+    slopes = W.alibi_slopes(H) if alibi else None
+    scale = 1.0 / np.sqrt(d)
+    ro, rl = O.attention_varlen_ref(qf, kf, vf, cq, ck, scale, causal, wl, wr, slopes, cap)
+    dq, dk, dv = run_varlen_bwd(q, k, v, ro, rl, do, cq, ck, max(int(max(lq)), 1),
+                                int(max(lk)), scale, causal, wl, wr, slopes, cap)
+    rq, rk, rv, bd = O.attention_varlen_bwd_ref(qf, kf, vf, gf, cq, ck, scale, causal, wl, wr,
+                                                slopes, cap, with_bounds=True)
+    return (check_grad(dq, rq, bd["dq"], what + " dQ", bd["dq_cancel"]),
+            check_grad(dk, rk, bd["dk"], what + " dK", bd["dk_cancel"]),
+            check_grad(dv, rv, bd["dv"], what + " dV"))
+
+
+@pytest.mark.parametrize("case", VARLEN_BWD_CASES)
+def test_varlen_bwd_packed_small(case):
+    """Packs with empty sequences (no query: dK = dV = 0; no key: dQ = 0),
+    Nq > Nk per sequence and every mask / score variant, against the oracle."""
+    d, H, lens, causal, wl, wr, alibi, cap = case
+    what = f"varlen bwd {case}"
+    say(what)
+    lq, lk = [a for a, _ in lens], [b for _, b in lens]
+    print(check_varlen_bwd(12000 + VARLEN_BWD_CASES.index(case), lq, lk, H, d, causal, wl, wr,
+                           alibi, cap, what))
+
+
+def test_varlen_bwd_equal_lengths_bitwise_equals_batched():
+    """A pack of equal-length sequences is the batched problem: the same
+    kernels compute the same tiles, so the gradients match fa_bwd bit for bit."""
+    B, nq, nk, H, d = 3, 200, 333, 4, 128
+    say("varlen bwd bitwise vs batched")
+    q, k, v, do = bwd_inputs(12100, B, nq, nk, H, d, 1.0)
+    tq, tk, tv, tg = (to_dev(x, "bf16") for x in (q, k, v, do))
+    ts = torch.from_numpy(W.alibi_slopes(H)).cuda()
+    o, lse = fa.attention(tq, tk, tv, 0.09, True, 100, 0, ts, 12.0)
+    gb = fa.attention_backward(tq, tk, tv, o, lse, tg, 0.09, True, 100, 0, ts, 12.0)
+    cq = torch.from_numpy(W.cu_seqlens([nq] * B)).cuda()
+    ck = torch.from_numpy(W.cu_seqlens([nk] * B)).cuda()
+    pk = lambda x, n: x.reshape(B * n, H, d)  # noqa: E731
+    gv = fa.attention_varlen_backward(
+        pk(tq, nq), pk(tk, nk), pk(tv, nk), pk(o, nq),
+        lse.permute(1, 0, 2).reshape(H, B * nq).contiguous(), pk(tg, nq), cq, ck, nq, nk, 0.09,
+        True, 100, 0, ts, 12.0)
+    torch.cuda.synchronize()
+    for a, b, n in zip(gb, gv, (nq, nk, nk)):
+        assert torch.equal(pk(a, n), b)
+
+
+def test_varlen_bwd_random_packs():
+    """Seeded random packs (0-300 rows per sequence, empty sequences included)
+    across head sizes and mask / score variants; bf16 gradients are the fp32
+    ones rounded."""
+    rng = np.random.default_rng(121)
+    for case in range(12):
+        d = (128, 64)[case % 2]
+        B = int(rng.integers(1, 6))
+        lq = rng.integers(0, 301, B)
+        lk = rng.integers(0, 301, B)
+        if case % 3 == 0:
+            lq[rng.integers(0, B)] = 0
+        if lq.sum() == 0:
+            lq[0] = 5
+        causal, wl, wr = [(True, -1, -1), (False, -1, -1), (True, 40, 0), (False, 17, 9)][(case // 2) % 4]
+        alibi, cap = case % 5 == 1, (6.0 if case % 7 == 3 else 0.0)
+        what = f"varlen bwd random {case}: d{d} lq{lq.tolist()} lk{lk.tolist()} {causal} {wl} {wr} {alibi} {cap}"
+        say(what)
+        check_varlen_bwd(12200 + case, lq.tolist(), lk.tolist(), 2, d, causal, wl, wr, alibi, cap,
+                         what)
+
+
+def test_varlen_bwd_deterministic_and_bf16_output():
+    lens = [300, 0, 77, 513]
+    q, k, v, do, cq, ck = varlen_bwd_inputs(12300, lens, [400, 10, 77, 513], 4, 128, 1.0)
+    tq, tk, tv, tg = (to_dev(x, "bf16") for x in (q, k, v, do))
+    tcq, tck = torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda()
+    say("varlen bwd determinism")
+    o, lse = fa.attention_varlen(tq, tk, tv, tcq, tck, 513, 513, 0.1, True)
+    a = fa.attention_varlen_backward(tq, tk, tv, o, lse, tg, tcq, tck, 513, 513, 0.1, True)
+    b = fa.attention_varlen_backward(tq, tk, tv, o, lse, tg, tcq, tck, 513, 513, 0.1, True)
+    c = fa.attention_varlen_backward(tq, tk, tv, o, lse, tg, tcq, tck, 513, 513, 0.1, True,
+                                     grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for x, y, z in zip(a, b, c):
+        assert torch.equal(x, y)
+        assert torch.equal(x.to(torch.bfloat16), z)
+
+
+def test_varlen_bwd_mixed_lengths_sampled_heads():
+    """Eight causal sequences of seeded lengths up to 2048 at the prefill head
+    shape (16 heads of 128), end to end from the GPU forward's O and LSE: two
+    heads of every sequence within 1e-2 of the oracle in relative norm."""
+    H, d = 16, 128
+    lens = W.varlen_lengths(91, 8, 2048)
+    say(f"varlen bwd mixed lengths {lens.tolist()}")
+    q, k, v, do, cq, ck = varlen_bwd_inputs(12400, lens, lens, H, d, 1.0)
+    tq, tk, tv, tg = (to_dev(x, "bf16") for x in (q, k, v, do))
+    tcq, tck = torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda()
+    n = int(lens.max())
+    scale = 1.0 / np.sqrt(d)
+    o, lse = fa.attention_varlen(tq, tk, tv, tcq, tck, n, n, scale, True)
+    dq, dk, dv = (x.cpu().numpy() for x in
+                  fa.attention_varlen_backward(tq, tk, tv, o, lse, tg, tcq, tck, n, n, scale, True))
+    assert not (np.isnan(dq).any() or np.isnan(dk).any() or np.isnan(dv).any())
+    assert np.array_equal(cq, ck)  # self-attention lengths: one row range per sequence
+    for b in range(len(lens)):
+        r = slice(int(cq[b]), int(cq[b + 1]))
+        for h in (b % H, (5 * b + 3) % H):
+            sl = lambda x: W.to_float(x[r, h], "bf16")  # noqa: E731
+            rq, rk, rv, _ = O.attention_bwd_bh(sl(q), sl(k), sl(v), sl(do), int(lens[b]), scale,
+                                               True)
+            for got, ref, name in ((dq[r, h], rq, "dQ"), (dk[r, h], rk, "dK"), (dv[r, h], rv, "dV")):
+                rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+                assert rel <= 1e-2, (b, h, name, rel)
