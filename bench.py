@@ -37,7 +37,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Source files each measured kernel is built from (a change voids its counters).
 KERNEL_SOURCES = {
     "prefill": ["fa_fwd_bf16.hip", "fa_lds.h", "fa_device.h", "fa_params.h"],
-    "decode_split": ["fa_decode_bf16.hip", "fa_device.h", "fa_params.h"],
+    "decode_split": ["fa_decode.hip", "fa_device.h", "fa_params.h"],
 }
 
 
@@ -440,6 +440,38 @@ def main():
                 "roofline": {"bound": "mfma", "achieved": round(f8_tflops, 3), "peak": PEAK_FP8_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(f8_tflops / PEAK_FP8_TFLOPS, 4)}}
 
+    # ---- paged decode over an E4M3 cache (side measurement): the decode pool above
+    # rounded to E4M3 on the device (input preparation, untimed; its NaN pages stay
+    # NaN), unit descales. Half the cache bytes of the bf16 decode.
+    dk8, dv8 = dk.to(torch.float8_e4m3fn), dv.to(torch.float8_e4m3fn)
+    f8_split_bytes = kv_bytes // 2 + dq.numel() * 2 + bt.size * 4 + part_bytes
+    f8_decode_bytes = f8_split_bytes + combine_bytes
+
+    def fp8_decode():
+        check(fa.fa_fwd_splitkv_fp8(dq, dk8, dv8, 1.0, 1.0, dbt, dbt.shape[1], wd.page_size, None,
+                                    o_part, lse_part, S, wd.B, wd.H, wd.Nq, wd.Nk, wd.d, wd.scale,
+                                    True, -1, -1, None, 0.0, stream), "fa_fwd_splitkv_fp8")
+        combine_pass()
+
+    for _ in range(args.warmup):
+        fp8_decode()
+    ev6 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for a, e in ev6:
+        a.record(stream)
+        fp8_decode()
+        e.record(stream)
+    torch.cuda.synchronize()
+    t_d8 = np.array([a.elapsed_time(e) for a, e in ev6]) * 1e-3
+    assert torch.isfinite(do).all()
+    del dk8, dv8
+    fp8_decode_line = {"workload": "paged_splitkv_decode over an E4M3 cache (fa_fwd_splitkv_fp8 + combine)",
+                       "gbytes": round(f8_decode_bytes / 1e9, 5), "ms": round(t_d8.mean() * 1e3, 5),
+                       "ms_median": round(float(np.median(t_d8)) * 1e3, 5),
+                       "gbs": round(f8_decode_bytes / t_d8.mean() / 1e9, 2),
+                       "pct_peak": round(100 * f8_decode_bytes / t_d8.mean() / 1e9 / PEAK_HBM_GBS, 2),
+                       "keys_per_s_vs_bf16": round(float((t_split + t_comb).mean() / t_d8.mean()), 3)}
+
     pre_tflops = prefill_flops / t_prefill.mean() / 1e12
     dec_time = (t_split + t_comb).mean()
     dec_gbs = decode_bytes / dec_time / 1e9
@@ -507,6 +539,7 @@ def main():
         "variable_lengths": variable,
         "backward": backward_line,
         "fp8_prefill": fp8_line,
+        "fp8_decode": fp8_decode_line,
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("prefill"),

@@ -24,11 +24,12 @@ import torch
 __all__ = [
     "FA_FP32", "FA_BF16", "FaError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
-    "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes",
-    "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len",
+    "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_splitkv_fp8", "fa_bwd",
+    "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
+    "fa_split_chunk_len",
     "attention", "attention_fp8", "attention_varlen", "attention_split", "attention_split_partials",
-    "attention_paged_splitkv", "attention_paged_append", "attention_backward",
-    "attention_varlen_backward", "combine", "decode_paged",
+    "attention_paged_splitkv", "attention_paged_splitkv_fp8", "attention_paged_append",
+    "attention_backward", "attention_varlen_backward", "combine", "decode_paged",
 ]
 
 FA_FP32, FA_BF16 = 0, 1
@@ -37,7 +38,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 _lib = None
 
 EXPORTED = ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
-            "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd",
+            "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_splitkv_fp8", "fa_bwd",
             "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len")
 
 
@@ -76,6 +77,9 @@ def load_library():
     lib.fa_fwd_splitkv_append.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, i, vp, i, i, i, i, i, f, i, i, i, vp, f, vp]
     lib.fa_fwd_fp8.restype = i
+    lib.fa_fwd_splitkv_fp8.argtypes = [vp, vp, vp, f, f, vp, i, i, vp, vp, vp, i, i, i, i, i, i,
+                                       f, i, i, i, vp, f, vp]
+    lib.fa_fwd_splitkv_fp8.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, i, vp, i, i, i, i, i, f, i,
                            i, i, vp, f, vp]
     lib.fa_bwd.restype = i
@@ -209,6 +213,20 @@ def fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, batch, heads, s
         float(v_descale), _ptr(o), _dtype_code(o), _ptr(lse), int(batch), int(heads),
         int(seqlen_q), int(seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)),
         int(window_left), int(window_right), _ptr(alibi_slopes), float(softcap), _stream(stream))
+
+
+def fa_fwd_splitkv_fp8(q, k_cache, v_cache, k_descale, v_descale, block_table,
+                       max_pages_per_seq, page_size, cache_seqlens, o_part, lse_part, num_splits,
+                       batch, heads, seqlen_q, seqlen_k, head_dim, softmax_scale, causal=False,
+                       window_left=-1, window_right=-1, alibi_slopes=None, softcap=0.0,
+                       stream=None) -> int:
+    """Call fa_fwd_splitkv_fp8 on caller-allocated tensors; returns the status code."""
+    return load_library().fa_fwd_splitkv_fp8(
+        _ptr(q), _ptr_fp8(k_cache), _ptr_fp8(v_cache), float(k_descale), float(v_descale),
+        _ptr(block_table), int(max_pages_per_seq), int(page_size), _ptr(cache_seqlens),
+        _ptr(o_part), _ptr(lse_part), int(num_splits), int(batch), int(heads), int(seqlen_q),
+        int(seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)), int(window_left),
+        int(window_right), _ptr(alibi_slopes), float(softcap), _stream(stream))
 
 
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, batch, heads, seqlen_q, seqlen_k,
@@ -379,6 +397,36 @@ def attention_paged_splitkv(q, k_cache, v_cache, block_table, seqlen_k, num_spli
                                       H, nq, seqlen_k, d, softmax_scale, causal, window_left,
                                       window_right, alibi_slopes, softcap, stream),
                "fa_fwd_splitkv_seqlens")
+    return o_part, lse_part
+
+
+def attention_paged_splitkv_fp8(q, k_cache, v_cache, k_descale, v_descale, block_table, seqlen_k,
+                                num_splits, softmax_scale=None, causal=False, window_left=-1,
+                                window_right=-1, alibi_slopes=None, softcap=0.0, stream=None,
+                                cache_seqlens=None):
+    """Split partials o_part [S,B,H,1,d] and lse_part [S,B,H,1] of one bf16 query row per
+    (b, h) over a paged cache of E4M3 codes [num_pages, page_size, H, d] (uint8 or
+    float8_e4m3fn) valued k_descale / v_descale times their decoded value."""
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bfloat16")
+    B, nq, H, d = q.shape
+    _, page_size, Hc, dc = k_cache.shape
+    if (Hc, dc) != (H, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache must be [num_pages, page_size, H, d] matching q")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages_per_seq]")
+    if cache_seqlens is not None and (cache_seqlens.dtype != torch.int32
+                                      or tuple(cache_seqlens.shape) != (B,)):
+        raise ValueError("cache_seqlens must be int32 [B]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    o_part = torch.empty((num_splits, B, H, nq, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((num_splits, B, H, nq), dtype=torch.float32, device=q.device)
+    _check(fa_fwd_splitkv_fp8(q, k_cache, v_cache, k_descale, v_descale, block_table,
+                              block_table.shape[1], page_size, cache_seqlens, o_part, lse_part,
+                              num_splits, B, H, nq, seqlen_k, d, softmax_scale, causal,
+                              window_left, window_right, alibi_slopes, softcap, stream),
+           "fa_fwd_splitkv_fp8")
     return o_part, lse_part
 
 

@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode_bf16.hip", "fa_combine.hip",
+HIP_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_combine.hip",
                "fa_bwd_bf16.hip", "fa_fwd_fp8.hip"]
 CPP_SOURCES = ["fa_api.cpp"]
 

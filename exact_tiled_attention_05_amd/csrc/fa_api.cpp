@@ -39,6 +39,18 @@ Launcher pick_f32(int head_dim, bool softcap, bool alibi) {
 #undef FA_PICK
 }
 
+// One query row per (batch, head) over an E4M3 cache.
+Launcher pick_decode_fp8(int head_dim, bool softcap, bool alibi) {
+#define FA_PICK_DEC8(D)                                                 \
+  if (softcap && alibi) return &fa::launch_decode_fp8<D, true, true>;   \
+  if (softcap) return &fa::launch_decode_fp8<D, true, false>;           \
+  if (alibi) return &fa::launch_decode_fp8<D, false, true>;             \
+  return &fa::launch_decode_fp8<D, false, false>;
+  if (head_dim == 64) { FA_PICK_DEC8(64) }
+  FA_PICK_DEC8(128)
+#undef FA_PICK_DEC8
+}
+
 // One query row per (batch, head): the split pass streams the cache with the
 // dedicated decode kernel.
 template <bool APPEND>
@@ -106,12 +118,15 @@ int64_t split_len(int seqlen_k, int num_splits, int page_size) {
 // fa_fwd_splitkv, fa_fwd_splitkv_seqlens and fa_fwd_splitkv_append
 // (seqlens_k = nullptr: every sequence holds seqlen_k keys; k_new = nullptr: no
 // append).
+// fp8_cache: k_cache / v_cache hold E4M3 codes valued k_descale / v_descale
+// times their decoded value (bf16 queries, one query row).
 int splitkv(const void* q, const void* k_cache, const void* v_cache, const void* k_new,
             const void* v_new, int in_dtype, const int* block_table, int max_pages_per_seq,
             int page_size, const int* seqlens_k,
             float* o_part, float* lse_part, int num_splits, int batch, int heads, int seqlen_q,
             int seqlen_k, int head_dim, float softmax_scale, int causal, int window_left,
-            int window_right, const float* alibi_slopes, float softcap, void* stream) {
+            int window_right, const float* alibi_slopes, float softcap, void* stream,
+            bool fp8_cache = false, float k_descale = 1.0f, float v_descale = 1.0f) {
   if (!q || !k_cache || !v_cache || !block_table || !o_part || !lse_part) return FA_ERR_NULL;
   int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
   if (st) return st;
@@ -122,11 +137,20 @@ int splitkv(const void* q, const void* k_cache, const void* v_cache, const void*
   if ((st = check_kind(in_dtype, head_dim))) return st;
   if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
     return st;
+  if (fp8_cache) {
+    if (in_dtype != FA_BF16 || seqlen_q != 1 || k_new) return FA_ERR_UNSUPPORTED;
+    for (float d : {k_descale, v_descale})
+      if (!(d > 0.0f) || !isfinite(d)) return FA_ERR_VALUE;
+    // K's descale scales every score, so it joins softmax_scale.
+    softmax_scale *= k_descale;
+    if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FA_ERR_VALUE;
+  }
 
   fa::FwdParams p = {};
   p.q = q;
   p.k = k_cache;
   p.v = v_cache;
+  p.v_descale = v_descale;
   p.o_part = o_part;
   p.lse_part = lse_part;
   p.block_table = block_table;
@@ -150,10 +174,11 @@ int splitkv(const void* q, const void* k_cache, const void* v_cache, const void*
   if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
 
   const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
-  Launcher fn = in_dtype != FA_BF16 ? pick_f32<true>(head_dim, sc, al)
-                : seqlen_q != 1     ? pick_bf16<fa::FWD_PAGED_SPLIT>(head_dim, sc, al)
-                : k_new             ? pick_decode<true>(head_dim, sc, al)
-                                    : pick_decode<false>(head_dim, sc, al);
+  Launcher fn = fp8_cache             ? pick_decode_fp8(head_dim, sc, al)
+                : in_dtype != FA_BF16 ? pick_f32<true>(head_dim, sc, al)
+                : seqlen_q != 1       ? pick_bf16<fa::FWD_PAGED_SPLIT>(head_dim, sc, al)
+                : k_new               ? pick_decode<true>(head_dim, sc, al)
+                                      : pick_decode<false>(head_dim, sc, al);
   return fn(p, stream) ? FA_ERR_HIP : FA_OK;
 }
 
@@ -329,6 +354,19 @@ int fa_fwd_splitkv(const void* q, const void* k_cache, const void* v_cache, int 
                  heads, seqlen_q, seqlen_k, head_dim, softmax_scale, causal, window_left,
                  window_right, alibi_slopes,
                  softcap, stream);
+}
+
+int fa_fwd_splitkv_fp8(const void* q, const void* k_cache, const void* v_cache,
+                       float k_descale, float v_descale, const int* block_table,
+                       int max_pages_per_seq, int page_size, const int* cache_seqlens,
+                       float* o_part, float* lse_part, int num_splits, int batch, int heads,
+                       int seqlen_q, int seqlen_k, int head_dim, float softmax_scale, int causal,
+                       int window_left, int window_right, const float* alibi_slopes,
+                       float softcap, void* stream) {
+  return splitkv(q, k_cache, v_cache, nullptr, nullptr, FA_BF16, block_table, max_pages_per_seq,
+                 page_size, cache_seqlens, o_part, lse_part, num_splits, batch, heads, seqlen_q,
+                 seqlen_k, head_dim, softmax_scale, causal, window_left, window_right,
+                 alibi_slopes, softcap, stream, true, k_descale, v_descale);
 }
 
 int fa_fwd_splitkv_seqlens(const void* q, const void* k_cache, const void* v_cache, int in_dtype,

@@ -4,17 +4,23 @@
 // for pages addressed through block_table; the inference article's point that
 // decode time goes to loading the cache when the query is one token).
 //
-// One workgroup of 4 wavefronts per (split, head, batch), head fastest. 16 lanes
-// (8 for head_dim 64) share one key row: each lane owns a 16-byte chunk of the
-// row, so a wavefront-wide load reads 4 (8) whole 256-byte (128-byte) rows. A
-// lane keeps 8 K and 8 V loads in flight per batch. Scores are reduced across
-// the row's lanes with DPP, and each lane runs an fp32 online softmax over its
-// group's keys for its 8 output columns. Groups, then wavefronts, are merged
-// by log-sum-exp at the end. With an append, this step's new keys are read
-// from k_new / v_new and written into their pages by one workgroup per
-// (batch, head) (the inference article's key-value cache, which keeps each
-// processed key for later steps).
+// One workgroup of 4 wavefronts per (split, head, batch), head fastest. Each
+// lane owns a 16-byte chunk of a key row (8 bf16 or 16 E4M3 columns), so
+// D / 8 (bf16) or D / 16 (E4M3) lanes share a row and a wavefront-wide load
+// reads several whole rows. A lane keeps 8 K and 8 V loads in flight per
+// batch. Scores are reduced across the row's lanes with DPP, and each lane
+// runs an fp32 online softmax over its group's keys for its output columns.
+// Groups, then wavefronts, are merged by log-sum-exp at the end. With an
+// append, this step's new keys are read from k_new / v_new and written into
+// their pages by one workgroup per (batch, head) (the inference article's
+// key-value cache, which keeps each processed key for later steps). An E4M3
+// cache (the FP8 forward support of the roadmap in "FlashAttention深度解析：
+// 从算法创新到产业变革的全面影响", applied to the stored keys and values) halves
+// the bytes per key; its codes are widened to fp32 in registers, K's descale
+// is folded into the score scale and V's into the output.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "fa_device.h"
 
@@ -38,13 +44,13 @@ __device__ __forceinline__ float dpp(float x) {
                                                                 0xf, 0xf, false));
 }
 
-// Sum over each group of CH consecutive lanes (CH = 8 or 16); every lane of the
-// group receives the sum.
+// Sum over each group of CH consecutive lanes (CH = 4, 8 or 16); every lane of
+// the group receives the sum.
 template <int CH>
 __device__ __forceinline__ float group_sum(float x) {
   x += dpp<0xB1>(x);   // quad_perm(1,0,3,2): swap neighbours
   x += dpp<0x4E>(x);   // quad_perm(2,3,0,1): swap pairs
-  x += dpp<0x141>(x);  // row_half_mirror: lane i <-> 7 - i within 8
+  if constexpr (CH >= 8) x += dpp<0x141>(x);   // row_half_mirror: lane i <-> 7 - i within 8
   if constexpr (CH == 16) x += dpp<0x140>(x);  // row_mirror: lane i <-> 15 - i within 16
   return x;
 }
@@ -52,11 +58,26 @@ __device__ __forceinline__ float group_sum(float x) {
 __device__ __forceinline__ float lo_bf16(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float hi_bf16(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+// The four E4M3 codes of a 32-bit word (byte i = column i) as floats; every
+// code converts exactly.
+__device__ __forceinline__ void e4m3x4_to_f32(unsigned w, float (&f)[4]) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
+}
+
 // APPEND: keys [n_cached, nk) are this step's new keys, read from k_new / v_new;
 // the split-0 workgroup of each (b, h) also copies them into their cache pages.
-template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
-__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
-  constexpr int CH = D / 8;       // lanes per key row
+// FP8: the cache holds E4M3 codes (no append).
+template <int D, bool SOFTCAP, bool ALIBI, bool APPEND, bool FP8>
+__device__ __forceinline__ void decode_body(const FwdParams& p) {
+  static_assert(!(FP8 && APPEND), "no append into an E4M3 cache");
+  using E = std::conditional_t<FP8, uint8_t, uint16_t>;  // cache element
+  constexpr int EPL = 16 / (int)sizeof(E);  // columns per lane: one 16-byte chunk
+  constexpr int CH = D / EPL;     // lanes per key row
   constexpr int KPI = 64 / CH;    // keys per wavefront-wide load
   constexpr int KPB = KPI * kU;   // keys per wavefront batch
   __shared__ float s_m[kWaves], s_l[kWaves];
@@ -94,24 +115,40 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
     for (int i = tid; i < np; i += kThreads) s_bt[i] = bt_row[p0 + i];
   __syncthreads();
 
-  const u32x4_t qv = *(const u32x4_t*)((const uint16_t*)p.q + q_offset(p, si, 0, h, D) + 8 * c);
+  // The lane's EPL query columns: bf16 pairs for the dot2 products with a bf16
+  // cache, floats for an E4M3 cache.
+  const uint16_t* qrow = (const uint16_t*)p.q + q_offset(p, si, 0, h, D) + EPL * c;
   bf16x2_t qp[4];
+  float qx[FP8 ? EPL : 1];
+  if constexpr (FP8) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const unsigned wq = qv[e];
-    qp[e] = as_bf16x2(wq);
+    for (int half = 0; half < 2; ++half) {
+      const u32x4_t qv = *(const u32x4_t*)(qrow + 8 * half);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qx[8 * half + 2 * e] = lo_bf16(qv[e]);
+        qx[8 * half + 2 * e + 1] = hi_bf16(qv[e]);
+      }
+    }
+  } else {
+    const u32x4_t qv = *(const u32x4_t*)qrow;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned wq = qv[e];
+      qp[e] = as_bf16x2(wq);
+    }
   }
   float slope_log2 = 0.0f;
   if constexpr (ALIBI) slope_log2 = p.alibi[h] * kLog2e;
 
-  float m = kNegInf, l = 0.0f, o[8];
+  float m = kNegInf, l = 0.0f, o[EPL];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+  for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
 
-  const uint16_t* kbase = (const uint16_t*)p.k + 8 * c;
-  const uint16_t* vbase = (const uint16_t*)p.v + 8 * c;
-  const uint16_t* knew = (const uint16_t*)p.k_new + 8 * c;
-  const uint16_t* vnew = (const uint16_t*)p.v_new + 8 * c;
+  const E* kbase = (const E*)p.k + EPL * c;
+  const E* vbase = (const E*)p.v + EPL * c;
+  const E* knew = (const E*)p.k_new + EPL * c;
+  const E* vnew = (const E*)p.v_new + EPL * c;
   for (int base = lo + w * KPB; base < hi; base += kWaves * KPB) {
     // Row offsets first, then every load back to back (no branches between
     // them). A key past the end re-reads key `lo`, whose page is real, and its
@@ -148,10 +185,22 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       float a = 0.0f;
+      if constexpr (FP8) {
+        float a2[2] = {0.0f, 0.0f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned wk = kx[u][e];
-        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wk), qp[e], a, false);
+        for (int e = 0; e < 4; ++e) {
+          float f[4];
+          e4m3x4_to_f32(kx[u][e], f);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a2[i & 1] = __builtin_fmaf(f[i], qx[4 * e + i], a2[i & 1]);
+        }
+        a = a2[0] + a2[1];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const unsigned wk = kx[u][e];
+          a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wk), qp[e], a, false);
+        }
       }
       a = group_sum<CH>(a);
       if constexpr (SOFTCAP) {
@@ -172,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
       const float alpha = fast_exp2(m - m_new);
       l *= alpha;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] *= alpha;
+      for (int e = 0; e < EPL; ++e) o[e] *= alpha;
       m = m_new;
     }
     const float bse = m == kNegInf ? 0.0f : m;
@@ -182,8 +231,15 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
       l += pu;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        o[2 * e] += pu * lo_bf16(vx[u][e]);
-        o[2 * e + 1] += pu * hi_bf16(vx[u][e]);
+        if constexpr (FP8) {
+          float f[4];
+          e4m3x4_to_f32(vx[u][e], f);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[4 * e + i] += pu * f[i];
+        } else {
+          o[2 * e] += pu * lo_bf16(vx[u][e]);
+          o[2 * e + 1] += pu * hi_bf16(vx[u][e]);
+        }
       }
     }
   }
@@ -198,12 +254,12 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
     const float a2 = m2 == kNegInf ? 0.0f : fast_exp2(m2 - mn);
     l = l * a1 + l2 * a2;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = o[e] * a1 + __shfl_xor(o[e], msk) * a2;
+    for (int e = 0; e < EPL; ++e) o[e] = o[e] * a1 + __shfl_xor(o[e], msk) * a2;
     m = mn;
   }
   if (g == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_o[w][8 * c + e] = o[e];
+    for (int e = 0; e < EPL; ++e) s_o[w][EPL * c + e] = o[e];
     if (c == 0) {
       s_m[w] = m;
       s_l[w] = l;
@@ -224,12 +280,32 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
       }
     }
     const int64_t ro = (((int64_t)s * p.B + b) * p.H + h) * p.Nq;
-    p.o_part[ro * D + tid] = L > 0.0f ? acc / L : 0.0f;
+    float out = L > 0.0f ? acc / L : 0.0f;
+    if constexpr (FP8) out *= p.v_descale;
+    p.o_part[ro * D + tid] = out;
     if (tid == 0) p.lse_part[ro] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
   }
 }
 
+template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
+  decode_body<D, SOFTCAP, ALIBI, APPEND, false>(p);
+}
+
+template <int D, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(kThreads) void decode_fp8_kernel(FwdParams p) {
+  decode_body<D, SOFTCAP, ALIBI, false, true>(p);
+}
+
 }  // namespace
+
+template <int D, bool SOFTCAP, bool ALIBI>
+int launch_decode_fp8(const FwdParams& p, void* stream) {
+  const int64_t groups = (int64_t)p.H * p.B * p.num_splits;
+  hipLaunchKernelGGL((decode_fp8_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)groups),
+                     dim3(kThreads), 0, (hipStream_t)stream, p);
+  return (int)hipGetLastError();
+}
 
 template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream) {
@@ -241,7 +317,8 @@ int launch_decode_bf16(const FwdParams& p, void* stream) {
 
 #define FA_INST(D, SC, AL) \
   template int launch_decode_bf16<D, SC, AL, false>(const FwdParams&, void*); \
-  template int launch_decode_bf16<D, SC, AL, true>(const FwdParams&, void*);
+  template int launch_decode_bf16<D, SC, AL, true>(const FwdParams&, void*); \
+  template int launch_decode_fp8<D, SC, AL>(const FwdParams&, void*);
 FA_INST(64, false, false)
 FA_INST(64, false, true)
 FA_INST(64, true, false)

@@ -95,6 +95,8 @@ template <bool SOFTCAP, bool ALIBI>
 int launch_fwd_fp8(const FwdParams& p, void* stream);  // head_dim 128
 template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream);
+template <int D, bool SOFTCAP, bool ALIBI>
+int launch_decode_fp8(const FwdParams& p, void* stream);  // E4M3 paged cache, one query row
 template <int D>
 int launch_combine(const CombineParams& p, void* stream);
 template <int D, bool SOFTCAP, bool ALIBI>

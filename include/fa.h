@@ -255,6 +255,33 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, flo
                void* stream);
 
 /*
+ * fa_fwd_splitkv_fp8 - fa_fwd_splitkv for one query row over a paged cache of
+ * E4M3 codes (the FP8 forward support of the roadmap in "FlashAttention深度
+ * 解析：从算法创新到产业变革的全面影响", applied to the stored keys and values
+ * of the decode step; paging and splits as the update article's v2.2 and v2.5
+ * entries). Half the bytes of a bf16 cache per key.
+ *
+ *   q                  [batch, 1, heads, head_dim] bf16
+ *   k_cache, v_cache   [num_pages, page_size, heads, head_dim] E4M3 codes (as
+ *                      fa_fwd_fp8), one byte per element
+ *   k_descale, v_descale  per-tensor factors: code x stands for
+ *                      descale * e4m3(x); finite and > 0 (FA_ERR_VALUE otherwise)
+ *   cache_seqlens      device int32 [batch] keys per sequence, or NULL for
+ *                      seqlen_k keys everywhere (as fa_fwd_splitkv_seqlens)
+ * The partials are fa_fwd_splitkv's for the dequantised cache, computed in fp32
+ * (the codes widen exactly; no rounding of the probabilities). seqlen_q must be
+ * 1 and head_dim 64 or 128 (FA_ERR_UNSUPPORTED otherwise). Other arguments,
+ * outputs and errors as fa_fwd_splitkv; merge with fa_splitkv_combine.
+ */
+int fa_fwd_splitkv_fp8(const void* q, const void* k_cache, const void* v_cache,
+                       float k_descale, float v_descale, const int* block_table,
+                       int max_pages_per_seq, int page_size, const int* cache_seqlens,
+                       float* o_part, float* lse_part, int num_splits, int batch, int heads,
+                       int seqlen_q, int seqlen_k, int head_dim, float softmax_scale, int causal,
+                       int window_left, int window_right, const float* alibi_slopes,
+                       float softcap, void* stream);
+
+/*
  * fa_bwd - backward pass of fa_fwd: dQ, dK, dV from dO, with the attention
  * probabilities recomputed from the forward's LSE (no Nq x Nk matrix is
  * stored; "IO感知技术革命: FlashAttention如何重塑大模型训练的经济学", tiling and

@@ -217,6 +217,30 @@ def test_fa_fwd_varlen_empty_pack_launches_nothing():
     assert varlen(total_q=0, total_k=0, q=None, o=None, k=None, v=None, max_k=0) == OK
 
 
+def split_fp8(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kd=1.0, vd=1.0, bt=FAKE, maxp=4, ps=16, sl=None, op=FAKE,
+             lp=FAKE, S=2, batch=1, heads=1, seqlen_q=1, nk=64, head_dim=128, scale=0.1, causal=1,
+             wl=-1, wr=-1, alibi=None, softcap=0.0, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_fwd_splitkv_fp8(
+        a["q"], a["k"], a["v"], a["kd"], a["vd"], a["bt"], a["maxp"], a["ps"], a["sl"], a["op"],
+        a["lp"], a["S"], a["batch"], a["heads"], a["seqlen_q"], a["nk"], a["head_dim"],
+        a["scale"], a["causal"], a["wl"], a["wr"], a["alibi"], a["softcap"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(bt=None), NULL),
+    (dict(op=None), NULL), (dict(lp=None), NULL),
+    (dict(S=0), SHAPE), (dict(batch=0), SHAPE), (dict(nk=0), SHAPE), (dict(maxp=3), SHAPE),
+    (dict(seqlen_q=2), UNSUP), (dict(head_dim=96), UNSUP),
+    (dict(kd=0.0), VALUE), (dict(vd=-1.0), VALUE), (dict(kd=math.inf), VALUE),
+    (dict(vd=math.nan), VALUE), (dict(kd=1e30, scale=1e30), VALUE), (dict(scale=0.0), VALUE),
+    (dict(causal=1, wr=2), MASK), (dict(softcap=-1.0), VALUE),
+])
+def test_fa_fwd_splitkv_fp8_rejects(kw, code):
+    assert split_fp8(**kw) == code
+
+
 def split_append(**kw):
     a = dict(q=FAKE, kn=FAKE, vn=FAKE, k=FAKE, v=FAKE, in_dtype=1, bt=FAKE, maxp=4, ps=16, sl=FAKE,
              op=FAKE, lp=FAKE, S=2, batch=1, heads=1, seqlen_q=1, max_k=64, head_dim=128,

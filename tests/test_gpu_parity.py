@@ -1106,3 +1106,80 @@ def test_varlen_bwd_mixed_lengths_sampled_heads():
             for got, ref, name in ((dq[r, h], rq, "dQ"), (dk[r, h], rk, "dK"), (dv[r, h], rv, "dV")):
                 rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
                 assert rel <= 1e-2, (b, h, name, rel)
+
+
+# --------------------------------------------------------------------------
+# Decode over an E4M3 paged cache (fa_fwd_splitkv_fp8)
+# --------------------------------------------------------------------------
+# The kernel widens the codes exactly and works in fp32 with unrounded
+# probabilities, as the bf16 decode does, so O is held to the fp32 bound after
+# dividing by V's descale (the output scales with it), and LSE to the usual one.
+FP8_DECODE_CASES = [
+    # (d, H, max_k, page_size, num_splits, seqlens or None, causal, wl, wr, alibi, cap, kd, vd)
+    (128, 2, 1000, 64, 4, [1000, 0, 1, 513, 64, 999], True, -1, -1, False, 0.0, 1.0, 1.0),
+    (64, 3, 777, 16, 16, [777, 5, 300, 0], True, 100, 0, True, 0.0, 0.5, 2.0),
+    (128, 2, 4096, 256, 16, None, True, -1, -1, True, 30.0, 0.25, 0.125),
+    (128, 2, 300, 7, 3, [300, 4, 0, 150], True, 50, 0, False, 10.0, 1.0, 1.0),
+    (64, 2, 500, 32, 5, None, False, -1, -1, False, 0.0, 3.0, 1.0),
+    (128, 1, 2000, 128, 7, [2000, 1999, 1000], False, 300, 40, True, 0.0, 0.75, 0.5),
+]
+
+
+def fp8_decode_case(case, seed, B=None):
+    d, H, nk, ps, S, seqlens, causal, wl, wr, alibi, cap, kd, vd = case
+    B = len(seqlens) if seqlens else (B or 3)
+    w = W.Workload(0, "fp8_decode", B=B, H=H, Nq=1, Nk=nk, d=d, dtype="fp8", causal=causal,
+                   paged=True, page_size=ps, pool_factor=1.3, num_splits=S, seed=seed)
+    q, kc, vc, bt = W.gen_paged(w, seqlens=seqlens)
+    slopes = W.alibi_slopes(H) if alibi else None
+    ts = None if slopes is None else torch.from_numpy(slopes).cuda()
+    tsl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32).cuda()
+    scale = 1.0 / np.sqrt(d)
+    o_part, lse_part = fa.attention_paged_splitkv_fp8(
+        to_dev(q, "bf16"), torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda(), kd, vd,
+        torch.from_numpy(bt).cuda(), nk, S, scale, causal, wl, wr, ts, cap, cache_seqlens=tsl)
+    o, lse = fa.combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    return w, q, kc, vc, bt, slopes, scale, o_part.cpu().numpy(), lse_part.cpu().numpy(), \
+        o.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", FP8_DECODE_CASES)
+def test_fp8_decode_small(case):
+    d, H, nk, ps, S, seqlens, causal, wl, wr, alibi, cap, kd, vd = case
+    say(f"fp8 decode {case}")
+    w, q, kc, vc, bt, slopes, scale, op, lp, o, lse = fp8_decode_case(
+        case, 13000 + FP8_DECODE_CASES.index(case))
+    lens = seqlens or [nk] * w.B
+    kf, vf = W.to_float(kc, "fp8") * kd, W.to_float(vc, "fp8") * vd
+    k = np.zeros((w.B, nk, H, d))
+    v = np.zeros((w.B, nk, H, d))
+    for b, n in enumerate(lens):
+        k[b, :n] = O.paged_gather_ref(kf, bt, b, n)
+        v[b, :n] = O.paged_gather_ref(vf, bt, b, n)
+    rop, rlp = O.splitkv_ref(W.to_float(q, "bf16"), k, v, S, ps, scale, causal, wl, wr, slopes,
+                             cap, seqlens_k=seqlens)
+    check(op / vd, lp, rop / vd, rlp, "fp32", "partials")
+    ro, rl = O.combine_ref(rop, rlp)
+    check(o.transpose(0, 2, 1, 3) / vd, lse, ro / vd, rl, "fp32", "combined")
+
+
+def test_fp8_decode_long_cache_sampled():
+    """32768 keys per sequence in 256-key pages, 16 splits, head_dim 128:
+    sampled (b, h) pairs against the oracle; no NaN from the poisoned pool."""
+    case = (128, 4, 32768, 256, 16, [32768, 20000, 1, 0], True, -1, -1, False, 0.0, 0.5, 0.25)
+    say("fp8 decode long cache")
+    w, q, kc, vc, bt, slopes, scale, op, lp, o, lse = fp8_decode_case(case, 13100)
+    assert not np.isnan(op).any() and not np.isnan(o).any()
+    kd, vd = 0.5, 0.25
+    for b, h in [(0, 0), (0, 3), (1, 2), (2, 1), (3, 1)]:
+        n = case[5][b]
+        qf = W.to_float(q[b, :, h], "bf16")
+        k = np.zeros((1, w.Nk, 1, w.d))
+        v = np.zeros((1, w.Nk, 1, w.d))
+        k[0, :n, 0] = O.paged_gather_ref(W.to_float(kc[:, :, h:h + 1], "fp8") * kd, bt, b, n)[:, 0]
+        v[0, :n, 0] = O.paged_gather_ref(W.to_float(vc[:, :, h:h + 1], "fp8") * vd, bt, b, n)[:, 0]
+        rop, rlp = O.splitkv_ref(qf[None, :, None], k, v, w.num_splits, w.page_size, scale, True,
+                                 seqlens_k=[n])
+        check(op[:, b:b + 1, h:h + 1] / vd, lp[:, b:b + 1, h:h + 1], rop / vd, rlp, "fp32",
+              f"partials b{b} h{h}")

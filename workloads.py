@@ -57,6 +57,7 @@ def to_float(x: np.ndarray, dtype: str) -> np.ndarray:
 # largest finite 448, smallest subnormal 2^-9)
 # --------------------------------------------------------------------------
 E4M3_MAX = 448.0
+E4M3_NAN_BITS = 0x7F
 
 
 def e4m3_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -218,14 +219,17 @@ def gen_paged(w: Workload, poison_unused: bool = True, seqlens=None):
     Every sequence holds pages for w.Nk keys. With `seqlens`, sequence b stores
     only its first seqlens[b] keys (the first seqlens[b] rows of the same
     slices). With poison_unused, every pool row that holds no stored key (pages
-    no sequence references, and rows past a sequence's length) is bf16 NaN (or
-    float32 NaN), so a wrong gather or a read past a length shows up as NaN.
+    no sequence references, and rows past a sequence's length) is NaN (bf16,
+    float32 or the E4M3 NaN code), so a wrong gather or a read past a length
+    shows up as NaN. For w.dtype "fp8" the pool holds E4M3 codes and Q is bf16.
     """
-    q = gen_tensor(w.seed, TENSOR_Q, w.B, w.Nq, w.H, w.d, w.amp, w.dtype)
+    # An E4M3 cache ("fp8") is read with bf16 queries.
+    q = gen_tensor(w.seed, TENSOR_Q, w.B, w.Nq, w.H, w.d, w.amp,
+                   "bf16" if w.dtype == "fp8" else w.dtype)
     bt = gen_block_table(w.table_seed, w.B, w.pages_per_seq, w.pool_pages)
-    st = np.uint16 if w.dtype == "bf16" else np.float32
+    st = {"bf16": np.uint16, "fp8": np.uint8}.get(w.dtype, np.float32)
     shape = (w.pool_pages, w.page_size, w.H, w.d)
-    nan = BF16_NAN_BITS if w.dtype == "bf16" else np.float32("nan")
+    nan = {"bf16": BF16_NAN_BITS, "fp8": E4M3_NAN_BITS}.get(w.dtype, np.float32("nan"))
     kc = np.full(shape, nan if poison_unused else 0, dtype=st)
     vc = np.full(shape, nan if poison_unused else 0, dtype=st)
     for b in range(w.B):
