@@ -69,29 +69,51 @@ __device__ __forceinline__ void e4m3x4_to_f32(unsigned w, float (&f)[4]) {
   f[3] = hi[1];
 }
 
+// Heads per workgroup: a key's rows of G adjacent heads are contiguous in a
+// page, so G heads together make a 256-byte segment per key (one head when its
+// row alone is 256 bytes).
+template <int D, int ESIZE>
+struct DecodeGroup {
+  static constexpr int EPL = 16 / ESIZE;  // columns per lane: one 16-byte chunk
+  static constexpr int CH = D / EPL;      // lanes per head row
+  static constexpr int G = CH >= 16 ? 1 : 16 / CH;
+};
+
 // APPEND: keys [n_cached, nk) are this step's new keys, read from k_new / v_new;
-// the split-0 workgroup of each (b, h) also copies them into their cache pages.
-// FP8: the cache holds E4M3 codes (no append).
+// the split-0 workgroup of each (b, head group) also copies them into their
+// cache pages. FP8: the cache holds E4M3 codes (no append).
 template <int D, bool SOFTCAP, bool ALIBI, bool APPEND, bool FP8>
 __device__ __forceinline__ void decode_body(const FwdParams& p) {
   static_assert(!(FP8 && APPEND), "no append into an E4M3 cache");
   using E = std::conditional_t<FP8, uint8_t, uint16_t>;  // cache element
-  constexpr int EPL = 16 / (int)sizeof(E);  // columns per lane: one 16-byte chunk
-  constexpr int CH = D / EPL;     // lanes per key row
-  constexpr int KPI = 64 / CH;    // keys per wavefront-wide load
+  using DG = DecodeGroup<D, (int)sizeof(E)>;
+  constexpr int EPL = DG::EPL;
+  constexpr int CH = DG::CH;      // lanes per head row
+  constexpr int G = DG::G;        // heads per workgroup
+  constexpr int LPK = CH * G;     // lanes per key (its G head rows)
+  constexpr int KPI = 64 / LPK;   // keys per wavefront-wide load
   constexpr int KPB = KPI * kU;   // keys per wavefront batch
-  __shared__ float s_m[kWaves], s_l[kWaves];
-  __shared__ float s_o[kWaves][D];
+  __shared__ float s_m[kWaves][G], s_l[kWaves][G];
+  __shared__ float s_o[kWaves][G * D];
   __shared__ int s_bt[kTablePages];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int c = lane % CH, g = lane / CH;
-  const WorkItem wi = decode_work<true>(p);
-  const int b = wi.b, h = wi.h, s = wi.s;
-  const SeqInfo si = seq_info(p, b, h);
+  const int ck = lane % LPK, g = lane / LPK;  // chunk of the key's segment, key group
+  const int hg = ck / CH, c = ck % CH;        // head in the group, chunk of its row
+  // Workgroup id: head group fastest, then batch, then split.
+  int wid = blockIdx.x;
+  const int HG = (p.H + G - 1) / G;
+  const int h0 = G * (wid % HG);  // first head of the group
+  wid /= HG;
+  const int b = wid % p.B, s = wid / p.B;
+  // A group past the last head repeats the last head and writes nothing for it.
+  const int h = min(h0 + hg, p.H - 1);
+  const SeqInfo si = seq_info(p, b, h0);
   const int nk = si.nk;
   if constexpr (APPEND) {
-    if (s == 0) append_rows<uint16_t>(p, si, b, h, D, tid, kThreads);
+    if (s == 0)
+      for (int j = 0; j < G && h0 + j < p.H; ++j)
+        append_rows<uint16_t>(p, si, b, h0 + j, D, tid, kThreads);
   }
 
   int slo, shi;
@@ -101,7 +123,8 @@ __device__ __forceinline__ void decode_body(const FwdParams& p) {
   if (p.window_left >= 0) lo = max(lo, ip - p.window_left);
   if (p.window_right >= 0) hi = min(hi, ip + p.window_right + 1);
   if (hi <= lo) {
-    write_empty_rows<true>(p, si, b, h, s, 0, 1, D, tid, kThreads);
+    for (int j = 0; j < G && h0 + j < p.H; ++j)
+      write_empty_rows<true>(p, si, b, h0 + j, s, 0, 1, D, tid, kThreads);
     return;
   }
 
@@ -145,10 +168,11 @@ __device__ __forceinline__ void decode_body(const FwdParams& p) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
 
-  const E* kbase = (const E*)p.k + EPL * c;
-  const E* vbase = (const E*)p.v + EPL * c;
-  const E* knew = (const E*)p.k_new + EPL * c;
-  const E* vnew = (const E*)p.v_new + EPL * c;
+  const int lane_col = h * D + EPL * c;  // the lane's 16 bytes of a key's row
+  const E* kbase = (const E*)p.k + lane_col;
+  const E* vbase = (const E*)p.v + lane_col;
+  const E* knew = (const E*)p.k_new + lane_col;
+  const E* vnew = (const E*)p.v_new + lane_col;
   for (int base = lo + w * KPB; base < hi; base += kWaves * KPB) {
     // Row offsets first, then every load back to back (no branches between
     // them). A key past the end re-reads key `lo`, whose page is real, and its
@@ -168,11 +192,11 @@ __device__ __forceinline__ void decode_body(const FwdParams& p) {
         slot = tt - idx * p.page_size;
       }
       const int page = table_in_lds ? s_bt[idx - p0] : bt_row[idx];
-      off[u] = (int64_t)page * p.page_stride + slot * p.row_stride + h * D;
+      off[u] = (int64_t)page * p.page_stride + slot * p.row_stride;
       fresh[u] = false;
       if constexpr (APPEND) {
         fresh[u] = tt >= si.n_cached;
-        if (fresh[u]) off[u] = new_key_offset(p, si, b, tt, h, D);
+        if (fresh[u]) off[u] = new_key_offset(p, si, b, tt, 0, D);
       }
     }
     u32x4_t kx[kU], vx[kU];
@@ -246,7 +270,7 @@ __device__ __forceinline__ void decode_body(const FwdParams& p) {
 
   // Merge the KPI lane groups of this wavefront (same columns, different keys).
 #pragma unroll
-  for (int msk = CH; msk < 64; msk <<= 1) {
+  for (int msk = LPK; msk < 64; msk <<= 1) {
     const float m2 = __shfl_xor(m, msk);
     const float l2 = __shfl_xor(l, msk);
     const float mn = fmaxf(m, m2);
@@ -259,31 +283,33 @@ __device__ __forceinline__ void decode_body(const FwdParams& p) {
   }
   if (g == 0) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) s_o[w][EPL * c + e] = o[e];
+    for (int e = 0; e < EPL; ++e) s_o[w][D * hg + EPL * c + e] = o[e];
     if (c == 0) {
-      s_m[w] = m;
-      s_l[w] = l;
+      s_m[w][hg] = m;
+      s_l[w][hg] = l;
     }
   }
   __syncthreads();
-  if (tid < D) {
+  static_assert(G * D <= kThreads, "one output column per thread");
+  const int oh = tid / D, col = tid % D;  // head in the group, column
+  if (tid < G * D && h0 + oh < p.H) {
     float M = kNegInf;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) M = fmaxf(M, s_m[i]);
+    for (int i = 0; i < kWaves; ++i) M = fmaxf(M, s_m[i][oh]);
     float L = 0.0f, acc = 0.0f;
     if (M != kNegInf) {
 #pragma unroll
       for (int i = 0; i < kWaves; ++i) {
-        const float a = s_m[i] == kNegInf ? 0.0f : fast_exp2(s_m[i] - M);
-        L += a * s_l[i];
+        const float a = s_m[i][oh] == kNegInf ? 0.0f : fast_exp2(s_m[i][oh] - M);
+        L += a * s_l[i][oh];
         acc += a * s_o[i][tid];
       }
     }
-    const int64_t ro = (((int64_t)s * p.B + b) * p.H + h) * p.Nq;
+    const int64_t ro = (((int64_t)s * p.B + b) * p.H + h0 + oh) * p.Nq;
     float out = L > 0.0f ? acc / L : 0.0f;
     if constexpr (FP8) out *= p.v_descale;
-    p.o_part[ro * D + tid] = out;
-    if (tid == 0) p.lse_part[ro] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
+    p.o_part[ro * D + col] = out;
+    if (col == 0) p.lse_part[ro] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
   }
 }
 
@@ -297,11 +323,18 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(FwdParams p) {
   decode_body<D, SOFTCAP, ALIBI, false, true>(p);
 }
 
+// Workgroups of a decode launch: (head group, batch, split).
+template <int D, int ESIZE>
+int64_t decode_groups(const FwdParams& p) {
+  constexpr int G = DecodeGroup<D, ESIZE>::G;
+  return (int64_t)((p.H + G - 1) / G) * p.B * p.num_splits;
+}
+
 }  // namespace
 
 template <int D, bool SOFTCAP, bool ALIBI>
 int launch_decode_fp8(const FwdParams& p, void* stream) {
-  const int64_t groups = (int64_t)p.H * p.B * p.num_splits;
+  const int64_t groups = decode_groups<D, 1>(p);
   hipLaunchKernelGGL((decode_fp8_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)groups),
                      dim3(kThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
@@ -309,7 +342,7 @@ int launch_decode_fp8(const FwdParams& p, void* stream) {
 
 template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream) {
-  const int64_t groups = (int64_t)p.H * p.B * p.num_splits;
+  const int64_t groups = decode_groups<D, 2>(p);
   hipLaunchKernelGGL((decode_bf16_kernel<D, SOFTCAP, ALIBI, APPEND>), dim3((unsigned)groups),
                      dim3(kThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
