@@ -1183,3 +1183,40 @@ def test_fp8_decode_long_cache_sampled():
                                  seqlens_k=[n])
         check(op[:, b:b + 1, h:h + 1] / vd, lp[:, b:b + 1, h:h + 1], rop / vd, rlp, "fp32",
               f"partials b{b} h{h}")
+
+
+def test_fp8_decode_every_code():
+    """A cache whose keys and values cycle through all 254 finite E4M3 codes
+    (subnormals, +-0 and +-448 included), read with small descales so the scores
+    stay moderate: the kernel's widening of every code matches the oracle's."""
+    d, H, nk, ps, S = 128, 2, 1024, 64, 4
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    assert len(codes) == 254
+    rng = np.random.default_rng(13200)
+    B = 2
+    pages = nk // ps
+    pool = B * pages + 3
+    kc = np.full((pool, ps, H, d), W.E4M3_NAN_BITS, dtype=np.uint8)
+    vc = np.full((pool, ps, H, d), W.E4M3_NAN_BITS, dtype=np.uint8)
+    bt = rng.permutation(pool)[: B * pages].reshape(B, pages).astype(np.int32)
+    for b in range(B):
+        for h in range(H):
+            ks = codes[(np.arange(nk * d) * 7 + 31 * b + 5 * h) % 254].reshape(nk, d)
+            vs = codes[(np.arange(nk * d) * 11 + 17 * b + 3 * h) % 254].reshape(nk, d)
+            W.scatter_pages(kc, bt, b, h, ks, ps)
+            W.scatter_pages(vc, bt, b, h, vs, ps)
+    q = W.gen_tensor(13201, W.TENSOR_Q, B, 1, H, d, 1.0, "bf16")
+    kd, vd = 2.0 ** -10, 2.0 ** -6
+    scale = 1.0 / np.sqrt(d)
+    say("fp8 decode every code")
+    o_part, lse_part = fa.attention_paged_splitkv_fp8(
+        to_dev(q, "bf16"), torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda(), kd, vd,
+        torch.from_numpy(bt).cuda(), nk, S, scale, True)
+    torch.cuda.synchronize()
+    k = np.stack([O.paged_gather_ref(W.to_float(kc, "fp8") * kd, bt, b, nk) for b in range(B)])
+    v = np.stack([O.paged_gather_ref(W.to_float(vc, "fp8") * vd, bt, b, nk) for b in range(B)])
+    rop, rlp = O.splitkv_ref(W.to_float(q, "bf16"), k, v, S, ps, scale, True)
+    # fp32 arithmetic on values up to 448 vd: the bound is relative to max|v|.
+    vmax = float(np.abs(v).max())
+    assert vmax == 448.0 * vd
+    check(o_part.cpu().numpy() / vmax, lse_part.cpu().numpy(), rop / vmax, rlp, "fp32", "every code")
