@@ -472,6 +472,66 @@ def main():
                        "pct_peak": round(100 * f8_decode_bytes / t_d8.mean() / 1e9 / PEAK_HBM_GBS, 2),
                        "keys_per_s_vs_bf16": round(float((t_split + t_comb).mean() / t_d8.mean()), 3)}
 
+    # ---- one decode step of a small serving batch (side measurement): append of
+    # the step's key and value, split pass and combine for 1 sequence of 4096
+    # cached keys (32 heads, 256-key pages, the split count fa_num_splits picks),
+    # 100 steps back to back, eager against a HIP graph of the step replayed.
+    gw = W.Workload(0, "serving_step", B=1, H=32, Nq=1, Nk=4097, d=128, dtype="bf16",
+                    causal=True, paged=True, page_size=256, pool_factor=1.0, num_splits=4,
+                    seed=wd.seed)
+    gq_np, gk_np, gv_np, gbt_np = W.gen_paged(gw, seqlens=[4096])
+    gq, gk, gv = up(gq_np, "bf16"), up(gk_np, "bf16"), up(gv_np, "bf16")
+    gkn = up(W.gen_tensor(gw.seed, W.TENSOR_K, 1, 1, gw.H, gw.d, 1.0, "bf16"), "bf16")
+    gvn = up(W.gen_tensor(gw.seed, W.TENSOR_V, 1, 1, gw.H, gw.d, 1.0, "bf16"), "bf16")
+    gbt = torch.from_numpy(gbt_np).to(dev)
+    gsl = torch.full((1,), 4096, dtype=torch.int32, device=dev)
+    GS = fa.fa_num_splits(1, gw.H, 1, gw.Nk, gw.d, gw.page_size)
+    gop = torch.empty((GS, 1, gw.H, 1, gw.d), dtype=torch.float32, device=dev)
+    glp = torch.empty((GS, 1, gw.H, 1), dtype=torch.float32, device=dev)
+    go = torch.empty((1, 1, gw.H, gw.d), dtype=torch.bfloat16, device=dev)
+    glse = torch.empty((1, gw.H, 1), dtype=torch.float32, device=dev)
+    gstream = torch.cuda.Stream()  # capture needs a stream other than the default one
+
+    def serving_step():
+        check(fa.fa_fwd_splitkv_append(gq, gkn, gvn, gk, gv, gbt, gbt.shape[1], gw.page_size, gsl,
+                                       gop, glp, GS, 1, gw.H, 1, gw.Nk, gw.d, gw.scale, True,
+                                       stream=gstream), "fa_fwd_splitkv_append")
+        check(fa.fa_splitkv_combine(gop, glp, GS, 1, gw.H, 1, gw.d, go, glse, gstream),
+              "fa_splitkv_combine")
+
+    n_steps = 100
+    for _ in range(3):
+        serving_step()
+    torch.cuda.synchronize()
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(gstream)
+    for _ in range(n_steps):
+        serving_step()
+    e.record(gstream)
+    torch.cuda.synchronize()
+    t_eager = a.elapsed_time(e) * 1e-3 / n_steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gstream):
+        serving_step()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(gstream):
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        a.record(gstream)
+        for _ in range(n_steps):
+            graph.replay()
+        e.record(gstream)
+    torch.cuda.synchronize()
+    t_graph = a.elapsed_time(e) * 1e-3 / n_steps
+    assert torch.isfinite(go.float()).all()
+    serving_line = {"workload": "decode step with a cache append, 1 sequence x 32 heads, 4097 keys "
+                                "(fa_fwd_splitkv_append + fa_splitkv_combine)",
+                    "num_splits": GS, "steps": n_steps,
+                    "eager_us_per_step": round(t_eager * 1e6, 2),
+                    "hip_graph_us_per_step": round(t_graph * 1e6, 2)}
+    del graph
+
     pre_tflops = prefill_flops / t_prefill.mean() / 1e12
     dec_time = (t_split + t_comb).mean()
     dec_gbs = decode_bytes / dec_time / 1e9
@@ -540,6 +600,7 @@ def main():
         "backward": backward_line,
         "fp8_prefill": fp8_line,
         "fp8_decode": fp8_decode_line,
+        "serving_step": serving_line,
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("prefill"),

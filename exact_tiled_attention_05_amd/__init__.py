@@ -26,7 +26,7 @@ __all__ = [
     "fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
     "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_splitkv_fp8", "fa_bwd",
     "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
-    "fa_split_chunk_len",
+    "fa_split_chunk_len", "fa_num_splits",
     "attention", "attention_fp8", "attention_varlen", "attention_split", "attention_split_partials",
     "attention_paged_splitkv", "attention_paged_splitkv_fp8", "attention_paged_append",
     "attention_backward", "attention_varlen_backward", "combine", "decode_paged",
@@ -34,12 +34,14 @@ __all__ = [
 
 FA_FP32, FA_BF16 = 0, 1
 FA_OK = 0
+FA_ERR_SHAPE = 2
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 _lib = None
 
 EXPORTED = ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
             "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_splitkv_fp8", "fa_bwd",
-            "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string", "fa_split_chunk_len")
+            "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
+            "fa_split_chunk_len", "fa_num_splits")
 
 
 class FaError(RuntimeError):
@@ -97,6 +99,8 @@ def load_library():
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_split_chunk_len.argtypes = [i, i, i]
     lib.fa_split_chunk_len.restype = i
+    lib.fa_num_splits.argtypes = [i, i, i, i, i, i, i, i]
+    lib.fa_num_splits.restype = i
     _lib = lib
     return lib
 
@@ -140,6 +144,23 @@ def _check(status: int, where: str):
 # --------------------------------------------------------------------------
 def fa_status_string(status: int) -> str:
     return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_num_splits(batch: int, heads: int, seqlen_q: int, seqlen_k: int, head_dim: int,
+                  page_size: int = 64, fp8_cache: bool = False, num_cus: int = 0) -> int:
+    """Split count for the split passes (fa_num_splits); -1 on bad sizes."""
+    return int(load_library().fa_num_splits(int(batch), int(heads), int(seqlen_q), int(seqlen_k),
+                                            int(head_dim), int(page_size), int(bool(fp8_cache)),
+                                            int(num_cus)))
+
+
+def _splits(num_splits, *args, **kw) -> int:
+    if num_splits is not None:
+        return int(num_splits)
+    s = fa_num_splits(*args, **kw)
+    if s <= 0:
+        raise FaError(FA_ERR_SHAPE, "fa_num_splits")
+    return s
 
 
 def fa_split_chunk_len(seqlen_k: int, num_splits: int, page_size: int) -> int:
@@ -365,10 +386,11 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seql
     return o, lse
 
 
-def attention_paged_splitkv(q, k_cache, v_cache, block_table, seqlen_k, num_splits,
+def attention_paged_splitkv(q, k_cache, v_cache, block_table, seqlen_k, num_splits=None,
                             softmax_scale=None, causal=False, window_left=-1, window_right=-1,
                             alibi_slopes=None, softcap=0.0, stream=None, cache_seqlens=None):
-    """Split partials o_part [S,B,H,Nq,d] and lse_part [S,B,H,Nq] over a paged cache.
+    """Split partials o_part [S,B,H,Nq,d] and lse_part [S,B,H,Nq] over a paged cache
+    (num_splits None: fa_num_splits' choice for the current device).
 
     With cache_seqlens (int32 [B] on the device), sequence b uses its first
     cache_seqlens[b] keys and seqlen_k is the maximum length.
@@ -382,6 +404,7 @@ def attention_paged_splitkv(q, k_cache, v_cache, block_table, seqlen_k, num_spli
         raise ValueError("block_table must be int32 [B, max_pages_per_seq]")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
+    num_splits = _splits(num_splits, B, H, nq, seqlen_k, d, page_size)
     o_part = torch.empty((num_splits, B, H, nq, d), dtype=torch.float32, device=q.device)
     lse_part = torch.empty((num_splits, B, H, nq), dtype=torch.float32, device=q.device)
     if cache_seqlens is None:
@@ -401,7 +424,7 @@ def attention_paged_splitkv(q, k_cache, v_cache, block_table, seqlen_k, num_spli
 
 
 def attention_paged_splitkv_fp8(q, k_cache, v_cache, k_descale, v_descale, block_table, seqlen_k,
-                                num_splits, softmax_scale=None, causal=False, window_left=-1,
+                                num_splits=None, softmax_scale=None, causal=False, window_left=-1,
                                 window_right=-1, alibi_slopes=None, softcap=0.0, stream=None,
                                 cache_seqlens=None):
     """Split partials o_part [S,B,H,1,d] and lse_part [S,B,H,1] of one bf16 query row per
@@ -420,6 +443,7 @@ def attention_paged_splitkv_fp8(q, k_cache, v_cache, k_descale, v_descale, block
         raise ValueError("cache_seqlens must be int32 [B]")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
+    num_splits = _splits(num_splits, B, H, nq, seqlen_k, d, page_size, fp8_cache=True)
     o_part = torch.empty((num_splits, B, H, nq, d), dtype=torch.float32, device=q.device)
     lse_part = torch.empty((num_splits, B, H, nq), dtype=torch.float32, device=q.device)
     _check(fa_fwd_splitkv_fp8(q, k_cache, v_cache, k_descale, v_descale, block_table,
@@ -492,7 +516,7 @@ def attention_varlen_backward(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k,
 
 
 def attention_paged_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens,
-                           max_seqlen_k, num_splits, softmax_scale=None, causal=False,
+                           max_seqlen_k, num_splits=None, softmax_scale=None, causal=False,
                            window_left=-1, window_right=-1, alibi_slopes=None, softcap=0.0,
                            stream=None):
     """Append k_new/v_new [B,Nq,H,d] to the paged cache behind cache_seqlens[b] keys and
@@ -511,6 +535,7 @@ def attention_paged_append(q, k_new, v_new, k_cache, v_cache, block_table, cache
         raise ValueError("cache_seqlens must be int32 [B]")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
+    num_splits = _splits(num_splits, B, H, nq, max_seqlen_k, d, page_size)
     o_part = torch.empty((num_splits, B, H, nq, d), dtype=torch.float32, device=q.device)
     lse_part = torch.empty((num_splits, B, H, nq), dtype=torch.float32, device=q.device)
     _check(fa_fwd_splitkv_append(q, k_new, v_new, k_cache, v_cache, block_table,
@@ -521,7 +546,7 @@ def attention_paged_append(q, k_new, v_new, k_cache, v_cache, block_table, cache
     return o_part, lse_part
 
 
-def attention_split_partials(q, k, v, num_splits, softmax_scale=None, causal=False,
+def attention_split_partials(q, k, v, num_splits=None, softmax_scale=None, causal=False,
                              window_left=-1, window_right=-1, alibi_slopes=None, softcap=0.0,
                              stream=None):
     """Split partials o_part [S,B,H,Nq,d] and lse_part [S,B,H,Nq] over contiguous K/V."""
@@ -532,6 +557,7 @@ def attention_split_partials(q, k, v, num_splits, softmax_scale=None, causal=Fal
         raise ValueError("k and v must be [B, Nk, H, d] matching q")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
+    num_splits = _splits(num_splits, B, H, nq, nk, d, 64)
     o_part = torch.empty((num_splits, B, H, nq, d), dtype=torch.float32, device=q.device)
     lse_part = torch.empty((num_splits, B, H, nq), dtype=torch.float32, device=q.device)
     _check(fa_fwd_split(q, k, v, o_part, lse_part, num_splits, B, H, nq, nk, d, softmax_scale,
@@ -540,7 +566,7 @@ def attention_split_partials(q, k, v, num_splits, softmax_scale=None, causal=Fal
     return o_part, lse_part
 
 
-def attention_split(q, k, v, num_splits, out_dtype=torch.float32, stream=None, **kw):
+def attention_split(q, k, v, num_splits=None, out_dtype=torch.float32, stream=None, **kw):
     """fa_fwd_split followed by the combine kernel: the same result as attention()."""
     o_part, lse_part = attention_split_partials(q, k, v, num_splits, stream=stream, **kw)
     return combine(o_part, lse_part, out_dtype=out_dtype, stream=stream)
@@ -556,8 +582,8 @@ def combine(o_part, lse_part, out_dtype=torch.float32, stream=None):
     return o, lse
 
 
-def decode_paged(q, k_cache, v_cache, block_table, seqlen_k, num_splits, out_dtype=torch.float32,
-                 **kw):
+def decode_paged(q, k_cache, v_cache, block_table, seqlen_k, num_splits=None,
+                 out_dtype=torch.float32, **kw):
     """Split-KV pass followed by the combine kernel, both on the current stream."""
     o_part, lse_part = attention_paged_splitkv(q, k_cache, v_cache, block_table, seqlen_k,
                                                num_splits, **kw)

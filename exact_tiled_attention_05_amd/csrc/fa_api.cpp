@@ -3,8 +3,11 @@
 // contract of each entry point.
 #include "fa.h"
 
+#include <hip/hip_runtime_api.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "fa_params.h"
 
@@ -280,6 +283,36 @@ int fa_split_chunk_len(int seqlen_k, int num_splits, int page_size) {
   if (seqlen_k <= 0 || num_splits <= 0 || page_size <= 0) return -1;
   const int64_t c = split_len(seqlen_k, num_splits, page_size);
   return c > kMaxSeq ? -1 : (int)c;
+}
+
+int fa_num_splits(int batch, int heads, int seqlen_q, int seqlen_k, int head_dim, int page_size,
+                  int fp8_cache, int num_cus) {
+  if (batch <= 0 || heads <= 0 || seqlen_q <= 0 || seqlen_k <= 0 || page_size <= 0) return -1;
+  if (head_dim != 64 && head_dim != 128) return -1;
+  if (num_cus <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        num_cus <= 0)
+      return -1;
+  }
+  int64_t per_split, target;
+  if (seqlen_q == 1) {
+    // The decode kernel: one workgroup per (head group, batch, split); a head
+    // group is the heads whose rows of one key make 256 bytes.
+    const int row_bytes = head_dim * (fp8_cache ? 1 : 2);
+    const int g = row_bytes >= 256 ? 1 : 256 / row_bytes;
+    per_split = (int64_t)batch * ((heads + g - 1) / g);
+    target = num_cus;
+  } else {
+    // The tiled kernel: one workgroup per (128-row query tile, head, batch,
+    // split), two resident per compute unit.
+    per_split = (int64_t)batch * heads * ((seqlen_q + fa::BF16_BM - 1) / fa::BF16_BM);
+    target = 2 * (int64_t)num_cus;
+  }
+  const int64_t chunks = (seqlen_k + (int64_t)page_size - 1) / page_size;
+  const int64_t s = std::min<int64_t>({(target + per_split - 1) / per_split, chunks, 64});
+  return (int)std::max<int64_t>(s, 1);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, int in_dtype, void* o, int o_dtype,

@@ -367,6 +367,21 @@ const char* fa_status_string(int status);
  * or fa_fwd_split (page_size = 64) for these sizes, or -1 on bad sizes. */
 int fa_split_chunk_len(int seqlen_k, int num_splits, int page_size);
 
+/*
+ * A split count for the split passes (fa_fwd_splitkv and its _seqlens, _append
+ * and _fp8 forms, with page_size = the cache's page size and fp8_cache set for
+ * an E4M3 cache; fa_fwd_split with page_size = 64): the smallest count whose
+ * launch has at least one workgroup per compute unit for a single query row
+ * (the split pass of the update article's v2.2 entry, which exists to occupy
+ * a GPU that the batch and heads alone leave idle), or two per compute unit
+ * for more rows, at most one split per page (per 64 keys) and at most 64.
+ * num_cus <= 0 asks the current HIP device for its compute-unit count. Returns
+ * -1 on bad sizes (any size <= 0, head_dim not 64 or 128) or when no device
+ * answers.
+ */
+int fa_num_splits(int batch, int heads, int seqlen_q, int seqlen_k, int head_dim, int page_size,
+                  int fp8_cache, int num_cus);
+
 #ifdef __cplusplus
 }
 #endif

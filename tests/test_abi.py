@@ -351,3 +351,23 @@ def fp8(**kw):
 ])
 def test_fa_fwd_fp8_rejects(kw, code):
     assert fp8(**kw) == code
+
+
+def test_num_splits_heuristic():
+    # One query row: at least one workgroup per compute unit (256 here), head
+    # groups of 256-byte segments, at most one split per page and 64 splits.
+    ns = fa.fa_num_splits
+    assert ns(1, 32, 1, 4096, 128, 256, num_cus=256) == 8
+    assert ns(4, 32, 1, 8192, 128, 256, num_cus=256) == 2
+    assert ns(1, 8, 1, 16384, 128, 256, num_cus=256) == 32
+    assert ns(16, 32, 1, 2048, 128, 256, num_cus=256) == 1
+    assert ns(1, 32, 1, 4096, 128, 256, fp8_cache=True, num_cus=256) == 16  # 2 heads per group
+    assert ns(1, 32, 1, 4096, 64, 256, fp8_cache=True, num_cus=256) == 16   # capped: 16 pages
+    assert ns(1, 1, 1, 300, 128, 256, num_cus=256) == 2                      # 2 pages
+    assert ns(1, 1, 1, 1 << 20, 128, 16, num_cus=256) == 64                  # at most 64
+    # Several rows: two workgroups per compute unit (128-row query tiles).
+    assert ns(2, 8, 512, 4096, 128, 64, num_cus=256) == 8
+    assert ns(4, 16, 2048, 2048, 128, 64, num_cus=256) == 1
+    for bad in [(0, 1, 1, 1, 128, 64), (1, 0, 1, 1, 128, 64), (1, 1, 0, 1, 128, 64),
+                (1, 1, 1, 0, 128, 64), (1, 1, 1, 1, 96, 64), (1, 1, 1, 1, 128, 0)]:
+        assert ns(*bad, num_cus=256) == -1

@@ -1220,3 +1220,91 @@ def test_fp8_decode_every_code():
     vmax = float(np.abs(v).max())
     assert vmax == 448.0 * vd
     check(o_part.cpu().numpy() / vmax, lse_part.cpu().numpy(), rop / vmax, rlp, "fp32", "every code")
+
+
+# --------------------------------------------------------------------------
+# Capture in a HIP graph: a serving step (cache append + split pass + combine)
+# --------------------------------------------------------------------------
+def test_decode_step_replays_from_a_hip_graph():
+    """The library allocates and clears nothing, so a decode step (append of the
+    step's key and value, split pass, combine) captures as three kernel nodes.
+    Every replay, with eager work and synchronisations in between, equals the
+    eager call bit for bit (the append rewrites the same rows each time)."""
+    w = W.Workload(0, "graph_step", B=3, H=4, Nq=1, Nk=3000, d=128, dtype="bf16", causal=True,
+                   paged=True, page_size=64, pool_factor=1.3, num_splits=8, seed=14000)
+    seqlens = [2999, 1500, 0]
+    q, kc, vc, bt = W.gen_paged(w, seqlens=seqlens)
+    kn = W.gen_tensor(14001, W.TENSOR_K, w.B, 1, w.H, w.d, 1.0, "bf16")
+    vn = W.gen_tensor(14001, W.TENSOR_V, w.B, 1, w.H, w.d, 1.0, "bf16")
+    tq, tkn, tvn = to_dev(q, "bf16"), to_dev(kn, "bf16"), to_dev(vn, "bf16")
+    tk, tv = to_dev(kc, "bf16"), to_dev(vc, "bf16")
+    tbt = torch.from_numpy(bt).cuda()
+    tsl = torch.tensor(seqlens, dtype=torch.int32).cuda()
+    S = w.num_splits
+    op = torch.empty((S, w.B, w.H, 1, w.d), dtype=torch.float32, device="cuda")
+    lp = torch.empty((S, w.B, w.H, 1), dtype=torch.float32, device="cuda")
+    o = torch.empty((w.B, 1, w.H, w.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H, 1), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def step():
+        st = fa.fa_fwd_splitkv_append(tq, tkn, tvn, tk, tv, tbt, tbt.shape[1], w.page_size, tsl,
+                                      op, lp, S, w.B, w.H, 1, w.Nk, w.d, w.scale, True,
+                                      stream=stream)
+        assert st == 0, st
+        assert fa.fa_splitkv_combine(op, lp, S, w.B, w.H, 1, w.d, o, lse, stream=stream) == 0
+
+    say("hip graph: eager step")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        step()
+    stream.synchronize()
+    o_ref, lse_ref, k_ref = o.clone(), lse.clone(), tk.clone()
+    g = torch.cuda.CUDAGraph()
+    say("hip graph: capture")
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        o.fill_(float("nan"))
+        lse.fill_(0.0)
+        op.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"hip graph: replay {rep}")
+        assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref), rep
+        assert torch.equal(tk.view(torch.int16), k_ref.view(torch.int16)), rep
+    # and the eager result is the oracle's
+    kf = W.to_float(kc, "bf16")
+    vf = W.to_float(vc, "bf16")
+    k2, v2 = O.kvcache_append_ref(kf, vf, bt, seqlens, W.to_float(kn, "bf16"), W.to_float(vn, "bf16"))
+    k = np.zeros((w.B, w.Nk, w.H, w.d))
+    v = np.zeros((w.B, w.Nk, w.H, w.d))
+    for b, n in enumerate(seqlens):
+        k[b, :n + 1] = O.paged_gather_ref(k2, bt, b, n + 1)
+        v[b, :n + 1] = O.paged_gather_ref(v2, bt, b, n + 1)
+    rop, rlp = O.splitkv_ref(W.to_float(q, "bf16"), k, v, S, w.page_size, w.scale, True,
+                             seqlens_k=[n + 1 for n in seqlens])
+    ro, rl = O.combine_ref(rop, rlp)
+    check(o_ref.cpu().numpy().transpose(0, 2, 1, 3), lse_ref.cpu().numpy(), ro, rl, "bf16",
+          "graph step")
+
+
+def test_num_splits_from_the_device():
+    """fa_num_splits with no compute-unit count asks the device (the same answer
+    as with its count given), and the helpers use it when num_splits is None."""
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    for args in [(1, 32, 1, 4096, 128, 256), (2, 8, 512, 4096, 128, 64), (3, 5, 1, 1000, 64, 16)]:
+        assert fa.fa_num_splits(*args) == fa.fa_num_splits(*args, num_cus=cus) > 0
+    w = W.Workload(0, "auto_split", B=2, H=4, Nq=1, Nk=2000, d=128, dtype="bf16", causal=True,
+                   paged=True, page_size=64, pool_factor=1.2, num_splits=1, seed=14100)
+    q, kc, vc, bt = W.gen_paged(w)
+    tq, tk, tv, tbt = to_dev(q, "bf16"), to_dev(kc, "bf16"), to_dev(vc, "bf16"), torch.from_numpy(bt).cuda()
+    S = fa.fa_num_splits(w.B, w.H, 1, w.Nk, w.d, w.page_size)
+    op_auto, lp_auto = fa.attention_paged_splitkv(tq, tk, tv, tbt, w.Nk)
+    op, lp = fa.attention_paged_splitkv(tq, tk, tv, tbt, w.Nk, S)
+    torch.cuda.synchronize()
+    assert op_auto.shape[0] == S
+    assert torch.equal(op_auto, op) and torch.equal(lp_auto, lp)
