@@ -472,6 +472,44 @@ def main():
                        "pct_peak": round(100 * f8_decode_bytes / t_d8.mean() / 1e9 / PEAK_HBM_GBS, 2),
                        "keys_per_s_vs_bf16": round(float((t_split + t_comb).mean() / t_d8.mean()), 3)}
 
+    # ---- a chunk of 512 query rows over the first sequence of the decode pool
+    # (chunked prefill over a paged cache; side measurement): the multi-row split
+    # pass, bottom-right causal over 32768 keys, then the combine.
+    cq = up(W.gen_tensor(wd.seed, W.TENSOR_Q, 1, 512, wd.H, wd.d, 1.0, "bf16"), "bf16")
+    CS = fa.fa_num_splits(1, wd.H, 512, wd.Nk, wd.d, wd.page_size)
+    cop = torch.empty((CS, 1, wd.H, 512, wd.d), dtype=torch.float32, device=dev)
+    clp = torch.empty((CS, 1, wd.H, 512), dtype=torch.float32, device=dev)
+    co = torch.empty((1, 512, wd.H, wd.d), dtype=torch.float32, device=dev)
+    clse = torch.empty((1, wd.H, 512), dtype=torch.float32, device=dev)
+    cbt = dbt[:1].contiguous()
+    chunk_flops = 4.0 * wd.H * wd.d * allowed_pairs(512, wd.Nk, True, -1, -1)
+
+    def paged_chunk():
+        check(fa.fa_fwd_splitkv(cq, dk, dv, cbt, cbt.shape[1], wd.page_size, cop, clp, CS, 1, wd.H,
+                                512, wd.Nk, wd.d, wd.scale, True, -1, -1, None, 0.0, stream),
+              "fa_fwd_splitkv")
+        check(fa.fa_splitkv_combine(cop, clp, CS, 1, wd.H, 512, wd.d, co, clse, stream),
+              "fa_splitkv_combine")
+
+    for _ in range(args.warmup):
+        paged_chunk()
+    ev7 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for a, e in ev7:
+        a.record(stream)
+        paged_chunk()
+        e.record(stream)
+    torch.cuda.synchronize()
+    t_pc = np.array([a.elapsed_time(e) for a, e in ev7]) * 1e-3
+    assert torch.isfinite(co).all()
+    chunk_line = {"workload": "512-row chunk over a 32768-key paged sequence, H32 d128, 256-key "
+                              "pages (fa_fwd_splitkv multi-row + combine)",
+                  "num_splits": CS, "gflop": round(chunk_flops / 1e9, 4),
+                  "ms": round(t_pc.mean() * 1e3, 5), "ms_median": round(float(np.median(t_pc)) * 1e3, 5),
+                  "tflops": round(chunk_flops / t_pc.mean() / 1e12, 3),
+                  "pct_peak": round(100 * chunk_flops / t_pc.mean() / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    del cop, clp, co, clse
+
     # ---- one decode step of a small serving batch (side measurement): append of
     # the step's key and value, split pass and combine for 1 sequence of 4096
     # cached keys (32 heads, 256-key pages, the split count fa_num_splits picks),
@@ -601,6 +639,7 @@ def main():
         "fp8_prefill": fp8_line,
         "fp8_decode": fp8_decode_line,
         "serving_step": serving_line,
+        "paged_prefill_chunk": chunk_line,
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("prefill"),

@@ -179,6 +179,8 @@ int splitkv(const void* q, const void* k_cache, const void* v_cache, const void*
   const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
   Launcher fn = fp8_cache             ? pick_decode_fp8(head_dim, sc, al)
                 : in_dtype != FA_BF16 ? pick_f32<true>(head_dim, sc, al)
+                : seqlen_q != 1 && !k_new && page_size % 64 == 0
+                    ? pick_bf16<fa::FWD_PAGED_TILES>(head_dim, sc, al)
                 : seqlen_q != 1       ? pick_bf16<fa::FWD_PAGED_SPLIT>(head_dim, sc, al)
                 : k_new               ? pick_decode<true>(head_dim, sc, al)
                                       : pick_decode<false>(head_dim, sc, al);

@@ -48,13 +48,15 @@ struct Tuning {
 };
 
 // MODE: FWD_CONTIG (contiguous K/V -> O, LSE), FWD_CONTIG_SPLIT (contiguous K/V,
-// one key split per workgroup -> normalised partials) or FWD_PAGED_SPLIT (paged
+// one key split per workgroup -> normalised partials), FWD_PAGED_TILES (paged
+// K/V in pages of a multiple of 64 keys -> partials) or FWD_PAGED_SPLIT (paged
 // K/V through the block table -> partials).
 template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Tuning<D, SOFTCAP>::kWaves, Tuning<D, SOFTCAP>::kWaves)))
 void fwd_bf16_kernel(FwdParams p) {
   constexpr bool PAGED = MODE == FWD_PAGED_SPLIT;  // K/V rows gathered through the block table
+  constexpr bool PTILES = MODE == FWD_PAGED_TILES; // K/V tiles from one page each
   constexpr bool SPLIT = MODE != FWD_CONTIG;       // one key split per workgroup, partial outputs
   constexpr int KS = D / 16;                 // MFMA k-steps of Q K^T
   constexpr int NDB = D / 32;                // 32-row blocks of O^T
@@ -127,6 +129,41 @@ void fwd_bf16_kernel(FwdParams p) {
   const int j_first = (wg.lo / kBN) * kBN;
   const int ntiles = (wg.hi - j_first + kBN - 1) / kBN;
 
+  // Paged K/V. With pages of a multiple of the 64-key tile and no appended key
+  // (PTILES) every tile lies inside one page with the row stride of a
+  // contiguous tensor, so tiles travel as in the contiguous path from a
+  // per-tile base address. Otherwise (PAGED) rows are gathered one by one,
+  // with the page ids of the workgroup's keys [j_first, wg.hi) staged in LDS
+  // (in the third K buffer, which that path does not use) so that a copy needs
+  // no dependent block-table load.
+  constexpr int kTablePages = TILE / 2;  // ints in one K buffer
+  int* const s_pt = (int*)sK2;
+  int pt0 = 0;
+  bool pt_lds = false;
+  if constexpr (PAGED) {
+    pt0 = p.page_shift >= 0 ? j_first >> p.page_shift : j_first / p.page_size;
+    const int pt1 = p.page_shift >= 0 ? (wg.hi - 1) >> p.page_shift : (wg.hi - 1) / p.page_size;
+    pt_lds = pt1 - pt0 < kTablePages;
+    if (pt_lds) {
+      const int* bt_row = p.block_table + (int64_t)b * p.max_pages;
+      for (int i = tid; i <= pt1 - pt0; i += kThreads) s_pt[i] = bt_row[pt0 + i];
+    }
+    __syncthreads();
+  }
+  // Element offset of key `key` (in [j_first, wg.hi)) of this (b, h) in the page pool.
+  auto paged_offset = [&](int key) __attribute__((always_inline)) {
+    int idx, slot;
+    if (p.page_shift >= 0) {
+      idx = key >> p.page_shift;
+      slot = key & (p.page_size - 1);
+    } else {
+      idx = key / p.page_size;
+      slot = key - idx * p.page_size;
+    }
+    const int page = pt_lds ? s_pt[idx - pt0] : p.block_table[(int64_t)b * p.max_pages + idx];
+    return (((int64_t)page * p.page_size + slot) * p.H + h) * D;
+  };
+
   // ---- HBM -> LDS copies of one tile of K and V. Copy i of this wavefront
   // fills tile rows [ROWS_PER_LOAD * (LOADS*w + i), +ROWS_PER_LOAD); lane L
   // writes physical chunk L % CPR of its row, i.e. logical chunk
@@ -147,19 +184,39 @@ void fwd_bf16_kernel(FwdParams p) {
     const int chunk = (lane % CPR) ^ swz<D>(trow);
     lane_bytes[i] = (unsigned)(trow * row_bytes + 16 * chunk);
   }
-  // Paged K/V: rows past the end re-read the last key (finite data; masked later);
-  // appended keys come from k_new / v_new.
+  // Paged K/V: rows past the workgroup's key range re-read its last key (finite
+  // data; masked later); appended keys come from k_new / v_new.
   const uint16_t* kg = (const uint16_t*)p.k;
   const uint16_t* vg = (const uint16_t*)p.v;
   const uint16_t* kn = (const uint16_t*)p.k_new;
   const uint16_t* vn = (const uint16_t*)p.v_new;
-  auto copy_one = [&](const char* bh, uint16_t* dst, int j0) __attribute__((always_inline)) {
-    const int64_t tb = (int64_t)j0 * row_bytes;
-    const int64_t left = end_bytes - tb;
+  // One tile from `base` (its first row), `left` bytes of it in range.
+  auto copy_rows = [&](const char* base, int64_t left, uint16_t* dst) __attribute__((always_inline)) {
     const int n = left <= 0 ? 0 : (left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(bh + tb, n);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, n);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) buffer_load_lds16(rs, dst + 512 * (LOADS * wu + i), lane_bytes[i]);
+  };
+  auto copy_one = [&](const char* bh, uint16_t* dst, int j0) __attribute__((always_inline)) {
+    const int64_t tb = (int64_t)j0 * row_bytes;
+    copy_rows(bh + tb, end_bytes - tb, dst);
+  };
+  // Tile j0 of a page-aligned pool (PTILES) from page `page`; rows past the
+  // sequence's last key read as zeros.
+  auto copy_page_tile = [&](const void* pool, int page, uint16_t* dst, int j0) __attribute__((always_inline)) {
+    const int slot0 = p.page_shift >= 0 ? j0 & (p.page_size - 1) : j0 % p.page_size;
+    const char* base = (const char*)pool + 2 * ((((int64_t)page * p.page_size + slot0) * p.H + h) * D);
+    copy_rows(base, (int64_t)(nk - 1 - j0) * row_bytes + 2 * D, dst);
+  };
+  // Page of tile j0 (tiles past the key range, which read nothing, take the
+  // range's last page so the index stays in the table). The id is read with a
+  // vector load (the address is written per lane: lane >> 6 is 0) and made
+  // uniform afterwards: a scalar load would be waited for with the counter
+  // that also tracks LDS reads, stalling the products' operand reads.
+  auto page_of = [&](int j0) __attribute__((always_inline)) {
+    const int kk = min(j0, wg.hi - 1);
+    const int idx = p.page_shift >= 0 ? kk >> p.page_shift : kk / p.page_size;
+    return __builtin_amdgcn_readfirstlane(p.block_table[(int64_t)b * p.max_pages + idx + (lane >> 6)]);
   };
   auto copy_tiles = [&](uint16_t* kdst, uint16_t* vdst, int j0) __attribute__((always_inline)) {
     if constexpr (!PAGED) {
@@ -171,10 +228,9 @@ void fwd_bf16_kernel(FwdParams p) {
         const int ld = LOADS * wu + i;
         const int trow = ROWS_PER_LOAD * ld + lane / CPR;
         const int chunk = (lane % CPR) ^ swz<D>(trow);
-        const int key = min(j0 + trow, nk - 1);
+        const int key = min(j0 + trow, wg.hi - 1);
         const bool fresh = key >= si.n_cached;
-        const int64_t o = (fresh ? new_key_offset(p, si, b, key, h, D)
-                                 : kv_offset<PAGED>(p, b, si, key, h, D)) + 8 * chunk;
+        const int64_t o = (fresh ? new_key_offset(p, si, b, key, h, D) : paged_offset(key)) + 8 * chunk;
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)((fresh ? kn : kg) + o),
                                          (lds_ptr_t)(kdst + 512 * ld), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)((fresh ? vn : vg) + o),
@@ -287,15 +343,16 @@ void fwd_bf16_kernel(FwdParams p) {
 
   auto live = [&](int j0) __attribute__((always_inline)) { return wave_live && j0 < wk.hi && j0 + kBN > wk.lo; };
 
-  if constexpr (!PAGED) {
-    // ---- contiguous K/V: K(t) in stage t % 3, V(t) in buffer t & 1. Step t
-    // copies V(t+1) over V(t-1) and K(t+2) over K(t-1) (both last read in step
-    // t-1, ended by a barrier), computes tile t, then waits for all but the
-    // K(t+2) copies. Copies past the key range read nothing and write zeros.
+  // ---- tile loop: K(t) in stage t % 3, V(t) in buffer t & 1. Step t copies
+  // V(t+1) over V(t-1) and K(t+2) over K(t-1) (both last read in step t-1,
+  // ended by a barrier), computes tile t, then waits for all but the K(t+2)
+  // copies. Copies past the key range read nothing and write zeros. kcopy /
+  // vcopy (dst, j0) copy the K / V tile of key j0.
+  auto tile_loop = [&](auto kcopy, auto vcopy) __attribute__((always_inline)) {
     constexpr int kKC = LOADS;  // vector-memory ops of one K tile copy
-    copy_one(kbh, sK0, j_first);
-    copy_one(vbh, sV0, j_first);
-    copy_one(kbh, sK1, j_first + kBN);
+    kcopy(sK0, j_first);
+    vcopy(sV0, j_first);
+    kcopy(sK1, j_first + kBN);
     wait_vmem_barrier<kKC>();
     f32x16_t sacc[2];
     auto step3 = [&](auto kst, auto vpar, int it) __attribute__((always_inline)) {
@@ -306,10 +363,10 @@ void fwd_bf16_kernel(FwdParams p) {
       const uint16_t* v_cur = VODD ? sV1 : sV0;
       uint16_t* v_nxt = VODD ? sV0 : sV1;
       const int j0 = j_first + it * kBN;
-      copy_one(vbh, v_nxt, j0 + kBN);
+      vcopy(v_nxt, j0 + kBN);
       const bool lv = live(j0);
       if (lv) qk(k_cur, sacc);
-      copy_one(kbh, k_nn, j0 + 2 * kBN);
+      kcopy(k_nn, j0 + 2 * kBN);
       if (lv) {
         if (j0 >= wk.flo && j0 + kBN <= wk.fhi)
           softmax_pv(std::false_type{}, sacc, v_cur, j0);
@@ -330,8 +387,31 @@ void fwd_bf16_kernel(FwdParams p) {
       if (it + 5 < ntiles) step3(I2{}, std::true_type{}, it + 5);
     }
     wait_vmem_barrier<0>();  // no copy may still be writing LDS at exit
+  };
+
+  if constexpr (PTILES) {
+    // The loop copies K(t+2) and V(t+1) in step t: each K copy also loads the
+    // page of the next tile, one step before the next K copy needs it, and
+    // leaves its own page for the V copy of the next step.
+    int pk_j = -1, pk = 0, pv_j = -1, pv = 0;
+    tile_loop(
+        [&](uint16_t* dst, int j0) __attribute__((always_inline)) {
+          const int pg = j0 == pk_j ? pk : page_of(j0);
+          copy_page_tile(p.k, pg, dst, j0);
+          pv = pg;
+          pv_j = j0;
+          pk = page_of(j0 + kBN);
+          pk_j = j0 + kBN;
+        },
+        [&](uint16_t* dst, int j0) __attribute__((always_inline)) {
+          copy_page_tile(p.v, j0 == pv_j ? pv : page_of(j0), dst, j0);
+        });
+  } else if constexpr (!PAGED) {
+    tile_loop([&](uint16_t* dst, int j0) __attribute__((always_inline)) { copy_one(kbh, dst, j0); },
+              [&](uint16_t* dst, int j0) __attribute__((always_inline)) { copy_one(vbh, dst, j0); });
   } else {
-    // ---- paged K/V: two buffers each; step t copies tile t+1 and waits for it.
+    // ---- paged K/V gathered row by row: two buffers each; step t copies tile
+    // t+1 and waits for it.
     copy_tiles(sK0, sV0, j_first);
     wait_vmem();
     __syncthreads();
@@ -409,7 +489,8 @@ int launch_fwd_bf16(const FwdParams& p, void* stream) {
 #define FA_INST(D, SC, AL, M) template int launch_fwd_bf16<D, SC, AL, M>(const FwdParams&, void*);
 #define FA_INST_M(D, M) \
   FA_INST(D, false, false, M) FA_INST(D, false, true, M) FA_INST(D, true, false, M) FA_INST(D, true, true, M)
-#define FA_INST_D(D) FA_INST_M(D, FWD_CONTIG) FA_INST_M(D, FWD_CONTIG_SPLIT) FA_INST_M(D, FWD_PAGED_SPLIT)
+#define FA_INST_D(D) FA_INST_M(D, FWD_CONTIG) FA_INST_M(D, FWD_CONTIG_SPLIT) \
+  FA_INST_M(D, FWD_PAGED_SPLIT) FA_INST_M(D, FWD_PAGED_TILES)
 FA_INST_D(64)
 FA_INST_D(128)
 #undef FA_INST_D

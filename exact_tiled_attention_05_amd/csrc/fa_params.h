@@ -84,6 +84,9 @@ enum FwdMode {
   FWD_CONTIG = 0,        // contiguous K/V, whole key range -> O, LSE
   FWD_CONTIG_SPLIT = 1,  // contiguous K/V, one key split per workgroup -> o_part, lse_part
   FWD_PAGED_SPLIT = 2,   // paged K/V through the block table, per split -> o_part, lse_part
+                         //   (rows gathered one by one: any page size, appended keys)
+  FWD_PAGED_TILES = 3,   // the same with page_size a multiple of 64 and no append:
+                         //   whole 64-key tiles from one page each
 };
 
 // Launchers (defined in the .hip files). Return hipError_t as int.

@@ -1308,3 +1308,28 @@ def test_num_splits_from_the_device():
     torch.cuda.synchronize()
     assert op_auto.shape[0] == S
     assert torch.equal(op_auto, op) and torch.equal(lp_auto, lp)
+
+
+@pytest.mark.parametrize("d,alibi,cap", [(128, False, 0.0), (64, True, 0.0), (128, True, 20.0)])
+def test_paged_tiles_bitwise_equal_contiguous_split(d, alibi, cap):
+    """With 64-key pages a paged cache cuts the same split chunks as fa_fwd_split,
+    and every 64-key tile comes whole from one page: the multi-row paged pass
+    runs the contiguous loop on per-tile addresses, so the partials are equal
+    bit for bit to those over the same keys stored contiguously."""
+    B, H, nq, nk, S = 2, 3, 200, 1000, 3
+    say(f"paged tiles vs contiguous d{d} alibi{alibi} cap{cap}")
+    w = W.Workload(0, "ptiles", B=B, H=H, Nq=nq, Nk=nk, d=d, dtype="bf16", causal=True,
+                   paged=True, page_size=64, pool_factor=1.4, num_splits=S, seed=14200 + d)
+    q, kc, vc, bt = W.gen_paged(w)
+    slopes = W.alibi_slopes(H) if alibi else None
+    ts = None if slopes is None else torch.from_numpy(slopes).cuda()
+    scale = 1.0 / np.sqrt(d)
+    op, lp = fa.attention_paged_splitkv(to_dev(q, "bf16"), to_dev(kc, "bf16"), to_dev(vc, "bf16"),
+                                        torch.from_numpy(bt).cuda(), nk, S, scale, True, 100, 0,
+                                        ts, cap)
+    k = np.stack([O.paged_gather_ref(kc, bt, b, nk) for b in range(B)])  # bf16 bits, contiguous
+    v = np.stack([O.paged_gather_ref(vc, bt, b, nk) for b in range(B)])
+    oc, lc = fa.attention_split_partials(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                                         S, scale, True, 100, 0, ts, cap)
+    torch.cuda.synchronize()
+    assert torch.equal(op, oc) and torch.equal(lp, lc)
