@@ -1333,3 +1333,38 @@ def test_paged_tiles_bitwise_equal_contiguous_split(d, alibi, cap):
                                          S, scale, True, 100, 0, ts, cap)
     torch.cuda.synchronize()
     assert torch.equal(op, oc) and torch.equal(lp, lc)
+
+
+def test_concurrent_streams_match_sequential():
+    """The library keeps no state between calls: a prefill, a paged decode and a
+    backward launched on three streams at once give the bits they give one after
+    another on the default stream."""
+    q, k, v = qkv_case(14300, 2, 300, 500, 4, 128, "bf16")
+    tq, tk, tv = (to_dev(x, "bf16") for x in (q, k, v))
+    w = W.Workload(0, "streams", B=2, H=4, Nq=1, Nk=3000, d=128, dtype="bf16", causal=True,
+                   paged=True, page_size=64, pool_factor=1.2, num_splits=6, seed=14301)
+    dq, kc, vc, bt = W.gen_paged(w)
+    tdq, tkc, tvc, tbt = to_dev(dq, "bf16"), to_dev(kc, "bf16"), to_dev(vc, "bf16"), torch.from_numpy(bt).cuda()
+    tg = to_dev(W.gen_tensor(14302, 3, 2, 300, 4, 128, 1.0, "bf16"), "bf16")
+    o0, l0 = fa.attention(tq, tk, tv, 0.1, True)
+
+    def work(streams):
+        s1, s2, s3 = streams
+        with torch.cuda.stream(s1):
+            a = fa.attention(tq, tk, tv, 0.1, True, stream=s1)
+        with torch.cuda.stream(s2):
+            b = fa.decode_paged(tdq, tkc, tvc, tbt, w.Nk, w.num_splits, causal=True, stream=s2)
+        with torch.cuda.stream(s3):
+            c = fa.attention_backward(tq, tk, tv, o0, l0, tg, 0.1, True, stream=s3)
+        torch.cuda.synchronize()
+        return [*a, *b, *c]
+
+    say("streams: sequential")
+    d = torch.cuda.default_stream()
+    ref = work((d, d, d))
+    say("streams: concurrent")
+    streams = (torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream())
+    for _ in range(3):
+        got = work(streams)
+        for x, y in zip(got, ref):
+            assert torch.equal(x, y)
