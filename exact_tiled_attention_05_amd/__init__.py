@@ -34,7 +34,6 @@ __all__ = [
 
 FA_FP32, FA_BF16 = 0, 1
 FA_OK = 0
-FA_ERR_SHAPE = 2
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 _lib = None
 
@@ -159,7 +158,8 @@ def _splits(num_splits, *args, **kw) -> int:
         return int(num_splits)
     s = fa_num_splits(*args, **kw)
     if s <= 0:
-        raise FaError(FA_ERR_SHAPE, "fa_num_splits")
+        raise ValueError(f"fa_num_splits{args}: bad sizes, or no HIP device to ask for its "
+                         "compute-unit count; pass num_splits explicitly")
     return s
 
 
