@@ -66,7 +66,25 @@ def build(verbose: bool = False, extra_flags=None, out: str = LIB, build_dir: st
     tmp = out + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, out)
+    if out == LIB:
+        build_c_example()
     return out
+
+
+C_EXAMPLE_DIR = os.path.join(ROOT, "tests", "c_abi")
+C_EXAMPLE = os.path.join(C_EXAMPLE_DIR, "fa_c_example")
+
+
+def build_c_example() -> str:
+    """Compile the plain C consumer of the C ABI (tests/c_abi/fa_c_example.c) with gcc,
+    linked against the in-tree libfa.so and the HIP runtime."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    _run(["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          f"-I{rocm}/include", f"-I{INCLUDE}", os.path.join(C_EXAMPLE_DIR, "fa_c_example.c"),
+          f"-L{PKG}", "-lfa", f"-L{rocm}/lib", "-lamdhip64", "-lm",
+          "-Wl,-rpath,$ORIGIN/../../exact_tiled_attention_05_amd", f"-Wl,-rpath,{rocm}/lib",
+          "-o", C_EXAMPLE])
+    return C_EXAMPLE
 
 
 if __name__ == "__main__":
