@@ -5,12 +5,14 @@
 // 的经济学", the section on H100 and FP8; the deep-analysis page lists FP8
 // forward support on its roadmap). The method is the bf16 kernel's: one
 // workgroup of 4 wavefronts per 128-row query tile of one (batch, head), each
-// wavefront holding 32 query rows, 64-key tiles of K and V staged in LDS by
+// wavefront holding 32 query rows, 128-key tiles of K and V staged in LDS by
 // copies that write LDS directly, S^T = K Q^T, an online softmax per lane pair
 // and O^T += V^T P^T. The products run on the gfx950 FP8 matrix instruction
 // v_mfma_scale_f32_32x32x64_f8f6f4 (K = 64 per instruction, unit block
-// scales), so a 64-key tile takes 4 MFMAs for S and 4 for the output instead
-// of 16 + 16 in bf16.
+// scales), so a 128-key tile takes 8 MFMAs for S and 8 for the output instead
+// of 32 + 32 in bf16. The FP8 operands need fewer registers than bf16 ones,
+// which leaves room for the 128-key score block (64 fp32 per lane) at two
+// wavefronts per SIMD; 64 KB of LDS per workgroup still lets two share a CU.
 //
 // P: with the exact running maximum the largest probability of a row is 1;
 // it is scaled by 2^8 (folded into the exponent) so that the E4M3 grid reaches
@@ -34,12 +36,14 @@ namespace {
 
 constexpr int kD = 128;        // head_dim (bytes per K/V row of one head)
 constexpr int kBM = FP8_BM;    // query rows per workgroup
-constexpr int kBN = 64;        // keys per tile
+constexpr int kBN = 128;       // keys per tile
 constexpr int kThreads = 256;  // 4 wavefronts
 constexpr int kTile = kBN * kD;  // bytes per K or V tile
 constexpr int kCPR = kD / 16;    // 16-byte chunks per row
 constexpr int kRPL = 64 / kCPR;  // rows per wavefront-wide copy
 constexpr int kLoads = kBN / kRPL / 4;  // copies per wavefront per tensor per tile
+constexpr int kNB = kBN / 32;  // 32-key blocks of S^T per tile
+constexpr int kNH = kBN / 64;  // 64-key halves: one output MFMA each per 32 head_dim rows
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
@@ -147,10 +151,10 @@ void fwd_fp8_kernel(FwdParams p) {
   auto compute = [&](auto masked_t, const uint8_t* kt, const uint8_t* vt, int j0)
                      __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_t)::value;
-    // S^T for the tile's two 32-key blocks: A = K row 32j + r, bytes 64ks + 32h2 .. +31.
-    f32x16_t sacc[2];
+    // S^T for the tile's 32-key blocks: A = K row 32j + r, bytes 64ks + 32h2 .. +31.
+    f32x16_t sacc[kNB];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kNB; ++j) {
       sacc[j] = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -160,27 +164,28 @@ void fwd_fp8_kernel(FwdParams p) {
         sacc[j] = mfma_fp8(mfma_operand(a0, a1), qf[ks], sacc[j]);
       }
     }
-    float t[2][16];
+    float t[kNB][16];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kNB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) t[j][v] = sacc[j][v];
     const float rel = (float)(row + off) - (float)(j0 + 4 * h2);
-    transform_scores<2, SOFTCAP, ALIBI>(t, p, slope_log2, rel, MASKED, j0, rk.lo, rk.hi, h2);
+    transform_scores<kNB, SOFTCAP, ALIBI>(t, p, slope_log2, rel, MASKED, j0, rk.lo, rk.hi, h2);
     bool any_rescale;
     float mc;
-    const float alpha = online_max<2>(t, c, m_run, l_run, any_rescale, mc, 0.0f);
+    const float alpha = online_max<kNB>(t, c, m_run, l_run, any_rescale, mc, 0.0f);
     if (any_rescale) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
-    // P * 2^8 (exponent shifted by 8), its fp32 row sum, and its E4M3 codes in
-    // byte order 16j + v (the P^T operand: this lane's 32 keys of the tile).
+    // P * 2^8 (exponent shifted by 8), its fp32 row sum, and its E4M3 codes:
+    // operand pq[hb] holds this lane's 32 keys of the 64-key half hb in byte
+    // order 16(j - 2hb) + v (the P^T operand).
     const float mc8 = mc - 8.0f;
-    i32x8_t pq;
+    i32x8_t pq[kNH];
     float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int wd = 0; wd < 8; ++wd) {
+    for (int wd = 0; wd < 8 * kNH; ++wd) {
       const int j = wd >> 2, v0 = 4 * (wd & 3);
       float e[4];
 #pragma unroll
@@ -190,25 +195,29 @@ void fwd_fp8_kernel(FwdParams p) {
       }
       int x = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
       x = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], x, true);
-      pq[wd] = x;
+      pq[wd >> 3][wd & 7] = x;
     }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    // O^T += V^T P^T, one MFMA per 32 head_dim rows: byte 8tr + k of lane l's
-    // operand is V[key(h2, tr, k)][32db + l % 32], gathered with 4 transposed reads.
+    // O^T += V^T P^T, one MFMA per 64-key half and 32 head_dim rows: byte
+    // 8tr + k of lane l's operand is V[64hb + key(h2, tr, k)][32db + l % 32],
+    // gathered with 4 transposed reads.
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      i32x8_t a;
+    for (int hb = 0; hb < kNH; ++hb) {
 #pragma unroll
-      for (int tr = 0; tr < 4; ++tr) {
-        const int k = a16 >> 1, pc = a16 & 1;
-        const int jj = tr >> 1, g = 2 * (tr & 1) + (k >> 2), e = k & 3;
-        const int key = 32 * jj + 8 * g + 4 * h2 + e;
-        const int ch = 2 * db + (grp & 1);
-        const i32x2_t x = ds_read_tr8(vt + tile_byte(key, ch) + 8 * pc);
-        a[2 * tr] = x[0];
-        a[2 * tr + 1] = x[1];
+      for (int db = 0; db < NDB; ++db) {
+        i32x8_t a;
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr) {
+          const int k = a16 >> 1, pc = a16 & 1;
+          const int jj = tr >> 1, g = 2 * (tr & 1) + (k >> 2), e = k & 3;
+          const int key = 64 * hb + 32 * jj + 8 * g + 4 * h2 + e;
+          const int ch = 2 * db + (grp & 1);
+          const i32x2_t x = ds_read_tr8(vt + tile_byte(key, ch) + 8 * pc);
+          a[2 * tr] = x[0];
+          a[2 * tr + 1] = x[1];
+        }
+        oacc[db] = mfma_fp8(a, pq[hb], oacc[db]);
       }
-      oacc[db] = mfma_fp8(a, pq, oacc[db]);
     }
   };
 
