@@ -940,6 +940,67 @@ def test_decode_over_a_quarter_million_keys():
         check(o[0, :, h], lse[0, h], ro, rl, "bf16", f"long decode h{h}")
 
 
+def test_tensors_over_4_gib():
+    """K and V of 4 GiB each (262144 keys x 64 heads x 128 bf16 = 2^31 elements), so
+    element and byte offsets pass 2^31 and 2^32. Heads 0, 37 and 63 hold seeded
+    N(0,1) slices checked against the oracle (head 63's last keys sit at the top
+    of the range); the other heads are filled on the device. Covered: the prefill
+    (64 query rows over every key), the same bytes as a paged cache of 1024
+    permuted 256-key pages (one query row, and the 64-row page-tile pass), and the
+    backward (bf16 gradients, relative norm)."""
+    B, H, nk, d, nq, ps = 1, 64, 262144, 128, 64, 256
+    heads = (0, 37, 63)
+    seed, scale = 4100, 1.0 / np.sqrt(128)
+    say("over 4 GiB: filling K and V on the device")
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    k = torch.randn((B, nk, H, d), generator=g, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn((B, nk, H, d), generator=g, device="cuda", dtype=torch.bfloat16)
+    assert k.numel() == 2 ** 31
+    ks, vs = {}, {}
+    for h in heads:
+        ks[h] = W.gen_slice(seed, W.TENSOR_K, 0, h, nk, d, 1.0, "bf16")
+        vs[h] = W.gen_slice(seed, W.TENSOR_V, 0, h, nk, d, 1.0, "bf16")
+        k[0, :, h] = to_dev(ks[h], "bf16")
+        v[0, :, h] = to_dev(vs[h], "bf16")
+    q = W.gen_tensor(seed, W.TENSOR_Q, B, nq, H, d, 1.0, "bf16")
+    do = W.gen_tensor(seed, 3, B, nq, H, d, 1.0, "bf16")
+    tq, tg = to_dev(q, "bf16"), to_dev(do, "bf16")
+    perm = np.random.default_rng(seed).permutation(nk // ps).astype(np.int32)
+    bt = torch.from_numpy(perm[None, :].copy()).cuda()
+    # Logical key t of the paged view lives at page perm[t // ps], row t % ps.
+    logical = (perm.astype(np.int64)[:, None] * ps + np.arange(ps)).reshape(-1)
+    kc, vc = k.view(nk // ps, ps, H, d), v.view(nk // ps, ps, H, d)
+
+    say("over 4 GiB: prefill, paged decode, paged 64-row pass")
+    o, lse = fa.attention(tq, k, v, scale, True)
+    od, lsed = fa.decode_paged(tq[:, :1].contiguous(), kc, vc, bt, nk, softmax_scale=scale,
+                               causal=True)
+    op, lsep = fa.decode_paged(tq, kc, vc, bt, nk, softmax_scale=scale, causal=True)
+    torch.cuda.synchronize()
+    say("over 4 GiB: backward")
+    dq, dk, dv = fa.attention_backward(tq, k, v, o, lse, tg, scale, True,
+                                       grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    o, lse, od, lsed, op, lsep, dq = (x.float().cpu().numpy() for x in (o, lse, od, lsed, op, lsep, dq))
+    for h in heads:
+        say(f"over 4 GiB: oracle for head {h}")
+        qf = W.to_float(q[0, :, h], "bf16")
+        kf, vf = W.to_float(ks[h], "bf16"), W.to_float(vs[h], "bf16")
+        ro, rl = O.attention_bh(qf, kf, vf, np.arange(nq), nq, scale, True)
+        check(o[0, :, h], lse[0, h], ro, rl, "bf16", f"prefill h{h}")
+        kl, vl = kf[logical], vf[logical]
+        ro, rl = O.attention_bh(qf[:1], kl, vl, np.arange(1), 1, scale, True)
+        check(od[0, :, h], lsed[0, h], ro, rl, "bf16", f"paged decode h{h}")
+        ro, rl = O.attention_bh(qf, kl, vl, np.arange(nq), nq, scale, True)
+        check(op[0, :, h], lsep[0, h], ro, rl, "bf16", f"paged 64 rows h{h}")
+        rq, rk, rv, _ = O.attention_bwd_bh(qf, kf, vf, W.to_float(do[0, :, h], "bf16"), nq,
+                                           scale, True)
+        got = (dq[0, :, h], dk[0, :, h].float().cpu().numpy(), dv[0, :, h].float().cpu().numpy())
+        for x, ref, name in zip(got, (rq, rk, rv), ("dQ", "dK", "dV")):
+            rel = np.linalg.norm(x - ref) / np.linalg.norm(ref)
+            assert rel <= 1e-2, (h, name, rel)
+
+
 def test_bwd_many_heads():
     """The backward with 1024 heads (its row-term workspace and tile decode at large H)."""
     B, H, nq, nk, d = 1, 1024, 40, 150, 128
