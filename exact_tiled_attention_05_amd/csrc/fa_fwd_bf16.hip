@@ -69,6 +69,9 @@ void fwd_bf16_kernel(FwdParams p) {
   // transforms need registers, so their PV product reads less far ahead.
   constexpr int kQkReadAhead = 8 < 2 * KS ? 8 : 2 * KS;
   constexpr int kPvReadAhead = (SOFTCAP || ALIBI) ? 4 : 6;
+  // Plain scores at head_dim 128 also spell the read-ahead out in source order
+  // (the other variants keep it from the schedule alone and would spill with it).
+  constexpr bool kPvRingInSource = D == 128 && !SOFTCAP && !ALIBI;
 
   __shared__ __attribute__((aligned(1024))) uint16_t sK0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sK1[TILE];
@@ -316,17 +319,35 @@ void fwd_bf16_kernel(FwdParams p) {
     // m = lane % 32, keys 16tt + 4*h2 + {0..3, 8..11}) comes from two transposed
     // reads: in each 16-lane group, lanes 4k..4k+3 address the four 4-column
     // pieces of key k, and lane i receives column i of those 4 keys.
+    auto v_operand = [&](int tt, int db) __attribute__((always_inline)) {
+      const int vrow = 16 * tt + 4 * h2 + (gl >> 2);
+      const int col = 32 * db + 16 * sub + 4 * (gl & 3);
+      const s16x4_t lo = ds_read_tr16(vt + tile_off<D>(vrow, col >> 3) + (col & 7));
+      const s16x4_t hi = ds_read_tr16(vt + tile_off<D>(vrow + 8, col >> 3) + (col & 7));
+      return s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    if constexpr (kPvRingInSource) {
+      // MFMA i = (i / NDB, i % NDB); its operand is read kPvReadAhead MFMAs
+      // ahead in source order as well, which the scheduler keeps when it falls
+      // back to source order under register pressure (the masked tiles).
+      s16x8_t vring[kPvReadAhead];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+      for (int i = 0; i < kPvReadAhead; ++i) vring[i] = v_operand(i / NDB, i % NDB);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int vrow = 16 * tt + 4 * h2 + (gl >> 2);
-        const int col = 32 * db + 16 * sub + 4 * (gl & 3);
-        const s16x4_t lo = ds_read_tr16(vt + tile_off<D>(vrow, col >> 3) + (col & 7));
-        const s16x4_t hi = ds_read_tr16(vt + tile_off<D>(vrow + 8, col >> 3) + (col & 7));
-        const s16x8_t x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x), pf[tt],
-                                                           oacc[db], 0, 0, 0);
+      for (int i = 0; i < 4 * NDB; ++i) {
+        const s16x8_t x = vring[i % kPvReadAhead];
+        if (i + kPvReadAhead < 4 * NDB)
+          vring[i % kPvReadAhead] = v_operand((i + kPvReadAhead) / NDB, (i + kPvReadAhead) % NDB);
+        oacc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, x), pf[i / NDB], oacc[i % NDB], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, v_operand(tt, db)), pf[tt], oacc[db], 0, 0, 0);
       }
     }
     // Schedule: the reads of kPvReadAhead MFMAs first, then one MFMA and the
