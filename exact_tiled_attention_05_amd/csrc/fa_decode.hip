@@ -71,22 +71,22 @@ __device__ __forceinline__ void e4m3x4_to_f32(unsigned w, float (&f)[4]) {
 
 // Heads per workgroup: a key's rows of G adjacent heads are contiguous in a
 // page, so G heads together make a 256-byte segment per key (one head when its
-// row alone is 256 bytes).
-template <int D, int ESIZE>
+// row alone is 256 bytes). WIDE doubles the group to 512-byte segments.
+template <int D, int ESIZE, bool WIDE>
 struct DecodeGroup {
   static constexpr int EPL = 16 / ESIZE;  // columns per lane: one 16-byte chunk
   static constexpr int CH = D / EPL;      // lanes per head row
-  static constexpr int G = CH >= 16 ? 1 : 16 / CH;
+  static constexpr int G = (CH >= 16 ? 1 : 16 / CH) * (WIDE ? 2 : 1);
 };
 
 // APPEND: keys [n_cached, nk) are this step's new keys, read from k_new / v_new;
 // the split-0 workgroup of each (b, head group) also copies them into their
 // cache pages. FP8: the cache holds E4M3 codes (no append).
-template <int D, bool SOFTCAP, bool ALIBI, bool APPEND, bool FP8>
+template <int D, bool SOFTCAP, bool ALIBI, bool APPEND, bool FP8, bool WIDE>
 __device__ __forceinline__ void decode_body(const FwdParams& p) {
   static_assert(!(FP8 && APPEND), "no append into an E4M3 cache");
   using E = std::conditional_t<FP8, uint8_t, uint16_t>;  // cache element
-  using DG = DecodeGroup<D, (int)sizeof(E)>;
+  using DG = DecodeGroup<D, (int)sizeof(E), WIDE>;
   constexpr int EPL = DG::EPL;
   constexpr int CH = DG::CH;      // lanes per head row
   constexpr int G = DG::G;        // heads per workgroup
@@ -313,28 +313,43 @@ __device__ __forceinline__ void decode_body(const FwdParams& p) {
   }
 }
 
-template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
+template <int D, bool SOFTCAP, bool ALIBI, bool APPEND, bool WIDE>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
-  decode_body<D, SOFTCAP, ALIBI, APPEND, false>(p);
+  decode_body<D, SOFTCAP, ALIBI, APPEND, false, WIDE>(p);
 }
 
 template <int D, bool SOFTCAP, bool ALIBI>
 __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(FwdParams p) {
-  decode_body<D, SOFTCAP, ALIBI, false, true>(p);
+  decode_body<D, SOFTCAP, ALIBI, false, true, false>(p);
 }
 
 // Workgroups of a decode launch: (head group, batch, split).
-template <int D, int ESIZE>
+template <int D, int ESIZE, bool WIDE>
 int64_t decode_groups(const FwdParams& p) {
-  constexpr int G = DecodeGroup<D, ESIZE>::G;
+  constexpr int G = DecodeGroup<D, ESIZE, WIDE>::G;
   return (int64_t)((p.H + G - 1) / G) * p.B * p.num_splits;
+}
+
+// Wide groups (two 256-byte heads per workgroup, 512-byte segments) stream the
+// cache 2-4% faster on MI355X, but halve the workgroup count: they are used
+// when the launch still has a workgroup per compute unit (256) and each split
+// holds at least 1024 keys; smaller launches are latency-bound and keep one
+// head per workgroup.
+constexpr int64_t kWideMinGroups = 256;
+constexpr int64_t kWideMinSplitKeys = 1024;
+template <int D>
+bool decode_wide(const FwdParams& p) {
+  if (D != 128) return false;
+  const int64_t a = p.split_align;
+  const int64_t chunk = ((p.Nk + (int64_t)p.num_splits - 1) / p.num_splits + a - 1) / a * a;
+  return decode_groups<D, 2, true>(p) >= kWideMinGroups && chunk >= kWideMinSplitKeys;
 }
 
 }  // namespace
 
 template <int D, bool SOFTCAP, bool ALIBI>
 int launch_decode_fp8(const FwdParams& p, void* stream) {
-  const int64_t groups = decode_groups<D, 1>(p);
+  const int64_t groups = decode_groups<D, 1, false>(p);
   hipLaunchKernelGGL((decode_fp8_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)groups),
                      dim3(kThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
@@ -342,9 +357,17 @@ int launch_decode_fp8(const FwdParams& p, void* stream) {
 
 template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream) {
-  const int64_t groups = decode_groups<D, 2>(p);
-  hipLaunchKernelGGL((decode_bf16_kernel<D, SOFTCAP, ALIBI, APPEND>), dim3((unsigned)groups),
-                     dim3(kThreads), 0, (hipStream_t)stream, p);
+  if constexpr (D == 128) {
+    if (decode_wide<D>(p)) {
+      const int64_t groups = decode_groups<D, 2, true>(p);
+      hipLaunchKernelGGL((decode_bf16_kernel<D, SOFTCAP, ALIBI, APPEND, true>),
+                         dim3((unsigned)groups), dim3(kThreads), 0, (hipStream_t)stream, p);
+      return (int)hipGetLastError();
+    }
+  }
+  const int64_t groups = decode_groups<D, 2, false>(p);
+  hipLaunchKernelGGL((decode_bf16_kernel<D, SOFTCAP, ALIBI, APPEND, false>),
+                     dim3((unsigned)groups), dim3(kThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 

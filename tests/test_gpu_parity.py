@@ -528,6 +528,63 @@ def test_splitkv_append_small(case):
     check(o.cpu().numpy().transpose(0, 2, 1, 3), lse.cpu().numpy(), ro, rl, dtype, "combined")
 
 
+WIDE_CASES = [
+    # (H, seqlens or None, window_left, alibi, softcap, append one key per sequence)
+    (33, None, -1, False, 0.0, False),
+    (32, [8192, 5000, 1, 0], 3000, True, 30.0, False),
+    (31, [8000, 4095, 0, 8191], -1, True, 0.0, True),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES)
+def test_decode_wide_head_groups(case):
+    """Decode launches large enough for two 256-byte heads per workgroup (at least
+    256 workgroups and 1024 keys per split): odd head counts (the last group holds
+    one head), per-sequence lengths, a window, ALiBi, softcap and appended keys;
+    the partials and the combined output against the oracle."""
+    H, seqlens, wl, alibi, cap, append = case
+    B, nk, d, ps, S = 4, 8192, 128, 256, 8
+    assert (H + 1) // 2 * B * S >= 256 and nk // S >= 1024  # the launch takes wide groups
+    seed = 7600 + WIDE_CASES.index(case)
+    say(f"wide decode {case}")
+    w = W.Workload(0, "wide", B=B, H=H, Nq=1, Nk=nk, d=d, dtype="bf16", causal=True, paged=True,
+                   page_size=ps, pool_factor=1.2, num_splits=S, seed=seed)
+    lens = seqlens if seqlens is not None else [nk] * B
+    q, kc, vc, bt = W.gen_paged(w, seqlens=lens)
+    slopes = W.alibi_slopes(H) if alibi else None
+    ts = None if slopes is None else torch.from_numpy(slopes).cuda()
+    scale = 1.0 / np.sqrt(d)
+    tq, tkc, tvc, tbt = to_dev(q, "bf16"), to_dev(kc, "bf16"), to_dev(vc, "bf16"), torch.from_numpy(bt).cuda()
+    tsl = torch.tensor(lens, dtype=torch.int32).cuda()
+    if append:
+        kn = W.gen_tensor(seed + 500, W.TENSOR_K, B, 1, H, d, 1.0, "bf16")
+        vn = W.gen_tensor(seed + 500, W.TENSOR_V, B, 1, H, d, 1.0, "bf16")
+        o_part, lse_part = fa.attention_paged_append(tq, to_dev(kn, "bf16"), to_dev(vn, "bf16"), tkc,
+                                                     tvc, tbt, tsl, nk, S, scale, True, wl, -1, ts, cap)
+    else:
+        o_part, lse_part = fa.attention_paged_splitkv(tq, tkc, tvc, tbt, nk, S, scale, True, wl, -1,
+                                                      ts, cap, cache_seqlens=tsl)
+    o, lse = fa.combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    qf = W.to_float(q, "bf16")
+    k = np.zeros((B, nk, H, d), dtype=np.float32)
+    v = np.zeros((B, nk, H, d), dtype=np.float32)
+    for b, n in enumerate(lens):
+        k[b, :n] = W.to_float(O.paged_gather_ref(kc, bt, b, n), "bf16")
+        v[b, :n] = W.to_float(O.paged_gather_ref(vc, bt, b, n), "bf16")
+    if append:
+        want_k, want_v = O.kvcache_append_ref(kc, vc, bt, lens, kn, vn)
+        assert np.array_equal(bits(from_dev(tkc, "bf16")), bits(want_k))
+        assert np.array_equal(bits(from_dev(tvc, "bf16")), bits(want_v))
+        rop, rlp = O.splitkv_append_ref(qf, k, v, W.to_float(kn, "bf16"), W.to_float(vn, "bf16"),
+                                        lens, S, ps, scale, True, wl, -1, slopes, cap)
+    else:
+        rop, rlp = O.splitkv_ref(qf, k, v, S, ps, scale, True, wl, -1, slopes, cap, seqlens_k=lens)
+    check(o_part.cpu().numpy(), lse_part.cpu().numpy(), rop, rlp, "bf16", "wide partials")
+    ro, rl = O.combine_ref(rop, rlp)
+    check(o.cpu().numpy().transpose(0, 2, 1, 3), lse.cpu().numpy(), ro, rl, "bf16", "wide combined")
+
+
 def test_incremental_decode_three_steps():
     """Three decode steps, each appending one token per sequence and attending
     over everything cached so far, against the oracle on the growing cache."""
