@@ -161,6 +161,13 @@ __device__ __forceinline__ void decode_body(const FwdParams& p) {
       qp[e] = as_bf16x2(wq);
     }
   }
+  // ALiBi distances are taken from the workgroup's last key (kref), not from the
+  // query: for a split far from the query the bias is then small for the keys
+  // that carry its weight, instead of thousands of log2 units that fp32 holds
+  // to ~1e-4. The dropped constant slope * (ip - kref) is the same for every key
+  // of the workgroup, so it leaves the normalised partial unchanged and is
+  // subtracted from its log-sum-exp at the end.
+  const int kref = hi - 1;
   float slope_log2 = 0.0f;
   if constexpr (ALIBI) slope_log2 = p.alibi[h] * kLog2e;
 
@@ -234,7 +241,7 @@ __device__ __forceinline__ void decode_body(const FwdParams& p) {
         a *= p.scale_log2;
       }
       const int t = base + g + KPI * u;
-      if constexpr (ALIBI) a -= slope_log2 * (float)(ip - t);
+      if constexpr (ALIBI) a -= slope_log2 * (float)(kref - t);
       sc[u] = t < hi ? a : kNegInf;
     }
     float mb = sc[0];
@@ -290,9 +297,9 @@ __device__ __forceinline__ void decode_body(const FwdParams& p) {
     }
   }
   __syncthreads();
-  static_assert(G * D <= kThreads, "one output column per thread");
-  const int oh = tid / D, col = tid % D;  // head in the group, column
-  if (tid < G * D && h0 + oh < p.H) {
+  for (int t = tid; t < G * D; t += kThreads) {
+    const int oh = t / D, col = t % D;  // head in the group, column
+    if (h0 + oh >= p.H) continue;
     float M = kNegInf;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) M = fmaxf(M, s_m[i][oh]);
@@ -302,14 +309,18 @@ __device__ __forceinline__ void decode_body(const FwdParams& p) {
       for (int i = 0; i < kWaves; ++i) {
         const float a = s_m[i][oh] == kNegInf ? 0.0f : fast_exp2(s_m[i][oh] - M);
         L += a * s_l[i][oh];
-        acc += a * s_o[i][tid];
+        acc += a * s_o[i][t];
       }
     }
     const int64_t ro = (((int64_t)s * p.B + b) * p.H + h0 + oh) * p.Nq;
     float out = L > 0.0f ? acc / L : 0.0f;
     if constexpr (FP8) out *= p.v_descale;
     p.o_part[ro * D + col] = out;
-    if (col == 0) p.lse_part[ro] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
+    if (col == 0) {
+      float mref = M;  // the maximum in query-relative units
+      if constexpr (ALIBI) mref -= p.alibi[h0 + oh] * kLog2e * (float)(ip - kref);
+      p.lse_part[ro] = L > 0.0f ? (mref + __log2f(L)) * kLn2 : kNegInf;
+    }
   }
 }
 
@@ -318,9 +329,9 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(FwdParams p) {
   decode_body<D, SOFTCAP, ALIBI, APPEND, false, WIDE>(p);
 }
 
-template <int D, bool SOFTCAP, bool ALIBI>
+template <int D, bool SOFTCAP, bool ALIBI, bool WIDE>
 __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(FwdParams p) {
-  decode_body<D, SOFTCAP, ALIBI, false, true, false>(p);
+  decode_body<D, SOFTCAP, ALIBI, false, true, WIDE>(p);
 }
 
 // Workgroups of a decode launch: (head group, batch, split).
@@ -330,27 +341,35 @@ int64_t decode_groups(const FwdParams& p) {
   return (int64_t)((p.H + G - 1) / G) * p.B * p.num_splits;
 }
 
-// Wide groups (two 256-byte heads per workgroup, 512-byte segments) stream the
-// cache 2-4% faster on MI355X, but halve the workgroup count: they are used
-// when the launch still has a workgroup per compute unit (256) and each split
-// holds at least 1024 keys; smaller launches are latency-bound and keep one
-// head per workgroup.
+// Wide groups (twice the heads per workgroup: 512-byte segments of a key's
+// rows) stream the cache 2-6% faster on MI355X at head_dim 128, but halve the
+// workgroup count: they are used when the launch still has a workgroup per
+// compute unit (256) and each split holds at least 1024 keys; smaller launches
+// are latency-bound and keep 256-byte segments.
 constexpr int64_t kWideMinGroups = 256;
 constexpr int64_t kWideMinSplitKeys = 1024;
-template <int D>
+template <int D, int ESIZE>
 bool decode_wide(const FwdParams& p) {
   if (D != 128) return false;
   const int64_t a = p.split_align;
   const int64_t chunk = ((p.Nk + (int64_t)p.num_splits - 1) / p.num_splits + a - 1) / a * a;
-  return decode_groups<D, 2, true>(p) >= kWideMinGroups && chunk >= kWideMinSplitKeys;
+  return decode_groups<D, ESIZE, true>(p) >= kWideMinGroups && chunk >= kWideMinSplitKeys;
 }
 
 }  // namespace
 
 template <int D, bool SOFTCAP, bool ALIBI>
 int launch_decode_fp8(const FwdParams& p, void* stream) {
+  if constexpr (D == 128) {
+    if (decode_wide<D, 1>(p)) {
+      const int64_t groups = decode_groups<D, 1, true>(p);
+      hipLaunchKernelGGL((decode_fp8_kernel<D, SOFTCAP, ALIBI, true>), dim3((unsigned)groups),
+                         dim3(kThreads), 0, (hipStream_t)stream, p);
+      return (int)hipGetLastError();
+    }
+  }
   const int64_t groups = decode_groups<D, 1, false>(p);
-  hipLaunchKernelGGL((decode_fp8_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)groups),
+  hipLaunchKernelGGL((decode_fp8_kernel<D, SOFTCAP, ALIBI, false>), dim3((unsigned)groups),
                      dim3(kThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
@@ -358,7 +377,7 @@ int launch_decode_fp8(const FwdParams& p, void* stream) {
 template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream) {
   if constexpr (D == 128) {
-    if (decode_wide<D>(p)) {
+    if (decode_wide<D, 2>(p)) {
       const int64_t groups = decode_groups<D, 2, true>(p);
       hipLaunchKernelGGL((decode_bf16_kernel<D, SOFTCAP, ALIBI, APPEND, true>),
                          dim3((unsigned)groups), dim3(kThreads), 0, (hipStream_t)stream, p);

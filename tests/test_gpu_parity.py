@@ -1240,6 +1240,10 @@ FP8_DECODE_CASES = [
     (128, 2, 300, 7, 3, [300, 4, 0, 150], True, 50, 0, False, 10.0, 1.0, 1.0),
     (64, 2, 500, 32, 5, None, False, -1, -1, False, 0.0, 3.0, 1.0),
     (128, 1, 2000, 128, 7, [2000, 1999, 1000], False, 300, 40, True, 0.0, 0.75, 0.5),
+    # Large enough for four heads per workgroup (at least 256 workgroups, 1024 keys per split);
+    # 33 and 31 heads leave a partial last group.
+    (128, 33, 8192, 256, 8, [8192, 5000, 1, 0], True, 3000, 0, True, 30.0, 0.5, 0.25),
+    (128, 31, 8192, 256, 8, [8192] * 4, True, -1, -1, False, 0.0, 1.0, 1.0),
 ]
 
 
