@@ -93,6 +93,17 @@ __device__ __forceinline__ KeyBounds key_bounds(int r0, int r1, int off, int slo
   return kb;
 }
 
+// ALiBi anchor of a row: its diagonal position i' clamped into its visible keys
+// [lo, hi). For every visible key j, |i' - j| = |i' - a| + |a - j|, so biases
+// measured from the anchor give the same softmax over the row's keys, and the
+// dropped constant slope * |i' - a| is subtracted from the row's log-sum-exp.
+// In a key split far from the row, the keys that carry the split's weight then
+// keep small biases instead of thousands of log2 units (where fp32 resolves
+// only ~1e-4).
+__device__ __forceinline__ int alibi_anchor(int ip, const KeyBounds& rk) {
+  return rk.hi > rk.lo ? min(max(ip, rk.lo), rk.hi - 1) : ip;
+}
+
 // Score units. Without a softcap or ALiBi the kernels keep the raw dot product
 // q.k and fold softmax_scale * log2(e) into the exponent (one FMA per score);
 // with either transform the transform itself yields log2-domain scores and the

@@ -286,7 +286,7 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) t[j][v] = sacc[j][v];
-    const float rel = (float)(row + off) - (float)(j0 + 4 * h2);
+    const float rel = (float)(ALIBI ? alibi_anchor(row + off, rk) : row + off) - (float)(j0 + 4 * h2);
     transform_scores<2, SOFTCAP, ALIBI>(t, p, slope_log2, rel, MASKED, j0, rk.lo, rk.hi, h2);
     bool any_rescale;
     float mc;
@@ -471,7 +471,9 @@ void fwd_bf16_kernel(FwdParams p) {
   const float l_ex = half_sum(l_exact);
   if (row >= nq) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse = l_ex > 0.0f ? (m_run * c + __log2f(l_ex)) * kLn2 : kNegInf;
+  float mref = m_run * c;  // the maximum in units of the unshifted ALiBi bias
+  if constexpr (ALIBI) mref -= slope_log2 * (float)abs(row + off - alibi_anchor(row + off, rk));
+  const float lse = l_ex > 0.0f ? (mref + __log2f(l_ex)) * kLn2 : kNegInf;
   if constexpr (SPLIT) {
     const int64_t ro = (((int64_t)s * p.B + b) * p.H + h) * p.Nq + row;
     float* op = p.o_part + ro * D;

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) t[0][v] = sacc[v];
     const bool full = j0 >= wk.flo && j0 + kBN <= wk.fhi;
-    const float rel = (float)(row + off) - (float)(j0 + 4 * h2);
+    const float rel = (float)(ALIBI ? alibi_anchor(row + off, rk) : row + off) - (float)(j0 + 4 * h2);
     transform_scores<1, SOFTCAP, ALIBI>(t, p, slope_log2, rel, !full, j0, rk.lo, rk.hi, h2);
 
     bool any_rescale;
@@ -130,7 +130,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
   const float l_tot = half_sum(l_run);
   if (row >= nq) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse = l_tot > 0.0f ? (m_run * c + __log2f(l_tot)) * kLn2 : kNegInf;
+  float mref = m_run * c;  // the maximum in units of the unshifted ALiBi bias
+  if constexpr (ALIBI) mref -= slope_log2 * (float)abs(row + off - alibi_anchor(row + off, rk));
+  const float lse = l_tot > 0.0f ? (mref + __log2f(l_tot)) * kLn2 : kNegInf;
   if constexpr (PAGED) {
     const int64_t ro = (((int64_t)s * p.B + b) * p.H + h) * p.Nq + row;
     float* op = p.o_part + ro * D;

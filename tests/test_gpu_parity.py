@@ -528,6 +528,35 @@ def test_splitkv_append_small(case):
     check(o.cpu().numpy().transpose(0, 2, 1, 3), lse.cpu().numpy(), ro, rl, dtype, "combined")
 
 
+@pytest.mark.parametrize("dtype,nq", [("fp32", 1), ("fp32", 5), ("bf16", 1), ("bf16", 70)])
+def test_alibi_far_splits_keep_fp32_precision(dtype, nq):
+    """Splits thousands of keys away from the query rows under a strong ALiBi
+    slope (0.5 per key): each split's partial output is still held to its input's
+    bound (fp32: 1e-5), i.e. the bias of the keys that carry a split's weight
+    is not swamped by the distance to the query."""
+    B, H, d, nk, ps, S = 1, 2, 64, 4000, 64, 4
+    say(f"alibi far splits {dtype} nq{nq}")
+    w = W.Workload(0, "far", B=B, H=H, Nq=nq, Nk=nk, d=d, dtype=dtype, causal=True, paged=True,
+                   page_size=ps, pool_factor=1.1, num_splits=S, seed=7700 + nq)
+    q, kc, vc, bt = W.gen_paged(w)
+    slopes = np.array([0.5, 0.125], dtype=np.float32)
+    scale = 1.0 / np.sqrt(d)
+    o_part, lse_part = fa.attention_paged_splitkv(
+        to_dev(q, dtype), to_dev(kc, dtype), to_dev(vc, dtype), torch.from_numpy(bt).cuda(), nk,
+        S, scale, True, -1, -1, torch.from_numpy(slopes).cuda(), 0.0)
+    o, lse = fa.combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    k = np.zeros((B, nk, H, d))
+    v = np.zeros((B, nk, H, d))
+    k[0] = O.paged_gather_ref(W.to_float(kc, dtype), bt, 0, nk)
+    v[0] = O.paged_gather_ref(W.to_float(vc, dtype), bt, 0, nk)
+    rop, rlp = O.splitkv_ref(W.to_float(q, dtype), k, v, S, ps, scale, True, -1, -1, slopes, 0.0)
+    assert np.isfinite(rlp).all() and rlp.min() < -1000  # far splits: tiny but nonzero weight
+    check(o_part.cpu().numpy(), lse_part.cpu().numpy(), rop, rlp, dtype, "far partials")
+    ro, rl = O.combine_ref(rop, rlp)
+    check(o.cpu().numpy().transpose(0, 2, 1, 3), lse.cpu().numpy(), ro, rl, dtype, "combined")
+
+
 WIDE_CASES = [
     # (H, seqlens or None, window_left, alibi, softcap, append one key per sequence)
     (33, None, -1, False, 0.0, False),
