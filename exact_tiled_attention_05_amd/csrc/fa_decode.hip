@@ -4,10 +4,11 @@
 // for pages addressed through block_table; the inference article's point that
 // decode time goes to loading the cache when the query is one token).
 //
-// One workgroup of 4 wavefronts per (split, head, batch), head fastest. Each
-// lane owns a 16-byte chunk of a key row (8 bf16 or 16 E4M3 columns), so
-// D / 8 (bf16) or D / 16 (E4M3) lanes share a row and a wavefront-wide load
-// reads several whole rows. A lane keeps 8 K and 8 V loads in flight per
+// One workgroup of 4 wavefronts per (split, head group, batch), head group
+// fastest: the adjacent heads whose rows of one key form a 256-byte segment of
+// the page (512 bytes on large launches). Each lane owns a 16-byte chunk of a
+// key row (8 bf16 or 16 E4M3 columns), so D / 8 (bf16) or D / 16 (E4M3) lanes
+// share a row and a wavefront-wide load reads several whole segments. A lane keeps 8 K and 8 V loads in flight per
 // batch. Scores are reduced across the row's lanes with DPP, and each lane
 // runs an fp32 online softmax over its group's keys for its output columns.
 // Groups, then wavefronts, are merged by log-sum-exp at the end. With an
