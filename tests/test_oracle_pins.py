@@ -709,6 +709,145 @@ def test_t26_backward_row_term_is_do_dot_o():
     np.testing.assert_allclose(D, np.einsum("bihd,bihd->bhi", g, o), atol=1e-12)
 
 
+# T31: the backward's tolerance magnitudes ------------------------------------------
+def _loop_backward(q, k, v, g, scale, causal, wl, wr, slope, cap, p_pert=None, dz_pert=None,
+                   dpd_pert=None):
+    """dQ, dK, dV by pure-Python per-element loops, with optional perturbations of the
+    intermediates the kernels round: p_pert(i, j) is added to P_ij where it enters
+    dV = P^T dO, dpd_pert(i, j) to dP_ij - D_i, dz_pert(i, j) to dZ_ij where it enters
+    dQ and dK. Also returns the unperturbed P, dZ, O, the cap derivative (1 - tanh^2)
+    and the absolute-term sums of the two dot products, A_ij = sum_c |dO_ic v_jc| and
+    B_i = sum_c |dO_ic O_ic|."""
+    nq, d = len(q), len(q[0])
+    nk = len(k)
+    zero = lambda i, j: 0.0  # noqa: E731
+    p_pert, dz_pert, dpd_pert = p_pert or zero, dz_pert or zero, dpd_pert or zero
+    P = [[0.0] * nk for _ in range(nq)]
+    T = [[1.0] * nk for _ in range(nq)]
+    for i in range(nq):
+        ip = i + nk - nq
+        row = {}
+        for j in range(nk):
+            if (causal and j > ip) or (wl >= 0 and j < ip - wl) or (wr >= 0 and j > ip + wr):
+                continue
+            z = scale * sum(q[i][c] * k[j][c] for c in range(d))
+            s = z
+            if cap > 0:
+                t = math.tanh(z / cap)
+                s = cap * t
+                T[i][j] = 1.0 - t * t
+            if slope is not None:
+                s -= slope * abs(ip - j)
+            row[j] = s
+        if row:
+            m = max(row.values())
+            den = sum(math.exp(x - m) for x in row.values())
+            for j, x in row.items():
+                P[i][j] = math.exp(x - m) / den
+    O_ = [[sum(P[i][j] * v[j][c] for j in range(nk)) for c in range(d)] for i in range(nq)]
+    A = [[sum(abs(g[i][c] * v[j][c]) for c in range(d)) for j in range(nk)] for i in range(nq)]
+    B = [sum(abs(g[i][c] * O_[i][c]) for c in range(d)) for i in range(nq)]
+    dz0 = [[0.0] * nk for _ in range(nq)]
+    dz = [[0.0] * nk for _ in range(nq)]
+    for i in range(nq):
+        Di = sum(g[i][c] * O_[i][c] for c in range(d))
+        for j in range(nk):
+            dp = sum(g[i][c] * v[j][c] for c in range(d))
+            dz0[i][j] = P[i][j] * (dp - Di) * T[i][j]
+            dz[i][j] = P[i][j] * (dp - Di + dpd_pert(i, j)) * T[i][j] + dz_pert(i, j)
+    dq = [[scale * sum(dz[i][j] * k[j][c] for j in range(nk)) for c in range(d)] for i in range(nq)]
+    dk = [[scale * sum(dz[i][j] * q[i][c] for i in range(nq)) for c in range(d)] for j in range(nk)]
+    dv = [[sum((P[i][j] + p_pert(i, j)) * g[i][c] for i in range(nq)) for c in range(d)]
+          for j in range(nk)]
+    return np.array(dq), np.array(dk), np.array(dv), P, dz0, T, A, B
+
+
+@pytest.mark.parametrize("nq,nk,causal,wl,wr,slope,cap", [
+    (3, 5, False, -1, -1, None, 0.0), (4, 4, True, -1, -1, 0.3, 0.0),
+    (5, 3, True, -1, -1, None, 0.0),          # Nq > Nk: rows (and dQ bounds) that are 0
+    (4, 5, False, 1, 2, 0.2, 0.0), (3, 6, True, 2, 0, None, 1.5), (4, 4, False, -1, -1, 0.4, 2.0)])
+def test_t31_backward_bounds_are_the_worst_case_perturbations(nq, nk, causal, wl, wr, slope, cap):
+    """The magnitudes that set the backward's tolerances, against their meaning rather
+    than their formula. A relative change of at most r in every P_ij (where it meets dO)
+    moves dV_jc by at most r * bound_dv; of every dZ_ij, dQ_ic and dK_jc by r * bound_dq
+    and r * bound_dk; an error of at most e (A_ij + B_i) in dP_ij - D_i (the error bound
+    of the two fp32 dot products: e times the sum of the absolute values of their terms)
+    moves dQ_ic and dK_jc by at most e * the cancellation magnitudes. Each bound is found
+    here as the largest change over every sign pattern of those perturbations (each
+    output is linear in them, so the largest sits at a vertex), by loop backwards that
+    share nothing with the oracle. Without a cap the bounds are attained exactly; with
+    one the cancellation magnitudes take P where the perturbation meets P (1 - tanh^2),
+    so they must be at least the largest change."""
+    d, scale, r, e = 3, 0.7, 2.0 ** -8, 2.0 ** -16
+    qa, ka, va, ga = rnd(96, nq, d), rnd(97, nk, d), rnd(98, nk, d), rnd(99, nq, d)
+    q, k, v, g = (x.tolist() for x in (qa, ka, va, ga))
+    args = (scale, causal, wl, wr, slope, cap)
+    dq0, dk0, dv0, P, dz0, T, A, B = _loop_backward(q, k, v, g, *args)
+    _, _, _, _, bd = O.attention_bwd_bh(qa, ka, va, ga, nq, *args, with_bounds=True)
+
+    def worst(n_signs, make_pert, which):
+        best = None
+        for sig in itertools.product((-1.0, 1.0), repeat=n_signs):
+            out = _loop_backward(q, k, v, g, *args, **make_pert(sig))
+            ch = np.abs(out[which] - (dq0, dk0, dv0)[which])
+            best = ch if best is None else np.maximum(best, ch)
+        return best
+
+    got = {
+        "dq": worst(nk, lambda s: {"dz_pert": lambda i, j: r * s[j] * abs(dz0[i][j])}, 0) / r,
+        "dk": worst(nq, lambda s: {"dz_pert": lambda i, j: r * s[i] * abs(dz0[i][j])}, 1) / r,
+        "dv": worst(nq, lambda s: {"p_pert": lambda i, j: r * s[i] * P[i][j]}, 2) / r,
+        "dq_cancel": worst(nk, lambda s: {"dpd_pert": lambda i, j: e * s[j] * (A[i][j] + B[i])},
+                           0) / e,
+        "dk_cancel": worst(nq, lambda s: {"dpd_pert": lambda i, j: e * s[i] * (A[i][j] + B[i])},
+                           1) / e,
+    }
+    for name, want in got.items():
+        tol = 1e-9 * max(float(np.abs(want).max()), 1e-12)
+        if cap > 0 and name.endswith("cancel"):
+            assert np.all(bd[name] >= want - tol), name
+            assert np.all(bd[name] <= want / min(min(t) for t in T) + tol), name
+        else:
+            np.testing.assert_allclose(bd[name], want, rtol=1e-9, atol=tol, err_msg=name)
+    assert max(float(np.abs(x).max()) for x in bd.values()) > 0
+
+
+def _bf16(x):
+    """Round float64 values to bf16 (nearest even) through float32, as torch does."""
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).double().numpy()
+
+
+@pytest.mark.parametrize("causal,wl,wr,slope,cap", [(True, -1, -1, None, 0.0),
+                                                    (False, 20, 5, 0.05, 0.0),
+                                                    (True, -1, -1, 0.1, 8.0)])
+def test_t31_backward_bounds_cover_simulated_rounding(causal, wl, wr, slope, cap):
+    """The tolerance the GPU tests apply, 2^-8 * bound + 2^-16 * cancellation (bf16's unit
+    roundoff on the P and dZ operands; fp32 dot products over 64 terms), covers a
+    backward computed with exactly that rounding: P and dZ rounded to bf16 before the
+    products, dP and D summed in float32."""
+    nq, nk, d, scale = 40, 70, 64, 0.125
+    q, k, v, g = (_bf16(rnd(s, n, d) * 2.0) for s, n in ((100, nq), (101, nk), (102, nk), (103, nq)))
+    rq, rk, rv, _, bd = O.attention_bwd_bh(q, k, v, g, nq, scale, causal, wl, wr, slope, cap,
+                                           with_bounds=True)
+    s = O.scores_ref(q, k, np.arange(nq), nq, scale, causal, wl, wr, slope, cap)
+    p, _, _ = O.softmax_rows(s)
+    o = p @ v
+    dp = (g.astype(np.float32) @ v.astype(np.float32).T).astype(np.float64)
+    D = np.einsum("ic,ic->i", g.astype(np.float32), o.astype(np.float32)).astype(np.float64)
+    dz = p * (dp - D[:, None])
+    if cap > 0:
+        t = np.tanh((q @ k.T) * scale / cap)
+        dz = dz * (1.0 - t * t)
+    pb, dzb = _bf16(p), _bf16(dz)
+    sim = {"dq": scale * (dzb @ k), "dk": scale * (dzb.T @ q), "dv": pb.T @ g}
+    for name, ref, cancel in (("dq", rq, bd["dq_cancel"]), ("dk", rk, bd["dk_cancel"]),
+                              ("dv", rv, 0.0)):
+        err = np.abs(sim[name] - ref)
+        tol = 2.0 ** -8 * bd[name] + 2.0 ** -16 * cancel + 1e-12
+        assert np.all(err <= tol), (name, float((err / tol).max()))
+        assert float((err / tol).max()) > 1e-3, name   # the bound is not vacuous
+
+
 # T27-T29: fp8 inputs ----------------------------------------------------------------
 def test_t27_e4m3_decode_closed_form_and_torch():
     """E4M3 (1 sign, 4 exponent bits biased by 7, 3 mantissa bits, no infinities)."""
