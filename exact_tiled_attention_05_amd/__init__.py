@@ -127,6 +127,22 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _slopes_ptr(slopes, heads, like):
+    """ALiBi slopes as the C ABI reads them: float32 [heads], contiguous, on q's device
+    (a wrong dtype or a short tensor would be read past its end on the device)."""
+    if slopes is None:
+        return None
+    if not isinstance(slopes, torch.Tensor):
+        raise TypeError("alibi_slopes must be a torch.Tensor (float32 [heads]) or None")
+    if slopes.dtype != torch.float32:
+        raise TypeError(f"alibi_slopes must be float32, got {slopes.dtype}")
+    if slopes.dim() != 1 or slopes.shape[0] != int(heads):
+        raise ValueError(f"alibi_slopes must have shape ({int(heads)},), got {tuple(slopes.shape)}")
+    if like is not None and slopes.device != like.device:
+        raise ValueError(f"alibi_slopes lives on {slopes.device}, q on {like.device}")
+    return _ptr(slopes)
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -175,7 +191,7 @@ def fa_fwd(q, k, v, o, lse, batch, heads, seqlen_q, seqlen_k, head_dim, softmax_
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(o), _dtype_code(o), _ptr(lse),
         int(batch), int(heads), int(seqlen_q), int(seqlen_k), int(head_dim),
         float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
-        _ptr(alibi_slopes), float(softcap), _stream(stream))
+        _slopes_ptr(alibi_slopes, heads, q), float(softcap), _stream(stream))
 
 
 def fa_fwd_splitkv(q, k_cache, v_cache, block_table, max_pages_per_seq, page_size, o_part,
@@ -188,7 +204,7 @@ def fa_fwd_splitkv(q, k_cache, v_cache, block_table, max_pages_per_seq, page_siz
         int(max_pages_per_seq), int(page_size), _ptr(o_part), _ptr(lse_part), int(num_splits),
         int(batch), int(heads), int(seqlen_q), int(seqlen_k), int(head_dim),
         float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
-        _ptr(alibi_slopes), float(softcap), _stream(stream))
+        _slopes_ptr(alibi_slopes, heads, q), float(softcap), _stream(stream))
 
 
 def fa_fwd_splitkv_seqlens(q, k_cache, v_cache, block_table, max_pages_per_seq, page_size,
@@ -201,7 +217,7 @@ def fa_fwd_splitkv_seqlens(q, k_cache, v_cache, block_table, max_pages_per_seq, 
         int(max_pages_per_seq), int(page_size), _ptr(cache_seqlens), _ptr(o_part), _ptr(lse_part),
         int(num_splits), int(batch), int(heads), int(seqlen_q), int(max_seqlen_k), int(head_dim),
         float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
-        _ptr(alibi_slopes), float(softcap), _stream(stream))
+        _slopes_ptr(alibi_slopes, heads, q), float(softcap), _stream(stream))
 
 
 def fa_fwd_splitkv_append(q, k_new, v_new, k_cache, v_cache, block_table, max_pages_per_seq,
@@ -215,7 +231,7 @@ def fa_fwd_splitkv_append(q, k_new, v_new, k_cache, v_cache, block_table, max_pa
         _ptr(block_table), int(max_pages_per_seq), int(page_size), _ptr(cache_seqlens),
         _ptr(o_part), _ptr(lse_part), int(num_splits), int(batch), int(heads), int(seqlen_q),
         int(max_seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)),
-        int(window_left), int(window_right), _ptr(alibi_slopes), float(softcap),
+        int(window_left), int(window_right), _slopes_ptr(alibi_slopes, heads, q), float(softcap),
         _stream(stream))
 
 
@@ -233,7 +249,7 @@ def fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, batch, heads, s
         _ptr_fp8(q), _ptr_fp8(k), _ptr_fp8(v), float(q_descale), float(k_descale),
         float(v_descale), _ptr(o), _dtype_code(o), _ptr(lse), int(batch), int(heads),
         int(seqlen_q), int(seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)),
-        int(window_left), int(window_right), _ptr(alibi_slopes), float(softcap), _stream(stream))
+        int(window_left), int(window_right), _slopes_ptr(alibi_slopes, heads, q), float(softcap), _stream(stream))
 
 
 def fa_fwd_splitkv_fp8(q, k_cache, v_cache, k_descale, v_descale, block_table,
@@ -247,7 +263,7 @@ def fa_fwd_splitkv_fp8(q, k_cache, v_cache, k_descale, v_descale, block_table,
         _ptr(block_table), int(max_pages_per_seq), int(page_size), _ptr(cache_seqlens),
         _ptr(o_part), _ptr(lse_part), int(num_splits), int(batch), int(heads), int(seqlen_q),
         int(seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)), int(window_left),
-        int(window_right), _ptr(alibi_slopes), float(softcap), _stream(stream))
+        int(window_right), _slopes_ptr(alibi_slopes, heads, q), float(softcap), _stream(stream))
 
 
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, batch, heads, seqlen_q, seqlen_k,
@@ -258,7 +274,7 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, batch, heads, seqlen_q,
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _dtype_code(q), _dtype_code(o),
         _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq), _ptr(workspace), int(batch), int(heads),
         int(seqlen_q), int(seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)),
-        int(window_left), int(window_right), _ptr(alibi_slopes), float(softcap), _stream(stream))
+        int(window_left), int(window_right), _slopes_ptr(alibi_slopes, heads, q), float(softcap), _stream(stream))
 
 
 def fa_bwd_workspace_bytes(batch: int, heads: int, seqlen_q: int) -> int:
@@ -275,7 +291,7 @@ def fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens_q, cu
         _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq), _ptr(workspace), _ptr(cu_seqlens_q),
         _ptr(cu_seqlens_k), int(batch), int(heads), int(total_q), int(total_k),
         int(max_seqlen_q), int(max_seqlen_k), int(head_dim), float(softmax_scale),
-        int(bool(causal)), int(window_left), int(window_right), _ptr(alibi_slopes),
+        int(bool(causal)), int(window_left), int(window_right), _slopes_ptr(alibi_slopes, heads, q),
         float(softcap), _stream(stream))
 
 
@@ -289,7 +305,7 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, heads, tot
         _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(batch), int(heads), int(total_q),
         int(total_k), int(max_seqlen_q), int(max_seqlen_k), int(head_dim),
         float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
-        _ptr(alibi_slopes), float(softcap), _stream(stream))
+        _slopes_ptr(alibi_slopes, heads, q), float(softcap), _stream(stream))
 
 
 def fa_fwd_split(q, k, v, o_part, lse_part, num_splits, batch, heads, seqlen_q, seqlen_k,
@@ -300,7 +316,7 @@ def fa_fwd_split(q, k, v, o_part, lse_part, num_splits, batch, heads, seqlen_q, 
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(o_part), _ptr(lse_part),
         int(num_splits), int(batch), int(heads), int(seqlen_q), int(seqlen_k), int(head_dim),
         float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
-        _ptr(alibi_slopes), float(softcap), _stream(stream))
+        _slopes_ptr(alibi_slopes, heads, q), float(softcap), _stream(stream))
 
 
 def fa_splitkv_combine(o_part, lse_part, num_splits, batch, heads, seqlen_q, head_dim, o, lse,

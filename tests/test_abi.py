@@ -371,3 +371,24 @@ def test_num_splits_heuristic():
     for bad in [(0, 1, 1, 1, 128, 64), (1, 0, 1, 1, 128, 64), (1, 1, 0, 1, 128, 64),
                 (1, 1, 1, 0, 128, 64), (1, 1, 1, 1, 96, 64), (1, 1, 1, 1, 128, 0)]:
         assert ns(*bad, num_cus=256) == -1
+
+
+def test_binding_checks_alibi_slopes():
+    """The binding passes slopes as a raw pointer the kernels read as float32 [heads]:
+    anything else (another dtype, another length, another device) is refused before
+    the call."""
+    import torch
+    h = 4
+    assert fa._slopes_ptr(None, h, None) is None
+    with pytest.raises(TypeError):
+        fa._slopes_ptr([0.5] * h, h, None)
+    with pytest.raises(TypeError):
+        fa._slopes_ptr(torch.ones(h, dtype=torch.float64), h, None)
+    with pytest.raises(ValueError):
+        fa._slopes_ptr(torch.ones(h - 1, dtype=torch.float32), h, None)
+    with pytest.raises(ValueError):
+        fa._slopes_ptr(torch.ones(1, h, dtype=torch.float32), h, None)
+    with pytest.raises(ValueError):  # host memory, never a device pointer
+        fa._slopes_ptr(torch.ones(h, dtype=torch.float32), h, None)
+    with pytest.raises(ValueError):  # q on another device
+        fa._slopes_ptr(torch.ones(h, dtype=torch.float32), h, torch.empty(1, device="meta"))
