@@ -5,10 +5,14 @@ One step = one pass of the whole path over one batch of seeded synthetic input:
   2. fa_fwd_splitkv + fa_splitkv_combine on the paged decode
      (B=8, H=32, Nq=1, Nk=32768, d=128, bf16, 256-token pages, 16 splits),
   3. fa_fwd_split (8 key splits) + fa_splitkv_combine on the short query set
-     with ALiBi and a tanh cap (B=2, H=8, Nq=512, Nk=4096, d=128, bf16).
+     with ALiBi and a tanh cap (B=2, H=8, Nq=512, Nk=4096, d=128, bf16),
+  4. fa_fwd on the sliding-window prefill (B=1, H=16, Nq=Nk=16384, d=64, bf16,
+     causal, window_left=4096: only the in-window pairs are computed),
+  5. fa_fwd on the tiny fp32 case (B=1, H=2, Nq=Nk=128, d=64, fp32).
 `value` is the prefill's algorithmic TFLOP/s (4*B*H*d*allowed pairs over the
-prefill launch time); the decode's algorithmic GB/s and the split forward's
-TFLOP/s are reported beside it. After the timed steps, the variable-length
+prefill launch time); the decode's algorithmic GB/s, the split forward's and
+the window's TFLOP/s (each with its roofline) and the tiny case's launch time
+are reported beside it. After the timed steps, the variable-length
 entry points are timed on their own (a packed causal prefill of 8 sequences of
 seeded lengths, the decode with seeded per-sequence cache lengths, and the
 decode step that appends one key per sequence before attending), the
@@ -30,6 +34,7 @@ import numpy as np
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "exact_tiled_attention_05_amd", "csrc")
@@ -38,6 +43,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "prefill": ["fa_fwd_bf16.hip", "fa_lds.h", "fa_device.h", "fa_params.h"],
     "decode_split": ["fa_decode.hip", "fa_device.h", "fa_params.h"],
+    "window": ["fa_fwd_bf16.hip", "fa_lds.h", "fa_device.h", "fa_params.h"],
+    "short_split": ["fa_fwd_bf16.hip", "fa_lds.h", "fa_device.h", "fa_params.h"],
 }
 
 
@@ -206,6 +213,27 @@ def main():
     s_o = torch.empty((ws.B, ws.Nq, ws.H, ws.d), dtype=torch.float32, device=dev)
     s_lse = torch.empty((ws.B, ws.H, ws.Nq), dtype=torch.float32, device=dev)
     split_flops = 4.0 * ws.B * ws.H * ws.d * allowed_pairs(ws.Nq, ws.Nk, True, -1, -1)
+    split_bytes5 = (sq.numel() + sk.numel() + sv.numel()) * 2 + s_opart.numel() * 4 + s_lpart.numel() * 4
+
+    # ---- sliding-window prefill: 16384 rows over a 4096-key window (d = 64)
+    ww = W.WORKLOADS[3]
+    log(f"generating {ww.name}")
+    wq_np, wk_np, wv_np = W.gen_qkv(ww)
+    wq, wk, wv = up(wq_np, ww.dtype), up(wk_np, ww.dtype), up(wv_np, ww.dtype)
+    del wq_np, wk_np, wv_np
+    wo = torch.empty((ww.B, ww.Nq, ww.H, ww.d), dtype=torch.float32, device=dev)
+    wlse = torch.empty((ww.B, ww.H, ww.Nq), dtype=torch.float32, device=dev)
+    window_pairs = allowed_pairs(ww.Nq, ww.Nk, True, ww.window_left, ww.window_right)
+    window_flops = 4.0 * ww.B * ww.H * ww.d * window_pairs
+    window_bytes = 3 * wq.numel() * 2 + wo.numel() * 4 + wlse.numel() * 4
+
+    # ---- tiny fp32 case (launch-bound)
+    wt = W.WORKLOADS[1]
+    tq_np, tk_np, tv_np = W.gen_qkv(wt)
+    tq, tk, tv = up(tq_np, wt.dtype), up(tk_np, wt.dtype), up(tv_np, wt.dtype)
+    to_ = torch.empty((wt.B, wt.Nq, wt.H, wt.d), dtype=torch.float32, device=dev)
+    tlse = torch.empty((wt.B, wt.H, wt.Nq), dtype=torch.float32, device=dev)
+    tiny_flops = 4.0 * wt.B * wt.H * wt.d * allowed_pairs(wt.Nq, wt.Nk, False, -1, -1)
 
     stream = torch.cuda.current_stream()
 
@@ -226,42 +254,49 @@ def main():
         check(fa.fa_splitkv_combine(o_part, lse_part, S, wd.B, wd.H, wd.Nq, wd.d, do, dlse,
                                     stream), "fa_splitkv_combine")
 
-    def short_split():
+    def short_split_pass():
         check(fa.fa_fwd_split(sq, sk, sv, s_opart, s_lpart, SS, ws.B, ws.H, ws.Nq, ws.Nk, ws.d,
                               ws.scale, True, -1, -1, s_slopes, ws.softcap, stream),
               "fa_fwd_split")
+
+    def short_combine():
         check(fa.fa_splitkv_combine(s_opart, s_lpart, SS, ws.B, ws.H, ws.Nq, ws.d, s_o, s_lse,
                                     stream), "fa_splitkv_combine")
 
+    def window():
+        check(fa.fa_fwd(wq, wk, wv, wo, wlse, ww.B, ww.H, ww.Nq, ww.Nk, ww.d, ww.scale, True,
+                        ww.window_left, ww.window_right, None, 0.0, stream), "fa_fwd")
+
+    def tiny():
+        check(fa.fa_fwd(tq, tk, tv, to_, tlse, wt.B, wt.H, wt.Nq, wt.Nk, wt.d, wt.scale, False,
+                        -1, -1, None, 0.0, stream), "fa_fwd")
+
+    step_parts = [prefill, split_pass, combine_pass, short_split_pass, short_combine, window, tiny]
     log("warmup")
     for _ in range(args.warmup):
-        prefill()
-        split_pass()
-        combine_pass()
-        short_split()
+        for f in step_parts:
+            f()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(step_parts) + 1)]
+          for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
         e = ev[s]
         e[0].record(stream)
-        prefill()
-        e[1].record(stream)
-        split_pass()
-        e[2].record(stream)
-        combine_pass()
-        e[3].record(stream)
-        short_split()
-        e[4].record(stream)
+        for i, f in enumerate(step_parts):
+            f()
+            e[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_prefill = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
-    t_split = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
-    t_comb = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
-    t_short = np.array([e[3].elapsed_time(e[4]) for e in ev]) * 1e-3
+
+    def part(i):
+        return np.array([e[i].elapsed_time(e[i + 1]) for e in ev]) * 1e-3
+
+    t_prefill, t_split, t_comb, t_s5, t_s5c, t_win, t_tiny = (part(i) for i in range(len(step_parts)))
+    t_short = t_s5 + t_s5c
 
     # ---- variable sequence lengths (side measurements, after the timed steps):
     # a packed causal prefill of 8 sequences of seeded lengths in [1, 2048] at the
@@ -575,7 +610,11 @@ def main():
     dec_gbs = decode_bytes / dec_time / 1e9
     split_gbs = split_bytes / t_split.mean() / 1e9
     short_tflops = split_flops / t_short.mean() / 1e12
+    short_kernel_tflops = split_flops / t_s5.mean() / 1e12
+    win_tflops = window_flops / t_win.mean() / 1e12
+    tiny_tflops = tiny_flops / t_tiny.mean() / 1e12
     assert torch.isfinite(po).all() and torch.isfinite(do).all() and torch.isfinite(s_o).all()
+    assert torch.isfinite(wo).all() and torch.isfinite(to_).all()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -611,7 +650,9 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 inputs, seeded block-table permutation)",
         "config": {"workload": "gpt_causal_prefill B4 H16 Nq=Nk=2048 d128 bf16 causal "
                                "+ paged_splitkv_decode B8 H32 Nq1 Nk32768 d128 page256 S16 "
-                               "+ alibi_softcap_nq_ne_nk B2 H8 Nq512 Nk4096 d128 split8",
+                               "+ alibi_softcap_nq_ne_nk B2 H8 Nq512 Nk4096 d128 split8 "
+                               "+ sliding_window_16k B1 H16 Nq=Nk=16384 d64 bf16 causal wl4096 "
+                               "+ tiny_fp32_noncausal B1 H2 Nq=Nk=128 d64 fp32",
                    "prefill_gflop": round(prefill_flops / 1e9, 4),
                    "decode_gbytes": round(decode_bytes / 1e9, 5)},
         "device": device_info(torch, dev),
@@ -631,9 +672,38 @@ def main():
         "short_query_split": {"ms": round(t_short.mean() * 1e3, 5),
                               "ms_min": round(t_short.min() * 1e3, 5),
                               "ms_median": round(float(np.median(t_short)) * 1e3, 5),
+                              "split_ms": round(t_s5.mean() * 1e3, 5),
+                              "split_ms_min": round(t_s5.min() * 1e3, 5),
+                              "split_ms_max": round(t_s5.max() * 1e3, 5),
+                              "combine_ms": round(t_s5c.mean() * 1e3, 5),
                               "tflops": round(short_tflops, 3),
                               "pct_peak": round(100 * short_tflops / PEAK_BF16_TFLOPS, 2),
-                              "num_splits": SS, "gflop": round(split_flops / 1e9, 4)},
+                              "num_splits": SS, "gflop": round(split_flops / 1e9, 4),
+                              "roofline": {"bound": "mfma", "achieved": round(short_kernel_tflops, 3),
+                                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                           "frac": round(short_kernel_tflops / PEAK_BF16_TFLOPS, 4),
+                                           "traffic": measured_traffic("short_split"),
+                                           "algorithmic_bytes": int(split_bytes5),
+                                           "kernel": "fwd_bf16_kernel<128, true, true, FWD_CONTIG_SPLIT>"}},
+        "sliding_window": {"workload": "sliding_window_16k B1 H16 Nq=Nk=16384 d64 causal wl4096",
+                           "in_window_pairs_per_head": int(window_pairs),
+                           "dense_fraction": round(window_pairs / (ww.Nq * ww.Nk), 4),
+                           "gflop": round(window_flops / 1e9, 4),
+                           "ms": round(t_win.mean() * 1e3, 5), "ms_min": round(t_win.min() * 1e3, 5),
+                           "ms_median": round(float(np.median(t_win)) * 1e3, 5),
+                           "tflops": round(win_tflops, 3),
+                           "pct_peak": round(100 * win_tflops / PEAK_BF16_TFLOPS, 2),
+                           "roofline": {"bound": "mfma", "achieved": round(win_tflops, 3),
+                                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": round(win_tflops / PEAK_BF16_TFLOPS, 4),
+                                        "traffic": measured_traffic("window"),
+                                        "algorithmic_bytes": int(window_bytes),
+                                        "kernel": "fwd_bf16_kernel<64, false, false, FWD_CONTIG>"}},
+        "tiny_fp32": {"workload": "tiny_fp32_noncausal B1 H2 Nq=Nk=128 d64 fp32 (launch-bound)",
+                      "us": round(t_tiny.mean() * 1e6, 2), "us_min": round(t_tiny.min() * 1e6, 2),
+                      "us_median": round(float(np.median(t_tiny)) * 1e6, 2),
+                      "tflops": round(tiny_tflops, 4),
+                      "pct_fp32_peak": round(100 * tiny_tflops / PEAK_FP32_TFLOPS, 3)},
         "variable_lengths": variable,
         "backward": backward_line,
         "fp8_prefill": fp8_line,

@@ -104,22 +104,48 @@ def scores_ref(q_bh: np.ndarray, k_bh: np.ndarray, rows: np.ndarray, nq: int,
                scale: float, causal: bool = False, window_left: int = -1,
                window_right: int = -1, slope: float | None = None,
                softcap: float = 0.0, key_lo: int = 0,
-               key_hi: int | None = None) -> np.ndarray:
+               key_hi: int | None = None, span: tuple | None = None) -> np.ndarray:
     """S[r, j] for the selected query rows: scaled, capped, biased, masked (-inf).
 
-    q_bh: [len(rows), d] (the selected rows), k_bh: [nk, d].
+    q_bh: [len(rows), d] (the selected rows), k_bh: [nk, d]. span = (a, b): only the
+    columns of keys a..b-1 are formed (S[:, j - a] for key j; positions stay absolute).
     """
     nk = k_bh.shape[0]
-    s = (q_bh @ k_bh.T) * scale                       # standard attention: Q K^T, scaled
+    a, b = (0, nk) if span is None else span
+    s = (q_bh @ k_bh[a:b].T) * scale                  # standard attention: Q K^T, scaled
     if softcap > 0.0:                                 # v2.6: tanh cap on the scaled score
         s = softcap * np.tanh(s / softcap)
     if slope is not None:                             # v2.4: linear distance penalty
         off = nk - nq
         ip = (np.asarray(rows, dtype=np.int64) + off)[:, None]
-        j = np.arange(nk, dtype=np.int64)[None, :]
+        j = np.arange(a, b, dtype=np.int64)[None, :]
         s = s - slope * np.abs(ip - j).astype(np.float64)
-    ok = allowed_mask(nq, nk, rows, causal, window_left, window_right, key_lo, key_hi)
+    ok = allowed_mask(nq, nk, rows, causal, window_left, window_right, key_lo, key_hi)[:, a:b]
     return np.where(ok, s, NEG_INF)
+
+
+def visible_span(nq: int, nk: int, rows: np.ndarray, causal: bool, window_left: int,
+                 window_right: int, key_lo: int = 0, key_hi: int | None = None):
+    """Keys [a, b) that at least one of `rows` may see (a >= b: none).
+
+    Row i sees the interval [i' - window_left, i' + window_right] (i' = i + nk - nq;
+    causal caps the right end at i'; -1 leaves a side open) cut to [key_lo, key_hi).
+    Both ends grow with i, so every row's interval lies between the smallest row's
+    left end and the largest row's right end (for consecutive rows, whose intervals
+    touch, that is exactly their union). Keys outside it are masked for every row:
+    their probabilities are exactly 0, so leaving them out changes no result.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    off = nk - nq
+    hi_end = nk if key_hi is None else min(nk, key_hi)
+    first, last = int(rows.min()) + off, int(rows.max()) + off
+    a = key_lo if window_left < 0 else max(key_lo, first - window_left)
+    b = hi_end
+    if causal:
+        b = min(b, last + 1)
+    if window_right >= 0:
+        b = min(b, last + window_right + 1)
+    return max(0, a), max(0, b)
 
 
 def softmax_rows(s: np.ndarray):
@@ -163,11 +189,15 @@ def attention_bh(q_all, k_bh, v_bh, rows, nq, scale, causal=False, window_left=-
         return o, lse
     pos = 0
     for rc in _row_chunks(rows, k_bh.shape[0]):
-        s = scores_ref(q_all[rc], k_bh, rc, nq, scale, causal, window_left,
-                       window_right, slope, softcap, key_lo, key_hi)
-        oc, lc = attend_rows(s, v_bh)
-        o[pos:pos + len(rc)] = oc
-        lse[pos:pos + len(rc)] = lc
+        # Only the keys some row of the chunk may see (the others have P = 0).
+        a, b = visible_span(nq, k_bh.shape[0], rc, causal, window_left, window_right, key_lo,
+                            key_hi)
+        if b > a:
+            s = scores_ref(q_all[rc], k_bh, rc, nq, scale, causal, window_left,
+                           window_right, slope, softcap, key_lo, key_hi, span=(a, b))
+            oc, lc = attend_rows(s, v_bh[a:b])
+            o[pos:pos + len(rc)] = oc
+            lse[pos:pos + len(rc)] = lc
         pos += len(rc)
     return o, lse
 

@@ -1,6 +1,8 @@
 """Helpers for the GPU parity tests: upload seeded inputs, run the library, compare
 with the oracle at the stated tolerances."""
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -62,3 +64,13 @@ def e4m3_half_spacing(x):
     x = np.asarray(x, dtype=np.float64)
     e = np.floor(np.log2(np.maximum(x, 2.0 ** -6)))
     return np.where(x < 2.0 ** -6, 2.0 ** -10, np.exp2(e - 4))
+
+
+def oracle_map(fn, items):
+    """fn over items on a thread pool the size of the usable cores (at most 16): the
+    oracle's numpy work releases the interpreter lock, so independent (batch, head)
+    problems run side by side. Results come back in the order of items."""
+    items = list(items)
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(items)))
+    with ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, items))

@@ -29,7 +29,8 @@ def test_source_hashes_cover_every_measured_kernel():
     r = run_bench("--print-source-hashes")
     assert r.returncode == 0
     hashes = json.loads(r.stdout)
-    assert set(hashes) == set(bench.KERNEL_SOURCES) == {"prefill", "decode_split"}
+    assert set(hashes) == set(bench.KERNEL_SOURCES) == {"prefill", "decode_split", "window",
+                                                     "short_split"}
     for kind, h in hashes.items():
         assert h == bench.source_hash(kind) and len(h) == 64
         for f in bench.KERNEL_SOURCES[kind]:

@@ -5,6 +5,7 @@ in the oracle (a dropped transform, a wrong sign, a shifted diagonal, a
 transposed operand, a wrong log base, a wrong split rule) fails at least one.
 All CPU, float64.
 """
+import importlib
 import itertools
 import json
 import math
@@ -846,6 +847,53 @@ def test_t31_backward_bounds_cover_simulated_rounding(causal, wl, wr, slope, cap
         tol = 2.0 ** -8 * bd[name] + 2.0 ** -16 * cancel + 1e-12
         assert np.all(err <= tol), (name, float((err / tol).max()))
         assert float((err / tol).max()) > 1e-3, name   # the bound is not vacuous
+
+
+# T32: evaluating a row block over its visible key span -----------------------------
+@pytest.mark.parametrize("nq,nk", [(7, 7), (5, 12), (12, 5), (1, 9), (9, 1), (16, 40)])
+def test_t32_visible_span_is_the_masks_visible_columns(nq, nk):
+    """For every block of consecutive rows, visible_span is the first and one past the
+    last key column the mask keeps for some row of the block (the mask itself decides;
+    empty when it keeps none), for every mask and split range; for any subset of rows
+    it contains every kept column."""
+    rng = np.random.default_rng(104)
+    for causal, wl, wr in MASKS:
+        for key_lo, key_hi in [(0, None), (2, 6), (0, 3), (4, None)]:
+            for r0 in range(nq):
+                for r1 in range(r0 + 1, nq + 1):
+                    rows = np.arange(r0, r1)
+                    cols = np.flatnonzero(O.allowed_mask(nq, nk, rows, causal, wl, wr, key_lo,
+                                                         key_hi).any(axis=0))
+                    a, b = O.visible_span(nq, nk, rows, causal, wl, wr, key_lo, key_hi)
+                    if len(cols) == 0:
+                        assert b <= a or not O.allowed_mask(nq, nk, rows, causal, wl, wr, key_lo,
+                                                            key_hi)[:, a:b].any()
+                    else:
+                        assert (a, b) == (cols[0], cols[-1] + 1), (causal, wl, wr, r0, r1)
+            sub = np.sort(rng.choice(nq, size=min(nq, 3), replace=False))
+            cols = np.flatnonzero(O.allowed_mask(nq, nk, sub, causal, wl, wr).any(axis=0))
+            a, b = O.visible_span(nq, nk, sub, causal, wl, wr)
+            assert len(cols) == 0 or (a <= cols[0] and cols[-1] < b)
+
+
+@pytest.mark.parametrize("causal,wl,wr", MASKS)
+def test_t32_span_evaluation_equals_every_key(causal, wl, wr, monkeypatch):
+    """attention_bh (row blocks over their visible spans, blocks forced small) against
+    the same rows over every key in one block: masked keys contribute exactly 0."""
+    nq, nk, d = 23, 37, 5
+    q, k, v = rnd(110, nq, d), rnd(111, nk, d), rnd(112, nk, d)
+    for slope, cap in [(None, 0.0), (0.3, 2.0)]:
+        rows = np.arange(nq)
+        s = O.scores_ref(q, k, rows, nq, 0.6, causal, wl, wr, slope, cap)
+        want_o, want_l = O.attend_rows(s, v)
+        monkeypatch.setattr(importlib.import_module("oracle.attention_ref"), "_CHUNK_BYTES",
+                            8 * nk * 3 * 4)  # blocks of 4 rows
+        got_o, got_l = O.attention_bh(q, k, v, rows, nq, 0.6, causal, wl, wr, slope, cap)
+        monkeypatch.undo()
+        np.testing.assert_allclose(got_o, want_o, atol=1e-13)
+        assert np.array_equal(np.isfinite(got_l), np.isfinite(want_l))
+        np.testing.assert_allclose(got_l[np.isfinite(want_l)], want_l[np.isfinite(want_l)],
+                                   atol=1e-13)
 
 
 # T27-T29: fp8 inputs ----------------------------------------------------------------
