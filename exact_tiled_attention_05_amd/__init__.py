@@ -25,7 +25,7 @@ __all__ = [
     "FA_FP32", "FA_BF16", "FaError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
     "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_splitkv_fp8", "fa_bwd",
-    "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
+    "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
     "fa_split_chunk_len", "fa_num_splits",
     "attention", "attention_fp8", "attention_varlen", "attention_split", "attention_split_partials",
     "attention_paged_splitkv", "attention_paged_splitkv_fp8", "attention_paged_append",
@@ -39,7 +39,7 @@ _lib = None
 
 EXPORTED = ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
             "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_splitkv_fp8", "fa_bwd",
-            "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
+            "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
             "fa_split_chunk_len", "fa_num_splits")
 
 
@@ -84,6 +84,9 @@ def load_library():
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, i, vp, i, i, i, i, i, f, i,
                            i, i, vp, f, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, i, i, i, i, i, i,
+                                   f, i, i, i, vp, f, vp]
+    lib.fa_bwd_noalloc.restype = i
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, i, vp, vp, vp, i, i,
                                   i, i, i, i, i, f, i, i, i, vp, f, vp]
     lib.fa_bwd_varlen.restype = i
@@ -275,6 +278,18 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, batch, heads, seqlen_q,
         _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq), _ptr(workspace), int(batch), int(heads),
         int(seqlen_q), int(seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)),
         int(window_left), int(window_right), _slopes_ptr(alibi_slopes, heads, q), float(softcap), _stream(stream))
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, batch, heads, seqlen_q, seqlen_k,
+                   head_dim, softmax_scale, causal=False, window_left=-1, window_right=-1,
+                   alibi_slopes=None, softcap=0.0, stream=None) -> int:
+    """Call fa_bwd_noalloc (fa_bwd with the library's static row-term buffer); returns the
+    status code."""
+    return load_library().fa_bwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _dtype_code(q), _dtype_code(o),
+        _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq), int(batch), int(heads), int(seqlen_q),
+        int(seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)), int(window_left),
+        int(window_right), _slopes_ptr(alibi_slopes, heads, q), float(softcap), _stream(stream))
 
 
 def fa_bwd_workspace_bytes(batch: int, heads: int, seqlen_q: int) -> int:

@@ -10,6 +10,10 @@
 #include <algorithm>
 
 #include "fa_params.h"
+#include "fa_noalloc.h"
+
+static_assert(fa::NOALLOC_SCRATCH_BYTES == FA_NOALLOC_SCRATCH_BYTES,
+              "the header states the static buffer's size");
 
 namespace {
 
@@ -194,7 +198,7 @@ int bwd(const void* q, const void* k, const void* v, const void* o, const void* 
         float* workspace, const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int heads,
         int total_q, int total_k, int seqlen_q, int seqlen_k, int head_dim, float softmax_scale,
         int causal, int window_left, int window_right, const float* alibi_slopes, float softcap,
-        void* stream) {
+        void* stream, bool noalloc = false) {
   int st = check_kind(in_dtype, head_dim);
   if (st) return st;
   if (in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
@@ -244,6 +248,8 @@ int bwd(const void* q, const void* k, const void* v, const void* o, const void* 
       (int64_t)p.num_k_tiles * heads * batch > kMaxGroups ||
       (int64_t)p.nblk * fa::BWD_RB * heads * batch / 8 > kMaxGroups)
     return FA_ERR_SHAPE;
+  // Everything is validated: only now the static buffer's address (a HIP call).
+  if (noalloc && fa::noalloc_scratch(&p.rowterms)) return FA_ERR_HIP;
 
   const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
   int rc;
@@ -277,6 +283,10 @@ const char* fa_status_string(int status) {
     case FA_ERR_MASK: return "bad mask: windows must be >= -1 and causal needs window_right <= 0";
     case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case FA_ERR_VALUE: return "bad value: softmax_scale must be finite and > 0, softcap finite and >= 0";
+    case FA_ERR_SCRATCH:
+      return "the problem needs more than the allocation-free backward's static buffer: "
+             "fa_bwd_workspace_bytes(batch, heads, seqlen_q) must be <= FA_NOALLOC_SCRATCH_BYTES "
+             "(16 MiB per GPU); call fa_bwd with a workspace instead";
     default: return "unknown status";
   }
 }
@@ -529,6 +539,21 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   return bwd(q, k, v, o, dout, lse, in_dtype, o_dtype, dq, dk, dv, grad_dtype, workspace, nullptr,
              nullptr, batch, heads, 0, 0, seqlen_q, seqlen_k, head_dim, softmax_scale, causal,
              window_left, window_right, alibi_slopes, softcap, stream);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, int in_dtype, int o_dtype, void* dq, void* dk, void* dv,
+                   int grad_dtype, int batch, int heads, int seqlen_q, int seqlen_k,
+                   int head_dim, float softmax_scale, int causal, int window_left,
+                   int window_right, const float* alibi_slopes, float softcap, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  const int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
+  if (st) return st;
+  if (fa_bwd_workspace_bytes(batch, heads, seqlen_q) > fa::NOALLOC_SCRATCH_BYTES)
+    return FA_ERR_SCRATCH;
+  return bwd(q, k, v, o, dout, lse, in_dtype, o_dtype, dq, dk, dv, grad_dtype, nullptr, nullptr,
+             nullptr, batch, heads, 0, 0, seqlen_q, seqlen_k, head_dim, softmax_scale, causal,
+             window_left, window_right, alibi_slopes, softcap, stream, /*noalloc=*/true);
 }
 
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,

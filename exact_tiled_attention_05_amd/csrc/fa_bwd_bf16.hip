@@ -29,10 +29,12 @@
 // two stages deep, in the forward's swizzled layout.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "fa_device.h"
 #include "fa_lds.h"
+#include "fa_noalloc.h"
 
 namespace fa {
 
@@ -1024,6 +1026,35 @@ int launch_bwd_bf16(const BwdParams& p, void* stream) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, SOFTCAP, ALIBI>),
                      dim3((unsigned)((int64_t)p.num_q_tiles * p.H * p.B)), dim3(kThreads), 0, s, p);
   return (int)hipGetLastError();
+}
+
+// Row-term buffer of fa_bwd_noalloc (callers that cannot allocate device
+// memory): a static device array, one copy per GPU the library runs on, held
+// until the process ends. In host code `scratch` names a host-side stand-in;
+// its device address on the current GPU comes from hipGetSymbolAddress, looked
+// up once per device and kept.
+static __device__ __align__(256) float scratch[NOALLOC_SCRATCH_FLOATS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int noalloc_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    g_scratch_ptr[dev] = (float*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
 }
 
 #define FA_INST(D, SC, AL) template int launch_bwd_bf16<D, SC, AL>(const BwdParams&, void*);

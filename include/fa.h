@@ -71,7 +71,8 @@ enum fa_status {
   FA_ERR_UNSUPPORTED = 3, /* head_dim or dtype not instantiated */
   FA_ERR_MASK = 4,        /* window < -1, or causal with window_right > 0 */
   FA_ERR_HIP = 5,         /* the HIP runtime rejected a launch */
-  FA_ERR_VALUE = 6        /* softmax_scale not finite and > 0, softcap < 0 or not finite */
+  FA_ERR_VALUE = 6,       /* softmax_scale not finite and > 0, softcap < 0 or not finite */
+  FA_ERR_SCRATCH = 7      /* fa_bwd_noalloc: the problem exceeds its static buffer */
 };
 
 /*
@@ -316,6 +317,35 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 
 /* Bytes of the workspace fa_bwd needs (-1 for a size <= 0). */
 long long fa_bwd_workspace_bytes(int batch, int heads, int seqlen_q);
+
+/* Size of fa_bwd_noalloc's static row-term buffer on each GPU. */
+#define FA_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+
+/*
+ * fa_bwd_noalloc - fa_bwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving or training loops, and harnesses that
+ * forbid hipMalloc. Same arguments, gradients, rounding, determinism and errors
+ * as fa_bwd, without the workspace argument: the per-row terms live in a static
+ * device buffer of FA_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on
+ * every GPU it runs on until the process ends. The call allocates nothing.
+ *
+ * Limit: fa_bwd_workspace_bytes(batch, heads, seqlen_q) must not exceed
+ * FA_NOALLOC_SCRATCH_BYTES (batch * heads * ceil(seqlen_q / 32) <= 65536), else
+ * FA_ERR_SCRATCH with nothing launched.
+ *
+ * Sharing: every call on one GPU uses that GPU's one buffer, which keeps the
+ * last call's contents (each call writes every row term it reads before
+ * reading it, so no clearing is needed). Calls that overlap in time on one GPU
+ * (on different streams, or from different host threads without ordering)
+ * race on the buffer and may produce wrong gradients: order them, e.g. on one
+ * stream. The first call on a device looks up the buffer's address there (a
+ * HIP runtime query, after argument validation).
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, int in_dtype, int o_dtype, void* dq, void* dk, void* dv,
+                   int grad_dtype, int batch, int heads, int seqlen_q, int seqlen_k,
+                   int head_dim, float softmax_scale, int causal, int window_left,
+                   int window_right, const float* alibi_slopes, float softcap, void* stream);
 
 /*
  * fa_bwd_varlen - backward of fa_fwd_varlen: dQ, dK, dV of a packed batch of

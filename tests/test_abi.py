@@ -19,7 +19,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(fa.library_path()),
                                 reason="libfa.so not built (run __graft_entry__.build())")
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
-OK, NULL, SHAPE, UNSUP, MASK, HIP, VALUE = range(7)
+OK, NULL, SHAPE, UNSUP, MASK, HIP, VALUE, SCRATCH = range(8)
 
 
 def declared_functions():
@@ -55,7 +55,7 @@ def test_library_never_allocates_device_memory():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert fa.fa_status_string(s)
     assert fa.fa_status_string(99) == "unknown status"
 
@@ -287,6 +287,39 @@ def bwd(**kw):
 ])
 def test_fa_bwd_rejects(kw, code):
     assert bwd(**kw) == code
+
+
+def bwd_noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, in_dtype=1, o_dtype=0, dq=FAKE,
+             dk=FAKE, dv=FAKE, g_dtype=0, batch=1, heads=2, seqlen_q=8, seqlen_k=8,
+             head_dim=128, scale=0.1, causal=1, wl=-1, wr=-1, alibi=None, softcap=0.0, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_bwd_noalloc(
+        a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["in_dtype"], a["o_dtype"], a["dq"],
+        a["dk"], a["dv"], a["g_dtype"], a["batch"], a["heads"], a["seqlen_q"], a["seqlen_k"],
+        a["head_dim"], a["scale"], a["causal"], a["wl"], a["wr"], a["alibi"], a["softcap"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(lse=None), NULL), (dict(dv=None), NULL),
+    (dict(batch=0), SHAPE), (dict(seqlen_k=-1), SHAPE), (dict(in_dtype=0), UNSUP),
+    (dict(head_dim=96), UNSUP), (dict(causal=1, wr=2), MASK), (dict(scale=0.0), VALUE),
+    # the static buffer holds 65536 blocks of 32 rows: one block more is refused
+    (dict(batch=2, heads=32, seqlen_q=32 * 1024 + 1), SCRATCH),
+    (dict(batch=1, heads=1, seqlen_q=32 * 65536 + 1), SCRATCH),
+])
+def test_fa_bwd_noalloc_rejects(kw, code):
+    assert bwd_noalloc(**kw) == code
+
+
+def test_noalloc_limit_matches_the_workspace_rule():
+    """FA_NOALLOC_SCRATCH_BYTES (the header's figure) against fa_bwd_workspace_bytes at the
+    edge: 65536 blocks of 32 rows fit, one more does not."""
+    text = open(HEADER).read()
+    limit = int(re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \((\d+) \* 1024 \* 1024\)", text).group(1)) << 20
+    assert fa.fa_bwd_workspace_bytes(2, 32, 32 * 1024) == limit
+    assert fa.fa_bwd_workspace_bytes(2, 32, 32 * 1024 + 1) > limit
 
 
 def test_bwd_workspace_bytes():
