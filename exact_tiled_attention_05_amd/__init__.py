@@ -61,7 +61,12 @@ def load_library():
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
                            "`python -m exact_tiled_attention_05_amd.build`")
-    lib = ctypes.CDLL(_LIB_PATH)
+    _lib = declare(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def declare(lib):
+    """Set the ctypes signatures of the C ABI's functions on a loaded library."""
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa_fwd.argtypes = [vp, vp, vp, i, vp, i, vp, i, i, i, i, i, f, i, i, i, vp, f, vp]
     lib.fa_fwd.restype = i
@@ -103,7 +108,6 @@ def load_library():
     lib.fa_split_chunk_len.restype = i
     lib.fa_num_splits.argtypes = [i, i, i, i, i, i, i, i]
     lib.fa_num_splits.restype = i
-    _lib = lib
     return lib
 
 

@@ -571,7 +571,7 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   if (max_seqlen_q > kMaxSeq || max_seqlen_k > kMaxSeq) return FA_ERR_SHAPE;
   return bwd(q, k, v, o, dout, lse, in_dtype, o_dtype, dq, dk, dv, grad_dtype, workspace,
              cu_seqlens_q, cu_seqlens_k, batch, heads, total_q, total_k, max_seqlen_q,
-             max(max_seqlen_k, 1), head_dim, softmax_scale, causal, window_left, window_right,
+             std::max(max_seqlen_k, 1), head_dim, softmax_scale, causal, window_left, window_right,
              alibi_slopes, softcap, stream);
 }
 

@@ -15,8 +15,19 @@ import exact_tiled_attention_05_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(fa.library_path()),
+# FA_ABI_TEST_LIB names a host-only build of the C ABI (the same fa_api.cpp with stub
+# launchers, compiled under AddressSanitizer and UndefinedBehaviorSanitizer by
+# tests/test_abi_sanitized.py); when it is set, every call below goes to that build.
+SANITIZED_LIB = os.environ.get("FA_ABI_TEST_LIB")
+if SANITIZED_LIB:
+    fa._lib = fa.declare(ctypes.CDLL(SANITIZED_LIB))
+    fa._lib.fa_stub_launches.restype = ctypes.c_longlong
+
+pytestmark = pytest.mark.skipif(not SANITIZED_LIB and not os.path.exists(fa.library_path()),
                                 reason="libfa.so not built (run __graft_entry__.build())")
+real_library_only = pytest.mark.skipif(bool(SANITIZED_LIB), reason="inspects the built libfa.so")
+stub_launchers_only = pytest.mark.skipif(
+    not SANITIZED_LIB, reason="passes valid sizes with placeholder pointers: host-only build only")
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 OK, NULL, SHAPE, UNSUP, MASK, HIP, VALUE, SCRATCH = range(8)
@@ -36,6 +47,7 @@ def test_header_declares_the_calls():
     assert set(fa.EXPORTED) == set(names)
 
 
+@real_library_only
 def test_library_exports_every_declared_symbol():
     lib = fa.load_library()
     for n in declared_functions():
@@ -47,6 +59,7 @@ def test_library_exports_every_declared_symbol():
         assert n in exported, n
 
 
+@real_library_only
 def test_library_never_allocates_device_memory():
     out = subprocess.run(["nm", "-D", "--undefined-only", fa.library_path()], capture_output=True,
                          text=True, check=True).stdout
@@ -425,3 +438,42 @@ def test_binding_checks_alibi_slopes():
         fa._slopes_ptr(torch.ones(h, dtype=torch.float32), h, None)
     with pytest.raises(ValueError):  # q on another device
         fa._slopes_ptr(torch.ones(h, dtype=torch.float32), h, torch.empty(1, device="meta"))
+
+
+def launches():
+    return fa.load_library().fa_stub_launches()
+
+
+@stub_launchers_only
+@pytest.mark.parametrize("call,kw", [
+    (lambda **kw: fwd(**kw), dict()),
+    (lambda **kw: fwd(**kw), dict(batch=1 << 24, heads=1, seqlen_q=1, seqlen_k=1 << 28)),
+    (lambda **kw: fwd(**kw), dict(batch=1, heads=1 << 16, seqlen_q=1 << 14, seqlen_k=7)),
+    (lambda **kw: split(**kw), dict()),
+    (lambda **kw: split(**kw), dict(S=1 << 16, seqlen_k=1 << 28, maxp=(1 << 28) // 16)),
+    (lambda **kw: fsplit(**kw), dict()),
+    (lambda **kw: comb(**kw), dict()),
+    (lambda **kw: varlen(**kw), dict()),
+    (lambda **kw: split_fp8(**kw), dict()),
+    (lambda **kw: split_append(**kw), dict()),
+    (lambda **kw: fp8(**kw), dict()),
+    (lambda **kw: bwd(**kw), dict()),
+    (lambda **kw: bwd(**kw), dict(batch=1 << 10, heads=1 << 10, seqlen_q=1 << 11, seqlen_k=1)),
+    (lambda **kw: bwd_noalloc(**kw), dict()),
+])
+def test_valid_calls_reach_the_launchers(call, kw):
+    """Valid sizes, up to the stated limits, pass validation and reach the launchers with
+    parameters the kernels can run (the stubs check them); run under the sanitizers, the
+    size arithmetic on the way is free of overflow and out-of-bounds access."""
+    n = launches()
+    assert call(**kw) == OK
+    assert launches() > n
+
+
+@stub_launchers_only
+def test_refused_and_empty_calls_launch_nothing():
+    n = launches()
+    assert fwd(batch=0) == SHAPE and fwd(head_dim=96) == UNSUP and bwd(ws=None) == NULL
+    assert varlen(total_q=0, total_k=0, q=None, o=None, k=None, v=None, max_k=0) == OK
+    assert bwd_noalloc(batch=2, heads=32, seqlen_q=32 * 1024 + 1) == SCRATCH
+    assert launches() == n
