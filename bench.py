@@ -16,7 +16,8 @@ are reported beside it. After the timed steps, the variable-length
 entry points are timed on their own (a packed causal prefill of 8 sequences of
 seeded lengths, the decode with seeded per-sequence cache lengths, and the
 decode step that appends one key per sequence before attending), the
-backward pass of the causal prefill, and its forward in FP8.
+backward pass of the causal prefill, its forward in FP8 and the window's forward
+in FP8 (head_dim 64).
 Inputs are resident in device memory before the timed region starts.
 
 Prints ONE JSON line on stdout. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -475,6 +476,36 @@ def main():
                 "roofline": {"bound": "mfma", "achieved": round(f8_tflops, 3), "peak": PEAK_FP8_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(f8_tflops / PEAK_FP8_TFLOPS, 4)}}
 
+    # ---- FP8 forward on the sliding-window shape (head_dim 64; side measurement).
+    f8w = [up8(W.gen_tensor(ww.seed, t, ww.B, ww.Nq, ww.H, ww.d, 1.0, "fp8"))
+           for t in (W.TENSOR_Q, W.TENSOR_K, W.TENSOR_V)]
+
+    def fp8_window():
+        check(fa.fa_fwd_fp8(f8w[0], f8w[1], f8w[2], 1.0, 1.0, 1.0, wo, wlse, ww.B, ww.H, ww.Nq,
+                            ww.Nk, ww.d, ww.scale, True, ww.window_left, ww.window_right, None, 0.0,
+                            stream), "fa_fwd_fp8")
+
+    for _ in range(args.warmup):
+        fp8_window()
+    ev8 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for a, e in ev8:
+        a.record(stream)
+        fp8_window()
+        e.record(stream)
+    torch.cuda.synchronize()
+    t_f8w = np.array([a.elapsed_time(e) for a, e in ev8]) * 1e-3
+    assert torch.isfinite(wo).all()
+    f8w_tflops = window_flops / t_f8w.mean() / 1e12
+    fp8_window_line = {"workload": "sliding_window_16k in E4M3 (fa_fwd_fp8, head_dim 64)",
+                       "gflop": round(window_flops / 1e9, 4), "ms": round(t_f8w.mean() * 1e3, 5),
+                       "ms_median": round(float(np.median(t_f8w)) * 1e3, 5),
+                       "tflops": round(f8w_tflops, 3),
+                       "roofline": {"bound": "mfma", "achieved": round(f8w_tflops, 3),
+                                    "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                                    "frac": round(f8w_tflops / PEAK_FP8_TFLOPS, 4)}}
+    del f8w
+
     # ---- paged decode over an E4M3 cache (side measurement): the decode pool above
     # rounded to E4M3 on the device (input preparation, untimed; its NaN pages stay
     # NaN), unit descales. Half the cache bytes of the bf16 decode.
@@ -707,6 +738,7 @@ def main():
         "variable_lengths": variable,
         "backward": backward_line,
         "fp8_prefill": fp8_line,
+        "fp8_window": fp8_window_line,
         "fp8_decode": fp8_decode_line,
         "serving_step": serving_line,
         "paged_prefill_chunk": chunk_line,

@@ -492,7 +492,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, flo
   if (!q || !k || !v || !o) return FA_ERR_NULL;
   int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
   if (st) return st;
-  if (head_dim != 128) return FA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return FA_ERR_UNSUPPORTED;
   if (o_dtype != FA_FP32 && o_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
     return st;
@@ -515,10 +515,13 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, flo
               alibi_slopes, softcap, fa::FP8_BM);
   if ((int64_t)p.num_q_tiles * heads * batch > kMaxGroups) return FA_ERR_SHAPE;
   const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
-  const int rc = sc && al ? fa::launch_fwd_fp8<true, true>(p, stream)
-                 : sc     ? fa::launch_fwd_fp8<true, false>(p, stream)
-                 : al     ? fa::launch_fwd_fp8<false, true>(p, stream)
-                          : fa::launch_fwd_fp8<false, false>(p, stream);
+#define FA_FP8(D)                                              \
+  (sc && al ? fa::launch_fwd_fp8<D, true, true>(p, stream)     \
+   : sc     ? fa::launch_fwd_fp8<D, true, false>(p, stream)    \
+   : al     ? fa::launch_fwd_fp8<D, false, true>(p, stream)    \
+            : fa::launch_fwd_fp8<D, false, false>(p, stream))
+  const int rc = head_dim == 64 ? FA_FP8(64) : FA_FP8(128);
+#undef FA_FP8
   return rc ? FA_ERR_HIP : FA_OK;
 }
 

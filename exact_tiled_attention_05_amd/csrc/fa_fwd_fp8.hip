@@ -1,4 +1,4 @@
-// FP8 (E4M3) tiled attention forward for gfx950 (MI355X), head_dim 128.
+// FP8 (E4M3) tiled attention forward for gfx950 (MI355X), head_dim 64 or 128.
 //
 // Q, K and V arrive as E4M3 codes with one descale factor per tensor
 // (FlashAttention-3's FP8 forward, "IO感知技术革命: FlashAttention如何重塑大模型训练
@@ -10,7 +10,7 @@
 // and O^T += V^T P^T. The products run on the gfx950 FP8 matrix instruction
 // v_mfma_scale_f32_32x32x64_f8f6f4 (K = 64 per instruction, unit block
 // scales), so a 128-key tile takes 8 MFMAs for S and 8 for the output instead
-// of 32 + 32 in bf16. The FP8 operands need fewer registers than bf16 ones,
+// of 32 + 32 in bf16 at head_dim 128 (4 + 4 at head_dim 64). The FP8 operands need fewer registers than bf16 ones,
 // which leaves room for the 128-key score block (64 fp32 per lane) at two
 // wavefronts per SIMD; 64 KB of LDS per workgroup still lets two share a CU.
 //
@@ -34,25 +34,28 @@ namespace fa {
 
 namespace {
 
-constexpr int kD = 128;        // head_dim (bytes per K/V row of one head)
 constexpr int kBM = FP8_BM;    // query rows per workgroup
 constexpr int kBN = 128;       // keys per tile
 constexpr int kThreads = 256;  // 4 wavefronts
-constexpr int kTile = kBN * kD;  // bytes per K or V tile
-constexpr int kCPR = kD / 16;    // 16-byte chunks per row
-constexpr int kRPL = 64 / kCPR;  // rows per wavefront-wide copy
-constexpr int kLoads = kBN / kRPL / 4;  // copies per wavefront per tensor per tile
 constexpr int kNB = kBN / 32;  // 32-key blocks of S^T per tile
 constexpr int kNH = kBN / 64;  // 64-key halves: one output MFMA each per 32 head_dim rows
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
-// Chunk swizzle of a 128-byte LDS row (8 chunks): rows read together by the K
-// operand and the transposed V reads land on distinct chunks.
-__device__ __forceinline__ int swz8(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+// Chunk swizzle of an LDS row of D bytes (D / 16 chunks): the 16 rows read
+// together by a K operand load land on 16 distinct 16-byte slots of a bank
+// sweep, and so do the rows of the transposed V reads. 128-byte rows (two per
+// sweep) take three row bits; 64-byte rows (four per sweep) take rows 4 apart
+// onto the four chunks of their slot group.
+template <int D>
+__device__ __forceinline__ int swz_fp8(int r) {
+  if constexpr (D == 128) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return (r >> 2) & 3;
+}
+template <int D>
 __device__ __forceinline__ int tile_byte(int row, int chunk) {
-  return row * kD + 16 * (chunk ^ swz8(row));
+  return row * D + 16 * (chunk ^ swz_fp8<D>(row));
 }
 
 __device__ __forceinline__ i32x8_t mfma_operand(u32x4_t a, u32x4_t b) {
@@ -68,10 +71,24 @@ __device__ __forceinline__ i32x2_t ds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)p);
 }
 
-template <bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Wavefronts per SIMD the register budget is sized for: two at head_dim 128,
+// three at 64 (half the output accumulators and Q operand).
+template <int D>
+struct Fp8Waves {
+  static constexpr int kWaves = D == 128 ? 2 : 3;
+};
+
+template <int D, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Fp8Waves<D>::kWaves, Fp8Waves<D>::kWaves)))
 void fwd_fp8_kernel(FwdParams p) {
-  constexpr int NDB = kD / 32;  // 32-row blocks of O^T
+  constexpr int kD = D;             // head_dim (bytes per K/V row of one head)
+  constexpr int kTile = kBN * kD;   // bytes per K or V tile
+  constexpr int kCPR = kD / 16;     // 16-byte chunks per row
+  constexpr int kRPL = 64 / kCPR;   // rows per wavefront-wide copy
+  constexpr int kLoads = kBN / kRPL / 4;  // copies per wavefront per tensor per tile
+  constexpr int KS = kD / 64;       // k-steps of the score product (64 bytes each)
+  constexpr int NDB = kD / 32;      // 32-row blocks of O^T
   __shared__ __attribute__((aligned(1024))) uint8_t sK0[kTile];
   __shared__ __attribute__((aligned(1024))) uint8_t sK1[kTile];
   __shared__ __attribute__((aligned(1024))) uint8_t sV0[kTile];
@@ -103,11 +120,11 @@ void fwd_fp8_kernel(FwdParams p) {
   const float c = exponent_scale<SOFTCAP, ALIBI>(p);
 
   // Q of this lane's row: bytes 64ks + 32h2 .. +31 (B operand of S^T = K Q^T).
-  i32x8_t qf[2];
+  i32x8_t qf[KS];
   {
     const uint8_t* qp = (const uint8_t*)p.q + ((si.q_row0 + min(row, nq - 1)) * p.H + h) * kD + 32 * h2;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       u32x4_t x0 = *(const u32x4_t*)(qp + 64 * ks);
       u32x4_t x1 = *(const u32x4_t*)(qp + 64 * ks + 16);
       if (row >= nq) x0 = x1 = u32x4_t{0, 0, 0, 0};
@@ -127,7 +144,7 @@ void fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int trow = kRPL * (kLoads * wu + i) + lane / kCPR;
-    lane_bytes[i] = (unsigned)(trow * row_bytes + 16 * ((lane % kCPR) ^ swz8(trow)));
+    lane_bytes[i] = (unsigned)(trow * row_bytes + 16 * ((lane % kCPR) ^ swz_fp8<kD>(trow)));
   }
   auto copy_tiles = [&](uint8_t* kd, uint8_t* vd, int j0) __attribute__((always_inline)) {
     const int64_t tb = (int64_t)j0 * row_bytes;
@@ -157,10 +174,10 @@ void fwd_fp8_kernel(FwdParams p) {
     for (int j = 0; j < kNB; ++j) {
       sacc[j] = f32x16_t{};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         const int kr = 32 * j + r, ch = 4 * ks + 2 * h2;
-        const u32x4_t a0 = *(const u32x4_t*)(kt + tile_byte(kr, ch));
-        const u32x4_t a1 = *(const u32x4_t*)(kt + tile_byte(kr, ch + 1));
+        const u32x4_t a0 = *(const u32x4_t*)(kt + tile_byte<kD>(kr, ch));
+        const u32x4_t a1 = *(const u32x4_t*)(kt + tile_byte<kD>(kr, ch + 1));
         sacc[j] = mfma_fp8(mfma_operand(a0, a1), qf[ks], sacc[j]);
       }
     }
@@ -212,7 +229,7 @@ void fwd_fp8_kernel(FwdParams p) {
           const int jj = tr >> 1, g = 2 * (tr & 1) + (k >> 2), e = k & 3;
           const int key = 64 * hb + 32 * jj + 8 * g + 4 * h2 + e;
           const int ch = 2 * db + (grp & 1);
-          const i32x2_t x = ds_read_tr8(vt + tile_byte(key, ch) + 8 * pc);
+          const i32x2_t x = ds_read_tr8(vt + tile_byte<kD>(key, ch) + 8 * pc);
           a[2 * tr] = x[0];
           a[2 * tr + 1] = x[1];
         }
@@ -263,17 +280,23 @@ void fwd_fp8_kernel(FwdParams p) {
 
 }  // namespace
 
-template <bool SOFTCAP, bool ALIBI>
+template <int D, bool SOFTCAP, bool ALIBI>
 int launch_fwd_fp8(const FwdParams& p, void* stream) {
   const int64_t groups = (int64_t)p.num_q_tiles * p.H * p.B;
-  hipLaunchKernelGGL((fwd_fp8_kernel<SOFTCAP, ALIBI>), dim3((unsigned)groups), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)groups), dim3(kThreads), 0,
                      (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 
-template int launch_fwd_fp8<false, false>(const FwdParams&, void*);
-template int launch_fwd_fp8<false, true>(const FwdParams&, void*);
-template int launch_fwd_fp8<true, false>(const FwdParams&, void*);
-template int launch_fwd_fp8<true, true>(const FwdParams&, void*);
+#define FA_INST(D, SC, AL) template int launch_fwd_fp8<D, SC, AL>(const FwdParams&, void*);
+FA_INST(64, false, false)
+FA_INST(64, false, true)
+FA_INST(64, true, false)
+FA_INST(64, true, true)
+FA_INST(128, false, false)
+FA_INST(128, false, true)
+FA_INST(128, true, false)
+FA_INST(128, true, true)
+#undef FA_INST
 
 }  // namespace fa

@@ -94,8 +94,8 @@ template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 int launch_fwd_bf16(const FwdParams& p, void* stream);
 template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
 int launch_fwd_f32(const FwdParams& p, void* stream);
-template <bool SOFTCAP, bool ALIBI>
-int launch_fwd_fp8(const FwdParams& p, void* stream);  // head_dim 128
+template <int D, bool SOFTCAP, bool ALIBI>
+int launch_fwd_fp8(const FwdParams& p, void* stream);  // head_dim 64 or 128
 template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream);
 template <int D, bool SOFTCAP, bool ALIBI>

@@ -236,7 +236,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, int in_dtype,
  * 经济学"; FP8 forward support on the roadmap of "FlashAttention深度解析：从算法
  * 创新到产业变革的全面影响").
  *
- *   q, k, v   [batch, seqlen, heads, 128] E4M3 codes (OCP "E4M3FN": bias 7,
+ *   q, k, v   [batch, seqlen, heads, head_dim] E4M3 codes (OCP "E4M3FN": bias 7,
  *             no infinities, largest 448), one byte per element
  *   q_descale, k_descale, v_descale  per-tensor factors: element x stands for
  *             descale * e4m3(x); finite and > 0 (FA_ERR_VALUE otherwise)
@@ -246,7 +246,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, int in_dtype,
  * probabilities are scaled so that a row's largest is 2^8 and rounded to E4M3
  * (nearest even) for the output product, so O can differ from the exact
  * result by up to 2^-4 * sum_j P_ij |v_j| (plus fp32 rounding); O and LSE are
- * normalised by the unrounded row sum. head_dim 128 only (FA_ERR_UNSUPPORTED
+ * normalised by the unrounded row sum. head_dim 64 or 128 (FA_ERR_UNSUPPORTED
  * otherwise).
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, float k_descale,

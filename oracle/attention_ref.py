@@ -251,11 +251,15 @@ def prob_weighted_abs_ref(q, k, v, scale, causal=False, window_left=-1, window_r
             out[b, :, h] = 0.0
             continue
         for rc in _row_chunks(rows, k.shape[1]):
+            a, e = visible_span(nq, k.shape[1], rc, causal, window_left, window_right)
+            if e <= a:                                # no visible key: P = 0
+                out[b, rc, h] = 0.0
+                continue
             s = scores_ref(q[b, rc, h], k[b, :, h], rc, nq, scale, causal, window_left,
-                           window_right, slope, softcap)
+                           window_right, slope, softcap, span=(a, e))
             p, _, _ = softmax_rows(s)
             wp = p if weight is None else np.where(p > 0, weight(p), 0.0)
-            out[b, rc, h] = wp @ np.abs(v[b, :, h])
+            out[b, rc, h] = wp @ np.abs(v[b, a:e, h])
     return out
 
 

@@ -390,7 +390,7 @@ def fp8(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL),
-    (dict(batch=0), SHAPE), (dict(seqlen_k=0), SHAPE), (dict(head_dim=64), UNSUP),
+    (dict(batch=0), SHAPE), (dict(seqlen_k=0), SHAPE), (dict(head_dim=96), UNSUP),
     (dict(o_dtype=3), UNSUP), (dict(causal=1, wr=2), MASK), (dict(qd=0.0), VALUE),
     (dict(kd=-1.0), VALUE), (dict(vd=math.inf), VALUE), (dict(qd=math.nan), VALUE),
     (dict(qd=1e30, kd=1e30), VALUE), (dict(scale=0.0), VALUE),

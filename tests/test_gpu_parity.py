@@ -838,8 +838,7 @@ FP8_CASES = [
 ]
 
 
-def fp8_case(seed, B, nq, nk, H):
-    d = 128
+def fp8_case(seed, B, nq, nk, H, d=128):
     return (W.gen_tensor(seed, W.TENSOR_Q, B, nq, H, d, 1.0, "fp8"),
             W.gen_tensor(seed, W.TENSOR_K, B, nk, H, d, 1.0, "fp8"),
             W.gen_tensor(seed, W.TENSOR_V, B, nk, H, d, 1.0, "fp8"))
@@ -873,14 +872,15 @@ def to_dev_fp8(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("case", FP8_CASES)
-def test_fp8_small(case):
+def test_fp8_small(case, d):
     B, H, nq, nk, causal, wl, wr, alibi, cap, qd, kd, vd = case
-    say(f"fp8 {case}")
-    q8, k8, v8 = fp8_case(9000 + FP8_CASES.index(case), B, nq, nk, H)
+    say(f"fp8 d{d} {case}")
+    q8, k8, v8 = fp8_case(9000 + FP8_CASES.index(case) + 50 * (d == 64), B, nq, nk, H, d)
     slopes = W.alibi_slopes(H) if alibi else None
     ts = None if slopes is None else torch.from_numpy(slopes).cuda()
-    scale = 1.0 / np.sqrt(128)
+    scale = 1.0 / np.sqrt(d)
     o, lse = fa.attention_fp8(to_dev_fp8(q8), to_dev_fp8(k8), to_dev_fp8(v8), qd, kd, vd, scale,
                               causal, wl, wr, ts, cap)
     torch.cuda.synchronize()
@@ -913,6 +913,22 @@ def test_fp8_causal_prefill_sampled_heads():
     assert not np.isnan(o).any()
     check_fp8(o, lse, q8, k8, v8, (1.0, 1.0, 1.0), w.scale, True, -1, -1, None, 0.0,
               "fp8 prefill", bh=[(0, 0), (3, 15), (2, 7)])
+
+
+def test_fp8_sliding_window_head_dim_64():
+    """The 16K sliding-window shape (B1 H16 N16384 d64, causal, window 4096) in FP8:
+    three heads, every row, against the oracle on the dequantised inputs."""
+    w = W.WORKLOADS[3]
+    say("fp8 sliding window d64")
+    q8, k8, v8 = (W.gen_tensor(w.seed, t, w.B, w.Nq, w.H, w.d, 1.0, "fp8")
+                  for t in (W.TENSOR_Q, W.TENSOR_K, W.TENSOR_V))
+    o, lse = fa.attention_fp8(to_dev_fp8(q8), to_dev_fp8(k8), to_dev_fp8(v8), 1.0, 1.0, 1.0,
+                              w.scale, True, w.window_left, w.window_right)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    assert not np.isnan(o).any()
+    check_fp8(o, lse, q8, k8, v8, (1.0, 1.0, 1.0), w.scale, True, w.window_left,
+              w.window_right, None, 0.0, "fp8 window", bh=[(0, 0), (0, 9), (0, 15)])
 
 
 # --------------------------------------------------------------------------
@@ -949,7 +965,8 @@ def test_bwd_sweep_small_shapes(d):
             check_grad(dv.cpu().numpy(), rv, bd["dv"], what + " dV")
 
 
-def test_fp8_sweep_small_shapes():
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp8_sweep_small_shapes(d):
     case = 0
     for nq, nk in itertools.product(SIZES, SIZES):
         for (causal, wl, wr) in mask_variants(nq, nk):
@@ -959,12 +976,12 @@ def test_fp8_sweep_small_shapes():
             alibi = case % 3 == 1
             cap = 7.5 if case % 4 == 2 else 0.0
             ds = (0.5, 2.0, 0.25) if case % 5 == 0 else (1.0, 1.0, 1.0)
-            what = f"fp8 nq{nq} nk{nk} causal{causal} wl{wl} wr{wr} alibi{alibi} cap{cap} ds{ds}"
+            what = f"fp8 d{d} nq{nq} nk{nk} causal{causal} wl{wl} wr{wr} alibi{alibi} cap{cap} ds{ds}"
             say(what)
-            q8, k8, v8 = fp8_case(30000 + case, 1 + case % 2, nq, nk, 2)
+            q8, k8, v8 = fp8_case(30000 + case + 5000 * (d == 64), 1 + case % 2, nq, nk, 2, d)
             slopes = W.alibi_slopes(2) if alibi else None
             ts = None if slopes is None else torch.from_numpy(slopes).cuda()
-            scale = 1.0 / np.sqrt(128)
+            scale = 1.0 / np.sqrt(d)
             o, lse = fa.attention_fp8(to_dev_fp8(q8), to_dev_fp8(k8), to_dev_fp8(v8), *ds, scale,
                                       causal, wl, wr, ts, cap)
             torch.cuda.synchronize()

@@ -894,6 +894,17 @@ def test_t32_span_evaluation_equals_every_key(causal, wl, wr, monkeypatch):
         assert np.array_equal(np.isfinite(got_l), np.isfinite(want_l))
         np.testing.assert_allclose(got_l[np.isfinite(want_l)], want_l[np.isfinite(want_l)],
                                    atol=1e-13)
+        # The probability-weighted bound over the spans against every key.
+        p_all, _, _ = O.softmax_rows(s)
+        for weight in (None, lambda x: 0.5 * np.sqrt(x)):
+            want = (p_all if weight is None else np.where(p_all > 0, weight(p_all), 0.0)) @ np.abs(v)
+            monkeypatch.setattr(importlib.import_module("oracle.attention_ref"), "_CHUNK_BYTES",
+                                8 * nk * 3 * 4)
+            got = O.prob_weighted_abs_ref(q[None, :, None], k[None, :, None], v[None, :, None], 0.6,
+                                          causal, wl, wr, None if slope is None else [slope], cap,
+                                          weight=weight)[0, :, 0]
+            monkeypatch.undo()
+            np.testing.assert_allclose(got, want, atol=1e-13)
 
 
 # T27-T29: fp8 inputs ----------------------------------------------------------------
