@@ -39,10 +39,12 @@
  *
  * Ownership and execution: every pointer is a device pointer owned by the
  * caller. The library allocates no device memory and keeps no mutable global
- * state; calls are enqueued on `stream` (a hipStream_t passed as void*; NULL is
- * the null stream) and return without synchronising, so results are ready
- * once the stream has reached the call. Calls on different streams may run
- * concurrently as long as they do not write the same buffers.
+ * state, except the static row-term buffer that fa_bwd_noalloc uses on each
+ * GPU (see there); calls are enqueued on `stream` (a hipStream_t passed as
+ * void*; NULL is the null stream) and return without synchronising, so results
+ * are ready once the stream has reached the call. Calls on different streams
+ * may run concurrently as long as they do not write the same buffers (and, for
+ * fa_bwd_noalloc, do not overlap on one GPU).
  *
  * Errors: all arguments are validated on the host before any HIP call; on a
  * validation error nothing is launched and nothing is written. FA_ERR_HIP
