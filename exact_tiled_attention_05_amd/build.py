@@ -68,7 +68,38 @@ def build(verbose: bool = False, extra_flags=None, out: str = LIB, build_dir: st
     os.replace(tmp, out)
     if out == LIB:
         build_c_example()
+        build_serial_copies(objs, build_dir, extra)
     return out
+
+
+# Sources whose LDS pipelines have a single-buffered verification form
+# (FA_SERIAL_COPIES: every tile copied, waited for and fenced by barriers on
+# both sides, no copy overlapping compute).
+SERIAL_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_fp8.hip"]
+SERIAL_LIB = os.path.join(ROOT, "tests", "hazard", "libfa_serial_copies.so")
+
+
+def build_serial_copies(objs, build_dir=BUILD, extra=()) -> str:
+    """A verification copy of the library (tests only): the sources in SERIAL_SOURCES
+    rebuilt with FA_SERIAL_COPIES, linked with the other objects of the main build.
+    The GPU hazard test checks that it gives the same bits as libfa.so."""
+    hipcc = _hipcc()
+    sdir = os.path.join(build_dir, "serial_copies")
+    os.makedirs(sdir, exist_ok=True)
+    os.makedirs(os.path.dirname(SERIAL_LIB), exist_ok=True)
+    jobs, swap = [], {}
+    for src in SERIAL_SOURCES:
+        obj = os.path.join(sdir, src + ".o")
+        jobs.append([hipcc, *COMMON, *HIP_FLAGS, *extra, "-DFA_SERIAL_COPIES", "-c",
+                     os.path.join(CSRC, src), "-o", obj])
+        swap[os.path.join(build_dir, src + ".o")] = obj
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        list(ex.map(_run, jobs))
+    tmp = SERIAL_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[swap.get(o, o) for o in objs],
+          "-o", tmp])
+    os.replace(tmp, SERIAL_LIB)
+    return SERIAL_LIB
 
 
 C_EXAMPLE_DIR = os.path.join(ROOT, "tests", "c_abi")

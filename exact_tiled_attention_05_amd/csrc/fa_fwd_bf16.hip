@@ -370,6 +370,27 @@ void fwd_bf16_kernel(FwdParams p) {
   // copies. Copies past the key range read nothing and write zeros. kcopy /
   // vcopy (dst, j0) copy the K / V tile of key j0.
   auto tile_loop = [&](auto kcopy, auto vcopy) __attribute__((always_inline)) {
+#ifdef FA_SERIAL_COPIES
+    // Verification build: one buffer per tensor, each tile copied, waited for
+    // and fenced by barriers on both sides (no copy overlaps any compute). The
+    // arithmetic is the pipelined loop's, so the results must agree bit for bit.
+    f32x16_t sacc_s[2];
+    for (int it = 0; it < ntiles; ++it) {
+      const int j0 = j_first + it * kBN;
+      kcopy(sK0, j0);
+      vcopy(sV0, j0);
+      wait_vmem_barrier<0>();
+      if (live(j0)) {
+        qk(sK0, sacc_s);
+        if (j0 >= wk.flo && j0 + kBN <= wk.fhi)
+          softmax_pv(std::false_type{}, sacc_s, sV0, j0);
+        else
+          softmax_pv(std::true_type{}, sacc_s, sV0, j0);
+      }
+      __syncthreads();
+    }
+    return;
+#endif
     constexpr int kKC = LOADS;  // vector-memory ops of one K tile copy
     kcopy(sK0, j_first);
     vcopy(sV0, j_first);
@@ -433,6 +454,25 @@ void fwd_bf16_kernel(FwdParams p) {
   } else {
     // ---- paged K/V gathered row by row: two buffers each; step t copies tile
     // t+1 and waits for it.
+#ifdef FA_SERIAL_COPIES
+    {  // verification build: one buffer, no overlap (see tile_loop)
+      f32x16_t sacc[2];
+      for (int it = 0; it < ntiles; ++it) {
+        const int j0 = j_first + it * kBN;
+        copy_tiles(sK0, sV0, j0);
+        wait_vmem();
+        __syncthreads();
+        if (live(j0)) {
+          qk(sK0, sacc);
+          if (j0 >= wk.flo && j0 + kBN <= wk.fhi)
+            softmax_pv(std::false_type{}, sacc, sV0, j0);
+          else
+            softmax_pv(std::true_type{}, sacc, sV0, j0);
+        }
+        __syncthreads();
+      }
+    }
+#else
     copy_tiles(sK0, sV0, j_first);
     wait_vmem();
     __syncthreads();
@@ -463,6 +503,7 @@ void fwd_bf16_kernel(FwdParams p) {
       step(std::false_type{}, it);
       if (it + 1 < ntiles) step(std::true_type{}, it + 1);
     }
+#endif
   }
 
   // ---- epilogue: O = O / l, LSE = (c m + log2 l) ln 2

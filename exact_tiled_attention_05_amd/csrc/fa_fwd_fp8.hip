@@ -243,6 +243,23 @@ void fwd_fp8_kernel(FwdParams p) {
   };
   const int j_first = (wg.lo / kBN) * kBN;
   const int ntiles = (wg.hi - j_first + kBN - 1) / kBN;
+#ifdef FA_SERIAL_COPIES
+  // Verification build: one buffer per tensor, each tile copied, waited for and
+  // fenced by barriers on both sides; the results must match the two-stage
+  // loop bit for bit.
+  for (int it = 0; it < ntiles; ++it) {
+    const int j0 = j_first + it * kBN;
+    copy_tiles(sK0, sV0, j0);
+    wait_vmem_barrier<0>();
+    if (live(j0)) {
+      if (j0 >= wk.flo && j0 + kBN <= wk.fhi)
+        compute(std::false_type{}, sK0, sV0, j0);
+      else
+        compute(std::true_type{}, sK0, sV0, j0);
+    }
+    __syncthreads();
+  }
+#else
   copy_tiles(sK0, sV0, j_first);
   wait_vmem_barrier<0>();
   auto step = [&](auto par, int it) __attribute__((always_inline)) {
@@ -261,6 +278,7 @@ void fwd_fp8_kernel(FwdParams p) {
     step(std::false_type{}, it);
     if (it + 1 < ntiles) step(std::true_type{}, it + 1);
   }
+#endif
 
   // Epilogue: O = v_descale * O~ / l, LSE = (c m + log2 l - 8) ln 2.
   if (!wave_live) return;
