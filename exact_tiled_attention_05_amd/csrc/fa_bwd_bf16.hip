@@ -939,7 +939,7 @@ void bwd_dq_kernel(BwdParams p) {
       }
     }
     // Slot v of block j holds key j0 + 32j + 8*(v/4) + 4*h2 + v%4 of this lane's row.
-    const bool masked = !(j0 >= wk.flo && j0 + kBN <= wk.fhi);
+    const bool masked = __builtin_amdgcn_readfirstlane(!(j0 >= wk.flo && j0 + kBN <= wk.fhi));
     const int lo_rel = rk.lo - j0 - 4 * h2, hi_rel = rk.hi - j0 - 4 * h2;
     const float rel = (float)(row + off - j0 - 4 * h2);
     float zv[2][16];
@@ -952,11 +952,22 @@ void bwd_dq_kernel(BwdParams p) {
         const float x = bwd_score<SOFTCAP, ALIBI>(p, sacc[j][v], slope_log2,
                                                   __builtin_fabsf(rel - (float)kk), th);
         float pr = fast_exp2(x - lse2);
-        if (masked && (kk < lo_rel || kk >= hi_rel)) pr = 0.0f;
         float dz = pr * (pacc[j][v] - drow);
         if constexpr (SOFTCAP) dz *= 1.0f - th * th;
         zv[j][v] = dz;
       }
+    // Only tiles that cross a row's key range (or Nk) take the per-element mask:
+    // a wave-uniform branch, so the other tiles skip the compares.
+    if (masked) {
+      asm volatile("");  // keeps the branch (not if-converted into every tile)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kk = 32 * j + 8 * (v >> 2) + (v & 3);
+          if (kk < lo_rel || kk >= hi_rel) zv[j][v] = 0.0f;
+        }
+    }
     // dQ^T += K^T dZ^T: k-step tt covers keys 16tt + 4h2 + {0..3, 8..11},
     // K read transposed from LDS.
 #pragma unroll
