@@ -11,14 +11,15 @@
 //
 //   1. prep:  D_i = dO_i . O_i and the LSE in log2 units (+inf for a row with
 //             no key, so that its probabilities come out 0).
-//   2. dK/dV: one workgroup per (128-key tile, head, batch), keys in lanes (32
-//             per wavefront): K as the B operand of S = Q K^T in registers, V in
-//             LDS for dP = dO V^T, walking the 32-row query blocks that see the keys:
+//   2. dK/dV: one workgroup per (key tile, head, batch), keys in lanes (32 per
+//             wavefront): K as the B operand of S = Q K^T in registers, V as the
+//             B operand of dP = dO V^T (in registers at head_dim 128, in LDS at
+//             64), walking the 32-row query blocks that see the keys:
 //               P = exp2(S' - LSE2), dS = P (dP - D), dZ = dS (1 - tanh^2) with a cap,
 //               dV^T += dO^T P and dK^T += Q^T dZ, the transposed dO and Q read
-//               from LDS with ds_read_b64_tr_b16. At head_dim 128 two wavefronts
-//               share each 32-key group (one for S, P, dV; one for dP, dZ, dK),
-//               at head_dim 64 one wavefront does all of it.
+//               from LDS with ds_read_b64_tr_b16. At head_dim 128 (64-key tiles)
+//               two wavefronts share each 32-key group (one for S, P, dV; one for
+//               dP, dZ, dK); at head_dim 64 (128-key tiles) one wavefront does all of it.
 //   3. dQ:    one workgroup per (128-row query tile, head, batch), laid out as
 //             the forward (a query row per lane pair): S^T = K Q^T and
 //             dP^T = V dO^T with Q and dO in registers, dQ^T += K^T dZ^T with K
@@ -189,17 +190,20 @@ __device__ void zero_rows(void* base, int bf16, int64_t row0, int h, int H, int 
 // ---------------------------------------------------------------------------
 // 2. dK and dV (head_dim 128)
 //
-// Eight wavefronts: four key groups of 32 keys (the workgroup's 128 keys) times
-// two roles, so that each SIMD runs one wavefront of each role side by side.
-// Role 0 (S, P, dV): S = Q K^T with K in registers, P = exp2(S' - LSE2) under
-// the mask, dV^T += dO^T P; it also publishes P' = P (1 - tanh^2 with a cap, 1
-// without) in fp32 through LDS. Role 1 (dP, dZ, dK): dP = dO V^T with V from
-// LDS, and one block behind, dZ = P' (dP - D) and dK^T += Q^T dZ. The 32-row
-// query blocks (Q, dO, row terms) cycle through four LDS stages with the copy
-// of block t+2 issued in step t, so block t-1 is still resident while role 1
-// finishes it.
+// Four wavefronts: two key groups of 32 keys (the workgroup's 64 keys) times
+// two roles. Role 0 (S, P, dV): S = Q K^T with K in registers, P = exp2(S' -
+// LSE2) under the mask, dV^T += dO^T P; it also publishes P' = P (1 - tanh^2
+// with a cap, 1 without) in fp32 through LDS. Role 1 (dP, dZ, dK): dP = dO V^T
+// with V in registers, and one block behind, dZ = P' (dP - D) and dK^T += Q^T
+// dZ. The 32-row query blocks (Q, dO, row terms) cycle through three LDS
+// stages, the copy of block t+1 issued in step t, so block t-1 is still
+// resident while role 1 finishes it. 65 KiB of LDS and 256 registers per lane
+// let two workgroups share a CU: each SIMD then runs one wavefront of each, and
+// the two workgroups' barriers are independent of each other.
 // ---------------------------------------------------------------------------
-constexpr int kDkdvThreads = 512;
+constexpr int kDkdvThreads = 256;
+constexpr int kDkdvGroups = 2;                   // key groups of 32 per workgroup
+constexpr int kDkdvKeys = 32 * kDkdvGroups;      // keys per workgroup (head_dim 128)
 
 template <int D, bool SOFTCAP, bool ALIBI>
 __global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -208,35 +212,29 @@ void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NDB = D / 32;              // 32-row blocks of dK^T / dV^T
   constexpr int CPR = D / 8;               // 16-byte chunks per row
   constexpr int RPL = 64 / CPR;            // rows per wavefront-wide copy
-  constexpr int QL = kBQ / RPL / 4;        // copies per wavefront of its role's tensor per block
-  constexpr int VL = kBK / RPL / 8;        // copies per wavefront for the V tile
-  static_assert(QL >= 1 && VL >= 1 && kBQ == BWD_RB, "tile shape");
+  constexpr int QL = kBQ / RPL / kDkdvGroups;  // copies per wavefront of its role's tensor per block
+  static_assert(QL >= 1 && kBQ == BWD_RB, "tile shape");
   constexpr int QT = kBQ * D;
-  constexpr int kCopies = QL + 1;          // vector-memory ops per wavefront per block
-  constexpr int kSReadAhead = 2;           // k-steps of operands read ahead
+  constexpr int kSReadAhead = 3;           // k-steps of dO operands read ahead in dP
   constexpr int kReadAhead = 4;            // transposed-read MFMAs in flight
   constexpr int XG = 16 * 64;              // floats of P' per key group
 
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[kBK * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sQ0[QT];
   __shared__ __attribute__((aligned(1024))) uint16_t sQ1[QT];
   __shared__ __attribute__((aligned(1024))) uint16_t sQ2[QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ3[QT];
   __shared__ __attribute__((aligned(1024))) uint16_t sG0[QT];  // dO
   __shared__ __attribute__((aligned(1024))) uint16_t sG1[QT];
   __shared__ __attribute__((aligned(1024))) uint16_t sG2[QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sG3[QT];
   __shared__ __attribute__((aligned(256))) float sR0[2 * kBQ];  // LSE2 | D
   __shared__ __attribute__((aligned(256))) float sR1[2 * kBQ];
   __shared__ __attribute__((aligned(256))) float sR2[2 * kBQ];
-  __shared__ __attribute__((aligned(256))) float sR3[2 * kBQ];
-  __shared__ __attribute__((aligned(1024))) float sX0[4 * XG];  // P' of even blocks
-  __shared__ __attribute__((aligned(1024))) float sX1[4 * XG];  // P' of odd blocks
+  __shared__ __attribute__((aligned(1024))) float sX0[kDkdvGroups * XG];  // P' of even blocks
+  __shared__ __attribute__((aligned(1024))) float sX1[kDkdvGroups * XG];  // P' of odd blocks
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
-  const int grp = w & 3;
-  const int role = __builtin_amdgcn_readfirstlane(w >> 2);
+  const int grp = w & (kDkdvGroups - 1);
+  const int role = __builtin_amdgcn_readfirstlane(w / kDkdvGroups);
   int L = blockIdx.x;
   const int h = L % p.H;
   L /= p.H;
@@ -245,8 +243,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   const BwdSeq sq = bwd_seq(p, b, h);
   const int nq = sq.nq, nk = sq.nk, off = nk - nq;
   const int wl = p.window_left, wr = p.window_right;
-  const int k0 = kt * kBK, k1 = min(nk, k0 + kBK);
-  if (k0 >= nk) return;  // a packed sequence shorter than the longest
+  const int k0 = kt * kDkdvKeys, k1 = min(nk, k0 + kDkdvKeys);
+  if (k0 >= nk) return;  // past the keys (a packed sequence shorter than the longest)
 
   // Query rows the workgroup's keys are seen by (union over its keys).
   int ulo, uhi, tmp;
@@ -276,43 +274,45 @@ void bwd_dkdv_kernel(BwdParams p) {
     return group_live && qb < whi && qb + kBQ > wlo;
   };
 
+  // This lane's key row of K (role 0) or V (role 1), columns 16ks + 8h2 .. +7:
+  // the B operand of S = Q K^T and of dP = dO V^T (zero past Nk).
+  bf16x8_t kvf[KS];
+  {
+    const uint16_t* kp = (const uint16_t*)(role == 0 ? p.k : p.v) +
+                         ((sq.k_row0 + min(key, nk - 1)) * p.H + h) * D + 8 * h2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t x = *(const u32x4_t*)(kp + 16 * ks);
+      if (key >= k1) x = u32x4_t{0, 0, 0, 0};
+      kvf[ks] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+
   // HBM -> LDS copies. Copy i of a wavefront with copy slot c fills rows
-  // RPL*(n*c + i) + lane/CPR (n copies per slot), lane L the physical chunk L % CPR.
+  // RPL*(QL*c + i) + lane/CPR, lane L the physical chunk L % CPR. Role 0 copies
+  // Q, role 1 copies dO (two wavefronts each); every wavefront copies the
+  // block's 64 row terms (identical values). Blocks past the range are not copied.
   const int64_t row_bytes = 2 * (int64_t)p.H * D;
   auto lane_off = [&](int ld) __attribute__((always_inline)) {
     const int trow = RPL * ld + lane / CPR;
     const int chunk = (lane % CPR) ^ swz<D>(trow);
     return (unsigned)(trow * row_bytes + 16 * chunk);
   };
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  {
-    // V tile of the workgroup's keys (rows past Nk arrive as zeros), all eight wavefronts.
-    const char* vb = (const char*)p.v + 2 * (((sq.k_row0 + k0) * p.H + h) * D);
-    const int64_t left = (int64_t)(nk - 1 - k0) * row_bytes + 2 * D;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vb, left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
-#pragma unroll
-    for (int i = 0; i < VL; ++i) buffer_load_lds16(rs, sV + 512 * (VL * wu + i), lane_off(VL * wu + i));
-  }
-  // Role 0 copies Q, role 1 copies dO (4 wavefronts each); every wavefront
-  // copies the block's 64 row terms (identical values). Blocks past the range
-  // read nothing and write zeros, which keeps the wait counts fixed.
   const int cs = __builtin_amdgcn_readfirstlane(grp);
   const char* tbh = (const char*)(role == 0 ? p.q : p.dout) + 2 * ((sq.q_row0 * p.H + h) * D);
   const int64_t qend = (int64_t)(nq - 1) * row_bytes + 2 * D;
   const float* rbh = p.rowterms + ((int64_t)b * p.H + h) * p.nblk * (2 * kBQ);
   const int qb_first = (ulo / kBQ) * kBQ;
   const int nblocks = (uhi - qb_first + kBQ - 1) / kBQ;
-  const int qb_end = qb_first + nblocks * kBQ;
   auto copy_block = [&](uint16_t* dq_, uint16_t* dg_, float* dr_, int qb) __attribute__((always_inline)) {
     const int64_t tb = (int64_t)qb * row_bytes;
-    const int64_t left = qb < qb_end ? qend - tb : 0;
+    const int64_t left = qend - tb;
     const int n = left <= 0 ? 0 : (left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(tbh + tb, n);
     uint16_t* dst = role == 0 ? dq_ : dg_;
 #pragma unroll
     for (int i = 0; i < QL; ++i) buffer_load_lds16(rt, dst + 512 * (QL * cs + i), lane_off(QL * cs + i));
-    const __amdgpu_buffer_rsrc_t rr =
-        make_rsrc((const char*)(rbh + (int64_t)(qb / kBQ) * (2 * kBQ)), qb < qb_end ? 8 * kBQ : 0);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc((const char*)(rbh + (int64_t)(qb / kBQ) * (2 * kBQ)), 8 * kBQ);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr_t)dr_, 4, 4 * lane, 0, 0, 0);
   };
 
@@ -320,24 +320,23 @@ void bwd_dkdv_kernel(BwdParams p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
   auto stq = [&](auto st) __attribute__((always_inline)) {
     constexpr int S = decltype(st)::value;
-    return S == 0 ? sQ0 : S == 1 ? sQ1 : S == 2 ? sQ2 : sQ3;
+    return S == 0 ? sQ0 : S == 1 ? sQ1 : sQ2;
   };
   auto stg = [&](auto st) __attribute__((always_inline)) {
     constexpr int S = decltype(st)::value;
-    return S == 0 ? sG0 : S == 1 ? sG1 : S == 2 ? sG2 : sG3;
+    return S == 0 ? sG0 : S == 1 ? sG1 : sG2;
   };
   auto str = [&](auto st) __attribute__((always_inline)) {
     constexpr int S = decltype(st)::value;
-    return S == 0 ? sR0 : S == 1 ? sR1 : S == 2 ? sR2 : sR3;
+    return S == 0 ? sR0 : S == 1 ? sR1 : sR2;
   };
-  // Issue the copies of block it + 2 into stage (S + 2) % 4 (held block it - 2).
+  // Issue the copies of block it + 1 into stage (S + 1) % 3 (held block it - 2).
   auto prefetch = [&](auto st, int it) __attribute__((always_inline)) {
     constexpr int S = decltype(st)::value;
-    using N = std::integral_constant<int, (S + 2) % 4>;
-    copy_block(stq(N{}), stg(N{}), str(N{}), qb_first + (it + 2) * kBQ);
+    using N = std::integral_constant<int, (S + 1) % 3>;
+    if (it + 1 < nblocks) copy_block(stq(N{}), stg(N{}), str(N{}), qb_first + (it + 1) * kBQ);
   };
   // Transposed head_dim x 16-row operand of k-step tt from a 32-row tile.
   auto tr_operand = [&](const uint16_t* t, int tt, int db) __attribute__((always_inline)) {
@@ -350,8 +349,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   };
 
   copy_block(sQ0, sG0, sR0, qb_first);
-  copy_block(sQ1, sG1, sR1, qb_first + kBQ);
-  wait_vmem_barrier<kCopies>();  // V and block 0 have landed
+  wait_vmem_barrier<0>();  // K or V and block 0 have landed
 
   f32x16_t acc[NDB];  // dV^T (role 0) or dK^T (role 1)
 #pragma unroll
@@ -361,17 +359,6 @@ void bwd_dkdv_kernel(BwdParams p) {
     // ---- role 0: S, P, dV
     float slope_log2 = 0.0f;
     if constexpr (ALIBI) slope_log2 = p.alibi[h] * kLog2e;
-    bf16x8_t kf[KS];
-    {
-      const uint16_t* kp =
-          (const uint16_t*)p.k + ((sq.k_row0 + min(key, nk - 1)) * p.H + h) * D + 8 * h2;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4_t x = *(const u32x4_t*)(kp + 16 * ks);
-        if (key >= k1) x = u32x4_t{0, 0, 0, 0};
-        kf[ks] = __builtin_bit_cast(bf16x8_t, x);
-      }
-    }
     auto compute = [&](auto masked_t, const uint16_t* sq, const uint16_t* sg, const float* sr,
                        float* sx, int qb) __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(masked_t)::value;
@@ -380,7 +367,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8_t aq =
             __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sq + tile_off<D>(r, 2 * ks + h2)));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kvf[ks], sacc, 0, 0, 0);
       }
       // Slot v holds query qb + 8*(v/4) + 4*h2 + v%4 of this lane's key.
       const int lo_rel = rlo - qb - 4 * h2, hi_rel = rhi - qb - 4 * h2;
@@ -435,13 +422,12 @@ void bwd_dkdv_kernel(BwdParams p) {
         else
           compute(std::true_type{}, stq(st), stg(st), str(st), sx, qb);
       }
-      wait_vmem_barrier<kCopies>();  // block it + 1 has landed; P' of block it is visible
+      wait_vmem_barrier<0>();  // block it + 1 has landed; P' of block it is visible
     };
-    for (int it = 0; it < nblocks; it += 4) {
+    for (int it = 0; it < nblocks; it += 3) {
       step(I0{}, it);
       if (it + 1 < nblocks) step(I1{}, it + 1);
       if (it + 2 < nblocks) step(I2{}, it + 2);
-      if (it + 3 < nblocks) step(I3{}, it + 3);
     }
   } else {
     // ---- role 1: dP, then dZ and dK one block behind
@@ -452,15 +438,13 @@ void bwd_dkdv_kernel(BwdParams p) {
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8_t ag =
             __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sg + tile_off<D>(r, 2 * ks + h2)));
-        const bf16x8_t bv =
-            __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sV + tile_off<D>(32 * grp + r, 2 * ks + h2)));
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, bv, pacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, kvf[ks], pacc, 0, 0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kSReadAhead, 2);
+      __builtin_amdgcn_sched_group_barrier(0x100, kSReadAhead, 2);
 #pragma unroll
       for (int i = 0; i < KS - kSReadAhead; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, kSReadAhead, 2);
       return pacc;
@@ -498,7 +482,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     };
     auto step = [&](auto st, int it) __attribute__((always_inline)) {
       constexpr int S = decltype(st)::value;
-      using P1 = std::integral_constant<int, (S + 3) % 4>;  // stage of block it - 1
+      using P1 = std::integral_constant<int, (S + 2) % 3>;  // stage of block it - 1
       const int qb = qb_first + it * kBQ;
       prefetch(st, it);
       f32x16_t pcur = f32x16_t{};
@@ -508,25 +492,23 @@ void bwd_dkdv_kernel(BwdParams p) {
         dk_block(stq(P1{}), str(P1{}), sx + grp * XG, pprev);
       }
       pprev = pcur;
-      wait_vmem_barrier<kCopies>();
+      wait_vmem_barrier<0>();
     };
-    for (int it = 0; it < nblocks; it += 4) {
+    for (int it = 0; it < nblocks; it += 3) {
       step(I0{}, it);
       if (it + 1 < nblocks) step(I1{}, it + 1);
       if (it + 2 < nblocks) step(I2{}, it + 2);
-      if (it + 3 < nblocks) step(I3{}, it + 3);
     }
     // The last block: its stage, row terms and P' are still resident.
     const int last = nblocks - 1;
     if (live(qb_first + last * kBQ)) {
-      const int sl = last & 3;
-      const uint16_t* sq = sl == 0 ? sQ0 : sl == 1 ? sQ1 : sl == 2 ? sQ2 : sQ3;
-      const float* sr = sl == 0 ? sR0 : sl == 1 ? sR1 : sl == 2 ? sR2 : sR3;
+      const int sl = last % 3;
+      const uint16_t* sq = sl == 0 ? sQ0 : sl == 1 ? sQ1 : sQ2;
+      const float* sr = sl == 0 ? sR0 : sl == 1 ? sR1 : sR2;
       const float* sx = (last & 1) ? sX1 : sX0;
       dk_block(sq, sr, sx + grp * XG, pprev);
     }
   }
-  wait_vmem_barrier<0>();  // no copy may still be writing LDS at exit
 
   // Epilogue: lane = key, slots = head_dim rows 32db + 8g + 4h2 + {0..3}.
   if (key >= k1) return;
@@ -1027,7 +1009,10 @@ int launch_bwd_bf16(const BwdParams& p, void* stream) {
                      0, s, p);
   int rc = (int)hipGetLastError();
   if (rc) return rc;
-  const dim3 kgrid((unsigned)((int64_t)p.num_k_tiles * p.H * p.B));
+  // Key tiles of BWD_BK keys (head_dim 64) or kDkdvKeys keys (head_dim 128; the
+  // workgroups past a sequence's keys exit at once).
+  const int64_t ktiles = D == 128 ? (int64_t)p.num_k_tiles * (BWD_BK / kDkdvKeys) : p.num_k_tiles;
+  const dim3 kgrid((unsigned)(ktiles * p.H * p.B));
   if constexpr (D == 128)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, SOFTCAP, ALIBI>), kgrid, dim3(kDkdvThreads), 0, s, p);
   else
