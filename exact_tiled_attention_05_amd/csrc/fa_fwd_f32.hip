@@ -2,9 +2,12 @@
 //
 // Same method and register layout as the bf16 kernel (S^T = K Q^T, online
 // softmax per lane pair, O^T += V^T P^T), with fp32 operands throughout so that
-// fp32 inputs keep fp32 products. One wavefront owns a 32-row query tile and
-// walks 32-key tiles staged in LDS. Used for fp32 inputs, where problem sizes
-// are small and accuracy, not throughput, is the point.
+// fp32 inputs keep fp32 products. A workgroup owns a 32-row query tile; its
+// four wavefronts take every fourth 32-key tile of the tile's key range (each
+// staging its own tiles in LDS), and their partial (max, sum, O) are merged by
+// the log-sum-exp rule at the end. Used for fp32 inputs, where problem sizes
+// are small and accuracy, not throughput, is the point: the four wavefronts
+// spread a short problem over four SIMDs instead of one.
 #include <hip/hip_runtime.h>
 
 #include "fa_device.h"
@@ -14,7 +17,15 @@ namespace fa {
 namespace {
 
 constexpr int kBN = 32;
-constexpr int kThreads = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+// Orders the LDS writes of one wavefront before its following reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
@@ -22,17 +33,21 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
   // Row strides chosen so that the 64 lanes of each MFMA operand read hit 64 distinct banks.
   constexpr int KSTR = D + 2;  // lane (r, h2) reads K[r][2ks + h2]
   constexpr int VSTR = D + 8;  // lane (r, h2) reads V[key(h2)][32db + r], keys 4 apart
-  __shared__ float sK[kBN * KSTR];
-  __shared__ __attribute__((aligned(16))) float sV[kBN * VSTR];
+  constexpr int kStage = kBN * (KSTR + VSTR);      // floats of one wavefront's K and V tile
+  constexpr int kMerge = NDB * 16 * 64 + 2 * 64;   // floats of one wavefront's partial output
+  constexpr int kPerWave = kStage > kMerge ? kStage : kMerge;
+  __shared__ __attribute__((aligned(16))) float smem[kWaves * kPerWave];
 
-  const int lane = threadIdx.x, r = lane & 31, h2 = lane >> 5;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
+  float* sK = smem + w * kPerWave;
+  float* sV = sK + kBN * KSTR;
   const WorkItem wi = decode_work<PAGED>(p);
   const int b = wi.b, h = wi.h, s = wi.s;
   const SeqInfo si = seq_info(p, b, h);
   const int nq = si.nq, nk = si.nk;
   if constexpr (PAGED) {
     // Append: one workgroup per (b, h) copies the new keys into their pages.
-    if (p.k_new && s == 0 && wi.rank == 0) append_rows<float>(p, si, b, h, D, lane, kThreads);
+    if (p.k_new && s == 0 && wi.rank == 0) append_rows<float>(p, si, b, h, D, tid, kThreads);
   }
   const int qt = query_tile(wi, nq, F32_BM);
   if (qt < 0) return;  // a packed sequence shorter than the longest
@@ -45,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
   const int q1 = min(nq, q0 + F32_BM);
   const KeyBounds wk = key_bounds(q0, q1, off, slo, shi, p.window_left, p.window_right);
   if (wk.hi <= wk.lo) {
-    write_empty_rows<PAGED>(p, si, b, h, s, q0, q1, D, lane, kThreads);
+    write_empty_rows<PAGED>(p, si, b, h, s, q0, q1, D, tid, kThreads);
     return;
   }
   const int row = q0 + r;
@@ -68,28 +83,28 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
   float m_run = kNegInf, l_run = 0.0f;
 
   const int j_first = (wk.lo / kBN) * kBN;
-  for (int j0 = j_first; j0 < wk.hi; j0 += kBN) {
-    __syncthreads();
-    for (int idx = lane; idx < kBN * D / 4; idx += kThreads) {
-      const int kk = idx / (D / 4), c = idx % (D / 4);
+  for (int j0 = j_first + w * kBN; j0 < wk.hi; j0 += kWaves * kBN) {
+    wave_lds_sync();  // the previous tile's reads came first
+    for (int idx = lane; idx < kBN * D / 4; idx += 64) {
+      const int kk = idx / (D / 4), c4 = idx % (D / 4);
       const int key = j0 + kk;
       f32x4_t kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
       if (key < nk) {
         // Appended keys (paged launches with k_new) come from k_new / v_new.
         const bool fresh = PAGED && key >= si.n_cached;
         const int64_t o = (fresh ? new_key_offset(p, si, b, key, h, D)
-                                 : kv_offset<PAGED>(p, b, si, key, h, D)) + 4 * c;
+                                 : kv_offset<PAGED>(p, b, si, key, h, D)) + 4 * c4;
         kx = *(const f32x4_t*)((const float*)(fresh ? p.k_new : p.k) + o);
         vx = *(const f32x4_t*)((const float*)(fresh ? p.v_new : p.v) + o);
       }
-      float* kd = &sK[kk * KSTR + 4 * c];
+      float* kd = &sK[kk * KSTR + 4 * c4];
       kd[0] = kx[0];
       kd[1] = kx[1];
       kd[2] = kx[2];
       kd[3] = kx[3];
-      *(f32x4_t*)&sV[kk * VSTR + 4 * c] = vx;
+      *(f32x4_t*)&sV[kk * VSTR + 4 * c4] = vx;
     }
-    __syncthreads();
+    wave_lds_sync();
 
     f32x16_t sacc = f32x16_t{};
 #pragma unroll
@@ -127,33 +142,71 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
     }
   }
 
-  const float l_tot = half_sum(l_run);
-  if (row >= nq) return;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  float mref = m_run * c;  // the maximum in units of the unshifted ALiBi bias
-  if constexpr (ALIBI) mref -= slope_log2 * (float)abs(row + off - alibi_anchor(row + off, rk));
-  const float lse = l_tot > 0.0f ? (mref + __log2f(l_tot)) * kLn2 : kNegInf;
-  if constexpr (PAGED) {
-    const int64_t ro = (((int64_t)s * p.B + b) * p.H + h) * p.Nq + row;
-    float* op = p.o_part + ro * D;
+  // Merge the wavefronts' partials: row max M = max_w m_w (log2 units), sum L =
+  // sum_w l_w 2^(m_w - M), O = sum_w O_w 2^(m_w - M) / L. Each wavefront
+  // publishes (m_w, l_w) per lane and its accumulators lane-contiguously.
+  const float mw = m_run == kNegInf ? kNegInf : m_run * c;
+  const float lw = half_sum(l_run);
+  __syncthreads();  // every wavefront is done with its K/V stage
+  {
+    float* mine = smem + w * kPerWave;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mine[(db * 16 + e) * 64 + lane] = oacc[db][e];
+    mine[NDB * 16 * 64 + lane] = mw;
+    mine[NDB * 16 * 64 + 64 + lane] = lw;
+  }
+  __syncthreads();
+  float M = kNegInf;
+#pragma unroll
+  for (int u = 0; u < kWaves; ++u) M = fmaxf(M, smem[u * kPerWave + NDB * 16 * 64 + lane]);
+  float wgt[kWaves];
+  float L = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kWaves; ++u) {
+    const float mu = smem[u * kPerWave + NDB * 16 * 64 + lane];
+    wgt[u] = M == kNegInf || mu == kNegInf ? 0.0f : fast_exp2(mu - M);
+    L += smem[u * kPerWave + NDB * 16 * 64 + 64 + lane] * wgt[u];
+  }
+  if (row >= nq) return;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+  for (int u = 0; u < kWaves; ++u) wgt[u] *= inv;
+  float mref = M;  // the maximum in units of the unshifted ALiBi bias
+  if constexpr (ALIBI) mref -= slope_log2 * (float)abs(row + off - alibi_anchor(row + off, rk));
+  const float lse = L > 0.0f ? (mref + __log2f(L)) * kLn2 : kNegInf;
+  // Wavefront w writes the 32-column blocks db = w, w + kWaves, ...
+  for (int db = w; db < NDB; db += kWaves) {
+    float ov[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float x = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kWaves; ++u) x += smem[u * kPerWave + (db * 16 + e) * 64 + lane] * wgt[u];
+      ov[e] = x;
+    }
+    if constexpr (PAGED) {
+      const int64_t ro = (((int64_t)s * p.B + b) * p.H + h) * p.Nq + row;
+      float* op = p.o_part + ro * D;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        f32x4_t x = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
-                     oacc[db][4 * g + 3] * inv};
+        f32x4_t x = {ov[4 * g], ov[4 * g + 1], ov[4 * g + 2], ov[4 * g + 3]};
         *(f32x4_t*)(op + 32 * db + 8 * g + 4 * h2) = x;
       }
-    if (h2 == 0) p.lse_part[ro] = lse;
-  } else {
-    const int64_t ob = q_offset(p, si, row, h, D);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    } else {
+      const int64_t ob = q_offset(p, si, row, h, D);
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        store_out4(p, ob + 32 * db + 8 * g + 4 * h2, oacc[db][4 * g] * inv,
-                   oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-    if (h2 == 0 && p.lse) p.lse[si.lse0 + row] = lse;
+        store_out4(p, ob + 32 * db + 8 * g + 4 * h2, ov[4 * g], ov[4 * g + 1], ov[4 * g + 2],
+                   ov[4 * g + 3]);
+    }
+  }
+  if (w == 0 && h2 == 0) {
+    if constexpr (PAGED)
+      p.lse_part[(((int64_t)s * p.B + b) * p.H + h) * p.Nq + row] = lse;
+    else if (p.lse)
+      p.lse[si.lse0 + row] = lse;
   }
 }
 
