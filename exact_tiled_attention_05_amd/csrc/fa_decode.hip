@@ -207,11 +207,14 @@ __device__ __forceinline__ void decode_body(const FwdParams& p) {
         if (fresh[u]) off[u] = new_key_offset(p, si, b, tt, 0, D);
       }
     }
+    // Every cache row is read once per launch: non-temporal loads keep the
+    // stream from displacing other lines (5.95 -> 6.65 TB/s on the 32768-key
+    // decode shape; a plain streaming read probe shows the same gap).
     u32x4_t kx[kU], vx[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      kx[u] = *(const u32x4_t*)((fresh[u] ? knew : kbase) + off[u]);
-      vx[u] = *(const u32x4_t*)((fresh[u] ? vnew : vbase) + off[u]);
+      kx[u] = __builtin_nontemporal_load((const u32x4_t*)((fresh[u] ? knew : kbase) + off[u]));
+      vx[u] = __builtin_nontemporal_load((const u32x4_t*)((fresh[u] ? vnew : vbase) + off[u]));
     }
     float sc[kU];
 #pragma unroll
