@@ -506,6 +506,41 @@ def main():
                                     "frac": round(f8w_tflops / PEAK_FP8_TFLOPS, 4)}}
     del f8w
 
+    # ---- FP8 key splits on the ALiBi + softcap set (side measurement): E4M3 inputs of
+    # that shape (amplitude 2), fa_fwd_split_fp8 with the bf16 line's split count, then
+    # the combine kernel into the same partial buffers.
+    f8s = [up8(W.gen_tensor(ws.seed, t, ws.B, n, ws.H, ws.d, ws.amp, "fp8"))
+           for t, n in ((W.TENSOR_Q, ws.Nq), (W.TENSOR_K, ws.Nk), (W.TENSOR_V, ws.Nk))]
+
+    def fp8_short_split():
+        check(fa.fa_fwd_split_fp8(f8s[0], f8s[1], f8s[2], 1.0, 1.0, 1.0, s_opart, s_lpart, SS,
+                                  ws.B, ws.H, ws.Nq, ws.Nk, ws.d, ws.scale, True, -1, -1, s_slopes,
+                                  ws.softcap, stream), "fa_fwd_split_fp8")
+        short_combine()
+
+    for _ in range(args.warmup):
+        fp8_short_split()
+    ev9 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for a, e in ev9:
+        a.record(stream)
+        fp8_short_split()
+        e.record(stream)
+    torch.cuda.synchronize()
+    t_f8s = np.array([a.elapsed_time(e) for a, e in ev9]) * 1e-3
+    assert torch.isfinite(s_o).all()
+    f8s_tflops = split_flops / t_f8s.mean() / 1e12
+    fp8_split_line = {"workload": "alibi_softcap_nq_ne_nk in E4M3 (fa_fwd_split_fp8, "
+                                  f"{SS} splits, + fa_splitkv_combine)",
+                      "num_splits": SS, "gflop": round(split_flops / 1e9, 4),
+                      "ms": round(t_f8s.mean() * 1e3, 5),
+                      "ms_median": round(float(np.median(t_f8s)) * 1e3, 5),
+                      "tflops": round(f8s_tflops, 3),
+                      "roofline": {"bound": "mfma", "achieved": round(f8s_tflops, 3),
+                                   "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": round(f8s_tflops / PEAK_FP8_TFLOPS, 4)}}
+    del f8s
+
     # ---- paged decode over an E4M3 cache (side measurement): the decode pool above
     # rounded to E4M3 on the device (input preparation, untimed; its NaN pages stay
     # NaN), unit descales. Half the cache bytes of the bf16 decode.
@@ -739,6 +774,7 @@ def main():
         "backward": backward_line,
         "fp8_prefill": fp8_line,
         "fp8_window": fp8_window_line,
+        "fp8_short_split": fp8_split_line,
         "fp8_decode": fp8_decode_line,
         "serving_step": serving_line,
         "paged_prefill_chunk": chunk_line,

@@ -2,11 +2,11 @@
 
 The functions named like the C ABI (``fa_fwd``, ``fa_fwd_split``,
 ``fa_fwd_splitkv``, ``fa_fwd_splitkv_seqlens``, ``fa_fwd_splitkv_append``, ``fa_fwd_varlen``,
-``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_splitkv_combine``, ``fa_status_string``,
+``fa_fwd_fp8``, ``fa_fwd_split_fp8``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_splitkv_combine``, ``fa_status_string``,
 ``fa_split_chunk_len``) only
 marshal arguments: torch tensors become device pointers, the current torch
 stream becomes the HIP stream, and every step of the computation runs in the
-library's kernels. ``attention``, ``attention_fp8``, ``attention_varlen``, ``attention_split``,
+library's kernels. ``attention``, ``attention_fp8``, ``attention_split_fp8``, ``attention_varlen``, ``attention_split``,
 ``attention_paged_splitkv``, ``attention_paged_append``, ``attention_backward``,
 ``combine`` and ``decode_paged`` add output allocation (torch.empty) on top of them.
 
@@ -24,10 +24,11 @@ import torch
 __all__ = [
     "FA_FP32", "FA_BF16", "FaError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
-    "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_splitkv_fp8", "fa_bwd",
-    "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
+    "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_split_fp8", "fa_fwd_splitkv_fp8",
+    "fa_bwd", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
     "fa_split_chunk_len", "fa_num_splits",
-    "attention", "attention_fp8", "attention_varlen", "attention_split", "attention_split_partials",
+    "attention", "attention_fp8", "attention_split_fp8", "attention_split_partials_fp8",
+    "attention_varlen", "attention_split", "attention_split_partials",
     "attention_paged_splitkv", "attention_paged_splitkv_fp8", "attention_paged_append",
     "attention_backward", "attention_varlen_backward", "combine", "decode_paged",
 ]
@@ -38,8 +39,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 _lib = None
 
 EXPORTED = ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
-            "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_splitkv_fp8", "fa_bwd",
-            "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
+            "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_split_fp8",
+            "fa_fwd_splitkv_fp8", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
             "fa_split_chunk_len", "fa_num_splits")
 
 
@@ -83,6 +84,9 @@ def declare(lib):
     lib.fa_fwd_splitkv_append.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, i, vp, i, i, i, i, i, f, i, i, i, vp, f, vp]
     lib.fa_fwd_fp8.restype = i
+    lib.fa_fwd_split_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, i, f, i, i, i, vp,
+                                     f, vp]
+    lib.fa_fwd_split_fp8.restype = i
     lib.fa_fwd_splitkv_fp8.argtypes = [vp, vp, vp, f, f, vp, i, i, vp, vp, vp, i, i, i, i, i, i,
                                        f, i, i, i, vp, f, vp]
     lib.fa_fwd_splitkv_fp8.restype = i
@@ -259,6 +263,19 @@ def fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, batch, heads, s
         int(window_left), int(window_right), _slopes_ptr(alibi_slopes, heads, q), float(softcap), _stream(stream))
 
 
+def fa_fwd_split_fp8(q, k, v, q_descale, k_descale, v_descale, o_part, lse_part, num_splits,
+                     batch, heads, seqlen_q, seqlen_k, head_dim, softmax_scale, causal=False,
+                     window_left=-1, window_right=-1, alibi_slopes=None, softcap=0.0,
+                     stream=None) -> int:
+    """Call fa_fwd_split_fp8 on caller-allocated tensors (q, k, v: E4M3 codes); returns the status."""
+    return load_library().fa_fwd_split_fp8(
+        _ptr_fp8(q), _ptr_fp8(k), _ptr_fp8(v), float(q_descale), float(k_descale),
+        float(v_descale), _ptr(o_part), _ptr(lse_part), int(num_splits), int(batch), int(heads),
+        int(seqlen_q), int(seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)),
+        int(window_left), int(window_right), _slopes_ptr(alibi_slopes, heads, q), float(softcap),
+        _stream(stream))
+
+
 def fa_fwd_splitkv_fp8(q, k_cache, v_cache, k_descale, v_descale, block_table,
                        max_pages_per_seq, page_size, cache_seqlens, o_part, lse_part, num_splits,
                        batch, heads, seqlen_q, seqlen_k, head_dim, softmax_scale, causal=False,
@@ -390,6 +407,32 @@ def attention_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, softmax_
                       softmax_scale, causal, window_left, window_right, alibi_slopes, softcap,
                       stream), "fa_fwd_fp8")
     return o, lse
+
+
+def attention_split_partials_fp8(q, k, v, num_splits=None, q_descale=1.0, k_descale=1.0,
+                                 v_descale=1.0, softmax_scale=None, causal=False, window_left=-1,
+                                 window_right=-1, alibi_slopes=None, softcap=0.0, stream=None):
+    """Split partials o_part [S,B,H,Nq,d] and lse_part [S,B,H,Nq] of the FP8 forward over
+    E4M3 q [B,Nq,H,d], k/v [B,Nk,H,d] (uint8 codes or float8_e4m3fn)."""
+    B, nq, H, d = q.shape
+    nk = k.shape[1]
+    if tuple(k.shape) != (B, nk, H, d) or tuple(v.shape) != (B, nk, H, d):
+        raise ValueError("k and v must be [B, Nk, H, d] matching q")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    num_splits = _splits(num_splits, B, H, nq, nk, d, 128)
+    o_part = torch.empty((num_splits, B, H, nq, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((num_splits, B, H, nq), dtype=torch.float32, device=q.device)
+    _check(fa_fwd_split_fp8(q, k, v, q_descale, k_descale, v_descale, o_part, lse_part,
+                            num_splits, B, H, nq, nk, d, softmax_scale, causal, window_left,
+                            window_right, alibi_slopes, softcap, stream), "fa_fwd_split_fp8")
+    return o_part, lse_part
+
+
+def attention_split_fp8(q, k, v, num_splits=None, out_dtype=torch.float32, stream=None, **kw):
+    """fa_fwd_split_fp8 followed by the combine kernel."""
+    o_part, lse_part = attention_split_partials_fp8(q, k, v, num_splits, stream=stream, **kw)
+    return combine(o_part, lse_part, out_dtype=out_dtype, stream=stream)
 
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,

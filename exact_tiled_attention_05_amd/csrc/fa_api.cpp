@@ -484,6 +484,21 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, int in_dtype, voi
   return fn(p, stream) ? FA_ERR_HIP : FA_OK;
 }
 
+namespace {
+// The FP8 forward instantiation for head_dim, score transforms and split mode.
+int launch_fp8(const fa::FwdParams& p, int head_dim, bool sc, bool al, bool split, void* stream) {
+#define FA_FP8(D, S)                                              \
+  (sc && al ? fa::launch_fwd_fp8<D, true, true, S>(p, stream)     \
+   : sc     ? fa::launch_fwd_fp8<D, true, false, S>(p, stream)    \
+   : al     ? fa::launch_fwd_fp8<D, false, true, S>(p, stream)    \
+            : fa::launch_fwd_fp8<D, false, false, S>(p, stream))
+  const int rc = head_dim == 64 ? (split ? FA_FP8(64, true) : FA_FP8(64, false))
+                                : (split ? FA_FP8(128, true) : FA_FP8(128, false));
+#undef FA_FP8
+  return rc ? FA_ERR_HIP : FA_OK;
+}
+}  // namespace
+
 int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, float k_descale,
                float v_descale, void* o, int o_dtype, float* lse, int batch, int heads,
                int seqlen_q, int seqlen_k, int head_dim, float softmax_scale, int causal,
@@ -514,15 +529,40 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, flo
   fill_common(p, batch, heads, seqlen_q, seqlen_k, qk, causal, window_left, window_right,
               alibi_slopes, softcap, fa::FP8_BM);
   if ((int64_t)p.num_q_tiles * heads * batch > kMaxGroups) return FA_ERR_SHAPE;
-  const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
-#define FA_FP8(D)                                              \
-  (sc && al ? fa::launch_fwd_fp8<D, true, true>(p, stream)     \
-   : sc     ? fa::launch_fwd_fp8<D, true, false>(p, stream)    \
-   : al     ? fa::launch_fwd_fp8<D, false, true>(p, stream)    \
-            : fa::launch_fwd_fp8<D, false, false>(p, stream))
-  const int rc = head_dim == 64 ? FA_FP8(64) : FA_FP8(128);
-#undef FA_FP8
-  return rc ? FA_ERR_HIP : FA_OK;
+  return launch_fp8(p, head_dim, softcap > 0.0f, alibi_slopes != nullptr, false, stream);
+}
+
+int fa_fwd_split_fp8(const void* q, const void* k, const void* v, float q_descale,
+                     float k_descale, float v_descale, float* o_part, float* lse_part,
+                     int num_splits, int batch, int heads, int seqlen_q, int seqlen_k,
+                     int head_dim, float softmax_scale, int causal, int window_left,
+                     int window_right, const float* alibi_slopes, float softcap, void* stream) {
+  if (!q || !k || !v || !o_part || !lse_part) return FA_ERR_NULL;
+  int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
+  if (st) return st;
+  if (num_splits <= 0 || num_splits > (1 << 16)) return FA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return FA_ERR_UNSUPPORTED;
+  if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
+    return st;
+  for (float d : {q_descale, k_descale, v_descale})
+    if (!(d > 0.0f) || !isfinite(d)) return FA_ERR_VALUE;
+  const float qk = softmax_scale * q_descale * k_descale;
+  if (!(qk > 0.0f) || !isfinite(qk)) return FA_ERR_VALUE;
+
+  fa::FwdParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.num_splits = num_splits;
+  p.v_descale = v_descale;
+  fill_common(p, batch, heads, seqlen_q, seqlen_k, qk, causal, window_left, window_right,
+              alibi_slopes, softcap, fa::FP8_BM);
+  if (split_len(seqlen_k, num_splits, fa::FP8_SPLIT_ALIGN) > kMaxSeq) return FA_ERR_SHAPE;
+  p.split_align = fa::FP8_SPLIT_ALIGN;
+  if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
+  return launch_fp8(p, head_dim, softcap > 0.0f, alibi_slopes != nullptr, true, stream);
 }
 
 long long fa_bwd_workspace_bytes(int batch, int heads, int seqlen_q) {

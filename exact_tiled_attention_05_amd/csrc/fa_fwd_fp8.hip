@@ -23,6 +23,11 @@
 // by lanes i / 8 + 2k (k = 0..7); pairs of addressing lanes name the same key
 // and neighbouring 8-column pieces, so byte 8t + k of every lane of a half-wave
 // holds the same key, matching the byte order of the P operand.
+//
+// SPLIT: one workgroup per (query tile, head, batch, key split); the split's
+// keys [s C, (s + 1) C) (C a multiple of the 128-key tile) bound the key range
+// like a window, and the epilogue writes normalised partials for the combine
+// kernel (the update article's split-KV entries, applied to the FP8 forward).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -78,7 +83,7 @@ struct Fp8Waves {
   static constexpr int kWaves = D == 128 ? 2 : 3;
 };
 
-template <int D, bool SOFTCAP, bool ALIBI>
+template <int D, bool SOFTCAP, bool ALIBI, bool SPLIT>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Fp8Waves<D>::kWaves, Fp8Waves<D>::kWaves)))
 void fwd_fp8_kernel(FwdParams p) {
@@ -96,24 +101,27 @@ void fwd_fp8_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
-  const WorkItem wi = decode_work<false>(p);
-  const int b = wi.b, h = wi.h;
+  const WorkItem wi = decode_work<SPLIT>(p);
+  const int b = wi.b, h = wi.h, s = wi.s;
   const SeqInfo si = seq_info(p, b, h);
   const int nq = si.nq, nk = si.nk;
   const int qt = query_tile(wi, nq, kBM);
   if (qt < 0) return;
   const int off = nk - nq;
+  int slo = 0, shi = nk;
+  if constexpr (SPLIT) split_range(p, nk, s, slo, shi);
   const int q0 = qt * kBM, q1 = min(nq, q0 + kBM);
-  const KeyBounds wg = key_bounds(q0, q1, off, 0, nk, p.window_left, p.window_right);
+  const KeyBounds wg = key_bounds(q0, q1, off, slo, shi, p.window_left, p.window_right);
   if (wg.hi <= wg.lo) {
-    write_empty_rows<false>(p, si, b, h, 0, q0, q1, kD, tid, kThreads);
+    write_empty_rows<SPLIT>(p, si, b, h, s, q0, q1, kD, tid, kThreads);
     return;
   }
   const int wq0 = q0 + 32 * w, wq1 = min(nq, wq0 + 32);
   const bool wave_live = wq0 < nq;
-  const KeyBounds wk = key_bounds(wq0, max(wq1, wq0 + 1), off, 0, nk, p.window_left, p.window_right);
+  const KeyBounds wk = key_bounds(wq0, max(wq1, wq0 + 1), off, slo, shi, p.window_left,
+                                  p.window_right);
   const int row = wq0 + r;
-  const KeyBounds rk = key_bounds(row, row + 1, off, 0, nk, p.window_left, p.window_right);
+  const KeyBounds rk = key_bounds(row, row + 1, off, slo, shi, p.window_left, p.window_right);
 
   float slope_log2 = 0.0f;
   if constexpr (ALIBI) slope_log2 = p.alibi[h] * kLog2e;
@@ -186,7 +194,10 @@ void fwd_fp8_kernel(FwdParams p) {
     for (int j = 0; j < kNB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) t[j][v] = sacc[j][v];
-    const float rel = (float)(row + off) - (float)(j0 + 4 * h2);
+    // ALiBi distances are measured from the row's anchor (its diagonal position
+    // clamped into its visible keys), which only differs from the diagonal in
+    // a key split far from the row.
+    const float rel = (float)(ALIBI ? alibi_anchor(row + off, rk) : row + off) - (float)(j0 + 4 * h2);
     transform_scores<kNB, SOFTCAP, ALIBI>(t, p, slope_log2, rel, MASKED, j0, rk.lo, rk.hi, h2);
     bool any_rescale;
     float mc;
@@ -280,33 +291,52 @@ void fwd_fp8_kernel(FwdParams p) {
   }
 #endif
 
-  // Epilogue: O = v_descale * O~ / l, LSE = (c m + log2 l - 8) ln 2.
+  // Epilogue: O = v_descale * O~ / l, LSE = (c m + log2 l - 8) ln 2, with the
+  // anchor's dropped ALiBi constant subtracted (zero without a key split).
   if (!wave_live) return;
   const float l_tot = half_sum(l_run);
   if (row >= nq) return;
   const float inv = l_tot > 0.0f ? p.v_descale / l_tot : 0.0f;
-  const float lse = l_tot > 0.0f ? (m_run * c + __log2f(l_tot) - 8.0f) * kLn2 : kNegInf;
-  const int64_t ob = q_offset(p, si, row, h, kD);
+  float mref = m_run * c;
+  if constexpr (ALIBI) mref -= slope_log2 * (float)abs(row + off - alibi_anchor(row + off, rk));
+  const float lse = l_tot > 0.0f ? (mref + __log2f(l_tot) - 8.0f) * kLn2 : kNegInf;
+  if constexpr (SPLIT) {
+    const int64_t ro = (((int64_t)s * p.B + b) * p.H + h) * p.Nq + row;
+    float* op = p.o_part + ro * kD;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      store_out4(p, ob + 32 * db + 8 * g + 4 * h2, oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
-                 oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-  if (h2 == 0 && p.lse) p.lse[si.lse0 + row] = lse;
+      for (int g = 0; g < 4; ++g) {
+        f32x4_t x = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                     oacc[db][4 * g + 3] * inv};
+        *(f32x4_t*)(op + 32 * db + 8 * g + 4 * h2) = x;
+      }
+    if (h2 == 0) p.lse_part[ro] = lse;
+  } else {
+    const int64_t ob = q_offset(p, si, row, h, kD);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store_out4(p, ob + 32 * db + 8 * g + 4 * h2, oacc[db][4 * g] * inv,
+                   oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+    if (h2 == 0 && p.lse) p.lse[si.lse0 + row] = lse;
+  }
 }
 
 }  // namespace
 
-template <int D, bool SOFTCAP, bool ALIBI>
+template <int D, bool SOFTCAP, bool ALIBI, bool SPLIT>
 int launch_fwd_fp8(const FwdParams& p, void* stream) {
-  const int64_t groups = (int64_t)p.num_q_tiles * p.H * p.B;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)groups), dim3(kThreads), 0,
-                     (hipStream_t)stream, p);
+  const int64_t groups = (int64_t)p.num_q_tiles * p.H * p.B * (SPLIT ? p.num_splits : 1);
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, SOFTCAP, ALIBI, SPLIT>), dim3((unsigned)groups),
+                     dim3(kThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 
-#define FA_INST(D, SC, AL) template int launch_fwd_fp8<D, SC, AL>(const FwdParams&, void*);
+#define FA_INST(D, SC, AL)                                                       \
+  template int launch_fwd_fp8<D, SC, AL, false>(const FwdParams&, void*);        \
+  template int launch_fwd_fp8<D, SC, AL, true>(const FwdParams&, void*);
 FA_INST(64, false, false)
 FA_INST(64, false, true)
 FA_INST(64, true, false)

@@ -94,7 +94,7 @@ template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 int launch_fwd_bf16(const FwdParams& p, void* stream);
 template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
 int launch_fwd_f32(const FwdParams& p, void* stream);
-template <int D, bool SOFTCAP, bool ALIBI>
+template <int D, bool SOFTCAP, bool ALIBI, bool SPLIT>
 int launch_fwd_fp8(const FwdParams& p, void* stream);  // head_dim 64 or 128
 template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream);
@@ -111,6 +111,7 @@ constexpr int BF16_BM = 128;
 constexpr int SPLIT_ALIGN = 64;
 constexpr int F32_BM = 32;
 constexpr int FP8_BM = 128;
+constexpr int FP8_SPLIT_ALIGN = 128;  // key tile of the FP8 forward: fa_fwd_split_fp8 chunks are multiples
 // Backward tiles: keys per dK/dV workgroup, query rows per dQ workgroup, and
 // the query-row block of the row-term workspace.
 constexpr int BWD_BK = 128;

@@ -258,6 +258,29 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, flo
                void* stream);
 
 /*
+ * fa_fwd_split_fp8 - fa_fwd_split for FP8 inputs: the FP8 forward of
+ * fa_fwd_fp8 with its key range cut into splits (the update article's v2.2
+ * split-KV entry applied to the FP8 forward on the deep-analysis page's
+ * roadmap), for short query sets over long key ranges.
+ *
+ * Inputs, descales, score rules and the probability rounding as fa_fwd_fp8
+ * (head_dim 64 or 128). The keys [0, seqlen_k) are cut into num_splits chunks
+ * of C keys, C = ceil(seqlen_k / num_splits) rounded up to a multiple of 128
+ * (the FP8 key tile; fa_split_chunk_len(seqlen_k, num_splits, 128) returns it);
+ * trailing chunks may be empty. Writes, per split s, o_part[s] [batch, heads,
+ * seqlen_q, head_dim] fp32 (normalised, v_descale applied) and lse_part[s]
+ * [batch, heads, seqlen_q] as fa_fwd_split does; fa_splitkv_combine merges them.
+ * Within a split the probabilities are rounded to E4M3 relative to the split's
+ * own largest, so each partial carries fa_fwd_fp8's error bound over its own
+ * keys. Errors as fa_fwd_fp8 and fa_fwd_split (num_splits in [1, 65536]).
+ */
+int fa_fwd_split_fp8(const void* q, const void* k, const void* v, float q_descale,
+                     float k_descale, float v_descale, float* o_part, float* lse_part,
+                     int num_splits, int batch, int heads, int seqlen_q, int seqlen_k,
+                     int head_dim, float softmax_scale, int causal, int window_left,
+                     int window_right, const float* alibi_slopes, float softcap, void* stream);
+
+/*
  * fa_fwd_splitkv_fp8 - fa_fwd_splitkv for one query row over a paged cache of
  * E4M3 codes (the FP8 forward support of the roadmap in "FlashAttention深度
  * 解析：从算法创新到产业变革的全面影响", applied to the stored keys and values
@@ -395,8 +418,9 @@ int fa_splitkv_combine(const float* o_part, const float* lse_part, int num_split
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(int status);
 
-/* Split chunk length C used by fa_fwd_splitkv (page_size = the cache's page size)
- * or fa_fwd_split (page_size = 64) for these sizes, or -1 on bad sizes. */
+/* Split chunk length C used by fa_fwd_splitkv (page_size = the cache's page size),
+ * fa_fwd_split (page_size = 64) or fa_fwd_split_fp8 (page_size = 128) for these
+ * sizes, or -1 on bad sizes. */
 int fa_split_chunk_len(int seqlen_k, int num_splits, int page_size);
 
 /*

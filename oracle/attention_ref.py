@@ -229,14 +229,16 @@ def attention_ref(q, k, v, scale, causal=False, window_left=-1, window_right=-1,
 
 
 def prob_weighted_abs_ref(q, k, v, scale, causal=False, window_left=-1, window_right=-1,
-                          alibi_slopes=None, softcap=0.0, bh=None, weight=None):
+                          alibi_slopes=None, softcap=0.0, bh=None, weight=None, key_lo=0,
+                          key_hi=None):
     """sum_j w(P_ij) |v_j| per row and column, shaped like attention_ref's O
     (w = identity unless `weight` is given, a function applied to P elementwise).
 
     If every probability moves by at most w(P) (before the row is normalised by
     the unchanged sum), O_i moves by at most this; it is the bound used where
     probabilities are rounded to a short format (w(P) = r P for a relative
-    error r, or half the format's spacing at P).
+    error r, or half the format's spacing at P). key_lo/key_hi restrict the keys
+    to one split chunk, P then being the chunk's own softmax (as in splitkv_ref).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -251,12 +253,13 @@ def prob_weighted_abs_ref(q, k, v, scale, causal=False, window_left=-1, window_r
             out[b, :, h] = 0.0
             continue
         for rc in _row_chunks(rows, k.shape[1]):
-            a, e = visible_span(nq, k.shape[1], rc, causal, window_left, window_right)
+            a, e = visible_span(nq, k.shape[1], rc, causal, window_left, window_right, key_lo,
+                                key_hi)
             if e <= a:                                # no visible key: P = 0
                 out[b, rc, h] = 0.0
                 continue
             s = scores_ref(q[b, rc, h], k[b, :, h], rc, nq, scale, causal, window_left,
-                           window_right, slope, softcap, span=(a, e))
+                           window_right, slope, softcap, key_lo, key_hi, span=(a, e))
             p, _, _ = softmax_rows(s)
             wp = p if weight is None else np.where(p > 0, weight(p), 0.0)
             out[b, rc, h] = wp @ np.abs(v[b, a:e, h])

@@ -56,10 +56,12 @@ int launch_fwd_f32(const FwdParams& p, void*) {
   check_fwd(p, (int64_t)p.num_q_tiles * p.H * p.B * (PAGED ? p.num_splits : 1));
   return 0;
 }
-template <int D, bool SOFTCAP, bool ALIBI>
+template <int D, bool SOFTCAP, bool ALIBI, bool SPLIT>
 int launch_fwd_fp8(const FwdParams& p, void*) {
-  require(p.q && p.k && p.v && p.o, "fp8 forward pointers");
-  check_fwd(p, (int64_t)p.num_q_tiles * p.H * p.B);
+  require(p.q && p.k && p.v && (SPLIT ? (p.o_part && p.lse_part) : p.o != nullptr),
+          "fp8 forward pointers");
+  require(!SPLIT || (p.num_splits >= 1 && p.split_align == 128), "fp8 split chunking");
+  check_fwd(p, (int64_t)p.num_q_tiles * p.H * p.B * (SPLIT ? p.num_splits : 1));
   return 0;
 }
 template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
@@ -115,7 +117,8 @@ int noalloc_scratch(float** out) {
   template int launch_decode_bf16<D, SC, AL, false>(const FwdParams&, void*);         \
   template int launch_decode_bf16<D, SC, AL, true>(const FwdParams&, void*);          \
   template int launch_decode_fp8<D, SC, AL>(const FwdParams&, void*);                 \
-  template int launch_fwd_fp8<D, SC, AL>(const FwdParams&, void*);                    \
+  template int launch_fwd_fp8<D, SC, AL, false>(const FwdParams&, void*);             \
+  template int launch_fwd_fp8<D, SC, AL, true>(const FwdParams&, void*);              \
   template int launch_bwd_bf16<D, SC, AL>(const BwdParams&, void*);
 STUB_D(64)
 STUB_D(128)

@@ -399,6 +399,34 @@ def test_fa_fwd_fp8_rejects(kw, code):
     assert fp8(**kw) == code
 
 
+def split8(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, qd=1.0, kd=1.0, vd=1.0, op=FAKE, lp=FAKE, S=4, batch=1,
+             heads=1, seqlen_q=4, seqlen_k=1000, head_dim=128, scale=0.125, causal=0, wl=-1, wr=-1,
+             alibi=None, softcap=0.0, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_fwd_split_fp8(
+        a["q"], a["k"], a["v"], a["qd"], a["kd"], a["vd"], a["op"], a["lp"], a["S"], a["batch"],
+        a["heads"], a["seqlen_q"], a["seqlen_k"], a["head_dim"], a["scale"], a["causal"], a["wl"],
+        a["wr"], a["alibi"], a["softcap"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(op=None), NULL),
+    (dict(lp=None), NULL), (dict(batch=0), SHAPE), (dict(seqlen_q=0), SHAPE), (dict(S=0), SHAPE),
+    (dict(S=(1 << 16) + 1), SHAPE), (dict(head_dim=96), UNSUP), (dict(causal=1, wr=2), MASK),
+    (dict(wl=-2), MASK), (dict(qd=0.0), VALUE), (dict(vd=math.nan), VALUE),
+    (dict(qd=1e30, kd=1e30), VALUE), (dict(scale=-1.0), VALUE), (dict(softcap=-1.0), VALUE),
+])
+def test_fa_fwd_split_fp8_rejects(kw, code):
+    assert split8(**kw) == code
+
+
+def test_fp8_split_chunks_are_multiples_of_the_fp8_key_tile():
+    assert fa.fa_split_chunk_len(1000, 4, 128) == 256
+    assert fa.fa_split_chunk_len(4096, 8, 128) == 512
+    assert fa.fa_split_chunk_len(100, 3, 128) == 128
+
+
 def test_num_splits_heuristic():
     # One query row: at least one workgroup per compute unit (256 here), head
     # groups of 256-byte segments, at most one split per page and 64 splits.
@@ -457,6 +485,8 @@ def launches():
     (lambda **kw: split_fp8(**kw), dict()),
     (lambda **kw: split_append(**kw), dict()),
     (lambda **kw: fp8(**kw), dict()),
+    (lambda **kw: split8(**kw), dict()),
+    (lambda **kw: split8(**kw), dict(S=1 << 16, seqlen_k=1 << 28)),
     (lambda **kw: bwd(**kw), dict()),
     (lambda **kw: bwd(**kw), dict(batch=1 << 10, heads=1 << 10, seqlen_q=1 << 11, seqlen_k=1)),
     (lambda **kw: bwd_noalloc(**kw), dict()),

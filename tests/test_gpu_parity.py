@@ -931,6 +931,98 @@ def test_fp8_sliding_window_head_dim_64():
               w.window_right, None, 0.0, "fp8 window", bh=[(0, 0), (0, 9), (0, 15)])
 
 
+# (B, H, nq, nk, splits, causal, wl, wr, alibi, cap, q/k/v descales)
+FP8_SPLIT_CASES = [
+    (2, 3, 200, 1000, 4, True, -1, -1, False, 0.0, 1.0, 1.0, 1.0),
+    (1, 2, 64, 3000, 7, True, -1, -1, True, 30.0, 0.5, 2.0, 0.25),   # ALiBi far from the row
+    (1, 2, 300, 300, 3, False, 50, 20, True, 0.0, 1.0, 1.0, 1.0),
+    (2, 2, 500, 90, 2, True, -1, -1, False, 10.0, 1.0, 1.0, 1.0),    # Nq > Nk: rows with no key
+    (1, 2, 5, 129, 6, False, -1, -1, False, 0.0, 1.0, 1.0, 1.0),     # more splits than key tiles
+]
+
+
+def check_fp8_partials(o_part, lse_part, q8, k8, v8, ds, scale, causal, wl, wr, slopes, cap, S,
+                       what):
+    """Each split's partial against the oracle's split partial on the dequantised inputs,
+    within twice the E4M3 rounding bound over that split's own keys."""
+    from gpu_common import e4m3_half_spacing
+    qf = W.to_float(q8, "fp8") * ds[0]
+    kf = W.to_float(k8, "fp8") * ds[1]
+    vf = W.to_float(v8, "fp8") * ds[2]
+    nk = k8.shape[1]
+    rop, rlp = O.splitkv_ref(qf, kf, vf, S, 128, scale, causal, wl, wr, slopes, cap)
+    for si, (lo, hi) in enumerate(O.split_bounds(nk, S, 128)):
+        bound = O.prob_weighted_abs_ref(qf, kf, vf, scale, causal, wl, wr, slopes, cap,
+                                        weight=lambda pp: e4m3_half_spacing(256.0 * pp) / 256.0,
+                                        key_lo=lo, key_hi=hi)
+        for b in range(q8.shape[0]):
+            for h in range(q8.shape[2]):
+                og, rg = o_part[si, b, h], rop[si, b, h]
+                empty = ~np.isfinite(rlp[si, b, h])
+                assert np.array_equal(empty, ~np.isfinite(lse_part[si, b, h])), \
+                    f"{what} split {si}: empty-row pattern"
+                assert not np.isnan(og).any(), f"{what} split {si}: NaN"
+                assert np.all(og[empty] == 0.0), f"{what} split {si}: empty rows not zero"
+                tol = 2.0 * bound[b, :, h] + 1e-5 * max(float(np.abs(rg).max()), 1e-30)
+                bad = np.argwhere(np.abs(og - rg) > tol)
+                assert len(bad) == 0, f"{what} split {si} b{b} h{h}: {len(bad)} over the bound"
+                if (~empty).any():
+                    dl = np.abs(lse_part[si, b, h][~empty] - rlp[si, b, h][~empty]).max()
+                    assert dl <= TOL_LSE, f"{what} split {si}: lse {dl:.2e}"
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("case", FP8_SPLIT_CASES)
+def test_fp8_split_partials_and_combined(case, d):
+    B, H, nq, nk, S, causal, wl, wr, alibi, cap, qd, kd, vd = case
+    say(f"fp8 split d{d} {case}")
+    q8, k8, v8 = fp8_case(9500 + FP8_SPLIT_CASES.index(case) + 50 * (d == 64), B, nq, nk, H, d)
+    slopes = W.alibi_slopes(H) if alibi else None
+    ts = None if slopes is None else torch.from_numpy(slopes).cuda()
+    scale = 1.0 / np.sqrt(d)
+    tq, tk, tv = to_dev_fp8(q8), to_dev_fp8(k8), to_dev_fp8(v8)
+    o_part, lse_part = fa.attention_split_partials_fp8(tq, tk, tv, S, qd, kd, vd, scale, causal,
+                                                       wl, wr, ts, cap)
+    o, lse = fa.combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    assert fa.fa_split_chunk_len(nk, S, 128) == -(-(-(-nk // S)) // 128) * 128
+    check_fp8_partials(o_part.cpu().numpy(), lse_part.cpu().numpy(), q8, k8, v8, (qd, kd, vd),
+                       scale, causal, wl, wr, slopes, cap, S, f"fp8 split {case}")
+    print(check_fp8(o.cpu().numpy(), lse.cpu().numpy(), q8, k8, v8, (qd, kd, vd), scale, causal,
+                    wl, wr, slopes, cap, f"fp8 split combined {case}"))
+
+
+@pytest.mark.parametrize("d,alibi,cap", [(128, True, 30.0), (64, False, 0.0)])
+def test_fp8_one_split_is_bitwise_fa_fwd_fp8(d, alibi, cap):
+    """One split covers every key with the same tiles in the same order: its partial is
+    fa_fwd_fp8's fp32 output and LSE bit for bit."""
+    q8, k8, v8 = fp8_case(9600 + d, 2, 300, 700, 4, d)
+    ts = torch.from_numpy(W.alibi_slopes(4)).cuda() if alibi else None
+    tq, tk, tv = to_dev_fp8(q8), to_dev_fp8(k8), to_dev_fp8(v8)
+    o, lse = fa.attention_fp8(tq, tk, tv, 0.5, 1.5, 2.0, 0.1, True, -1, -1, ts, cap)
+    o_part, lse_part = fa.attention_split_partials_fp8(tq, tk, tv, 1, 0.5, 1.5, 2.0, 0.1, True,
+                                                       -1, -1, ts, cap)
+    torch.cuda.synchronize()
+    assert torch.equal(o_part[0], o.permute(0, 2, 1, 3)) and torch.equal(lse_part[0], lse)
+
+
+def test_fp8_split_alibi_softcap_shape():
+    """The ALiBi + softcap set (B2 H8 Nq512 Nk4096 d128, amplitude 2, causal) in E4M3
+    through 8 key splits and the combine kernel, every head and row."""
+    w = W.WORKLOADS[5]
+    say("fp8 split alibi softcap shape")
+    q8, k8, v8 = (W.gen_tensor(w.seed, t, w.B, n, w.H, w.d, w.amp, "fp8")
+                  for t, n in ((W.TENSOR_Q, w.Nq), (W.TENSOR_K, w.Nk), (W.TENSOR_V, w.Nk)))
+    slopes = w.slopes()
+    ts = torch.from_numpy(np.asarray(slopes, np.float32)).cuda()
+    o, lse = fa.attention_split_fp8(to_dev_fp8(q8), to_dev_fp8(k8), to_dev_fp8(v8), 8,
+                                    softmax_scale=w.scale, causal=True, alibi_slopes=ts,
+                                    softcap=w.softcap)
+    torch.cuda.synchronize()
+    print(check_fp8(o.cpu().numpy(), lse.cpu().numpy(), q8, k8, v8, (1.0, 1.0, 1.0), w.scale,
+                    True, -1, -1, slopes, w.softcap, "fp8 split cfg5 shape"))
+
+
 # --------------------------------------------------------------------------
 # Brute-force sweeps of small and ragged shapes: backward and FP8
 # --------------------------------------------------------------------------

@@ -8,7 +8,8 @@ are unchanged, so every output must agree bit for bit with libfa.so; a copy that
 overwrote a stage still being read, or a read of a stage not yet written, would show
 up as a difference. Covered: the contiguous forward (whole key range, batched and
 packed), its key splits, the paged multi-row pass with page-aligned tiles and with
-rows gathered one by one, and the FP8 forward at both head sizes.
+rows gathered one by one, and the FP8 forward (whole key range and key splits) at both
+head sizes.
 """
 import ctypes
 import os
@@ -126,3 +127,15 @@ def test_fp8_forward_matches_serial_copies(serial_lib, d):
     m, s = both(serial_lib, fa.attention_fp8, q8, k8, v8, 0.5, 1.0, 2.0, 1.0 / np.sqrt(d), True,
                 -1, -1, ts, 20.0)
     assert_same(m, s, f"fa_fwd_fp8 d{d}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp8_split_matches_serial_copies(serial_lib, d):
+    say(f"hazard fa_fwd_split_fp8 d{d}")
+    B, H, nq, nk = 2, 4, 600, 3000
+    q8, k8, v8 = (torch.from_numpy(W.gen_tensor(7400 + d, t, B, n, H, d, 1.0, "fp8")).cuda()
+                  for t, n in ((W.TENSOR_Q, nq), (W.TENSOR_K, nk), (W.TENSOR_V, nk)))
+    ts = torch.from_numpy(W.alibi_slopes(H)).cuda()
+    m, s = both(serial_lib, fa.attention_split_partials_fp8, q8, k8, v8, 5, 0.5, 1.0, 2.0,
+                1.0 / np.sqrt(d), True, -1, -1, ts, 20.0)
+    assert_same(m, s, f"fa_fwd_split_fp8 d{d}")

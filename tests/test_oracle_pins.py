@@ -944,6 +944,58 @@ def test_t29_probability_weighted_bound():
     assert np.all(b3[0, :4] == 0.0)
 
 
+def _loop_weighted_abs(q, k, v, scale, causal, wl, wr, slope, cap, lo, hi, weight):
+    """sum_j w(P_ij) |v_j| with P the softmax over the keys [lo, hi) row i may see,
+    written out key by key (mask, cap and ALiBi from their definitions)."""
+    nq, nk = q.shape[0], k.shape[0]
+    off = nk - nq
+    out = np.zeros((nq, v.shape[1]))
+    for i in range(nq):
+        ip = i + off
+        keys, sc = [], []
+        for j in range(lo, hi):
+            if (causal and j > ip) or (wl >= 0 and j < ip - wl) or (wr >= 0 and j > ip + wr):
+                continue
+            x = scale * float(np.dot(q[i], k[j]))
+            if cap > 0:
+                x = cap * math.tanh(x / cap)
+            if slope is not None:
+                x -= slope * abs(ip - j)
+            keys.append(j)
+            sc.append(x)
+        if not keys:
+            continue
+        m = max(sc)
+        e = [math.exp(x - m) for x in sc]
+        tot = sum(e)
+        for j, ej in zip(keys, e):
+            out[i] += weight(ej / tot) * np.abs(v[j])
+    return out
+
+
+@pytest.mark.parametrize("causal,wl,wr,slope,cap", [(True, -1, -1, None, 0.0),
+                                                   (False, 3, 2, 0.4, 2.0),
+                                                   (True, 5, -1, 0.2, 0.0)])
+def test_t29_probability_weighted_bound_over_a_key_range(causal, wl, wr, slope, cap):
+    """Restricted to one split's keys [lo, hi), the bound is the split's own softmax
+    weighting |V| (checked against a key-by-key loop), and over [0, Nk) it is the
+    unrestricted bound."""
+    nq, nk, d = 6, 11, 3
+    q, k, v = rnd(81, 1, nq, 1, d), rnd(82, 1, nk, 1, d), rnd(83, 1, nk, 1, d)
+    slopes = None if slope is None else np.array([slope])
+    w = lambda pp: 0.25 * np.sqrt(pp)                  # any function of P; nonlinear on purpose
+    for lo, hi in [(0, nk), (0, 4), (4, 8), (8, 11), (3, 3)]:
+        got = O.prob_weighted_abs_ref(q, k, v, 0.7, causal, wl, wr, slopes, cap, weight=w,
+                                      key_lo=lo, key_hi=hi)[0, :, 0]
+        ref = _loop_weighted_abs(q[0, :, 0], k[0, :, 0], v[0, :, 0], 0.7, causal, wl, wr, slope,
+                                 cap, lo, hi, lambda pp: 0.25 * math.sqrt(pp))
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+    full = O.prob_weighted_abs_ref(q, k, v, 0.7, causal, wl, wr, slopes, cap, weight=w)
+    np.testing.assert_array_equal(full, O.prob_weighted_abs_ref(q, k, v, 0.7, causal, wl, wr,
+                                                                 slopes, cap, weight=w,
+                                                                 key_lo=0, key_hi=nk))
+
+
 def test_t29_e4m3_half_spacing_matches_the_code_table():
     import gpu_common as G
     vals = W.e4m3_bits_to_f32(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)   # 0 .. 448
