@@ -565,7 +565,6 @@ def main():
     torch.cuda.synchronize()
     t_d8 = np.array([a.elapsed_time(e) for a, e in ev6]) * 1e-3
     assert torch.isfinite(do).all()
-    del dk8, dv8
     fp8_decode_line = {"workload": "paged_splitkv_decode over an E4M3 cache (fa_fwd_splitkv_fp8 + combine)",
                        "gbytes": round(f8_decode_bytes / 1e9, 5), "ms": round(t_d8.mean() * 1e3, 5),
                        "ms_median": round(float(np.median(t_d8)) * 1e3, 5),
@@ -609,7 +608,41 @@ def main():
                   "ms": round(t_pc.mean() * 1e3, 5), "ms_median": round(float(np.median(t_pc)) * 1e3, 5),
                   "tflops": round(chunk_flops / t_pc.mean() / 1e12, 3),
                   "pct_peak": round(100 * chunk_flops / t_pc.mean() / 1e12 / PEAK_BF16_TFLOPS, 2)}
-    del cop, clp, co, clse
+
+    # ---- the same chunk in E4M3 (side measurement): 512 E4M3 query rows over the
+    # E4M3 copy of the pool's first sequence, fa_fwd_paged_fp8 with the same split
+    # count, then the combine into the same buffers.
+    cq8 = up8(W.gen_tensor(wd.seed, W.TENSOR_Q, 1, 512, wd.H, wd.d, 1.0, "fp8"))
+
+    def paged_chunk_fp8():
+        check(fa.fa_fwd_paged_fp8(cq8, dk8, dv8, 1.0, 1.0, 1.0, cbt, cbt.shape[1], wd.page_size,
+                                  None, cop, clp, CS, 1, wd.H, 512, wd.Nk, wd.d, wd.scale, True,
+                                  -1, -1, None, 0.0, stream), "fa_fwd_paged_fp8")
+        check(fa.fa_splitkv_combine(cop, clp, CS, 1, wd.H, 512, wd.d, co, clse, stream),
+              "fa_splitkv_combine")
+
+    for _ in range(args.warmup):
+        paged_chunk_fp8()
+    ev10 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(K)]
+    for a, e in ev10:
+        a.record(stream)
+        paged_chunk_fp8()
+        e.record(stream)
+    torch.cuda.synchronize()
+    t_pc8 = np.array([a.elapsed_time(e) for a, e in ev10]) * 1e-3
+    assert torch.isfinite(co).all()
+    pc8_tflops = chunk_flops / t_pc8.mean() / 1e12
+    chunk8_line = {"workload": "the 512-row chunk in E4M3 over an E4M3 copy of the paged sequence "
+                               "(fa_fwd_paged_fp8 + combine)",
+                   "num_splits": CS, "gflop": round(chunk_flops / 1e9, 4),
+                   "ms": round(t_pc8.mean() * 1e3, 5),
+                   "ms_median": round(float(np.median(t_pc8)) * 1e3, 5),
+                   "tflops": round(pc8_tflops, 3),
+                   "roofline": {"bound": "mfma", "achieved": round(pc8_tflops, 3),
+                                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                                "frac": round(pc8_tflops / PEAK_FP8_TFLOPS, 4)}}
+    del cop, clp, co, clse, cq8, dk8, dv8
 
     # ---- one decode step of a small serving batch (side measurement): append of
     # the step's key and value, split pass and combine for 1 sequence of 4096
@@ -778,6 +811,7 @@ def main():
         "fp8_decode": fp8_decode_line,
         "serving_step": serving_line,
         "paged_prefill_chunk": chunk_line,
+        "fp8_paged_prefill_chunk": chunk8_line,
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("prefill"),

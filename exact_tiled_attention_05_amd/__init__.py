@@ -2,12 +2,12 @@
 
 The functions named like the C ABI (``fa_fwd``, ``fa_fwd_split``,
 ``fa_fwd_splitkv``, ``fa_fwd_splitkv_seqlens``, ``fa_fwd_splitkv_append``, ``fa_fwd_varlen``,
-``fa_fwd_fp8``, ``fa_fwd_split_fp8``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_splitkv_combine``, ``fa_status_string``,
+``fa_fwd_fp8``, ``fa_fwd_split_fp8``, ``fa_fwd_splitkv_fp8``, ``fa_fwd_paged_fp8``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_splitkv_combine``, ``fa_status_string``,
 ``fa_split_chunk_len``) only
 marshal arguments: torch tensors become device pointers, the current torch
 stream becomes the HIP stream, and every step of the computation runs in the
 library's kernels. ``attention``, ``attention_fp8``, ``attention_split_fp8``, ``attention_varlen``, ``attention_split``,
-``attention_paged_splitkv``, ``attention_paged_append``, ``attention_backward``,
+``attention_paged_splitkv``, ``attention_paged_fp8``, ``attention_paged_append``, ``attention_backward``,
 ``combine`` and ``decode_paged`` add output allocation (torch.empty) on top of them.
 
 The library must be built (``python -m exact_tiled_attention_05_amd.build``);
@@ -25,11 +25,12 @@ __all__ = [
     "FA_FP32", "FA_BF16", "FaError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
     "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_split_fp8", "fa_fwd_splitkv_fp8",
-    "fa_bwd", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
+    "fa_fwd_paged_fp8", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
     "fa_split_chunk_len", "fa_num_splits",
     "attention", "attention_fp8", "attention_split_fp8", "attention_split_partials_fp8",
     "attention_varlen", "attention_split", "attention_split_partials",
-    "attention_paged_splitkv", "attention_paged_splitkv_fp8", "attention_paged_append",
+    "attention_paged_splitkv", "attention_paged_splitkv_fp8", "attention_paged_fp8",
+    "attention_paged_append",
     "attention_backward", "attention_varlen_backward", "combine", "decode_paged",
 ]
 
@@ -40,7 +41,7 @@ _lib = None
 
 EXPORTED = ("fa_fwd", "fa_fwd_split", "fa_fwd_splitkv", "fa_fwd_splitkv_seqlens",
             "fa_fwd_splitkv_append", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_split_fp8",
-            "fa_fwd_splitkv_fp8", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
+            "fa_fwd_splitkv_fp8", "fa_fwd_paged_fp8", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "fa_bwd_varlen", "fa_splitkv_combine", "fa_status_string",
             "fa_split_chunk_len", "fa_num_splits")
 
 
@@ -90,6 +91,9 @@ def declare(lib):
     lib.fa_fwd_splitkv_fp8.argtypes = [vp, vp, vp, f, f, vp, i, i, vp, vp, vp, i, i, i, i, i, i,
                                        f, i, i, i, vp, f, vp]
     lib.fa_fwd_splitkv_fp8.restype = i
+    lib.fa_fwd_paged_fp8.argtypes = [vp, vp, vp, f, f, f, vp, i, i, vp, vp, vp, i, i, i, i, i, i,
+                                     f, i, i, i, vp, f, vp]
+    lib.fa_fwd_paged_fp8.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, i, vp, i, i, i, i, i, f, i,
                            i, i, vp, f, vp]
     lib.fa_bwd.restype = i
@@ -288,6 +292,22 @@ def fa_fwd_splitkv_fp8(q, k_cache, v_cache, k_descale, v_descale, block_table,
         _ptr(o_part), _ptr(lse_part), int(num_splits), int(batch), int(heads), int(seqlen_q),
         int(seqlen_k), int(head_dim), float(softmax_scale), int(bool(causal)), int(window_left),
         int(window_right), _slopes_ptr(alibi_slopes, heads, q), float(softcap), _stream(stream))
+
+
+def fa_fwd_paged_fp8(q, k_cache, v_cache, q_descale, k_descale, v_descale, block_table,
+                     max_pages_per_seq, page_size, cache_seqlens, o_part, lse_part, num_splits,
+                     batch, heads, seqlen_q, seqlen_k, head_dim, softmax_scale, causal=False,
+                     window_left=-1, window_right=-1, alibi_slopes=None, softcap=0.0,
+                     stream=None) -> int:
+    """Call fa_fwd_paged_fp8 on caller-allocated tensors (q and the caches: E4M3 codes);
+    returns the status code."""
+    return load_library().fa_fwd_paged_fp8(
+        _ptr_fp8(q), _ptr_fp8(k_cache), _ptr_fp8(v_cache), float(q_descale), float(k_descale),
+        float(v_descale), _ptr(block_table), int(max_pages_per_seq), int(page_size),
+        _ptr(cache_seqlens), _ptr(o_part), _ptr(lse_part), int(num_splits), int(batch),
+        int(heads), int(seqlen_q), int(seqlen_k), int(head_dim), float(softmax_scale),
+        int(bool(causal)), int(window_left), int(window_right),
+        _slopes_ptr(alibi_slopes, heads, q), float(softcap), _stream(stream))
 
 
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, batch, heads, seqlen_q, seqlen_k,
@@ -529,6 +549,35 @@ def attention_paged_splitkv_fp8(q, k_cache, v_cache, k_descale, v_descale, block
                               num_splits, B, H, nq, seqlen_k, d, softmax_scale, causal,
                               window_left, window_right, alibi_slopes, softcap, stream),
            "fa_fwd_splitkv_fp8")
+    return o_part, lse_part
+
+
+def attention_paged_fp8(q, k_cache, v_cache, block_table, seqlen_k, num_splits=None,
+                        q_descale=1.0, k_descale=1.0, v_descale=1.0, softmax_scale=None,
+                        causal=False, window_left=-1, window_right=-1, alibi_slopes=None,
+                        softcap=0.0, stream=None, cache_seqlens=None):
+    """Split partials o_part [S,B,H,Nq,d] and lse_part [S,B,H,Nq] of the FP8 forward of E4M3
+    q [B,Nq,H,d] over a paged E4M3 cache [num_pages, page_size, H, d] (page_size a multiple
+    of 128; uint8 codes or float8_e4m3fn)."""
+    B, nq, H, d = q.shape
+    _, page_size, Hc, dc = k_cache.shape
+    if (Hc, dc) != (H, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache must be [num_pages, page_size, H, d] matching q")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages_per_seq]")
+    if cache_seqlens is not None and (cache_seqlens.dtype != torch.int32
+                                      or tuple(cache_seqlens.shape) != (B,)):
+        raise ValueError("cache_seqlens must be int32 [B]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    num_splits = _splits(num_splits, B, H, nq, seqlen_k, d, page_size)
+    o_part = torch.empty((num_splits, B, H, nq, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((num_splits, B, H, nq), dtype=torch.float32, device=q.device)
+    _check(fa_fwd_paged_fp8(q, k_cache, v_cache, q_descale, k_descale, v_descale, block_table,
+                            block_table.shape[1], page_size, cache_seqlens, o_part, lse_part,
+                            num_splits, B, H, nq, seqlen_k, d, softmax_scale, causal,
+                            window_left, window_right, alibi_slopes, softcap, stream),
+           "fa_fwd_paged_fp8")
     return o_part, lse_part
 
 

@@ -485,15 +485,20 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, int in_dtype, voi
 }
 
 namespace {
-// The FP8 forward instantiation for head_dim, score transforms and split mode.
-int launch_fp8(const fa::FwdParams& p, int head_dim, bool sc, bool al, bool split, void* stream) {
-#define FA_FP8(D, S)                                              \
-  (sc && al ? fa::launch_fwd_fp8<D, true, true, S>(p, stream)     \
-   : sc     ? fa::launch_fwd_fp8<D, true, false, S>(p, stream)    \
-   : al     ? fa::launch_fwd_fp8<D, false, true, S>(p, stream)    \
-            : fa::launch_fwd_fp8<D, false, false, S>(p, stream))
-  const int rc = head_dim == 64 ? (split ? FA_FP8(64, true) : FA_FP8(64, false))
-                                : (split ? FA_FP8(128, true) : FA_FP8(128, false));
+// The FP8 forward instantiation for head_dim, score transforms and mode
+// (fa::FWD_CONTIG, fa::FWD_CONTIG_SPLIT or fa::FWD_PAGED_TILES).
+int launch_fp8(const fa::FwdParams& p, int head_dim, bool sc, bool al, int mode, void* stream) {
+#define FA_FP8(D, M)                                              \
+  (sc && al ? fa::launch_fwd_fp8<D, true, true, M>(p, stream)     \
+   : sc     ? fa::launch_fwd_fp8<D, true, false, M>(p, stream)    \
+   : al     ? fa::launch_fwd_fp8<D, false, true, M>(p, stream)    \
+            : fa::launch_fwd_fp8<D, false, false, M>(p, stream))
+#define FA_FP8_D(D)                                                    \
+  (mode == fa::FWD_CONTIG         ? FA_FP8(D, fa::FWD_CONTIG)          \
+   : mode == fa::FWD_CONTIG_SPLIT ? FA_FP8(D, fa::FWD_CONTIG_SPLIT)    \
+                                  : FA_FP8(D, fa::FWD_PAGED_TILES))
+  const int rc = head_dim == 64 ? FA_FP8_D(64) : FA_FP8_D(128);
+#undef FA_FP8_D
 #undef FA_FP8
   return rc ? FA_ERR_HIP : FA_OK;
 }
@@ -529,7 +534,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, flo
   fill_common(p, batch, heads, seqlen_q, seqlen_k, qk, causal, window_left, window_right,
               alibi_slopes, softcap, fa::FP8_BM);
   if ((int64_t)p.num_q_tiles * heads * batch > kMaxGroups) return FA_ERR_SHAPE;
-  return launch_fp8(p, head_dim, softcap > 0.0f, alibi_slopes != nullptr, false, stream);
+  return launch_fp8(p, head_dim, softcap > 0.0f, alibi_slopes != nullptr, fa::FWD_CONTIG, stream);
 }
 
 int fa_fwd_split_fp8(const void* q, const void* k, const void* v, float q_descale,
@@ -562,7 +567,59 @@ int fa_fwd_split_fp8(const void* q, const void* k, const void* v, float q_descal
   if (split_len(seqlen_k, num_splits, fa::FP8_SPLIT_ALIGN) > kMaxSeq) return FA_ERR_SHAPE;
   p.split_align = fa::FP8_SPLIT_ALIGN;
   if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
-  return launch_fp8(p, head_dim, softcap > 0.0f, alibi_slopes != nullptr, true, stream);
+  return launch_fp8(p, head_dim, softcap > 0.0f, alibi_slopes != nullptr, fa::FWD_CONTIG_SPLIT,
+                    stream);
+}
+
+int fa_fwd_paged_fp8(const void* q, const void* k_cache, const void* v_cache, float q_descale,
+                     float k_descale, float v_descale, const int* block_table,
+                     int max_pages_per_seq, int page_size, const int* cache_seqlens,
+                     float* o_part, float* lse_part, int num_splits, int batch, int heads,
+                     int seqlen_q, int seqlen_k, int head_dim, float softmax_scale, int causal,
+                     int window_left, int window_right, const float* alibi_slopes, float softcap,
+                     void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !o_part || !lse_part) return FA_ERR_NULL;
+  int st = check_sizes(batch, heads, seqlen_q, seqlen_k);
+  if (st) return st;
+  if (num_splits <= 0 || num_splits > (1 << 16) || max_pages_per_seq <= 0 || page_size <= 0)
+    return FA_ERR_SHAPE;
+  if ((int64_t)max_pages_per_seq * page_size < seqlen_k) return FA_ERR_SHAPE;
+  if ((int64_t)page_size * heads * head_dim >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return FA_ERR_UNSUPPORTED;
+  // Every 128-key tile must lie inside one page.
+  if (page_size % fa::FP8_SPLIT_ALIGN != 0) return FA_ERR_UNSUPPORTED;
+  if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
+    return st;
+  for (float d : {q_descale, k_descale, v_descale})
+    if (!(d > 0.0f) || !isfinite(d)) return FA_ERR_VALUE;
+  const float qk = softmax_scale * q_descale * k_descale;
+  if (!(qk > 0.0f) || !isfinite(qk)) return FA_ERR_VALUE;
+
+  fa::FwdParams p = {};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.block_table = block_table;
+  p.max_pages = max_pages_per_seq;
+  p.page_size = page_size;
+  p.page_shift = -1;
+  if ((page_size & (page_size - 1)) == 0)
+    for (int sh = 0; sh < 31; ++sh)
+      if ((1 << sh) == page_size) p.page_shift = sh;
+  p.row_stride = heads * head_dim;
+  p.page_stride = (int64_t)page_size * heads * head_dim;
+  p.seqlens_k = cache_seqlens;
+  p.num_splits = num_splits;
+  p.v_descale = v_descale;
+  fill_common(p, batch, heads, seqlen_q, seqlen_k, qk, causal, window_left, window_right,
+              alibi_slopes, softcap, fa::FP8_BM);
+  if (split_len(seqlen_k, num_splits, page_size) > kMaxSeq) return FA_ERR_SHAPE;
+  p.split_align = page_size;
+  if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
+  return launch_fp8(p, head_dim, softcap > 0.0f, alibi_slopes != nullptr, fa::FWD_PAGED_TILES,
+                    stream);
 }
 
 long long fa_bwd_workspace_bytes(int batch, int heads, int seqlen_q) {

@@ -24,10 +24,14 @@
 // and neighbouring 8-column pieces, so byte 8t + k of every lane of a half-wave
 // holds the same key, matching the byte order of the P operand.
 //
-// SPLIT: one workgroup per (query tile, head, batch, key split); the split's
-// keys [s C, (s + 1) C) (C a multiple of the 128-key tile) bound the key range
-// like a window, and the epilogue writes normalised partials for the combine
-// kernel (the update article's split-KV entries, applied to the FP8 forward).
+// MODE FWD_CONTIG_SPLIT: one workgroup per (query tile, head, batch, key
+// split); the split's keys [s C, (s + 1) C) (C a multiple of the 128-key tile)
+// bound the key range like a window, and the epilogue writes normalised
+// partials for the combine kernel (the update article's split-KV entries,
+// applied to the FP8 forward). MODE FWD_PAGED_TILES: the same over a paged
+// cache (the article's paged KV entry) whose pages hold a multiple of 128 keys,
+// so every key tile lies inside one page with the row stride of a contiguous
+// tensor and travels from a per-tile base address.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -83,10 +87,13 @@ struct Fp8Waves {
   static constexpr int kWaves = D == 128 ? 2 : 3;
 };
 
-template <int D, bool SOFTCAP, bool ALIBI, bool SPLIT>
+template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Fp8Waves<D>::kWaves, Fp8Waves<D>::kWaves)))
 void fwd_fp8_kernel(FwdParams p) {
+  static_assert(MODE == FWD_CONTIG || MODE == FWD_CONTIG_SPLIT || MODE == FWD_PAGED_TILES, "mode");
+  constexpr bool SPLIT = MODE != FWD_CONTIG;       // one key split per workgroup, partial outputs
+  constexpr bool PTILES = MODE == FWD_PAGED_TILES; // K/V tiles from one page each
   constexpr int kD = D;             // head_dim (bytes per K/V row of one head)
   constexpr int kTile = kBN * kD;   // bytes per K or V tile
   constexpr int kCPR = kD / 16;     // 16-byte chunks per row
@@ -154,17 +161,40 @@ void fwd_fp8_kernel(FwdParams p) {
     const int trow = kRPL * (kLoads * wu + i) + lane / kCPR;
     lane_bytes[i] = (unsigned)(trow * row_bytes + 16 * ((lane % kCPR) ^ swz_fp8<kD>(trow)));
   }
-  auto copy_tiles = [&](uint8_t* kd, uint8_t* vd, int j0) __attribute__((always_inline)) {
-    const int64_t tb = (int64_t)j0 * row_bytes;
-    const int64_t left = end_bytes - tb;
+  // One tile of K and V whose first rows start `koff` bytes into the K and V
+  // tensors (or page pools), `left` bytes of it in range.
+  auto copy_at = [&](const char* kb, const char* vb, int64_t left, uint8_t* kd, uint8_t* vd)
+                     __attribute__((always_inline)) {
     const int n = left <= 0 ? 0 : (left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
-    const __amdgpu_buffer_rsrc_t rk_ = make_rsrc(kbh + tb, n);
-    const __amdgpu_buffer_rsrc_t rv_ = make_rsrc(vbh + tb, n);
+    const __amdgpu_buffer_rsrc_t rk_ = make_rsrc(kb, n);
+    const __amdgpu_buffer_rsrc_t rv_ = make_rsrc(vb, n);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       buffer_load_lds16(rk_, (uint16_t*)(kd + 1024 * (kLoads * wu + i)), lane_bytes[i]);
       buffer_load_lds16(rv_, (uint16_t*)(vd + 1024 * (kLoads * wu + i)), lane_bytes[i]);
     }
+  };
+  auto copy_tiles = [&](uint8_t* kd, uint8_t* vd, int j0) __attribute__((always_inline)) {
+    const int64_t tb = (int64_t)j0 * row_bytes;
+    copy_at(kbh + tb, vbh + tb, end_bytes - tb, kd, vd);
+  };
+  // Paged cache (PTILES): the tile of key j0 from page `page` (its slot j0 mod
+  // page_size is a multiple of the tile); rows past the sequence's last key
+  // read as zeros.
+  auto copy_page_tiles = [&](int page, uint8_t* kd, uint8_t* vd, int j0) __attribute__((always_inline)) {
+    const int slot0 = p.page_shift >= 0 ? j0 & (p.page_size - 1) : j0 % p.page_size;
+    const int64_t pb = (((int64_t)page * p.page_size + slot0) * p.H + h) * kD;
+    copy_at((const char*)p.k + pb, (const char*)p.v + pb, (int64_t)(nk - 1 - j0) * row_bytes + kD,
+            kd, vd);
+  };
+  // Block-table entry of the tile of key j0 (clamped into the workgroup's keys,
+  // so the index stays in the table), read by a vector load: the caller makes it
+  // uniform once the load has been waited for, so the load never stalls the
+  // copies issued beside it.
+  auto page_entry = [&](int j0) __attribute__((always_inline)) {
+    const int kk = min(j0, wg.hi - 1);
+    const int idx = p.page_shift >= 0 ? kk >> p.page_shift : kk / p.page_size;
+    return p.block_table[(int64_t)b * p.max_pages + idx + (lane >> 6)];
   };
 
   f32x16_t oacc[NDB];
@@ -260,7 +290,13 @@ void fwd_fp8_kernel(FwdParams p) {
   // loop bit for bit.
   for (int it = 0; it < ntiles; ++it) {
     const int j0 = j_first + it * kBN;
-    copy_tiles(sK0, sV0, j0);
+    if constexpr (PTILES) {
+      const int pe = page_entry(j0);
+      wait_vmem();
+      copy_page_tiles(__builtin_amdgcn_readfirstlane(pe), sK0, sV0, j0);
+    } else {
+      copy_tiles(sK0, sV0, j0);
+    }
     wait_vmem_barrier<0>();
     if (live(j0)) {
       if (j0 >= wk.flo && j0 + kBN <= wk.fhi)
@@ -271,12 +307,31 @@ void fwd_fp8_kernel(FwdParams p) {
     __syncthreads();
   }
 #else
-  copy_tiles(sK0, sV0, j_first);
+  // Paged cache: step t copies tile t + 1 from the page whose id step t - 1
+  // loaded, then loads the id of tile t + 2's page; the step's closing wait
+  // covers that load too.
+  int pg_next = 0;
+  if constexpr (PTILES) {
+    const int pe0 = page_entry(j_first);
+    wait_vmem();
+    copy_page_tiles(__builtin_amdgcn_readfirstlane(pe0), sK0, sV0, j_first);
+    pg_next = page_entry(j_first + kBN);
+  } else {
+    copy_tiles(sK0, sV0, j_first);
+  }
   wait_vmem_barrier<0>();
   auto step = [&](auto par, int it) __attribute__((always_inline)) {
     constexpr bool ODD = decltype(par)::value;
     const int j0 = j_first + it * kBN;
-    if (it + 1 < ntiles) copy_tiles(ODD ? sK0 : sK1, ODD ? sV0 : sV1, j0 + kBN);
+    if constexpr (PTILES) {
+      if (it + 1 < ntiles) {
+        copy_page_tiles(__builtin_amdgcn_readfirstlane(pg_next), ODD ? sK0 : sK1, ODD ? sV0 : sV1,
+                        j0 + kBN);
+        if (it + 2 < ntiles) pg_next = page_entry(j0 + 2 * kBN);
+      }
+    } else {
+      if (it + 1 < ntiles) copy_tiles(ODD ? sK0 : sK1, ODD ? sV0 : sV1, j0 + kBN);
+    }
     if (live(j0)) {
       if (j0 >= wk.flo && j0 + kBN <= wk.fhi)
         compute(std::false_type{}, ODD ? sK1 : sK0, ODD ? sV1 : sV0, j0);
@@ -326,17 +381,19 @@ void fwd_fp8_kernel(FwdParams p) {
 
 }  // namespace
 
-template <int D, bool SOFTCAP, bool ALIBI, bool SPLIT>
+template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 int launch_fwd_fp8(const FwdParams& p, void* stream) {
-  const int64_t groups = (int64_t)p.num_q_tiles * p.H * p.B * (SPLIT ? p.num_splits : 1);
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, SOFTCAP, ALIBI, SPLIT>), dim3((unsigned)groups),
+  const int64_t groups =
+      (int64_t)p.num_q_tiles * p.H * p.B * (MODE != FWD_CONTIG ? p.num_splits : 1);
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, SOFTCAP, ALIBI, MODE>), dim3((unsigned)groups),
                      dim3(kThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 
-#define FA_INST(D, SC, AL)                                                       \
-  template int launch_fwd_fp8<D, SC, AL, false>(const FwdParams&, void*);        \
-  template int launch_fwd_fp8<D, SC, AL, true>(const FwdParams&, void*);
+#define FA_INST(D, SC, AL)                                                          \
+  template int launch_fwd_fp8<D, SC, AL, FWD_CONTIG>(const FwdParams&, void*);       \
+  template int launch_fwd_fp8<D, SC, AL, FWD_CONTIG_SPLIT>(const FwdParams&, void*); \
+  template int launch_fwd_fp8<D, SC, AL, FWD_PAGED_TILES>(const FwdParams&, void*);
 FA_INST(64, false, false)
 FA_INST(64, false, true)
 FA_INST(64, true, false)

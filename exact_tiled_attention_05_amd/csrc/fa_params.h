@@ -86,7 +86,8 @@ enum FwdMode {
   FWD_PAGED_SPLIT = 2,   // paged K/V through the block table, per split -> o_part, lse_part
                          //   (rows gathered one by one: any page size, appended keys)
   FWD_PAGED_TILES = 3,   // the same with page_size a multiple of 64 and no append:
-                         //   whole 64-key tiles from one page each
+                         //   whole 64-key tiles from one page each (FP8 forward:
+                         //   a multiple of 128, its key tile)
 };
 
 // Launchers (defined in the .hip files). Return hipError_t as int.
@@ -94,8 +95,9 @@ template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 int launch_fwd_bf16(const FwdParams& p, void* stream);
 template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
 int launch_fwd_f32(const FwdParams& p, void* stream);
-template <int D, bool SOFTCAP, bool ALIBI, bool SPLIT>
-int launch_fwd_fp8(const FwdParams& p, void* stream);  // head_dim 64 or 128
+template <int D, bool SOFTCAP, bool ALIBI, int MODE>
+int launch_fwd_fp8(const FwdParams& p, void* stream);  // head_dim 64 or 128; FWD_CONTIG,
+                                                       // FWD_CONTIG_SPLIT or FWD_PAGED_TILES
 template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream);
 template <int D, bool SOFTCAP, bool ALIBI>

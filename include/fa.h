@@ -308,6 +308,37 @@ int fa_fwd_splitkv_fp8(const void* q, const void* k_cache, const void* v_cache,
                        float softcap, void* stream);
 
 /*
+ * fa_fwd_paged_fp8 - the FP8 forward of fa_fwd_split_fp8 over a paged cache:
+ * E4M3 queries (any number of rows, e.g. a chunk of a prompt) against keys and
+ * values stored as E4M3 codes in pages (the FP8 forward support on the
+ * roadmap of "FlashAttention深度解析：从算法创新到产业变革的全面影响", with the
+ * update article's v2.2 split and v2.5 paged-cache entries).
+ *
+ *   q                  [batch, seqlen_q, heads, head_dim] E4M3 codes
+ *   k_cache, v_cache   [num_pages, page_size, heads, head_dim] E4M3 codes
+ *   q_descale, k_descale, v_descale  per-tensor factors as fa_fwd_fp8
+ *   block_table        device int32 [batch, max_pages_per_seq], as fa_fwd_splitkv
+ *   cache_seqlens      device int32 [batch] keys per sequence (clamped to
+ *                      seqlen_k), or NULL for seqlen_k keys everywhere
+ * page_size must be a multiple of 128 (the FP8 key tile: every tile then lies in
+ * one page; FA_ERR_UNSUPPORTED otherwise) and head_dim 64 or 128. Splits as
+ * fa_fwd_splitkv (chunks of whole pages, cut from each sequence's own key
+ * count); scores, masks, biases and the rounding of the probabilities as
+ * fa_fwd_split_fp8. Writes o_part [num_splits, batch, heads, seqlen_q, head_dim]
+ * fp32 (normalised, v_descale applied) and lse_part [num_splits, batch, heads,
+ * seqlen_q]; merge with fa_splitkv_combine. With equal key counts and
+ * 128-key pages the partials are fa_fwd_split_fp8's over the gathered keys.
+ * Errors as fa_fwd_splitkv and fa_fwd_fp8.
+ */
+int fa_fwd_paged_fp8(const void* q, const void* k_cache, const void* v_cache, float q_descale,
+                     float k_descale, float v_descale, const int* block_table,
+                     int max_pages_per_seq, int page_size, const int* cache_seqlens,
+                     float* o_part, float* lse_part, int num_splits, int batch, int heads,
+                     int seqlen_q, int seqlen_k, int head_dim, float softmax_scale, int causal,
+                     int window_left, int window_right, const float* alibi_slopes, float softcap,
+                     void* stream);
+
+/*
  * fa_bwd - backward pass of fa_fwd: dQ, dK, dV from dO, with the attention
  * probabilities recomputed from the forward's LSE (no Nq x Nk matrix is
  * stored; "IO感知技术革命: FlashAttention如何重塑大模型训练的经济学", tiling and

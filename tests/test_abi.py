@@ -421,6 +421,35 @@ def test_fa_fwd_split_fp8_rejects(kw, code):
     assert split8(**kw) == code
 
 
+def paged8(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, qd=1.0, kd=1.0, vd=1.0, bt=FAKE, maxp=8, page=128,
+             seqlens=None, op=FAKE, lp=FAKE, S=4, batch=1, heads=1, seqlen_q=300, seqlen_k=1000,
+             head_dim=128, scale=0.125, causal=1, wl=-1, wr=-1, alibi=None, softcap=0.0,
+             stream=None)
+    a.update(kw)
+    return fa.load_library().fa_fwd_paged_fp8(
+        a["q"], a["kc"], a["vc"], a["qd"], a["kd"], a["vd"], a["bt"], a["maxp"], a["page"],
+        a["seqlens"], a["op"], a["lp"], a["S"], a["batch"], a["heads"], a["seqlen_q"],
+        a["seqlen_k"], a["head_dim"], a["scale"], a["causal"], a["wl"], a["wr"], a["alibi"],
+        a["softcap"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(kc=None), NULL), (dict(vc=None), NULL), (dict(bt=None), NULL),
+    (dict(op=None), NULL), (dict(lp=None), NULL), (dict(batch=0), SHAPE),
+    (dict(seqlen_q=0), SHAPE), (dict(seqlen_k=0), SHAPE), (dict(S=0), SHAPE),
+    (dict(S=(1 << 16) + 1), SHAPE), (dict(maxp=0), SHAPE), (dict(page=0), SHAPE),
+    (dict(maxp=7), SHAPE),                                   # 7 pages of 128 < 1000 keys
+    (dict(page=1 << 20, heads=1 << 4), SHAPE),               # a page of >= 2^31 bytes
+    (dict(page=64, maxp=16), UNSUP), (dict(page=192, maxp=8), UNSUP),  # not whole 128-key tiles
+    (dict(head_dim=96), UNSUP), (dict(causal=1, wr=2), MASK), (dict(wl=-2), MASK),
+    (dict(qd=0.0), VALUE), (dict(kd=math.inf), VALUE), (dict(vd=math.nan), VALUE),
+    (dict(qd=1e30, kd=1e30), VALUE), (dict(scale=-1.0), VALUE), (dict(softcap=-1.0), VALUE),
+])
+def test_fa_fwd_paged_fp8_rejects(kw, code):
+    assert paged8(**kw) == code
+
+
 def test_fp8_split_chunks_are_multiples_of_the_fp8_key_tile():
     assert fa.fa_split_chunk_len(1000, 4, 128) == 256
     assert fa.fa_split_chunk_len(4096, 8, 128) == 512
@@ -487,6 +516,10 @@ def launches():
     (lambda **kw: fp8(**kw), dict()),
     (lambda **kw: split8(**kw), dict()),
     (lambda **kw: split8(**kw), dict(S=1 << 16, seqlen_k=1 << 28)),
+    (lambda **kw: paged8(**kw), dict()),
+    (lambda **kw: paged8(**kw), dict(page=384, maxp=3)),   # a page size that is no power of two
+    (lambda **kw: paged8(**kw), dict(seqlen_q=1, S=1 << 16, seqlen_k=1 << 28, page=128,
+                                     maxp=1 << 21)),
     (lambda **kw: bwd(**kw), dict()),
     (lambda **kw: bwd(**kw), dict(batch=1 << 10, heads=1 << 10, seqlen_q=1 << 11, seqlen_k=1)),
     (lambda **kw: bwd_noalloc(**kw), dict()),

@@ -942,16 +942,17 @@ FP8_SPLIT_CASES = [
 
 
 def check_fp8_partials(o_part, lse_part, q8, k8, v8, ds, scale, causal, wl, wr, slopes, cap, S,
-                       what):
+                       what, align=128):
     """Each split's partial against the oracle's split partial on the dequantised inputs,
-    within twice the E4M3 rounding bound over that split's own keys."""
+    within twice the E4M3 rounding bound over that split's own keys (chunks of whole
+    multiples of `align` keys)."""
     from gpu_common import e4m3_half_spacing
     qf = W.to_float(q8, "fp8") * ds[0]
     kf = W.to_float(k8, "fp8") * ds[1]
     vf = W.to_float(v8, "fp8") * ds[2]
     nk = k8.shape[1]
-    rop, rlp = O.splitkv_ref(qf, kf, vf, S, 128, scale, causal, wl, wr, slopes, cap)
-    for si, (lo, hi) in enumerate(O.split_bounds(nk, S, 128)):
+    rop, rlp = O.splitkv_ref(qf, kf, vf, S, align, scale, causal, wl, wr, slopes, cap)
+    for si, (lo, hi) in enumerate(O.split_bounds(nk, S, align)):
         bound = O.prob_weighted_abs_ref(qf, kf, vf, scale, causal, wl, wr, slopes, cap,
                                         weight=lambda pp: e4m3_half_spacing(256.0 * pp) / 256.0,
                                         key_lo=lo, key_hi=hi)
@@ -990,6 +991,85 @@ def test_fp8_split_partials_and_combined(case, d):
                        scale, causal, wl, wr, slopes, cap, S, f"fp8 split {case}")
     print(check_fp8(o.cpu().numpy(), lse.cpu().numpy(), q8, k8, v8, (qd, kd, vd), scale, causal,
                     wl, wr, slopes, cap, f"fp8 split combined {case}"))
+
+
+# fa_fwd_paged_fp8: E4M3 queries over a paged E4M3 cache (pages of a multiple of 128
+# keys). Each sequence's partials are checked against the oracle's split partials over
+# its gathered, dequantised keys, within the E4M3 rounding bound over each split's keys;
+# the pool's unused rows are NaN codes, so any read outside a sequence's keys shows.
+FP8_PAGED_CASES = [
+    # (B, H, nq, nk, page_size, S, seqlens or None, causal, wl, wr, alibi, cap, qd, kd, vd)
+    (2, 3, 300, 1000, 128, 3, None, True, -1, -1, False, 0.0, 1.0, 1.0, 1.0),
+    (3, 2, 129, 700, 256, 2, [700, 129, 1], False, 100, 30, True, 0.0, 0.5, 2.0, 1.5),
+    (3, 2, 200, 1500, 384, 4, [1500, 999, 200], True, -1, -1, True, 20.0, 1.0, 0.5, 2.0),
+    (2, 2, 64, 2000, 512, 5, [2000, 0], True, 300, 0, False, 10.0, 1.0, 1.0, 0.25),
+    (1, 4, 500, 4096, 256, 8, None, True, -1, -1, True, 30.0, 0.75, 1.25, 1.0),
+]
+
+
+def fp8_paged_case(case, seed, d):
+    B, H, nq, nk, ps, S, seqlens, causal, wl, wr, alibi, cap, qd, kd, vd = case
+    w = W.Workload(0, "fp8_paged", B=B, H=H, Nq=nq, Nk=nk, d=d, dtype="fp8", causal=causal,
+                   paged=True, page_size=ps, pool_factor=1.3, num_splits=S, seed=seed)
+    _, kc, vc, bt = W.gen_paged(w, seqlens=seqlens)
+    q8 = W.gen_tensor(seed, W.TENSOR_Q, B, nq, H, d, 1.0, "fp8")
+    slopes = W.alibi_slopes(H) if alibi else None
+    ts = None if slopes is None else torch.from_numpy(slopes).cuda()
+    tsl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32).cuda()
+    o_part, lse_part = fa.attention_paged_fp8(
+        to_dev_fp8(q8), to_dev_fp8(kc), to_dev_fp8(vc), torch.from_numpy(bt).cuda(), nk, S, qd,
+        kd, vd, 1.0 / np.sqrt(d), causal, wl, wr, ts, cap, cache_seqlens=tsl)
+    o, lse = fa.combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    return q8, kc, vc, bt, slopes, o_part.cpu().numpy(), lse_part.cpu().numpy(), \
+        o.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("case", FP8_PAGED_CASES)
+def test_fp8_paged_partials_and_combined(case, d):
+    B, H, nq, nk, ps, S, seqlens, causal, wl, wr, alibi, cap, qd, kd, vd = case
+    say(f"fp8 paged d{d} {case}")
+    seed = 9700 + FP8_PAGED_CASES.index(case) + 50 * (d == 64)
+    q8, kc, vc, bt, slopes, op, lp, o, lse = fp8_paged_case(case, seed, d)
+    assert not np.isnan(op).any() and not np.isnan(o).any(), "NaN: a poisoned pool row was read"
+    scale = 1.0 / np.sqrt(d)
+    for b in range(B):
+        n = nk if seqlens is None else seqlens[b]
+        if n == 0:  # no key: every split empty
+            assert np.all(op[:, b] == 0.0) and np.all(lp[:, b] == -np.inf)
+            assert np.all(o[b] == 0.0) and np.all(lse[b] == -np.inf)
+            continue
+        k8 = O.paged_gather_ref(kc, bt, b, n)[None]
+        v8 = O.paged_gather_ref(vc, bt, b, n)[None]
+        check_fp8_partials(op[:, b:b + 1], lp[:, b:b + 1], q8[b:b + 1], k8, v8, (qd, kd, vd),
+                           scale, causal, wl, wr, slopes, cap, S, f"fp8 paged b{b} {case}",
+                           align=ps)
+        print(check_fp8(o[b:b + 1], lse[b:b + 1], q8[b:b + 1], k8, v8, (qd, kd, vd), scale,
+                        causal, wl, wr, slopes, cap, f"fp8 paged combined b{b} {case}"))
+
+
+@pytest.mark.parametrize("d,ps,nk,S,alibi,cap", [(128, 128, 1000, 3, True, 30.0),
+                                                  (64, 256, 2048, 4, False, 0.0),
+                                                  (128, 512, 4096, 8, False, 20.0)])
+def test_fp8_paged_is_bitwise_fa_fwd_split_fp8(d, ps, nk, S, alibi, cap):
+    """With chunks that coincide (equal key counts; chunk lengths a multiple of the page
+    size either way) the paged pass reads the same 128-key tiles in the same order as
+    fa_fwd_split_fp8 over the gathered keys: partials bit for bit."""
+    say(f"fp8 paged == split d{d} page {ps} nk {nk} S{S}")
+    B, H, nq = 2, 3, 257
+    case = (B, H, nq, nk, ps, S, None, True, -1, -1, alibi, cap, 0.5, 1.5, 2.0)
+    seed = 9800 + d + ps
+    q8, kc, vc, bt, slopes, op, lp, _, _ = fp8_paged_case(case, seed, d)
+    assert O.split_bounds(nk, S, ps) == O.split_bounds(nk, S, 128)
+    k8 = np.stack([O.paged_gather_ref(kc, bt, b, nk) for b in range(B)])
+    v8 = np.stack([O.paged_gather_ref(vc, bt, b, nk) for b in range(B)])
+    ts = None if slopes is None else torch.from_numpy(slopes).cuda()
+    op2, lp2 = fa.attention_split_partials_fp8(to_dev_fp8(q8), to_dev_fp8(k8), to_dev_fp8(v8), S,
+                                               0.5, 1.5, 2.0, 1.0 / np.sqrt(d), True, -1, -1,
+                                               ts, cap)
+    torch.cuda.synchronize()
+    assert np.array_equal(op, op2.cpu().numpy()) and np.array_equal(lp, lp2.cpu().numpy())
 
 
 @pytest.mark.parametrize("d,alibi,cap", [(128, True, 30.0), (64, False, 0.0)])

@@ -8,8 +8,8 @@ are unchanged, so every output must agree bit for bit with libfa.so; a copy that
 overwrote a stage still being read, or a read of a stage not yet written, would show
 up as a difference. Covered: the contiguous forward (whole key range, batched and
 packed), its key splits, the paged multi-row pass with page-aligned tiles and with
-rows gathered one by one, and the FP8 forward (whole key range and key splits) at both
-head sizes.
+rows gathered one by one, and the FP8 forward (whole key range, key splits and page
+tiles of a paged cache) at both head sizes.
 """
 import ctypes
 import os
@@ -139,3 +139,20 @@ def test_fp8_split_matches_serial_copies(serial_lib, d):
     m, s = both(serial_lib, fa.attention_split_partials_fp8, q8, k8, v8, 5, 0.5, 1.0, 2.0,
                 1.0 / np.sqrt(d), True, -1, -1, ts, 20.0)
     assert_same(m, s, f"fa_fwd_split_fp8 d{d}")
+
+
+@pytest.mark.parametrize("d,page_size", [(128, 256), (64, 384)])
+def test_fp8_paged_matches_serial_copies(serial_lib, d, page_size):
+    say(f"hazard fa_fwd_paged_fp8 d{d} page {page_size}")
+    w = W.Workload(0, "hazard_fp8_paged", B=2, H=4, Nq=300, Nk=3000, d=d, dtype="fp8",
+                   causal=True, paged=True, page_size=page_size, pool_factor=1.2, num_splits=3,
+                   seed=7500 + d)
+    _, kc, vc, bt = W.gen_paged(w, seqlens=[3000, 1700])
+    q8 = torch.from_numpy(W.gen_tensor(7500 + d, W.TENSOR_Q, 2, 300, 4, d, 1.0, "fp8")).cuda()
+    tk, tv = torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda()
+    tbt = torch.from_numpy(bt).cuda()
+    tsl = torch.tensor([3000, 1700], dtype=torch.int32).cuda()
+    ts = torch.from_numpy(W.alibi_slopes(4)).cuda()
+    m, s = both(serial_lib, fa.attention_paged_fp8, q8, tk, tv, tbt, w.Nk, 3, 0.5, 1.0, 2.0,
+                1.0 / np.sqrt(d), True, -1, -1, ts, 20.0, cache_seqlens=tsl)
+    assert_same(m, s, f"fa_fwd_paged_fp8 d{d}")
