@@ -486,7 +486,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, int in_dtype, voi
 
 namespace {
 // The FP8 forward instantiation for head_dim, score transforms and mode
-// (fa::FWD_CONTIG, fa::FWD_CONTIG_SPLIT or fa::FWD_PAGED_TILES).
+// (fa::FWD_CONTIG, fa::FWD_CONTIG_SPLIT, fa::FWD_PAGED_TILES or fa::FWD_PAGED_SPLIT).
 int launch_fp8(const fa::FwdParams& p, int head_dim, bool sc, bool al, int mode, void* stream) {
 #define FA_FP8(D, M)                                              \
   (sc && al ? fa::launch_fwd_fp8<D, true, true, M>(p, stream)     \
@@ -496,7 +496,8 @@ int launch_fp8(const fa::FwdParams& p, int head_dim, bool sc, bool al, int mode,
 #define FA_FP8_D(D)                                                    \
   (mode == fa::FWD_CONTIG         ? FA_FP8(D, fa::FWD_CONTIG)          \
    : mode == fa::FWD_CONTIG_SPLIT ? FA_FP8(D, fa::FWD_CONTIG_SPLIT)    \
-                                  : FA_FP8(D, fa::FWD_PAGED_TILES))
+   : mode == fa::FWD_PAGED_TILES  ? FA_FP8(D, fa::FWD_PAGED_TILES)     \
+                                  : FA_FP8(D, fa::FWD_PAGED_SPLIT))
   const int rc = head_dim == 64 ? FA_FP8_D(64) : FA_FP8_D(128);
 #undef FA_FP8_D
 #undef FA_FP8
@@ -586,8 +587,6 @@ int fa_fwd_paged_fp8(const void* q, const void* k_cache, const void* v_cache, fl
   if ((int64_t)max_pages_per_seq * page_size < seqlen_k) return FA_ERR_SHAPE;
   if ((int64_t)page_size * heads * head_dim >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return FA_ERR_UNSUPPORTED;
-  // Every 128-key tile must lie inside one page.
-  if (page_size % fa::FP8_SPLIT_ALIGN != 0) return FA_ERR_UNSUPPORTED;
   if ((st = check_mask_and_values(causal, window_left, window_right, softmax_scale, softcap)))
     return st;
   for (float d : {q_descale, k_descale, v_descale})
@@ -618,8 +617,9 @@ int fa_fwd_paged_fp8(const void* q, const void* k_cache, const void* v_cache, fl
   if (split_len(seqlen_k, num_splits, page_size) > kMaxSeq) return FA_ERR_SHAPE;
   p.split_align = page_size;
   if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
-  return launch_fp8(p, head_dim, softcap > 0.0f, alibi_slopes != nullptr, fa::FWD_PAGED_TILES,
-                    stream);
+  // Pages of whole 128-key tiles travel tile by tile; other page sizes row by row.
+  const int mode = page_size % fa::FP8_SPLIT_ALIGN == 0 ? fa::FWD_PAGED_TILES : fa::FWD_PAGED_SPLIT;
+  return launch_fp8(p, head_dim, softcap > 0.0f, alibi_slopes != nullptr, mode, stream);
 }
 
 long long fa_bwd_workspace_bytes(int batch, int heads, int seqlen_q) {

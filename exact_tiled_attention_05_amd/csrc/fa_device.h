@@ -121,24 +121,44 @@ __device__ __forceinline__ void transform_scores(float (&t)[NB][16], const FwdPa
                                                  float slope_log2, float rel_pos,
                                                  bool need_mask, int key0, int row_lo,
                                                  int row_hi, int h2) {
-  if constexpr (SOFTCAP || ALIBI) {
+  if constexpr (SOFTCAP) {
+    // tanh(y) = 1 - 2 / (exp(2y) + 1), evaluated with exp2 and a reciprocal in
+    // three passes over the tile. Each pass holds NB * 16 independent operations,
+    // so no instruction waits for a transcendental issued just before it (taken
+    // score by score, the schedule keeps two scores in flight and stalls on every
+    // exponential and reciprocal). Same operations per score, same results.
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) t[j][v] = fast_exp2(t[j][v] * p.scale_over_cap2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) t[j][v] = __builtin_amdgcn_rcpf(t[j][v] + 1.0f);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float x = t[j][v];
-        if constexpr (SOFTCAP) {
-          // tanh(y) = 1 - 2 / (exp(2y) + 1), evaluated with exp2 and a reciprocal.
-          const float e = fast_exp2(x * p.scale_over_cap2);
-          x = p.softcap_log2 - 2.0f * p.softcap_log2 * __builtin_amdgcn_rcpf(e + 1.0f);
-        } else {
-          x *= p.scale_log2;
-        }
+        float x = p.softcap_log2 - 2.0f * p.softcap_log2 * t[j][v];
         if constexpr (ALIBI) {
           // rel_pos = (i + off) - (key0 + 4*h2): distance to the key = rel_pos - offset.
           const float dist = rel_pos - (float)(32 * j + 8 * (v >> 2) + (v & 3));
           x -= slope_log2 * __builtin_fabsf(dist);
         }
+        t[j][v] = x;
+      }
+    }
+  } else if constexpr (ALIBI) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        // rel_pos = (i + off) - (key0 + 4*h2): distance to the key = rel_pos - offset.
+        const float dist = rel_pos - (float)(32 * j + 8 * (v >> 2) + (v & 3));
+        float x = t[j][v] * p.scale_log2;
+        x -= slope_log2 * __builtin_fabsf(dist);
         t[j][v] = x;
       }
     }

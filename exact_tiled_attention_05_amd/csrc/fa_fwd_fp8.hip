@@ -31,7 +31,9 @@
 // applied to the FP8 forward). MODE FWD_PAGED_TILES: the same over a paged
 // cache (the article's paged KV entry) whose pages hold a multiple of 128 keys,
 // so every key tile lies inside one page with the row stride of a contiguous
-// tensor and travels from a per-tile base address.
+// tensor and travels from a per-tile base address. MODE FWD_PAGED_SPLIT: any
+// page size; each lane gathers its 16-byte pieces of key rows from their pages,
+// with the workgroup's page ids staged in LDS.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -91,9 +93,9 @@ template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Fp8Waves<D>::kWaves, Fp8Waves<D>::kWaves)))
 void fwd_fp8_kernel(FwdParams p) {
-  static_assert(MODE == FWD_CONTIG || MODE == FWD_CONTIG_SPLIT || MODE == FWD_PAGED_TILES, "mode");
-  constexpr bool SPLIT = MODE != FWD_CONTIG;       // one key split per workgroup, partial outputs
-  constexpr bool PTILES = MODE == FWD_PAGED_TILES; // K/V tiles from one page each
+  constexpr bool SPLIT = MODE != FWD_CONTIG;        // one key split per workgroup, partial outputs
+  constexpr bool PTILES = MODE == FWD_PAGED_TILES;  // K/V tiles from one page each
+  constexpr bool PGATHER = MODE == FWD_PAGED_SPLIT; // K/V rows gathered from their pages
   constexpr int kD = D;             // head_dim (bytes per K/V row of one head)
   constexpr int kTile = kBN * kD;   // bytes per K or V tile
   constexpr int kCPR = kD / 16;     // 16-byte chunks per row
@@ -105,6 +107,9 @@ void fwd_fp8_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK1[kTile];
   __shared__ __attribute__((aligned(1024))) uint8_t sV0[kTile];
   __shared__ __attribute__((aligned(1024))) uint8_t sV1[kTile];
+  // Page ids of the workgroup's keys (row gathers): 8 KB, which covers 2048 pages.
+  constexpr int kTablePages = PGATHER ? 2048 : 1;
+  __shared__ int s_pt[kTablePages];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
@@ -196,6 +201,46 @@ void fwd_fp8_kernel(FwdParams p) {
     const int idx = p.page_shift >= 0 ? kk >> p.page_shift : kk / p.page_size;
     return p.block_table[(int64_t)b * p.max_pages + idx + (lane >> 6)];
   };
+  // Row gathers (PGATHER): the page ids of keys [j_first, wg.hi) are staged in
+  // LDS when they fit, so a copy needs no dependent global load; lane L of copy
+  // i fetches physical chunk L % kCPR of tile row kRPL (kLoads w + i) + L / kCPR.
+  // Rows past the workgroup's keys re-read its last key (finite data, masked).
+  const int j_first = (wg.lo / kBN) * kBN;
+  int pt0 = 0;
+  bool pt_lds = false;
+  if constexpr (PGATHER) {
+    pt0 = p.page_shift >= 0 ? j_first >> p.page_shift : j_first / p.page_size;
+    const int pt1 = p.page_shift >= 0 ? (wg.hi - 1) >> p.page_shift : (wg.hi - 1) / p.page_size;
+    pt_lds = pt1 - pt0 < kTablePages;
+    if (pt_lds) {
+      const int* bt_row = p.block_table + (int64_t)b * p.max_pages;
+      for (int i = tid; i <= pt1 - pt0; i += kThreads) s_pt[i] = bt_row[pt0 + i];
+    }
+    __syncthreads();
+  }
+  auto copy_gather = [&](uint8_t* kd, uint8_t* vd, int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int ld = kLoads * wu + i;
+      const int trow = kRPL * ld + lane / kCPR;
+      const int key = min(j0 + trow, wg.hi - 1);
+      int idx, slot;
+      if (p.page_shift >= 0) {
+        idx = key >> p.page_shift;
+        slot = key & (p.page_size - 1);
+      } else {
+        idx = key / p.page_size;
+        slot = key - idx * p.page_size;
+      }
+      const int page = pt_lds ? s_pt[idx - pt0] : p.block_table[(int64_t)b * p.max_pages + idx];
+      const int64_t o = (((int64_t)page * p.page_size + slot) * p.H + h) * kD +
+                        16 * ((lane % kCPR) ^ swz_fp8<kD>(trow));
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)((const uint8_t*)p.k + o), (lds_ptr_t)(kd + 1024 * ld),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)((const uint8_t*)p.v + o), (lds_ptr_t)(vd + 1024 * ld),
+                                       16, 0, 0);
+    }
+  };
 
   f32x16_t oacc[NDB];
 #pragma unroll
@@ -282,7 +327,6 @@ void fwd_fp8_kernel(FwdParams p) {
   auto live = [&](int j0) __attribute__((always_inline)) {
     return wave_live && j0 < wk.hi && j0 + kBN > wk.lo;
   };
-  const int j_first = (wg.lo / kBN) * kBN;
   const int ntiles = (wg.hi - j_first + kBN - 1) / kBN;
 #ifdef FA_SERIAL_COPIES
   // Verification build: one buffer per tensor, each tile copied, waited for and
@@ -294,6 +338,8 @@ void fwd_fp8_kernel(FwdParams p) {
       const int pe = page_entry(j0);
       wait_vmem();
       copy_page_tiles(__builtin_amdgcn_readfirstlane(pe), sK0, sV0, j0);
+    } else if constexpr (PGATHER) {
+      copy_gather(sK0, sV0, j0);
     } else {
       copy_tiles(sK0, sV0, j0);
     }
@@ -316,6 +362,8 @@ void fwd_fp8_kernel(FwdParams p) {
     wait_vmem();
     copy_page_tiles(__builtin_amdgcn_readfirstlane(pe0), sK0, sV0, j_first);
     pg_next = page_entry(j_first + kBN);
+  } else if constexpr (PGATHER) {
+    copy_gather(sK0, sV0, j_first);
   } else {
     copy_tiles(sK0, sV0, j_first);
   }
@@ -329,6 +377,8 @@ void fwd_fp8_kernel(FwdParams p) {
                         j0 + kBN);
         if (it + 2 < ntiles) pg_next = page_entry(j0 + 2 * kBN);
       }
+    } else if constexpr (PGATHER) {
+      if (it + 1 < ntiles) copy_gather(ODD ? sK0 : sK1, ODD ? sV0 : sV1, j0 + kBN);
     } else {
       if (it + 1 < ntiles) copy_tiles(ODD ? sK0 : sK1, ODD ? sV0 : sV1, j0 + kBN);
     }
@@ -393,7 +443,8 @@ int launch_fwd_fp8(const FwdParams& p, void* stream) {
 #define FA_INST(D, SC, AL)                                                          \
   template int launch_fwd_fp8<D, SC, AL, FWD_CONTIG>(const FwdParams&, void*);       \
   template int launch_fwd_fp8<D, SC, AL, FWD_CONTIG_SPLIT>(const FwdParams&, void*); \
-  template int launch_fwd_fp8<D, SC, AL, FWD_PAGED_TILES>(const FwdParams&, void*);
+  template int launch_fwd_fp8<D, SC, AL, FWD_PAGED_TILES>(const FwdParams&, void*);    \
+  template int launch_fwd_fp8<D, SC, AL, FWD_PAGED_SPLIT>(const FwdParams&, void*);
 FA_INST(64, false, false)
 FA_INST(64, false, true)
 FA_INST(64, true, false)

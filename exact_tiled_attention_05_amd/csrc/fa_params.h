@@ -84,7 +84,8 @@ enum FwdMode {
   FWD_CONTIG = 0,        // contiguous K/V, whole key range -> O, LSE
   FWD_CONTIG_SPLIT = 1,  // contiguous K/V, one key split per workgroup -> o_part, lse_part
   FWD_PAGED_SPLIT = 2,   // paged K/V through the block table, per split -> o_part, lse_part
-                         //   (rows gathered one by one: any page size, appended keys)
+                         //   (rows gathered one by one: any page size, appended keys in
+                         //   the bf16 forward)
   FWD_PAGED_TILES = 3,   // the same with page_size a multiple of 64 and no append:
                          //   whole 64-key tiles from one page each (FP8 forward:
                          //   a multiple of 128, its key tile)
@@ -96,8 +97,7 @@ int launch_fwd_bf16(const FwdParams& p, void* stream);
 template <int D, bool SOFTCAP, bool ALIBI, bool PAGED>
 int launch_fwd_f32(const FwdParams& p, void* stream);
 template <int D, bool SOFTCAP, bool ALIBI, int MODE>
-int launch_fwd_fp8(const FwdParams& p, void* stream);  // head_dim 64 or 128; FWD_CONTIG,
-                                                       // FWD_CONTIG_SPLIT or FWD_PAGED_TILES
+int launch_fwd_fp8(const FwdParams& p, void* stream);  // head_dim 64 or 128; any mode
 template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream);
 template <int D, bool SOFTCAP, bool ALIBI>

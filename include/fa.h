@@ -320,15 +320,15 @@ int fa_fwd_splitkv_fp8(const void* q, const void* k_cache, const void* v_cache,
  *   block_table        device int32 [batch, max_pages_per_seq], as fa_fwd_splitkv
  *   cache_seqlens      device int32 [batch] keys per sequence (clamped to
  *                      seqlen_k), or NULL for seqlen_k keys everywhere
- * page_size must be a multiple of 128 (the FP8 key tile: every tile then lies in
- * one page; FA_ERR_UNSUPPORTED otherwise) and head_dim 64 or 128. Splits as
+ * Any page_size (pages of a multiple of 128 keys, the FP8 key tile, are copied
+ * tile by tile; others row by row); head_dim 64 or 128. Splits as
  * fa_fwd_splitkv (chunks of whole pages, cut from each sequence's own key
  * count); scores, masks, biases and the rounding of the probabilities as
  * fa_fwd_split_fp8. Writes o_part [num_splits, batch, heads, seqlen_q, head_dim]
  * fp32 (normalised, v_descale applied) and lse_part [num_splits, batch, heads,
- * seqlen_q]; merge with fa_splitkv_combine. With equal key counts and
- * 128-key pages the partials are fa_fwd_split_fp8's over the gathered keys.
- * Errors as fa_fwd_splitkv and fa_fwd_fp8.
+ * seqlen_q]; merge with fa_splitkv_combine. With equal key counts and split
+ * chunks of a multiple of 128 keys the partials are fa_fwd_split_fp8's over
+ * the gathered keys. Errors as fa_fwd_splitkv and fa_fwd_fp8.
  */
 int fa_fwd_paged_fp8(const void* q, const void* k_cache, const void* v_cache, float q_descale,
                      float k_descale, float v_descale, const int* block_table,

@@ -59,18 +59,19 @@ int launch_fwd_f32(const FwdParams& p, void*) {
 template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 int launch_fwd_fp8(const FwdParams& p, void*) {
   constexpr bool SPLIT = MODE != FWD_CONTIG;
-  require(MODE == FWD_CONTIG || MODE == FWD_CONTIG_SPLIT || MODE == FWD_PAGED_TILES, "fp8 mode");
+
   require(p.q && p.k && p.v && (SPLIT ? (p.o_part && p.lse_part) : p.o != nullptr),
           "fp8 forward pointers");
   require(MODE != FWD_CONTIG_SPLIT || (p.num_splits >= 1 && p.split_align == 128),
           "fp8 split chunking");
-  // Page tiles: every 128-key tile inside one page, chunks of whole pages.
-  require(MODE != FWD_PAGED_TILES ||
-              (p.block_table && p.page_size > 0 && p.page_size % 128 == 0 &&
-               p.split_align == p.page_size && p.max_pages > 0 &&
-               (int64_t)p.max_pages * p.page_size >= p.Nk &&
+  // Paged: chunks of whole pages, a table that covers every key; page tiles
+  // need every 128-key tile inside one page.
+  require(MODE < FWD_PAGED_SPLIT ||
+              (p.block_table && p.page_size > 0 && p.split_align == p.page_size &&
+               p.max_pages > 0 && (int64_t)p.max_pages * p.page_size >= p.Nk &&
                (p.page_shift < 0 || (1 << p.page_shift) == p.page_size)),
-          "fp8 page tiles");
+          "fp8 paged cache");
+  require(MODE != FWD_PAGED_TILES || p.page_size % 128 == 0, "fp8 page tiles");
   check_fwd(p, (int64_t)p.num_q_tiles * p.H * p.B * (SPLIT ? p.num_splits : 1));
   return 0;
 }
@@ -130,6 +131,7 @@ int noalloc_scratch(float** out) {
   template int launch_fwd_fp8<D, SC, AL, FWD_CONTIG>(const FwdParams&, void*);        \
   template int launch_fwd_fp8<D, SC, AL, FWD_CONTIG_SPLIT>(const FwdParams&, void*);  \
   template int launch_fwd_fp8<D, SC, AL, FWD_PAGED_TILES>(const FwdParams&, void*);   \
+  template int launch_fwd_fp8<D, SC, AL, FWD_PAGED_SPLIT>(const FwdParams&, void*);   \
   template int launch_bwd_bf16<D, SC, AL>(const BwdParams&, void*);
 STUB_D(64)
 STUB_D(128)

@@ -441,7 +441,6 @@ def paged8(**kw):
     (dict(S=(1 << 16) + 1), SHAPE), (dict(maxp=0), SHAPE), (dict(page=0), SHAPE),
     (dict(maxp=7), SHAPE),                                   # 7 pages of 128 < 1000 keys
     (dict(page=1 << 20, heads=1 << 4), SHAPE),               # a page of >= 2^31 bytes
-    (dict(page=64, maxp=16), UNSUP), (dict(page=192, maxp=8), UNSUP),  # not whole 128-key tiles
     (dict(head_dim=96), UNSUP), (dict(causal=1, wr=2), MASK), (dict(wl=-2), MASK),
     (dict(qd=0.0), VALUE), (dict(kd=math.inf), VALUE), (dict(vd=math.nan), VALUE),
     (dict(qd=1e30, kd=1e30), VALUE), (dict(scale=-1.0), VALUE), (dict(softcap=-1.0), VALUE),
@@ -518,6 +517,8 @@ def launches():
     (lambda **kw: split8(**kw), dict(S=1 << 16, seqlen_k=1 << 28)),
     (lambda **kw: paged8(**kw), dict()),
     (lambda **kw: paged8(**kw), dict(page=384, maxp=3)),   # a page size that is no power of two
+    (lambda **kw: paged8(**kw), dict(page=16, maxp=63)),   # rows gathered page by page
+    (lambda **kw: paged8(**kw), dict(page=7, maxp=143)),
     (lambda **kw: paged8(**kw), dict(seqlen_q=1, S=1 << 16, seqlen_k=1 << 28, page=128,
                                      maxp=1 << 21)),
     (lambda **kw: bwd(**kw), dict()),

@@ -994,7 +994,7 @@ def test_fp8_split_partials_and_combined(case, d):
 
 
 # fa_fwd_paged_fp8: E4M3 queries over a paged E4M3 cache (pages of a multiple of 128
-# keys). Each sequence's partials are checked against the oracle's split partials over
+# keys copied tile by tile, other page sizes row by row). Each sequence's partials are checked against the oracle's split partials over
 # its gathered, dequantised keys, within the E4M3 rounding bound over each split's keys;
 # the pool's unused rows are NaN codes, so any read outside a sequence's keys shows.
 FP8_PAGED_CASES = [
@@ -1004,6 +1004,11 @@ FP8_PAGED_CASES = [
     (3, 2, 200, 1500, 384, 4, [1500, 999, 200], True, -1, -1, True, 20.0, 1.0, 0.5, 2.0),
     (2, 2, 64, 2000, 512, 5, [2000, 0], True, 300, 0, False, 10.0, 1.0, 1.0, 0.25),
     (1, 4, 500, 4096, 256, 8, None, True, -1, -1, True, 30.0, 0.75, 1.25, 1.0),
+    # Row gathers: pages of 16, 64, 7 and 200 keys.
+    (2, 3, 300, 1000, 16, 4, [1000, 333], True, -1, -1, True, 0.0, 1.0, 1.0, 1.0),
+    (2, 2, 129, 900, 64, 3, None, False, 200, 50, False, 15.0, 0.5, 1.0, 2.0),
+    (3, 2, 100, 500, 7, 5, [500, 1, 0], True, 64, 0, True, 30.0, 1.0, 0.5, 1.0),
+    (1, 3, 256, 3000, 200, 6, None, True, -1, -1, False, 0.0, 1.0, 2.0, 0.5),
 ]
 
 
@@ -1051,11 +1056,14 @@ def test_fp8_paged_partials_and_combined(case, d):
 
 @pytest.mark.parametrize("d,ps,nk,S,alibi,cap", [(128, 128, 1000, 3, True, 30.0),
                                                   (64, 256, 2048, 4, False, 0.0),
-                                                  (128, 512, 4096, 8, False, 20.0)])
+                                                  (128, 512, 4096, 8, False, 20.0),
+                                                  (128, 64, 2048, 4, True, 0.0),    # gathers
+                                                  (64, 16, 1000, 1, False, 10.0)])  # gathers
 def test_fp8_paged_is_bitwise_fa_fwd_split_fp8(d, ps, nk, S, alibi, cap):
-    """With chunks that coincide (equal key counts; chunk lengths a multiple of the page
-    size either way) the paged pass reads the same 128-key tiles in the same order as
-    fa_fwd_split_fp8 over the gathered keys: partials bit for bit."""
+    """With chunks that coincide (equal key counts; chunk lengths a multiple of 128
+    either way) the paged pass reads the same 128-key tiles in the same order as
+    fa_fwd_split_fp8 over the gathered keys, whether its pages travel as tiles or row
+    by row: partials bit for bit."""
     say(f"fp8 paged == split d{d} page {ps} nk {nk} S{S}")
     B, H, nq = 2, 3, 257
     case = (B, H, nq, nk, ps, S, None, True, -1, -1, alibi, cap, 0.5, 1.5, 2.0)
