@@ -248,6 +248,48 @@ def test_splitkv_paged_small(case):
     check(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, dtype, "combined")
 
 
+def test_paged_gather_beyond_the_lds_page_table():
+    """Row gathers whose workgroup spans more pages than the kernel stages in LDS read the
+    block table directly: 64 bf16 rows over 30000 keys in 7-key pages (4286 pages; the
+    bf16 multi-row pass stages 4096 ids at head_dim 128) and 64 E4M3 rows over 16000 keys
+    (2286 pages; the FP8 pass stages 2048), one split each; the pools' unused rows are
+    NaN."""
+    d, H, nq, ps = 128, 2, 64, 7
+    scale = 1.0 / np.sqrt(d)
+    slopes = W.alibi_slopes(H)
+    ts = torch.from_numpy(slopes).cuda()
+    say("paged gather past the LDS page table: bf16, 30000 keys in 7-key pages")
+    nk = 30000
+    w = W.Workload(0, "gather_long", B=1, H=H, Nq=nq, Nk=nk, d=d, dtype="bf16", causal=True,
+                   paged=True, page_size=ps, pool_factor=1.2, num_splits=1, seed=4400)
+    q, kc, vc, bt = W.gen_paged(w)
+    assert w.pages_per_seq > 4096
+    o_part, lse_part = fa.attention_paged_splitkv(
+        to_dev(q, "bf16"), to_dev(kc, "bf16"), to_dev(vc, "bf16"), torch.from_numpy(bt).cuda(), nk,
+        1, scale, True, -1, -1, ts, 0.0)
+    torch.cuda.synchronize()
+    k = O.paged_gather_ref(W.to_float(kc, "bf16"), bt, 0, nk)[None]
+    v = O.paged_gather_ref(W.to_float(vc, "bf16"), bt, 0, nk)[None]
+    rop, rlp = O.splitkv_ref(W.to_float(q, "bf16"), k, v, 1, ps, scale, True, alibi_slopes=slopes)
+    check(o_part.cpu().numpy(), lse_part.cpu().numpy(), rop, rlp, "bf16", "bf16 partials")
+
+    say("paged gather past the LDS page table: E4M3, 16000 keys in 7-key pages")
+    nk = 16000
+    w = W.Workload(0, "gather_long_fp8", B=1, H=H, Nq=nq, Nk=nk, d=d, dtype="fp8", causal=True,
+                   paged=True, page_size=ps, pool_factor=1.2, num_splits=1, seed=4401)
+    _, kc, vc, bt = W.gen_paged(w)
+    assert w.pages_per_seq > 2048
+    q8 = W.gen_tensor(4401, W.TENSOR_Q, 1, nq, H, d, 1.0, "fp8")
+    o_part, lse_part = fa.attention_paged_fp8(to_dev_fp8(q8), to_dev_fp8(kc), to_dev_fp8(vc),
+                                              torch.from_numpy(bt).cuda(), nk, 1, 1.0, 1.0, 1.0,
+                                              scale, True, -1, -1, ts, 0.0)
+    torch.cuda.synchronize()
+    k8 = O.paged_gather_ref(kc, bt, 0, nk)[None]
+    v8 = O.paged_gather_ref(vc, bt, 0, nk)[None]
+    check_fp8_partials(o_part.cpu().numpy(), lse_part.cpu().numpy(), q8, k8, v8, (1.0, 1.0, 1.0),
+                       scale, True, -1, -1, slopes, 0.0, 1, "fp8 partials", align=ps)
+
+
 # --------------------------------------------------------------------------
 # Split-KV over contiguous K/V (fa_fwd_split): chunks of whole 64-key tiles
 # --------------------------------------------------------------------------
