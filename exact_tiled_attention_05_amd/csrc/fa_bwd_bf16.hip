@@ -819,11 +819,16 @@ void bwd_dq_kernel(BwdParams p) {
   constexpr int RPL = 64 / CPR;
   constexpr int LOADS = kBN / RPL / 4;
   constexpr int TILE = kBN * D;
+  // Operands of the score and dP products (K, then V) read this many MFMAs ahead.
+  constexpr int kDqReadAhead = 4;
 
-  __shared__ __attribute__((aligned(1024))) uint16_t sK0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sK1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV1[TILE];
+  // The four stages in one array: a K read and the V read of the same k-step
+  // differ by a constant, so they share an address register (immediate offset).
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
+  uint16_t* const sK0 = smem;
+  uint16_t* const sK1 = smem + TILE;
+  uint16_t* const sV0 = smem + 2 * TILE;
+  uint16_t* const sV1 = smem + 3 * TILE;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
@@ -902,24 +907,36 @@ void bwd_dq_kernel(BwdParams p) {
   const int gl = lane & 15, sub = (lane >> 4) & 1;
 
   auto compute = [&](const uint16_t* kt, const uint16_t* vt, int j0) __attribute__((always_inline)) {
-    // S^T = K Q^T and dP^T = V dO^T for 64 keys x this wavefront's 32 rows.
+    // S^T = K Q^T and dP^T = V dO^T for 64 keys x this wavefront's 32 rows:
+    // MFMA i (k-step (i / 2) % KS, 32-key block i % 2) takes K for i < 2 KS and
+    // V after. Each operand is read kDqReadAhead MFMAs ahead, in source order as
+    // well, since under this register pressure the scheduler keeps source order.
+    constexpr int NOP = 4 * KS;
     f32x16_t sacc[2], pacc[2];
+    auto sp_operand = [&](int i) __attribute__((always_inline)) {
+      const uint16_t* t = i < 2 * KS ? kt : vt;
+      return *(const u32x4_t*)(t + tile_off<D>(32 * (i & 1) + r, 2 * ((i >> 1) % KS) + h2));
+    };
+    u32x4_t ring[kDqReadAhead];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int i = 0; i < kDqReadAhead; ++i) ring[i] = sp_operand(i);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kt + tile_off<D>(32 * j + r, 2 * ks + h2)));
+    for (int i = 0; i < NOP; ++i) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ring[i % kDqReadAhead]);
+      if (i + kDqReadAhead < NOP) ring[i % kDqReadAhead] = sp_operand(i + kDqReadAhead);
+      const int ks = (i >> 1) % KS, j = i & 1;
+      if (i < 2 * KS)
         sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? f32x16_t{} : sacc[j], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(vt + tile_off<D>(32 * j + r, 2 * ks + h2)));
+      else
         pacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gf[ks], ks == 0 ? f32x16_t{} : pacc[j], 0, 0, 0);
-      }
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, kDqReadAhead, 4);  // DS reads
+#pragma unroll
+    for (int i = 0; i < NOP - kDqReadAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 4);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 4);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kDqReadAhead, 4);
     // Slot v of block j holds key j0 + 32j + 8*(v/4) + 4*h2 + v%4 of this lane's row.
     const bool masked = __builtin_amdgcn_readfirstlane(!(j0 >= wk.flo && j0 + kBN <= wk.fhi));
     const int lo_rel = rk.lo - j0 - 4 * h2, hi_rel = rk.hi - j0 - 4 * h2;
