@@ -132,10 +132,12 @@ void fwd_bf16_kernel(FwdParams p) {
   const int j_first = (wg.lo / kBN) * kBN;
   const int ntiles = (wg.hi - j_first + kBN - 1) / kBN;
 
-  // Paged K/V. With pages of a multiple of the 64-key tile and no appended key
-  // (PTILES) every tile lies inside one page with the row stride of a
-  // contiguous tensor, so tiles travel as in the contiguous path from a
-  // per-tile base address. Otherwise (PAGED) rows are gathered one by one,
+  // Paged K/V. Each wavefront copies a slab of kSlab consecutive rows of every
+  // tile; with pages of a multiple of kSlab keys and no appended key (PTILES)
+  // every slab lies inside one page with the row stride of a contiguous tensor,
+  // so it travels as in the contiguous path from a per-wavefront base address
+  // (pages of a multiple of the 64-key tile give every wavefront of a tile the
+  // same page). Otherwise (PAGED) rows are gathered one by one,
   // with the page ids of the workgroup's keys [j_first, wg.hi) staged in LDS
   // (in the third K buffer, which that path does not use) so that a copy needs
   // no dependent block-table load.
@@ -204,20 +206,28 @@ void fwd_bf16_kernel(FwdParams p) {
     const int64_t tb = (int64_t)j0 * row_bytes;
     copy_rows(bh + tb, end_bytes - tb, dst);
   };
-  // Tile j0 of a page-aligned pool (PTILES) from page `page`; rows past the
-  // sequence's last key read as zeros.
+  // This wavefront's slab of tile j0 (rows kSlab wu .. +kSlab-1) from page
+  // `page` of a pool whose pages hold a multiple of kSlab keys (PTILES). The
+  // descriptor is based kSlab wu rows before the slab, so the per-lane offsets
+  // of the contiguous path apply unchanged; only the slab's rows are read, and
+  // rows past the sequence's last key read as zeros.
+  constexpr int kSlab = ROWS_PER_LOAD * LOADS;
+  static_assert(kSlab == 16, "slab rows");
   auto copy_page_tile = [&](const void* pool, int page, uint16_t* dst, int j0) __attribute__((always_inline)) {
-    const int slot0 = p.page_shift >= 0 ? j0 & (p.page_size - 1) : j0 % p.page_size;
-    const char* base = (const char*)pool + 2 * ((((int64_t)page * p.page_size + slot0) * p.H + h) * D);
+    const int js = j0 + kSlab * wu;
+    const int slot = p.page_shift >= 0 ? js & (p.page_size - 1) : js % p.page_size;
+    const char* base = (const char*)pool + 2 * ((((int64_t)page * p.page_size + slot) * p.H + h) * D) -
+                       (int64_t)kSlab * wu * row_bytes;
     copy_rows(base, (int64_t)(nk - 1 - j0) * row_bytes + 2 * D, dst);
   };
-  // Page of tile j0 (tiles past the key range, which read nothing, take the
-  // range's last page so the index stays in the table). The id is read with a
-  // vector load (the address is written per lane: lane >> 6 is 0) and made
-  // uniform afterwards: a scalar load would be waited for with the counter
-  // that also tracks LDS reads, stalling the products' operand reads.
+  // Page of this wavefront's slab of tile j0 (slabs past the key range, which
+  // read nothing, take the range's last page so the index stays in the table).
+  // The id is read with a vector load (the address is written per lane:
+  // lane >> 6 is 0) and made uniform afterwards: a scalar load would be waited
+  // for with the counter that also tracks LDS reads, stalling the products'
+  // operand reads.
   auto page_of = [&](int j0) __attribute__((always_inline)) {
-    const int kk = min(j0, wg.hi - 1);
+    const int kk = min(j0 + kSlab * wu, wg.hi - 1);
     const int idx = p.page_shift >= 0 ? kk >> p.page_shift : kk / p.page_size;
     return __builtin_amdgcn_readfirstlane(p.block_table[(int64_t)b * p.max_pages + idx + (lane >> 6)]);
   };

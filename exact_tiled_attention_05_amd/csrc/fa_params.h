@@ -86,9 +86,9 @@ enum FwdMode {
   FWD_PAGED_SPLIT = 2,   // paged K/V through the block table, per split -> o_part, lse_part
                          //   (rows gathered one by one: any page size, appended keys in
                          //   the bf16 forward)
-  FWD_PAGED_TILES = 3,   // the same with page_size a multiple of 64 and no append:
-                         //   whole 64-key tiles from one page each (FP8 forward:
-                         //   a multiple of 128, its key tile)
+  FWD_PAGED_TILES = 3,   // the same with page_size a multiple of 16 and no append:
+                         //   each wavefront's 16-row slab of a 64-key tile from one
+                         //   page (FP8 forward: a multiple of 128, its key tile)
 };
 
 // Launchers (defined in the .hip files). Return hipError_t as int.

@@ -47,6 +47,8 @@ int launch_fwd_bf16(const FwdParams& p, void*) {
   require(p.q && (p.k || p.total_k == 0) && (p.v || p.total_k == 0), "forward inputs");
   require(MODE == FWD_CONTIG ? p.o != nullptr : (p.o_part && p.lse_part), "forward outputs");
   require(MODE < FWD_PAGED_SPLIT || p.block_table, "block table");
+  // Page tiles: every wavefront's 16-row slab of a 64-key tile inside one page.
+  require(MODE != FWD_PAGED_TILES || (p.page_size % 16 == 0 && !p.k_new), "bf16 page tiles");
   check_fwd(p, (int64_t)p.num_q_tiles * p.H * p.B * splits);
   return 0;
 }

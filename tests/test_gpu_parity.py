@@ -1799,16 +1799,21 @@ def test_num_splits_from_the_device():
     assert torch.equal(op_auto, op) and torch.equal(lp_auto, lp)
 
 
-@pytest.mark.parametrize("d,alibi,cap", [(128, False, 0.0), (64, True, 0.0), (128, True, 20.0)])
-def test_paged_tiles_bitwise_equal_contiguous_split(d, alibi, cap):
-    """With 64-key pages a paged cache cuts the same split chunks as fa_fwd_split,
-    and every 64-key tile comes whole from one page: the multi-row paged pass
-    runs the contiguous loop on per-tile addresses, so the partials are equal
-    bit for bit to those over the same keys stored contiguously."""
-    B, H, nq, nk, S = 2, 3, 200, 1000, 3
-    say(f"paged tiles vs contiguous d{d} alibi{alibi} cap{cap}")
+@pytest.mark.parametrize("d,alibi,cap,ps,nk", [(128, False, 0.0, 64, 1000), (64, True, 0.0, 64, 1000),
+                                               (128, True, 20.0, 64, 1000),
+                                               (128, False, 0.0, 16, 1152), (64, True, 0.0, 48, 1152),
+                                               (128, True, 20.0, 32, 1152)])
+def test_paged_tiles_bitwise_equal_contiguous_split(d, alibi, cap, ps, nk):
+    """With pages of a multiple of 16 keys every wavefront's 16-row slab of a 64-key
+    tile comes from one page, and with these key counts the paged split chunks are
+    fa_fwd_split's: the multi-row paged pass runs the contiguous loop on
+    per-wavefront addresses, so the partials are equal bit for bit to those over
+    the same keys stored contiguously."""
+    B, H, nq, S = 2, 3, 200, 3
+    say(f"paged tiles vs contiguous d{d} alibi{alibi} cap{cap} page {ps}")
+    assert O.split_bounds(nk, S, ps) == O.split_bounds(nk, S, 64)
     w = W.Workload(0, "ptiles", B=B, H=H, Nq=nq, Nk=nk, d=d, dtype="bf16", causal=True,
-                   paged=True, page_size=64, pool_factor=1.4, num_splits=S, seed=14200 + d)
+                   paged=True, page_size=ps, pool_factor=1.4, num_splits=S, seed=14200 + d + ps)
     q, kc, vc, bt = W.gen_paged(w)
     slopes = W.alibi_slopes(H) if alibi else None
     ts = None if slopes is None else torch.from_numpy(slopes).cuda()

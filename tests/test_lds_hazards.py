@@ -7,8 +7,8 @@ barriers on both sides, so no copy overlaps any compute. The arithmetic and its 
 are unchanged, so every output must agree bit for bit with libfa.so; a copy that
 overwrote a stage still being read, or a read of a stage not yet written, would show
 up as a difference. Covered: the contiguous forward (whole key range, batched and
-packed), its key splits, the paged multi-row pass with page-aligned tiles and with
-rows gathered one by one, and the FP8 forward (whole key range, key splits, and a paged
+packed), its key splits, the paged multi-row pass with page-aligned tiles, with
+per-wavefront slabs of 16-key pages and with rows gathered one by one, and the FP8 forward (whole key range, key splits, and a paged
 cache in page tiles and in row gathers) at both head sizes.
 """
 import ctypes
@@ -103,7 +103,7 @@ def test_key_splits_match_serial_copies(serial_lib, d, splits, alibi, cap):
     assert_same(m, s, f"fa_fwd_split d{d}")
 
 
-@pytest.mark.parametrize("page_size", [256, 16])  # page tiles; rows gathered one by one
+@pytest.mark.parametrize("page_size", [256, 16, 7])  # page tiles, 16-row slabs, row gathers
 def test_paged_multirow_matches_serial_copies(serial_lib, page_size):
     say(f"hazard fa_fwd_splitkv multi-row, page {page_size}")
     w = W.Workload(0, "hazard_paged", B=2, H=4, Nq=300, Nk=3000, d=128, dtype="bf16",
