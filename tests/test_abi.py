@@ -456,14 +456,17 @@ def test_fp8_split_chunks_are_multiples_of_the_fp8_key_tile():
 
 
 def test_num_splits_heuristic():
-    # One query row: at least one workgroup per compute unit (256 here), head
-    # groups of 256-byte segments, at most one split per page and 64 splits.
+    # One query row: at least two workgroups per compute unit (256 here), head
+    # groups of 256-byte segments (512 at head_dim 128: the wide groups), at most
+    # one split per page and 64 splits.
     ns = fa.fa_num_splits
-    assert ns(1, 32, 1, 4096, 128, 256, num_cus=256) == 8
-    assert ns(4, 32, 1, 8192, 128, 256, num_cus=256) == 2
-    assert ns(1, 8, 1, 16384, 128, 256, num_cus=256) == 32
-    assert ns(16, 32, 1, 2048, 128, 256, num_cus=256) == 1
-    assert ns(1, 32, 1, 4096, 128, 256, fp8_cache=True, num_cus=256) == 16  # 2 heads per group
+    assert ns(1, 32, 1, 4096, 128, 256, num_cus=256) == 16
+    assert ns(4, 32, 1, 8192, 128, 256, num_cus=256) == 8
+    assert ns(1, 8, 1, 16384, 128, 256, num_cus=256) == 64
+    assert ns(16, 32, 1, 2048, 128, 256, num_cus=256) == 2
+    assert ns(64, 32, 1, 2048, 128, 256, num_cus=256) == 1
+    assert ns(8, 32, 1, 32768, 128, 256, fp8_cache=True, num_cus=256) == 8  # 4 heads per group
+    assert ns(1, 32, 1, 4096, 128, 256, fp8_cache=True, num_cus=256) == 16  # capped: 16 pages
     assert ns(1, 32, 1, 4096, 64, 256, fp8_cache=True, num_cus=256) == 16   # capped: 16 pages
     assert ns(1, 1, 1, 300, 128, 256, num_cus=256) == 2                      # 2 pages
     assert ns(1, 1, 1, 1 << 20, 128, 16, num_cus=256) == 64                  # at most 64
