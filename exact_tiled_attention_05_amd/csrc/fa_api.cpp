@@ -620,8 +620,9 @@ int fa_fwd_paged_fp8(const void* q, const void* k_cache, const void* v_cache, fl
   if (split_len(seqlen_k, num_splits, page_size) > kMaxSeq) return FA_ERR_SHAPE;
   p.split_align = page_size;
   if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
-  // Pages of whole 128-key tiles travel tile by tile; other page sizes row by row.
-  const int mode = page_size % fa::FP8_SPLIT_ALIGN == 0 ? fa::FWD_PAGED_TILES : fa::FWD_PAGED_SPLIT;
+  // Pages of a multiple of 32 keys travel as per-wavefront slabs of the 128-key
+  // tiles; other page sizes row by row.
+  const int mode = page_size % 32 == 0 ? fa::FWD_PAGED_TILES : fa::FWD_PAGED_SPLIT;
   return launch_fp8(p, head_dim, softcap > 0.0f, alibi_slopes != nullptr, mode, stream);
 }
 

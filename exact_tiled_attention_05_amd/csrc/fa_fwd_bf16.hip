@@ -15,7 +15,9 @@
 // whose range check turns keys past the end into zero rows; K sits in a
 // three-stage ring and V in two buffers, so step t copies V(t+1) as it starts
 // and K(t+2) after its score MFMAs (spreading the copies of a step over time)
-// and ends with K(t+2) still in flight. Paged K/V gather rows through the
+// and ends with K(t+2) still in flight. Paged K/V whose pages hold a multiple
+// of 16 keys run the same loop, each wavefront's 16-row slab of a tile taken
+// from its page; other page sizes and appended keys gather rows through the
 // block table with global loads into two buffers each. Inside a tile the LDS
 // reads run several MFMAs ahead of their use (pinned with scheduling groups).
 // Tiles inside every row's key range take a path with no per-element mask.
@@ -49,14 +51,14 @@ struct Tuning {
 
 // MODE: FWD_CONTIG (contiguous K/V -> O, LSE), FWD_CONTIG_SPLIT (contiguous K/V,
 // one key split per workgroup -> normalised partials), FWD_PAGED_TILES (paged
-// K/V in pages of a multiple of 64 keys -> partials) or FWD_PAGED_SPLIT (paged
+// K/V in pages of a multiple of 16 keys -> partials) or FWD_PAGED_SPLIT (paged
 // K/V through the block table -> partials).
 template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Tuning<D, SOFTCAP>::kWaves, Tuning<D, SOFTCAP>::kWaves)))
 void fwd_bf16_kernel(FwdParams p) {
   constexpr bool PAGED = MODE == FWD_PAGED_SPLIT;  // K/V rows gathered through the block table
-  constexpr bool PTILES = MODE == FWD_PAGED_TILES; // K/V tiles from one page each
+  constexpr bool PTILES = MODE == FWD_PAGED_TILES; // each wavefront's slab of a tile from one page
   constexpr bool SPLIT = MODE != FWD_CONTIG;       // one key split per workgroup, partial outputs
   constexpr int KS = D / 16;                 // MFMA k-steps of Q K^T
   constexpr int NDB = D / 32;                // 32-row blocks of O^T

@@ -29,9 +29,10 @@
 // bound the key range like a window, and the epilogue writes normalised
 // partials for the combine kernel (the update article's split-KV entries,
 // applied to the FP8 forward). MODE FWD_PAGED_TILES: the same over a paged
-// cache (the article's paged KV entry) whose pages hold a multiple of 128 keys,
-// so every key tile lies inside one page with the row stride of a contiguous
-// tensor and travels from a per-tile base address. MODE FWD_PAGED_SPLIT: any
+// cache (the article's paged KV entry) whose pages hold a multiple of 32 keys:
+// each wavefront copies a slab of 32 consecutive rows of every 128-key tile,
+// which then lies inside one page with the row stride of a contiguous tensor
+// and travels from a per-wavefront base address. MODE FWD_PAGED_SPLIT: any
 // page size; each lane gathers its 16-byte pieces of key rows from their pages,
 // with the workgroup's page ids staged in LDS.
 #include <hip/hip_runtime.h>
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Fp8Waves<D>::kWaves, Fp8Waves<D>::kWaves)))
 void fwd_fp8_kernel(FwdParams p) {
   constexpr bool SPLIT = MODE != FWD_CONTIG;        // one key split per workgroup, partial outputs
-  constexpr bool PTILES = MODE == FWD_PAGED_TILES;  // K/V tiles from one page each
+  constexpr bool PTILES = MODE == FWD_PAGED_TILES;  // each wavefront's slab of a tile from one page
   constexpr bool PGATHER = MODE == FWD_PAGED_SPLIT; // K/V rows gathered from their pages
   constexpr int kD = D;             // head_dim (bytes per K/V row of one head)
   constexpr int kTile = kBN * kD;   // bytes per K or V tile
@@ -183,21 +184,26 @@ void fwd_fp8_kernel(FwdParams p) {
     const int64_t tb = (int64_t)j0 * row_bytes;
     copy_at(kbh + tb, vbh + tb, end_bytes - tb, kd, vd);
   };
-  // Paged cache (PTILES): the tile of key j0 from page `page` (its slot j0 mod
-  // page_size is a multiple of the tile); rows past the sequence's last key
-  // read as zeros.
+  // Paged cache (PTILES): this wavefront's slab of tile j0 (rows kSlab wu ..
+  // +kSlab-1) from page `page`, whose slot for the slab is a multiple of kSlab.
+  // The descriptors are based kSlab wu rows before the slab, so the per-lane
+  // offsets of the contiguous path apply unchanged; only the slab's rows are
+  // read, and rows past the sequence's last key read as zeros.
+  constexpr int kSlab = kRPL * kLoads;
+  static_assert(kSlab == 32, "slab rows");
   auto copy_page_tiles = [&](int page, uint8_t* kd, uint8_t* vd, int j0) __attribute__((always_inline)) {
-    const int slot0 = p.page_shift >= 0 ? j0 & (p.page_size - 1) : j0 % p.page_size;
-    const int64_t pb = (((int64_t)page * p.page_size + slot0) * p.H + h) * kD;
+    const int js = j0 + kSlab * wu;
+    const int slot = p.page_shift >= 0 ? js & (p.page_size - 1) : js % p.page_size;
+    const int64_t pb = (((int64_t)page * p.page_size + slot) * p.H + h) * kD - (int64_t)kSlab * wu * row_bytes;
     copy_at((const char*)p.k + pb, (const char*)p.v + pb, (int64_t)(nk - 1 - j0) * row_bytes + kD,
             kd, vd);
   };
-  // Block-table entry of the tile of key j0 (clamped into the workgroup's keys,
-  // so the index stays in the table), read by a vector load: the caller makes it
-  // uniform once the load has been waited for, so the load never stalls the
-  // copies issued beside it.
+  // Block-table entry of this wavefront's slab of tile j0 (clamped into the
+  // workgroup's keys, so the index stays in the table), read by a vector load:
+  // the caller makes it uniform once the load has been waited for, so the load
+  // never stalls the copies issued beside it.
   auto page_entry = [&](int j0) __attribute__((always_inline)) {
-    const int kk = min(j0, wg.hi - 1);
+    const int kk = min(j0 + kSlab * wu, wg.hi - 1);
     const int idx = p.page_shift >= 0 ? kk >> p.page_shift : kk / p.page_size;
     return p.block_table[(int64_t)b * p.max_pages + idx + (lane >> 6)];
   };

@@ -320,8 +320,8 @@ int fa_fwd_splitkv_fp8(const void* q, const void* k_cache, const void* v_cache,
  *   block_table        device int32 [batch, max_pages_per_seq], as fa_fwd_splitkv
  *   cache_seqlens      device int32 [batch] keys per sequence (clamped to
  *                      seqlen_k), or NULL for seqlen_k keys everywhere
- * Any page_size (pages of a multiple of 128 keys, the FP8 key tile, are copied
- * tile by tile; others row by row); head_dim 64 or 128. Splits as
+ * Any page_size (pages of a multiple of 32 keys are copied in slabs of the
+ * 128-key tile; others row by row); head_dim 64 or 128. Splits as
  * fa_fwd_splitkv (chunks of whole pages, cut from each sequence's own key
  * count); scores, masks, biases and the rounding of the probabilities as
  * fa_fwd_split_fp8. Writes o_part [num_splits, batch, heads, seqlen_q, head_dim]

@@ -67,13 +67,13 @@ int launch_fwd_fp8(const FwdParams& p, void*) {
   require(MODE != FWD_CONTIG_SPLIT || (p.num_splits >= 1 && p.split_align == 128),
           "fp8 split chunking");
   // Paged: chunks of whole pages, a table that covers every key; page tiles
-  // need every 128-key tile inside one page.
+  // need every wavefront's 32-row slab of a 128-key tile inside one page.
   require(MODE < FWD_PAGED_SPLIT ||
               (p.block_table && p.page_size > 0 && p.split_align == p.page_size &&
                p.max_pages > 0 && (int64_t)p.max_pages * p.page_size >= p.Nk &&
                (p.page_shift < 0 || (1 << p.page_shift) == p.page_size)),
           "fp8 paged cache");
-  require(MODE != FWD_PAGED_TILES || p.page_size % 128 == 0, "fp8 page tiles");
+  require(MODE != FWD_PAGED_TILES || p.page_size % 32 == 0, "fp8 page tiles");
   check_fwd(p, (int64_t)p.num_q_tiles * p.H * p.B * (SPLIT ? p.num_splits : 1));
   return 0;
 }

@@ -1035,8 +1035,8 @@ def test_fp8_split_partials_and_combined(case, d):
                     wl, wr, slopes, cap, f"fp8 split combined {case}"))
 
 
-# fa_fwd_paged_fp8: E4M3 queries over a paged E4M3 cache (pages of a multiple of 128
-# keys copied tile by tile, other page sizes row by row). Each sequence's partials are checked against the oracle's split partials over
+# fa_fwd_paged_fp8: E4M3 queries over a paged E4M3 cache (pages of a multiple of 32
+# keys copied in per-wavefront slabs of the 128-key tiles, other page sizes row by row). Each sequence's partials are checked against the oracle's split partials over
 # its gathered, dequantised keys, within the E4M3 rounding bound over each split's keys;
 # the pool's unused rows are NaN codes, so any read outside a sequence's keys shows.
 FP8_PAGED_CASES = [
@@ -1099,8 +1099,10 @@ def test_fp8_paged_partials_and_combined(case, d):
 @pytest.mark.parametrize("d,ps,nk,S,alibi,cap", [(128, 128, 1000, 3, True, 30.0),
                                                   (64, 256, 2048, 4, False, 0.0),
                                                   (128, 512, 4096, 8, False, 20.0),
-                                                  (128, 64, 2048, 4, True, 0.0),    # gathers
-                                                  (64, 16, 1000, 1, False, 10.0)])  # gathers
+                                                  (128, 64, 2048, 4, True, 0.0),    # slabs
+                                                  (64, 32, 2048, 4, False, 0.0),    # slabs
+                                                  (64, 16, 1000, 1, False, 10.0),   # gathers
+                                                  (128, 48, 1152, 3, True, 20.0)])  # gathers
 def test_fp8_paged_is_bitwise_fa_fwd_split_fp8(d, ps, nk, S, alibi, cap):
     """With chunks that coincide (equal key counts; chunk lengths a multiple of 128
     either way) the paged pass reads the same 128-key tiles in the same order as

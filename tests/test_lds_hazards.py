@@ -9,7 +9,7 @@ overwrote a stage still being read, or a read of a stage not yet written, would 
 up as a difference. Covered: the contiguous forward (whole key range, batched and
 packed), its key splits, the paged multi-row pass with page-aligned tiles, with
 per-wavefront slabs of 16-key pages and with rows gathered one by one, and the FP8 forward (whole key range, key splits, and a paged
-cache in page tiles and in row gathers) at both head sizes.
+cache in whole tiles, in per-wavefront slabs and in row gathers) at both head sizes.
 """
 import ctypes
 import os
@@ -141,7 +141,7 @@ def test_fp8_split_matches_serial_copies(serial_lib, d):
     assert_same(m, s, f"fa_fwd_split_fp8 d{d}")
 
 
-@pytest.mark.parametrize("d,page_size", [(128, 256), (64, 384), (128, 16), (64, 100)])
+@pytest.mark.parametrize("d,page_size", [(128, 256), (64, 384), (128, 64), (128, 16), (64, 100)])
 def test_fp8_paged_matches_serial_copies(serial_lib, d, page_size):
     say(f"hazard fa_fwd_paged_fp8 d{d} page {page_size}")
     w = W.Workload(0, "hazard_fp8_paged", B=2, H=4, Nq=300, Nk=3000, d=d, dtype="fp8",
