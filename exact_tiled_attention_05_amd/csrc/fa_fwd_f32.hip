@@ -85,24 +85,33 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
   const int j_first = (wk.lo / kBN) * kBN;
   for (int j0 = j_first + w * kBN; j0 < wk.hi; j0 += kWaves * kBN) {
     wave_lds_sync();  // the previous tile's reads came first
-    for (int idx = lane; idx < kBN * D / 4; idx += 64) {
+    // The tile's K and V, 16 bytes per lane per load: every load is issued
+    // before any is stored (a rolled loop waited for each load in turn). Keys
+    // past the end load the last key (in range) and are stored as zeros.
+    constexpr int kLoadsPerLane = kBN * D / 4 / 64;
+    f32x4_t kx[kLoadsPerLane], vx[kLoadsPerLane];
+#pragma unroll
+    for (int it = 0; it < kLoadsPerLane; ++it) {
+      const int idx = lane + 64 * it;
+      const int key = min(j0 + idx / (D / 4), nk - 1);
+      // Appended keys (paged launches with k_new) come from k_new / v_new.
+      const bool fresh = PAGED && key >= si.n_cached;
+      const int64_t o = (fresh ? new_key_offset(p, si, b, key, h, D)
+                               : kv_offset<PAGED>(p, b, si, key, h, D)) + 4 * (idx % (D / 4));
+      kx[it] = *(const f32x4_t*)((const float*)(fresh ? p.k_new : p.k) + o);
+      vx[it] = *(const f32x4_t*)((const float*)(fresh ? p.v_new : p.v) + o);
+    }
+#pragma unroll
+    for (int it = 0; it < kLoadsPerLane; ++it) {
+      const int idx = lane + 64 * it;
       const int kk = idx / (D / 4), c4 = idx % (D / 4);
-      const int key = j0 + kk;
-      f32x4_t kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-      if (key < nk) {
-        // Appended keys (paged launches with k_new) come from k_new / v_new.
-        const bool fresh = PAGED && key >= si.n_cached;
-        const int64_t o = (fresh ? new_key_offset(p, si, b, key, h, D)
-                                 : kv_offset<PAGED>(p, b, si, key, h, D)) + 4 * c4;
-        kx = *(const f32x4_t*)((const float*)(fresh ? p.k_new : p.k) + o);
-        vx = *(const f32x4_t*)((const float*)(fresh ? p.v_new : p.v) + o);
-      }
+      const bool in = j0 + kk < nk;
       float* kd = &sK[kk * KSTR + 4 * c4];
-      kd[0] = kx[0];
-      kd[1] = kx[1];
-      kd[2] = kx[2];
-      kd[3] = kx[3];
-      *(f32x4_t*)&sV[kk * VSTR + 4 * c4] = vx;
+      kd[0] = in ? kx[it][0] : 0.0f;
+      kd[1] = in ? kx[it][1] : 0.0f;
+      kd[2] = in ? kx[it][2] : 0.0f;
+      kd[3] = in ? kx[it][3] : 0.0f;
+      *(f32x4_t*)&sV[kk * VSTR + 4 * c4] = in ? vx[it] : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     wave_lds_sync();
 
