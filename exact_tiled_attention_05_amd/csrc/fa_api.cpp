@@ -181,6 +181,18 @@ int splitkv(const void* q, const void* k_cache, const void* v_cache, const void*
   if ((int64_t)p.num_q_tiles * heads * batch * num_splits > kMaxGroups) return FA_ERR_SHAPE;
 
   const bool sc = softcap > 0.0f, al = alibi_slopes != nullptr;
+  if (k_new && in_dtype == FA_BF16 && seqlen_q != 1 && page_size % 16 == 0) {
+    // Several appended rows: the append runs as a launch of its own, then the
+    // split pass reads every key from the cache in page slabs (the fused form
+    // would gather the rows one by one).
+    const int head = head_dim == 64 ? fa::launch_append_bf16<64>(p, stream)
+                                    : fa::launch_append_bf16<128>(p, stream);
+    if (head) return FA_ERR_HIP;
+    fa::FwdParams q2 = p;
+    q2.k_new = q2.v_new = nullptr;
+    q2.appended = seqlen_q;
+    return pick_bf16<fa::FWD_PAGED_TILES>(head_dim, sc, al)(q2, stream) ? FA_ERR_HIP : FA_OK;
+  }
   Launcher fn = fp8_cache             ? pick_decode_fp8(head_dim, sc, al)
                 : in_dtype != FA_BF16 ? pick_f32<true>(head_dim, sc, al)
                 : seqlen_q != 1 && !k_new && page_size % 16 == 0

@@ -252,6 +252,11 @@ __device__ __forceinline__ SeqInfo seq_info(const FwdParams& p, int b, int h) {
       n = min(n, p.Nk - p.Nq);
       si.n_cached = n;
       n += p.Nq;
+    } else if (p.appended) {
+      // After a separate append of `appended` rows: the same counts, every key
+      // now in the cache.
+      n = min(n, p.Nk - p.appended) + p.appended;
+      si.n_cached = n;
     } else {
       si.n_cached = n;
     }

@@ -551,7 +551,26 @@ void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
+// The append of a multi-row split pass as a launch of its own (one workgroup
+// per (batch, head) copies its k_new / v_new rows into their cache pages), so
+// that the pass after it can read every key from the cache in page slabs.
+template <int D>
+__global__ __launch_bounds__(kThreads) void append_kernel(FwdParams p) {
+  const int h = blockIdx.x % p.H, b = blockIdx.x / p.H;
+  const SeqInfo si = seq_info(p, b, h);
+  append_rows<uint16_t>(p, si, b, h, D, threadIdx.x, kThreads);
+}
+
 }  // namespace
+
+template <int D>
+int launch_append_bf16(const FwdParams& p, void* stream) {
+  hipLaunchKernelGGL((append_kernel<D>), dim3((unsigned)((int64_t)p.B * p.H)), dim3(kThreads), 0,
+                     (hipStream_t)stream, p);
+  return (int)hipGetLastError();
+}
+template int launch_append_bf16<64>(const FwdParams&, void*);
+template int launch_append_bf16<128>(const FwdParams&, void*);
 
 template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 int launch_fwd_bf16(const FwdParams& p, void* stream) {

@@ -19,6 +19,8 @@ struct FwdParams {
   const int* cu_seqlens_q;  // [B + 1] packed batch offsets, or nullptr (batched layout)
   const int* cu_seqlens_k;  // [B + 1]
   const int* seqlens_k;     // [B] per-sequence key counts of a batched layout, or nullptr
+  int appended;             // rows already appended behind every seqlens_k count (the
+                            //   pass after a separate append): key counts seqlens_k + appended
   const void* k_new;        // [B, Nq, H, D] keys appended to the paged cache before attending
   const void* v_new;        //   (fa_fwd_splitkv_append), or nullptr
   int B, H;
@@ -100,6 +102,8 @@ template <int D, bool SOFTCAP, bool ALIBI, int MODE>
 int launch_fwd_fp8(const FwdParams& p, void* stream);  // head_dim 64 or 128; any mode
 template <int D, bool SOFTCAP, bool ALIBI, bool APPEND>
 int launch_decode_bf16(const FwdParams& p, void* stream);
+template <int D>
+int launch_append_bf16(const FwdParams& p, void* stream);  // k_new/v_new rows into their pages
 template <int D, bool SOFTCAP, bool ALIBI>
 int launch_decode_fp8(const FwdParams& p, void* stream);  // E4M3 paged cache, one query row
 template <int D>

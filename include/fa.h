@@ -169,8 +169,7 @@ int fa_fwd_splitkv_seqlens(const void* q, const void* k_cache, const void* v_cac
 
 /*
  * fa_fwd_splitkv_append - append each sequence's new keys to its paged cache,
- * then run the split pass over the cached keys followed by the new ones, in
- * one launch. (The key-value cache of "解密FlashAttention：如何让大语言模型推理
+ * then run the split pass over the cached keys followed by the new ones. (The key-value cache of "解密FlashAttention：如何让大语言模型推理
  * 速度翻倍": processed keys are kept and reused, and each step only adds its own
  * new tokens; page addressing as the update article's v2.5 entry.)
  *
@@ -182,9 +181,12 @@ int fa_fwd_splitkv_seqlens(const void* q, const void* k_cache, const void* v_cac
  * b (page block_table[b, t / page_size], row t % page_size). The partials are
  * those of fa_fwd_splitkv_seqlens with lengths n_b + seqlen_q: the queries
  * line up with the new keys (bottom-right rule), so under causal the last
- * query sees every key. The new keys are read from k_new / v_new during the
- * launch, never from the cache rows being written, so the call is
- * well-defined in one launch; when it has completed the cache holds them.
+ * query sees every key. In one launch (one query row, fp32, or page sizes
+ * that are not a multiple of 16) the new keys are read from k_new / v_new,
+ * never from the cache rows being written; with several bf16 rows and pages of
+ * a multiple of 16 keys the append is a launch of its own and the pass that
+ * follows it on the stream reads every key from the cache. Either way, when
+ * the call has completed the cache holds the new keys.
  * cache_seqlens is not updated (the caller owns it and adds seqlen_q).
  *
  * Requires max_seqlen_k >= seqlen_q and max_pages_per_seq * page_size >=

@@ -49,6 +49,8 @@ int launch_fwd_bf16(const FwdParams& p, void*) {
   require(MODE < FWD_PAGED_SPLIT || p.block_table, "block table");
   // Page tiles: every wavefront's 16-row slab of a 64-key tile inside one page.
   require(MODE != FWD_PAGED_TILES || (p.page_size % 16 == 0 && !p.k_new), "bf16 page tiles");
+  require(p.appended == 0 || (MODE == FWD_PAGED_TILES && p.seqlens_k && p.Nk >= p.appended),
+          "pass after an append");
   check_fwd(p, (int64_t)p.num_q_tiles * p.H * p.B * splits);
   return 0;
 }
@@ -82,6 +84,13 @@ int launch_decode_bf16(const FwdParams& p, void*) {
   require(p.q && p.k && p.v && p.block_table && p.o_part && p.lse_part, "decode pointers");
   require(!APPEND || (p.k_new && p.v_new), "append rows");
   check_fwd(p, (int64_t)p.H * p.B * p.num_splits);
+  return 0;
+}
+template <int D>
+int launch_append_bf16(const FwdParams& p, void*) {
+  require(p.k_new && p.v_new && p.k && p.v && p.block_table && p.seqlens_k, "append pointers");
+  require(p.Nq >= 1 && p.Nk >= p.Nq && p.appended == 0, "append sizes");
+  ++g_launches;
   return 0;
 }
 template <int D, bool SOFTCAP, bool ALIBI>
@@ -119,6 +128,7 @@ int noalloc_scratch(float** out) {
 
 #define STUB_D(D)                                                                      \
   template int launch_combine<D>(const CombineParams&, void*);                        \
+  template int launch_append_bf16<D>(const FwdParams&, void*);                        \
   STUB_SA(D, false, false) STUB_SA(D, false, true) STUB_SA(D, true, false) STUB_SA(D, true, true)
 #define STUB_SA(D, SC, AL)                                                             \
   template int launch_fwd_bf16<D, SC, AL, 0>(const FwdParams&, void*);                \

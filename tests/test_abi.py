@@ -515,6 +515,8 @@ def launches():
     (lambda **kw: varlen(**kw), dict()),
     (lambda **kw: split_fp8(**kw), dict()),
     (lambda **kw: split_append(**kw), dict()),
+    (lambda **kw: split_append(**kw), dict(seqlen_q=8)),             # append launch, then slabs
+    (lambda **kw: split_append(**kw), dict(seqlen_q=8, ps=7, maxp=10)),  # rows gathered
     (lambda **kw: fp8(**kw), dict()),
     (lambda **kw: split8(**kw), dict()),
     (lambda **kw: split8(**kw), dict(S=1 << 16, seqlen_k=1 << 28)),

@@ -531,6 +531,7 @@ APPEND_CASES = [
     ("bf16", 128, 2, 1, 4096, 256, 16, [4095, 2047, 255, 1], True, -1, -1, True, 30.0),
     ("bf16", 128, 2, 5, 300, 7, 3, [295, 4, 0, 150], True, 50, 0, False, 10.0),
     ("bf16", 64, 2, 130, 400, 64, 2, [270, 100, 0], True, -1, -1, True, 0.0),
+    ("bf16", 128, 3, 40, 1000, 16, 4, [960, 500, 0, 1], True, -1, -1, True, 30.0),
     ("fp32", 64, 2, 1, 500, 32, 5, [499, 0, 77], True, -1, -1, False, 0.0),
     ("fp32", 128, 2, 20, 200, 16, 3, [180, 10, 0], True, -1, -1, True, 5.0),
 ]
@@ -582,6 +583,33 @@ def test_splitkv_append_small(case):
     check(o_part.cpu().numpy(), lse_part.cpu().numpy(), rop, rlp, dtype, "partials")
     ro, rl = O.combine_ref(rop, rlp)
     check(o.cpu().numpy().transpose(0, 2, 1, 3), lse.cpu().numpy(), ro, rl, dtype, "combined")
+
+
+@pytest.mark.parametrize("d,ps", [(128, 16), (64, 64)])
+def test_multirow_append_bitwise_equals_append_then_seqlens(d, ps):
+    """Several appended rows over pages of a multiple of 16 keys: the call appends in a
+    launch of its own and then runs the slab pass over the cache, so its partials equal
+    bit for bit those of fa_fwd_splitkv_seqlens over a cache appended beforehand (by
+    the oracle) with every count raised by the appended rows."""
+    B, H, nq, nk, S = 3, 2, 60, 700, 3
+    seqlens = [640, 200, 0]
+    say(f"multi-row append vs append-then-seqlens d{d} page {ps}")
+    w = W.Workload(0, "append_eq", B=B, H=H, Nq=nq, Nk=nk, d=d, dtype="bf16", causal=True,
+                   paged=True, page_size=ps, pool_factor=1.3, num_splits=S, seed=7800 + ps)
+    q, kc, vc, bt = W.gen_paged(w, seqlens=seqlens)
+    kn = W.gen_tensor(7801 + ps, W.TENSOR_K, B, nq, H, d, 1.0, "bf16")
+    vn = W.gen_tensor(7801 + ps, W.TENSOR_V, B, nq, H, d, 1.0, "bf16")
+    tq, tbt = to_dev(q, "bf16"), torch.from_numpy(bt).cuda()
+    tkc, tvc = to_dev(kc, "bf16"), to_dev(vc, "bf16")
+    op1, lp1 = fa.attention_paged_append(tq, to_dev(kn, "bf16"), to_dev(vn, "bf16"), tkc, tvc, tbt,
+                                         torch.tensor(seqlens, dtype=torch.int32).cuda(), nk, S,
+                                         1.0 / np.sqrt(d), True)
+    want_k, want_v = O.kvcache_append_ref(kc, vc, bt, seqlens, kn, vn)
+    op2, lp2 = fa.attention_paged_splitkv(
+        tq, to_dev(want_k, "bf16"), to_dev(want_v, "bf16"), tbt, nk, S, 1.0 / np.sqrt(d), True,
+        cache_seqlens=torch.tensor([n + nq for n in seqlens], dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(op1, op2) and torch.equal(lp1, lp2)
 
 
 @pytest.mark.parametrize("dtype,nq", [("fp32", 1), ("fp32", 5), ("bf16", 1), ("bf16", 70)])
