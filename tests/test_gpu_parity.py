@@ -356,6 +356,62 @@ def test_combine_matches_oracle_on_random_partials():
 
 
 
+
+def _unaligned(t):
+    """A copy of t whose data starts 4 bytes past a 16-byte boundary."""
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    u = buf[1:].view(t.shape)
+    u.copy_(t)
+    return u
+
+
+@pytest.mark.parametrize("S,d", [(1, 128), (6, 64), (8, 128), (16, 128), (16, 64), (17, 64),
+                                 (17, 128), (32, 128), (33, 128), (70, 64)])
+def test_combine_forms(S, d):
+    """Both combine forms (16-byte segments for up to d/4 splits on aligned buffers, one
+    row per wavefront otherwise) against the oracle, on rows with some empty splits and
+    rows with every split empty; in fp32 the two forms agree to within a few roundings,
+    and each form's bf16 output is its fp32 output rounded to nearest even."""
+    say(f"combine forms S={S} d={d}")
+    rng = np.random.default_rng(1000 + 7 * S + d)
+    B, H, nq = 2, 5, 37                   # 370 rows: a partial last workgroup in both forms
+    op = rng.standard_normal((S, B, H, nq, d)).astype(np.float32)
+    lp = (rng.standard_normal((S, B, H, nq)) * 4).astype(np.float32)
+    lp[rng.random((S, B, H, nq)) < 0.2] = -np.inf
+    lp[:, 1, 2, :5] = -np.inf              # rows with every split empty
+    top = torch.from_numpy(op).cuda()
+    tlp = torch.from_numpy(lp).cuda()
+    ro, rl = O.combine_ref(op, lp)        # [B, H, nq, d]
+
+    def run(aligned, out_dtype):
+        o = torch.zeros((B, nq, H, d), dtype=out_dtype, device="cuda")
+        if not aligned:
+            o = _unaligned(o)
+        lse = torch.empty((B, H, nq), dtype=torch.float32, device="cuda")
+        fa._check(fa.fa_splitkv_combine(top if aligned else _unaligned(top), tlp, S, B, H, nq,
+                                        d, o, lse, None), "fa_splitkv_combine")
+        torch.cuda.synchronize()
+        return o.contiguous(), lse
+
+    res = {}
+    for aligned in (True, False):
+        o32, lse32 = run(aligned, torch.float32)
+        o16, lse16 = run(aligned, torch.bfloat16)
+        on = o32.cpu().numpy().transpose(0, 2, 1, 3)
+        check(on, lse32.cpu().numpy(), ro, rl, "fp32", f"combine aligned={aligned}")
+        assert np.all(on[1, 2, :5] == 0) and np.all(np.isneginf(lse32.cpu().numpy()[1, 2, :5]))
+        assert torch.equal(o16.view(torch.int16), o32.bfloat16().view(torch.int16))
+        assert torch.equal(lse16, lse32)
+        res[aligned] = (o32, lse32)
+    # The forms round the exponent arguments differently (one rounds lse*log2(e)
+    # before subtracting the maximum, the other fuses the two), nothing else.
+    (oa, la), (ou, lu) = res[True], res[False]
+    assert torch.allclose(oa, ou, rtol=1e-5, atol=1e-6)
+    fin = torch.isfinite(la)
+    assert torch.equal(fin, torch.isfinite(lu))
+    assert torch.allclose(la[fin], lu[fin], rtol=1e-6, atol=1e-6)
+
+
 # --------------------------------------------------------------------------
 # Variable sequence lengths: packed batches (fa_fwd_varlen)
 # --------------------------------------------------------------------------
