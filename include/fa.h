@@ -442,7 +442,10 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
  * Rows where every split is empty get O = 0 and L = -inf.
  *
  * Writes o [batch, seqlen_q, heads, head_dim] in o_dtype and, if lse != NULL,
- * lse [batch, heads, seqlen_q].
+ * lse [batch, heads, seqlen_q]. Any float alignment is accepted; with at most
+ * head_dim / 4 splits, o_part on a 16-byte boundary and o on a 16-byte (fp32)
+ * or 8-byte (bf16) boundary, rows are merged in 16-byte pieces (the faster form;
+ * results differ from the other form only in rounding).
  */
 int fa_splitkv_combine(const float* o_part, const float* lse_part, int num_splits,
                        int batch, int heads, int seqlen_q, int head_dim,
