@@ -701,7 +701,14 @@ def attention_split(q, k, v, num_splits=None, out_dtype=torch.float32, stream=No
 
 def combine(o_part, lse_part, out_dtype=torch.float32, stream=None):
     """Merge split partials into O [B, Nq, H, d] and LSE [B, H, Nq]."""
+    if o_part.dim() != 5 or o_part.dtype != torch.float32:
+        raise ValueError("o_part must be float32 [S, B, H, Nq, d]")
     S, B, H, nq, d = o_part.shape
+    if tuple(lse_part.shape) != (S, B, H, nq) or lse_part.dtype != torch.float32:
+        raise ValueError(f"lse_part must be float32 {(S, B, H, nq)} to match o_part, "
+                         f"got {lse_part.dtype} {tuple(lse_part.shape)}")
+    if lse_part.device != o_part.device:
+        raise ValueError(f"lse_part lives on {lse_part.device}, o_part on {o_part.device}")
     o = torch.empty((B, nq, H, d), dtype=out_dtype, device=o_part.device)
     lse = torch.empty((B, H, nq), dtype=torch.float32, device=o_part.device)
     _check(fa_splitkv_combine(o_part, lse_part, S, B, H, nq, d, o, lse, stream),

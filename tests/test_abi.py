@@ -499,6 +499,23 @@ def test_binding_checks_alibi_slopes():
         fa._slopes_ptr(torch.ones(h, dtype=torch.float32), h, torch.empty(1, device="meta"))
 
 
+
+def test_binding_combine_checks_partials():
+    """combine() takes its sizes from o_part, so a log-sum-exp buffer of another
+    shape or dtype (which the kernel would read past its end) is refused first."""
+    import torch
+    op = torch.zeros(3, 2, 4, 5, 64)
+    with pytest.raises(ValueError):
+        fa.combine(op, torch.zeros(3, 2, 4, 6))
+    with pytest.raises(ValueError):
+        fa.combine(op, torch.zeros(3, 2, 4, 5, dtype=torch.float64))
+    with pytest.raises(ValueError):
+        fa.combine(op.double(), torch.zeros(3, 2, 4, 5))
+    with pytest.raises(ValueError):
+        fa.combine(op[0], torch.zeros(2, 4, 5))
+    with pytest.raises(ValueError):  # lse_part on another device
+        fa.combine(op, torch.zeros(3, 2, 4, 5, device="meta"))
+
 def launches():
     return fa.load_library().fa_stub_launches()
 
