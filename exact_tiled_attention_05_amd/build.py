@@ -75,7 +75,7 @@ def build(verbose: bool = False, extra_flags=None, out: str = LIB, build_dir: st
 # Sources whose LDS pipelines have a single-buffered verification form
 # (FA_SERIAL_COPIES: every tile copied, waited for and fenced by barriers on
 # both sides, no copy overlapping compute).
-SERIAL_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_fp8.hip"]
+SERIAL_SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_bwd_bf16.hip"]
 SERIAL_LIB = os.path.join(ROOT, "tests", "hazard", "libfa_serial_copies.so")
 
 

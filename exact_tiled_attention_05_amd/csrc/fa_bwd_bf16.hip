@@ -424,11 +424,30 @@ void bwd_dkdv_kernel(BwdParams p) {
       }
       wait_vmem_barrier<0>();  // block it + 1 has landed; P' of block it is visible
     };
+#ifdef FA_SERIAL_COPIES
+    // Verification build: one stage, each block copied, waited for and fenced by
+    // barriers; role 1 finishes the block before the next copy. Three barriers per
+    // block, as in role 1's loop below. The arithmetic and its order are unchanged.
+    for (int it = 0; it < nblocks; ++it) {
+      const int qb = qb_first + it * kBQ;
+      copy_block(sQ0, sG0, sR0, qb);
+      wait_vmem_barrier<0>();
+      if (live(qb)) {
+        if (group_full && qb >= wflo && qb + kBQ <= wfhi)
+          compute(std::false_type{}, sQ0, sG0, sR0, sX0 + grp * XG, qb);
+        else
+          compute(std::true_type{}, sQ0, sG0, sR0, sX0 + grp * XG, qb);
+      }
+      __syncthreads();  // P' of the block is visible to role 1
+      __syncthreads();  // role 1 is done with the block
+    }
+#else
     for (int it = 0; it < nblocks; it += 3) {
       step(I0{}, it);
       if (it + 1 < nblocks) step(I1{}, it + 1);
       if (it + 2 < nblocks) step(I2{}, it + 2);
     }
+#endif
   } else {
     // ---- role 1: dP, then dZ and dK one block behind
     f32x16_t pprev = f32x16_t{};
@@ -494,6 +513,19 @@ void bwd_dkdv_kernel(BwdParams p) {
       pprev = pcur;
       wait_vmem_barrier<0>();
     };
+#ifdef FA_SERIAL_COPIES
+    (void)pprev;
+    for (int it = 0; it < nblocks; ++it) {
+      const int qb = qb_first + it * kBQ;
+      copy_block(sQ0, sG0, sR0, qb);
+      wait_vmem_barrier<0>();
+      f32x16_t pcur = f32x16_t{};
+      if (live(qb)) pcur = dp_block(sG0);
+      __syncthreads();  // role 0's P' of the block is visible
+      if (live(qb)) dk_block(sQ0, sR0, sX0 + grp * XG, pcur);
+      __syncthreads();
+    }
+#else
     for (int it = 0; it < nblocks; it += 3) {
       step(I0{}, it);
       if (it + 1 < nblocks) step(I1{}, it + 1);
@@ -508,6 +540,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       const float* sx = (last & 1) ? sX1 : sX0;
       dk_block(sq, sr, sx + grp * XG, pprev);
     }
+#endif
   }
 
   // Epilogue: lane = key, slots = head_dim rows 32db + 8g + 4h2 + {0..3}.
@@ -757,6 +790,22 @@ void bwd_dkdv_w4_kernel(BwdParams p) {
     __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 1);
   };
 
+#ifdef FA_SERIAL_COPIES
+  // Verification build: one stage, each block copied, waited for and fenced by
+  // barriers on both sides (the arithmetic and its order are unchanged).
+  for (int it = 0; it < nblocks; ++it) {
+    const int qb = qb_first + it * kBQ;
+    copy_block(sQ0, sG0, sR0, qb);
+    wait_vmem_barrier<0>();
+    if (wave_live && qb < whi && qb + kBQ > wlo) {
+      if (wave_full && qb >= wflo && qb + kBQ <= wfhi)
+        compute(std::false_type{}, sQ0, sG0, sR0, qb);
+      else
+        compute(std::true_type{}, sQ0, sG0, sR0, qb);
+    }
+    __syncthreads();
+  }
+#else
   copy_block(sQ0, sG0, sR0, qb_first);
   copy_block(sQ1, sG1, sR1, qb_first + kBQ);
   copy_block(sQ2, sG2, sR2, qb_first + 2 * kBQ);
@@ -791,6 +840,7 @@ void bwd_dkdv_w4_kernel(BwdParams p) {
     if (it + 3 < nblocks) step(I3{}, it + 3);
   }
   wait_vmem_barrier<0>();  // no copy may still be writing LDS at exit
+#endif
 
   // Epilogue: lane = key, slots = head_dim rows 32db + 8g + 4h2 + {0..3}.
   if (key >= k1) return;
@@ -990,6 +1040,17 @@ void bwd_dq_kernel(BwdParams p) {
 
   const int j_first = (wg.lo / kBN) * kBN;
   const int ntiles = (wg.hi - j_first + kBN - 1) / kBN;
+#ifdef FA_SERIAL_COPIES
+  // Verification build: one buffer per tensor, each tile copied, waited for and
+  // fenced by barriers on both sides (the arithmetic and its order are unchanged).
+  for (int it = 0; it < ntiles; ++it) {
+    const int j0 = j_first + it * kBN;
+    copy_tiles(sK0, sV0, j0);
+    wait_vmem_barrier<0>();
+    if (wave_live && j0 < wk.hi && j0 + kBN > wk.lo) compute(sK0, sV0, j0);
+    __syncthreads();
+  }
+#else
   copy_tiles(sK0, sV0, j_first);
   wait_vmem_barrier<0>();
   auto step = [&](auto par, int it) __attribute__((always_inline)) {
@@ -1003,6 +1064,7 @@ void bwd_dq_kernel(BwdParams p) {
     step(std::false_type{}, it);
     if (it + 1 < ntiles) step(std::true_type{}, it + 1);
   }
+#endif
 
   if (row >= nq) return;
   const int64_t base = ((sq.q_row0 + row) * p.H + h) * D;

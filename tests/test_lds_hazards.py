@@ -8,8 +8,10 @@ are unchanged, so every output must agree bit for bit with libfa.so; a copy that
 overwrote a stage still being read, or a read of a stage not yet written, would show
 up as a difference. Covered: the contiguous forward (whole key range, batched and
 packed), its key splits, the paged multi-row pass with page-aligned tiles, with
-per-wavefront slabs of 16-key pages and with rows gathered one by one, and the FP8 forward (whole key range, key splits, and a paged
-cache in whole tiles, in per-wavefront slabs and in row gathers) at both head sizes.
+per-wavefront slabs of 16-key pages and with rows gathered one by one, the FP8 forward (whole key range, key splits, and a paged
+cache in whole tiles, in per-wavefront slabs and in row gathers) at both head sizes, and the
+backward (the dK/dV kernels' query-block rings at both head sizes, including the two-role
+exchange of P' at head_dim 128, and the dQ kernel's key-tile buffers), batched and packed.
 """
 import ctypes
 import os
@@ -156,3 +158,46 @@ def test_fp8_paged_matches_serial_copies(serial_lib, d, page_size):
     m, s = both(serial_lib, fa.attention_paged_fp8, q8, tk, tv, tbt, w.Nk, 3, 0.5, 1.0, 2.0,
                 1.0 / np.sqrt(d), True, -1, -1, ts, 20.0, cache_seqlens=tsl)
     assert_same(m, s, f"fa_fwd_paged_fp8 d{d}")
+
+
+
+BWD_CASES = [
+    # (B, H, nq, nk, d, causal, wl, wr, alibi, cap)
+    (4, 16, 2048, 2048, 128, True, -1, -1, False, 0.0),     # the causal prefill shape
+    (2, 8, 512, 4096, 128, True, -1, -1, True, 30.0),       # ALiBi + softcap, Nq != Nk
+    (2, 4, 1000, 333, 128, True, -1, -1, False, 0.0),       # rows with no key
+    (1, 3, 300, 1000, 128, False, 77, 30, True, 0.0),       # a window on both sides
+    (2, 2, 129, 65, 128, False, -1, -1, False, 12.0),       # ragged blocks
+    (2, 8, 1024, 1024, 64, True, -1, -1, False, 0.0),
+    (1, 3, 300, 1000, 64, False, 77, 30, True, 10.0),
+    (2, 2, 1000, 333, 64, True, -1, -1, False, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES)
+def test_backward_matches_serial_copies(serial_lib, case):
+    B, H, nq, nk, d, causal, wl, wr, alibi, cap = case
+    say(f"hazard fa_bwd {case}")
+    seed = 7600 + BWD_CASES.index(case)
+    q, k, v = qkv(seed, B, nq, nk, H, d, 2.0 if cap else 1.0)
+    dout = to_dev(W.gen_tensor(seed, W.TENSOR_V, B, nq, H, d, 1.0, "bf16"), "bf16")
+    ts = torch.from_numpy(W.alibi_slopes(H)).cuda() if alibi else None
+    o, lse = fa.attention(q, k, v, 1.0 / np.sqrt(d), causal, wl, wr, ts, cap)
+    m, s = both(serial_lib, fa.attention_backward, q, k, v, o, lse, dout, 1.0 / np.sqrt(d),
+                causal, wl, wr, ts, cap)
+    assert_same(m, s, f"fa_bwd {case}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_packed_backward_matches_serial_copies(serial_lib, d):
+    lens = W.varlen_lengths(93, 6, 1500)
+    say(f"hazard fa_bwd_varlen d{d} {lens.tolist()}")
+    q, k, v, cq, ck = W.gen_varlen(12600 + d, lens, lens, 4, d, 1.0, "bf16")
+    tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    tcq, tck = torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda()
+    n = int(lens.max())
+    o, lse = fa.attention_varlen(tq, tk, tv, tcq, tck, n, n, 1.0 / np.sqrt(d), True)
+    dout = torch.randn(tq.shape, generator=torch.Generator().manual_seed(d)).bfloat16().cuda()
+    m, s = both(serial_lib, fa.attention_varlen_backward, tq, tk, tv, o, lse, dout, tcq, tck, n,
+                n, 1.0 / np.sqrt(d), True)
+    assert_same(m, s, f"fa_bwd_varlen d{d}")
