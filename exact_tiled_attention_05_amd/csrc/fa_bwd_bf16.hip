@@ -888,8 +888,11 @@ void bwd_dq_kernel(BwdParams p) {
   const int b = L % p.B;
   const BwdSeq sq = bwd_seq(p, b, h);
   const int nq = sq.nq, nk = sq.nk, off = nk - nq;
-  const int qt = (nq + kBM - 1) / kBM - 1 - L / p.B;  // heaviest (last) tile first
-  if (qt < 0) return;  // a packed sequence shorter than the longest
+  // Heaviest (last) tile first: of the sequence in a batched layout, of the
+  // longest sequence in a packed one (one order of absolute tile position
+  // across the pack, as in the forward).
+  const int qt = p.cu_seqlens_q ? p.num_q_tiles - 1 - L / p.B : (nq + kBM - 1) / kBM - 1 - L / p.B;
+  if (qt < 0 || qt * kBM >= nq) return;  // a packed sequence without this tile
   const int q0 = qt * kBM, q1 = min(nq, q0 + kBM);
   const KeyBounds wg = key_bounds(q0, q1, off, 0, nk, p.window_left, p.window_right);
   if (wg.hi <= wg.lo) {

@@ -393,10 +393,16 @@ __device__ __forceinline__ WorkItem decode_work(const FwdParams& p) {
   return w;
 }
 
-// Query tile of a work item in a sequence of nq rows; negative when the
-// sequence has fewer tiles than the longest one.
-__device__ __forceinline__ int query_tile(const WorkItem& w, int nq, int tile_rows) {
-  return (nq + tile_rows - 1) / tile_rows - 1 - w.rank;
+// Query tile of a work item in a sequence of nq rows, counted from the last
+// tile: of the sequence in a batched layout, of the longest sequence
+// (num_q_tiles - 1 - rank) in a packed one, so that a packed batch runs its
+// tiles in one order of absolute position (under a causal mask, heaviest
+// first across the whole pack). Negative when the sequence has no such tile.
+__device__ __forceinline__ int query_tile(const FwdParams& p, const WorkItem& w, int nq,
+                                          int tile_rows) {
+  const int qt = p.cu_seqlens_q ? p.num_q_tiles - 1 - w.rank
+                                : (nq + tile_rows - 1) / tile_rows - 1 - w.rank;
+  return qt * tile_rows < nq ? qt : -1;
 }
 
 }  // namespace fa

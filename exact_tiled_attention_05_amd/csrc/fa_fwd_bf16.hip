@@ -91,7 +91,7 @@ void fwd_bf16_kernel(FwdParams p) {
     // Append: one workgroup per (b, h) copies the new keys into their pages.
     if (p.k_new && s == 0 && wi.rank == 0) append_rows<uint16_t>(p, si, b, h, D, tid, kThreads);
   }
-  const int qt = query_tile(wi, nq, kBM);
+  const int qt = query_tile(p, wi, nq, kBM);
   if (qt < 0) return;  // a packed sequence shorter than the longest
 
   const int off = nk - nq;

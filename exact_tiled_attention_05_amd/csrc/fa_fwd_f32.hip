@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
     // Append: one workgroup per (b, h) copies the new keys into their pages.
     if (p.k_new && s == 0 && wi.rank == 0) append_rows<float>(p, si, b, h, D, tid, kThreads);
   }
-  const int qt = query_tile(wi, nq, F32_BM);
+  const int qt = query_tile(p, wi, nq, F32_BM);
   if (qt < 0) return;  // a packed sequence shorter than the longest
 
   const int off = nk - nq;

@@ -118,7 +118,7 @@ void fwd_fp8_kernel(FwdParams p) {
   const int b = wi.b, h = wi.h, s = wi.s;
   const SeqInfo si = seq_info(p, b, h);
   const int nq = si.nq, nk = si.nk;
-  const int qt = query_tile(wi, nq, kBM);
+  const int qt = query_tile(p, wi, nq, kBM);
   if (qt < 0) return;
   const int off = nk - nq;
   int slo = 0, shi = nk;
