@@ -256,8 +256,9 @@ int bwd(const void* q, const void* k, const void* v, const void* o, const void* 
   p.scale_log2 = f.scale_log2;
   p.softcap_log2 = f.softcap_log2;
   p.scale_over_cap2 = f.scale_over_cap2;
-  if ((int64_t)p.num_q_tiles * heads * batch > kMaxGroups ||
-      (int64_t)p.num_k_tiles * heads * batch > kMaxGroups ||
+  // (dK/dV and dQ share one grid at head_dim 128: two key-tile workgroups per
+  // BWD_BK keys, then the query tiles.)
+  if ((2 * (int64_t)p.num_k_tiles + p.num_q_tiles) * heads * batch > kMaxGroups ||
       (int64_t)p.nblk * fa::BWD_RB * heads * batch / 8 > kMaxGroups)
     return FA_ERR_SHAPE;
   // Everything is validated: only now the static buffer's address (a HIP call).

@@ -205,9 +205,13 @@ constexpr int kDkdvThreads = 256;
 constexpr int kDkdvGroups = 2;                   // key groups of 32 per workgroup
 constexpr int kDkdvKeys = 32 * kDkdvGroups;      // keys per workgroup (head_dim 128)
 
+// LDS of the head_dim-128 dK/dV workgroup: three Q and three dO stages, two P'
+// buffers and three row-term stages, in that order.
+constexpr int kDkdvLdsBytes = 6 * (BWD_RB * 128 * 2) + 2 * (kDkdvGroups * 16 * 64 * 4) + 3 * (2 * BWD_RB * 4);
+
+// dK/dV of key tile `block` (flat index, head fastest) with its LDS at `lds`.
 template <int D, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dkdv_kernel(BwdParams p) {
+__device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int block, char* lds) {
   constexpr int KS = D / 16;               // k-steps over head_dim
   constexpr int NDB = D / 32;              // 32-row blocks of dK^T / dV^T
   constexpr int CPR = D / 8;               // 16-byte chunks per row
@@ -219,23 +223,24 @@ void bwd_dkdv_kernel(BwdParams p) {
   constexpr int kReadAhead = 4;            // transposed-read MFMAs in flight
   constexpr int XG = 16 * 64;              // floats of P' per key group
 
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ0[QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ1[QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ2[QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sG0[QT];  // dO
-  __shared__ __attribute__((aligned(1024))) uint16_t sG1[QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sG2[QT];
-  __shared__ __attribute__((aligned(256))) float sR0[2 * kBQ];  // LSE2 | D
-  __shared__ __attribute__((aligned(256))) float sR1[2 * kBQ];
-  __shared__ __attribute__((aligned(256))) float sR2[2 * kBQ];
-  __shared__ __attribute__((aligned(1024))) float sX0[kDkdvGroups * XG];  // P' of even blocks
-  __shared__ __attribute__((aligned(1024))) float sX1[kDkdvGroups * XG];  // P' of odd blocks
+  static_assert(D == 128, "layout of kDkdvLdsBytes");
+  uint16_t* const sQ0 = (uint16_t*)lds;  // 1024-byte aligned, as every stage below
+  uint16_t* const sQ1 = sQ0 + QT;
+  uint16_t* const sQ2 = sQ1 + QT;
+  uint16_t* const sG0 = sQ2 + QT;  // dO
+  uint16_t* const sG1 = sG0 + QT;
+  uint16_t* const sG2 = sG1 + QT;
+  float* const sX0 = (float*)(sG2 + QT);      // P' of even blocks
+  float* const sX1 = sX0 + kDkdvGroups * XG;  // P' of odd blocks
+  float* const sR0 = sX1 + kDkdvGroups * XG;  // LSE2 | D
+  float* const sR1 = sR0 + 2 * kBQ;
+  float* const sR2 = sR1 + 2 * kBQ;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
   const int grp = w & (kDkdvGroups - 1);
   const int role = __builtin_amdgcn_readfirstlane(w / kDkdvGroups);
-  int L = blockIdx.x;
+  int L = block;
   const int h = L % p.H;
   L /= p.H;
   const int b = L % p.B;
@@ -860,9 +865,9 @@ void bwd_dkdv_w4_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // 3. dQ
 // ---------------------------------------------------------------------------
+// dQ of query tile `block` (flat index, head fastest) with its LDS at `lds`.
 template <int D, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int block, char* lds) {
   constexpr int KS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int CPR = D / 8;
@@ -874,7 +879,7 @@ void bwd_dq_kernel(BwdParams p) {
 
   // The four stages in one array: a K read and the V read of the same k-step
   // differ by a constant, so they share an address register (immediate offset).
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
+  uint16_t* const smem = (uint16_t*)lds;  // 1024-byte aligned
   uint16_t* const sK0 = smem;
   uint16_t* const sK1 = smem + TILE;
   uint16_t* const sV0 = smem + 2 * TILE;
@@ -882,7 +887,7 @@ void bwd_dq_kernel(BwdParams p) {
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
-  int L = blockIdx.x;
+  int L = block;
   const int h = L % p.H;
   L /= p.H;
   const int b = L % p.B;
@@ -1080,6 +1085,30 @@ void bwd_dq_kernel(BwdParams p) {
                   dqacc[db][4 * g + 3] * p.scale);
 }
 
+// dQ on its own (head_dim 64, after the four-wavefront dK/dV kernel).
+template <int D, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds[4 * kBN * D * 2];
+  bwd_dq_body<D, SOFTCAP, ALIBI>(p, blockIdx.x, lds);
+}
+
+// dK/dV and dQ in one launch (head_dim 128): workgroups [0, n_dkdv) are dK/dV's
+// key tiles, the rest dQ's query tiles. Both only read the row terms, so the
+// dQ workgroups start as soon as CUs free up and fill the slots that dK/dV's
+// last workgroups leave idle (two launches would wait for dK/dV to drain).
+template <int D, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_dq_kernel(BwdParams p, int n_dkdv) {
+  static_assert(kDkdvThreads == kThreads, "one workgroup size");
+  constexpr int kDqLds = 4 * kBN * D * 2;
+  __shared__ __attribute__((aligned(1024))) char lds[kDkdvLdsBytes > kDqLds ? kDkdvLdsBytes : kDqLds];
+  if ((int)blockIdx.x < n_dkdv)
+    bwd_dkdv_body<D, SOFTCAP, ALIBI>(p, blockIdx.x, lds);
+  else
+    bwd_dq_body<D, SOFTCAP, ALIBI>(p, blockIdx.x - n_dkdv, lds);
+}
+
 }  // namespace
 
 template <int D, bool SOFTCAP, bool ALIBI>
@@ -1094,15 +1123,18 @@ int launch_bwd_bf16(const BwdParams& p, void* stream) {
   // Key tiles of BWD_BK keys (head_dim 64) or kDkdvKeys keys (head_dim 128; the
   // workgroups past a sequence's keys exit at once).
   const int64_t ktiles = D == 128 ? (int64_t)p.num_k_tiles * (BWD_BK / kDkdvKeys) : p.num_k_tiles;
-  const dim3 kgrid((unsigned)(ktiles * p.H * p.B));
-  if constexpr (D == 128)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, SOFTCAP, ALIBI>), kgrid, dim3(kDkdvThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_w4_kernel<D, SOFTCAP, ALIBI>), kgrid, dim3(kThreads), 0, s, p);
+  const int64_t n_dkdv = ktiles * p.H * p.B;
+  const int64_t n_dq = (int64_t)p.num_q_tiles * p.H * p.B;
+  if constexpr (D == 128) {
+    hipLaunchKernelGGL((bwd_dkdv_dq_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)(n_dkdv + n_dq)),
+                       dim3(kThreads), 0, s, p, (int)n_dkdv);
+    return (int)hipGetLastError();
+  }
+  hipLaunchKernelGGL((bwd_dkdv_w4_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)n_dkdv), dim3(kThreads), 0,
+                     s, p);
   rc = (int)hipGetLastError();
   if (rc) return rc;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, SOFTCAP, ALIBI>),
-                     dim3((unsigned)((int64_t)p.num_q_tiles * p.H * p.B)), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)n_dq), dim3(kThreads), 0, s, p);
   return (int)hipGetLastError();
 }
 
