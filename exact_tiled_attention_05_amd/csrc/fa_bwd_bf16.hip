@@ -570,9 +570,13 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int block, cha
 // P' exchange, so its 50 KiB of LDS let two workgroups share a CU, which the
 // split kernel's larger footprint does not.
 // ---------------------------------------------------------------------------
+// LDS of the head_dim-64 dK/dV workgroup: the V tile, four Q and four dO
+// stages and four row-term stages, in that order.
+constexpr int kW4LdsBytes = BWD_BK * 64 * 2 + 8 * (BWD_RB * 64 * 2) + 4 * (2 * BWD_RB * 4);
+
+// dK/dV of key tile `block` (flat index, head fastest) with its LDS at `lds`.
 template <int D, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dkdv_w4_kernel(BwdParams p) {
+__device__ __forceinline__ void bwd_dkdv_w4_body(const BwdParams& p, int block, char* lds) {
   constexpr int KS = D / 16;               // k-steps over head_dim
   constexpr int NDB = D / 32;              // 32-row blocks of dK^T / dV^T
   constexpr int CPR = D / 8;               // 16-byte chunks per row
@@ -588,23 +592,24 @@ void bwd_dkdv_w4_kernel(BwdParams p) {
 
   // Q / dO / row-term blocks cycle through four stages: the copy of block t+3
   // is issued while block t is computed, so three blocks of copies are in flight.
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[kBK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ0[QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ1[QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ2[QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ3[QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sG0[QT];  // dO
-  __shared__ __attribute__((aligned(1024))) uint16_t sG1[QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sG2[QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t sG3[QT];
-  __shared__ __attribute__((aligned(256))) float sR0[2 * kBQ];  // LSE2 | D
-  __shared__ __attribute__((aligned(256))) float sR1[2 * kBQ];
-  __shared__ __attribute__((aligned(256))) float sR2[2 * kBQ];
-  __shared__ __attribute__((aligned(256))) float sR3[2 * kBQ];
+  static_assert(D == 64, "layout of kW4LdsBytes");
+  uint16_t* const sV = (uint16_t*)lds;  // 1024-byte aligned, as every stage below
+  uint16_t* const sQ0 = sV + kBK * D;
+  uint16_t* const sQ1 = sQ0 + QT;
+  uint16_t* const sQ2 = sQ1 + QT;
+  uint16_t* const sQ3 = sQ2 + QT;
+  uint16_t* const sG0 = sQ3 + QT;  // dO
+  uint16_t* const sG1 = sG0 + QT;
+  uint16_t* const sG2 = sG1 + QT;
+  uint16_t* const sG3 = sG2 + QT;
+  float* const sR0 = (float*)(sG3 + QT);  // LSE2 | D
+  float* const sR1 = sR0 + 2 * kBQ;
+  float* const sR2 = sR1 + 2 * kBQ;
+  float* const sR3 = sR2 + 2 * kBQ;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h2 = lane >> 5;
-  int L = blockIdx.x;
+  int L = block;
   const int h = L % p.H;
   L /= p.H;
   const int b = L % p.B;
@@ -1085,28 +1090,26 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int block, char*
                   dqacc[db][4 * g + 3] * p.scale);
 }
 
-// dQ on its own (head_dim 64, after the four-wavefront dK/dV kernel).
-template <int D, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char lds[4 * kBN * D * 2];
-  bwd_dq_body<D, SOFTCAP, ALIBI>(p, blockIdx.x, lds);
-}
-
-// dK/dV and dQ in one launch (head_dim 128): workgroups [0, n_dkdv) are dK/dV's
-// key tiles, the rest dQ's query tiles. Both only read the row terms, so the
-// dQ workgroups start as soon as CUs free up and fill the slots that dK/dV's
+// dK/dV and dQ in one launch: workgroups [0, n_dkdv) are dK/dV's key tiles,
+// the rest dQ's query tiles. Both only read the row terms, so the dQ
+// workgroups start as soon as CUs free up and fill the slots that dK/dV's
 // last workgroups leave idle (two launches would wait for dK/dV to drain).
+// One LDS allocation, the larger of the two layouts.
 template <int D, bool SOFTCAP, bool ALIBI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_dq_kernel(BwdParams p, int n_dkdv) {
   static_assert(kDkdvThreads == kThreads, "one workgroup size");
+  constexpr int kDkdvLds = D == 128 ? kDkdvLdsBytes : kW4LdsBytes;
   constexpr int kDqLds = 4 * kBN * D * 2;
-  __shared__ __attribute__((aligned(1024))) char lds[kDkdvLdsBytes > kDqLds ? kDkdvLdsBytes : kDqLds];
-  if ((int)blockIdx.x < n_dkdv)
-    bwd_dkdv_body<D, SOFTCAP, ALIBI>(p, blockIdx.x, lds);
-  else
+  __shared__ __attribute__((aligned(1024))) char lds[kDkdvLds > kDqLds ? kDkdvLds : kDqLds];
+  if ((int)blockIdx.x < n_dkdv) {
+    if constexpr (D == 128)
+      bwd_dkdv_body<D, SOFTCAP, ALIBI>(p, blockIdx.x, lds);
+    else
+      bwd_dkdv_w4_body<D, SOFTCAP, ALIBI>(p, blockIdx.x, lds);
+  } else {
     bwd_dq_body<D, SOFTCAP, ALIBI>(p, blockIdx.x - n_dkdv, lds);
+  }
 }
 
 }  // namespace
@@ -1125,16 +1128,8 @@ int launch_bwd_bf16(const BwdParams& p, void* stream) {
   const int64_t ktiles = D == 128 ? (int64_t)p.num_k_tiles * (BWD_BK / kDkdvKeys) : p.num_k_tiles;
   const int64_t n_dkdv = ktiles * p.H * p.B;
   const int64_t n_dq = (int64_t)p.num_q_tiles * p.H * p.B;
-  if constexpr (D == 128) {
-    hipLaunchKernelGGL((bwd_dkdv_dq_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)(n_dkdv + n_dq)),
-                       dim3(kThreads), 0, s, p, (int)n_dkdv);
-    return (int)hipGetLastError();
-  }
-  hipLaunchKernelGGL((bwd_dkdv_w4_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)n_dkdv), dim3(kThreads), 0,
-                     s, p);
-  rc = (int)hipGetLastError();
-  if (rc) return rc;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)n_dq), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((bwd_dkdv_dq_kernel<D, SOFTCAP, ALIBI>), dim3((unsigned)(n_dkdv + n_dq)),
+                     dim3(kThreads), 0, s, p, (int)n_dkdv);
   return (int)hipGetLastError();
 }
 
