@@ -364,8 +364,8 @@ int fa_fwd_paged_fp8(const void* q, const void* k_cache, const void* v_cache, fl
  *                  rounded up to a multiple of 32 per (batch, head)); overwritten
  * P and dZ are rounded to bf16 as matrix-core operands (accumulation in
  * fp32). Masks, scale, ALiBi and softcap must be those of the forward call.
- * Three kernels run in order on `stream`. Errors as fa_fwd; fp32 inputs are
- * FA_ERR_UNSUPPORTED.
+ * Two launches run in order on `stream`: the per-row terms, then dK/dV and dQ
+ * together. Errors as fa_fwd; fp32 inputs are FA_ERR_UNSUPPORTED.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, int in_dtype, int o_dtype, void* dq, void* dk, void* dv,
