@@ -220,7 +220,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int block, cha
   static_assert(QL >= 1 && kBQ == BWD_RB, "tile shape");
   constexpr int QT = kBQ * D;
   constexpr int kSReadAhead = 3;           // k-steps of dO operands read ahead in dP
-  constexpr int kReadAhead = 4;            // transposed-read MFMAs in flight
+  constexpr int kReadAhead = 8;            // transposed-read MFMAs in flight (all of a product's)
+  static_assert(kReadAhead <= 2 * (D / 32), "read-ahead");
   constexpr int XG = 16 * 64;              // floats of P' per key group
 
   static_assert(D == 128, "layout of kDkdvLdsBytes");
