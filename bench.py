@@ -127,6 +127,45 @@ def allowed_pairs(nq, nk, causal, wl, wr):
     return int(np.maximum(0, hi - lo + 1).sum())
 
 
+def window_sweep(fa, W, dev, up, args):
+    """Time fa_fwd on the sliding-window shape (B1 H16 N16384 d64, causal) for window widths from
+    256 keys to the whole causal range: with tiles outside each row's window skipped, the time
+    follows the in-window pairs, not N^2 ([Updates] v2.3)."""
+    import torch
+    ww = W.WORKLOADS[3]
+    q, k, v = (up(x, ww.dtype) for x in W.gen_qkv(ww))
+    o = torch.empty((ww.B, ww.Nq, ww.H, ww.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((ww.B, ww.H, ww.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    n = max(args.steps, 5)
+    for wl in (256, 512, 1024, 2048, 4096, 8192, -1):
+        def call():
+            st = fa.fa_fwd(q, k, v, o, lse, ww.B, ww.H, ww.Nq, ww.Nk, ww.d, ww.scale, True, wl, 0,
+                           None, 0.0, stream)
+            if st != 0:
+                raise fa.FaError(st, "fa_fwd")
+        for _ in range(max(args.warmup, 1)):
+            call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call()
+            b.record(stream)
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+        pairs = allowed_pairs(ww.Nq, ww.Nk, True, wl, 0)
+        gflop = 4.0 * ww.B * ww.H * ww.d * pairs / 1e9
+        us = float(np.median(times))
+        print(json.dumps({"workload": f"sliding window B{ww.B} H{ww.H} N{ww.Nq} d{ww.d} causal",
+                          "window_left": wl, "in_window_pairs_per_head": pairs,
+                          "dense_fraction": round(pairs / (ww.Nq * ww.Nk), 4),
+                          "gflop": round(gflop, 3), "us_median": round(us, 1),
+                          "us_min": round(float(np.min(times)), 1),
+                          "tflops": round(gflop / us * 1e3, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +175,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--print-source-hashes", action="store_true")
+    ap.add_argument("--window-sweep", action="store_true",
+                    help="only time fa_fwd on the 16K sliding-window shape at several window widths "
+                         "(one JSON line per width: time against the in-window work)")
     args = ap.parse_args()
     if args.print_source_hashes:
         print(json.dumps({k: source_hash(k) for k in KERNEL_SOURCES}))
@@ -167,6 +209,10 @@ def main():
         if dtype == "bf16":
             return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(x).to(dev)
+
+    if args.window_sweep:
+        window_sweep(fa, W, dev, up, args)
+        return
 
     def up8(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # E4M3 codes as uint8
